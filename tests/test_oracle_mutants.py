@@ -1,0 +1,81 @@
+"""Plants plausible mistakes in a copy of the oracle (on the CPU) and checks
+that the pins catch every one of them: a pin set that a wrong oracle passes
+would pin nothing."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import build as obuild
+from pins import ALL_PINS
+
+SRC = open(obuild.SRC).read()
+
+MUTANTS = {
+    # decay of token t taken from the previous token's dt
+    "decay_index": ("const double decay = exp(dtt * A[h]);",
+                    "const double decay = exp(dt[(size_t)(t > t0 ? t - 1 : t) * H + h] * A[h]);"),
+    # wrong sign of A
+    "sign_A": ("const double decay = exp(dtt * A[h]);",
+               "const double decay = exp(-dtt * A[h]);"),
+    # skip term dropped
+    "drop_D": ("yt[p] += acc + Dh * xt[p];", "yt[p] += acc;"),
+    # dt dropped from the input term
+    "drop_dt_input": ("hp[n] = decay * hp[n] + dtt * Bt[n] * xt[p];",
+                      "hp[n] = decay * hp[n] + Bt[n] * xt[p];"),
+    # B and C exchanged
+    "swap_BC": ("const double *Bt = B + ((size_t)t * G + g) * N;\n        const double *Ct = C + ((size_t)t * G + g) * N;",
+                "const double *Bt = C + ((size_t)t * G + g) * N;\n        const double *Ct = B + ((size_t)t * G + g) * N;"),
+    # reverse stream not reversed
+    "no_reverse": ("const int t = reverse ? (t1 - 1 - step) : (t0 + step);",
+                   "const int t = t0 + step;"),
+    # output read before the state update (y_t from h_{t-1})
+    "stale_output": ("                hp[n] = decay * hp[n] + dtt * Bt[n] * xt[p];\n                acc += Ct[n] * hp[n];",
+                     "                acc += Ct[n] * hp[n];\n                hp[n] = decay * hp[n] + dtt * Bt[n] * xt[p];"),
+    # wrong head -> group map
+    "group_map": ("const int g = h / (H / G);", "const int g = h % G;"),
+    # state layout [n][p] instead of [p][n]
+    "state_layout": ("hp[n] = decay * hp[n] + dtt * Bt[n] * xt[p];\n                acc += Ct[n] * hp[n];",
+                     "state[(size_t)n * P + p] = decay * state[(size_t)n * P + p] + dtt * Bt[n] * xt[p];\n                acc += Ct[n] * state[(size_t)n * P + p];"),
+    # reverse stream starts from the forward stream's final state
+    "no_reset_between": ("            if (xb) {\n                memset(state, 0, sizeof(double) * sz);",
+                         "            if (xb) {"),
+    # merge by subtraction instead of addition
+    "merge_sub": ("scan_one_head(1, t0, t1, h, H, P, N, G, xb + xo, dtb + to, Ab,",
+                  "scan_one_head(1, t0, t1, h, H, P, N, G, xb + xo, dtb + to, Ab,"),
+}
+
+
+def _mutant_src(name):
+    a, b = MUTANTS[name]
+    assert a in SRC, f"mutation site for {name} not found"
+    if name == "merge_sub":
+        # negate the reverse stream's contribution
+        return SRC.replace("            yt[p] += acc + Dh * xt[p];",
+                           "            yt[p] += (reverse ? -1.0 : 1.0) * (acc + Dh * xt[p]);")
+    return SRC.replace(a, b)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    src = tmp_path / "mutant.c"
+    text = _mutant_src(name)
+    assert text != SRC, f"mutation {name} changed nothing"
+    src.write_text(text)
+    lib_path = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                    str(src), "-o", lib_path, "-lm"], check=True)
+    lib = oracle.bind(lib_path)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin, (fn, tol) in ALL_PINS.items():
+            try:
+                err = fn(lib)
+            except Exception:
+                caught.append(pin)
+                continue
+            if not (err <= tol):
+                caught.append(pin)
+    assert caught, f"no pin catches mutant {name}"

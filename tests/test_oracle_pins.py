@@ -1,0 +1,11 @@
+"""The oracle against what the pages and the mathematics fix (CPU only)."""
+import pytest
+
+from pins import ALL_PINS
+
+
+@pytest.mark.parametrize("name", sorted(ALL_PINS))
+def test_oracle_pin(name):
+    fn, tol = ALL_PINS[name]
+    err = fn(None)
+    assert err <= tol, f"pin {name}: error {err} > {tol}"
