@@ -1,0 +1,88 @@
+"""ctypes declarations of libbimamba's C ABI (include/bimamba.h)."""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbimamba.so")
+
+F32 = 0
+BF16 = 1
+
+OK = 0
+EINVAL = -1
+EUNSUPPORTED = -2
+ENOMEM = -3
+EHIP = -4
+EWORKSPACE = -5
+
+EXPORTS = (
+    "bimamba_ssd_workspace_size", "bimamba_ssd_fwd", "bimamba_state_alloc",
+    "bimamba_state_reset", "bimamba_state_data", "bimamba_state_free",
+    "bimamba_block_step", "bimamba_seq_index", "bimamba_status_str",
+    "bimamba_last_error", "bimamba_version",
+)
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int), ("seqlen", ctypes.c_int),
+                ("nheads", ctypes.c_int), ("headdim", ctypes.c_int),
+                ("d_state", ctypes.c_int), ("ngroups", ctypes.c_int),
+                ("chunk", ctypes.c_int), ("dtype", ctypes.c_int)]
+
+
+class Dir(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
+                ("C", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load():
+    """Load libbimamba.so; raises LibraryMissing when it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+            "python bidirectional_mamba_ssm_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    sp, dp = ctypes.POINTER(Shape), ctypes.POINTER(Dir)
+    lib.bimamba_ssd_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.bimamba_ssd_fwd.argtypes = [sp, dp, dp, i32p, ctypes.c_int, vp, vp, vp,
+                                    vp, ctypes.c_size_t, vp]
+    lib.bimamba_state_alloc.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int]
+    lib.bimamba_state_reset.argtypes = [vp, i32p, ctypes.c_int, vp]
+    lib.bimamba_state_data.argtypes = [vp]
+    lib.bimamba_state_data.restype = vp
+    lib.bimamba_state_free.argtypes = [vp]
+    lib.bimamba_block_step.argtypes = [vp, sp, dp, dp, ctypes.c_int, vp, vp]
+    lib.bimamba_seq_index.argtypes = [i32p, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.bimamba_status_str.argtypes = [ctypes.c_int]
+    lib.bimamba_status_str.restype = ctypes.c_char_p
+    lib.bimamba_last_error.restype = ctypes.c_char_p
+    lib.bimamba_version.restype = ctypes.c_int
+    for name in EXPORTS:
+        getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+class BimambaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def check(rc):
+    if rc != OK:
+        lib = load()
+        raise BimambaError(rc, lib.bimamba_last_error().decode(errors="replace"))

@@ -1,0 +1,289 @@
+// C ABI of libbimamba: argument validation (host only, before any HIP call),
+// workspace layout, dispatch to the kernel launchers, state-cache objects.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/bimamba.h"
+#include "internal.hpp"
+
+using namespace bm;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(BIMAMBA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int check_shape(const bimamba_shape *s, bool block_step) {
+    if (!s) return fail(BIMAMBA_EINVAL, "shape is NULL");
+    if (s->dtype != BIMAMBA_F32 && s->dtype != BIMAMBA_BF16)
+        return fail(BIMAMBA_EINVAL, "dtype %d is not BIMAMBA_F32 or BIMAMBA_BF16", s->dtype);
+    if (s->batch < 1) return fail(BIMAMBA_EINVAL, "batch %d < 1", s->batch);
+    if (s->seqlen < 0) return fail(BIMAMBA_EINVAL, "seqlen %d < 0", s->seqlen);
+    if (s->nheads < 1 || s->headdim < 1 || s->d_state < 1 || s->ngroups < 1)
+        return fail(BIMAMBA_EINVAL, "nheads/headdim/d_state/ngroups must be >= 1");
+    if (s->nheads % s->ngroups)
+        return fail(BIMAMBA_EINVAL, "ngroups %d does not divide nheads %d", s->ngroups, s->nheads);
+    if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256)
+        return fail(BIMAMBA_EUNSUPPORTED, "chunk %d not in {64, 128, 256}", s->chunk);
+    if (!seq_supported(s->headdim, s->d_state))
+        return fail(BIMAMBA_EUNSUPPORTED,
+                    "headdim %d / d_state %d unsupported (headdim <= 128, d_state in {16,32,64,128})",
+                    s->headdim, s->d_state);
+    if (block_step && (s->seqlen < 1 || s->seqlen > 256))
+        return fail(BIMAMBA_EINVAL, "block length %d not in [1, 256]", s->seqlen);
+    // every element index must fit comfortably in 63 bits and the token count in int32
+    const long long tok = (long long)s->batch * s->seqlen;
+    if (tok > (1LL << 31) - 1)
+        return fail(BIMAMBA_EUNSUPPORTED, "batch*seqlen %lld exceeds 2^31-1", tok);
+    return BIMAMBA_OK;
+}
+
+int check_dir(const bimamba_dir *d, const char *name, bool empty) {
+    if (!d) return fail(BIMAMBA_EINVAL, "%s direction is NULL", name);
+    if (!d->A) return fail(BIMAMBA_EINVAL, "%s: A is required", name);
+    if (empty) return BIMAMBA_OK;   // no token: x, dt, B, C are never read
+    if (!d->x || !d->dt || !d->B || !d->C)
+        return fail(BIMAMBA_EINVAL, "%s: x, dt, A, B and C are required", name);
+    if (!aligned16(d->x) || !aligned16(d->B) || !aligned16(d->C))
+        return fail(BIMAMBA_EINVAL, "%s: x, B and C must be 16-byte aligned", name);
+    return BIMAMBA_OK;
+}
+
+int check_offsets(const int32_t *cu, int nseq, int total) {
+    if (nseq < 1) return fail(BIMAMBA_EINVAL, "nseq %d < 1 with cu_seqlens", nseq);
+    if (cu[0] != 0) return fail(BIMAMBA_EINVAL, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    for (int i = 0; i < nseq; ++i)
+        if (cu[i + 1] < cu[i])
+            return fail(BIMAMBA_EINVAL, "cu_seqlens decreases at %d (%d > %d)", i, cu[i], cu[i + 1]);
+    if (cu[nseq] != total)
+        return fail(BIMAMBA_EINVAL, "cu_seqlens[nseq] = %d but seqlen = %d", cu[nseq], total);
+    return BIMAMBA_OK;
+}
+
+struct Layout {
+    size_t cu_off = 0, seq_off = 0, total = 0;
+};
+
+Layout workspace_layout(const bimamba_shape *s, int nseq) {
+    Layout w;
+    size_t off = 0;
+    if (nseq > 0) {
+        w.cu_off = off;
+        off += align256((size_t)(nseq + 1) * 4);
+        w.seq_off = off;
+        off += align256((size_t)s->seqlen * 4);
+    }
+    w.total = off;
+    return w;
+}
+
+DirPtrs to_ptrs(const bimamba_dir *d) {
+    DirPtrs p;
+    p.x = d->x; p.dt = d->dt; p.B = d->B; p.C = d->C; p.A = d->A; p.D = d->D;
+    return p;
+}
+
+}  // namespace
+
+struct bimamba_state {
+    float *data;
+    int nslots, nheads, headdim, d_state;
+};
+
+extern "C" {
+
+int bimamba_version(void) { return BIMAMBA_VERSION; }
+
+const char *bimamba_last_error(void) { return g_err; }
+
+const char *bimamba_status_str(int status) {
+    switch (status) {
+        case BIMAMBA_OK: return "ok";
+        case BIMAMBA_EINVAL: return "invalid argument";
+        case BIMAMBA_EUNSUPPORTED: return "unsupported shape";
+        case BIMAMBA_ENOMEM: return "out of device memory";
+        case BIMAMBA_EHIP: return "HIP error";
+        case BIMAMBA_EWORKSPACE: return "workspace too small";
+    }
+    return "unknown status";
+}
+
+int bimamba_ssd_workspace_size(const bimamba_shape *s, int nseq, size_t *bytes) {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    if (!bytes) return fail(BIMAMBA_EINVAL, "bytes is NULL");
+    if (nseq < 0) return fail(BIMAMBA_EINVAL, "nseq %d < 0", nseq);
+    *bytes = workspace_layout(s, nseq).total;
+    return BIMAMBA_OK;
+}
+
+int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
+                    const bimamba_dir *bwd, const int32_t *cu_seqlens, int nseq,
+                    const float *init_state, float *final_state, float *y,
+                    void *workspace, size_t workspace_bytes,
+                    bimamba_stream stream) {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    const bool empty = s->seqlen == 0;
+    if ((rc = check_dir(fwd, "forward", empty))) return rc;
+    if (bwd && (rc = check_dir(bwd, "reverse", empty))) return rc;
+    if (!y && !empty) return fail(BIMAMBA_EINVAL, "y is NULL");
+    if (!aligned16(y)) return fail(BIMAMBA_EINVAL, "y must be 16-byte aligned");
+    if (cu_seqlens) {
+        if (s->batch != 1) return fail(BIMAMBA_EINVAL, "cu_seqlens requires batch == 1");
+        if ((rc = check_offsets(cu_seqlens, nseq, s->seqlen))) return rc;
+        if (init_state || final_state)
+            return fail(BIMAMBA_EUNSUPPORTED, "init_state/final_state are not available with cu_seqlens");
+    } else if (nseq != 0) {
+        return fail(BIMAMBA_EINVAL, "nseq %d given without cu_seqlens", nseq);
+    }
+    const Layout w = workspace_layout(s, cu_seqlens ? nseq : 0);
+    if (w.total > 0) {
+        if (!workspace) return fail(BIMAMBA_EWORKSPACE, "workspace of %zu bytes required", w.total);
+        if (workspace_bytes < w.total)
+            return fail(BIMAMBA_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, w.total);
+        if ((uintptr_t)workspace & 255u)
+            return fail(BIMAMBA_EINVAL, "workspace must be 256-byte aligned");
+    }
+
+    hipStream_t st = (hipStream_t)stream;
+    Problem p;
+    p.batch = s->batch; p.L = s->seqlen; p.H = s->nheads; p.P = s->headdim;
+    p.N = s->d_state; p.G = s->ngroups; p.Q = s->chunk;
+    p.bf16 = s->dtype == BIMAMBA_BF16;
+    p.has_bwd = bwd != nullptr;
+    p.dir[0] = to_ptrs(fwd);
+    p.dir[1] = bwd ? to_ptrs(bwd) : to_ptrs(fwd);
+    p.cu_dev = nullptr;
+    p.seq_idx = nullptr;
+    p.nseq = cu_seqlens ? nseq : 0;
+    p.init_state = init_state;
+    p.final_state = final_state;
+    p.y = y;
+
+    hipError_t e;
+    if (cu_seqlens) {
+        char *ws = (char *)workspace;
+        int32_t *cu_dev = (int32_t *)(ws + w.cu_off);
+        int32_t *seq = (int32_t *)(ws + w.seq_off);
+        if ((e = launch_store_offsets(cu_seqlens, nseq, cu_dev, st)) != hipSuccess)
+            return hip_fail(e, "storing sequence offsets");
+        if ((e = launch_seq_index(cu_seqlens, nseq, s->seqlen, seq, st)) != hipSuccess)
+            return hip_fail(e, "building sequence index");
+        p.cu_dev = cu_dev;
+        p.seq_idx = seq;
+    }
+    if ((e = launch_scan_seq(p, st)) != hipSuccess) return hip_fail(e, "scan launch");
+    return BIMAMBA_OK;
+}
+
+int bimamba_state_alloc(bimamba_state **out, int nslots, int nheads, int headdim,
+                        int d_state) {
+    if (!out) return fail(BIMAMBA_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (nslots < 1 || nheads < 1 || headdim < 1 || d_state < 1)
+        return fail(BIMAMBA_EINVAL, "state dimensions must be >= 1");
+    const size_t bytes = (size_t)nslots * nheads * headdim * d_state * sizeof(float);
+    float *data = nullptr;
+    hipError_t e = hipMalloc((void **)&data, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(BIMAMBA_ENOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    }
+    e = hipMemset(data, 0, bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(data);
+        return hip_fail(e, "zeroing state");
+    }
+    bimamba_state *st = new bimamba_state;
+    st->data = data;
+    st->nslots = nslots; st->nheads = nheads; st->headdim = headdim; st->d_state = d_state;
+    *out = st;
+    return BIMAMBA_OK;
+}
+
+int bimamba_state_reset(bimamba_state *st, const int32_t *slots, int n,
+                        bimamba_stream stream) {
+    if (!st) return fail(BIMAMBA_EINVAL, "state is NULL");
+    if (slots) {
+        if (n < 0) return fail(BIMAMBA_EINVAL, "n %d < 0", n);
+        for (int i = 0; i < n; ++i)
+            if (slots[i] < 0 || slots[i] >= st->nslots)
+                return fail(BIMAMBA_EINVAL, "slot %d out of range [0, %d)", slots[i], st->nslots);
+        if (n == 0) return BIMAMBA_OK;
+    }
+    const size_t slot_elems = (size_t)st->nheads * st->headdim * st->d_state;
+    hipError_t e = launch_zero_slots(st->data, slot_elems, slots, n, st->nslots,
+                                     (hipStream_t)stream);
+    return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "state reset");
+}
+
+float *bimamba_state_data(bimamba_state *st) { return st ? st->data : nullptr; }
+
+int bimamba_state_free(bimamba_state *st) {
+    if (!st) return BIMAMBA_OK;
+    hipError_t e = hipFree(st->data);
+    delete st;
+    return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "hipFree");
+}
+
+int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
+                       const bimamba_dir *fwd, const bimamba_dir *bwd, int commit,
+                       float *y, bimamba_stream stream) {
+    if (!st) return fail(BIMAMBA_EINVAL, "state is NULL");
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if ((rc = check_dir(fwd, "forward", false))) return rc;
+    if ((rc = check_dir(bwd, "reverse", false))) return rc;
+    if (!y) return fail(BIMAMBA_EINVAL, "y is NULL");
+    if (!aligned16(y)) return fail(BIMAMBA_EINVAL, "y must be 16-byte aligned");
+    if (s->batch > st->nslots)
+        return fail(BIMAMBA_EINVAL, "batch %d exceeds the state's %d slots", s->batch, st->nslots);
+    if (s->nheads != st->nheads || s->headdim != st->headdim || s->d_state != st->d_state)
+        return fail(BIMAMBA_EINVAL, "shape (H=%d, P=%d, N=%d) does not match the state (%d, %d, %d)",
+                    s->nheads, s->headdim, s->d_state, st->nheads, st->headdim, st->d_state);
+    Problem p;
+    p.batch = s->batch; p.L = s->seqlen; p.H = s->nheads; p.P = s->headdim;
+    p.N = s->d_state; p.G = s->ngroups; p.Q = s->chunk;
+    p.bf16 = s->dtype == BIMAMBA_BF16;
+    p.has_bwd = true;
+    p.dir[0] = to_ptrs(fwd);
+    p.dir[1] = to_ptrs(bwd);
+    p.cu_dev = nullptr; p.seq_idx = nullptr; p.nseq = 0;
+    p.init_state = st->data;
+    p.final_state = commit ? st->data : nullptr;
+    p.y = y;
+    hipError_t e = launch_scan_seq(p, (hipStream_t)stream);
+    return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "block step launch");
+}
+
+int bimamba_seq_index(const int32_t *cu_seqlens, int nseq, int total, int32_t *seq_idx,
+                      bimamba_stream stream) {
+    if (!cu_seqlens || !seq_idx) return fail(BIMAMBA_EINVAL, "cu_seqlens and seq_idx are required");
+    if (total < 0) return fail(BIMAMBA_EINVAL, "total %d < 0", total);
+    int rc = check_offsets(cu_seqlens, nseq, total);
+    if (rc) return rc;
+    hipError_t e = launch_seq_index(cu_seqlens, nseq, total, seq_idx, (hipStream_t)stream);
+    return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "sequence index launch");
+}
+
+}  // extern "C"

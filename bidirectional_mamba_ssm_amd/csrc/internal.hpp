@@ -1,0 +1,40 @@
+// Host-side interfaces between the C ABI (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bm {
+
+struct DirPtrs {
+    const void *x, *dt, *B, *C;
+    const float *A, *D;
+};
+
+// Problem as the launchers see it (already validated).
+struct Problem {
+    int batch, L, H, P, N, G, Q;
+    bool bf16;
+    bool has_bwd;
+    DirPtrs dir[2];            // [0] forward, [1] reverse
+    const int32_t *cu_dev;     // packed offsets on device, or nullptr
+    const int32_t *seq_idx;    // per-token packed sequence index, or nullptr
+    int nseq;                  // packed sequences (0 when not packed)
+    const float *init_state;   // [units][H][P][N] or nullptr
+    float *final_state;        // [units][H][P][N] or nullptr
+    float *y;
+};
+
+// plan.hip
+hipError_t launch_store_offsets(const int32_t *cu_host, int nseq, int32_t *cu_dev,
+                                hipStream_t s);
+hipError_t launch_seq_index(const int32_t *cu_host, int nseq, int total,
+                            int32_t *seq_idx, hipStream_t s);
+hipError_t launch_zero_slots(float *data, size_t slot_elems, const int32_t *slots,
+                             int n, int nslots, hipStream_t s);
+
+// ssd_seq.hip: token-sequential scan, any (P <= 128, N in {16,32,64,128})
+bool seq_supported(int P, int N);
+hipError_t launch_scan_seq(const Problem &p, hipStream_t s);
+
+}  // namespace bm

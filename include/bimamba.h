@@ -1,0 +1,163 @@
+/*
+ * bimamba: bidirectional Mamba-2 selective state-space (SSD) mixer for
+ * AMD Instinct MI355X (gfx950), plain C ABI.
+ *
+ * The operator (per head h, group g = h / (nheads / ngroups)):
+ *
+ *   forward  h_t = exp(dt_t*A_h) h_{t-1} + dt_t B_t x_t^T,  y_t = C_t^T h_t + D_h x_t
+ *   reverse  the same recurrence over the time-reversed sequence with its own
+ *            parameters (flip / scan / flip-back, DiffuMamba blog, "network
+ *            architecture"), evaluated here by index arithmetic, never a copy
+ *   output   y = y_forward + y_reverse (streams merged by addition,
+ *            gist.science/ja DiffuMamba summary, Sec. 2 "proposed method")
+ *
+ * The recurrence is Mamba-2's selective SSM, which the DiffuMamba pages name
+ * as the mixer ("Fixed state, long reach: constant-size caches in large-scale
+ * block diffusion", Sec. 1: a linear-time recurrence whose hidden state is a
+ * fixed-size summary of the history).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers, caller-owned; the library never
+ *    keeps them past the call. Layouts are dense row-major as stated below.
+ *  - Every argument is validated on the host BEFORE any HIP call. On error the
+ *    function returns a negative bimamba_status, records a message readable
+ *    through bimamba_last_error() (per thread) and launches nothing.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream). Nothing synchronizes. A failed launch returns BIMAMBA_EHIP.
+ *  - Results are deterministic: the same inputs give the same bits.
+ *  - x, B, C and y must be 16-byte aligned.
+ */
+#ifndef BIMAMBA_H
+#define BIMAMBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BIMAMBA_VERSION 1
+
+typedef enum {
+    BIMAMBA_F32 = 0,   /* x, dt, B, C are float                        */
+    BIMAMBA_BF16 = 1   /* x, dt, B, C are bfloat16 (raw 16-bit words)  */
+} bimamba_dtype;
+
+typedef enum {
+    BIMAMBA_OK = 0,
+    BIMAMBA_EINVAL = -1,        /* malformed argument                        */
+    BIMAMBA_EUNSUPPORTED = -2,  /* well-formed but not built for this shape  */
+    BIMAMBA_ENOMEM = -3,        /* device allocation failed (state objects)  */
+    BIMAMBA_EHIP = -4,          /* a HIP call or kernel launch failed         */
+    BIMAMBA_EWORKSPACE = -5     /* workspace missing or too small             */
+} bimamba_status;
+
+/* Problem shape. `chunk` is the block length Q of the SSD block
+ * decomposition: tokens inside one chunk interact through the masked
+ * quadratic form, chunks interact only through the carried state. It changes
+ * rounding, not the mathematical result. */
+typedef struct {
+    int batch;      /* rows; 1 when sequences are packed                    */
+    int seqlen;     /* tokens per row (packed: total tokens)                */
+    int nheads;     /* H                                                    */
+    int headdim;    /* P                                                    */
+    int d_state;    /* N                                                    */
+    int ngroups;    /* G, divides H; head h reads B/C group h/(H/G)          */
+    int chunk;      /* Q: 64, 128 or 256                                    */
+    int dtype;      /* bimamba_dtype of x, dt, B, C                          */
+} bimamba_shape;
+
+/* One direction's inputs, all read-only device pointers. The reverse
+ * direction is given in the SAME (forward) time order; the library walks it
+ * backwards. Directions may alias any pointer. */
+typedef struct {
+    const void  *x;   /* [batch][seqlen][nheads][headdim]   dtype               */
+    const void  *dt;  /* [batch][seqlen][nheads]            dtype, > 0, used as
+                         given (already softplus'd)                            */
+    const float *A;   /* [nheads] float, the per-head decay rate (<= 0)         */
+    const void  *B;   /* [batch][seqlen][ngroups][d_state]  dtype               */
+    const void  *C;   /* [batch][seqlen][ngroups][d_state]  dtype               */
+    const float *D;   /* [nheads] float skip weights; NULL means D = 0          */
+} bimamba_dir;
+
+/* Opaque per-sequence forward-state cache (the block cache of cached block
+ * diffusion, "Fixed state, long reach", Sec. 1). Device memory owned by the
+ * library: float [nslots][nheads][headdim][d_state], zero after alloc. */
+typedef struct bimamba_state bimamba_state;
+
+typedef void *bimamba_stream;   /* hipStream_t */
+
+/* Bytes of device workspace bimamba_ssd_fwd needs for this shape and number
+ * of packed sequences (nseq = 0 when not packed). Writes *bytes and returns
+ * BIMAMBA_OK, or an error for a shape bimamba_ssd_fwd would reject. */
+int bimamba_ssd_workspace_size(const bimamba_shape *s, int nseq, size_t *bytes);
+
+/* Bidirectional SSD over whole sequences (prefill / full-sequence denoising).
+ *
+ *  fwd            forward-direction inputs (required).
+ *  bwd            reverse-direction inputs; NULL computes the forward stream
+ *                 only.
+ *  cu_seqlens     HOST int32[nseq+1] offsets of sequences packed in one row
+ *                 (batch must be 1), or NULL. Non-decreasing, cu[0] = 0,
+ *                 cu[nseq] = seqlen; empty sequences are allowed. Each
+ *                 sequence starts from a zero state in both directions.
+ *  init_state     float [batch][nheads][headdim][d_state], the forward state
+ *                 before token 0 of each row, or NULL (zeros). Not with
+ *                 cu_seqlens.
+ *  final_state    float [batch][nheads][headdim][d_state] receiving the
+ *                 forward state after each row's last token, or NULL. Not with
+ *                 cu_seqlens. May equal init_state (updated in place).
+ *  y              float [batch][seqlen][nheads][headdim], fully overwritten.
+ *  workspace      device scratch of at least bimamba_ssd_workspace_size()
+ *                 bytes, 256-byte aligned; may be NULL when that size is 0.
+ *                 Its contents are dead after the stream reaches the end of
+ *                 this call's work.
+ */
+int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
+                    const bimamba_dir *bwd, const int32_t *cu_seqlens, int nseq,
+                    const float *init_state, float *final_state, float *y,
+                    void *workspace, size_t workspace_bytes,
+                    bimamba_stream stream);
+
+/* State cache objects. alloc allocates and zeroes (synchronously) nslots
+ * forward states; reset zeroes the listed slots (HOST int32 slot indices,
+ * NULL = all) asynchronously on `stream`; data returns the device pointer
+ * (layout above) for saving and loading; free releases it (NULL is a no-op). */
+int bimamba_state_alloc(bimamba_state **out, int nslots, int nheads,
+                        int headdim, int d_state);
+int bimamba_state_reset(bimamba_state *st, const int32_t *slots, int n,
+                        bimamba_stream stream);
+float *bimamba_state_data(bimamba_state *st);
+int bimamba_state_free(bimamba_state *st);
+
+/* One cached block-diffusion denoising step ("Fixed state, long reach",
+ * Sec. 1: the forward SSM state of the finalized prefix is the cache, and the
+ * reverse scan is restricted to the active block). For every slot b in
+ * [0, s->batch):
+ *   y[b] = forward scan of the active block resumed from state[b]
+ *        + reverse scan of the block alone (zero state at the block end).
+ * s->seqlen is the block length (1..256), s->batch the number of slots used
+ * (<= the object's nslots), inputs are [batch][seqlen]... as in
+ * bimamba_ssd_fwd. With commit != 0 the block is finalized: state[b] becomes
+ * the forward state after the block's last token; otherwise the cache is
+ * only read. y is float [batch][seqlen][nheads][headdim]. */
+int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
+                       const bimamba_dir *fwd, const bimamba_dir *bwd,
+                       int commit, float *y, bimamba_stream stream);
+
+/* Writes int32 seq_idx[total] (DEVICE), the packed-sequence index of every
+ * token derived from HOST cu_seqlens[nseq+1], with the same device code the
+ * scan kernels use. Exposed so the index arithmetic can be checked bit for
+ * bit. */
+int bimamba_seq_index(const int32_t *cu_seqlens, int nseq, int total,
+                      int32_t *seq_idx, bimamba_stream stream);
+
+const char *bimamba_status_str(int status);
+const char *bimamba_last_error(void);
+int bimamba_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BIMAMBA_H */

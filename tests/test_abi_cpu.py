@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects malformed arguments on the host before any HIP
+call (so no error path launches anything)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bidirectional_mamba_ssm_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        from bidirectional_mamba_ssm_amd import build
+        build.build()
+    return _abi.load()
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "bimamba.h")).read()
+    return sorted(set(re.findall(r"\b(bimamba_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_symbols()
+    assert declared, "no declarations found"
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in bimamba.h but not exported"
+    assert set(declared) == set(_abi.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bimamba_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.bimamba_status_str(code)
+    assert lib.bimamba_status_str(99) == b"unknown status"
+
+
+def shape(**kw):
+    d = dict(batch=1, seqlen=256, nheads=4, headdim=16, d_state=16, ngroups=1,
+             chunk=64, dtype=_abi.F32)
+    d.update(kw)
+    return _abi.Shape(**d)
+
+
+FAKE = 0x10000  # 16-aligned, never dereferenced: every call below fails validation
+
+
+def fake_dir(**kw):
+    d = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None)
+    d.update(kw)
+    return _abi.Dir(**d)
+
+
+def call_fwd(lib, s, f, b=None, cu=None, nseq=0, init=None, final=None, y=FAKE,
+             ws=None, wsb=0):
+    arr = None
+    if cu is not None:
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+    return lib.bimamba_ssd_fwd(ctypes.byref(s) if s is not None else None,
+                               ctypes.byref(f) if f is not None else None,
+                               ctypes.byref(b) if b is not None else None,
+                               arr, nseq, init, final, y, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _abi.EINVAL),
+    (dict(batch=0), _abi.EINVAL),
+    (dict(seqlen=-1), _abi.EINVAL),
+    (dict(nheads=0), _abi.EINVAL),
+    (dict(nheads=4, ngroups=3), _abi.EINVAL),
+    (dict(chunk=32), _abi.EUNSUPPORTED),
+    (dict(chunk=0), _abi.EUNSUPPORTED),
+    (dict(d_state=24), _abi.EUNSUPPORTED),
+    (dict(headdim=256), _abi.EUNSUPPORTED),
+    (dict(batch=1 << 16, seqlen=1 << 16), _abi.EUNSUPPORTED),
+])
+def test_shape_rejected(lib, kw, code):
+    assert call_fwd(lib, shape(**kw), fake_dir()) == code
+    assert lib.bimamba_last_error()
+
+
+def test_null_arguments(lib):
+    assert call_fwd(lib, None, fake_dir()) == _abi.EINVAL
+    assert call_fwd(lib, shape(), None) == _abi.EINVAL
+    assert call_fwd(lib, shape(), fake_dir(x=None)) == _abi.EINVAL
+    assert call_fwd(lib, shape(), fake_dir(A=None)) == _abi.EINVAL
+    assert call_fwd(lib, shape(), fake_dir(), y=None) == _abi.EINVAL
+    assert call_fwd(lib, shape(), fake_dir(), b=fake_dir(C=None)) == _abi.EINVAL
+
+
+def test_misaligned(lib):
+    assert call_fwd(lib, shape(), fake_dir(x=FAKE + 2)) == _abi.EINVAL
+    assert call_fwd(lib, shape(), fake_dir(), y=FAKE + 4) == _abi.EINVAL
+
+
+def test_bad_offsets(lib):
+    s = shape(seqlen=10)
+    assert call_fwd(lib, s, fake_dir(), cu=[0, 4, 3, 10], nseq=3) == _abi.EINVAL  # decreasing
+    assert call_fwd(lib, s, fake_dir(), cu=[1, 4, 10], nseq=2) == _abi.EINVAL     # cu[0] != 0
+    assert call_fwd(lib, s, fake_dir(), cu=[0, 4, 9], nseq=2) == _abi.EINVAL      # wrong total
+    assert call_fwd(lib, shape(seqlen=10, batch=2), fake_dir(), cu=[0, 10], nseq=1) == _abi.EINVAL
+    assert call_fwd(lib, s, fake_dir(), cu=None, nseq=2) == _abi.EINVAL           # nseq w/o offsets
+    assert call_fwd(lib, s, fake_dir(), cu=[0, 10], nseq=1, init=FAKE) == _abi.EUNSUPPORTED
+
+
+def test_workspace_checks(lib):
+    s = shape(seqlen=10)
+    n = ctypes.c_size_t(0)
+    assert lib.bimamba_ssd_workspace_size(ctypes.byref(s), 2, ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert call_fwd(lib, s, fake_dir(), cu=[0, 4, 10], nseq=2, ws=None) == _abi.EWORKSPACE
+    assert call_fwd(lib, s, fake_dir(), cu=[0, 4, 10], nseq=2, ws=FAKE * 256,
+                    wsb=n.value - 1) == _abi.EWORKSPACE
+    assert call_fwd(lib, s, fake_dir(), cu=[0, 4, 10], nseq=2, ws=FAKE * 256 + 16,
+                    wsb=n.value) == _abi.EINVAL
+    assert lib.bimamba_ssd_workspace_size(ctypes.byref(shape(chunk=48)), 0,
+                                          ctypes.byref(n)) == _abi.EUNSUPPORTED
+
+
+def test_state_and_block_step_validation(lib):
+    assert lib.bimamba_state_alloc(None, 1, 1, 1, 1) == _abi.EINVAL
+    h = ctypes.c_void_p()
+    assert lib.bimamba_state_alloc(ctypes.byref(h), 0, 4, 16, 16) == _abi.EINVAL
+    assert lib.bimamba_state_reset(None, None, 0, None) == _abi.EINVAL
+    assert lib.bimamba_state_data(None) is None
+    assert lib.bimamba_state_free(None) == 0
+    s = shape(seqlen=64)
+    assert lib.bimamba_block_step(None, ctypes.byref(s), ctypes.byref(fake_dir()),
+                                  ctypes.byref(fake_dir()), 0, FAKE, None) == _abi.EINVAL
+
+
+def test_seq_index_validation(lib):
+    arr = (ctypes.c_int32 * 3)(0, 5, 4)
+    assert lib.bimamba_seq_index(arr, 2, 4, FAKE, None) == _abi.EINVAL
+    assert lib.bimamba_seq_index(None, 2, 4, FAKE, None) == _abi.EINVAL

@@ -1,0 +1,171 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs, element by element."""
+import numpy as np
+import pytest
+import torch
+
+import bidirectional_mamba_ssm_amd as bm
+import oracle
+import synth
+from metrics import within
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _zero_D(d):
+    if d is None:
+        return None
+    d = dict(d)
+    d["D"] = torch.zeros_like(d["D"])
+    return d
+
+
+def _run(f, b, chunk, cu=None, init=None, want_final=False):
+    final = None
+    if want_final:
+        batch, _, H, P = f["x"].shape
+        N = f["B"].shape[3]
+        final = torch.full((batch, H, P, N), float("nan"), device=DEV)
+    y = bm.ssd_fwd(f, b, chunk=chunk, cu_seqlens=cu, init_state=init, final_state=final)
+    torch.cuda.synchronize()
+    return y.double().cpu().numpy(), (final.double().cpu().numpy() if want_final else None)
+
+
+CASES = [
+    # name, batch, L, H, P, N, G, dtype, chunk, seed
+    ("tiny_f32", 1, 256, 4, 16, 16, 1, "f32", 64, 0),
+    ("f32_ragged_groups", 2, 203, 4, 16, 32, 2, "f32", 64, 11),
+    ("f32_p64_n64", 1, 130, 2, 64, 64, 1, "f32", 128, 12),
+    ("bf16_layer_slice", 2, 300, 4, 64, 128, 1, "bf16", 256, 13),
+    ("bf16_small_state", 1, 257, 4, 16, 16, 1, "bf16", 64, 14),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("zero_D", [False, True], ids=["D", "D0"])
+@pytest.mark.parametrize("bidir", [True, False], ids=["bi", "fwd"])
+def test_ssd_parity(case, zero_D, bidir):
+    name, batch, L, H, P, N, G, dtype, chunk, seed = case
+    print(f"case {name} zero_D={zero_D} bidir={bidir}", flush=True)
+    f, b = synth.make_inputs(batch, L, H, P, N, G, dtype, seed, device=DEV)
+    if zero_D:
+        f, b = _zero_D(f), _zero_D(b)
+    if not bidir:
+        b = None
+    got, _ = _run(f, b, chunk)
+    ref = oracle.bissd(f, b)
+    err, ok = within(got, ref, dtype)
+    assert ok, f"{name}: error {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_init_and_final_state(dtype):
+    batch, L, H, P, N = 2, 150, 4, 16 if dtype == "f32" else 64, 16 if dtype == "f32" else 128
+    f, b = synth.make_inputs(batch, L, H, P, N, 1, dtype, 21, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(22)
+    init = torch.randn(batch, H, P, N, generator=g, device=DEV) * 0.5
+    got, fs = _run(f, b, 64, init=init, want_final=True)
+    ref, fs_ref = oracle.bissd(f, b, init_state=init, want_final_state=True)
+    err, ok = within(got, ref, dtype)
+    assert ok, f"y error {err:.3e}"
+    err, ok = within(fs, fs_ref, dtype)
+    assert ok, f"final state error {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_packed_sequences(dtype):
+    lens = [37, 0, 100, 1, 70, 64]
+    cu = synth.cu_seqlens_of(lens)
+    H, P, N = (4, 16, 16) if dtype == "f32" else (4, 64, 128)
+    f, b = synth.make_inputs(1, cu[-1], H, P, N, 1, dtype, 31, device=DEV)
+    got, _ = _run(f, b, 64, cu=cu)
+    ref = oracle.bissd(f, b, cu_seqlens=cu)
+    err, ok = within(got, ref, dtype)
+    assert ok, f"packed error {err:.3e}"
+
+
+def test_empty_sequence_batch():
+    f, b = synth.make_inputs(2, 0, 4, 16, 16, 1, "f32", 41, device=DEV)
+    init = torch.randn(2, 4, 16, 16, device=DEV)
+    final = torch.full_like(init, float("nan"))
+    y = bm.ssd_fwd(f, b, chunk=64, init_state=init, final_state=final)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    assert torch.equal(final, init)
+
+
+def test_seq_index_bit_exact():
+    lens = [5, 0, 300, 1, 0, 0, 700, 2]
+    cu = synth.cu_seqlens_of(lens)
+    got = bm.seq_index(cu).cpu().numpy()
+    ref = np.concatenate([np.full(n, i, dtype=np.int32) for i, n in enumerate(lens)])
+    assert got.dtype == np.int32 and np.array_equal(got, ref)
+    # more sequences than one launch covers
+    lens = [(i * 7) % 5 for i in range(700)]
+    cu = synth.cu_seqlens_of(lens)
+    got = bm.seq_index(cu).cpu().numpy()
+    ref = np.concatenate([np.full(n, i, dtype=np.int32) for i, n in enumerate(lens)])
+    assert np.array_equal(got, ref)
+
+
+def test_deterministic():
+    f, b = synth.make_inputs(2, 300, 4, 64, 128, 1, "bf16", 51, device=DEV)
+    y1 = bm.ssd_fwd(f, b, chunk=256).clone()
+    y2 = bm.ssd_fwd(f, b, chunk=256)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_step_matches_oracle(dtype):
+    nslots, H, P, N, Lb = 3, 4, (16 if dtype == "f32" else 64), (16 if dtype == "f32" else 128), 64
+    st = bm.State(nslots, H, P, N)
+    prefix_f, _ = synth.make_inputs(nslots, 200, H, P, N, 1, dtype, 61, device=DEV,
+                                    bidirectional=False)
+    bm.ssd_fwd(prefix_f, None, chunk=64, final_state=st.tensor())
+    f, b = synth.make_inputs(nslots, Lb, H, P, N, 1, dtype, 62, device=DEV)
+    state0 = st.tensor().clone()
+    y = bm.block_step(st, f, b, commit=False)
+    torch.cuda.synchronize()
+    assert torch.equal(st.tensor(), state0), "non-committing step changed the cache"
+    ref, _ = oracle.block_step(state0, f, b, commit=False)
+    err, ok = within(y.double().cpu().numpy(), ref, dtype)
+    assert ok, f"block step y error {err:.3e}"
+    y2 = bm.block_step(st, f, b, commit=True)
+    torch.cuda.synchronize()
+    ref2, new_state = oracle.block_step(state0, f, b, commit=True)
+    err, ok = within(y2.double().cpu().numpy(), ref2, dtype)
+    assert ok, f"committing step y error {err:.3e}"
+    err, ok = within(st.tensor().double().cpu().numpy(), new_state, dtype)
+    assert ok, f"committed state error {err:.3e}"
+    st.reset([1])
+    torch.cuda.synchronize()
+    s = st.tensor()
+    assert torch.count_nonzero(s[1]) == 0
+    assert torch.count_nonzero(s[0]) > 0 and torch.count_nonzero(s[2]) > 0
+    st.free()
+
+
+def test_block_decode_equals_full_scan():
+    """Blocks decoded one after another with commit reproduce the full
+    forward scan ("Fixed state, long reach", Sec. 1: the cache is exact)."""
+    H, P, N, Lb, nb = 4, 64, 128, 64, 4
+    f, b = synth.make_inputs(1, Lb * nb, H, P, N, 1, "bf16", 71, device=DEV)
+    silent = {k: (torch.zeros_like(v) if k in ("x", "D") else v) for k, v in b.items()}
+    full = bm.ssd_fwd(f, None, chunk=64).double().cpu().numpy()
+    st = bm.State(1, H, P, N)
+    outs = []
+    for k in range(nb):
+        sl = slice(k * Lb, (k + 1) * Lb)
+        fk = {kk: (v[:, sl].contiguous() if kk in ("x", "dt", "B", "C") else v) for kk, v in f.items()}
+        sk = {kk: (v[:, sl].contiguous() if kk in ("x", "dt", "B", "C") else v) for kk, v in silent.items()}
+        outs.append(bm.block_step(st, fk, sk, commit=True).double().cpu().numpy())
+    got = np.concatenate(outs, axis=1)
+    ref = oracle.bissd(f, None)
+    err, ok = within(got, ref, "bf16")
+    assert ok, f"block-by-block vs oracle {err:.3e}"
+    err, ok = within(got, full, "bf16")
+    assert ok, f"block-by-block vs full GPU scan {err:.3e}"
+    st.free()
