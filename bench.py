@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the bidirectional Mamba-2 SSD mixer on one MI355X.
+
+A step is one bidirectional bimamba_ssd_fwd call (every kernel of the scan:
+planning, chunk states, state passing, outputs) over one batch of synthetic
+input already resident in HBM. The headline workload is one mixer layer of a
+DiffuMamba-1.3B-shaped model at its training length: batch 8 x 1024 tokens,
+64 heads x headdim 64 (d_inner 4096), d_state 128, chunk 256, bf16 inputs,
+fp32 accumulation and output.
+
+Prints ONE JSON line. Besides the contract fields it carries:
+  roofline      HBM roofline of the dominant kernel (algorithmic bytes per
+                launch / its average HIP-event duration over the timed steps)
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded
+                sample of the same inputs, with its parity against the GPU
+  extra         the long-sequence (32k, 128k), packed-varlen and cached
+                block-step workloads, each with its own roofline fraction
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+
+
+def bytes_per_token(H, P, N, G, elem):
+    """Algorithmic bytes per token: every input of both directions read once
+    (x, dt, B, C), y (fp32) written once."""
+    per_dir = H * P * elem + H * elem + 2 * G * N * elem
+    return 2 * per_dir + H * P * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--prefix", type=int, default=262144,
+                    help="prefix length of the block-step state")
+    return ap.parse_args()
+
+
+def time_steps(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def profile_steps(bm, fn, steps, torch):
+    torch.cuda.synchronize()
+    with bm.profile() as prof:
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
+    ker = {k: (c, t) for k, (c, t) in prof.kernels.items()}
+    dom = max(ker, key=lambda k: ker[k][1])
+    return ker, dom
+
+
+def roofline_for(ker, dom, bytes_per_launch):
+    launches, total_ms = ker[dom]
+    avg_s = total_ms / launches / 1e3
+    achieved = bytes_per_launch / avg_s / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None, "kernel": dom, "avg_us": round(avg_s * 1e6, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bidirectional_mamba_ssm_amd as bm
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS["layer_1p3b_train"]
+    f, b = synth.make_workload(w, device=dev)
+    torch.cuda.synchronize()
+    y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+    shape = bm.make_shape(f["x"], f["B"], w.chunk)
+    ws_bytes = bm.workspace_size(shape, 0)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        bm.ssd_fwd(f, b, chunk=w.chunk, y=y, workspace=ws)
+
+    ms, wall = time_steps(step, args.steps, args.warmup, torch)
+    tokens = w.batch * w.seqlen
+    bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
+    ker, dom = profile_steps(bm, step, args.steps, torch)
+    # the dominant kernel reads every input of the step once and writes y
+    roof = roofline_for(ker, dom, bpt * tokens)
+
+    out = {
+        "metric": "BiMamba-2 SSD tokens/s (one bidirectional mixer layer)",
+        "value": round(tokens / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": w.batch, "seq_len": w.seqlen,
+                   "nheads": w.nheads, "headdim": w.headdim, "d_state": w.d_state,
+                   "ngroups": w.ngroups, "chunk": w.chunk, "bidirectional": True,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "algorithmic_bytes_per_token": bpt,
+        "kernels_ms_per_step": {k: round(t / args.steps, 4) for k, (c, t) in ker.items()},
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_extra:
+        out["extra"] = extras(args, bm, synth, torch, dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(f, b, y, w, torch, np)
+    print(json.dumps(out), flush=True)
+
+
+def extras(args, bm, synth, torch, dev):
+    res = {}
+    steps = max(3, args.steps // 4)
+    for name in ("long_32k", "long_128k"):
+        w = synth.WORKLOADS[name]
+        f, b = synth.make_workload(w, device=dev)
+        y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+        shape = bm.make_shape(f["x"], f["B"], w.chunk)
+        ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=dev)
+        fn = lambda: bm.ssd_fwd(f, b, chunk=w.chunk, y=y, workspace=ws)  # noqa: E731
+        ms, _ = time_steps(fn, steps, 2, torch)
+        tok = w.batch * w.seqlen
+        bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
+        ker, dom = profile_steps(bm, fn, steps, torch)
+        res[name] = {"tokens_per_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+                     "hbm_roofline_frac_step": round(bpt * tok / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "roofline": roofline_for(ker, dom, bpt * tok)}
+        del f, b, y, ws
+        torch.cuda.empty_cache()
+
+    # packed variable-length batch with per-sequence resets
+    w = synth.packed_workload()
+    f, b = synth.make_inputs(1, w.seqlen, w.nheads, w.headdim, w.d_state, w.ngroups,
+                             w.dtype, w.seed, device=dev)
+    cu = synth.cu_seqlens_of(w.seqlens)
+    y = torch.empty(1, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+    shape = bm.make_shape(f["x"], f["B"], w.chunk)
+    ws = torch.empty(max(bm.workspace_size(shape, len(cu) - 1), 256), dtype=torch.uint8, device=dev)
+    fn = lambda: bm.ssd_fwd(f, b, chunk=w.chunk, cu_seqlens=cu, y=y, workspace=ws)  # noqa: E731
+    ms, _ = time_steps(fn, steps, 2, torch)
+    bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
+    res["packed_varlen"] = {"tokens_per_s": round(w.seqlen / (ms / 1e3), 1),
+                            "ms_per_step": round(ms, 4), "tokens": w.seqlen, "nseq": len(cu) - 1,
+                            "hbm_roofline_frac_step": round(bpt * w.seqlen / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del f, b, y, ws
+    torch.cuda.empty_cache()
+
+    res["block_step"] = block_step_bench(args, bm, synth, torch, dev, steps)
+    return res
+
+
+def block_step_bench(args, bm, synth, torch, dev, steps):
+    c = synth.BLOCK_STEP
+    H, P, N, G, Lb = c["nheads"], c["headdim"], c["d_state"], c["ngroups"], c["block"]
+    out = {}
+    seg = 8192
+    for nseq, prefix in ((1, args.prefix), (16, args.prefix), (1, 4096)):
+        st = bm.State(nseq, H, P, N)
+        done, s = 0, 0
+        # the forward state after the prefix, built in segments chained through the cache
+        while done < prefix:
+            n = min(seg, prefix - done)
+            pf, _ = synth.make_inputs(nseq, n, H, P, N, G, "bf16", c["seed"] * 1000 + s,
+                                      device=dev, bidirectional=False)
+            bm.ssd_fwd(pf, None, chunk=256, init_state=st.tensor(), final_state=st.tensor())
+            done += n
+            s += 1
+            del pf
+        torch.cuda.synchronize()
+        f, b = synth.make_inputs(nseq, Lb, H, P, N, G, "bf16", c["seed"], device=dev)
+        y = torch.empty(nseq, Lb, H, P, dtype=torch.float32, device=dev)
+        fn = lambda: bm.block_step(st, f, b, commit=False, chunk=64, y=y)  # noqa: E731
+        ms, _ = time_steps(fn, max(steps, 10), 3, torch)
+        per_seq = H * P * N * 4 + bytes_per_token(H, P, N, G, 2) * Lb
+        ker, dom = profile_steps(bm, fn, max(steps, 10), torch)
+        key = f"b{nseq}_prefix{prefix}"
+        out[key] = {"ms_per_step": round(ms, 5), "bytes_per_step": per_seq * nseq,
+                    "hbm_roofline_frac_step": round(per_seq * nseq / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "roofline": roofline_for(ker, dom, per_seq * nseq)}
+        fc = lambda: bm.block_step(st, f, b, commit=True, chunk=64, y=y)  # noqa: E731
+        msc, _ = time_steps(fc, 5, 1, torch)
+        out[key]["ms_per_commit_step"] = round(msc, 5)
+        st.free()
+        del f, b, y
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(f, b, y, w, torch, np):
+    """The fp64 oracle on this host's cores, on whole rows of the same inputs
+    (as many rows as fit in about 10-20 s), plus parity of those rows."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_num_threads(cores)
+
+    def rows(lo, hi):
+        fr = {k: (v[lo:hi] if v.dim() > 1 else v) for k, v in f.items()}
+        br = {k: (v[lo:hi] if v.dim() > 1 else v) for k, v in b.items()}
+        return fr, br
+
+    # whole rows of the same inputs; the full batch is repeated until about
+    # 10 s of CPU time have been spent (rows are independent units of work)
+    fr, br = rows(0, 1)
+    t0 = time.perf_counter()
+    ref0 = oracle.bissd(fr, br)
+    t1 = time.perf_counter() - t0
+    n_rows = int(min(w.batch, max(1, math.ceil(10.0 / max(t1, 1e-3)))))
+    fr, br = rows(0, n_rows)
+    reps, total_t, ref = 0, 0.0, None
+    while reps == 0 or total_t < 10.0:
+        t0 = time.perf_counter()
+        ref = oracle.bissd(fr, br)
+        total_t += time.perf_counter() - t0
+        reps += 1
+        if reps >= 1000:
+            break
+    got = y[:n_rows].double().cpu().numpy()
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(got - ref)) / rms)
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(reps * n_rows * w.seqlen / total_t, 2), "unit": "tokens/s",
+            "cores": int(oracle.num_threads()), "kind": "oracle",
+            "sample": f"{n_rows} of {w.batch} rows x {w.seqlen} tokens of the same inputs, "
+                      f"run {reps}x, fp64 sequential recurrence, {total_t:.1f} s",
+            "cpu_model": cpu_model,
+            "parity_max_abs_err_over_rms": err, "parity_ok": err <= 1e-2}
+
+
+if __name__ == "__main__":
+    main()

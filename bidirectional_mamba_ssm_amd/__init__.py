@@ -161,3 +161,33 @@ def seq_index(cu_seqlens, device="cuda", stream=None):
     arr = (ctypes.c_int32 * len(vals))(*vals)
     _abi.check(lib().bimamba_seq_index(arr, len(vals) - 1, total, _ptr(out), _stream(stream)))
     return out[:total]
+
+
+class profile:
+    """Context manager: per-kernel launch counts and summed device time (ms)
+    of every library kernel launched from this thread inside the block,
+    measured with HIP events on each kernel's stream.
+
+        with bm.profile() as prof:
+            bm.ssd_fwd(...)
+        prof.kernels  # {name: (launches, total_ms)}
+    """
+
+    def __enter__(self):
+        _abi.check(lib().bimamba_profile_begin())
+        self.kernels = {}
+        return self
+
+    def __exit__(self, *exc):
+        cap, nl = 64, 64
+        names = ctypes.create_string_buffer(cap * nl)
+        counts = (ctypes.c_int * cap)()
+        ms = (ctypes.c_double * cap)()
+        n = lib().bimamba_profile_end(names, nl, counts, ms, cap)
+        if n < 0:
+            _abi.check(n)
+        raw = names.raw
+        for i in range(min(n, cap)):
+            name = raw[i * nl:(i + 1) * nl].split(b"\0", 1)[0].decode()
+            self.kernels[name] = (counts[i], ms[i])
+        return False

@@ -19,7 +19,8 @@ EXPORTS = (
     "bimamba_ssd_workspace_size", "bimamba_ssd_fwd", "bimamba_state_alloc",
     "bimamba_state_reset", "bimamba_state_data", "bimamba_state_free",
     "bimamba_block_step", "bimamba_seq_index", "bimamba_status_str",
-    "bimamba_last_error", "bimamba_version",
+    "bimamba_last_error", "bimamba_version", "bimamba_profile_begin",
+    "bimamba_profile_end",
 )
 
 
@@ -70,6 +71,9 @@ def load():
     lib.bimamba_status_str.restype = ctypes.c_char_p
     lib.bimamba_last_error.restype = ctypes.c_char_p
     lib.bimamba_version.restype = ctypes.c_int
+    lib.bimamba_profile_end.argtypes = [ctypes.c_char_p, ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int),
+                                        ctypes.POINTER(ctypes.c_double), ctypes.c_int]
     for name in EXPORTS:
         getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
     _LIB = lib

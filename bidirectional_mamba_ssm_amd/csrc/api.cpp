@@ -6,6 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <string>
+#include <vector>
+
 #include "../../include/bimamba.h"
 #include "internal.hpp"
 
@@ -78,8 +81,18 @@ int check_offsets(const int32_t *cu, int nseq, int total) {
     return BIMAMBA_OK;
 }
 
+// Which kernel family serves a shape: the matrix-core chunked scan where it
+// is built (bf16, headdim 64, d_state 128), the token-sequential scan
+// otherwise (every fp32 problem and the remaining shapes).
+bool use_chunked(const bimamba_shape *s) {
+    Problem p;
+    p.bf16 = s->dtype == BIMAMBA_BF16;
+    p.P = s->headdim; p.N = s->d_state; p.L = s->seqlen; p.Q = s->chunk;
+    return chunked_supported(p);
+}
+
 struct Layout {
-    size_t cu_off = 0, seq_off = 0, total = 0;
+    size_t cu_off = 0, seq_off = 0, scan_off = 0, total = 0;
 };
 
 Layout workspace_layout(const bimamba_shape *s, int nseq) {
@@ -91,6 +104,9 @@ Layout workspace_layout(const bimamba_shape *s, int nseq) {
         w.seq_off = off;
         off += align256((size_t)s->seqlen * 4);
     }
+    w.scan_off = off;
+    if (use_chunked(s))
+        off += chunked_workspace(s->batch, s->seqlen, s->nheads, s->ngroups, s->chunk);
     w.total = off;
     return w;
 }
@@ -101,7 +117,31 @@ DirPtrs to_ptrs(const bimamba_dir *d) {
     return p;
 }
 
+struct ProfRecord {
+    const char *name;
+    hipEvent_t start, stop;
+};
+thread_local bool g_prof_on = false;
+thread_local std::vector<ProfRecord> g_prof;
+
 }  // namespace
+
+namespace bm {
+void prof_before(const char *name, hipStream_t s) {
+    if (!g_prof_on) return;
+    ProfRecord r{name, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
+        (void)hipGetLastError();
+        return;
+    }
+    (void)hipEventRecord(r.start, s);
+    g_prof.push_back(r);
+}
+void prof_after(hipStream_t s) {
+    if (!g_prof_on || g_prof.empty()) return;
+    (void)hipEventRecord(g_prof.back().stop, s);
+}
+}  // namespace bm
 
 struct bimamba_state {
     float *data;
@@ -111,6 +151,49 @@ struct bimamba_state {
 extern "C" {
 
 int bimamba_version(void) { return BIMAMBA_VERSION; }
+
+int bimamba_profile_begin(void) {
+    for (auto &r : g_prof) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    g_prof.clear();
+    g_prof_on = true;
+    return BIMAMBA_OK;
+}
+
+int bimamba_profile_end(char *names, int name_len, int *counts, double *ms, int cap) {
+    if (!g_prof_on) return fail(BIMAMBA_EINVAL, "profiling was not begun on this thread");
+    g_prof_on = false;
+    std::vector<std::string> seen;
+    std::vector<int> cnt;
+    std::vector<double> tot;
+    int status = BIMAMBA_OK;
+    for (auto &r : g_prof) {
+        float t = 0.f;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+        if (e != hipSuccess && status == BIMAMBA_OK) status = hip_fail(e, "profile events");
+        size_t i = 0;
+        while (i < seen.size() && seen[i] != r.name) ++i;
+        if (i == seen.size()) { seen.push_back(r.name); cnt.push_back(0); tot.push_back(0.0); }
+        cnt[i] += 1;
+        tot[i] += t;
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    g_prof.clear();
+    if (status != BIMAMBA_OK) return status;
+    for (size_t i = 0; i < seen.size() && (int)i < cap; ++i) {
+        if (names && name_len > 0) {
+            strncpy(names + i * name_len, seen[i].c_str(), name_len - 1);
+            names[i * name_len + name_len - 1] = 0;
+        }
+        if (counts) counts[i] = cnt[i];
+        if (ms) ms[i] = tot[i];
+    }
+    return (int)seen.size();
+}
 
 const char *bimamba_last_error(void) { return g_err; }
 
@@ -191,7 +274,12 @@ int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
         p.cu_dev = cu_dev;
         p.seq_idx = seq;
     }
-    if ((e = launch_scan_seq(p, st)) != hipSuccess) return hip_fail(e, "scan launch");
+    if (use_chunked(s)) {
+        if ((e = launch_chunked(p, (char *)workspace + w.scan_off, st)) != hipSuccess)
+            return hip_fail(e, "chunked scan launch");
+    } else if ((e = launch_scan_seq(p, st)) != hipSuccess) {
+        return hip_fail(e, "scan launch");
+    }
     return BIMAMBA_OK;
 }
 

@@ -49,7 +49,7 @@ hipError_t launch_store_offsets(const int32_t *cu, int nseq, int32_t *cu_dev,
         int count = nseq + 1 - first;
         if (count > kOffsPerLaunch) count = kOffsPerLaunch;
         OffsetBatch b = make_batch(cu, first, count);
-        hipLaunchKernelGGL(k_store_offsets, dim3(1), dim3(kOffsPerLaunch), 0, s, b, cu_dev);
+        BM_LAUNCH("store_offsets", k_store_offsets, dim3(1), dim3(kOffsPerLaunch), 0, s, b, cu_dev);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -67,7 +67,7 @@ hipError_t launch_seq_index(const int32_t *cu, int nseq, int total,
         int ntok = cu[first + count - 1] - cu[first];
         if (ntok <= 0) continue;
         int blocks = (ntok + 255) / 256;
-        hipLaunchKernelGGL(k_seq_index, dim3(blocks), dim3(256), 0, s, b, seq_idx);
+        BM_LAUNCH("seq_index", k_seq_index, dim3(blocks), dim3(256), 0, s, b, seq_idx);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -100,16 +100,16 @@ hipError_t launch_zero_slots(float *data, size_t slot_elems, const int32_t *slot
     if (!slots) {
         SlotBatch b;
         b.count = 0;
-        hipLaunchKernelGGL(k_zero_slots, dim3(xblocks, nslots), dim3(256), 0, s, data,
-                           slot_elems, b, nslots);
+        BM_LAUNCH("zero_slots", k_zero_slots, dim3(xblocks, nslots), dim3(256), 0, s, data,
+                  slot_elems, b, nslots);
         return hipGetLastError();
     }
     for (int first = 0; first < n; first += 64) {
         SlotBatch b;
         b.count = n - first < 64 ? n - first : 64;
         for (int i = 0; i < b.count; ++i) b.slot[i] = slots[first + i];
-        hipLaunchKernelGGL(k_zero_slots, dim3(xblocks, b.count), dim3(256), 0, s, data,
-                           slot_elems, b, nslots);
+        BM_LAUNCH("zero_slots", k_zero_slots, dim3(xblocks, b.count), dim3(256), 0, s, data,
+                  slot_elems, b, nslots);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

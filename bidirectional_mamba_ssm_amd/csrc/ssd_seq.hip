@@ -118,7 +118,7 @@ bool seq_supported(int P, int N) {
 template <typename T, int N>
 static hipError_t launch_typed(const SeqArgs &a, int units, hipStream_t s) {
     int threads = ((a.P + 63) / 64) * 64;
-    hipLaunchKernelGGL((k_scan_seq<T, N>), dim3(units, a.H), dim3(threads), 0, s, a);
+    BM_LAUNCH("scan_seq", (k_scan_seq<T, N>), dim3(units, a.H), dim3(threads), 0, s, a);
     return hipGetLastError();
 }
 

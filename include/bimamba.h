@@ -153,6 +153,18 @@ int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
 int bimamba_seq_index(const int32_t *cu_seqlens, int nseq, int total,
                       int32_t *seq_idx, bimamba_stream stream);
 
+/* Per-kernel timing for benchmarks and profilers, per calling thread.
+ * Between bimamba_profile_begin() and bimamba_profile_end(), every kernel the
+ * library launches from this thread is bracketed by two hipEvents recorded on
+ * the kernel's own stream. bimamba_profile_end() waits for those events and,
+ * for up to `cap` distinct kernels in first-launch order, writes the kernel's
+ * name (NUL-terminated, at most name_len bytes each, into names + i*name_len),
+ * its launch count and its summed duration in milliseconds. It returns the
+ * number of distinct kernels seen, or a negative status. The work itself is
+ * unchanged; only event records are added between launches. */
+int bimamba_profile_begin(void);
+int bimamba_profile_end(char *names, int name_len, int *counts, double *ms, int cap);
+
 const char *bimamba_status_str(int status);
 const char *bimamba_last_error(void);
 int bimamba_version(void);

@@ -40,6 +40,10 @@ CASES = [
     ("f32_p64_n64", 1, 130, 2, 64, 64, 1, "f32", 128, 12),
     ("bf16_layer_slice", 2, 300, 4, 64, 128, 1, "bf16", 256, 13),
     ("bf16_small_state", 1, 257, 4, 16, 16, 1, "bf16", 64, 14),
+    ("bf16_q64_ragged_groups", 2, 200, 4, 64, 128, 2, "bf16", 64, 15),
+    ("bf16_q128", 1, 384, 2, 64, 128, 1, "bf16", 128, 16),
+    ("bf16_q256_ragged", 1, 777, 2, 64, 128, 1, "bf16", 256, 17),
+    ("bf16_q256_short", 3, 40, 2, 64, 128, 1, "bf16", 256, 18),
 ]
 
 
@@ -74,16 +78,32 @@ def test_init_and_final_state(dtype):
     assert ok, f"final state error {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_packed_sequences(dtype):
-    lens = [37, 0, 100, 1, 70, 64]
+@pytest.mark.parametrize("dtype,chunk,lens", [
+    ("f32", 64, [37, 0, 100, 1, 70, 64]),
+    ("bf16", 64, [37, 0, 100, 1, 70, 64]),
+    ("bf16", 256, [300, 1, 0, 512, 129, 255, 256, 2]),
+    ("bf16", 128, [1] * 9 + [500]),
+])
+def test_packed_sequences(dtype, chunk, lens):
     cu = synth.cu_seqlens_of(lens)
     H, P, N = (4, 16, 16) if dtype == "f32" else (4, 64, 128)
     f, b = synth.make_inputs(1, cu[-1], H, P, N, 1, dtype, 31, device=DEV)
-    got, _ = _run(f, b, 64, cu=cu)
-    ref = oracle.bissd(f, b, cu_seqlens=cu)
-    err, ok = within(got, ref, dtype)
-    assert ok, f"packed error {err:.3e}"
+    for zero_D in (False, True):
+        ff, bb = (_zero_D(f), _zero_D(b)) if zero_D else (f, b)
+        got, _ = _run(ff, bb, chunk, cu=cu)
+        ref = oracle.bissd(ff, bb, cu_seqlens=cu)
+        err, ok = within(got, ref, dtype)
+        assert ok, f"packed error {err:.3e} (zero_D={zero_D})"
+        # each sequence alone gives the same result
+        for i in range(len(lens)):
+            if lens[i] == 0:
+                continue
+            sl = slice(cu[i], cu[i + 1])
+            fi = {k: (v[:, sl].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in ff.items()}
+            bi = {k: (v[:, sl].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in bb.items()}
+            alone, _ = _run(fi, bi, chunk)
+            e2, ok2 = within(got[:, sl], alone, dtype)
+            assert e2 <= 2 * (1e-4 if dtype == "f32" else 1e-2), f"sequence {i}: {e2:.3e}"
 
 
 def test_empty_sequence_batch():
@@ -169,3 +189,55 @@ def test_block_decode_equals_full_scan():
     err, ok = within(got, full, "bf16")
     assert ok, f"block-by-block vs full GPU scan {err:.3e}"
     st.free()
+
+
+def _heads(d, sel):
+    """The same inputs restricted to a subset of heads (B, C are shared)."""
+    out = dict(d)
+    out["x"] = d["x"][:, :, sel].contiguous()
+    out["dt"] = d["dt"][:, :, sel].contiguous()
+    out["A"] = d["A"][sel].contiguous()
+    out["D"] = d["D"][sel].contiguous()
+    return out
+
+
+@pytest.mark.parametrize("name", ["layer_1p3b_train", "long_32k", "long_128k"])
+def test_full_size_sampled(name):
+    """Full-size workloads in the benchmark's launch configuration; the oracle
+    recomputes a sample of rows and heads completely (every position)."""
+    w = synth.WORKLOADS[name]
+    print(f"full-size {name}", flush=True)
+    f, b = synth.make_workload(w, device=DEV)
+    y = bm.ssd_fwd(f, b, chunk=w.chunk)
+    torch.cuda.synchronize()
+    rows = [0, w.batch - 1] if w.batch > 1 else [0]
+    heads = [0, 37] if w.seqlen <= 32768 else [5]
+    for r in rows:
+        for zero_D in (False, True):
+            fr = {k: (v[r:r + 1] if v.dim() > 1 else v) for k, v in f.items()}
+            br = {k: (v[r:r + 1] if v.dim() > 1 else v) for k, v in b.items()}
+            fr, br = _heads(fr, heads), _heads(br, heads)
+            got = y[r:r + 1][:, :, heads].double().cpu().numpy()
+            if zero_D:
+                fr, br = _zero_D(fr), _zero_D(br)
+                # y without the skip term: subtract D x exactly in fp64
+                fx = f["x"][r:r + 1][:, :, heads].double().cpu().numpy()
+                bx = b["x"][r:r + 1][:, :, heads].double().cpu().numpy()
+                got = (got - f["D"][heads].double().cpu().numpy()[None, None, :, None] * fx
+                       - b["D"][heads].double().cpu().numpy()[None, None, :, None] * bx)
+            ref = oracle.bissd(fr, br)
+            err, ok = within(got, ref, "bf16")
+            assert ok, f"{name} row {r} zero_D={zero_D}: {err:.3e}"
+
+
+def test_chunk_invariance():
+    """Q in {64, 128, 256} gives the same operator (up to rounding)."""
+    f, b = synth.make_inputs(2, 1000, 4, 64, 128, 1, "bf16", 81, device=DEV)
+    ys = [bm.ssd_fwd(f, b, chunk=q).double().cpu().numpy() for q in (64, 128, 256)]
+    ref = oracle.bissd(f, b)
+    for y in ys:
+        err, ok = within(y, ref, "bf16")
+        assert ok, f"{err:.3e}"
+    for y in ys[1:]:
+        err, _ = within(y, ys[0], "bf16")
+        assert err <= 1e-2, f"chunk sizes disagree: {err:.3e}"
