@@ -52,7 +52,7 @@ def make_shape(x, B, chunk, seqlen=None):
     if x.dtype not in DTYPES:
         raise TypeError(f"unsupported dtype {x.dtype}")
     return _abi.Shape(batch, L if seqlen is None else seqlen, H, P, N, G, chunk,
-                      DTYPES[x.dtype])
+                      DTYPES[x.dtype], 0)
 
 
 def workspace_size(shape, nseq=0):

@@ -28,7 +28,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int), ("seqlen", ctypes.c_int),
                 ("nheads", ctypes.c_int), ("headdim", ctypes.c_int),
                 ("d_state", ctypes.c_int), ("ngroups", ctypes.c_int),
-                ("chunk", ctypes.c_int), ("dtype", ctypes.c_int)]
+                ("chunk", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("flags", ctypes.c_int)]
 
 
 class Dir(ctypes.Structure):

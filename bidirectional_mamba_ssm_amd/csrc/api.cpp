@@ -42,6 +42,8 @@ int check_shape(const bimamba_shape *s, bool block_step) {
     if (s->seqlen < 0) return fail(BIMAMBA_EINVAL, "seqlen %d < 0", s->seqlen);
     if (s->nheads < 1 || s->headdim < 1 || s->d_state < 1 || s->ngroups < 1)
         return fail(BIMAMBA_EINVAL, "nheads/headdim/d_state/ngroups must be >= 1");
+    if (s->flags != 0)
+        return fail(BIMAMBA_EINVAL, "flags 0x%x: no flag is defined", s->flags);
     if (s->nheads % s->ngroups)
         return fail(BIMAMBA_EINVAL, "ngroups %d does not divide nheads %d", s->ngroups, s->nheads);
     if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256)

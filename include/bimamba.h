@@ -66,6 +66,7 @@ typedef struct {
     int ngroups;    /* G, divides H; head h reads B/C group h/(H/G)          */
     int chunk;      /* Q: 64, 128 or 256                                    */
     int dtype;      /* bimamba_dtype of x, dt, B, C                          */
+    int flags;      /* reserved, must be 0                                  */
 } bimamba_shape;
 
 /* One direction's inputs, all read-only device pointers. The reverse

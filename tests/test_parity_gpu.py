@@ -61,6 +61,7 @@ def test_ssd_parity(case, zero_D, bidir):
     got, _ = _run(f, b, chunk)
     ref = oracle.bissd(f, b)
     err, ok = within(got, ref, dtype)
+    print(f"  error {err:.3e}", flush=True)
     assert ok, f"{name}: error {err:.3e}"
 
 
@@ -76,6 +77,16 @@ def test_init_and_final_state(dtype):
     assert ok, f"y error {err:.3e}"
     err, ok = within(fs, fs_ref, dtype)
     assert ok, f"final state error {err:.3e}"
+    if dtype == "bf16":
+        for L2 in (1000, 5000):   # several segments: the state chain across them
+            f2, b2 = synth.make_inputs(1, L2, H, P, N, 1, dtype, 23, device=DEV)
+            init2 = init[:1].contiguous()
+            got2, fs2 = _run(f2, b2, 64, init=init2, want_final=True)
+            ref2, fs2_ref = oracle.bissd(f2, b2, init_state=init2, want_final_state=True)
+            err, ok = within(got2, ref2, dtype)
+            assert ok, f"L={L2} y error {err:.3e}"
+            err, ok = within(fs2, fs2_ref, dtype)
+            assert ok, f"L={L2} final state error {err:.3e}"
 
 
 @pytest.mark.parametrize("dtype,chunk,lens", [
@@ -93,6 +104,7 @@ def test_packed_sequences(dtype, chunk, lens):
         got, _ = _run(ff, bb, chunk, cu=cu)
         ref = oracle.bissd(ff, bb, cu_seqlens=cu)
         err, ok = within(got, ref, dtype)
+        print(f"packed zero_D={zero_D}: {err:.3e}", flush=True)
         assert ok, f"packed error {err:.3e} (zero_D={zero_D})"
         # each sequence alone gives the same result
         for i in range(len(lens)):
@@ -227,6 +239,7 @@ def test_full_size_sampled(name):
                        - b["D"][heads].double().cpu().numpy()[None, None, :, None] * bx)
             ref = oracle.bissd(fr, br)
             err, ok = within(got, ref, "bf16")
+            print(f"{name} row {r} zero_D={zero_D}: {err:.3e}", flush=True)
             assert ok, f"{name} row {r} zero_D={zero_D}: {err:.3e}"
 
 
@@ -241,3 +254,19 @@ def test_chunk_invariance():
     for y in ys[1:]:
         err, _ = within(y, ys[0], "bf16")
         assert err <= 1e-2, f"chunk sizes disagree: {err:.3e}"
+
+
+@pytest.mark.parametrize("scale", [0.0, 1e-3, 3e-2], ids=["A0", "A1e-3", "A3e-2"])
+def test_slow_decay_chains(scale):
+    """Slowly decaying heads carry state across many chunks and segments (the
+    segment carry factors are far from 0), including A = 0 where the state is
+    a plain running sum."""
+    f, b = synth.make_inputs(1, 3000, 4, 64, 128, 1, "bf16", 91, device=DEV)
+    f = dict(f, A=(f["A"] * scale).contiguous())
+    b = dict(b, A=(b["A"] * scale).contiguous())
+    for chunk in (64, 256):
+        got, _ = _run(f, b, chunk)
+        ref = oracle.bissd(f, b)
+        err, ok = within(got, ref, "bf16")
+        print(f"scale={scale} chunk={chunk}: {err:.3e}", flush=True)
+        assert ok, f"error {err:.3e}"
