@@ -362,7 +362,12 @@ int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
     p.init_state = st->data;
     p.final_state = commit ? st->data : nullptr;
     p.y = y;
-    hipError_t e = launch_scan_seq(p, (hipStream_t)stream);
+    // the block is one segment of its row: the chunked kernels need no
+    // workspace then (each workgroup reads its slice of the cache before it
+    // writes it back, so the in-place update is safe)
+    hipError_t e = chunked_supported(p) && chunked_workspace(p.batch, p.L, p.H, p.G, p.Q) == 0
+                       ? launch_chunked(p, nullptr, (hipStream_t)stream)
+                       : launch_scan_seq(p, (hipStream_t)stream);
     return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "block step launch");
 }
 

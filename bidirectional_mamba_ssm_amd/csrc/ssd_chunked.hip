@@ -165,7 +165,7 @@ __device__ __forceinline__ float absmax8(u32x4 r) {
 // --------------------------------------------------------- staging helpers
 // B^T of the 64 tokens [t0, t0+64) (rows row0 + t, valid for t < tlimit) into
 // bt[n][t] as fp16 scaled by 2^s, s chosen from the tokens' largest |B|;
-// returns s. Two barriers.
+// returns s; the tile is visible to the whole block on return. Three barriers.
 __device__ int stage_bt16(const SegArgs &a, const uint16_t *Bm, int b, int grp, int row0, int t0,
                           int tlimit, uint32_t *bt, float *tmp) {
     constexpr int PER = 32 * (kN / 8) / kThreads;   // 2
@@ -195,12 +195,14 @@ __device__ int stage_bt16(const SegArgs &a, const uint16_t *Bm, int b, int grp, 
                 pack2h(ldexpf(b_hi(r0[k][q]), sc), ldexpf(b_hi(r1[k][q]), sc));
         }
     }
+    __syncthreads();   // every wave reads rows other waves wrote
     return sc;
 }
 
 // x of COUNT tokens (rows row0 + t, valid for t < tlimit) of head h into
 // xt[p][t] (row stride xrs) as fp16 scaled by 2^sx, sx chosen from the tile's
-// largest |x|. Returns sx (the same in every thread). Two barriers.
+// largest |x|. Returns sx (the same in every thread); the tile is visible to
+// the whole block on return. Three barriers.
 template <int COUNT>
 __device__ int stage_x16(const SegArgs &a, const uint16_t *X, int b, int h, int row0, int tlimit,
                          uint32_t *xt, int xrs, float *tmp) {
@@ -237,6 +239,7 @@ __device__ int stage_x16(const SegArgs &a, const uint16_t *X, int b, int h, int 
             }
         }
     }
+    __syncthreads();   // every wave reads rows other waves wrote
     return sx;
 }
 
@@ -330,8 +333,8 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
                 sm.sw = sw;
             }
         }
-        const int sB = stage_bt16(a, Bm, b, grp, 0, s0, s1, sm.bt, sm.tmp);  // has barriers
-        const int sx = stage_x16<kSub>(a, X, b, h, s0, n, sm.xt, kRS, sm.tmp);  // has barriers
+        const int sB = stage_bt16(a, Bm, b, grp, 0, s0, s1, sm.bt, sm.tmp);
+        const int sx = stage_x16<kSub>(a, X, b, h, s0, n, sm.xt, kRS, sm.tmp);
         f32x4 T[kN / 16];
 #pragma unroll
         for (int nt = 0; nt < kN / 16; ++nt) T[nt] = zero4();
@@ -701,7 +704,7 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                prev[pt][r] = __builtin_nontemporal_load(yrow[r] + 16 * pt);
+                prev[pt][r] = yrow[r][16 * pt];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
@@ -853,8 +856,9 @@ size_t chunked_workspace(int batch, int L, int H, int G, int Q) {
     const int ts = pick_ts(batch, L, H, Q);
     const size_t nseg = (size_t)(L + ts - 1) / ts;
     const size_t nC = (size_t)(L + Q - 1) / Q;
-    const size_t st = nseg > 1 ? batch * 2 * nseg * H * (size_t)(kP * kN) * 4 : 0;
     (void)nC; (void)G;
+    if (nseg == 1) return 0;   // one segment per row: no segment states
+    const size_t st = batch * 2 * nseg * H * (size_t)(kP * kN) * 4;
     return al256(st) * 2 + al256(batch * 2 * nseg * H * 4);
 }
 
@@ -868,15 +872,17 @@ hipError_t launch_chunked(const Problem &p, void *ws, hipStream_t s) {
     a.Ts = pick_ts(p.batch, p.L, p.H, p.Q);
     a.nseg = (p.L + a.Ts - 1) / a.Ts;
     a.seq = p.seq_idx;
-    const size_t nseg = a.nseg, nC = a.nC;
-    const size_t st = nseg > 1 ? p.batch * 2 * nseg * p.H * (size_t)(kP * kN) * 4 : 0;
-    char *w = (char *)ws;
-    a.S = (float *)w;
-    w += al256(st);
-    a.Hs = (float *)w;
-    w += al256(st);
-    a.gam = (float *)w;
-    (void)nC;
+    const size_t nseg = a.nseg;
+    a.S = a.Hs = a.gam = nullptr;   // only read when a row has several segments
+    if (nseg > 1) {
+        const size_t st = p.batch * 2 * nseg * p.H * (size_t)(kP * kN) * 4;
+        char *w = (char *)ws;
+        a.S = (float *)w;
+        w += al256(st);
+        a.Hs = (float *)w;
+        w += al256(st);
+        a.gam = (float *)w;
+    }
     a.init_state = p.init_state;
     a.final_state = p.final_state;
     a.y = p.y;
