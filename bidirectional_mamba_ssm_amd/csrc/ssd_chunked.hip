@@ -15,7 +15,7 @@
 //         + D x_i
 //   H    <- e^{cs_end} H + sum_j e^{sum_{k>j} a_k} dt_j B_j x_j^T
 //
-// Work split (one WG = 4 waves):
+// Kernels (one workgroup = 4 waves):
 //   k_seg_state  each segment's (Ts tokens) outgoing state from a zero state,
 //                walking away from the outgoing edge and stopping where every
 //                remaining weight is exactly 0.0f in fp32 (e^x underflows)
@@ -25,22 +25,18 @@
 //   k_seg_out    per (row, segment, head): the reverse direction walks the
 //                segment's chunks right to left writing its part of y, the
 //                forward direction walks left to right and adds its part.
-//                Per chunk, B and x are staged once in LDS; for each 64-row
-//                block C is staged and wave w computes rows 16w..16w+15: the
-//                Gram tiles G^T = B C^T on the matrix cores (their accumulator
-//                layout is already the A operand of the following M.x product),
-//                the masked decay, M.x, the carried-state term and D x. The
-//                state update runs with wave w owning state columns
-//                16w..16w+15, kept in registers as MFMA accumulators.
+//                Per chunk x, B (and per 64-row block C) are staged raw in LDS;
+//                wave w computes rows 16w..16w+15 of a row block: the Gram
+//                tiles G^T = B C^T (their accumulator layout is directly the A
+//                operand of the next product), the masked decay, M.x, the
+//                carried-state term and D x. The state update runs with wave
+//                w owning state columns 16w..16w+15 as MFMA accumulators.
 //
-// Operands enter the matrix cores as fp16 (v_mfma_f32_16x16x32_f16), each
-// tile scaled by a power of two chosen from a bound on its magnitude so that
-// it stays inside fp16's range; the fp32 results are scaled back exactly.
-// bf16 inputs (8 significant bits) are exact in fp16 after scaling; the
-// operands that must be rounded (the masked decayed Gram matrix, the carried
-// state, the dt-weighted inputs) keep 11 bits instead of bf16's 8, and the
-// Gram-matrix terms within 16 tokens of the diagonal (undecayed, the largest)
-// enter as an fp16 hi + lo pair.
+// Everything runs on v_mfma_f32_16x16x32_bf16. x, B, C are bf16 already and
+// enter exactly. An operand that has to be rounded (the masked decayed Gram
+// matrix M, the carried state H, the dt-weighted inputs w x) is split into
+// hi = bf16(v) and lo = bf16(v - hi) and multiplied twice: ~16 significant
+// bits, fp32's exponent range, no scaling.
 //
 // Packed sequences: a per-token sequence index masks every term that would
 // cross a sequence boundary, and a chunk or segment holding a boundary (in
@@ -59,39 +55,24 @@ constexpr int kP = 64;         // headdim handled here
 constexpr int kN = 128;        // d_state handled here
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kSub = 64;       // tokens per staged sub-block
-constexpr int kRS = kSub + 8;  // LDS row stride (16-bit elements) of 64-wide tiles
+constexpr int kRS = kSub + 8;  // LDS row stride (16-bit elements) of [n][64 tokens] tiles
+constexpr int kNRS = kN + 8;   // LDS row stride (16-bit elements) of [row][n] tiles
 constexpr float kDead = -110.f;  // expf(x) is exactly 0.0f for every x < kDead
-// magnitude targets (log2) of the scaled fp16 operands
-constexpr int kTop = 14;       // generic operand: |v| < 2^14 (fp16 max 65504)
-constexpr int kTopX = 10;      // x, multiplied later by weights < 2^4
+constexpr float kLog2e = 1.4426950408889634f;
 
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ f32x4 mfma_h(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+// v = hi + lo, hi = bf16(v), lo = bf16(v - hi), packed per pair of values
+__device__ __forceinline__ void split2(float v0, float v1, uint32_t &hi, uint32_t &lo) {
+    const bf16x2_t h = {(__bf16)v0, (__bf16)v1};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+    const bf16x2_t l = {(__bf16)(v0 - h0), (__bf16)(v1 - h1)};
+    lo = __builtin_bit_cast(uint32_t, l);
 }
-__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
-    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-__device__ __forceinline__ float h_lo(uint32_t u) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
-}
-__device__ __forceinline__ float h_hi(uint32_t u) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
-}
-__device__ __forceinline__ float b_lo(uint32_t u) { return bf2f((uint16_t)(u & 0xffffu)); }
-__device__ __forceinline__ float b_hi(uint32_t u) { return bf2f((uint16_t)(u >> 16)); }
-
-// smallest e with m < 2^e for finite m >= 0 (e = -126 for m == 0), clamped
-__device__ __forceinline__ int exp_bound(float m) {
-    if (!(m > 0.f)) return -126;
-    int e;
-    (void)frexpf(m, &e);
-    return e;
-}
-__device__ __forceinline__ int clamp_scale(int s) { return s < -60 ? -60 : (s > 60 ? 60 : s); }
+__device__ __forceinline__ float b_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float b_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct SegArgs {
     DirPtrs dir[2];
@@ -109,22 +90,7 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ size_t tok(const SegArgs &a, int b, int t) { return (size_t)b * a.L + t; }
 __device__ __forceinline__ u32x4 ld8(const uint16_t *p) { return *(const u32x4 *)p; }
-__device__ __forceinline__ u32x2 ld4(const uint16_t *p) { return *(const u32x2 *)p; }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-// max over the block's 256 threads; tmp is 4 floats of LDS; two barriers
-__device__ float block_max(float v, float *tmp) {
-    v = wave_max(v);
-    if (lane_id() == 0) tmp[wave_id()] = v;
-    __syncthreads();
-    const float m = fmaxf(fmaxf(tmp[0], tmp[1]), fmaxf(tmp[2], tmp[3]));
-    __syncthreads();
-    return m;
-}
 // inclusive prefix sum over the block's 256 threads; *total = sum; two barriers
 __device__ float block_scan(float v, float *tmp, float *total) {
     const int lane = lane_id(), w = wave_id();
@@ -155,97 +121,63 @@ __device__ __forceinline__ float wave_scan(float v) {
     }
     return v;
 }
-__device__ __forceinline__ float absmax8(u32x4 r) {
-    float m = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) m = fmaxf(m, fmaxf(fabsf(b_lo(r[q])), fabsf(b_hi(r[q]))));
-    return m;
-}
 
 // --------------------------------------------------------- staging helpers
-// B^T of the 64 tokens [t0, t0+64) (rows row0 + t, valid for t < tlimit) into
-// bt[n][t] as fp16 scaled by 2^s, s chosen from the tokens' largest |B|;
-// returns s; the tile is visible to the whole block on return. Three barriers.
-__device__ int stage_bt16(const SegArgs &a, const uint16_t *Bm, int b, int grp, int row0, int t0,
-                          int tlimit, uint32_t *bt, float *tmp) {
-    constexpr int PER = 32 * (kN / 8) / kThreads;   // 2
-    u32x4 r0[PER], r1[PER];
-    float m = 0.f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int item = threadIdx.x + kThreads * k;
-        const int rp = item >> 4, cg = item & 15;
-        const int t = t0 + 2 * rp;
-        r0[k] = u32x4{0u, 0u, 0u, 0u};
-        r1[k] = u32x4{0u, 0u, 0u, 0u};
-        if (t < tlimit) r0[k] = ld8(Bm + (tok(a, b, row0 + t) * a.G + grp) * kN + 8 * cg);
-        if (t + 1 < tlimit) r1[k] = ld8(Bm + (tok(a, b, row0 + t + 1) * a.G + grp) * kN + 8 * cg);
-        m = fmaxf(m, fmaxf(absmax8(r0[k]), absmax8(r1[k])));
-    }
-    const int sc = clamp_scale(kTop - exp_bound(block_max(m, tmp)));
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int item = threadIdx.x + kThreads * k;
-        const int rp = item >> 4, cg = item & 15;
+// x of COUNT tokens (rows row0 + t, zero for t >= tlimit) of head h, raw bf16,
+// transposed into xt[p][t] (row stride xrs). Consecutive lanes read
+// consecutive 16-byte column groups of a token row. No barrier.
+template <int COUNT>
+__device__ __forceinline__ void stage_xt(const SegArgs &a, const uint16_t *X, int b, int h,
+                                         int row0, int tlimit, uint32_t *xt, int xrs) {
+    constexpr int ITEMS = (COUNT / 2) * (kP / 8);
+    for (int item = threadIdx.x; item < ITEMS; item += kThreads) {
+        const int rp = item >> 3, cg = item & 7;
+        const int t = 2 * rp;
+        u32x4 r0 = {0u, 0u, 0u, 0u}, r1 = {0u, 0u, 0u, 0u};
+        if (t < tlimit) r0 = ld8(X + (tok(a, b, row0 + t) * a.H + h) * kP + 8 * cg);
+        if (t + 1 < tlimit) r1 = ld8(X + (tok(a, b, row0 + t + 1) * a.H + h) * kP + 8 * cg);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            bt[((8 * cg + 2 * q) * kRS) / 2 + rp] =
-                pack2h(ldexpf(b_lo(r0[k][q]), sc), ldexpf(b_lo(r1[k][q]), sc));
-            bt[((8 * cg + 2 * q + 1) * kRS) / 2 + rp] =
-                pack2h(ldexpf(b_hi(r0[k][q]), sc), ldexpf(b_hi(r1[k][q]), sc));
+            xt[((8 * cg + 2 * q) * xrs) / 2 + rp] = (r0[q] & 0xffffu) | (r1[q] << 16);
+            xt[((8 * cg + 2 * q + 1) * xrs) / 2 + rp] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
         }
     }
-    __syncthreads();   // every wave reads rows other waves wrote
-    return sc;
 }
 
-// x of COUNT tokens (rows row0 + t, valid for t < tlimit) of head h into
-// xt[p][t] (row stride xrs) as fp16 scaled by 2^sx, sx chosen from the tile's
-// largest |x|. Returns sx (the same in every thread); the tile is visible to
-// the whole block on return. Three barriers.
-template <int COUNT>
-__device__ int stage_x16(const SegArgs &a, const uint16_t *X, int b, int h, int row0, int tlimit,
-                         uint32_t *xt, int xrs, float *tmp) {
-    constexpr int PAIRS = COUNT / 2;
-    constexpr int ITEMS = PAIRS * (kP / 8);
-    constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
-    u32x4 r0[PER], r1[PER];
-    float m = 0.f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int item = threadIdx.x + kThreads * k;
-        r0[k] = u32x4{0u, 0u, 0u, 0u};
-        r1[k] = u32x4{0u, 0u, 0u, 0u};
-        if (item < ITEMS) {
-            const int rp = item / (kP / 8), cg = item % (kP / 8);
-            const int t = 2 * rp;
-            if (t < tlimit) r0[k] = ld8(X + (tok(a, b, row0 + t) * a.H + h) * kP + 8 * cg);
-            if (t + 1 < tlimit) r1[k] = ld8(X + (tok(a, b, row0 + t + 1) * a.H + h) * kP + 8 * cg);
-            m = fmaxf(m, fmaxf(absmax8(r0[k]), absmax8(r1[k])));
-        }
+// 64 token rows [t0, t0+64) (zero for t >= tlimit) of a [t][G][N] bf16
+// tensor, raw, into dst[row][n] (row stride kNRS). No barrier.
+__device__ __forceinline__ void stage_rows(const SegArgs &a, const uint16_t *M, int b, int grp,
+                                           int row0, int t0, int tlimit, uint32_t *dst) {
+    for (int item = threadIdx.x; item < 64 * (kN / 8); item += kThreads) {
+        const int row = item >> 4, cg = item & 15;
+        const int t = t0 + row;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (t < tlimit) v = ld8(M + (tok(a, b, row0 + t) * a.G + grp) * kN + 8 * cg);
+        *(u32x4 *)(dst + (row * kNRS + 8 * cg) / 2) = v;
     }
-    const int sx = clamp_scale(kTopX - exp_bound(block_max(m, tmp)));
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int item = threadIdx.x + kThreads * k;
-        if (item < ITEMS) {
-            const int rp = item / (kP / 8), cg = item % (kP / 8);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                xt[((8 * cg + 2 * q) * xrs) / 2 + rp] =
-                    pack2h(ldexpf(b_lo(r0[k][q]), sx), ldexpf(b_lo(r1[k][q]), sx));
-                xt[((8 * cg + 2 * q + 1) * xrs) / 2 + rp] =
-                    pack2h(ldexpf(b_hi(r0[k][q]), sx), ldexpf(b_hi(r1[k][q]), sx));
-            }
-        }
-    }
-    __syncthreads();   // every wave reads rows other waves wrote
-    return sx;
 }
 
-// T[n][p-block w] = sum_t B^T[n][t] (w_t x_t[p]) over one staged 64-token
-// sub-block (scaled domain). xt: X^T[p][t] fp16 (row stride xrs, column
-// offset xoff); wv: 64 scaled weights.
+// B^T of the 64 tokens [t0, t0+64) (zero for t >= tlimit) into bt[n][t]
+// (row stride kRS), raw bf16. No barrier.
+__device__ __forceinline__ void stage_bt(const SegArgs &a, const uint16_t *Bm, int b, int grp,
+                                         int row0, int t0, int tlimit, uint32_t *bt) {
+    for (int item = threadIdx.x; item < 32 * (kN / 8); item += kThreads) {
+        const int rp = item >> 4, cg = item & 15;
+        const int t = t0 + 2 * rp;
+        u32x4 r0 = {0u, 0u, 0u, 0u}, r1 = {0u, 0u, 0u, 0u};
+        if (t < tlimit) r0 = ld8(Bm + (tok(a, b, row0 + t) * a.G + grp) * kN + 8 * cg);
+        if (t + 1 < tlimit) r1 = ld8(Bm + (tok(a, b, row0 + t + 1) * a.G + grp) * kN + 8 * cg);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bt[((8 * cg + 2 * q) * kRS) / 2 + rp] = (r0[q] & 0xffffu) | (r1[q] << 16);
+            bt[((8 * cg + 2 * q + 1) * kRS) / 2 + rp] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
+        }
+    }
+}
+
+// T[n][p-block w] += sum_t B^T[n][t] (w_t x_t[p]) over one staged 64-token
+// sub-block; w x enters as a hi + lo bf16 pair. xt: X^T[p][t] (row stride
+// xrs, column offset xoff); wv: the 64 weights.
 __device__ __forceinline__ void state_mfma(f32x4 (&T)[kN / 16], const uint32_t *bt,
                                            const uint16_t *xt, int xrs, int xoff, const float *wv) {
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
@@ -256,14 +188,17 @@ __device__ __forceinline__ void state_mfma(f32x4 (&T)[kN / 16], const uint32_t *
         const u32x4 xv = *(const u32x4 *)(xt + (16 * w + l16) * xrs + xoff + tk);
         const f32x4 w0 = *(const f32x4 *)(wv + tk);
         const f32x4 w1 = *(const f32x4 *)(wv + tk + 4);
-        const u32x4 bop = {pack2h(h_lo(xv[0]) * w0[0], h_hi(xv[0]) * w0[1]),
-                           pack2h(h_lo(xv[1]) * w0[2], h_hi(xv[1]) * w0[3]),
-                           pack2h(h_lo(xv[2]) * w1[0], h_hi(xv[2]) * w1[1]),
-                           pack2h(h_lo(xv[3]) * w1[2], h_hi(xv[3]) * w1[3])};
+        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+        split2(b_lo(xv[0]) * w0[0], b_hi(xv[0]) * w0[1], h0, l0);
+        split2(b_lo(xv[1]) * w0[2], b_hi(xv[1]) * w0[3], h1, l1);
+        split2(b_lo(xv[2]) * w1[0], b_hi(xv[2]) * w1[1], h2, l2);
+        split2(b_lo(xv[3]) * w1[2], b_hi(xv[3]) * w1[3], h3, l3);
+        const u32x4 bhi = {h0, h1, h2, h3}, blo = {l0, l1, l2, l3};
 #pragma unroll
         for (int nt = 0; nt < kN / 16; ++nt) {
             const u32x4 aop = *(const u32x4 *)(btp + (16 * nt + l16) * kRS + tk);
-            T[nt] = mfma_h(aop, bop, T[nt]);
+            T[nt] = mfma16x16x32(aop, bhi, T[nt]);
+            T[nt] = mfma16x16x32(aop, blo, T[nt]);
         }
     }
 }
@@ -271,11 +206,9 @@ __device__ __forceinline__ void state_mfma(f32x4 (&T)[kN / 16], const uint32_t *
 // ----------------------------------------------------------- k_seg_state
 struct StateSmem {
     float w[kSub];
-    float tmp[4];
-    uint32_t bt[kN * kRS / 2];
-    uint32_t xt[kP * kRS / 2];
+    alignas(16) uint32_t bt[kN * kRS / 2];
+    alignas(16) uint32_t xt[kP * kRS / 2];
     float run[2];   // running sum of a from the outgoing edge, by step parity
-    int sw;         // weight scale of the current sub-block
 };
 
 __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
@@ -311,6 +244,8 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
         const float run = sm.run[step & 1];
         if (run < kDead) break;
         if (a.seq && a.seq[tok(a, b, d == 0 ? s1 - 1 : s0)] != edge_seq) break;
+        stage_bt(a, Bm, b, grp, 0, s0, s1, sm.bt);
+        stage_xt<kSub>(a, X, b, h, s0, n, sm.xt, kRS);
         if (w == 0) {
             // lane 0 is the token nearest the outgoing edge
             const bool in = lane < n;
@@ -321,29 +256,16 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
                 at = dtt * Ah;
             }
             const float incl = wave_scan(at);
-            const int sw = clamp_scale(4 - exp_bound(wave_max(dtt)));
             float wt = 0.f;
             if (in && (!a.seq || a.seq[tok(a, b, s0 + pos)] == edge_seq))
-                wt = ldexpf(expf(run + incl - at) * dtt, sw);
+                wt = expf(run + incl - at) * dtt;
             if (in) sm.w[pos] = wt;
             else sm.w[lane] = 0.f;
             const float tot = __shfl(incl, 63, 64);
-            if (lane == 0) {
-                sm.run[(step + 1) & 1] = run + tot;
-                sm.sw = sw;
-            }
+            if (lane == 0) sm.run[(step + 1) & 1] = run + tot;
         }
-        const int sB = stage_bt16(a, Bm, b, grp, 0, s0, s1, sm.bt, sm.tmp);
-        const int sx = stage_x16<kSub>(a, X, b, h, s0, n, sm.xt, kRS, sm.tmp);
-        f32x4 T[kN / 16];
-#pragma unroll
-        for (int nt = 0; nt < kN / 16; ++nt) T[nt] = zero4();
-        state_mfma(T, sm.bt, (const uint16_t *)sm.xt, kRS, 0, sm.w);
-        const int unscale = -(sB + sm.sw + sx);
-#pragma unroll
-        for (int nt = 0; nt < kN / 16; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Hacc[nt][r] += ldexpf(T[nt][r], unscale);
+        __syncthreads();
+        state_mfma(Hacc, sm.bt, (const uint16_t *)sm.xt, kRS, 0, sm.w);
         __syncthreads();
     }
     const size_t si = (((size_t)b * 2 + d) * a.nseg + seg) * a.H + h;
@@ -393,61 +315,32 @@ __global__ void __launch_bounds__(256) k_seg_scan(const SegArgs a) {
 }
 
 // ------------------------------------------------------------- k_seg_out
-constexpr int kNRS = kN + 8;   // LDS row stride (16-bit elements) of [t][n] / [p][n] tiles
 constexpr int kTileU32 = (kN * kRS > 64 * kNRS ? kN * kRS : 64 * kNRS) / 2;
 
 template <int Q>
 struct OutSmem {
-    float cs[Q], w[Q], u[Q], dt[Q], a[Q];
+    static constexpr bool kBnLds = Q <= 128;    // B of the whole chunk kept in LDS
+    float cs2[Q];          // inclusive scan in the walking direction, times log2(e)
+    float u[Q];            // e^{cs}, 0 where the carried state does not reach
+    float w[Q];            // state-update weights
+    float v16[Q];          // e^{cs(edge of the token's 16-tile) - cs} dt
+    float v64[Q];          // e^{cs(edge of the token's 64-block) - cs} dt
+    float a[Q];
+    float dt[Q];
     int sq[Q];
     float tmp[4];
-    int utile[Q / 16];     // any nonzero e^{cs} in the 16-row tile
+    int utile[Q / 16];     // any nonzero u in the 16-row tile
     int wsub[Q / kSub];    // any nonzero weight in the 64-token sub-block
-    int sB[Q / kSub];      // fp16 scale exponent of each staged B sub-block
-    int eBmax;             // bound (log2) of |B| over the chunk
-    int sH[4];             // fp16 scale exponent of each 16-column block of H^T
     float gamma;
-    int sx, sw, edt;       // x scale, weight scale, dt bound of the chunk
-    uint32_t xt[kP * (Q + 8) / 2];   // X^T [p][t], fp16 scaled by 2^sx
-    uint32_t bn[Q * kNRS / 2];       // B [t][n] of the chunk, fp16 scaled per sub-block
-    uint32_t tile[kTileU32];         // C tile [64][n] (rows) or B^T [n][64] (state update)
-    uint32_t ht[kP * kNRS / 2];      // H^T [p][n], fp16 scaled per column block
+    alignas(16) uint32_t xt[kP * (Q + 8) / 2];            // X^T [p][t], raw bf16
+    alignas(16) uint32_t bn[kBnLds ? Q * kNRS / 2 : 4];   // B [t][n] of the chunk, raw bf16
+    alignas(16) uint32_t tile[kTileU32];                  // C [64][n] of a row block / B^T [n][64]
+    alignas(16) uint32_t hth[kP * kNRS / 2];              // H^T [p][n], bf16 high part
+    alignas(16) uint32_t htl[kP * kNRS / 2];              // H^T [p][n], bf16 residual
 };
 
-// 64 rows [t0, t0+64) (valid below tlimit) of a [t][G][N] bf16 tensor into
-// dst[row][n] (row stride kNRS) as fp16 scaled by 2^s, s chosen from the
-// rows' largest |value|; returns s, *e gets the bound. Two barriers.
-__device__ int stage_rows16(const SegArgs &a, const uint16_t *M, int b, int grp, int row0, int t0,
-                            int tlimit, uint32_t *dst, float *tmp, int *e) {
-    constexpr int PER = 64 * (kN / 8) / kThreads;   // 4
-    u32x4 r[PER];
-    float m = 0.f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int item = threadIdx.x + kThreads * k;
-        const int row = item >> 4, cg = item & 15;
-        const int t = t0 + row;
-        r[k] = u32x4{0u, 0u, 0u, 0u};
-        if (t < tlimit) r[k] = ld8(M + (tok(a, b, row0 + t) * a.G + grp) * kN + 8 * cg);
-        m = fmaxf(m, absmax8(r[k]));
-    }
-    const int eb = exp_bound(block_max(m, tmp));
-    const int sc = clamp_scale(kTop - eb);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int item = threadIdx.x + kThreads * k;
-        const int row = item >> 4, cg = item & 15;
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            o[q] = pack2h(ldexpf(b_lo(r[k][q]), sc), ldexpf(b_hi(r[k][q]), sc));
-        *(u32x4 *)(dst + (row * kNRS + 8 * cg) / 2) = o;
-    }
-    *e = eb;
-    return sc;
-}
-
-// One chunk [c0, c0+len) of direction d: scans, weights, masks, X^T, B.
+// One chunk [c0, c0+len) of direction d: scans, decay factors, weights,
+// masks; x (and B) staged.
 template <int Q>
 __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h, int grp, int c0,
                            int len) {
@@ -455,23 +348,27 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
     const DirPtrs &dp = a.dir[d];
     const uint16_t *DT = (const uint16_t *)dp.dt;
     const float Ah = dp.A[h];
+    // stage first: these loads overlap the scans below
+    stage_xt<Q>(a, (const uint16_t *)dp.x, b, h, c0, len, sm.xt, Q + 8);
+    if (OutSmem<Q>::kBnLds)
+        for (int sb = 0; sb < Q / kSub; ++sb)
+            stage_rows(a, (const uint16_t *)dp.B, b, grp, c0, kSub * sb, len,
+                       sm.bn + (kSub * sb * kNRS) / 2);
     // (1) inclusive scan in the walking direction
     const int iw = d == 0 ? tid : Q - 1 - tid;
     float at = 0.f, dtt = 0.f;
+    int sq = 0;
     if (tid < Q && iw < len) {
         dtt = bf2f(DT[tok(a, b, c0 + iw) * a.H + h]);
         at = dtt * Ah;
+        if (a.seq) sq = a.seq[tok(a, b, c0 + iw)];
     }
     float total;
     const float cs = block_scan(tid < Q ? at : 0.f, sm.tmp, &total);
-    const int edt = exp_bound(block_max(dtt, sm.tmp));
-    const int sw = clamp_scale(4 - edt);
-    int sq = 0;
     if (tid < Q) {
-        sm.cs[iw] = cs;
+        sm.cs2[iw] = cs * kLog2e;
         sm.dt[iw] = dtt;
         sm.a[iw] = at;
-        if (a.seq && iw < len) sq = a.seq[tok(a, b, c0 + iw)];
         sm.sq[iw] = sq;
         bool off_ok = iw < len;
         if (a.seq && iw < len) {
@@ -482,7 +379,8 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
         sm.u[iw] = off_ok ? expf(cs) : 0.f;
     }
     __syncthreads();
-    // (2) exclusive sums toward the outgoing edge -> state weights (scaled)
+    // (2) exclusive sums toward the outgoing edge -> state weights; decay of
+    // each token to the near edge of its 16-tile and of its 64-block
     const int ie = d == 0 ? Q - 1 - tid : tid;
     const float ae = (tid < Q && ie < len) ? sm.a[ie] : 0.f;
     float tot2;
@@ -491,9 +389,17 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
         float wt = 0.f;
         if (ie < len) {
             const int edge = d == 0 ? len - 1 : 0;
-            if (!a.seq || sm.sq[ie] == sm.sq[edge]) wt = ldexpf(expf(incl - ae) * sm.dt[ie], sw);
+            if (!a.seq || sm.sq[ie] == sm.sq[edge]) wt = expf(incl - ae) * sm.dt[ie];
         }
         sm.w[ie] = wt;
+        // the edge nearest the diagonal of a column tile: its last token
+        // (forward, j <= i) or its first (reverse, j >= i)
+        const int j = tid;
+        const int r16 = d == 0 ? (j | 15) : (j & ~15);
+        const int r64 = d == 0 ? (j | 63) : (j & ~63);
+        const float c = sm.cs2[j];
+        sm.v16[j] = exp2_(sm.cs2[r16] - c) * sm.dt[j];
+        sm.v64[j] = exp2_(sm.cs2[r64] - c) * sm.dt[j];
     }
     if (tid == 0) {
         bool carry = true;
@@ -502,22 +408,8 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
             if (d == 1 && c0 + len < a.L) carry = a.seq[tok(a, b, c0 + len)] == a.seq[tok(a, b, c0)];
         }
         sm.gamma = carry ? expf(total) : 0.f;
-        sm.sw = sw;
-        sm.edt = edt;
     }
-    const int sx = stage_x16<Q>(a, (const uint16_t *)dp.x, b, h, c0, len, sm.xt, Q + 8, sm.tmp);
-    // B of the chunk, natural layout, one scale per 64-token sub-block
-    int ebmax = -126;
-    for (int sb = 0; sb < Q / kSub; ++sb) {
-        int eb = -126;
-        const int sc = kSub * sb < len
-            ? stage_rows16(a, (const uint16_t *)dp.B, b, grp, c0, kSub * sb, len,
-                           sm.bn + (kSub * sb * kNRS) / 2, sm.tmp, &eb)
-            : 0;
-        if (tid == 0) sm.sB[sb] = sc;
-        ebmax = max(ebmax, eb);
-    }
-    if (tid == 0) { sm.sx = sx; sm.eBmax = ebmax; }
+    __syncthreads();
     if (tid < Q / 16) {
         int any = 0;
         for (int r = 0; r < 16; ++r) any |= sm.u[16 * tid + r] != 0.f;
@@ -532,25 +424,21 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
     __syncthreads();
 }
 
-// Writes H (the wave's 16 columns, fp32 accumulators) into sm.ht as fp16,
-// scaled by a per-wave power of two.
+// Writes the wave's 16 state columns (fp32 accumulators) into H^T hi / lo.
 template <int Q>
 __device__ void publish_state(OutSmem<Q> &sm, const f32x4 (&Hacc)[kN / 16]) {
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
-    float hm = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < kN / 16; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hm = fmaxf(hm, fabsf(Hacc[nt][r]));
-    const int sH = clamp_scale(kTop - exp_bound(wave_max(hm)));
-    uint16_t *ht = (uint16_t *)sm.ht;
+    uint16_t *hh = (uint16_t *)sm.hth;
+    uint16_t *hl = (uint16_t *)sm.htl;
 #pragma unroll
     for (int nt = 0; nt < kN / 16; ++nt) {
-        const u32x2 v = {pack2h(ldexpf(Hacc[nt][0], sH), ldexpf(Hacc[nt][1], sH)),
-                         pack2h(ldexpf(Hacc[nt][2], sH), ldexpf(Hacc[nt][3], sH))};
-        *(u32x2 *)(ht + (16 * w + l16) * kNRS + 16 * nt + 4 * g4) = v;
+        uint32_t a0, a1, b0, b1;
+        split2(Hacc[nt][0], Hacc[nt][1], a0, b0);
+        split2(Hacc[nt][2], Hacc[nt][3], a1, b1);
+        const int o = (16 * w + l16) * kNRS + 16 * nt + 4 * g4;
+        *(u32x2 *)(hh + o) = u32x2{a0, a1};
+        *(u32x2 *)(hl + o) = u32x2{b0, b1};
     }
-    if (lane == 0) sm.sH[w] = sH;
 }
 
 // Row block I (64 rows) of the chunk: intra-chunk form, carried state, skip
@@ -560,20 +448,17 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
                           int c0, int len, int I, bool has_state, float Dh, bool add) {
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
     const DirPtrs &dp = a.dir[d];
-    int eC;
-    const int sC = stage_rows16(a, (const uint16_t *)dp.C, b, grp, c0, 64 * I, len, sm.tile, sm.tmp, &eC);
-    // C is now in sm.tile (natural rows)
+    stage_rows(a, (const uint16_t *)dp.C, b, grp, c0, 64 * I, len, sm.tile);
     __syncthreads();
     const uint16_t *ct = (const uint16_t *)sm.tile;
-    const uint16_t *bn = (const uint16_t *)sm.bn;
     const uint16_t *xt = (const uint16_t *)sm.xt;
+    const uint16_t *Bg = (const uint16_t *)dp.B;
     constexpr int XRS = Q + 8;
     const int it = 4 * I + w;               // this wave's 16-row tile
     const int i = 16 * it + l16;            // this lane's row (A operand / G^T column)
     const bool row_ok = i < len;
-    const float csi = sm.cs[i];
+    const float csi = sm.cs2[i];
     const int sqi = sm.sq[i];
-    const int sM = clamp_scale(kTop - (sm.eBmax + eC + 7 + sm.edt));
     f32x4 acc[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
@@ -584,22 +469,16 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
         for (int J = Jlo; J <= Jhi; ++J) {
             if (64 * J >= len) break;
             if (J != I) {
-                const float near = d == 0 ? sm.cs[64 * I] - sm.cs[64 * J + 63]
-                                          : sm.cs[64 * I + 63] - sm.cs[64 * J];
-                if (near < kDead) continue;
+                const float near = d == 0 ? sm.cs2[64 * I] - sm.cs2[64 * J + 63]
+                                          : sm.cs2[64 * I + 63] - sm.cs2[64 * J];
+                if (near < kDead * kLog2e) continue;
             }
-            const int gexp = sM - sm.sB[J] - sC;   // G (scaled) -> M scaled by 2^sM
-            const int ref = d == 0 ? 64 * J + 63 : 64 * J;
-            const float ui = J != I ? expf(csi - sm.cs[ref]) : 0.f;
-            // terms within 16 tokens of the diagonal carry no decay and are the
-            // largest: they enter as an fp16 hi + lo pair
-            u32x4 mop[2], mlo[2];
-            bool near_diag[2];
+            const int r64 = d == 0 ? 64 * J + 63 : 64 * J;
+            const float u64 = exp2_(csi - sm.cs2[r64]);
+            u32x4 mhi[2], mlo[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const int jk = 64 * J + 32 * kk, ik = 16 * it;
-                near_diag[kk] = jk <= ik + 30 && jk + 31 >= ik - 15;
-                uint32_t pk[4], pl[4];
+                uint32_t ph[4], pl[4];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int jt = 2 * kk + half;
@@ -611,29 +490,53 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
                         f32x4 g = zero4();
 #pragma unroll
                         for (int ks = 0; ks < kN / 32; ++ks) {
-                            const u32x4 aop = *(const u32x4 *)(bn + (j0 + l16) * kNRS + 32 * ks + 8 * g4);
+                            u32x4 aop;
+                            if (OutSmem<Q>::kBnLds) {
+                                aop = *(const u32x4 *)((const uint16_t *)sm.bn + (j0 + l16) * kNRS + 32 * ks + 8 * g4);
+                            } else {
+                                const int jr = min(j0 + l16, len - 1);
+                                aop = ld8(Bg + (tok(a, b, c0 + jr) * a.G + grp) * kN + 32 * ks + 8 * g4);
+                            }
                             const u32x4 bop = *(const u32x4 *)(ct + (16 * w + l16) * kNRS + 32 * ks + 8 * g4);
-                            g = mfma_h(aop, bop, g);
+                            g = mfma16x16x32(aop, bop, g);
                         }
-                        // g[r] = G[i][j] (scaled), j = j0 + 4 g4 + r
+                        // g[r] = G[i][j], j = j0 + 4 g4 + r
+                        const int jb = j0 + 4 * g4;
+                        if (J != I) {
+                            const f32x4 vv = *(const f32x4 *)(sm.v64 + jb);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = j0 + 4 * g4 + r;
-                            bool ok = row_ok && j < len;
-                            if (J == I) ok = ok && (d == 0 ? j <= i : j >= i);
-                            if (a.seq) ok = ok && sm.sq[j] == sqi;
-                            float dec;
-                            if (J == I) dec = expf(csi - sm.cs[j]);
-                            else dec = ui * expf(sm.cs[ref] - sm.cs[j]);
-                            mv[r] = ok ? ldexpf(g[r], gexp) * dec * sm.dt[j] : 0.f;
+                            for (int r = 0; r < 4; ++r) mv[r] = g[r] * u64 * vv[r];
+                        } else if (jt != w) {
+                            // another 16-tile of the diagonal block: factor the
+                            // decay through that tile's edge
+                            const int r16 = d == 0 ? j0 + 15 : j0;
+                            const float u16 = exp2_(csi - sm.cs2[r16]);
+                            const f32x4 vv = *(const f32x4 *)(sm.v16 + jb);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) mv[r] = g[r] * u16 * vv[r];
+                        } else {
+                            // the diagonal 16x16 tile: one exponential per entry
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int j = jb + r;
+                                const bool tri = d == 0 ? j <= i : j >= i;
+                                mv[r] = tri ? g[r] * exp2_(csi - sm.cs2[j]) * sm.dt[j] : 0.f;
+                            }
+                        }
+                        if (!row_ok || jb + 3 >= len || a.seq) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int j = jb + r;
+                                bool ok = row_ok && j < len;
+                                if (a.seq) ok = ok && sm.sq[j] == sqi;
+                                if (!ok) mv[r] = 0.f;
+                            }
                         }
                     }
-                    pk[2 * half] = pack2h(mv[0], mv[1]);
-                    pk[2 * half + 1] = pack2h(mv[2], mv[3]);
-                    pl[2 * half] = pack2h(mv[0] - h_lo(pk[2 * half]), mv[1] - h_hi(pk[2 * half]));
-                    pl[2 * half + 1] = pack2h(mv[2] - h_lo(pk[2 * half + 1]), mv[3] - h_hi(pk[2 * half + 1]));
+                    split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
+                    split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
                 }
-                mop[kk] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+                mhi[kk] = u32x4{ph[0], ph[1], ph[2], ph[3]};
                 mlo[kk] = u32x4{pl[0], pl[1], pl[2], pl[3]};
             }
 #pragma unroll
@@ -645,21 +548,17 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
                     const u32x2 x0 = *(const u32x2 *)(xr + jb);
                     const u32x2 x1 = *(const u32x2 *)(xr + jb + 16);
                     const u32x4 xo = {x0[0], x0[1], x1[0], x1[1]};
-                    acc[pt] = mfma_h(mop[kk], xo, acc[pt]);
-                    if (near_diag[kk]) acc[pt] = mfma_h(mlo[kk], xo, acc[pt]);
+                    acc[pt] = mfma16x16x32(mhi[kk], xo, acc[pt]);
+                    acc[pt] = mfma16x16x32(mlo[kk], xo, acc[pt]);
                 }
             }
         }
     }
-    const int un = -(sM + sm.sx);
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[pt][r] = ldexpf(acc[pt][r], un);
 
-    // ---- carried state: u_i * C_i . H (rows with u == 0 skipped: exact)
+    // ---- carried state: u_i * C_i . H (tiles whose u is all 0: skipped, exact)
     if (has_state && sm.utile[it]) {
-        const uint16_t *ht = (const uint16_t *)sm.ht;
+        const uint16_t *hh = (const uint16_t *)sm.hth;
+        const uint16_t *hl = (const uint16_t *)sm.htl;
         f32x4 t[4];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) t[pt] = zero4();
@@ -668,29 +567,27 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
             const u32x4 aop = *(const u32x4 *)(ct + (16 * w + l16) * kNRS + 32 * ks + 8 * g4);
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
-                const u32x4 bop = *(const u32x4 *)(ht + (16 * pt + l16) * kNRS + 32 * ks + 8 * g4);
-                t[pt] = mfma_h(aop, bop, t[pt]);
+                const int o = (16 * pt + l16) * kNRS + 32 * ks + 8 * g4;
+                t[pt] = mfma16x16x32(aop, *(const u32x4 *)(hh + o), t[pt]);
+                t[pt] = mfma16x16x32(aop, *(const u32x4 *)(hl + o), t[pt]);
             }
         }
         const f32x4 uu = *(const f32x4 *)(sm.u + 16 * it + 4 * g4);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const int unh = -(sC + sm.sH[pt]);
+        for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(uu[r], ldexpf(t[pt][r], unh), acc[pt][r]);
-        }
+            for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(uu[r], t[pt][r], acc[pt][r]);
     }
 
     // ---- skip term (x exact) and output rows 16it + 4g4 + r
-    const int sxn = -sm.sx;
     const int i0 = 16 * it + 4 * g4;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
         const u32x2 xv = *(const u32x2 *)(xt + (16 * pt + l16) * XRS + i0);
-        acc[pt][0] = fmaf(Dh, ldexpf(h_lo(xv[0]), sxn), acc[pt][0]);
-        acc[pt][1] = fmaf(Dh, ldexpf(h_hi(xv[0]), sxn), acc[pt][1]);
-        acc[pt][2] = fmaf(Dh, ldexpf(h_lo(xv[1]), sxn), acc[pt][2]);
-        acc[pt][3] = fmaf(Dh, ldexpf(h_hi(xv[1]), sxn), acc[pt][3]);
+        acc[pt][0] = fmaf(Dh, b_lo(xv[0]), acc[pt][0]);
+        acc[pt][1] = fmaf(Dh, b_hi(xv[0]), acc[pt][1]);
+        acc[pt][2] = fmaf(Dh, b_lo(xv[1]), acc[pt][2]);
+        acc[pt][3] = fmaf(Dh, b_hi(xv[1]), acc[pt][3]);
     }
     float *yrow[4];
 #pragma unroll
@@ -703,8 +600,7 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                prev[pt][r] = yrow[r][16 * pt];
+            for (int r = 0; r < 4; ++r) prev[pt][r] = yrow[r][16 * pt];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
@@ -719,37 +615,35 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
 }
 
 // H <- gamma H + sum over the chunk's tokens of w_t B_t x_t^T (the wave's
-// 16 columns), B^T transposed inside LDS from the staged B.
+// 16 columns).
 template <int Q>
-__device__ void chunk_state_update(OutSmem<Q> &sm, f32x4 (&Hacc)[kN / 16], int len) {
+__device__ void chunk_state_update(const SegArgs &a, OutSmem<Q> &sm, f32x4 (&Hacc)[kN / 16],
+                                   const uint16_t *Bm, int b, int grp, int c0, int len) {
     const float gmm = sm.gamma;
 #pragma unroll
     for (int nt = 0; nt < kN / 16; ++nt) Hacc[nt] *= gmm;
-    const uint16_t *bn = (const uint16_t *)sm.bn;
     for (int sb = 0; sb < Q / kSub; ++sb) {
         if (kSub * sb >= len) break;
         if (!sm.wsub[sb]) continue;    // every weight is exactly 0
-        for (int item = threadIdx.x; item < 32 * (kN / 8); item += kThreads) {
-            const int rp = item & 31, cg = item >> 5;
-            const int t = kSub * sb + 2 * rp;
-            const u32x4 r0 = *(const u32x4 *)(bn + t * kNRS + 8 * cg);
-            const u32x4 r1 = *(const u32x4 *)(bn + (t + 1) * kNRS + 8 * cg);
+        if (OutSmem<Q>::kBnLds) {
+            // B^T transposed inside LDS from the staged B
+            const uint16_t *bn = (const uint16_t *)sm.bn;
+            for (int item = threadIdx.x; item < 32 * (kN / 8); item += kThreads) {
+                const int rp = item & 31, cg = item >> 5;
+                const int t = kSub * sb + 2 * rp;
+                const u32x4 r0 = *(const u32x4 *)(bn + t * kNRS + 8 * cg);
+                const u32x4 r1 = *(const u32x4 *)(bn + (t + 1) * kNRS + 8 * cg);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sm.tile[((8 * cg + 2 * q) * kRS) / 2 + rp] = (r0[q] & 0xffffu) | (r1[q] << 16);
-                sm.tile[((8 * cg + 2 * q + 1) * kRS) / 2 + rp] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
+                for (int q = 0; q < 4; ++q) {
+                    sm.tile[((8 * cg + 2 * q) * kRS) / 2 + rp] = (r0[q] & 0xffffu) | (r1[q] << 16);
+                    sm.tile[((8 * cg + 2 * q + 1) * kRS) / 2 + rp] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
+                }
             }
+        } else {
+            stage_bt(a, Bm, b, grp, c0, kSub * sb, len, sm.tile);
         }
         __syncthreads();
-        f32x4 T[kN / 16];
-#pragma unroll
-        for (int nt = 0; nt < kN / 16; ++nt) T[nt] = zero4();
-        state_mfma(T, sm.tile, (const uint16_t *)sm.xt, Q + 8, kSub * sb, sm.w + kSub * sb);
-        const int un = -(sm.sB[sb] + sm.sw + sm.sx);
-#pragma unroll
-        for (int nt = 0; nt < kN / 16; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Hacc[nt][r] += ldexpf(T[nt][r], un);
+        state_mfma(Hacc, sm.tile, (const uint16_t *)sm.xt, Q + 8, kSub * sb, sm.w + kSub * sb);
         __syncthreads();
     }
 }
@@ -806,7 +700,7 @@ __global__ void __launch_bounds__(kThreads) k_seg_out(const SegArgs a) {
             const bool last = s == nch - 1;
             const bool want_final = d == 0 && seg == a.nseg - 1 && a.final_state;
             if (!last || want_final) {
-                chunk_state_update<Q>(sm, Hacc, len);
+                chunk_state_update<Q>(a, sm, Hacc, (const uint16_t *)dp.B, b, grp, c0, len);
                 if (!last) {
                     publish_state<Q>(sm, Hacc);
                     has_state = true;
@@ -855,8 +749,7 @@ bool chunked_supported(const Problem &p) {
 size_t chunked_workspace(int batch, int L, int H, int G, int Q) {
     const int ts = pick_ts(batch, L, H, Q);
     const size_t nseg = (size_t)(L + ts - 1) / ts;
-    const size_t nC = (size_t)(L + Q - 1) / Q;
-    (void)nC; (void)G;
+    (void)G;
     if (nseg == 1) return 0;   // one segment per row: no segment states
     const size_t st = batch * 2 * nseg * H * (size_t)(kP * kN) * 4;
     return al256(st) * 2 + al256(batch * 2 * nseg * H * 4);
