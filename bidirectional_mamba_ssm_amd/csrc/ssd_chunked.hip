@@ -91,27 +91,6 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ size_t tok(const SegArgs &a, int b, int t) { return (size_t)b * a.L + t; }
 __device__ __forceinline__ u32x4 ld8(const uint16_t *p) { return *(const u32x4 *)p; }
 
-// inclusive prefix sum over the block's 256 threads; *total = sum; two barriers
-__device__ float block_scan(float v, float *tmp, float *total) {
-    const int lane = lane_id(), w = wave_id();
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float n = __shfl_up(v, off, 64);
-        if (lane >= off) v += n;
-    }
-    if (lane == 63) tmp[w] = v;
-    __syncthreads();
-    float add = 0.f, tot = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float t = tmp[k];
-        if (k < w) add += t;
-        tot += t;
-    }
-    __syncthreads();
-    *total = tot;
-    return v + add;
-}
 __device__ __forceinline__ float wave_scan(float v) {
     const int lane = lane_id();
 #pragma unroll
@@ -126,11 +105,11 @@ __device__ __forceinline__ float wave_scan(float v) {
 // x of COUNT tokens (rows row0 + t, zero for t >= tlimit) of head h, raw bf16,
 // transposed into xt[p][t] (row stride xrs). Consecutive lanes read
 // consecutive 16-byte column groups of a token row. No barrier.
-template <int COUNT>
+template <int COUNT, int NT>
 __device__ __forceinline__ void stage_xt(const SegArgs &a, const uint16_t *X, int b, int h,
                                          int row0, int tlimit, uint32_t *xt, int xrs) {
     constexpr int ITEMS = (COUNT / 2) * (kP / 8);
-    for (int item = threadIdx.x; item < ITEMS; item += kThreads) {
+    for (int item = threadIdx.x; item < ITEMS; item += NT) {
         const int rp = item >> 3, cg = item & 7;
         const int t = 2 * rp;
         u32x4 r0 = {0u, 0u, 0u, 0u}, r1 = {0u, 0u, 0u, 0u};
@@ -146,9 +125,10 @@ __device__ __forceinline__ void stage_xt(const SegArgs &a, const uint16_t *X, in
 
 // 64 token rows [t0, t0+64) (zero for t >= tlimit) of a [t][G][N] bf16
 // tensor, raw, into dst[row][n] (row stride kNRS). No barrier.
+template <int NT>
 __device__ __forceinline__ void stage_rows(const SegArgs &a, const uint16_t *M, int b, int grp,
                                            int row0, int t0, int tlimit, uint32_t *dst) {
-    for (int item = threadIdx.x; item < 64 * (kN / 8); item += kThreads) {
+    for (int item = threadIdx.x; item < 64 * (kN / 8); item += NT) {
         const int row = item >> 4, cg = item & 15;
         const int t = t0 + row;
         u32x4 v = {0u, 0u, 0u, 0u};
@@ -245,7 +225,7 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
         if (run < kDead) break;
         if (a.seq && a.seq[tok(a, b, d == 0 ? s1 - 1 : s0)] != edge_seq) break;
         stage_bt(a, Bm, b, grp, 0, s0, s1, sm.bt);
-        stage_xt<kSub>(a, X, b, h, s0, n, sm.xt, kRS);
+        stage_xt<kSub, kThreads>(a, X, b, h, s0, n, sm.xt, kRS);
         if (w == 0) {
             // lane 0 is the token nearest the outgoing edge
             const bool in = lane < n;
@@ -315,85 +295,112 @@ __global__ void __launch_bounds__(256) k_seg_scan(const SegArgs a) {
 }
 
 // ------------------------------------------------------------- k_seg_out
-constexpr int kTileU32 = (kN * kRS > 64 * kNRS ? kN * kRS : 64 * kNRS) / 2;
+// 8 waves: two per SIMD, so one wave's VALU and LDS work overlaps another's
+// matrix-core work and waits.
+constexpr int kOutWaves = 8;
+constexpr int kOutThreads = 64 * kOutWaves;
 
 template <int Q>
 struct OutSmem {
-    static constexpr bool kBnLds = Q <= 128;    // B of the whole chunk kept in LDS
-    float cs2[Q];          // inclusive scan in the walking direction, times log2(e)
-    float u[Q];            // e^{cs}, 0 where the carried state does not reach
+    float cs2[Q];          // inclusive scan of a in the walking direction, times log2(e)
     float w[Q];            // state-update weights
     float v16[Q];          // e^{cs(edge of the token's 16-tile) - cs} dt
     float v64[Q];          // e^{cs(edge of the token's 64-block) - cs} dt
-    float a[Q];
     float dt[Q];
-    int sq[Q];
-    float tmp[4];
-    int utile[Q / 16];     // any nonzero u in the 16-row tile
-    int wsub[Q / kSub];    // any nonzero weight in the 64-token sub-block
-    float gamma;
-    alignas(16) uint32_t xt[kP * (Q + 8) / 2];            // X^T [p][t], raw bf16
-    alignas(16) uint32_t bn[kBnLds ? Q * kNRS / 2 : 4];   // B [t][n] of the chunk, raw bf16
-    alignas(16) uint32_t tile[kTileU32];                  // C [64][n] of a row block / B^T [n][64]
-    alignas(16) uint32_t hth[kP * kNRS / 2];              // H^T [p][n], bf16 high part
-    alignas(16) uint32_t htl[kP * kNRS / 2];              // H^T [p][n], bf16 residual
+    int sq[Q];             // sequence index (packed) of each token
+    float tmp[kOutWaves];
+    int utile[Q / 16];     // the carried state reaches some row of the 16-row tile
+    int wsub[Q / kSub];    // some weight of the 64-token sub-block is nonzero
+    float gamma;           // decay of the whole chunk (0: the state does not pass)
+    int sq_nb;             // sequence index of the token the carried state comes from
+    alignas(16) uint32_t xt[kP * (Q + 8) / 2];   // X^T [p][t], raw bf16
+    alignas(16) uint32_t bn[Q * kNRS / 2];       // B [t][n], raw bf16
+    // H^T [p][n] as bf16 high part, then bf16 residual; during the state
+    // update: B^T [n][64 tokens] of one sub-block
+    alignas(16) uint32_t hs[kP * kNRS];
 };
+static_assert(kN * kRS / 2 <= kP * kNRS, "B^T tile must fit the state area");
 
 // One chunk [c0, c0+len) of direction d: scans, decay factors, weights,
-// masks; x (and B) staged.
+// skip masks; x and B staged. Threads 0-255 scan a in the walking direction,
+// threads 256-511 toward the outgoing edge, at the same time.
 template <int Q>
 __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h, int grp, int c0,
                            int len) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+    const int g = tid >> 8, t = tid & 255, wq = wv & 3;
     const DirPtrs &dp = a.dir[d];
     const uint16_t *DT = (const uint16_t *)dp.dt;
     const float Ah = dp.A[h];
-    // stage first: these loads overlap the scans below
-    stage_xt<Q>(a, (const uint16_t *)dp.x, b, h, c0, len, sm.xt, Q + 8);
-    if (OutSmem<Q>::kBnLds)
-        for (int sb = 0; sb < Q / kSub; ++sb)
-            stage_rows(a, (const uint16_t *)dp.B, b, grp, c0, kSub * sb, len,
-                       sm.bn + (kSub * sb * kNRS) / 2);
-    // (1) inclusive scan in the walking direction
-    const int iw = d == 0 ? tid : Q - 1 - tid;
-    float at = 0.f, dtt = 0.f;
+    // staging loads first: they overlap the scans below
+    stage_xt<Q, kOutThreads>(a, (const uint16_t *)dp.x, b, h, c0, len, sm.xt, Q + 8);
+    for (int sb = 0; sb < Q / kSub; ++sb)
+        stage_rows<kOutThreads>(a, (const uint16_t *)dp.B, b, grp, c0, kSub * sb, len,
+                                sm.bn + (kSub * sb * kNRS) / 2);
+    // group 0: position in the walking direction; group 1: toward the edge
+    const int pos = (g == 0) == (d == 0) ? t : Q - 1 - t;
+    const bool in = t < Q && pos < len;
+    float dtt = 0.f, at = 0.f;
     int sq = 0;
-    if (tid < Q && iw < len) {
-        dtt = bf2f(DT[tok(a, b, c0 + iw) * a.H + h]);
+    if (in) {
+        dtt = bf2f(DT[tok(a, b, c0 + pos) * a.H + h]);
         at = dtt * Ah;
-        if (a.seq) sq = a.seq[tok(a, b, c0 + iw)];
+        if (a.seq) sq = a.seq[tok(a, b, c0 + pos)];
     }
-    float total;
-    const float cs = block_scan(tid < Q ? at : 0.f, sm.tmp, &total);
-    if (tid < Q) {
-        sm.cs2[iw] = cs * kLog2e;
-        sm.dt[iw] = dtt;
-        sm.a[iw] = at;
-        sm.sq[iw] = sq;
-        bool off_ok = iw < len;
-        if (a.seq && iw < len) {
-            const int nb = d == 0 ? c0 - 1 : c0 + len;
-            const bool has_nb = d == 0 ? c0 > 0 : c0 + len < a.L;
-            off_ok = has_nb && a.seq[tok(a, b, nb)] == sq;
-        }
-        sm.u[iw] = off_ok ? expf(cs) : 0.f;
+    float v = wave_scan(at);
+    if (lane == 63) sm.tmp[wv] = v;
+    int sq_nb = 0, sq_edge = 0;
+    bool has_nb = true;
+    if (a.seq) {
+        const int nb = d == 0 ? c0 - 1 : c0 + len;
+        has_nb = d == 0 ? c0 > 0 : c0 + len < a.L;
+        sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
+        sq_edge = a.seq[tok(a, b, d == 0 ? c0 + len - 1 : c0)];
     }
     __syncthreads();
-    // (2) exclusive sums toward the outgoing edge -> state weights; decay of
-    // each token to the near edge of its 16-tile and of its 64-block
-    const int ie = d == 0 ? Q - 1 - tid : tid;
-    const float ae = (tid < Q && ie < len) ? sm.a[ie] : 0.f;
-    float tot2;
-    const float incl = block_scan(tid < Q ? ae : 0.f, sm.tmp, &tot2);
-    if (tid < Q) {
-        float wt = 0.f;
-        if (ie < len) {
-            const int edge = d == 0 ? len - 1 : 0;
-            if (!a.seq || sm.sq[ie] == sm.sq[edge]) wt = expf(incl - ae) * sm.dt[ie];
+    float add = 0.f, total = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float s = sm.tmp[4 * g + k];
+        if (k < wq) add += s;
+        total += s;
+    }
+    v += add;
+    if (g == 0) {
+        bool reach = false;
+        if (t < Q) {
+            sm.cs2[pos] = v * kLog2e;
+            sm.dt[pos] = dtt;
+            sm.sq[pos] = sq;
+            reach = in && (!a.seq || sq == sq_nb) && v >= kDead;
         }
-        sm.w[ie] = wt;
-        // the edge nearest the diagonal of a column tile: its last token
-        // (forward, j <= i) or its first (reverse, j >= i)
+        const unsigned long long m = __ballot(reach);
+        if (lane == 0 && 64 * wq < Q) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int tile = d == 0 ? 4 * wq + k : Q / 16 - 1 - 4 * wq - k;
+                sm.utile[tile] = ((m >> (16 * k)) & 0xffffull) != 0;
+            }
+        }
+        if (tid == 0) {
+            bool carry = true;
+            if (a.seq) carry = has_nb && sq_nb == sq_edge;
+            sm.gamma = carry ? expf(total) : 0.f;
+            sm.sq_nb = a.seq ? sq_nb : 0;
+        }
+    } else {
+        // exclusive sum toward the outgoing edge -> weight of the token in the
+        // state leaving the chunk
+        float wt = 0.f;
+        if (in && (!a.seq || sq == sq_edge)) wt = expf(v - at) * dtt;
+        if (t < Q) sm.w[pos] = wt;
+        const unsigned long long m = __ballot(wt != 0.f);
+        if (lane == 0 && 64 * wq < Q) sm.wsub[d == 0 ? Q / 64 - 1 - wq : wq] = m != 0ull;
+    }
+    __syncthreads();
+    if (tid < Q) {
+        // decay of each token to the edge of its 16-tile / 64-block nearest
+        // the diagonal: its last token (forward, j <= i) or first (reverse)
         const int j = tid;
         const int r16 = d == 0 ? (j | 15) : (j & ~15);
         const int r64 = d == 0 ? (j | 63) : (j & ~63);
@@ -401,62 +408,63 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
         sm.v16[j] = exp2_(sm.cs2[r16] - c) * sm.dt[j];
         sm.v64[j] = exp2_(sm.cs2[r64] - c) * sm.dt[j];
     }
-    if (tid == 0) {
-        bool carry = true;
-        if (a.seq) {
-            if (d == 0 && c0 > 0) carry = a.seq[tok(a, b, c0 - 1)] == a.seq[tok(a, b, c0 + len - 1)];
-            if (d == 1 && c0 + len < a.L) carry = a.seq[tok(a, b, c0 + len)] == a.seq[tok(a, b, c0)];
-        }
-        sm.gamma = carry ? expf(total) : 0.f;
-    }
-    __syncthreads();
-    if (tid < Q / 16) {
-        int any = 0;
-        for (int r = 0; r < 16; ++r) any |= sm.u[16 * tid + r] != 0.f;
-        sm.utile[tid] = any;
-    }
-    if (tid >= 64 && tid < 64 + Q / kSub) {
-        const int sb = tid - 64;
-        int any = 0;
-        for (int r = 0; r < kSub; ++r) any |= sm.w[kSub * sb + r] != 0.f;
-        sm.wsub[sb] = any;
-    }
     __syncthreads();
 }
 
-// Writes the wave's 16 state columns (fp32 accumulators) into H^T hi / lo.
+// The wave's state block (p-tile w%4, n-half w/4; fp32 accumulators) into
+// H^T hi / lo.
 template <int Q>
-__device__ void publish_state(OutSmem<Q> &sm, const f32x4 (&Hacc)[kN / 16]) {
+__device__ void publish_state(OutSmem<Q> &sm, const f32x4 (&Hacc)[4]) {
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
-    uint16_t *hh = (uint16_t *)sm.hth;
-    uint16_t *hl = (uint16_t *)sm.htl;
+    const int pq = w & 3, nh = w >> 2;
+    uint16_t *hh = (uint16_t *)sm.hs;
+    uint16_t *hl = hh + kP * kNRS;
 #pragma unroll
-    for (int nt = 0; nt < kN / 16; ++nt) {
+    for (int q = 0; q < 4; ++q) {
         uint32_t a0, a1, b0, b1;
-        split2(Hacc[nt][0], Hacc[nt][1], a0, b0);
-        split2(Hacc[nt][2], Hacc[nt][3], a1, b1);
-        const int o = (16 * w + l16) * kNRS + 16 * nt + 4 * g4;
+        split2(Hacc[q][0], Hacc[q][1], a0, b0);
+        split2(Hacc[q][2], Hacc[q][3], a1, b1);
+        const int o = (16 * pq + l16) * kNRS + 64 * nh + 16 * q + 4 * g4;
         *(u32x2 *)(hh + o) = u32x2{a0, a1};
         *(u32x2 *)(hl + o) = u32x2{b0, b1};
     }
 }
 
-// Row block I (64 rows) of the chunk: intra-chunk form, carried state, skip
-// term, output. Wave w owns rows 64I + 16w .. +15 and all 64 columns.
+// Row tile `it` (16 rows) of the chunk: intra-chunk form, carried state, skip
+// term, output, by one wave alone (no barrier). C of the tile lives in
+// registers in the layout that serves both as the B operand of the Gram tiles
+// and as the A operand of the carried-state product.
 template <int Q>
-__device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h, int grp,
-                          int c0, int len, int I, bool has_state, float Dh, bool add) {
-    const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
+__device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, int h, int grp,
+                         int c0, int len, int it, bool has_state, float Dh, bool add) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
     const DirPtrs &dp = a.dir[d];
-    stage_rows(a, (const uint16_t *)dp.C, b, grp, c0, 64 * I, len, sm.tile);
-    __syncthreads();
-    const uint16_t *ct = (const uint16_t *)sm.tile;
     const uint16_t *xt = (const uint16_t *)sm.xt;
-    const uint16_t *Bg = (const uint16_t *)dp.B;
+    const uint16_t *bn = (const uint16_t *)sm.bn;
     constexpr int XRS = Q + 8;
-    const int it = 4 * I + w;               // this wave's 16-row tile
-    const int i = 16 * it + l16;            // this lane's row (A operand / G^T column)
+    const int I = it >> 2, wq = it & 3;   // 64-row block, tile inside it
+    const int i = 16 * it + l16;          // this lane's row (G^T column)
     const bool row_ok = i < len;
+    const int i0 = 16 * it + 4 * g4;      // first of this lane's output rows
+    u32x4 cr[kN / 32];
+    {
+        const uint16_t *cp = (const uint16_t *)dp.C +
+                             (tok(a, b, c0 + min(i, len - 1)) * a.G + grp) * kN + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < kN / 32; ++ks) cr[ks] = ld8(cp + 32 * ks);
+    }
+    float *yrow[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        yrow[r] = a.y + (tok(a, b, c0 + min(i0 + r, len - 1)) * a.H + h) * kP + l16;
+    float prev[4][4];
+    if (add) {
+        // the reverse pass wrote these rows; fetched now, used at the end
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) prev[pt][r] = yrow[r][16 * pt];
+    }
     const float csi = sm.cs2[i];
     const int sqi = sm.sq[i];
     f32x4 acc[4];
@@ -465,122 +473,117 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
 
     // ---- intra-chunk: sum over column blocks J of M[i][j] x_j
     const int Jlo = d == 0 ? 0 : I, Jhi = d == 0 ? I : Q / 64 - 1;
-    if (16 * it < len) {
-        for (int J = Jlo; J <= Jhi; ++J) {
-            if (64 * J >= len) break;
-            if (J != I) {
-                const float near = d == 0 ? sm.cs2[64 * I] - sm.cs2[64 * J + 63]
-                                          : sm.cs2[64 * I + 63] - sm.cs2[64 * J];
-                if (near < kDead * kLog2e) continue;
-            }
-            const int r64 = d == 0 ? 64 * J + 63 : 64 * J;
-            const float u64 = exp2_(csi - sm.cs2[r64]);
-            u32x4 mhi[2], mlo[2];
+    for (int J = Jlo; J <= Jhi; ++J) {
+        if (64 * J >= len) break;
+        if (J != I) {
+            const float near = d == 0 ? sm.cs2[64 * I] - sm.cs2[64 * J + 63]
+                                      : sm.cs2[64 * I + 63] - sm.cs2[64 * J];
+            if (near < kDead * kLog2e) continue;   // every entry is exactly 0
+        }
+        const int r64 = d == 0 ? 64 * J + 63 : 64 * J;
+        const float u64 = exp2_(csi - sm.cs2[r64]);
+        u32x4 mhi[2], mlo[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                uint32_t ph[4], pl[4];
+        for (int kk = 0; kk < 2; ++kk) {
+            uint32_t ph[4], pl[4];
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int jt = 2 * kk + half;
-                    const int j0 = 64 * J + 16 * jt;
-                    // whole 16-column tile on the masked side of the diagonal
-                    const bool dead = J == I && (d == 0 ? jt > w : jt < w);
-                    float mv[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (!dead) {
-                        f32x4 g = zero4();
+            for (int half = 0; half < 2; ++half) {
+                const int jt = 2 * kk + half;
+                const int j0 = 64 * J + 16 * jt;
+                // the whole 16-column tile on the masked side of the diagonal
+                const bool dead = J == I && (d == 0 ? jt > wq : jt < wq);
+                float mv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (!dead) {
+                    f32x4 gg = zero4();
 #pragma unroll
-                        for (int ks = 0; ks < kN / 32; ++ks) {
-                            u32x4 aop;
-                            if (OutSmem<Q>::kBnLds) {
-                                aop = *(const u32x4 *)((const uint16_t *)sm.bn + (j0 + l16) * kNRS + 32 * ks + 8 * g4);
-                            } else {
-                                const int jr = min(j0 + l16, len - 1);
-                                aop = ld8(Bg + (tok(a, b, c0 + jr) * a.G + grp) * kN + 32 * ks + 8 * g4);
-                            }
-                            const u32x4 bop = *(const u32x4 *)(ct + (16 * w + l16) * kNRS + 32 * ks + 8 * g4);
-                            g = mfma16x16x32(aop, bop, g);
-                        }
-                        // g[r] = G[i][j], j = j0 + 4 g4 + r
-                        const int jb = j0 + 4 * g4;
-                        if (J != I) {
-                            const f32x4 vv = *(const f32x4 *)(sm.v64 + jb);
+                    for (int ks = 0; ks < kN / 32; ++ks) {
+                        const u32x4 aop = *(const u32x4 *)(bn + (j0 + l16) * kNRS + 32 * ks + 8 * g4);
+                        gg = mfma16x16x32(aop, cr[ks], gg);
+                    }
+                    // gg[r] = G[i][j], j = jb + r
+                    const int jb = j0 + 4 * g4;
+                    if (J != I) {
+                        const f32x4 vv = *(const f32x4 *)(sm.v64 + jb);
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) mv[r] = g[r] * u64 * vv[r];
-                        } else if (jt != w) {
-                            // another 16-tile of the diagonal block: factor the
-                            // decay through that tile's edge
-                            const int r16 = d == 0 ? j0 + 15 : j0;
-                            const float u16 = exp2_(csi - sm.cs2[r16]);
-                            const f32x4 vv = *(const f32x4 *)(sm.v16 + jb);
+                        for (int r = 0; r < 4; ++r) mv[r] = gg[r] * u64 * vv[r];
+                    } else if (jt != wq) {
+                        // another 16-tile of the diagonal block: factor the
+                        // decay through that tile's edge
+                        const int r16 = d == 0 ? j0 + 15 : j0;
+                        const float u16 = exp2_(csi - sm.cs2[r16]);
+                        const f32x4 vv = *(const f32x4 *)(sm.v16 + jb);
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) mv[r] = g[r] * u16 * vv[r];
-                        } else {
-                            // the diagonal 16x16 tile: one exponential per entry
+                        for (int r = 0; r < 4; ++r) mv[r] = gg[r] * u16 * vv[r];
+                    } else {
+                        // the diagonal 16x16 tile: one exponential per entry
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int j = jb + r;
-                                const bool tri = d == 0 ? j <= i : j >= i;
-                                mv[r] = tri ? g[r] * exp2_(csi - sm.cs2[j]) * sm.dt[j] : 0.f;
-                            }
-                        }
-                        if (!row_ok || jb + 3 >= len || a.seq) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int j = jb + r;
-                                bool ok = row_ok && j < len;
-                                if (a.seq) ok = ok && sm.sq[j] == sqi;
-                                if (!ok) mv[r] = 0.f;
-                            }
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = jb + r;
+                            const bool tri = d == 0 ? j <= i : j >= i;
+                            mv[r] = tri ? gg[r] * exp2_(csi - sm.cs2[j]) * sm.dt[j] : 0.f;
                         }
                     }
-                    split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
-                    split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
+                    if (!row_ok || jb + 3 >= len || a.seq) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = jb + r;
+                            bool ok = row_ok && j < len;
+                            if (a.seq) ok = ok && sm.sq[j] == sqi;
+                            if (!ok) mv[r] = 0.f;
+                        }
+                    }
                 }
-                mhi[kk] = u32x4{ph[0], ph[1], ph[2], ph[3]};
-                mlo[kk] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+                split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
+                split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
             }
+            mhi[kk] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+            mlo[kk] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+        }
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
+        for (int pt = 0; pt < 4; ++pt) {
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int jb = 64 * J + 32 * kk + 4 * g4;
-                    const uint16_t *xr = xt + (16 * pt + l16) * XRS;
-                    const u32x2 x0 = *(const u32x2 *)(xr + jb);
-                    const u32x2 x1 = *(const u32x2 *)(xr + jb + 16);
-                    const u32x4 xo = {x0[0], x0[1], x1[0], x1[1]};
-                    acc[pt] = mfma16x16x32(mhi[kk], xo, acc[pt]);
-                    acc[pt] = mfma16x16x32(mlo[kk], xo, acc[pt]);
-                }
+            for (int kk = 0; kk < 2; ++kk) {
+                const int jb = 64 * J + 32 * kk + 4 * g4;
+                const uint16_t *xr = xt + (16 * pt + l16) * XRS;
+                const u32x2 x0 = *(const u32x2 *)(xr + jb);
+                const u32x2 x1 = *(const u32x2 *)(xr + jb + 16);
+                const u32x4 xo = {x0[0], x0[1], x1[0], x1[1]};
+                acc[pt] = mfma16x16x32(mhi[kk], xo, acc[pt]);
+                acc[pt] = mfma16x16x32(mlo[kk], xo, acc[pt]);
             }
         }
     }
 
-    // ---- carried state: u_i * C_i . H (tiles whose u is all 0: skipped, exact)
+    // ---- carried state: e^{cs_i} C_i . H (tiles it does not reach: skipped, exact)
     if (has_state && sm.utile[it]) {
-        const uint16_t *hh = (const uint16_t *)sm.hth;
-        const uint16_t *hl = (const uint16_t *)sm.htl;
-        f32x4 t[4];
+        const uint16_t *hh = (const uint16_t *)sm.hs;
+        const uint16_t *hl = hh + kP * kNRS;
+        f32x4 tt[4];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) t[pt] = zero4();
+        for (int pt = 0; pt < 4; ++pt) tt[pt] = zero4();
 #pragma unroll
         for (int ks = 0; ks < kN / 32; ++ks) {
-            const u32x4 aop = *(const u32x4 *)(ct + (16 * w + l16) * kNRS + 32 * ks + 8 * g4);
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 const int o = (16 * pt + l16) * kNRS + 32 * ks + 8 * g4;
-                t[pt] = mfma16x16x32(aop, *(const u32x4 *)(hh + o), t[pt]);
-                t[pt] = mfma16x16x32(aop, *(const u32x4 *)(hl + o), t[pt]);
+                tt[pt] = mfma16x16x32(cr[ks], *(const u32x4 *)(hh + o), tt[pt]);
+                tt[pt] = mfma16x16x32(cr[ks], *(const u32x4 *)(hl + o), tt[pt]);
             }
         }
-        const f32x4 uu = *(const f32x4 *)(sm.u + 16 * it + 4 * g4);
+        float uu[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ii = i0 + r;
+            const bool reach = ii < len && (!a.seq || sm.sq[ii] == sm.sq_nb);
+            uu[r] = reach ? exp2_(sm.cs2[ii]) : 0.f;
+        }
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(uu[r], t[pt][r], acc[pt][r]);
+            for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(uu[r], tt[pt][r], acc[pt][r]);
     }
 
-    // ---- skip term (x exact) and output rows 16it + 4g4 + r
-    const int i0 = 16 * it + 4 * g4;
+    // ---- skip term (x exact) and output rows i0 + r
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
         const u32x2 xv = *(const u32x2 *)(xt + (16 * pt + l16) * XRS + i0);
@@ -589,18 +592,7 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
         acc[pt][2] = fmaf(Dh, b_lo(xv[1]), acc[pt][2]);
         acc[pt][3] = fmaf(Dh, b_hi(xv[1]), acc[pt][3]);
     }
-    float *yrow[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        yrow[r] = a.y + (tok(a, b, c0 + min(i0 + r, len - 1)) * a.H + h) * kP + l16;
     if (add) {
-        // the reverse pass wrote these rows: fetch all 16 values before any
-        // store so the loads overlap instead of forming a chain
-        float prev[4][4];
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) prev[pt][r] = yrow[r][16 * pt];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
@@ -611,45 +603,71 @@ __device__ void row_block(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h,
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (i0 + r < len) yrow[r][16 * pt] = acc[pt][r];
-    __syncthreads();   // the C tile is reused
+}
+
+// Row tiles of wave w: pairs whose column counts add up to the same total,
+// and the two waves of a SIMD (w, w+4) get equal shares.
+template <int Q>
+__device__ __forceinline__ int tile_of(int w, int k) {
+    if (Q == 256) return k == 0 ? w : 15 - w;
+    if (Q == 128) return k == 0 ? (w < 4 ? w : 11 - w) : -1;
+    return k == 0 && w < 4 ? w : -1;
 }
 
 // H <- gamma H + sum over the chunk's tokens of w_t B_t x_t^T (the wave's
-// 16 columns).
+// block of the state).
 template <int Q>
-__device__ void chunk_state_update(const SegArgs &a, OutSmem<Q> &sm, f32x4 (&Hacc)[kN / 16],
-                                   const uint16_t *Bm, int b, int grp, int c0, int len) {
+__device__ void chunk_state_update(OutSmem<Q> &sm, f32x4 (&Hacc)[4], int len) {
+    const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
+    const int pq = w & 3, nh = w >> 2;
     const float gmm = sm.gamma;
 #pragma unroll
-    for (int nt = 0; nt < kN / 16; ++nt) Hacc[nt] *= gmm;
+    for (int q = 0; q < 4; ++q) Hacc[q] *= gmm;
+    const uint16_t *bn = (const uint16_t *)sm.bn;
+    const uint16_t *bt = (const uint16_t *)sm.hs;
+    const uint16_t *xt = (const uint16_t *)sm.xt;
     for (int sb = 0; sb < Q / kSub; ++sb) {
         if (kSub * sb >= len) break;
         if (!sm.wsub[sb]) continue;    // every weight is exactly 0
-        if (OutSmem<Q>::kBnLds) {
-            // B^T transposed inside LDS from the staged B
-            const uint16_t *bn = (const uint16_t *)sm.bn;
-            for (int item = threadIdx.x; item < 32 * (kN / 8); item += kThreads) {
-                const int rp = item & 31, cg = item >> 5;
-                const int t = kSub * sb + 2 * rp;
-                const u32x4 r0 = *(const u32x4 *)(bn + t * kNRS + 8 * cg);
-                const u32x4 r1 = *(const u32x4 *)(bn + (t + 1) * kNRS + 8 * cg);
+        {
+            // B^T of the sub-block, transposed inside LDS: one item per thread
+            const int item = threadIdx.x;
+            const int rp = item & 31, cg = item >> 5;
+            const int t = kSub * sb + 2 * rp;
+            const u32x4 r0 = *(const u32x4 *)(bn + t * kNRS + 8 * cg);
+            const u32x4 r1 = *(const u32x4 *)(bn + (t + 1) * kNRS + 8 * cg);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    sm.tile[((8 * cg + 2 * q) * kRS) / 2 + rp] = (r0[q] & 0xffffu) | (r1[q] << 16);
-                    sm.tile[((8 * cg + 2 * q + 1) * kRS) / 2 + rp] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
-                }
+            for (int q = 0; q < 4; ++q) {
+                sm.hs[((8 * cg + 2 * q) * kRS) / 2 + rp] = (r0[q] & 0xffffu) | (r1[q] << 16);
+                sm.hs[((8 * cg + 2 * q + 1) * kRS) / 2 + rp] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
             }
-        } else {
-            stage_bt(a, Bm, b, grp, c0, kSub * sb, len, sm.tile);
         }
         __syncthreads();
-        state_mfma(Hacc, sm.tile, (const uint16_t *)sm.xt, Q + 8, kSub * sb, sm.w + kSub * sb);
+#pragma unroll
+        for (int ks = 0; ks < kSub / 32; ++ks) {
+            const int tk = 32 * ks + 8 * g4;
+            const u32x4 xv = *(const u32x4 *)(xt + (16 * pq + l16) * (Q + 8) + kSub * sb + tk);
+            const f32x4 w0 = *(const f32x4 *)(sm.w + kSub * sb + tk);
+            const f32x4 w1 = *(const f32x4 *)(sm.w + kSub * sb + tk + 4);
+            uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+            split2(b_lo(xv[0]) * w0[0], b_hi(xv[0]) * w0[1], h0, l0);
+            split2(b_lo(xv[1]) * w0[2], b_hi(xv[1]) * w0[3], h1, l1);
+            split2(b_lo(xv[2]) * w1[0], b_hi(xv[2]) * w1[1], h2, l2);
+            split2(b_lo(xv[3]) * w1[2], b_hi(xv[3]) * w1[3], h3, l3);
+            const u32x4 bhi = {h0, h1, h2, h3}, blo = {l0, l1, l2, l3};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 aop = *(const u32x4 *)(bt + (16 * (4 * nh + q) + l16) * kRS + tk);
+                Hacc[q] = mfma16x16x32(aop, bhi, Hacc[q]);
+                Hacc[q] = mfma16x16x32(aop, blo, Hacc[q]);
+            }
+        }
         __syncthreads();
     }
 }
 
 template <int Q>
-__global__ void __launch_bounds__(kThreads) k_seg_out(const SegArgs a) {
+__global__ void __launch_bounds__(kOutThreads) k_seg_out(const SegArgs a) {
     // XCD-aware order: consecutive workgroups go to different XCDs
     // (round-robin by 8), so the 8 streams of work that share one XCD's L2 are
     // made to hold the same (row, segment) and share its B and C.
@@ -663,16 +681,17 @@ __global__ void __launch_bounds__(kThreads) k_seg_out(const SegArgs a) {
     const int t0 = seg * a.Ts, t1 = min(t0 + a.Ts, a.L);
     const int cfirst = t0 / Q, clast = (t1 - 1) / Q;
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
+    const int pq = w & 3, nh = w >> 2;
     __shared__ __attribute__((aligned(16))) OutSmem<Q> sm;
     const size_t PN = (size_t)kP * kN;
     auto slot = [&](int d, int k) { return (((size_t)b * 2 + d) * a.nseg + k) * a.H + h; };
+    const int hoff = (16 * pq + l16) * kN + 64 * nh + 4 * g4;   // + 16 q: this lane's state entries
 
     for (int pass = 0; pass < a.ndir; ++pass) {
         const int d = a.ndir == 2 ? 1 - pass : 0;   // reverse first, then forward adds
         const DirPtrs &dp = a.dir[d];
         const float Dh = dp.D ? dp.D[h] : 0.f;
         // incoming state of this segment in the walking direction
-        f32x4 Hacc[kN / 16];
         const float *src = nullptr;
         if (d == 0) {
             if (seg == 0) src = a.init_state ? a.init_state + ((size_t)b * a.H + h) * PN : nullptr;
@@ -681,26 +700,29 @@ __global__ void __launch_bounds__(kThreads) k_seg_out(const SegArgs a) {
             if (seg == a.nseg - 1) src = nullptr;
             else src = a.gam[slot(1, seg + 1)] == 0.f ? a.S + slot(1, seg + 1) * PN : a.Hs + slot(1, seg) * PN;
         }
+        f32x4 Hacc[4];
 #pragma unroll
-        for (int nt = 0; nt < kN / 16; ++nt)
-            Hacc[nt] = src ? *(const f32x4 *)(src + (16 * w + l16) * kN + 16 * nt + 4 * g4) : zero4();
+        for (int q = 0; q < 4; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
         bool has_state = src != nullptr;
         if (has_state) publish_state<Q>(sm, Hacc);
 
         const int nch = clast - cfirst + 1;
+        const bool want_final = d == 0 && seg == a.nseg - 1 && a.final_state;
         for (int s = 0; s < nch; ++s) {
             const int c = d == 0 ? cfirst + s : clast - s;
             const int c0 = c * Q;
             const int len = min(Q, a.L - c0);
             chunk_prep<Q>(a, sm, d, b, h, grp, c0, len);
-            for (int I = 0; I < Q / 64; ++I) {
-                if (64 * I >= len) break;
-                row_block<Q>(a, sm, d, b, h, grp, c0, len, I, has_state, Dh, d == 0 && a.ndir == 2);
+#pragma unroll 1
+            for (int k = 0; k < 2; ++k) {
+                const int it = tile_of<Q>(w, k);
+                if (it >= 0 && 16 * it < len)
+                    row_tile<Q>(a, sm, d, b, h, grp, c0, len, it, has_state, Dh, d == 0 && a.ndir == 2);
             }
             const bool last = s == nch - 1;
-            const bool want_final = d == 0 && seg == a.nseg - 1 && a.final_state;
             if (!last || want_final) {
-                chunk_state_update<Q>(a, sm, Hacc, (const uint16_t *)dp.B, b, grp, c0, len);
+                __syncthreads();   // row tiles are done with the state area
+                chunk_state_update<Q>(sm, Hacc, len);
                 if (!last) {
                     publish_state<Q>(sm, Hacc);
                     has_state = true;
@@ -708,11 +730,10 @@ __global__ void __launch_bounds__(kThreads) k_seg_out(const SegArgs a) {
             }
             __syncthreads();
         }
-        if (d == 0 && seg == a.nseg - 1 && a.final_state) {
+        if (want_final) {
             float *fs = a.final_state + ((size_t)b * a.H + h) * PN;
 #pragma unroll
-            for (int nt = 0; nt < kN / 16; ++nt)
-                *(f32x4 *)(fs + (16 * w + l16) * kN + 16 * nt + 4 * g4) = Hacc[nt];
+            for (int q = 0; q < 4; ++q) *(f32x4 *)(fs + hoff + 16 * q) = Hacc[q];
         }
     }
 }
@@ -733,7 +754,7 @@ hipError_t launch_q(const SegArgs &a, hipStream_t s) {
                   s, a);
     }
     const int groups = (a.batch * a.nseg + 7) / 8;
-    BM_LAUNCH("ssd_seg_out", k_seg_out<Q>, dim3(groups * 8 * a.H), dim3(kThreads), 0, s, a);
+    BM_LAUNCH("ssd_seg_out", k_seg_out<Q>, dim3(groups * 8 * a.H), dim3(kOutThreads), 0, s, a);
     return hipGetLastError();
 }
 
