@@ -15,22 +15,23 @@
 //         + D x_i
 //   H    <- e^{cs_end} H + sum_j e^{sum_{k>j} a_k} dt_j B_j x_j^T
 //
-// Kernels (one workgroup = 4 waves):
-//   k_seg_state  each segment's (Ts tokens) outgoing state from a zero state,
-//                walking away from the outgoing edge and stopping where every
-//                remaining weight is exactly 0.0f in fp32 (e^x underflows)
+// Kernels:
+//   k_seg_state  (4 waves) each segment's (Ts tokens) outgoing state from a
+//                zero state, walking away from the outgoing edge and stopping
+//                where every remaining weight is exactly 0.0f in fp32
 //   k_seg_scan   incoming state of each segment where a chain carries over;
 //                where a segment's carry factor is 0 the next segment's
 //                incoming state is just the previous segment's local state
-//   k_seg_out    per (row, segment, head): the reverse direction walks the
-//                segment's chunks right to left writing its part of y, the
-//                forward direction walks left to right and adds its part.
-//                Per chunk x, B (and per 64-row block C) are staged raw in LDS;
-//                wave w computes rows 16w..16w+15 of a row block: the Gram
-//                tiles G^T = B C^T (their accumulator layout is directly the A
+//   k_seg_out    (8 waves, two per SIMD) per (row, segment, head): the reverse
+//                direction walks the segment's chunks right to left writing
+//                its part of y, the forward direction walks left to right and
+//                adds its part. Per chunk, x and B are staged raw in LDS; each
+//                wave then owns whole 16-row tiles with C in registers: Gram
+//                tiles G^T = B C^T (whose accumulator layout is directly the A
 //                operand of the next product), the masked decay, M.x, the
-//                carried-state term and D x. The state update runs with wave
-//                w owning state columns 16w..16w+15 as MFMA accumulators.
+//                carried-state term and D x, with no barrier. The state update
+//                runs with each wave owning a 16 x 64 block of H as MFMA
+//                accumulators.
 //
 // Everything runs on v_mfma_f32_16x16x32_bf16. x, B, C are bf16 already and
 // enter exactly. An operand that has to be rounded (the masked decayed Gram
@@ -53,9 +54,9 @@ namespace {
 
 constexpr int kP = 64;         // headdim handled here
 constexpr int kN = 128;        // d_state handled here
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kSub = 64;       // tokens per staged sub-block
-constexpr int kRS = kSub + 8;  // LDS row stride (16-bit elements) of [n][64 tokens] tiles
+constexpr int kThreads = 256;  // k_seg_state: 4 waves
+constexpr int kSub = 64;       // tokens per state-update sub-block
+constexpr int kRS = kSub + 8;  // LDS row stride (16-bit elements) of B^T [n][64 tokens] tiles
 constexpr int kNRS = kN + 8;   // LDS row stride (16-bit elements) of [row][n] tiles
 constexpr float kDead = -110.f;  // expf(x) is exactly 0.0f for every x < kDead
 constexpr float kLog2e = 1.4426950408889634f;
@@ -73,6 +74,21 @@ __device__ __forceinline__ void split2(float v0, float v1, uint32_t &hi, uint32_
 __device__ __forceinline__ float b_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float b_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Token order inside the LDS tiles of x^T and B^T: within each 32-token
+// block, tokens 4g+r and 16+4g+r (g, r < 4) sit side by side at positions
+// 8g+r and 8g+4+r. That is the k order in which a pair of Gram accumulator
+// tiles feeds the next product, so every operand read is one 16-byte load.
+__device__ __forceinline__ int tperm(int t) {
+    return (t & ~31) | ((t & 12) << 1) | ((t & 16) >> 2) | (t & 3);
+}
+// x^T rows also rotate their 16-byte groups (XOR with a function of the row),
+// so the transposing staging writes and the operand reads both spread over
+// all LDS banks. s: a permuted position; the 8 positions of its group stay
+// contiguous. Rows need at least 64 positions.
+__device__ __forceinline__ int xt_at(int p, int s, int xrs) {
+    return p * xrs + ((((s >> 3) ^ ((p ^ (p >> 3)) & 7)) << 3) | (s & 7));
+}
 
 struct SegArgs {
     DirPtrs dir[2];
@@ -102,92 +118,138 @@ __device__ __forceinline__ float wave_scan(float v) {
 }
 
 // --------------------------------------------------------- staging helpers
-// x of COUNT tokens (rows row0 + t, zero for t >= tlimit) of head h, raw bf16,
-// transposed into xt[p][t] (row stride xrs). Consecutive lanes read
-// consecutive 16-byte column groups of a token row. No barrier.
+// Every helper issues all of its global loads before its first LDS write so
+// that the loads overlap; rows past `tlimit` are loaded clamped and zeroed.
+
+// x^T: COUNT tokens of one head (x0 = the first token's row, tstride
+// elements between tokens), transposed into xt (permuted, rotated; row
+// stride xrs). Consecutive lanes read consecutive 16-byte groups of a row.
 template <int COUNT, int NT>
-__device__ __forceinline__ void stage_xt(const SegArgs &a, const uint16_t *X, int b, int h,
-                                         int row0, int tlimit, uint32_t *xt, int xrs) {
-    constexpr int ITEMS = (COUNT / 2) * (kP / 8);
-    for (int item = threadIdx.x; item < ITEMS; item += NT) {
-        const int rp = item >> 3, cg = item & 7;
-        const int t = 2 * rp;
-        u32x4 r0 = {0u, 0u, 0u, 0u}, r1 = {0u, 0u, 0u, 0u};
-        if (t < tlimit) r0 = ld8(X + (tok(a, b, row0 + t) * a.H + h) * kP + 8 * cg);
-        if (t + 1 < tlimit) r1 = ld8(X + (tok(a, b, row0 + t + 1) * a.H + h) * kP + 8 * cg);
+struct XStage {
+    static constexpr int ITEMS = (COUNT / 2) * (kP / 8);
+    static constexpr int PER = (ITEMS + NT - 1) / NT;
+    u32x4 r0[PER], r1[PER];
+    __device__ __forceinline__ void load(const uint16_t *x0, uint32_t tstride, int tlimit) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            xt[((8 * cg + 2 * q) * xrs) / 2 + rp] = (r0[q] & 0xffffu) | (r1[q] << 16);
-            xt[((8 * cg + 2 * q + 1) * xrs) / 2 + rp] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
+        for (int k = 0; k < PER; ++k) {
+            const int item = threadIdx.x + k * NT;
+            if (ITEMS % NT == 0 || item < ITEMS) {
+                const int t = 2 * (item >> 3), cg = item & 7;
+                r0[k] = ld8(x0 + (uint32_t)min(t, tlimit - 1) * tstride + 8 * cg);
+                r1[k] = ld8(x0 + (uint32_t)min(t + 1, tlimit - 1) * tstride + 8 * cg);
+            }
         }
     }
-}
+    __device__ __forceinline__ void store(int tlimit, uint32_t *xt, int xrs) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int item = threadIdx.x + k * NT;
+            if (ITEMS % NT == 0 || item < ITEMS) {
+                const int t = 2 * (item >> 3), cg = item & 7;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                const u32x4 a0 = t < tlimit ? r0[k] : z;
+                const u32x4 a1 = t + 1 < tlimit ? r1[k] : z;
+                const int s = tperm(t);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int p = 8 * cg + 2 * q;
+                    xt[xt_at(p, s, xrs) >> 1] = (a0[q] & 0xffffu) | (a1[q] << 16);
+                    xt[xt_at(p + 1, s, xrs) >> 1] = (a0[q] >> 16) | (a1[q] & 0xffff0000u);
+                }
+            }
+        }
+    }
+};
 
-// 64 token rows [t0, t0+64) (zero for t >= tlimit) of a [t][G][N] bf16
-// tensor, raw, into dst[row][n] (row stride kNRS). No barrier.
+// ROWS rows of a [t][n] bf16 tensor (m0 = the first row, rstride elements
+// between rows), raw, into dst[row][n] (row stride kNRS).
+template <int ROWS, int NT>
+struct RowStage {
+    static constexpr int ITEMS = ROWS * (kN / 8);
+    static constexpr int PER = (ITEMS + NT - 1) / NT;
+    u32x4 v[PER];
+    __device__ __forceinline__ void load(const uint16_t *m0, uint32_t rstride, int tlimit) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int item = threadIdx.x + k * NT;
+            if (ITEMS % NT == 0 || item < ITEMS) {
+                const int row = item >> 4, cg = item & 15;
+                v[k] = ld8(m0 + (uint32_t)min(row, tlimit - 1) * rstride + 8 * cg);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(int tlimit, uint32_t *dst) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int item = threadIdx.x + k * NT;
+            if (ITEMS % NT == 0 || item < ITEMS) {
+                const int row = item >> 4, cg = item & 15;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                *(u32x4 *)(dst + (row * kNRS + 8 * cg) / 2) = row < tlimit ? v[k] : z;
+            }
+        }
+    }
+};
+
+// B^T of 64 tokens (m0 = the first token's row) into bt[n][tperm(t)] (row
+// stride kRS). Consecutive lanes take consecutive token pairs, so the LDS
+// writes are conflict-free.
 template <int NT>
-__device__ __forceinline__ void stage_rows(const SegArgs &a, const uint16_t *M, int b, int grp,
-                                           int row0, int t0, int tlimit, uint32_t *dst) {
-    for (int item = threadIdx.x; item < 64 * (kN / 8); item += NT) {
-        const int row = item >> 4, cg = item & 15;
-        const int t = t0 + row;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (t < tlimit) v = ld8(M + (tok(a, b, row0 + t) * a.G + grp) * kN + 8 * cg);
-        *(u32x4 *)(dst + (row * kNRS + 8 * cg) / 2) = v;
-    }
-}
-
-// B^T of the 64 tokens [t0, t0+64) (zero for t >= tlimit) into bt[n][t]
-// (row stride kRS), raw bf16. No barrier.
-__device__ __forceinline__ void stage_bt(const SegArgs &a, const uint16_t *Bm, int b, int grp,
-                                         int row0, int t0, int tlimit, uint32_t *bt) {
-    for (int item = threadIdx.x; item < 32 * (kN / 8); item += kThreads) {
-        const int rp = item >> 4, cg = item & 15;
-        const int t = t0 + 2 * rp;
-        u32x4 r0 = {0u, 0u, 0u, 0u}, r1 = {0u, 0u, 0u, 0u};
-        if (t < tlimit) r0 = ld8(Bm + (tok(a, b, row0 + t) * a.G + grp) * kN + 8 * cg);
-        if (t + 1 < tlimit) r1 = ld8(Bm + (tok(a, b, row0 + t + 1) * a.G + grp) * kN + 8 * cg);
+struct BtStage {
+    static constexpr int ITEMS = 32 * (kN / 8);
+    static constexpr int PER = ITEMS / NT;
+    u32x4 r0[PER], r1[PER];
+    __device__ __forceinline__ void load(const uint16_t *m0, uint32_t rstride, int tlimit) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bt[((8 * cg + 2 * q) * kRS) / 2 + rp] = (r0[q] & 0xffffu) | (r1[q] << 16);
-            bt[((8 * cg + 2 * q + 1) * kRS) / 2 + rp] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
+        for (int k = 0; k < PER; ++k) {
+            const int item = threadIdx.x + k * NT;
+            const int t = 2 * (item & 31), cg = item >> 5;
+            r0[k] = ld8(m0 + (uint32_t)min(t, tlimit - 1) * rstride + 8 * cg);
+            r1[k] = ld8(m0 + (uint32_t)min(t + 1, tlimit - 1) * rstride + 8 * cg);
         }
     }
-}
-
-// T[n][p-block w] += sum_t B^T[n][t] (w_t x_t[p]) over one staged 64-token
-// sub-block; w x enters as a hi + lo bf16 pair. xt: X^T[p][t] (row stride
-// xrs, column offset xoff); wv: the 64 weights.
-__device__ __forceinline__ void state_mfma(f32x4 (&T)[kN / 16], const uint32_t *bt,
-                                           const uint16_t *xt, int xrs, int xoff, const float *wv) {
-    const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
-    const uint16_t *btp = (const uint16_t *)bt;
+    __device__ __forceinline__ void store(int tlimit, uint32_t *bt) {
 #pragma unroll
-    for (int ks = 0; ks < kSub / 32; ++ks) {
-        const int tk = 32 * ks + 8 * g4;
-        const u32x4 xv = *(const u32x4 *)(xt + (16 * w + l16) * xrs + xoff + tk);
-        const f32x4 w0 = *(const f32x4 *)(wv + tk);
-        const f32x4 w1 = *(const f32x4 *)(wv + tk + 4);
-        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-        split2(b_lo(xv[0]) * w0[0], b_hi(xv[0]) * w0[1], h0, l0);
-        split2(b_lo(xv[1]) * w0[2], b_hi(xv[1]) * w0[3], h1, l1);
-        split2(b_lo(xv[2]) * w1[0], b_hi(xv[2]) * w1[1], h2, l2);
-        split2(b_lo(xv[3]) * w1[2], b_hi(xv[3]) * w1[3], h3, l3);
-        const u32x4 bhi = {h0, h1, h2, h3}, blo = {l0, l1, l2, l3};
+        for (int k = 0; k < PER; ++k) {
+            const int item = threadIdx.x + k * NT;
+            const int t = 2 * (item & 31), cg = item >> 5;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 a0 = t < tlimit ? r0[k] : z;
+            const u32x4 a1 = t + 1 < tlimit ? r1[k] : z;
+            const int s = tperm(t) >> 1;
 #pragma unroll
-        for (int nt = 0; nt < kN / 16; ++nt) {
-            const u32x4 aop = *(const u32x4 *)(btp + (16 * nt + l16) * kRS + tk);
-            T[nt] = mfma16x16x32(aop, bhi, T[nt]);
-            T[nt] = mfma16x16x32(aop, blo, T[nt]);
+            for (int q = 0; q < 4; ++q) {
+                bt[((8 * cg + 2 * q) * kRS) / 2 + s] = (a0[q] & 0xffffu) | (a1[q] << 16);
+                bt[((8 * cg + 2 * q + 1) * kRS) / 2 + s] = (a0[q] >> 16) | (a1[q] & 0xffff0000u);
+            }
         }
     }
+};
+
+// Weighted input of the state update for k-block ks of a 64-token sub-block:
+// (w_t x_t[p]) at the 8 permuted positions 32ks + 8g4 .. +7 of row p, split
+// into bf16 hi / lo operands. xt: x^T (row stride xrs) with the sub-block at
+// permuted offset soff; wv: the sub-block's 64 weights, natural order.
+__device__ __forceinline__ void wx_operand(const uint16_t *xt, int xrs, int soff, int p,
+                                           const float *wv, int ks, u32x4 &bhi, u32x4 &blo) {
+    const int g4 = lane_id() >> 4;
+    const u32x4 xv = *(const u32x4 *)(xt + xt_at(p, soff + 32 * ks + 8 * g4, xrs));
+    const f32x4 w0 = *(const f32x4 *)(wv + 32 * ks + 4 * g4);        // tokens 4g4 + r
+    const f32x4 w1 = *(const f32x4 *)(wv + 32 * ks + 16 + 4 * g4);   // tokens 16 + 4g4 + r
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    split2(b_lo(xv[0]) * w0[0], b_hi(xv[0]) * w0[1], h0, l0);
+    split2(b_lo(xv[1]) * w0[2], b_hi(xv[1]) * w0[3], h1, l1);
+    split2(b_lo(xv[2]) * w1[0], b_hi(xv[2]) * w1[1], h2, l2);
+    split2(b_lo(xv[3]) * w1[2], b_hi(xv[3]) * w1[3], h3, l3);
+    bhi = u32x4{h0, h1, h2, h3};
+    blo = u32x4{l0, l1, l2, l3};
 }
 
 // ----------------------------------------------------------- k_seg_state
 struct StateSmem {
     float w[kSub];
     alignas(16) uint32_t bt[kN * kRS / 2];
-    alignas(16) uint32_t xt[kP * kRS / 2];
+    alignas(16) uint32_t xt[kP * kSub / 2];
     float run[2];   // running sum of a from the outgoing edge, by step parity
 };
 
@@ -207,6 +269,7 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
     const int edge = d == 0 ? t1 - 1 : t0;
     const int edge_seq = a.seq ? a.seq[tok(a, b, edge)] : 0;
     if (tid == 0) sm.run[0] = 0.f;
+    // wave w owns state columns p = 16w..16w+15 for all n
     f32x4 Hacc[kN / 16];
 #pragma unroll
     for (int nt = 0; nt < kN / 16; ++nt) Hacc[nt] = zero4();
@@ -224,8 +287,10 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
         const float run = sm.run[step & 1];
         if (run < kDead) break;
         if (a.seq && a.seq[tok(a, b, d == 0 ? s1 - 1 : s0)] != edge_seq) break;
-        stage_bt(a, Bm, b, grp, 0, s0, s1, sm.bt);
-        stage_xt<kSub, kThreads>(a, X, b, h, s0, n, sm.xt, kRS);
+        BtStage<kThreads> sb;
+        XStage<kSub, kThreads> sx;
+        sb.load(Bm + (tok(a, b, s0) * a.G + grp) * kN, (uint32_t)(a.G * kN), n);
+        sx.load(X + (tok(a, b, s0) * a.H + h) * kP, (uint32_t)(a.H * kP), n);
         if (w == 0) {
             // lane 0 is the token nearest the outgoing edge
             const bool in = lane < n;
@@ -244,10 +309,25 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
             const float tot = __shfl(incl, 63, 64);
             if (lane == 0) sm.run[(step + 1) & 1] = run + tot;
         }
+        sb.store(n, sm.bt);
+        sx.store(n, sm.xt, kSub);
         __syncthreads();
-        state_mfma(Hacc, sm.bt, (const uint16_t *)sm.xt, kRS, 0, sm.w);
+        // H[n][p] += sum_t B^T[n][t] (w_t x_t[p]): A = B^T rows, B = w x
+        const uint16_t *btp = (const uint16_t *)sm.bt;
+#pragma unroll
+        for (int ks = 0; ks < kSub / 32; ++ks) {
+            u32x4 bhi, blo;
+            wx_operand((const uint16_t *)sm.xt, kSub, 0, 16 * w + l16, sm.w, ks, bhi, blo);
+#pragma unroll
+            for (int nt = 0; nt < kN / 16; ++nt) {
+                const u32x4 aop = *(const u32x4 *)(btp + (16 * nt + l16) * kRS + 32 * ks + 8 * g4);
+                Hacc[nt] = mfma16x16x32(aop, bhi, Hacc[nt]);
+                Hacc[nt] = mfma16x16x32(aop, blo, Hacc[nt]);
+            }
+        }
         __syncthreads();
     }
+    // Hacc[nt][r] = H[n = 16nt + 4g4 + r][p = 16w + l16]
     const size_t si = (((size_t)b * 2 + d) * a.nseg + seg) * a.H + h;
     float *Sout = a.S + si * (size_t)(kP * kN);
 #pragma unroll
@@ -313,10 +393,10 @@ struct OutSmem {
     int wsub[Q / kSub];    // some weight of the 64-token sub-block is nonzero
     float gamma;           // decay of the whole chunk (0: the state does not pass)
     int sq_nb;             // sequence index of the token the carried state comes from
-    alignas(16) uint32_t xt[kP * (Q + 8) / 2];   // X^T [p][t], raw bf16
-    alignas(16) uint32_t bn[Q * kNRS / 2];       // B [t][n], raw bf16
+    alignas(16) uint32_t xt[kP * Q / 2];    // X^T [p][tperm(t)], rotated, raw bf16
+    alignas(16) uint32_t bn[Q * kNRS / 2];  // B [t][n], raw bf16
     // H^T [p][n] as bf16 high part, then bf16 residual; during the state
-    // update: B^T [n][64 tokens] of one sub-block
+    // update: B^T [n][tperm(t)] of one 64-token sub-block
     alignas(16) uint32_t hs[kP * kNRS];
 };
 static_assert(kN * kRS / 2 <= kP * kNRS, "B^T tile must fit the state area");
@@ -332,23 +412,16 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
     const DirPtrs &dp = a.dir[d];
     const uint16_t *DT = (const uint16_t *)dp.dt;
     const float Ah = dp.A[h];
-    // staging loads first: they overlap the scans below
-    stage_xt<Q, kOutThreads>(a, (const uint16_t *)dp.x, b, h, c0, len, sm.xt, Q + 8);
-    for (int sb = 0; sb < Q / kSub; ++sb)
-        stage_rows<kOutThreads>(a, (const uint16_t *)dp.B, b, grp, c0, kSub * sb, len,
-                                sm.bn + (kSub * sb * kNRS) / 2);
     // group 0: position in the walking direction; group 1: toward the edge
     const int pos = (g == 0) == (d == 0) ? t : Q - 1 - t;
     const bool in = t < Q && pos < len;
-    float dtt = 0.f, at = 0.f;
+    // the small loads first: the scans wait only for them
+    float dtt = 0.f;
     int sq = 0;
     if (in) {
         dtt = bf2f(DT[tok(a, b, c0 + pos) * a.H + h]);
-        at = dtt * Ah;
         if (a.seq) sq = a.seq[tok(a, b, c0 + pos)];
     }
-    float v = wave_scan(at);
-    if (lane == 63) sm.tmp[wv] = v;
     int sq_nb = 0, sq_edge = 0;
     bool has_nb = true;
     if (a.seq) {
@@ -357,6 +430,14 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
         sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
         sq_edge = a.seq[tok(a, b, d == 0 ? c0 + len - 1 : c0)];
     }
+    XStage<Q, kOutThreads> sx;
+    RowStage<Q, kOutThreads> sb;
+    sx.load((const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP, (uint32_t)(a.H * kP), len);
+    sb.load((const uint16_t *)dp.B + (tok(a, b, c0) * a.G + grp) * kN, (uint32_t)(a.G * kN), len);
+
+    const float at = dtt * Ah;
+    float v = wave_scan(at);
+    if (lane == 63) sm.tmp[wv] = v;
     __syncthreads();
     float add = 0.f, total = 0.f;
 #pragma unroll
@@ -397,6 +478,8 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
         const unsigned long long m = __ballot(wt != 0.f);
         if (lane == 0 && 64 * wq < Q) sm.wsub[d == 0 ? Q / 64 - 1 - wq : wq] = m != 0ull;
     }
+    sx.store(len, sm.xt, Q);
+    sb.store(len, sm.bn);
     __syncthreads();
     if (tid < Q) {
         // decay of each token to the edge of its 16-tile / 64-block nearest
@@ -430,10 +513,38 @@ __device__ void publish_state(OutSmem<Q> &sm, const f32x4 (&Hacc)[4]) {
     }
 }
 
+// G^T tile rows j0..j0+15 x this lane group's 16 rows i: gg[r] = G[i][j0 + 4g4 + r]
+__device__ __forceinline__ f32x4 gram_tile(const uint16_t *bn, int j0, const u32x4 (&cr)[kN / 32]) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+    f32x4 g = zero4();
+#pragma unroll
+    for (int ks = 0; ks < kN / 32; ++ks)
+        g = mfma16x16x32(*(const u32x4 *)(bn + (j0 + l16) * kNRS + 32 * ks + 8 * g4), cr[ks], g);
+    return g;
+}
+
+// acc[pt] += M x over the 32 columns j32..j32+31; M given as a hi / lo pair
+// in the permuted k order of a Gram accumulator pair.
+template <int Q>
+__device__ __forceinline__ void mx_step(f32x4 (&acc)[4], const uint16_t *xt, int j32, u32x4 mhi,
+                                        u32x4 mlo) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+        const u32x4 xo = *(const u32x4 *)(xt + xt_at(16 * pt + l16, j32 + 8 * g4, Q));
+        acc[pt] = mfma16x16x32(mhi, xo, acc[pt]);
+        acc[pt] = mfma16x16x32(mlo, xo, acc[pt]);
+    }
+}
+
 // Row tile `it` (16 rows) of the chunk: intra-chunk form, carried state, skip
 // term, output, by one wave alone (no barrier). C of the tile lives in
 // registers in the layout that serves both as the B operand of the Gram tiles
 // and as the A operand of the carried-state product.
+//
+// Rows and columns past the chunk's end need no mask: their x and B were
+// staged as zeros and their dt is 0, so every such entry is a finite value
+// times 0, and a row past the end only reaches its own (unstored) output.
 template <int Q>
 __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, int h, int grp,
                          int c0, int len, int it, bool has_state, float Dh, bool add) {
@@ -441,10 +552,9 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, i
     const DirPtrs &dp = a.dir[d];
     const uint16_t *xt = (const uint16_t *)sm.xt;
     const uint16_t *bn = (const uint16_t *)sm.bn;
-    constexpr int XRS = Q + 8;
+    const bool packed = a.seq != nullptr;
     const int I = it >> 2, wq = it & 3;   // 64-row block, tile inside it
     const int i = 16 * it + l16;          // this lane's row (G^T column)
-    const bool row_ok = i < len;
     const int i0 = 16 * it + 4 * g4;      // first of this lane's output rows
     u32x4 cr[kN / 32];
     {
@@ -471,87 +581,88 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, i
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
 
-    // ---- intra-chunk: sum over column blocks J of M[i][j] x_j
-    const int Jlo = d == 0 ? 0 : I, Jhi = d == 0 ? I : Q / 64 - 1;
-    for (int J = Jlo; J <= Jhi; ++J) {
-        if (64 * J >= len) break;
-        if (J != I) {
-            const float near = d == 0 ? sm.cs2[64 * I] - sm.cs2[64 * J + 63]
-                                      : sm.cs2[64 * I + 63] - sm.cs2[64 * J];
-            if (near < kDead * kLog2e) continue;   // every entry is exactly 0
-        }
-        const int r64 = d == 0 ? 64 * J + 63 : 64 * J;
-        const float u64 = exp2_(csi - sm.cs2[r64]);
-        u32x4 mhi[2], mlo[2];
+    // ---- 64-column blocks off the diagonal: M = G e^{cs_i - cs_r} v64_j,
+    // r the block's edge nearest the diagonal
+    const int nJ = d == 0 ? I : (len + 63) / 64 - 1 - I;
+    for (int q = 0; q < nJ; ++q) {
+        const int J = d == 0 ? q : I + 1 + q;
+        const float near = d == 0 ? sm.cs2[64 * I] - sm.cs2[64 * J + 63]
+                                  : sm.cs2[64 * I + 63] - sm.cs2[64 * J];
+        if (near < kDead * kLog2e) continue;   // every entry is exactly 0
+        const float u64 = exp2_(csi - sm.cs2[d == 0 ? 64 * J + 63 : 64 * J]);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             uint32_t ph[4], pl[4];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int jt = 2 * kk + half;
-                const int j0 = 64 * J + 16 * jt;
-                // the whole 16-column tile on the masked side of the diagonal
-                const bool dead = J == I && (d == 0 ? jt > wq : jt < wq);
-                float mv[4] = {0.f, 0.f, 0.f, 0.f};
-                if (!dead) {
-                    f32x4 gg = zero4();
+                const int j0 = 64 * J + 32 * kk + 16 * half;
+                const f32x4 gg = gram_tile(bn, j0, cr);
+                const int jb = j0 + 4 * g4;
+                const f32x4 vv = *(const f32x4 *)(sm.v64 + jb);
+                float mv[4];
 #pragma unroll
-                    for (int ks = 0; ks < kN / 32; ++ks) {
-                        const u32x4 aop = *(const u32x4 *)(bn + (j0 + l16) * kNRS + 32 * ks + 8 * g4);
-                        gg = mfma16x16x32(aop, cr[ks], gg);
-                    }
-                    // gg[r] = G[i][j], j = jb + r
-                    const int jb = j0 + 4 * g4;
-                    if (J != I) {
-                        const f32x4 vv = *(const f32x4 *)(sm.v64 + jb);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) mv[r] = gg[r] * u64 * vv[r];
-                    } else if (jt != wq) {
-                        // another 16-tile of the diagonal block: factor the
-                        // decay through that tile's edge
-                        const int r16 = d == 0 ? j0 + 15 : j0;
-                        const float u16 = exp2_(csi - sm.cs2[r16]);
-                        const f32x4 vv = *(const f32x4 *)(sm.v16 + jb);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) mv[r] = gg[r] * u16 * vv[r];
-                    } else {
-                        // the diagonal 16x16 tile: one exponential per entry
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = jb + r;
-                            const bool tri = d == 0 ? j <= i : j >= i;
-                            mv[r] = tri ? gg[r] * exp2_(csi - sm.cs2[j]) * sm.dt[j] : 0.f;
-                        }
-                    }
-                    if (!row_ok || jb + 3 >= len || a.seq) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = jb + r;
-                            bool ok = row_ok && j < len;
-                            if (a.seq) ok = ok && sm.sq[j] == sqi;
-                            if (!ok) mv[r] = 0.f;
-                        }
-                    }
+                for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u64 * vv[r]);
+                if (packed) {
+                    const int4 s4 = *(const int4 *)(sm.sq + jb);
+                    mv[0] = s4.x == sqi ? mv[0] : 0.f;
+                    mv[1] = s4.y == sqi ? mv[1] : 0.f;
+                    mv[2] = s4.z == sqi ? mv[2] : 0.f;
+                    mv[3] = s4.w == sqi ? mv[3] : 0.f;
                 }
                 split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
                 split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
             }
-            mhi[kk] = u32x4{ph[0], ph[1], ph[2], ph[3]};
-            mlo[kk] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+            mx_step<Q>(acc, xt, 64 * J + 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
+                       u32x4{pl[0], pl[1], pl[2], pl[3]});
         }
+    }
+
+    // ---- the diagonal block: 16-tiles on the far side are 0; the other tiles
+    // factor the decay through their edge nearest the diagonal; the diagonal
+    // tile itself takes one exponential per entry
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
+    for (int kk = 0; kk < 2; ++kk) {
+        const bool live = d == 0 ? 2 * kk <= wq : 2 * kk + 1 >= wq;
+        if (!live) continue;
+        uint32_t ph[4], pl[4];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int jb = 64 * J + 32 * kk + 4 * g4;
-                const uint16_t *xr = xt + (16 * pt + l16) * XRS;
-                const u32x2 x0 = *(const u32x2 *)(xr + jb);
-                const u32x2 x1 = *(const u32x2 *)(xr + jb + 16);
-                const u32x4 xo = {x0[0], x0[1], x1[0], x1[1]};
-                acc[pt] = mfma16x16x32(mhi[kk], xo, acc[pt]);
-                acc[pt] = mfma16x16x32(mlo[kk], xo, acc[pt]);
+        for (int half = 0; half < 2; ++half) {
+            const int jt = 2 * kk + half;
+            const int j0 = 64 * I + 16 * jt;
+            const bool dead = d == 0 ? jt > wq : jt < wq;
+            float mv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (!dead) {
+                const f32x4 gg = gram_tile(bn, j0, cr);
+                const int jb = j0 + 4 * g4;
+                if (jt != wq) {
+                    const float u16 = exp2_(csi - sm.cs2[d == 0 ? j0 + 15 : j0]);
+                    const f32x4 vv = *(const f32x4 *)(sm.v16 + jb);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u16 * vv[r]);
+                } else {
+                    const f32x4 c4 = *(const f32x4 *)(sm.cs2 + jb);
+                    const f32x4 d4 = *(const f32x4 *)(sm.dt + jb);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = jb + r;
+                        const bool tri = d == 0 ? j <= i : j >= i;
+                        const float e = exp2_(csi - c4[r]);
+                        mv[r] = tri ? gg[r] * (e * d4[r]) : 0.f;
+                    }
+                }
+                if (packed) {
+                    const int4 s4 = *(const int4 *)(sm.sq + jb);
+                    mv[0] = s4.x == sqi ? mv[0] : 0.f;
+                    mv[1] = s4.y == sqi ? mv[1] : 0.f;
+                    mv[2] = s4.z == sqi ? mv[2] : 0.f;
+                    mv[3] = s4.w == sqi ? mv[3] : 0.f;
+                }
             }
+            split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
+            split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
         }
+        mx_step<Q>(acc, xt, 64 * I + 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
+                   u32x4{pl[0], pl[1], pl[2], pl[3]});
     }
 
     // ---- carried state: e^{cs_i} C_i . H (tiles it does not reach: skipped, exact)
@@ -570,12 +681,13 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, i
                 tt[pt] = mfma16x16x32(cr[ks], *(const u32x4 *)(hl + o), tt[pt]);
             }
         }
+        const f32x4 c4 = *(const f32x4 *)(sm.cs2 + i0);
         float uu[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int ii = i0 + r;
-            const bool reach = ii < len && (!a.seq || sm.sq[ii] == sm.sq_nb);
-            uu[r] = reach ? exp2_(sm.cs2[ii]) : 0.f;
+            const bool reach = ii < len && (!packed || sm.sq[ii] == sm.sq_nb);
+            uu[r] = reach ? exp2_(c4[r]) : 0.f;
         }
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
@@ -584,9 +696,10 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, i
     }
 
     // ---- skip term (x exact) and output rows i0 + r
+    const int si0 = tperm(i0);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
-        const u32x2 xv = *(const u32x2 *)(xt + (16 * pt + l16) * XRS + i0);
+        const u32x2 xv = *(const u32x2 *)(xt + xt_at(16 * pt + l16, si0, Q));
         acc[pt][0] = fmaf(Dh, b_lo(xv[0]), acc[pt][0]);
         acc[pt][1] = fmaf(Dh, b_hi(xv[0]), acc[pt][1]);
         acc[pt][2] = fmaf(Dh, b_lo(xv[1]), acc[pt][2]);
@@ -630,34 +743,28 @@ __device__ void chunk_state_update(OutSmem<Q> &sm, f32x4 (&Hacc)[4], int len) {
         if (kSub * sb >= len) break;
         if (!sm.wsub[sb]) continue;    // every weight is exactly 0
         {
-            // B^T of the sub-block, transposed inside LDS: one item per thread
+            // B^T of the sub-block, transposed inside LDS: one item per thread;
+            // consecutive lanes take consecutive token pairs
             const int item = threadIdx.x;
             const int rp = item & 31, cg = item >> 5;
             const int t = kSub * sb + 2 * rp;
             const u32x4 r0 = *(const u32x4 *)(bn + t * kNRS + 8 * cg);
             const u32x4 r1 = *(const u32x4 *)(bn + (t + 1) * kNRS + 8 * cg);
+            const int s = tperm(2 * rp) >> 1;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                sm.hs[((8 * cg + 2 * q) * kRS) / 2 + rp] = (r0[q] & 0xffffu) | (r1[q] << 16);
-                sm.hs[((8 * cg + 2 * q + 1) * kRS) / 2 + rp] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
+                sm.hs[((8 * cg + 2 * q) * kRS) / 2 + s] = (r0[q] & 0xffffu) | (r1[q] << 16);
+                sm.hs[((8 * cg + 2 * q + 1) * kRS) / 2 + s] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
             }
         }
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks) {
-            const int tk = 32 * ks + 8 * g4;
-            const u32x4 xv = *(const u32x4 *)(xt + (16 * pq + l16) * (Q + 8) + kSub * sb + tk);
-            const f32x4 w0 = *(const f32x4 *)(sm.w + kSub * sb + tk);
-            const f32x4 w1 = *(const f32x4 *)(sm.w + kSub * sb + tk + 4);
-            uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-            split2(b_lo(xv[0]) * w0[0], b_hi(xv[0]) * w0[1], h0, l0);
-            split2(b_lo(xv[1]) * w0[2], b_hi(xv[1]) * w0[3], h1, l1);
-            split2(b_lo(xv[2]) * w1[0], b_hi(xv[2]) * w1[1], h2, l2);
-            split2(b_lo(xv[3]) * w1[2], b_hi(xv[3]) * w1[3], h3, l3);
-            const u32x4 bhi = {h0, h1, h2, h3}, blo = {l0, l1, l2, l3};
+            u32x4 bhi, blo;
+            wx_operand(xt, Q, kSub * sb, 16 * pq + l16, sm.w + kSub * sb, ks, bhi, blo);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const u32x4 aop = *(const u32x4 *)(bt + (16 * (4 * nh + q) + l16) * kRS + tk);
+                const u32x4 aop = *(const u32x4 *)(bt + (16 * (4 * nh + q) + l16) * kRS + 32 * ks + 8 * g4);
                 Hacc[q] = mfma16x16x32(aop, bhi, Hacc[q]);
                 Hacc[q] = mfma16x16x32(aop, blo, Hacc[q]);
             }
