@@ -537,6 +537,67 @@ __device__ __forceinline__ void mx_step(f32x4 (&acc)[4], const uint16_t *xt, int
     }
 }
 
+// Zero the entries of columns jb..jb+3 that belong to another sequence.
+template <int Q, bool PACKED>
+__device__ __forceinline__ void seq_mask(float (&mv)[4], const OutSmem<Q> &sm, int jb, int sqi) {
+    if (PACKED) {
+        const int4 s4 = *(const int4 *)(sm.sq + jb);
+        mv[0] = s4.x == sqi ? mv[0] : 0.f;
+        mv[1] = s4.y == sqi ? mv[1] : 0.f;
+        mv[2] = s4.z == sqi ? mv[2] : 0.f;
+        mv[3] = s4.w == sqi ? mv[3] : 0.f;
+    }
+}
+
+// The diagonal 64-column block of a row tile at position WQ in its 64-row
+// block: 16-tiles on the far side of the diagonal are 0; the others factor
+// the decay through their edge nearest the diagonal; the diagonal tile
+// itself takes one exponential per entry.
+template <int Q, bool PACKED, int D, int WQ>
+__device__ __forceinline__ void diag_block(f32x4 (&acc)[4], const OutSmem<Q> &sm,
+                                           const u32x4 (&cr)[kN / 32], int I, int i, float csi,
+                                           int sqi) {
+    const int g4 = lane_id() >> 4;
+    const uint16_t *xt = (const uint16_t *)sm.xt;
+    const uint16_t *bn = (const uint16_t *)sm.bn;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        if (D == 0 ? 2 * kk > WQ : 2 * kk + 1 < WQ) continue;   // both tiles dead
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int jt = 2 * kk + half;
+            const int j0 = 64 * I + 16 * jt;
+            float mv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (D == 0 ? jt <= WQ : jt >= WQ) {
+                const f32x4 gg = gram_tile(bn, j0, cr);
+                const int jb = j0 + 4 * g4;
+                if (jt != WQ) {
+                    const float u16 = exp2_(csi - sm.cs2[D == 0 ? j0 + 15 : j0]);
+                    const f32x4 vv = *(const f32x4 *)(sm.v16 + jb);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u16 * vv[r]);
+                } else {
+                    const f32x4 c4 = *(const f32x4 *)(sm.cs2 + jb);
+                    const f32x4 d4 = *(const f32x4 *)(sm.dt + jb);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = jb + r;
+                        const bool tri = D == 0 ? j <= i : j >= i;
+                        const float e = exp2_(csi - c4[r]);
+                        mv[r] = tri ? gg[r] * (e * d4[r]) : 0.f;
+                    }
+                }
+                seq_mask<Q, PACKED>(mv, sm, jb, sqi);
+            }
+            split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
+            split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
+        }
+        mx_step<Q>(acc, xt, 64 * I + 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
+                   u32x4{pl[0], pl[1], pl[2], pl[3]});
+    }
+}
+
 // Row tile `it` (16 rows) of the chunk: intra-chunk form, carried state, skip
 // term, output, by one wave alone (no barrier). C of the tile lives in
 // registers in the layout that serves both as the B operand of the Gram tiles
@@ -545,51 +606,52 @@ __device__ __forceinline__ void mx_step(f32x4 (&acc)[4], const uint16_t *xt, int
 // Rows and columns past the chunk's end need no mask: their x and B were
 // staged as zeros and their dt is 0, so every such entry is a finite value
 // times 0, and a row past the end only reaches its own (unstored) output.
-template <int Q>
-__device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, int h, int grp,
-                         int c0, int len, int it, bool has_state, float Dh, bool add) {
+template <int Q, bool PACKED, int D>
+__device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, int grp, int c0,
+                         int len, int it, bool has_state, float Dh, bool add) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
-    const DirPtrs &dp = a.dir[d];
+    const DirPtrs &dp = a.dir[D];
     const uint16_t *xt = (const uint16_t *)sm.xt;
     const uint16_t *bn = (const uint16_t *)sm.bn;
-    const bool packed = a.seq != nullptr;
     const int I = it >> 2, wq = it & 3;   // 64-row block, tile inside it
     const int i = 16 * it + l16;          // this lane's row (G^T column)
     const int i0 = 16 * it + 4 * g4;      // first of this lane's output rows
+    const bool full = 16 * it + 16 <= len;
     u32x4 cr[kN / 32];
     {
-        const uint16_t *cp = (const uint16_t *)dp.C +
-                             (tok(a, b, c0 + min(i, len - 1)) * a.G + grp) * kN + 8 * g4;
+        const uint16_t *cp = (const uint16_t *)dp.C + (tok(a, b, c0) * a.G + grp) * kN +
+                             (uint32_t)(min(i, len - 1) * a.G * kN) + 8 * g4;
 #pragma unroll
         for (int ks = 0; ks < kN / 32; ++ks) cr[ks] = ld8(cp + 32 * ks);
     }
-    float *yrow[4];
+    float *ybase = a.y + (tok(a, b, c0) * a.H + h) * kP + l16;
+    const uint32_t ystride = (uint32_t)(a.H * kP);
+    uint32_t yoff[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        yrow[r] = a.y + (tok(a, b, c0 + min(i0 + r, len - 1)) * a.H + h) * kP + l16;
+    for (int r = 0; r < 4; ++r) yoff[r] = (uint32_t)min(i0 + r, len - 1) * ystride;
     float prev[4][4];
     if (add) {
         // the reverse pass wrote these rows; fetched now, used at the end
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) prev[pt][r] = yrow[r][16 * pt];
+            for (int r = 0; r < 4; ++r) prev[pt][r] = ybase[yoff[r] + 16 * pt];
     }
     const float csi = sm.cs2[i];
-    const int sqi = sm.sq[i];
+    const int sqi = PACKED ? sm.sq[i] : 0;
     f32x4 acc[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
 
     // ---- 64-column blocks off the diagonal: M = G e^{cs_i - cs_r} v64_j,
     // r the block's edge nearest the diagonal
-    const int nJ = d == 0 ? I : (len + 63) / 64 - 1 - I;
+    const int nJ = D == 0 ? I : (len + 63) / 64 - 1 - I;
     for (int q = 0; q < nJ; ++q) {
-        const int J = d == 0 ? q : I + 1 + q;
-        const float near = d == 0 ? sm.cs2[64 * I] - sm.cs2[64 * J + 63]
+        const int J = D == 0 ? q : I + 1 + q;
+        const float near = D == 0 ? sm.cs2[64 * I] - sm.cs2[64 * J + 63]
                                   : sm.cs2[64 * I + 63] - sm.cs2[64 * J];
         if (near < kDead * kLog2e) continue;   // every entry is exactly 0
-        const float u64 = exp2_(csi - sm.cs2[d == 0 ? 64 * J + 63 : 64 * J]);
+        const float u64 = exp2_(csi - sm.cs2[D == 0 ? 64 * J + 63 : 64 * J]);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             uint32_t ph[4], pl[4];
@@ -602,13 +664,7 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, i
                 float mv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u64 * vv[r]);
-                if (packed) {
-                    const int4 s4 = *(const int4 *)(sm.sq + jb);
-                    mv[0] = s4.x == sqi ? mv[0] : 0.f;
-                    mv[1] = s4.y == sqi ? mv[1] : 0.f;
-                    mv[2] = s4.z == sqi ? mv[2] : 0.f;
-                    mv[3] = s4.w == sqi ? mv[3] : 0.f;
-                }
+                seq_mask<Q, PACKED>(mv, sm, jb, sqi);
                 split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
                 split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
             }
@@ -616,53 +672,11 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, i
                        u32x4{pl[0], pl[1], pl[2], pl[3]});
         }
     }
-
-    // ---- the diagonal block: 16-tiles on the far side are 0; the other tiles
-    // factor the decay through their edge nearest the diagonal; the diagonal
-    // tile itself takes one exponential per entry
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const bool live = d == 0 ? 2 * kk <= wq : 2 * kk + 1 >= wq;
-        if (!live) continue;
-        uint32_t ph[4], pl[4];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int jt = 2 * kk + half;
-            const int j0 = 64 * I + 16 * jt;
-            const bool dead = d == 0 ? jt > wq : jt < wq;
-            float mv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (!dead) {
-                const f32x4 gg = gram_tile(bn, j0, cr);
-                const int jb = j0 + 4 * g4;
-                if (jt != wq) {
-                    const float u16 = exp2_(csi - sm.cs2[d == 0 ? j0 + 15 : j0]);
-                    const f32x4 vv = *(const f32x4 *)(sm.v16 + jb);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u16 * vv[r]);
-                } else {
-                    const f32x4 c4 = *(const f32x4 *)(sm.cs2 + jb);
-                    const f32x4 d4 = *(const f32x4 *)(sm.dt + jb);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = jb + r;
-                        const bool tri = d == 0 ? j <= i : j >= i;
-                        const float e = exp2_(csi - c4[r]);
-                        mv[r] = tri ? gg[r] * (e * d4[r]) : 0.f;
-                    }
-                }
-                if (packed) {
-                    const int4 s4 = *(const int4 *)(sm.sq + jb);
-                    mv[0] = s4.x == sqi ? mv[0] : 0.f;
-                    mv[1] = s4.y == sqi ? mv[1] : 0.f;
-                    mv[2] = s4.z == sqi ? mv[2] : 0.f;
-                    mv[3] = s4.w == sqi ? mv[3] : 0.f;
-                }
-            }
-            split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
-            split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
-        }
-        mx_step<Q>(acc, xt, 64 * I + 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
-                   u32x4{pl[0], pl[1], pl[2], pl[3]});
+    switch (wq) {
+        case 0: diag_block<Q, PACKED, D, 0>(acc, sm, cr, I, i, csi, sqi); break;
+        case 1: diag_block<Q, PACKED, D, 1>(acc, sm, cr, I, i, csi, sqi); break;
+        case 2: diag_block<Q, PACKED, D, 2>(acc, sm, cr, I, i, csi, sqi); break;
+        default: diag_block<Q, PACKED, D, 3>(acc, sm, cr, I, i, csi, sqi); break;
     }
 
     // ---- carried state: e^{cs_i} C_i . H (tiles it does not reach: skipped, exact)
@@ -683,11 +697,16 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, i
         }
         const f32x4 c4 = *(const f32x4 *)(sm.cs2 + i0);
         float uu[4];
+        if (PACKED) {
+            const int4 s4 = *(const int4 *)(sm.sq + i0);
+            const int nb = sm.sq_nb;
+            uu[0] = s4.x == nb ? exp2_(c4[0]) : 0.f;
+            uu[1] = s4.y == nb ? exp2_(c4[1]) : 0.f;
+            uu[2] = s4.z == nb ? exp2_(c4[2]) : 0.f;
+            uu[3] = s4.w == nb ? exp2_(c4[3]) : 0.f;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ii = i0 + r;
-            const bool reach = ii < len && (!packed || sm.sq[ii] == sm.sq_nb);
-            uu[r] = reach ? exp2_(c4[r]) : 0.f;
+            for (int r = 0; r < 4; ++r) uu[r] = exp2_(c4[r]);
         }
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
@@ -711,11 +730,18 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int d, int b, i
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[pt][r] += prev[pt][r];
     }
+    if (full) {
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
+        for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (i0 + r < len) yrow[r][16 * pt] = acc[pt][r];
+            for (int r = 0; r < 4; ++r) ybase[yoff[r] + 16 * pt] = acc[pt][r];
+    } else {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (i0 + r < len) ybase[yoff[r] + 16 * pt] = acc[pt][r];
+    }
 }
 
 // Row tiles of wave w: pairs whose column counts add up to the same total,
@@ -773,7 +799,65 @@ __device__ void chunk_state_update(OutSmem<Q> &sm, f32x4 (&Hacc)[4], int len) {
     }
 }
 
-template <int Q>
+// One direction's walk over the segment's chunks.
+template <int Q, bool PACKED, int D>
+__device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h, int grp, bool add) {
+    const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
+    const int pq = w & 3, nh = w >> 2;
+    const int t0 = seg * a.Ts, t1 = min(t0 + a.Ts, a.L);
+    const int cfirst = t0 / Q, clast = (t1 - 1) / Q;
+    const size_t PN = (size_t)kP * kN;
+    auto slot = [&](int d, int k) { return (((size_t)b * 2 + d) * a.nseg + k) * a.H + h; };
+    const int hoff = (16 * pq + l16) * kN + 64 * nh + 4 * g4;   // + 16 q: this lane's state entries
+    const DirPtrs &dp = a.dir[D];
+    const float Dh = dp.D ? dp.D[h] : 0.f;
+    // incoming state of this segment in the walking direction
+    const float *src = nullptr;
+    if (D == 0) {
+        if (seg == 0) src = a.init_state ? a.init_state + ((size_t)b * a.H + h) * PN : nullptr;
+        else src = a.gam[slot(0, seg - 1)] == 0.f ? a.S + slot(0, seg - 1) * PN : a.Hs + slot(0, seg) * PN;
+    } else {
+        if (seg == a.nseg - 1) src = nullptr;
+        else src = a.gam[slot(1, seg + 1)] == 0.f ? a.S + slot(1, seg + 1) * PN : a.Hs + slot(1, seg) * PN;
+    }
+    f32x4 Hacc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
+    bool has_state = src != nullptr;
+    if (has_state) publish_state<Q>(sm, Hacc);
+
+    const int nch = clast - cfirst + 1;
+    const bool want_final = D == 0 && seg == a.nseg - 1 && a.final_state;
+    for (int s = 0; s < nch; ++s) {
+        const int c = D == 0 ? cfirst + s : clast - s;
+        const int c0 = c * Q;
+        const int len = min(Q, a.L - c0);
+        chunk_prep<Q>(a, sm, D, b, h, grp, c0, len);
+#pragma unroll 1
+        for (int k = 0; k < 2; ++k) {
+            const int it = tile_of<Q>(w, k);
+            if (it >= 0 && 16 * it < len)
+                row_tile<Q, PACKED, D>(a, sm, b, h, grp, c0, len, it, has_state, Dh, add);
+        }
+        const bool last = s == nch - 1;
+        if (!last || want_final) {
+            __syncthreads();   // row tiles are done with the state area
+            chunk_state_update<Q>(sm, Hacc, len);
+            if (!last) {
+                publish_state<Q>(sm, Hacc);
+                has_state = true;
+            }
+        }
+        __syncthreads();
+    }
+    if (want_final) {
+        float *fs = a.final_state + ((size_t)b * a.H + h) * PN;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *(f32x4 *)(fs + hoff + 16 * q) = Hacc[q];
+    }
+}
+
+template <int Q, bool PACKED>
 __global__ void __launch_bounds__(kOutThreads) k_seg_out(const SegArgs a) {
     // XCD-aware order: consecutive workgroups go to different XCDs
     // (round-robin by 8), so the 8 streams of work that share one XCD's L2 are
@@ -785,63 +869,13 @@ __global__ void __launch_bounds__(kOutThreads) k_seg_out(const SegArgs a) {
     if (rs >= a.batch * a.nseg) return;
     const int b = rs / a.nseg, seg = rs % a.nseg;
     const int grp = h / (a.H / a.G);
-    const int t0 = seg * a.Ts, t1 = min(t0 + a.Ts, a.L);
-    const int cfirst = t0 / Q, clast = (t1 - 1) / Q;
-    const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
-    const int pq = w & 3, nh = w >> 2;
     __shared__ __attribute__((aligned(16))) OutSmem<Q> sm;
-    const size_t PN = (size_t)kP * kN;
-    auto slot = [&](int d, int k) { return (((size_t)b * 2 + d) * a.nseg + k) * a.H + h; };
-    const int hoff = (16 * pq + l16) * kN + 64 * nh + 4 * g4;   // + 16 q: this lane's state entries
-
-    for (int pass = 0; pass < a.ndir; ++pass) {
-        const int d = a.ndir == 2 ? 1 - pass : 0;   // reverse first, then forward adds
-        const DirPtrs &dp = a.dir[d];
-        const float Dh = dp.D ? dp.D[h] : 0.f;
-        // incoming state of this segment in the walking direction
-        const float *src = nullptr;
-        if (d == 0) {
-            if (seg == 0) src = a.init_state ? a.init_state + ((size_t)b * a.H + h) * PN : nullptr;
-            else src = a.gam[slot(0, seg - 1)] == 0.f ? a.S + slot(0, seg - 1) * PN : a.Hs + slot(0, seg) * PN;
-        } else {
-            if (seg == a.nseg - 1) src = nullptr;
-            else src = a.gam[slot(1, seg + 1)] == 0.f ? a.S + slot(1, seg + 1) * PN : a.Hs + slot(1, seg) * PN;
-        }
-        f32x4 Hacc[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
-        bool has_state = src != nullptr;
-        if (has_state) publish_state<Q>(sm, Hacc);
-
-        const int nch = clast - cfirst + 1;
-        const bool want_final = d == 0 && seg == a.nseg - 1 && a.final_state;
-        for (int s = 0; s < nch; ++s) {
-            const int c = d == 0 ? cfirst + s : clast - s;
-            const int c0 = c * Q;
-            const int len = min(Q, a.L - c0);
-            chunk_prep<Q>(a, sm, d, b, h, grp, c0, len);
-#pragma unroll 1
-            for (int k = 0; k < 2; ++k) {
-                const int it = tile_of<Q>(w, k);
-                if (it >= 0 && 16 * it < len)
-                    row_tile<Q>(a, sm, d, b, h, grp, c0, len, it, has_state, Dh, d == 0 && a.ndir == 2);
-            }
-            const bool last = s == nch - 1;
-            if (!last || want_final) {
-                __syncthreads();   // row tiles are done with the state area
-                chunk_state_update<Q>(sm, Hacc, len);
-                if (!last) {
-                    publish_state<Q>(sm, Hacc);
-                    has_state = true;
-                }
-            }
-            __syncthreads();
-        }
-        if (want_final) {
-            float *fs = a.final_state + ((size_t)b * a.H + h) * PN;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) *(f32x4 *)(fs + hoff + 16 * q) = Hacc[q];
-        }
+    if (a.ndir == 2) {
+        // reverse first, then the forward pass adds its part
+        seg_pass<Q, PACKED, 1>(a, sm, b, seg, h, grp, false);
+        seg_pass<Q, PACKED, 0>(a, sm, b, seg, h, grp, true);
+    } else {
+        seg_pass<Q, PACKED, 0>(a, sm, b, seg, h, grp, false);
     }
 }
 
@@ -861,7 +895,10 @@ hipError_t launch_q(const SegArgs &a, hipStream_t s) {
                   s, a);
     }
     const int groups = (a.batch * a.nseg + 7) / 8;
-    BM_LAUNCH("ssd_seg_out", k_seg_out<Q>, dim3(groups * 8 * a.H), dim3(kOutThreads), 0, s, a);
+    if (a.seq)
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true>), dim3(groups * 8 * a.H), dim3(kOutThreads), 0, s, a);
+    else
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, false>), dim3(groups * 8 * a.H), dim3(kOutThreads), 0, s, a);
     return hipGetLastError();
 }
 
