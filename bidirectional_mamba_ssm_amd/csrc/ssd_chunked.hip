@@ -56,8 +56,8 @@ constexpr int kP = 64;         // headdim handled here
 constexpr int kN = 128;        // d_state handled here
 constexpr int kThreads = 256;  // k_seg_state: 4 waves
 constexpr int kSub = 64;       // tokens per state-update sub-block
-constexpr int kRS = kSub + 8;  // LDS row stride (16-bit elements) of B^T [n][64 tokens] tiles
-constexpr int kNRS = kN + 8;   // LDS row stride (16-bit elements) of [row][n] tiles
+constexpr int kNRS = kN + 8;   // LDS row stride (16-bit elements) of [t][n] tiles
+constexpr int kXS = kP + 16;   // LDS row stride (16-bit elements) of x [t][p] tiles
 constexpr float kDead = -110.f;  // expf(x) is exactly 0.0f for every x < kDead
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -75,19 +75,28 @@ __device__ __forceinline__ float b_lo(uint32_t u) { return __uint_as_float(u << 
 __device__ __forceinline__ float b_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Token order inside the LDS tiles of x^T and B^T: within each 32-token
-// block, tokens 4g+r and 16+4g+r (g, r < 4) sit side by side at positions
-// 8g+r and 8g+4+r. That is the k order in which a pair of Gram accumulator
-// tiles feeds the next product, so every operand read is one 16-byte load.
-__device__ __forceinline__ int tperm(int t) {
-    return (t & ~31) | ((t & 12) << 1) | ((t & 16) >> 2) | (t & 3);
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// Matrix-core operand (A or B of v_mfma_f32_16x16x32_bf16) for the 16
+// columns c0..c0+15 of a row-major [t][c] bf16 tile in LDS (row stride rs),
+// with k running over the 32 rows t32..t32+31, read by two transposing LDS
+// loads (ds_read_b64_tr_b16). Within each group of 16 lanes such a load hands
+// lane i the 4 values that the group's lanes 4q + i/4 (q < 4) point at, at
+// element i%4; so lane s points at row t0 + s/4, column c0 + 4(s%4), and lane
+// i receives column c0 + i of rows t0..t0+3. Lane group g4 thus holds k slots
+//   0..3 -> rows t32 + 4 g4 + (0..3),   4..7 -> rows t32 + 16 + 4 g4 + (0..3),
+// the k order in which a pair of Gram accumulator tiles feeds the next
+// product.
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
+    const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p);
+    return __builtin_bit_cast(u32x2, r);
 }
-// x^T rows also rotate their 16-byte groups (XOR with a function of the row),
-// so the transposing staging writes and the operand reads both spread over
-// all LDS banks. s: a permuted position; the 8 positions of its group stay
-// contiguous. Rows need at least 64 positions.
-__device__ __forceinline__ int xt_at(int p, int s, int xrs) {
-    return p * xrs + ((((s >> 3) ^ ((p ^ (p >> 3)) & 7)) << 3) | (s & 7));
+__device__ __forceinline__ u32x4 tr_operand(const uint16_t *base, int rs, int t32, int c0) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, s = lane & 15;
+    const uint16_t *p = base + (t32 + 4 * g4 + (s >> 2)) * rs + c0 + 4 * (s & 3);
+    const u32x2 a = ld_tr(p), b = ld_tr(p + 16 * rs);
+    return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 struct SegArgs {
@@ -118,54 +127,14 @@ __device__ __forceinline__ float wave_scan(float v) {
 }
 
 // --------------------------------------------------------- staging helpers
-// Every helper issues all of its global loads before its first LDS write so
-// that the loads overlap; rows past `tlimit` are loaded clamped and zeroed.
-
-// x^T: COUNT tokens of one head (x0 = the first token's row, tstride
-// elements between tokens), transposed into xt (permuted, rotated; row
-// stride xrs). Consecutive lanes read consecutive 16-byte groups of a row.
-template <int COUNT, int NT>
-struct XStage {
-    static constexpr int ITEMS = (COUNT / 2) * (kP / 8);
-    static constexpr int PER = (ITEMS + NT - 1) / NT;
-    u32x4 r0[PER], r1[PER];
-    __device__ __forceinline__ void load(const uint16_t *x0, uint32_t tstride, int tlimit) {
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int item = threadIdx.x + k * NT;
-            if (ITEMS % NT == 0 || item < ITEMS) {
-                const int t = 2 * (item >> 3), cg = item & 7;
-                r0[k] = ld8(x0 + (uint32_t)min(t, tlimit - 1) * tstride + 8 * cg);
-                r1[k] = ld8(x0 + (uint32_t)min(t + 1, tlimit - 1) * tstride + 8 * cg);
-            }
-        }
-    }
-    __device__ __forceinline__ void store(int tlimit, uint32_t *xt, int xrs) {
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int item = threadIdx.x + k * NT;
-            if (ITEMS % NT == 0 || item < ITEMS) {
-                const int t = 2 * (item >> 3), cg = item & 7;
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                const u32x4 a0 = t < tlimit ? r0[k] : z;
-                const u32x4 a1 = t + 1 < tlimit ? r1[k] : z;
-                const int s = tperm(t);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int p = 8 * cg + 2 * q;
-                    xt[xt_at(p, s, xrs) >> 1] = (a0[q] & 0xffffu) | (a1[q] << 16);
-                    xt[xt_at(p + 1, s, xrs) >> 1] = (a0[q] >> 16) | (a1[q] & 0xffff0000u);
-                }
-            }
-        }
-    }
-};
-
-// ROWS rows of a [t][n] bf16 tensor (m0 = the first row, rstride elements
-// between rows), raw, into dst[row][n] (row stride kNRS).
-template <int ROWS, int NT>
+// ROWS rows of COLS bf16 each (m0 = the first row, rstride elements between
+// rows in memory), raw, into dst (row stride RS). All global loads are issued
+// before the first LDS write so that they overlap; rows at or past `tlimit`
+// are loaded clamped and stored as zeros.
+template <int ROWS, int COLS, int RS, int NT>
 struct RowStage {
-    static constexpr int ITEMS = ROWS * (kN / 8);
+    static constexpr int CG = COLS / 8;
+    static constexpr int ITEMS = ROWS * CG;
     static constexpr int PER = (ITEMS + NT - 1) / NT;
     u32x4 v[PER];
     __device__ __forceinline__ void load(const uint16_t *m0, uint32_t rstride, int tlimit) {
@@ -173,69 +142,33 @@ struct RowStage {
         for (int k = 0; k < PER; ++k) {
             const int item = threadIdx.x + k * NT;
             if (ITEMS % NT == 0 || item < ITEMS) {
-                const int row = item >> 4, cg = item & 15;
+                const int row = item / CG, cg = item % CG;
                 v[k] = ld8(m0 + (uint32_t)min(row, tlimit - 1) * rstride + 8 * cg);
             }
         }
     }
-    __device__ __forceinline__ void store(int tlimit, uint32_t *dst) {
+    __device__ __forceinline__ void store(int tlimit, uint16_t *dst) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int item = threadIdx.x + k * NT;
             if (ITEMS % NT == 0 || item < ITEMS) {
-                const int row = item >> 4, cg = item & 15;
+                const int row = item / CG, cg = item % CG;
                 const u32x4 z = {0u, 0u, 0u, 0u};
-                *(u32x4 *)(dst + (row * kNRS + 8 * cg) / 2) = row < tlimit ? v[k] : z;
+                *(u32x4 *)(dst + row * RS + 8 * cg) = row < tlimit ? v[k] : z;
             }
         }
     }
 };
 
-// B^T of 64 tokens (m0 = the first token's row) into bt[n][tperm(t)] (row
-// stride kRS). Consecutive lanes take consecutive token pairs, so the LDS
-// writes are conflict-free.
-template <int NT>
-struct BtStage {
-    static constexpr int ITEMS = 32 * (kN / 8);
-    static constexpr int PER = ITEMS / NT;
-    u32x4 r0[PER], r1[PER];
-    __device__ __forceinline__ void load(const uint16_t *m0, uint32_t rstride, int tlimit) {
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int item = threadIdx.x + k * NT;
-            const int t = 2 * (item & 31), cg = item >> 5;
-            r0[k] = ld8(m0 + (uint32_t)min(t, tlimit - 1) * rstride + 8 * cg);
-            r1[k] = ld8(m0 + (uint32_t)min(t + 1, tlimit - 1) * rstride + 8 * cg);
-        }
-    }
-    __device__ __forceinline__ void store(int tlimit, uint32_t *bt) {
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int item = threadIdx.x + k * NT;
-            const int t = 2 * (item & 31), cg = item >> 5;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 a0 = t < tlimit ? r0[k] : z;
-            const u32x4 a1 = t + 1 < tlimit ? r1[k] : z;
-            const int s = tperm(t) >> 1;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                bt[((8 * cg + 2 * q) * kRS) / 2 + s] = (a0[q] & 0xffffu) | (a1[q] << 16);
-                bt[((8 * cg + 2 * q + 1) * kRS) / 2 + s] = (a0[q] >> 16) | (a1[q] & 0xffff0000u);
-            }
-        }
-    }
-};
-
-// Weighted input of the state update for k-block ks of a 64-token sub-block:
-// (w_t x_t[p]) at the 8 permuted positions 32ks + 8g4 .. +7 of row p, split
-// into bf16 hi / lo operands. xt: x^T (row stride xrs) with the sub-block at
-// permuted offset soff; wv: the sub-block's 64 weights, natural order.
-__device__ __forceinline__ void wx_operand(const uint16_t *xt, int xrs, int soff, int p,
-                                           const float *wv, int ks, u32x4 &bhi, u32x4 &blo) {
-    const int g4 = lane_id() >> 4;
-    const u32x4 xv = *(const u32x4 *)(xt + xt_at(p, soff + 32 * ks + 8 * g4, xrs));
-    const f32x4 w0 = *(const f32x4 *)(wv + 32 * ks + 4 * g4);        // tokens 4g4 + r
-    const f32x4 w1 = *(const f32x4 *)(wv + 32 * ks + 16 + 4 * g4);   // tokens 16 + 4g4 + r
+// B operand of the state update for the 32 tokens t32..t32+31 and the 16
+// columns p0..p0+15: (w_t x_t[p]) split into bf16 hi / lo. xs: x [t][p]
+// (row stride kXS); wv: the weights, natural token order.
+__device__ __forceinline__ void wx_operand(const uint16_t *xs, int t32, int p0, const float *wv,
+                                           u32x4 &bhi, u32x4 &blo) {
+    const int g4 = (threadIdx.x & 63) >> 4;
+    const u32x4 xv = tr_operand(xs, kXS, t32, p0);
+    const f32x4 w0 = *(const f32x4 *)(wv + t32 + 4 * g4);        // k slots 0..3
+    const f32x4 w1 = *(const f32x4 *)(wv + t32 + 16 + 4 * g4);   // k slots 4..7
     uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
     split2(b_lo(xv[0]) * w0[0], b_hi(xv[0]) * w0[1], h0, l0);
     split2(b_lo(xv[1]) * w0[2], b_hi(xv[1]) * w0[3], h1, l1);
@@ -248,8 +181,8 @@ __device__ __forceinline__ void wx_operand(const uint16_t *xt, int xrs, int soff
 // ----------------------------------------------------------- k_seg_state
 struct StateSmem {
     float w[kSub];
-    alignas(16) uint32_t bt[kN * kRS / 2];
-    alignas(16) uint32_t xt[kP * kSub / 2];
+    alignas(16) uint16_t bn[kSub * kNRS];   // B [t][n]
+    alignas(16) uint16_t xs[kSub * kXS];    // x [t][p]
     float run[2];   // running sum of a from the outgoing edge, by step parity
 };
 
@@ -287,8 +220,8 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
         const float run = sm.run[step & 1];
         if (run < kDead) break;
         if (a.seq && a.seq[tok(a, b, d == 0 ? s1 - 1 : s0)] != edge_seq) break;
-        BtStage<kThreads> sb;
-        XStage<kSub, kThreads> sx;
+        RowStage<kSub, kN, kNRS, kThreads> sb;
+        RowStage<kSub, kP, kXS, kThreads> sx;
         sb.load(Bm + (tok(a, b, s0) * a.G + grp) * kN, (uint32_t)(a.G * kN), n);
         sx.load(X + (tok(a, b, s0) * a.H + h) * kP, (uint32_t)(a.H * kP), n);
         if (w == 0) {
@@ -309,18 +242,17 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
             const float tot = __shfl(incl, 63, 64);
             if (lane == 0) sm.run[(step + 1) & 1] = run + tot;
         }
-        sb.store(n, sm.bt);
-        sx.store(n, sm.xt, kSub);
+        sb.store(n, sm.bn);
+        sx.store(n, sm.xs);
         __syncthreads();
         // H[n][p] += sum_t B^T[n][t] (w_t x_t[p]): A = B^T rows, B = w x
-        const uint16_t *btp = (const uint16_t *)sm.bt;
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks) {
             u32x4 bhi, blo;
-            wx_operand((const uint16_t *)sm.xt, kSub, 0, 16 * w + l16, sm.w, ks, bhi, blo);
+            wx_operand(sm.xs, 32 * ks, 16 * w, sm.w, bhi, blo);
 #pragma unroll
             for (int nt = 0; nt < kN / 16; ++nt) {
-                const u32x4 aop = *(const u32x4 *)(btp + (16 * nt + l16) * kRS + 32 * ks + 8 * g4);
+                const u32x4 aop = tr_operand(sm.bn, kNRS, 32 * ks, 16 * nt);
                 Hacc[nt] = mfma16x16x32(aop, bhi, Hacc[nt]);
                 Hacc[nt] = mfma16x16x32(aop, blo, Hacc[nt]);
             }
@@ -393,13 +325,10 @@ struct OutSmem {
     int wsub[Q / kSub];    // some weight of the 64-token sub-block is nonzero
     float gamma;           // decay of the whole chunk (0: the state does not pass)
     int sq_nb;             // sequence index of the token the carried state comes from
-    alignas(16) uint32_t xt[kP * Q / 2];    // X^T [p][tperm(t)], rotated, raw bf16
-    alignas(16) uint32_t bn[Q * kNRS / 2];  // B [t][n], raw bf16
-    // H^T [p][n] as bf16 high part, then bf16 residual; during the state
-    // update: B^T [n][tperm(t)] of one 64-token sub-block
-    alignas(16) uint32_t hs[kP * kNRS];
+    alignas(16) uint16_t xs[Q * kXS];       // x [t][p], raw bf16
+    alignas(16) uint16_t bn[Q * kNRS];      // B [t][n], raw bf16
+    alignas(16) uint16_t hs[2 * kP * kNRS]; // H^T [p][n]: bf16 high part, then bf16 residual
 };
-static_assert(kN * kRS / 2 <= kP * kNRS, "B^T tile must fit the state area");
 
 // One chunk [c0, c0+len) of direction d: scans, decay factors, weights,
 // skip masks; x and B staged. Threads 0-255 scan a in the walking direction,
@@ -430,8 +359,8 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
         sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
         sq_edge = a.seq[tok(a, b, d == 0 ? c0 + len - 1 : c0)];
     }
-    XStage<Q, kOutThreads> sx;
-    RowStage<Q, kOutThreads> sb;
+    RowStage<Q, kP, kXS, kOutThreads> sx;
+    RowStage<Q, kN, kNRS, kOutThreads> sb;
     sx.load((const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP, (uint32_t)(a.H * kP), len);
     sb.load((const uint16_t *)dp.B + (tok(a, b, c0) * a.G + grp) * kN, (uint32_t)(a.G * kN), len);
 
@@ -478,7 +407,7 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h
         const unsigned long long m = __ballot(wt != 0.f);
         if (lane == 0 && 64 * wq < Q) sm.wsub[d == 0 ? Q / 64 - 1 - wq : wq] = m != 0ull;
     }
-    sx.store(len, sm.xt, Q);
+    sx.store(len, sm.xs);
     sb.store(len, sm.bn);
     __syncthreads();
     if (tid < Q) {
@@ -500,7 +429,7 @@ template <int Q>
 __device__ void publish_state(OutSmem<Q> &sm, const f32x4 (&Hacc)[4]) {
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
     const int pq = w & 3, nh = w >> 2;
-    uint16_t *hh = (uint16_t *)sm.hs;
+    uint16_t *hh = sm.hs;
     uint16_t *hl = hh + kP * kNRS;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -524,14 +453,13 @@ __device__ __forceinline__ f32x4 gram_tile(const uint16_t *bn, int j0, const u32
 }
 
 // acc[pt] += M x over the 32 columns j32..j32+31; M given as a hi / lo pair
-// in the permuted k order of a Gram accumulator pair.
-template <int Q>
-__device__ __forceinline__ void mx_step(f32x4 (&acc)[4], const uint16_t *xt, int j32, u32x4 mhi,
+// in the k order of a Gram accumulator pair, which is the order in which the
+// transposing reads deliver x.
+__device__ __forceinline__ void mx_step(f32x4 (&acc)[4], const uint16_t *xs, int j32, u32x4 mhi,
                                         u32x4 mlo) {
-    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
-        const u32x4 xo = *(const u32x4 *)(xt + xt_at(16 * pt + l16, j32 + 8 * g4, Q));
+        const u32x4 xo = tr_operand(xs, kXS, j32, 16 * pt);
         acc[pt] = mfma16x16x32(mhi, xo, acc[pt]);
         acc[pt] = mfma16x16x32(mlo, xo, acc[pt]);
     }
@@ -558,8 +486,7 @@ __device__ __forceinline__ void diag_block(f32x4 (&acc)[4], const OutSmem<Q> &sm
                                            const u32x4 (&cr)[kN / 32], int I, int i, float csi,
                                            int sqi) {
     const int g4 = lane_id() >> 4;
-    const uint16_t *xt = (const uint16_t *)sm.xt;
-    const uint16_t *bn = (const uint16_t *)sm.bn;
+    const uint16_t *bn = sm.bn;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         if (D == 0 ? 2 * kk > WQ : 2 * kk + 1 < WQ) continue;   // both tiles dead
@@ -593,7 +520,7 @@ __device__ __forceinline__ void diag_block(f32x4 (&acc)[4], const OutSmem<Q> &sm
             split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
             split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
         }
-        mx_step<Q>(acc, xt, 64 * I + 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
+        mx_step(acc, sm.xs, 64 * I + 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
                    u32x4{pl[0], pl[1], pl[2], pl[3]});
     }
 }
@@ -611,8 +538,7 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
                          int len, int it, bool has_state, float Dh, bool add) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
     const DirPtrs &dp = a.dir[D];
-    const uint16_t *xt = (const uint16_t *)sm.xt;
-    const uint16_t *bn = (const uint16_t *)sm.bn;
+    const uint16_t *bn = sm.bn;
     const int I = it >> 2, wq = it & 3;   // 64-row block, tile inside it
     const int i = 16 * it + l16;          // this lane's row (G^T column)
     const int i0 = 16 * it + 4 * g4;      // first of this lane's output rows
@@ -668,7 +594,7 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
                 split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
                 split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
             }
-            mx_step<Q>(acc, xt, 64 * J + 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
+            mx_step(acc, sm.xs, 64 * J + 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
                        u32x4{pl[0], pl[1], pl[2], pl[3]});
         }
     }
@@ -681,7 +607,7 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
 
     // ---- carried state: e^{cs_i} C_i . H (tiles it does not reach: skipped, exact)
     if (has_state && sm.utile[it]) {
-        const uint16_t *hh = (const uint16_t *)sm.hs;
+        const uint16_t *hh = sm.hs;
         const uint16_t *hl = hh + kP * kNRS;
         f32x4 tt[4];
 #pragma unroll
@@ -715,10 +641,10 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
     }
 
     // ---- skip term (x exact) and output rows i0 + r
-    const int si0 = tperm(i0);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
-        const u32x2 xv = *(const u32x2 *)(xt + xt_at(16 * pt + l16, si0, Q));
+        // x of rows i0..i0+3, column 16 pt + l16 (one transposing read)
+        const u32x2 xv = ld_tr(sm.xs + (i0 + (l16 >> 2)) * kXS + 16 * pt + 4 * (l16 & 3));
         acc[pt][0] = fmaf(Dh, b_lo(xv[0]), acc[pt][0]);
         acc[pt][1] = fmaf(Dh, b_hi(xv[0]), acc[pt][1]);
         acc[pt][2] = fmaf(Dh, b_lo(xv[1]), acc[pt][2]);
@@ -754,48 +680,30 @@ __device__ __forceinline__ int tile_of(int w, int k) {
 }
 
 // H <- gamma H + sum over the chunk's tokens of w_t B_t x_t^T (the wave's
-// block of the state).
+// block of the state). B^T and x come straight from the staged natural tiles
+// through transposing reads: no barrier.
 template <int Q>
-__device__ void chunk_state_update(OutSmem<Q> &sm, f32x4 (&Hacc)[4], int len) {
-    const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
+__device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[4], int len) {
+    const int w = wave_id();
     const int pq = w & 3, nh = w >> 2;
     const float gmm = sm.gamma;
 #pragma unroll
     for (int q = 0; q < 4; ++q) Hacc[q] *= gmm;
-    const uint16_t *bn = (const uint16_t *)sm.bn;
-    const uint16_t *bt = (const uint16_t *)sm.hs;
-    const uint16_t *xt = (const uint16_t *)sm.xt;
     for (int sb = 0; sb < Q / kSub; ++sb) {
         if (kSub * sb >= len) break;
         if (!sm.wsub[sb]) continue;    // every weight is exactly 0
-        {
-            // B^T of the sub-block, transposed inside LDS: one item per thread;
-            // consecutive lanes take consecutive token pairs
-            const int item = threadIdx.x;
-            const int rp = item & 31, cg = item >> 5;
-            const int t = kSub * sb + 2 * rp;
-            const u32x4 r0 = *(const u32x4 *)(bn + t * kNRS + 8 * cg);
-            const u32x4 r1 = *(const u32x4 *)(bn + (t + 1) * kNRS + 8 * cg);
-            const int s = tperm(2 * rp) >> 1;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sm.hs[((8 * cg + 2 * q) * kRS) / 2 + s] = (r0[q] & 0xffffu) | (r1[q] << 16);
-                sm.hs[((8 * cg + 2 * q + 1) * kRS) / 2 + s] = (r0[q] >> 16) | (r1[q] & 0xffff0000u);
-            }
-        }
-        __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks) {
+            const int t32 = kSub * sb + 32 * ks;
             u32x4 bhi, blo;
-            wx_operand(xt, Q, kSub * sb, 16 * pq + l16, sm.w + kSub * sb, ks, bhi, blo);
+            wx_operand(sm.xs, t32, 16 * pq, sm.w, bhi, blo);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const u32x4 aop = *(const u32x4 *)(bt + (16 * (4 * nh + q) + l16) * kRS + 32 * ks + 8 * g4);
+                const u32x4 aop = tr_operand(sm.bn, kNRS, t32, 16 * (4 * nh + q));
                 Hacc[q] = mfma16x16x32(aop, bhi, Hacc[q]);
                 Hacc[q] = mfma16x16x32(aop, blo, Hacc[q]);
             }
         }
-        __syncthreads();
     }
 }
 
@@ -840,15 +748,13 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
                 row_tile<Q, PACKED, D>(a, sm, b, h, grp, c0, len, it, has_state, Dh, add);
         }
         const bool last = s == nch - 1;
-        if (!last || want_final) {
-            __syncthreads();   // row tiles are done with the state area
-            chunk_state_update<Q>(sm, Hacc, len);
-            if (!last) {
-                publish_state<Q>(sm, Hacc);
-                has_state = true;
-            }
-        }
+        if (!last || want_final) chunk_state_update<Q>(sm, Hacc, len);
+        // every wave is done with this chunk's tiles and the published state
         __syncthreads();
+        if (!last) {
+            publish_state<Q>(sm, Hacc);
+            has_state = true;
+        }
     }
     if (want_final) {
         float *fs = a.final_state + ((size_t)b * a.H + h) * PN;
