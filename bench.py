@@ -10,7 +10,12 @@ fp32 accumulation and output.
 
 Prints ONE JSON line. Besides the contract fields it carries:
   roofline      HBM roofline of the dominant kernel (algorithmic bytes per
-                launch / its average HIP-event duration over the timed steps)
+                launch / its average HIP-event duration over the timed steps);
+                `traffic` is the measured HBM bytes per launch from the
+                committed counter summary when it was taken on the kernel
+                source as it stands, else null
+  mfma          the same launches against the dense bf16 matrix-core peak,
+                counting the algorithmic flops of the chunked SSD form
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded
                 sample of the same inputs, with its parity against the GPU
   extra         the long-sequence (32k, 128k), packed-varlen and cached
@@ -28,6 +33,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+METRIC = "BiMamba-2 SSD tokens/s + % HBM/MFMA roofline; block-cached step ms"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ssd_seg_out_layer_1p3b_train_hbm_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_mamba_ssm_amd", "csrc", "ssd_chunked.hip")
 
 
 def bytes_per_token(H, P, N, G, elem):
@@ -35,6 +43,37 @@ def bytes_per_token(H, P, N, G, elem):
     (x, dt, B, C), y (fp32) written once."""
     per_dir = H * P * elem + H * elem + 2 * G * N * elem
     return 2 * per_dir + H * P * 4
+
+
+def flops_per_token(H, P, N, G, Q):
+    """Algorithmic flops per token of the chunked SSD form, both directions:
+    per chunk of Q tokens the Gram matrix C B^T over its causal half (once per
+    group), the masked product with x, the chunk's state contribution and the
+    carried-state output (per head)."""
+    per_dir = G * (Q + 1) * N + H * ((Q + 1) * P + 4 * N * P)
+    return 2 * per_dir
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the kernel source as it stands."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        src_hash = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -46,10 +85,16 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--prefix", type=int, default=262144,
                     help="prefix length of the block-step state")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
 
 
-def time_steps(fn, steps, warmup, torch):
+def time_steps(bm, fn, steps, warmup, torch):
+    """Times `steps` calls after `warmup`; the library's per-launch HIP events
+    (recorded on the stream each kernel is launched on) run over the same
+    timed steps. Returns ms per step, wall seconds, per-kernel (launches,
+    total ms) and the dominant kernel."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -57,33 +102,33 @@ def time_steps(fn, steps, warmup, torch):
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record(s)
-    for _ in range(steps):
-        fn()
-    e1.record(s)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
-
-
-def profile_steps(bm, fn, steps, torch):
-    torch.cuda.synchronize()
     with bm.profile() as prof:
+        e0.record(s)
         for _ in range(steps):
             fn()
-    torch.cuda.synchronize()
+        e1.record(s)
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     ker = {k: (c, t) for k, (c, t) in prof.kernels.items()}
     dom = max(ker, key=lambda k: ker[k][1])
-    return ker, dom
+    return e0.elapsed_time(e1) / steps, wall, ker, dom
 
 
-def roofline_for(ker, dom, bytes_per_launch):
+def roofline_for(ker, dom, bytes_per_launch, traffic=None):
     launches, total_ms = ker[dom]
     avg_s = total_ms / launches / 1e3
     achieved = bytes_per_launch / avg_s / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None, "kernel": dom, "avg_us": round(avg_s * 1e6, 2)}
+            "traffic": traffic, "kernel": dom, "avg_us": round(avg_s * 1e6, 2)}
+
+
+def mfma_for(ker, dom, flops_per_launch):
+    launches, total_ms = ker[dom]
+    tflops = flops_per_launch / (total_ms / launches / 1e3) / 1e12
+    return {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "kernel": dom,
+            "flops_per_launch": flops_per_launch}
 
 
 def main():
@@ -112,15 +157,23 @@ def main():
     def step():
         bm.ssd_fwd(f, b, chunk=w.chunk, y=y, workspace=ws)
 
-    ms, wall = time_steps(step, args.steps, args.warmup, torch)
+    if args.calibrate_copy:
+        # a plain copy of known size: 256 MiB read, 256 MiB written
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms, wall, ker, dom = time_steps(bm, step, args.steps, args.warmup, torch)
     tokens = w.batch * w.seqlen
     bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
-    ker, dom = profile_steps(bm, step, args.steps, torch)
+    fpt = flops_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, w.chunk)
     # the dominant kernel reads every input of the step once and writes y
-    roof = roofline_for(ker, dom, bpt * tokens)
+    roof = roofline_for(ker, dom, bpt * tokens, measured_traffic() if dom == "ssd_seg_out" else None)
 
     out = {
-        "metric": "BiMamba-2 SSD tokens/s (one bidirectional mixer layer)",
+        "metric": METRIC,
         "value": round(tokens / (ms / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -137,7 +190,9 @@ def main():
                    "ngroups": w.ngroups, "chunk": w.chunk, "bidirectional": True,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
+        "mfma": mfma_for(ker, dom, fpt * tokens),
         "algorithmic_bytes_per_token": bpt,
+        "algorithmic_flops_per_token": fpt,
         "kernels_ms_per_step": {k: round(t / args.steps, 4) for k, (c, t) in ker.items()},
         "wall_s_timed": round(wall, 3),
     }
@@ -159,13 +214,15 @@ def extras(args, bm, synth, torch, dev):
         shape = bm.make_shape(f["x"], f["B"], w.chunk)
         ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=dev)
         fn = lambda: bm.ssd_fwd(f, b, chunk=w.chunk, y=y, workspace=ws)  # noqa: E731
-        ms, _ = time_steps(fn, steps, 2, torch)
+        ms, _, ker, dom = time_steps(bm, fn, steps, 2, torch)
         tok = w.batch * w.seqlen
         bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
-        ker, dom = profile_steps(bm, fn, steps, torch)
+        fpt = flops_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, w.chunk)
         res[name] = {"tokens_per_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
                      "hbm_roofline_frac_step": round(bpt * tok / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "roofline": roofline_for(ker, dom, bpt * tok)}
+                     "kernels_ms_per_step": {k: round(t / steps, 4) for k, (c, t) in ker.items()},
+                     "roofline": roofline_for(ker, dom, bpt * tok),
+                     "mfma": mfma_for(ker, dom, fpt * tok)}
         del f, b, y, ws
         torch.cuda.empty_cache()
 
@@ -178,11 +235,12 @@ def extras(args, bm, synth, torch, dev):
     shape = bm.make_shape(f["x"], f["B"], w.chunk)
     ws = torch.empty(max(bm.workspace_size(shape, len(cu) - 1), 256), dtype=torch.uint8, device=dev)
     fn = lambda: bm.ssd_fwd(f, b, chunk=w.chunk, cu_seqlens=cu, y=y, workspace=ws)  # noqa: E731
-    ms, _ = time_steps(fn, steps, 2, torch)
+    ms, _, ker, dom = time_steps(bm, fn, steps, 2, torch)
     bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
     res["packed_varlen"] = {"tokens_per_s": round(w.seqlen / (ms / 1e3), 1),
                             "ms_per_step": round(ms, 4), "tokens": w.seqlen, "nseq": len(cu) - 1,
-                            "hbm_roofline_frac_step": round(bpt * w.seqlen / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+                            "hbm_roofline_frac_step": round(bpt * w.seqlen / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "kernels_ms_per_step": {k: round(t / steps, 4) for k, (c, t) in ker.items()}}
     del f, b, y, ws
     torch.cuda.empty_cache()
 
@@ -211,15 +269,14 @@ def block_step_bench(args, bm, synth, torch, dev, steps):
         f, b = synth.make_inputs(nseq, Lb, H, P, N, G, "bf16", c["seed"], device=dev)
         y = torch.empty(nseq, Lb, H, P, dtype=torch.float32, device=dev)
         fn = lambda: bm.block_step(st, f, b, commit=False, chunk=64, y=y)  # noqa: E731
-        ms, _ = time_steps(fn, max(steps, 10), 3, torch)
+        ms, _, ker, dom = time_steps(bm, fn, max(steps, 10), 3, torch)
         per_seq = H * P * N * 4 + bytes_per_token(H, P, N, G, 2) * Lb
-        ker, dom = profile_steps(bm, fn, max(steps, 10), torch)
         key = f"b{nseq}_prefix{prefix}"
         out[key] = {"ms_per_step": round(ms, 5), "bytes_per_step": per_seq * nseq,
                     "hbm_roofline_frac_step": round(per_seq * nseq / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "roofline": roofline_for(ker, dom, per_seq * nseq)}
         fc = lambda: bm.block_step(st, f, b, commit=True, chunk=64, y=y)  # noqa: E731
-        msc, _ = time_steps(fc, 5, 1, torch)
+        msc, _, _, _ = time_steps(bm, fc, 5, 1, torch)
         out[key]["ms_per_commit_step"] = round(msc, 5)
         st.free()
         del f, b, y

@@ -125,6 +125,23 @@ struct ProfRecord {
 };
 thread_local bool g_prof_on = false;
 thread_local std::vector<ProfRecord> g_prof;
+thread_local std::vector<hipEvent_t> g_event_pool;   // reused across sessions
+
+bool pool_event(hipEvent_t *e) {
+    if (!g_event_pool.empty()) {
+        *e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return true;
+    }
+    return hipEventCreate(e) == hipSuccess;
+}
+void release_records() {
+    for (auto &r : g_prof) {
+        g_event_pool.push_back(r.start);
+        g_event_pool.push_back(r.stop);
+    }
+    g_prof.clear();
+}
 
 }  // namespace
 
@@ -132,8 +149,13 @@ namespace bm {
 void prof_before(const char *name, hipStream_t s) {
     if (!g_prof_on) return;
     ProfRecord r{name, nullptr, nullptr};
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
+    if (!pool_event(&r.start)) {
         (void)hipGetLastError();
+        return;
+    }
+    if (!pool_event(&r.stop)) {
+        (void)hipGetLastError();
+        g_event_pool.push_back(r.start);
         return;
     }
     (void)hipEventRecord(r.start, s);
@@ -155,11 +177,7 @@ extern "C" {
 int bimamba_version(void) { return BIMAMBA_VERSION; }
 
 int bimamba_profile_begin(void) {
-    for (auto &r : g_prof) {
-        (void)hipEventDestroy(r.start);
-        (void)hipEventDestroy(r.stop);
-    }
-    g_prof.clear();
+    release_records();
     g_prof_on = true;
     return BIMAMBA_OK;
 }
@@ -181,10 +199,8 @@ int bimamba_profile_end(char *names, int name_len, int *counts, double *ms, int 
         if (i == seen.size()) { seen.push_back(r.name); cnt.push_back(0); tot.push_back(0.0); }
         cnt[i] += 1;
         tot[i] += t;
-        (void)hipEventDestroy(r.start);
-        (void)hipEventDestroy(r.stop);
     }
-    g_prof.clear();
+    release_records();
     if (status != BIMAMBA_OK) return status;
     for (size_t i = 0; i < seen.size() && (int)i < cap; ++i) {
         if (names && name_len > 0) {
