@@ -116,6 +116,26 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ size_t tok(const SegArgs &a, int b, int t) { return (size_t)b * a.L + t; }
 __device__ __forceinline__ u32x4 ld8(const uint16_t *p) { return *(const u32x4 *)p; }
 
+// Workgroup barrier that orders LDS only: global loads in flight (the next
+// chunk's prefetch) stay in flight across it. Workgroups here exchange data
+// through LDS alone; each y element is read back only by the lane that wrote
+// it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ double wave_scan_d(double v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double n = __shfl_up(v, off, 64);
+        if (lane >= off) v += n;
+    }
+    return v;
+}
+
 __device__ __forceinline__ float wave_scan(float v) {
     const int lane = lane_id();
 #pragma unroll
@@ -315,6 +335,7 @@ constexpr int kOutThreads = 64 * kOutWaves;
 template <int Q>
 struct OutSmem {
     float cs2[Q];          // inclusive scan of a in the walking direction, times log2(e)
+    float rl2[Q];          // the same scan restarted at the token's 64-block (walking order), times log2(e)
     float w[Q];            // state-update weights
     float v16[Q];          // e^{cs(edge of the token's 16-tile) - cs} dt
     float v64[Q];          // e^{cs(edge of the token's 64-block) - cs} dt
@@ -324,103 +345,161 @@ struct OutSmem {
     int utile[Q / 16];     // the carried state reaches some row of the 16-row tile
     int wsub[Q / kSub];    // some weight of the 64-token sub-block is nonzero
     float gamma;           // decay of the whole chunk (0: the state does not pass)
+    float bt2[Q / 64][Q / 64];  // [I][J] (walking order, J < I): sum of a over the blocks strictly between, times log2(e)
     int sq_nb;             // sequence index of the token the carried state comes from
     alignas(16) uint16_t xs[Q * kXS];       // x [t][p], raw bf16
     alignas(16) uint16_t bn[Q * kNRS];      // B [t][n], raw bf16
     alignas(16) uint16_t hs[2 * kP * kNRS]; // H^T [p][n]: bf16 high part, then bf16 residual
 };
 
-// One chunk [c0, c0+len) of direction d: scans, decay factors, weights,
-// skip masks; x and B staged. Threads 0-255 scan a in the walking direction,
-// threads 256-511 toward the outgoing edge, at the same time.
+// Loads of one chunk [c0, c0+len) of direction D, issued ahead of use (the
+// next chunk's are issued before the current chunk's state update, so their
+// latency overlaps it): x and B for every thread, and for waves 0 and 1 the
+// dt (and sequence index) of the chunk's tokens, Q/64 per lane, in walking
+// order (wave 0) or from the outgoing edge (wave 1).
 template <int Q>
-__device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, int d, int b, int h, int grp, int c0,
-                           int len) {
-    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
-    const int g = tid >> 8, t = tid & 255, wq = wv & 3;
-    const DirPtrs &dp = a.dir[d];
-    const uint16_t *DT = (const uint16_t *)dp.dt;
-    const float Ah = dp.A[h];
-    // group 0: position in the walking direction; group 1: toward the edge
-    const int pos = (g == 0) == (d == 0) ? t : Q - 1 - t;
-    const bool in = t < Q && pos < len;
-    // the small loads first: the scans wait only for them
-    float dtt = 0.f;
-    int sq = 0;
-    if (in) {
-        dtt = bf2f(DT[tok(a, b, c0 + pos) * a.H + h]);
-        if (a.seq) sq = a.seq[tok(a, b, c0 + pos)];
-    }
-    int sq_nb = 0, sq_edge = 0;
-    bool has_nb = true;
-    if (a.seq) {
-        const int nb = d == 0 ? c0 - 1 : c0 + len;
-        has_nb = d == 0 ? c0 > 0 : c0 + len < a.L;
-        sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
-        sq_edge = a.seq[tok(a, b, d == 0 ? c0 + len - 1 : c0)];
-    }
+struct ChunkLoads {
+    static constexpr int TPL = Q / 64;   // tokens per lane of the scanning waves
     RowStage<Q, kP, kXS, kOutThreads> sx;
     RowStage<Q, kN, kNRS, kOutThreads> sb;
-    sx.load((const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP, (uint32_t)(a.H * kP), len);
-    sb.load((const uint16_t *)dp.B + (tok(a, b, c0) * a.G + grp) * kN, (uint32_t)(a.G * kN), len);
+    uint16_t dtv[TPL];   // raw bf16 bits: no use (and no wait) until the scan
+    int sqv[TPL];
 
-    const float at = dtt * Ah;
-    float v = wave_scan(at);
-    if (lane == 63) sm.tmp[wv] = v;
-    __syncthreads();
-    float add = 0.f, total = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float s = sm.tmp[4 * g + k];
-        if (k < wq) add += s;
-        total += s;
+    // position in the chunk of the lane's i-th token; walking order for wave
+    // 0, from the outgoing edge for wave 1
+    __device__ static __forceinline__ int pos_of(int d, int wv, int lane, int i) {
+        const int k = lane * TPL + i;
+        return (wv == 0) == (d == 0) ? k : Q - 1 - k;
     }
-    v += add;
-    if (g == 0) {
-        bool reach = false;
-        if (t < Q) {
-            sm.cs2[pos] = v * kLog2e;
-            sm.dt[pos] = dtt;
-            sm.sq[pos] = sq;
-            reach = in && (!a.seq || sq == sq_nb) && v >= kDead;
-        }
-        const unsigned long long m = __ballot(reach);
-        if (lane == 0 && 64 * wq < Q) {
+
+    __device__ __forceinline__ void issue(const SegArgs &a, int d, int b, int h, int grp, int c0,
+                                          int len) {
+        const DirPtrs &dp = a.dir[d];
+        const int wv = wave_id(), lane = lane_id();
+        if (wv < 2) {
+            const uint16_t *DT = (const uint16_t *)dp.dt;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int tile = d == 0 ? 4 * wq + k : Q / 16 - 1 - 4 * wq - k;
-                sm.utile[tile] = ((m >> (16 * k)) & 0xffffull) != 0;
+            for (int i = 0; i < TPL; ++i) {
+                const int pos = pos_of(d, wv, lane, i);
+                dtv[i] = 0;
+                sqv[i] = 0;
+                if (pos < len) {
+                    dtv[i] = DT[tok(a, b, c0 + pos) * a.H + h];
+                    if (a.seq) sqv[i] = a.seq[tok(a, b, c0 + pos)];
+                }
             }
         }
-        if (tid == 0) {
-            bool carry = true;
-            if (a.seq) carry = has_nb && sq_nb == sq_edge;
-            sm.gamma = carry ? expf(total) : 0.f;
-            sm.sq_nb = a.seq ? sq_nb : 0;
+        sx.load((const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP, (uint32_t)(a.H * kP), len);
+        sb.load((const uint16_t *)dp.B + (tok(a, b, c0) * a.G + grp) * kN, (uint32_t)(a.G * kN), len);
+    }
+};
+
+// One chunk [c0, c0+len) of direction d: scans, decay factors, weights, skip
+// masks, staged x and B; one barrier. Wave 0 scans a over the chunk in the
+// walking direction, wave 1 toward the outgoing edge, each with Q/64 tokens
+// per lane; the tile-edge values come from lane shuffles.
+template <int Q>
+__device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, int d, int b,
+                           int h, int c0, int len) {
+    constexpr int TPL = ChunkLoads<Q>::TPL;
+    const int lane = lane_id(), wv = wave_id();
+    const float Ah = a.dir[d].A[h];
+    ld.sx.store(len, sm.xs);
+    ld.sb.store(len, sm.bn);
+    if (wv < 2) {
+        int sq_nb = 0, sq_edge = 0;
+        bool has_nb = true;
+        if (a.seq) {
+            const int nb = d == 0 ? c0 - 1 : c0 + len;
+            has_nb = d == 0 ? c0 > 0 : c0 + len < a.L;
+            sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
+            sq_edge = a.seq[tok(a, b, d == 0 ? c0 + len - 1 : c0)];
         }
-    } else {
-        // exclusive sum toward the outgoing edge -> weight of the token in the
-        // state leaving the chunk
-        float wt = 0.f;
-        if (in && (!a.seq || sq == sq_edge)) wt = expf(v - at) * dtt;
-        if (t < Q) sm.w[pos] = wt;
-        const unsigned long long m = __ballot(wt != 0.f);
-        if (lane == 0 && 64 * wq < Q) sm.wsub[d == 0 ? Q / 64 - 1 - wq : wq] = m != 0ull;
+        // inclusive scan over the lane's tokens, then across lanes, in fp64:
+        // every exponent below is a difference of these sums, formed in fp64
+        // and rounded once, so none is the difference of two large fp32 values
+        float at[TPL], dtf[TPL];
+        double cs[TPL];
+        double run = 0.0;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            dtf[i] = bf2f(ld.dtv[i]);
+            at[i] = dtf[i] * Ah;
+            run += (double)at[i];
+            cs[i] = run;
+        }
+        const double incl = wave_scan_d(run);
+        const double excl = incl - run;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) cs[i] += excl;
+        if (wv == 0) {
+            // in walking order a token's 16-tile (64-block) ends at the last
+            // token of lane (lane | (16/TPL - 1)) (resp. lane | (64/TPL - 1));
+            // its 64-block starts after the last token of lane
+            // (lane & ~(64/TPL - 1)) - 1
+            const double last = cs[TPL - 1];
+            const double e16 = __shfl(last, lane | (16 / TPL - 1), 64);
+            const double e64 = __shfl(last, lane | (64 / TPL - 1), 64);
+            const int sl = (lane & ~(64 / TPL - 1)) - 1;
+            const double b64 = __shfl(last, sl < 0 ? 0 : sl, 64);
+            const double start = sl < 0 ? 0.0 : b64;
+            bool reach = false;
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const int pos = ChunkLoads<Q>::pos_of(d, 0, lane, i);
+                const float dtv = dtf[i];
+                sm.cs2[pos] = (float)(cs[i] * kLog2e);
+                sm.rl2[pos] = (float)((cs[i] - start) * kLog2e);
+                sm.dt[pos] = dtv;
+                sm.sq[pos] = ld.sqv[i];
+                sm.v16[pos] = exp2_((float)((e16 - cs[i]) * kLog2e)) * dtv;
+                sm.v64[pos] = exp2_((float)((e64 - cs[i]) * kLog2e)) * dtv;
+                reach |= pos < len && (!a.seq || ld.sqv[i] == sq_nb) && cs[i] >= kDead;
+            }
+            // block table: the last token of walking block K is lane
+            // 64/TPL*(K+1) - 1; bt2[I][J] = cs(end of I-1) - cs(end of J)
+            {
+                const bool tl = lane < (Q / 64) * (Q / 64);
+                const int I = tl ? lane / (Q / 64) : 0, J = tl ? lane % (Q / 64) : 0;
+                const double eI = __shfl(last, (64 / TPL) * (I > 0 ? I : 1) - 1, 64);
+                const double eJ = __shfl(last, (64 / TPL) * (J + 1) - 1, 64);
+                if (tl) sm.bt2[I][J] = J < I ? (float)((eI - eJ) * kLog2e) : 0.f;
+            }
+            // 16-tiles (walking order m) the carried state reaches
+            const unsigned long long m = __ballot(reach);
+            if (lane < Q / 16) {
+                constexpr int LPT = 16 / TPL;   // lanes per 16-tile
+                const bool any = ((m >> (lane * LPT)) & ((1ull << LPT) - 1)) != 0;
+                sm.utile[d == 0 ? lane : Q / 16 - 1 - lane] = any;
+            }
+            if (lane == 63) {
+                bool carry = true;
+                if (a.seq) carry = has_nb && sq_nb == sq_edge;
+                sm.gamma = carry ? (float)exp(last) : 0.f;
+                sm.sq_nb = a.seq ? sq_nb : 0;
+            }
+        } else {
+            // exclusive sums toward the outgoing edge -> weight of each token
+            // in the state leaving the chunk
+            bool nz = false;
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const int pos = ChunkLoads<Q>::pos_of(d, 1, lane, i);
+                float wt = 0.f;
+                if (pos < len && (!a.seq || ld.sqv[i] == sq_edge))
+                    wt = expf((float)(cs[i] - (double)at[i])) * dtf[i];
+                sm.w[pos] = wt;
+                nz |= wt != 0.f;
+            }
+            const unsigned long long m = __ballot(nz);
+            if (lane < Q / 64) {
+                constexpr int LPS = 64 / TPL;   // lanes per 64-token sub-block
+                const bool any = LPS == 64 ? m != 0ull : ((m >> (lane * LPS)) & ((1ull << (LPS & 63)) - 1)) != 0;
+                sm.wsub[d == 0 ? Q / 64 - 1 - lane : lane] = any;
+            }
+        }
     }
-    sx.store(len, sm.xs);
-    sb.store(len, sm.bn);
-    __syncthreads();
-    if (tid < Q) {
-        // decay of each token to the edge of its 16-tile / 64-block nearest
-        // the diagonal: its last token (forward, j <= i) or first (reverse)
-        const int j = tid;
-        const int r16 = d == 0 ? (j | 15) : (j & ~15);
-        const int r64 = d == 0 ? (j | 63) : (j & ~63);
-        const float c = sm.cs2[j];
-        sm.v16[j] = exp2_(sm.cs2[r16] - c) * sm.dt[j];
-        sm.v64[j] = exp2_(sm.cs2[r64] - c) * sm.dt[j];
-    }
-    __syncthreads();
+    lds_barrier();
 }
 
 // The wave's state block (p-tile w%4, n-half w/4; fp32 accumulators) into
@@ -483,7 +562,7 @@ __device__ __forceinline__ void seq_mask(float (&mv)[4], const OutSmem<Q> &sm, i
 // itself takes one exponential per entry.
 template <int Q, bool PACKED, int D, int WQ>
 __device__ __forceinline__ void diag_block(f32x4 (&acc)[4], const OutSmem<Q> &sm,
-                                           const u32x4 (&cr)[kN / 32], int I, int i, float csi,
+                                           const u32x4 (&cr)[kN / 32], int I, int i, float rli,
                                            int sqi) {
     const int g4 = lane_id() >> 4;
     const uint16_t *bn = sm.bn;
@@ -500,18 +579,20 @@ __device__ __forceinline__ void diag_block(f32x4 (&acc)[4], const OutSmem<Q> &sm
                 const f32x4 gg = gram_tile(bn, j0, cr);
                 const int jb = j0 + 4 * g4;
                 if (jt != WQ) {
-                    const float u16 = exp2_(csi - sm.cs2[D == 0 ? j0 + 15 : j0]);
+                    // the J-tile's edge is in this 64-block: both exponents
+                    // are relative to the block's start
+                    const float u16 = exp2_(rli - sm.rl2[D == 0 ? j0 + 15 : j0]);
                     const f32x4 vv = *(const f32x4 *)(sm.v16 + jb);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u16 * vv[r]);
                 } else {
-                    const f32x4 c4 = *(const f32x4 *)(sm.cs2 + jb);
+                    const f32x4 c4 = *(const f32x4 *)(sm.rl2 + jb);
                     const f32x4 d4 = *(const f32x4 *)(sm.dt + jb);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = jb + r;
                         const bool tri = D == 0 ? j <= i : j >= i;
-                        const float e = exp2_(csi - c4[r]);
+                        const float e = exp2_(rli - c4[r]);
                         mv[r] = tri ? gg[r] * (e * d4[r]) : 0.f;
                     }
                 }
@@ -555,29 +636,25 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
     uint32_t yoff[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) yoff[r] = (uint32_t)min(i0 + r, len - 1) * ystride;
-    float prev[4][4];
-    if (add) {
-        // the reverse pass wrote these rows; fetched now, used at the end
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) prev[pt][r] = ybase[yoff[r] + 16 * pt];
-    }
-    const float csi = sm.cs2[i];
+    const float rli = sm.rl2[i];
     const int sqi = PACKED ? sm.sq[i] : 0;
     f32x4 acc[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
 
     // ---- 64-column blocks off the diagonal: M = G e^{cs_i - cs_r} v64_j,
-    // r the block's edge nearest the diagonal
+    // r the block's edge nearest the diagonal (its last token in walking
+    // order)
     const int nJ = D == 0 ? I : (len + 63) / 64 - 1 - I;
+    const int Iw = D == 0 ? I : Q / 64 - 1 - I;   // walking-order block of the rows
     for (int q = 0; q < nJ; ++q) {
         const int J = D == 0 ? q : I + 1 + q;
-        const float near = D == 0 ? sm.cs2[64 * I] - sm.cs2[64 * J + 63]
-                                  : sm.cs2[64 * I + 63] - sm.cs2[64 * J];
-        if (near < kDead * kLog2e) continue;   // every entry is exactly 0
-        const float u64 = exp2_(csi - sm.cs2[D == 0 ? 64 * J + 63 : 64 * J]);
+        const int Jw = D == 0 ? J : Q / 64 - 1 - J;
+        // e^{cs_i - cs_r} = e^{rl_i} e^{(sum of a over the blocks between)}, r
+        // the column block's edge; every entry is at most e^{bt2}
+        const float between = sm.bt2[Iw][Jw];
+        if (between < kDead * kLog2e) continue;   // every entry is exactly 0
+        const float u64 = exp2_(rli + between);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             uint32_t ph[4], pl[4];
@@ -599,10 +676,20 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
         }
     }
     switch (wq) {
-        case 0: diag_block<Q, PACKED, D, 0>(acc, sm, cr, I, i, csi, sqi); break;
-        case 1: diag_block<Q, PACKED, D, 1>(acc, sm, cr, I, i, csi, sqi); break;
-        case 2: diag_block<Q, PACKED, D, 2>(acc, sm, cr, I, i, csi, sqi); break;
-        default: diag_block<Q, PACKED, D, 3>(acc, sm, cr, I, i, csi, sqi); break;
+        case 0: diag_block<Q, PACKED, D, 0>(acc, sm, cr, I, i, rli, sqi); break;
+        case 1: diag_block<Q, PACKED, D, 1>(acc, sm, cr, I, i, rli, sqi); break;
+        case 2: diag_block<Q, PACKED, D, 2>(acc, sm, cr, I, i, rli, sqi); break;
+        default: diag_block<Q, PACKED, D, 3>(acc, sm, cr, I, i, rli, sqi); break;
+    }
+
+    float prev[4][4];
+    if (add) {
+        // the reverse pass wrote these rows; fetched here so that the loads
+        // overlap the carried-state products
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) prev[pt][r] = ybase[yoff[r] + 16 * pt];
     }
 
     // ---- carried state: e^{cs_i} C_i . H (tiles it does not reach: skipped, exact)
@@ -736,11 +823,21 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
 
     const int nch = clast - cfirst + 1;
     const bool want_final = D == 0 && seg == a.nseg - 1 && a.final_state;
-    for (int s = 0; s < nch; ++s) {
+    auto chunk_at = [&](int s, int &c0, int &len) {
         const int c = D == 0 ? cfirst + s : clast - s;
-        const int c0 = c * Q;
-        const int len = min(Q, a.L - c0);
-        chunk_prep<Q>(a, sm, D, b, h, grp, c0, len);
+        c0 = c * Q;
+        len = min(Q, a.L - c0);
+    };
+    ChunkLoads<Q> ld;
+    {
+        int c0, len;
+        chunk_at(0, c0, len);
+        ld.issue(a, D, b, h, grp, c0, len);
+    }
+    for (int s = 0; s < nch; ++s) {
+        int c0, len;
+        chunk_at(s, c0, len);
+        chunk_prep<Q>(a, sm, ld, D, b, h, c0, len);
 #pragma unroll 1
         for (int k = 0; k < 2; ++k) {
             const int it = tile_of<Q>(w, k);
@@ -748,9 +845,17 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
                 row_tile<Q, PACKED, D>(a, sm, b, h, grp, c0, len, it, has_state, Dh, add);
         }
         const bool last = s == nch - 1;
+        {
+            // next chunk's loads (the last chunk re-reads its own: the loads
+            // stay unconditional, so the registers they fill are dead across
+            // the row tiles)
+            int c0n, lenn;
+            chunk_at(last ? s : s + 1, c0n, lenn);
+            ld.issue(a, D, b, h, grp, c0n, lenn);
+        }
         if (!last || want_final) chunk_state_update<Q>(sm, Hacc, len);
         // every wave is done with this chunk's tiles and the published state
-        __syncthreads();
+        lds_barrier();
         if (!last) {
             publish_state<Q>(sm, Hacc);
             has_state = true;
