@@ -815,12 +815,6 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
         if (seg == a.nseg - 1) src = nullptr;
         else src = a.gam[slot(1, seg + 1)] == 0.f ? a.S + slot(1, seg + 1) * PN : a.Hs + slot(1, seg) * PN;
     }
-    f32x4 Hacc[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
-    bool has_state = src != nullptr;
-    if (has_state) publish_state<Q>(sm, Hacc);
-
     const int nch = clast - cfirst + 1;
     const bool want_final = D == 0 && seg == a.nseg - 1 && a.final_state;
     auto chunk_at = [&](int s, int &c0, int &len) {
@@ -828,12 +822,19 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
         c0 = c * Q;
         len = min(Q, a.L - c0);
     };
+    // the first chunk's loads go out before the incoming state is read, so
+    // the two round trips overlap
     ChunkLoads<Q> ld;
     {
         int c0, len;
         chunk_at(0, c0, len);
         ld.issue(a, D, b, h, grp, c0, len);
     }
+    f32x4 Hacc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
+    bool has_state = src != nullptr;
+    if (has_state) publish_state<Q>(sm, Hacc);
     for (int s = 0; s < nch; ++s) {
         int c0, len;
         chunk_at(s, c0, len);
@@ -870,14 +871,18 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
 
 template <int Q, bool PACKED>
 __global__ void __launch_bounds__(kOutThreads) k_seg_out(const SegArgs a) {
-    // XCD-aware order: consecutive workgroups go to different XCDs
-    // (round-robin by 8), so the 8 streams of work that share one XCD's L2 are
-    // made to hold the same (row, segment) and share its B and C.
+    // XCD-aware order: consecutive workgroup ids go round-robin over the 8
+    // XCDs, so XCD x runs ids x, x+8, x+16, ... It is given the contiguous
+    // range [x*per, (x+1)*per) of the (row-segment, head) pairs in
+    // head-fastest order: every XCD gets the same share, and the workgroups
+    // that share one XCD's L2 mostly hold the same (row, segment), so its B
+    // and C are read from HBM once.
     const int id = blockIdx.x;
-    const int xcd = id & 7, r8 = id >> 3;
-    const int h = r8 % a.H;
-    const int rs = (r8 / a.H) * 8 + xcd;        // (row, segment) index
-    if (rs >= a.batch * a.nseg) return;
+    const int total = a.batch * a.nseg * a.H;
+    const int per = (total + 7) / 8;
+    const int lin = (id & 7) * per + (id >> 3);
+    if (lin >= total) return;
+    const int rs = lin / a.H, h = lin % a.H;     // (row, segment) index, head
     const int b = rs / a.nseg, seg = rs % a.nseg;
     const int grp = h / (a.H / a.G);
     __shared__ __attribute__((aligned(16))) OutSmem<Q> sm;
@@ -905,11 +910,11 @@ hipError_t launch_q(const SegArgs &a, hipStream_t s) {
         BM_LAUNCH("ssd_seg_scan", k_seg_scan, dim3(kP * kN / 256, a.H, a.batch * nd), dim3(256), 0,
                   s, a);
     }
-    const int groups = (a.batch * a.nseg + 7) / 8;
+    const int per_xcd = (a.batch * a.nseg * a.H + 7) / 8;
     if (a.seq)
-        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true>), dim3(groups * 8 * a.H), dim3(kOutThreads), 0, s, a);
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true>), dim3(per_xcd * 8), dim3(kOutThreads), 0, s, a);
     else
-        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, false>), dim3(groups * 8 * a.H), dim3(kOutThreads), 0, s, a);
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, false>), dim3(per_xcd * 8), dim3(kOutThreads), 0, s, a);
     return hipGetLastError();
 }
 
