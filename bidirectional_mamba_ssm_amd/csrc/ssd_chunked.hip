@@ -157,15 +157,21 @@ struct RowStage {
     static constexpr int ITEMS = ROWS * CG;
     static constexpr int PER = (ITEMS + NT - 1) / NT;
     u32x4 v[PER];
-    __device__ __forceinline__ void load(const uint16_t *m0, uint32_t rstride, int tlimit) {
+    // items k0 <= k < k1 of this thread (the loads can be spread over a loop)
+    __device__ __forceinline__ void load_part(const uint16_t *m0, uint32_t rstride, int tlimit,
+                                              int k0, int k1) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
+            if (k < k0 || k >= k1) continue;
             const int item = threadIdx.x + k * NT;
             if (ITEMS % NT == 0 || item < ITEMS) {
                 const int row = item / CG, cg = item % CG;
                 v[k] = ld8(m0 + (uint32_t)min(row, tlimit - 1) * rstride + 8 * cg);
             }
         }
+    }
+    __device__ __forceinline__ void load(const uint16_t *m0, uint32_t rstride, int tlimit) {
+        load_part(m0, rstride, tlimit, 0, PER);
     }
     __device__ __forceinline__ void store(int tlimit, uint16_t *dst) {
 #pragma unroll
@@ -372,7 +378,12 @@ struct ChunkLoads {
         return (wv == 0) == (d == 0) ? k : Q - 1 - k;
     }
 
-    __device__ __forceinline__ void issue(const SegArgs &a, int d, int b, int h, int grp, int c0,
+    const uint16_t *x0, *b0;
+    uint32_t xstride, bstride;
+    int tl;
+
+    // dt (waves 0, 1) now; x and B in `parts` slices through part()
+    __device__ __forceinline__ void begin(const SegArgs &a, int d, int b, int h, int grp, int c0,
                                           int len) {
         const DirPtrs &dp = a.dir[d];
         const int wv = wave_id(), lane = lane_id();
@@ -389,8 +400,21 @@ struct ChunkLoads {
                 }
             }
         }
-        sx.load((const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP, (uint32_t)(a.H * kP), len);
-        sb.load((const uint16_t *)dp.B + (tok(a, b, c0) * a.G + grp) * kN, (uint32_t)(a.G * kN), len);
+        x0 = (const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP;
+        b0 = (const uint16_t *)dp.B + (tok(a, b, c0) * a.G + grp) * kN;
+        xstride = (uint32_t)(a.H * kP);
+        bstride = (uint32_t)(a.G * kN);
+        tl = len;
+    }
+    // the s-th of n equal slices of the x and B loads
+    __device__ __forceinline__ void part(int s, int n) {
+        sx.load_part(x0, xstride, tl, s * sx.PER / n, (s + 1) * sx.PER / n);
+        sb.load_part(b0, bstride, tl, s * sb.PER / n, (s + 1) * sb.PER / n);
+    }
+    __device__ __forceinline__ void issue(const SegArgs &a, int d, int b, int h, int grp, int c0,
+                                          int len) {
+        begin(a, d, b, h, grp, c0, len);
+        part(0, 1);
     }
 };
 
@@ -536,11 +560,32 @@ __device__ __forceinline__ f32x4 gram_tile(const uint16_t *bn, int j0, const u32
 // transposing reads deliver x.
 __device__ __forceinline__ void mx_step(f32x4 (&acc)[4], const uint16_t *xs, int j32, u32x4 mhi,
                                         u32x4 mlo) {
+    u32x4 xo[4];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-        const u32x4 xo = tr_operand(xs, kXS, j32, 16 * pt);
-        acc[pt] = mfma16x16x32(mhi, xo, acc[pt]);
-        acc[pt] = mfma16x16x32(mlo, xo, acc[pt]);
+    for (int pt = 0; pt < 4; ++pt) xo[pt] = tr_operand(xs, kXS, j32, 16 * pt);
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16x16x32(mhi, xo[pt], acc[pt]);
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16x16x32(mlo, xo[pt], acc[pt]);
+}
+
+// Two G^T tiles (rows j0a.., j0b..) at once: all operand loads first, then
+// the two MFMA chains interleaved.
+__device__ __forceinline__ void gram_pair(const uint16_t *bn, int j0a, int j0b,
+                                          const u32x4 (&cr)[kN / 32], f32x4 &ga, f32x4 &gb) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+    u32x4 oa[kN / 32], ob[kN / 32];
+#pragma unroll
+    for (int ks = 0; ks < kN / 32; ++ks) {
+        oa[ks] = *(const u32x4 *)(bn + (j0a + l16) * kNRS + 32 * ks + 8 * g4);
+        ob[ks] = *(const u32x4 *)(bn + (j0b + l16) * kNRS + 32 * ks + 8 * g4);
+    }
+    ga = zero4();
+    gb = zero4();
+#pragma unroll
+    for (int ks = 0; ks < kN / 32; ++ks) {
+        ga = mfma16x16x32(oa[ks], cr[ks], ga);
+        gb = mfma16x16x32(ob[ks], cr[ks], gb);
     }
 }
 
@@ -658,10 +703,12 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             uint32_t ph[4], pl[4];
+            f32x4 gp[2];
+            gram_pair(bn, 64 * J + 32 * kk, 64 * J + 32 * kk + 16, cr, gp[0], gp[1]);
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int j0 = 64 * J + 32 * kk + 16 * half;
-                const f32x4 gg = gram_tile(bn, j0, cr);
+                const f32x4 gg = gp[half];
                 const int jb = j0 + 4 * g4;
                 const f32x4 vv = *(const f32x4 *)(sm.v64 + jb);
                 float mv[4];
@@ -770,15 +817,21 @@ __device__ __forceinline__ int tile_of(int w, int k) {
 // block of the state). B^T and x come straight from the staged natural tiles
 // through transposing reads: no barrier.
 template <int Q>
-__device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[4], int len) {
+__device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[4], int len, bool math,
+                                   ChunkLoads<Q> &nxt) {
     const int w = wave_id();
     const int pq = w & 3, nh = w >> 2;
-    const float gmm = sm.gamma;
+    if (math) {
+        const float gmm = sm.gamma;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) Hacc[q] *= gmm;
+        for (int q = 0; q < 4; ++q) Hacc[q] *= gmm;
+    }
+#pragma unroll
     for (int sb = 0; sb < Q / kSub; ++sb) {
-        if (kSub * sb >= len) break;
-        if (!sm.wsub[sb]) continue;    // every weight is exactly 0
+        // a slice of the next chunk's loads per sub-block, so the memory
+        // pipeline works beside the matrix cores
+        nxt.part(sb, Q / kSub);
+        if (!math || kSub * sb >= len || !sm.wsub[sb]) continue;   // every weight is exactly 0
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks) {
             const int t32 = kSub * sb + 32 * ks;
@@ -847,14 +900,14 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
         }
         const bool last = s == nch - 1;
         {
-            // next chunk's loads (the last chunk re-reads its own: the loads
-            // stay unconditional, so the registers they fill are dead across
-            // the row tiles)
+            // next chunk's loads, spread over the state update (the last chunk
+            // re-reads its own: the loads stay unconditional, so the registers
+            // they fill are dead across the row tiles)
             int c0n, lenn;
             chunk_at(last ? s : s + 1, c0n, lenn);
-            ld.issue(a, D, b, h, grp, c0n, lenn);
+            ld.begin(a, D, b, h, grp, c0n, lenn);
         }
-        if (!last || want_final) chunk_state_update<Q>(sm, Hacc, len);
+        chunk_state_update<Q>(sm, Hacc, len, !last || want_final, ld);
         // every wave is done with this chunk's tiles and the published state
         lds_barrier();
         if (!last) {
