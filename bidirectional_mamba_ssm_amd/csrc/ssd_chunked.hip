@@ -615,13 +615,22 @@ __device__ __forceinline__ void diag_block(f32x4 (&acc)[4], const OutSmem<Q> &sm
     for (int kk = 0; kk < 2; ++kk) {
         if (D == 0 ? 2 * kk > WQ : 2 * kk + 1 < WQ) continue;   // both tiles dead
         uint32_t ph[4], pl[4];
+        const bool live0 = D == 0 ? 2 * kk <= WQ : 2 * kk >= WQ;
+        const bool live1 = D == 0 ? 2 * kk + 1 <= WQ : 2 * kk + 1 >= WQ;
+        f32x4 gp[2];
+        if (live0 && live1) {
+            gram_pair(bn, 64 * I + 32 * kk, 64 * I + 32 * kk + 16, cr, gp[0], gp[1]);
+        } else {
+            gp[0] = live0 ? gram_tile(bn, 64 * I + 32 * kk, cr) : zero4();
+            gp[1] = live1 ? gram_tile(bn, 64 * I + 32 * kk + 16, cr) : zero4();
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int jt = 2 * kk + half;
             const int j0 = 64 * I + 16 * jt;
             float mv[4] = {0.f, 0.f, 0.f, 0.f};
             if (D == 0 ? jt <= WQ : jt >= WQ) {
-                const f32x4 gg = gram_tile(bn, j0, cr);
+                const f32x4 gg = gp[half];
                 const int jb = j0 + 4 * g4;
                 if (jt != WQ) {
                     // the J-tile's edge is in this 64-block: both exponents
@@ -748,12 +757,17 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
         for (int pt = 0; pt < 4; ++pt) tt[pt] = zero4();
 #pragma unroll
         for (int ks = 0; ks < kN / 32; ++ks) {
+            u32x4 oh[4], ol[4];
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 const int o = (16 * pt + l16) * kNRS + 32 * ks + 8 * g4;
-                tt[pt] = mfma16x16x32(cr[ks], *(const u32x4 *)(hh + o), tt[pt]);
-                tt[pt] = mfma16x16x32(cr[ks], *(const u32x4 *)(hl + o), tt[pt]);
+                oh[pt] = *(const u32x4 *)(hh + o);
+                ol[pt] = *(const u32x4 *)(hl + o);
             }
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32(cr[ks], oh[pt], tt[pt]);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32(cr[ks], ol[pt], tt[pt]);
         }
         const f32x4 c4 = *(const f32x4 *)(sm.cs2 + i0);
         float uu[4];
@@ -835,14 +849,15 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[4], int l
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks) {
             const int t32 = kSub * sb + 32 * ks;
+            u32x4 aop[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) aop[q] = tr_operand(sm.bn, kNRS, t32, 16 * (4 * nh + q));
             u32x4 bhi, blo;
             wx_operand(sm.xs, t32, 16 * pq, sm.w, bhi, blo);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 aop = tr_operand(sm.bn, kNRS, t32, 16 * (4 * nh + q));
-                Hacc[q] = mfma16x16x32(aop, bhi, Hacc[q]);
-                Hacc[q] = mfma16x16x32(aop, blo, Hacc[q]);
-            }
+            for (int q = 0; q < 4; ++q) Hacc[q] = mfma16x16x32(aop[q], bhi, Hacc[q]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Hacc[q] = mfma16x16x32(aop[q], blo, Hacc[q]);
         }
     }
 }
