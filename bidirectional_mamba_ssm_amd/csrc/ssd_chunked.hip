@@ -126,13 +126,27 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// fp64 value moved across lanes by a DPP control (both 32-bit halves);
+// lanes without a source (or outside ROWMASK) read 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_d(double v) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    int lo = (int)(unsigned)(u & 0xffffffffull), hi = (int)(unsigned)(u >> 32);
+    lo = __builtin_amdgcn_update_dpp(0, lo, CTRL, ROWMASK, 0xf, true);
+    hi = __builtin_amdgcn_update_dpp(0, hi, CTRL, ROWMASK, 0xf, true);
+    return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Inclusive fp64 scan over the wave's 64 lanes with DPP lane moves (no LDS
+// round trips): shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the
+// row totals broadcast into the following rows.
 __device__ __forceinline__ double wave_scan_d(double v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double n = __shfl_up(v, off, 64);
-        if (lane >= off) v += n;
-    }
+    v += dpp_d<0x111, 0xf>(v);   // row_shr:1
+    v += dpp_d<0x112, 0xf>(v);   // row_shr:2
+    v += dpp_d<0x114, 0xf>(v);   // row_shr:4
+    v += dpp_d<0x118, 0xf>(v);   // row_shr:8
+    v += dpp_d<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_d<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
     return v;
 }
 
@@ -418,6 +432,26 @@ struct ChunkLoads {
     }
 };
 
+// Stores the T values a scanning lane holds for its consecutive tokens
+// (walking order k = lane*T + i) into a per-token array: ascending positions
+// when `asc`, else descending (pos = Q-1-k); one vector store.
+template <int Q, int T, typename V>
+__device__ __forceinline__ void store_run(V *dst, bool asc, int lane, const V (&v)[T]) {
+    const int base = asc ? lane * T : Q - (lane + 1) * T;
+    V o[T];
+#pragma unroll
+    for (int i = 0; i < T; ++i) o[i] = asc ? v[i] : v[T - 1 - i];
+    if constexpr (T == 4) {
+        typedef V v4 __attribute__((ext_vector_type(4)));
+        *(v4 *)(dst + base) = v4{o[0], o[1], o[2], o[3]};
+    } else if constexpr (T == 2) {
+        typedef V v2 __attribute__((ext_vector_type(2)));
+        *(v2 *)(dst + base) = v2{o[0], o[1]};
+    } else {
+        dst[base] = o[0];
+    }
+}
+
 // One chunk [c0, c0+len) of direction d: scans, decay factors, weights, skip
 // masks, staged x and B; one barrier. Wave 0 scans a over the chunk in the
 // walking direction, wave 1 toward the outgoing edge, each with Q/64 tokens
@@ -468,18 +502,23 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, 
             const double b64 = __shfl(last, sl < 0 ? 0 : sl, 64);
             const double start = sl < 0 ? 0.0 : b64;
             bool reach = false;
+            float c2v[TPL], rlv[TPL], v16v[TPL], v64v[TPL];
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
                 const int pos = ChunkLoads<Q>::pos_of(d, 0, lane, i);
-                const float dtv = dtf[i];
-                sm.cs2[pos] = (float)(cs[i] * kLog2e);
-                sm.rl2[pos] = (float)((cs[i] - start) * kLog2e);
-                sm.dt[pos] = dtv;
-                sm.sq[pos] = ld.sqv[i];
-                sm.v16[pos] = exp2_((float)((e16 - cs[i]) * kLog2e)) * dtv;
-                sm.v64[pos] = exp2_((float)((e64 - cs[i]) * kLog2e)) * dtv;
+                c2v[i] = (float)(cs[i] * kLog2e);
+                rlv[i] = (float)((cs[i] - start) * kLog2e);
+                v16v[i] = exp2_((float)((e16 - cs[i]) * kLog2e)) * dtf[i];
+                v64v[i] = exp2_((float)((e64 - cs[i]) * kLog2e)) * dtf[i];
                 reach |= pos < len && (!a.seq || ld.sqv[i] == sq_nb) && cs[i] >= kDead;
             }
+            const bool asc = d == 0;   // wave 0 walks ascending positions forward
+            store_run<Q, TPL>(sm.cs2, asc, lane, c2v);
+            store_run<Q, TPL>(sm.rl2, asc, lane, rlv);
+            store_run<Q, TPL>(sm.dt, asc, lane, dtf);
+            store_run<Q, TPL>(sm.sq, asc, lane, ld.sqv);
+            store_run<Q, TPL>(sm.v16, asc, lane, v16v);
+            store_run<Q, TPL>(sm.v64, asc, lane, v64v);
             // block table: the last token of walking block K is lane
             // 64/TPL*(K+1) - 1; bt2[I][J] = cs(end of I-1) - cs(end of J)
             {
@@ -499,22 +538,24 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, 
             if (lane == 63) {
                 bool carry = true;
                 if (a.seq) carry = has_nb && sq_nb == sq_edge;
-                sm.gamma = carry ? (float)exp(last) : 0.f;
+                sm.gamma = carry ? expf((float)last) : 0.f;
                 sm.sq_nb = a.seq ? sq_nb : 0;
             }
         } else {
             // exclusive sums toward the outgoing edge -> weight of each token
             // in the state leaving the chunk
             bool nz = false;
+            float wv_[TPL];
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
                 const int pos = ChunkLoads<Q>::pos_of(d, 1, lane, i);
                 float wt = 0.f;
                 if (pos < len && (!a.seq || ld.sqv[i] == sq_edge))
                     wt = expf((float)(cs[i] - (double)at[i])) * dtf[i];
-                sm.w[pos] = wt;
+                wv_[i] = wt;
                 nz |= wt != 0.f;
             }
+            store_run<Q, TPL>(sm.w, d != 0, lane, wv_);   // wave 1 walks from the edge
             const unsigned long long m = __ballot(nz);
             if (lane < Q / 64) {
                 constexpr int LPS = 64 / TPL;   // lanes per 64-token sub-block
