@@ -887,18 +887,22 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[4], int l
         // pipeline works beside the matrix cores
         nxt.part(sb, Q / kSub);
         if (!math || kSub * sb >= len || !sm.wsub[sb]) continue;   // every weight is exactly 0
+        // both 32-token halves' operands first, then their products
+        u32x4 aop[kSub / 32][4], bhi[kSub / 32], blo[kSub / 32];
+#pragma unroll
+        for (int ks = 0; ks < kSub / 32; ++ks)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                aop[ks][q] = tr_operand(sm.bn, kNRS, kSub * sb + 32 * ks, 16 * (4 * nh + q));
+#pragma unroll
+        for (int ks = 0; ks < kSub / 32; ++ks)
+            wx_operand(sm.xs, kSub * sb + 32 * ks, 16 * pq, sm.w, bhi[ks], blo[ks]);
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks) {
-            const int t32 = kSub * sb + 32 * ks;
-            u32x4 aop[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) aop[q] = tr_operand(sm.bn, kNRS, t32, 16 * (4 * nh + q));
-            u32x4 bhi, blo;
-            wx_operand(sm.xs, t32, 16 * pq, sm.w, bhi, blo);
+            for (int q = 0; q < 4; ++q) Hacc[q] = mfma16x16x32(aop[ks][q], bhi[ks], Hacc[q]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) Hacc[q] = mfma16x16x32(aop[q], bhi, Hacc[q]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) Hacc[q] = mfma16x16x32(aop[q], blo, Hacc[q]);
+            for (int q = 0; q < 4; ++q) Hacc[q] = mfma16x16x32(aop[ks][q], blo[ks], Hacc[q]);
         }
     }
 }
