@@ -79,8 +79,10 @@ def measured_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU takes some tens of milliseconds of work to reach its steady
+    # clock; the default warm-up covers that
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--prefix", type=int, default=262144,
@@ -90,11 +92,14 @@ def parse():
     return ap.parse_args()
 
 
-def time_steps(bm, fn, steps, warmup, torch):
-    """Times `steps` calls after `warmup`; the library's per-launch HIP events
-    (recorded on the stream each kernel is launched on) run over the same
-    timed steps. Returns ms per step, wall seconds, per-kernel (launches,
-    total ms) and the dominant kernel."""
+def time_steps(bm, fn, steps, warmup, torch, live=True):
+    """Times `steps` calls after `warmup`. With `live`, the library's
+    per-launch HIP events (recorded on the stream each kernel is launched on)
+    run over the same timed steps; otherwise (workloads of a few
+    microseconds, where recording events per launch would add host time to
+    the step) the steps are timed bare and the per-launch events are taken
+    over a second, identical set of steps. Returns ms per step, wall seconds,
+    per-kernel (launches, total ms) and the dominant kernel."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -102,13 +107,25 @@ def time_steps(bm, fn, steps, warmup, torch):
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    with bm.profile() as prof:
+    if live:
+        with bm.profile() as prof:
+            e0.record(s)
+            for _ in range(steps):
+                fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
         e0.record(s)
         for _ in range(steps):
             fn()
         e1.record(s)
         torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+        wall = time.perf_counter() - t0
+        with bm.profile() as prof:
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
     ker = {k: (c, t) for k, (c, t) in prof.kernels.items()}
     dom = max(ker, key=lambda k: ker[k][1])
     return e0.elapsed_time(e1) / steps, wall, ker, dom
@@ -214,7 +231,7 @@ def extras(args, bm, synth, torch, dev):
         shape = bm.make_shape(f["x"], f["B"], w.chunk)
         ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=dev)
         fn = lambda: bm.ssd_fwd(f, b, chunk=w.chunk, y=y, workspace=ws)  # noqa: E731
-        ms, _, ker, dom = time_steps(bm, fn, steps, 2, torch)
+        ms, _, ker, dom = time_steps(bm, fn, steps, max(2, args.warmup // 10), torch)
         tok = w.batch * w.seqlen
         bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
         fpt = flops_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, w.chunk)
@@ -235,7 +252,7 @@ def extras(args, bm, synth, torch, dev):
     shape = bm.make_shape(f["x"], f["B"], w.chunk)
     ws = torch.empty(max(bm.workspace_size(shape, len(cu) - 1), 256), dtype=torch.uint8, device=dev)
     fn = lambda: bm.ssd_fwd(f, b, chunk=w.chunk, cu_seqlens=cu, y=y, workspace=ws)  # noqa: E731
-    ms, _, ker, dom = time_steps(bm, fn, steps, 2, torch)
+    ms, _, ker, dom = time_steps(bm, fn, steps, max(2, args.warmup // 10), torch)
     bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
     res["packed_varlen"] = {"tokens_per_s": round(w.seqlen / (ms / 1e3), 1),
                             "ms_per_step": round(ms, 4), "tokens": w.seqlen, "nseq": len(cu) - 1,
@@ -269,14 +286,15 @@ def block_step_bench(args, bm, synth, torch, dev, steps):
         f, b = synth.make_inputs(nseq, Lb, H, P, N, G, "bf16", c["seed"], device=dev)
         y = torch.empty(nseq, Lb, H, P, dtype=torch.float32, device=dev)
         fn = lambda: bm.block_step(st, f, b, commit=False, chunk=64, y=y)  # noqa: E731
-        ms, _, ker, dom = time_steps(bm, fn, max(steps, 10), 3, torch)
+        ms, _, ker, dom = time_steps(bm, fn, max(steps, 10), max(3, args.warmup), torch,
+                                     live=False)
         per_seq = H * P * N * 4 + bytes_per_token(H, P, N, G, 2) * Lb
         key = f"b{nseq}_prefix{prefix}"
         out[key] = {"ms_per_step": round(ms, 5), "bytes_per_step": per_seq * nseq,
                     "hbm_roofline_frac_step": round(per_seq * nseq / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "roofline": roofline_for(ker, dom, per_seq * nseq)}
         fc = lambda: bm.block_step(st, f, b, commit=True, chunk=64, y=y)  # noqa: E731
-        msc, _, _, _ = time_steps(bm, fc, 5, 1, torch)
+        msc, _, _, _ = time_steps(bm, fc, 20, 5, torch, live=False)
         out[key]["ms_per_commit_step"] = round(msc, 5)
         st.free()
         del f, b, y
