@@ -347,10 +347,16 @@ __global__ void __launch_bounds__(256) k_seg_scan(const SegArgs a) {
 }
 
 // ------------------------------------------------------------- k_seg_out
-// 8 waves: two per SIMD, so one wave's VALU and LDS work overlaps another's
-// matrix-core work and waits.
-constexpr int kOutWaves = 8;
-constexpr int kOutThreads = 64 * kOutWaves;
+// Waves per workgroup: 8 (two per SIMD, so one wave's VALU and LDS work
+// overlaps another's matrix-core work and waits); with 64-token chunks, which
+// have only 4 row tiles and need 64 KB of LDS, 4 waves and two workgroups per
+// CU. Wave w owns state block (p-tile w%4, n-tiles NQ*(w/4) .. +NQ-1).
+template <int Q>
+struct Cfg {
+    static constexpr int NW = Q == 64 ? 4 : 8;
+    static constexpr int NT = 64 * NW;
+    static constexpr int NQ = 32 / NW;   // 16x16 state tiles per wave
+};
 
 template <int Q>
 struct OutSmem {
@@ -361,7 +367,6 @@ struct OutSmem {
     float v64[Q];          // e^{cs(edge of the token's 64-block) - cs} dt
     float dt[Q];
     int sq[Q];             // sequence index (packed) of each token
-    float tmp[kOutWaves];
     int utile[Q / 16];     // the carried state reaches some row of the 16-row tile
     int wsub[Q / kSub];    // some weight of the 64-token sub-block is nonzero
     float gamma;           // decay of the whole chunk (0: the state does not pass)
@@ -380,8 +385,8 @@ struct OutSmem {
 template <int Q>
 struct ChunkLoads {
     static constexpr int TPL = Q / 64;   // tokens per lane of the scanning waves
-    RowStage<Q, kP, kXS, kOutThreads> sx;
-    RowStage<Q, kN, kNRS, kOutThreads> sb;
+    RowStage<Q, kP, kXS, Cfg<Q>::NT> sx;
+    RowStage<Q, kN, kNRS, Cfg<Q>::NT> sb;
     uint16_t dtv[TPL];   // raw bf16 bits: no use (and no wait) until the scan
     int sqv[TPL];
 
@@ -570,17 +575,18 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, 
 // The wave's state block (p-tile w%4, n-half w/4; fp32 accumulators) into
 // H^T hi / lo.
 template <int Q>
-__device__ void publish_state(OutSmem<Q> &sm, const f32x4 (&Hacc)[4]) {
+__device__ void publish_state(OutSmem<Q> &sm, const f32x4 (&Hacc)[Cfg<Q>::NQ]) {
+    constexpr int NQ = Cfg<Q>::NQ;
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
-    const int pq = w & 3, nh = w >> 2;
+    const int pq = w & 3, nbase = NQ * (w >> 2);
     uint16_t *hh = sm.hs;
     uint16_t *hl = hh + kP * kNRS;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
         uint32_t a0, a1, b0, b1;
         split2(Hacc[q][0], Hacc[q][1], a0, b0);
         split2(Hacc[q][2], Hacc[q][3], a1, b1);
-        const int o = (16 * pq + l16) * kNRS + 64 * nh + 16 * q + 4 * g4;
+        const int o = (16 * pq + l16) * kNRS + 16 * (nbase + q) + 4 * g4;
         *(u32x2 *)(hh + o) = u32x2{a0, a1};
         *(u32x2 *)(hl + o) = u32x2{b0, b1};
     }
@@ -872,14 +878,15 @@ __device__ __forceinline__ int tile_of(int w, int k) {
 // block of the state). B^T and x come straight from the staged natural tiles
 // through transposing reads: no barrier.
 template <int Q>
-__device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[4], int len, bool math,
-                                   ChunkLoads<Q> &nxt) {
+__device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[Cfg<Q>::NQ], int len,
+                                   bool math, ChunkLoads<Q> &nxt) {
+    constexpr int NQ = Cfg<Q>::NQ;
     const int w = wave_id();
-    const int pq = w & 3, nh = w >> 2;
+    const int pq = w & 3, nbase = NQ * (w >> 2);
     if (math) {
         const float gmm = sm.gamma;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) Hacc[q] *= gmm;
+        for (int q = 0; q < NQ; ++q) Hacc[q] *= gmm;
     }
 #pragma unroll
     for (int sb = 0; sb < Q / kSub; ++sb) {
@@ -888,21 +895,21 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[4], int l
         nxt.part(sb, Q / kSub);
         if (!math || kSub * sb >= len || !sm.wsub[sb]) continue;   // every weight is exactly 0
         // both 32-token halves' operands first, then their products
-        u32x4 aop[kSub / 32][4], bhi[kSub / 32], blo[kSub / 32];
+        u32x4 aop[kSub / 32][NQ], bhi[kSub / 32], blo[kSub / 32];
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                aop[ks][q] = tr_operand(sm.bn, kNRS, kSub * sb + 32 * ks, 16 * (4 * nh + q));
+            for (int q = 0; q < NQ; ++q)
+                aop[ks][q] = tr_operand(sm.bn, kNRS, kSub * sb + 32 * ks, 16 * (nbase + q));
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks)
             wx_operand(sm.xs, kSub * sb + 32 * ks, 16 * pq, sm.w, bhi[ks], blo[ks]);
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) Hacc[q] = mfma16x16x32(aop[ks][q], bhi[ks], Hacc[q]);
+            for (int q = 0; q < NQ; ++q) Hacc[q] = mfma16x16x32(aop[ks][q], bhi[ks], Hacc[q]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) Hacc[q] = mfma16x16x32(aop[ks][q], blo[ks], Hacc[q]);
+            for (int q = 0; q < NQ; ++q) Hacc[q] = mfma16x16x32(aop[ks][q], blo[ks], Hacc[q]);
         }
     }
 }
@@ -910,13 +917,14 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[4], int l
 // One direction's walk over the segment's chunks.
 template <int Q, bool PACKED, int D>
 __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h, int grp, bool add) {
+    constexpr int NQ = Cfg<Q>::NQ;
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
-    const int pq = w & 3, nh = w >> 2;
+    const int pq = w & 3, nbase = NQ * (w >> 2);
     const int t0 = seg * a.Ts, t1 = min(t0 + a.Ts, a.L);
     const int cfirst = t0 / Q, clast = (t1 - 1) / Q;
     const size_t PN = (size_t)kP * kN;
     auto slot = [&](int d, int k) { return (((size_t)b * 2 + d) * a.nseg + k) * a.H + h; };
-    const int hoff = (16 * pq + l16) * kN + 64 * nh + 4 * g4;   // + 16 q: this lane's state entries
+    const int hoff = (16 * pq + l16) * kN + 16 * nbase + 4 * g4;   // + 16 q: this lane's state entries
     const DirPtrs &dp = a.dir[D];
     const float Dh = dp.D ? dp.D[h] : 0.f;
     // incoming state of this segment in the walking direction
@@ -943,9 +951,9 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
         chunk_at(0, c0, len);
         ld.issue(a, D, b, h, grp, c0, len);
     }
-    f32x4 Hacc[4];
+    f32x4 Hacc[NQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
+    for (int q = 0; q < NQ; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
     bool has_state = src != nullptr;
     if (has_state) publish_state<Q>(sm, Hacc);
     for (int s = 0; s < nch; ++s) {
@@ -978,12 +986,13 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
     if (want_final) {
         float *fs = a.final_state + ((size_t)b * a.H + h) * PN;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *(f32x4 *)(fs + hoff + 16 * q) = Hacc[q];
+        for (int q = 0; q < NQ; ++q) *(f32x4 *)(fs + hoff + 16 * q) = Hacc[q];
     }
 }
 
 template <int Q, bool PACKED>
-__global__ void __launch_bounds__(kOutThreads) k_seg_out(const SegArgs a) {
+__global__ void __launch_bounds__(Cfg<Q>::NT) __attribute__((amdgpu_waves_per_eu(2)))
+k_seg_out(const SegArgs a) {
     // XCD-aware order: consecutive workgroup ids go round-robin over the 8
     // XCDs, so XCD x runs ids x, x+8, x+16, ... It is given the contiguous
     // range [x*per, (x+1)*per) of the (row-segment, head) pairs in
@@ -1025,9 +1034,9 @@ hipError_t launch_q(const SegArgs &a, hipStream_t s) {
     }
     const int per_xcd = (a.batch * a.nseg * a.H + 7) / 8;
     if (a.seq)
-        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true>), dim3(per_xcd * 8), dim3(kOutThreads), 0, s, a);
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
     else
-        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, false>), dim3(per_xcd * 8), dim3(kOutThreads), 0, s, a);
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, false>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
     return hipGetLastError();
 }
 
