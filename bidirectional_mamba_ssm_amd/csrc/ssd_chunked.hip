@@ -737,6 +737,14 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
     uint32_t yoff[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) yoff[r] = (uint32_t)min(i0 + r, len - 1) * ystride;
+    float prev[4][4];
+    if (add) {
+        // the reverse pass wrote these rows; fetched now, used at the end
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) prev[pt][r] = ybase[yoff[r] + 16 * pt];
+    }
     const float rli = sm.rl2[i];
     const int sqi = PACKED ? sm.sq[i] : 0;
     f32x4 acc[4];
@@ -785,15 +793,6 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
         default: diag_block<Q, PACKED, D, 3>(acc, sm, cr, I, i, rli, sqi); break;
     }
 
-    float prev[4][4];
-    if (add) {
-        // the reverse pass wrote these rows; fetched here so that the loads
-        // overlap the carried-state products
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) prev[pt][r] = ybase[yoff[r] + 16 * pt];
-    }
 
     // ---- carried state: e^{cs_i} C_i . H (tiles it does not reach: skipped, exact)
     if (has_state && sm.utile[it]) {
