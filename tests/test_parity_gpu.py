@@ -270,3 +270,57 @@ def test_slow_decay_chains(scale):
         err, ok = within(got, ref, "bf16")
         print(f"scale={scale} chunk={chunk}: {err:.3e}", flush=True)
         assert ok, f"error {err:.3e}"
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_odd_grid_shapes(chunk):
+    """Workgroup counts that are not multiples of the XCD count, several
+    heads per group, partial last chunk: every (row, head) is produced once."""
+    f, b = synth.make_inputs(3, 2 * chunk + 37, 6, 64, 128, 3, "bf16", 101 + chunk, device=DEV)
+    got, _ = _run(f, b, chunk)
+    ref = oracle.bissd(f, b)
+    err, ok = within(got, ref, "bf16")
+    print(f"odd grid chunk={chunk}: {err:.3e}", flush=True)
+    assert ok, f"error {err:.3e}"
+
+
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_steep_decay(chunk):
+    """Large dt and |A| = 16 make the in-chunk decay sums reach thousands: the
+    decay exponents must not lose accuracy to cancellation."""
+    f, b = synth.make_inputs(1, 700, 4, 64, 128, 1, "bf16", 111, device=DEV)
+    big = lambda d: dict(d, dt=(d["dt"].float() * 6.0 + 0.5).to(d["dt"].dtype).contiguous(),
+                         A=torch.full_like(d["A"], -16.0))
+    f, b = big(f), big(b)
+    for zero_D in (False, True):
+        ff, bb = (_zero_D(f), _zero_D(b)) if zero_D else (f, b)
+        got, _ = _run(ff, bb, chunk)
+        ref = oracle.bissd(ff, bb)
+        err, ok = within(got, ref, "bf16")
+        print(f"steep chunk={chunk} zero_D={zero_D}: {err:.3e}", flush=True)
+        assert ok, f"error {err:.3e}"
+
+
+@pytest.mark.parametrize("nseq", [1, 16])
+def test_block_step_real_shape(nseq):
+    """The decode step at the cached-decode shape (80 heads x 64, d_state 128,
+    block 64) against the oracle on a sample of heads."""
+    c = synth.BLOCK_STEP
+    H, P, N, G, Lb = c["nheads"], c["headdim"], c["d_state"], c["ngroups"], c["block"]
+    st = bm.State(nseq, H, P, N)
+    pf, _ = synth.make_inputs(nseq, 300, H, P, N, G, "bf16", 121, device=DEV, bidirectional=False)
+    bm.ssd_fwd(pf, None, chunk=64, final_state=st.tensor())
+    f, b = synth.make_inputs(nseq, Lb, H, P, N, G, "bf16", 122, device=DEV)
+    state0 = st.tensor().clone()
+    y = bm.block_step(st, f, b, commit=True, chunk=64)
+    torch.cuda.synchronize()
+    heads = [0, 41, 79]
+    fr, br = _heads(f, heads), _heads(b, heads)
+    ref, new_state = oracle.block_step(state0[:, heads].contiguous(), fr, br, commit=True)
+    got = y[:, :, heads].double().cpu().numpy()
+    err, ok = within(got, ref, "bf16")
+    print(f"block step b{nseq}: {err:.3e}", flush=True)
+    assert ok, f"y error {err:.3e}"
+    err, ok = within(st.tensor()[:, heads].double().cpu().numpy(), new_state, "bf16")
+    assert ok, f"committed state error {err:.3e}"
+    st.free()
