@@ -81,8 +81,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     # the GPU takes some tens of milliseconds of work to reach its steady
     # clock; the default warm-up covers that
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--prefix", type=int, default=262144,
@@ -240,6 +240,24 @@ def extras(args, bm, synth, torch, dev):
                      "kernels_ms_per_step": {k: round(t / steps, 4) for k, (c, t) in ker.items()},
                      "roofline": roofline_for(ker, dom, bpt * tok),
                      "mfma": mfma_for(ker, dom, fpt * tok)}
+        del f, b, y, ws
+        torch.cuda.empty_cache()
+
+    # the headline layer and the 32k prefill with 64-token chunks: the same
+    # operator through a smaller block decomposition (4-wave workgroups, two
+    # per CU), for comparison with the configured chunk of 256
+    for name in ("layer_1p3b_train", "long_32k"):
+        w = synth.WORKLOADS[name]
+        f, b = synth.make_workload(w, device=dev)
+        y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+        shape = bm.make_shape(f["x"], f["B"], 64)
+        ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=dev)
+        fn = lambda: bm.ssd_fwd(f, b, chunk=64, y=y, workspace=ws)  # noqa: E731
+        ms, _, ker, dom = time_steps(bm, fn, steps, max(2, args.warmup // 10), torch)
+        tok = w.batch * w.seqlen
+        bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
+        res[name + "_chunk64"] = {"tokens_per_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+                                  "hbm_roofline_frac_step": round(bpt * tok / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
         del f, b, y, ws
         torch.cuda.empty_cache()
 
