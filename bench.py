@@ -131,6 +131,27 @@ def time_steps(bm, fn, steps, warmup, torch, live=True):
     return e0.elapsed_time(e1) / steps, wall, ker, dom
 
 
+def step_stats(fn, steps, torch, flush=None):
+    """Per-step times (ms) from a pair of events around each step: median,
+    p10, p90. With `flush`, a 512 MiB write evicts the L2s and the 256 MB
+    MALL before each step (outside the events): the cold-cache time."""
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(steps):
+        if flush is not None:
+            flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    q = lambda f: times[min(len(times) - 1, int(f * len(times)))]  # noqa: E731
+    return {"median_ms": round(q(0.5), 4), "p10_ms": round(q(0.1), 4), "p90_ms": round(q(0.9), 4)}
+
+
 def roofline_for(ker, dom, bytes_per_launch, traffic=None):
     launches, total_ms = ker[dom]
     avg_s = total_ms / launches / 1e3
@@ -214,6 +235,13 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
 
+    # per-step distribution, warm and with the caches flushed before each step
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    out["step_ms_warm"] = step_stats(step, 50, torch)
+    out["step_ms_cold_cache"] = step_stats(step, 50, torch, flush=flush)
+    del flush
+    torch.cuda.empty_cache()
+
     if not args.no_extra:
         out["extra"] = extras(args, bm, synth, torch, dev)
     if not args.no_cpu_baseline:
@@ -260,6 +288,24 @@ def extras(args, bm, synth, torch, dev):
                                   "hbm_roofline_frac_step": round(bpt * tok / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
         del f, b, y, ws
         torch.cuda.empty_cache()
+
+    # the secondary reading of the long-prefill shape: the tiny head shape
+    # (4 heads x headdim 16, d_state 16) at 131 072 tokens, chunk 256, bf16
+    # (served by the token-sequential kernel in segments: the matrix-core
+    # path is built for headdim 64 / d_state 128)
+    f, b = synth.make_inputs(1, 131072, 4, 16, 16, 1, "bf16", 3, device=dev)
+    y = torch.empty(1, 131072, 4, 16, dtype=torch.float32, device=dev)
+    shape = bm.make_shape(f["x"], f["B"], 256)
+    ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=dev)
+    fn = lambda: bm.ssd_fwd(f, b, chunk=256, y=y, workspace=ws)  # noqa: E731
+    ms, _, ker, dom = time_steps(bm, fn, 20, 5, torch)
+    bpt = bytes_per_token(4, 16, 16, 1, 2)
+    res["long_128k_small_heads"] = {"tokens_per_s": round(131072 / (ms / 1e3), 1),
+                                    "ms_per_step": round(ms, 4), "bytes_per_token": bpt,
+                                    "hbm_roofline_frac_step": round(bpt * 131072 / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    "kernels_ms_per_step": {k: round(t / 20, 4) for k, (c, t) in ker.items()}}
+    del f, b, y, ws
+    torch.cuda.empty_cache()
 
     # packed variable-length batch with per-sequence resets
     w = synth.packed_workload()

@@ -109,6 +109,8 @@ Layout workspace_layout(const bimamba_shape *s, int nseq) {
     w.scan_off = off;
     if (use_chunked(s))
         off += chunked_workspace(s->batch, s->seqlen, s->nheads, s->ngroups, s->chunk);
+    else
+        off += seq_workspace(s->batch, s->seqlen, s->nheads, s->headdim, s->d_state, nseq > 0);
     w.total = off;
     return w;
 }
@@ -295,7 +297,7 @@ int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
     if (use_chunked(s)) {
         if ((e = launch_chunked(p, (char *)workspace + w.scan_off, st)) != hipSuccess)
             return hip_fail(e, "chunked scan launch");
-    } else if ((e = launch_scan_seq(p, st)) != hipSuccess) {
+    } else if ((e = launch_scan_seq(p, (char *)workspace + w.scan_off, st)) != hipSuccess) {
         return hip_fail(e, "scan launch");
     }
     return BIMAMBA_OK;
@@ -383,7 +385,7 @@ int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
     // writes it back, so the in-place update is safe)
     hipError_t e = chunked_supported(p) && chunked_workspace(p.batch, p.L, p.H, p.G, p.Q) == 0
                        ? launch_chunked(p, nullptr, (hipStream_t)stream)
-                       : launch_scan_seq(p, (hipStream_t)stream);
+                       : launch_scan_seq(p, nullptr, (hipStream_t)stream);
     return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "block step launch");
 }
 

@@ -50,8 +50,11 @@ bool chunked_supported(const Problem &p);
 size_t chunked_workspace(int batch, int L, int H, int G, int Q);
 hipError_t launch_chunked(const Problem &p, void *ws, hipStream_t s);
 
-// ssd_seq.hip: token-sequential scan, any (P <= 128, N in {16,32,64,128})
+// ssd_seq.hip: token-sequential scan, any (P <= 128, N in {16,32,64,128}).
+// Long unpacked rows with few (row, head) pairs run in segments when the
+// workspace holds seq_workspace() bytes; ws may be nullptr (whole rows).
 bool seq_supported(int P, int N);
-hipError_t launch_scan_seq(const Problem &p, hipStream_t s);
+size_t seq_workspace(int batch, int L, int H, int P, int N, bool packed);
+hipError_t launch_scan_seq(const Problem &p, void *ws, hipStream_t s);
 
 }  // namespace bm

@@ -324,3 +324,35 @@ def test_block_step_real_shape(nseq):
     err, ok = within(st.tensor()[:, heads].double().cpu().numpy(), new_state, "bf16")
     assert ok, f"committed state error {err:.3e}"
     st.free()
+
+
+SEGMENTED = [
+    # name, batch, L, H, P, N, G, dtype, chunk, seed
+    ("f32_one_pair_ragged", 1, 4001, 1, 16, 16, 1, "f32", 64, 131),
+    ("f32_two_rows_p64", 2, 1800, 1, 64, 64, 1, "f32", 128, 132),
+    ("bf16_small_heads", 1, 3000, 2, 16, 16, 1, "bf16", 256, 133),
+]
+
+
+@pytest.mark.parametrize("case", SEGMENTED, ids=[c[0] for c in SEGMENTED])
+@pytest.mark.parametrize("zero_D", [False, True], ids=["D", "D0"])
+def test_segmented_sequential(case, zero_D):
+    """Long rows with few (row, head) pairs on the token-sequential path run
+    in segments chained through their states; incoming and outgoing states
+    included."""
+    name, batch, L, H, P, N, G, dtype, chunk, seed = case
+    print(f"segmented {name} zero_D={zero_D}", flush=True)
+    f, b = synth.make_inputs(batch, L, H, P, N, G, dtype, seed, device=DEV)
+    assert bm.workspace_size(bm.make_shape(f["x"], f["B"], chunk), 0) > 0
+    if zero_D:
+        f, b = _zero_D(f), _zero_D(b)
+    g = torch.Generator(device=DEV).manual_seed(seed + 1000)
+    init = torch.randn(batch, H, P, N, generator=g, device=DEV) * 0.5
+    got, fs = _run(f, b, chunk, init=init, want_final=True)
+    ref, fs_ref = oracle.bissd(f, b, init_state=init, want_final_state=True)
+    err, ok = within(got, ref, dtype)
+    print(f"  y error {err:.3e}", flush=True)
+    assert ok, f"{name}: y error {err:.3e}"
+    err, ok = within(fs, fs_ref, dtype)
+    print(f"  final state error {err:.3e}", flush=True)
+    assert ok, f"{name}: final state error {err:.3e}"
