@@ -56,7 +56,16 @@ constexpr int kP = 64;         // headdim handled here
 constexpr int kN = 128;        // d_state handled here
 constexpr int kThreads = 256;  // k_seg_state: 4 waves
 constexpr int kSub = 64;       // tokens per state-update sub-block
-constexpr int kNRS = kN + 8;   // LDS row stride (16-bit elements) of [t][n] tiles
+constexpr int kNRS = kN + 8;   // LDS row stride (16-bit elements) of H^T [p][n]
+// Staged B [t][n] tiles: row stride kBS, rows in odd groups of 8 shifted by 8
+// elements. A 16-byte row read by 16 lanes (the Gram operand, rows r..r+15)
+// and a transposing read by 32 lanes (the state-update operand, rows r..r+7,
+// 32 bytes each) both land on 64 distinct 4-byte banks.
+constexpr int kBS = kN + 16;
+__device__ __forceinline__ int bn_row(int t) { return t * kBS + ((t >> 3) & 1) * 8; }
+// bn_row(r + l) - r * kBS for a multiple r of 16 and l < 16
+__device__ __forceinline__ int bn_lane(int l) { return l * kBS + (l >> 3) * 8; }
+constexpr int bn_elems(int rows) { return rows * kBS; }
 constexpr int kXS = kP + 16;   // LDS row stride (16-bit elements) of x [t][p] tiles
 constexpr float kDead = -110.f;  // expf(x) is exactly 0.0f for every x < kDead
 constexpr float kLog2e = 1.4426950408889634f;
@@ -96,6 +105,15 @@ __device__ __forceinline__ u32x4 tr_operand(const uint16_t *base, int rs, int t3
     const int lane = threadIdx.x & 63, g4 = lane >> 4, s = lane & 15;
     const uint16_t *p = base + (t32 + 4 * g4 + (s >> 2)) * rs + c0 + 4 * (s & 3);
     const u32x2 a = ld_tr(p), b = ld_tr(p + 16 * rs);
+    return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// tr_operand for a staged B tile (bn_row layout); t32 is a multiple of 8, so
+// rows t and t + 16 share their shift.
+__device__ __forceinline__ u32x4 tr_operand_bn(const uint16_t *bn, int t32, int c0) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, s = lane & 15;
+    const uint16_t *p = bn + t32 * kBS + bn_lane(4 * g4 + (s >> 2)) + c0 + 4 * (s & 3);
+    const u32x2 a = ld_tr(p), b = ld_tr(p + 16 * kBS);
     return u32x4{a[0], a[1], b[0], b[1]};
 }
 
@@ -165,7 +183,7 @@ __device__ __forceinline__ float wave_scan(float v) {
 // rows in memory), raw, into dst (row stride RS). All global loads are issued
 // before the first LDS write so that they overlap; rows at or past `tlimit`
 // are loaded clamped and stored as zeros.
-template <int ROWS, int COLS, int RS, int NT>
+template <int ROWS, int COLS, int RS, int NT, bool BROWS = false>
 struct RowStage {
     static constexpr int CG = COLS / 8;
     static constexpr int ITEMS = ROWS * CG;
@@ -194,7 +212,8 @@ struct RowStage {
             if (ITEMS % NT == 0 || item < ITEMS) {
                 const int row = item / CG, cg = item % CG;
                 const u32x4 z = {0u, 0u, 0u, 0u};
-                *(u32x4 *)(dst + row * RS + 8 * cg) = row < tlimit ? v[k] : z;
+                const int ro = BROWS ? bn_row(row) : row * RS;
+                *(u32x4 *)(dst + ro + 8 * cg) = row < tlimit ? v[k] : z;
             }
         }
     }
@@ -221,7 +240,7 @@ __device__ __forceinline__ void wx_operand(const uint16_t *xs, int t32, int p0, 
 // ----------------------------------------------------------- k_seg_state
 struct StateSmem {
     float w[kSub];
-    alignas(16) uint16_t bn[kSub * kNRS];   // B [t][n]
+    alignas(16) uint16_t bn[bn_elems(kSub)];   // B [t][n], bn_row layout
     alignas(16) uint16_t xs[kSub * kXS];    // x [t][p]
     float run[2];   // running sum of a from the outgoing edge, by step parity
 };
@@ -260,7 +279,7 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
         const float run = sm.run[step & 1];
         if (run < kDead) break;
         if (a.seq && a.seq[tok(a, b, d == 0 ? s1 - 1 : s0)] != edge_seq) break;
-        RowStage<kSub, kN, kNRS, kThreads> sb;
+        RowStage<kSub, kN, kBS, kThreads, true> sb;
         RowStage<kSub, kP, kXS, kThreads> sx;
         sb.load(Bm + (tok(a, b, s0) * a.G + grp) * kN, (uint32_t)(a.G * kN), n);
         sx.load(X + (tok(a, b, s0) * a.H + h) * kP, (uint32_t)(a.H * kP), n);
@@ -292,7 +311,7 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
             wx_operand(sm.xs, 32 * ks, 16 * w, sm.w, bhi, blo);
 #pragma unroll
             for (int nt = 0; nt < kN / 16; ++nt) {
-                const u32x4 aop = tr_operand(sm.bn, kNRS, 32 * ks, 16 * nt);
+                const u32x4 aop = tr_operand_bn(sm.bn, 32 * ks, 16 * nt);
                 Hacc[nt] = mfma16x16x32(aop, bhi, Hacc[nt]);
                 Hacc[nt] = mfma16x16x32(aop, blo, Hacc[nt]);
             }
@@ -373,9 +392,41 @@ struct OutSmem {
     float bt2[Q / 64][Q / 64];  // [I][J] (walking order, J < I): sum of a over the blocks strictly between, times log2(e)
     int sq_nb;             // sequence index of the token the carried state comes from
     alignas(16) uint16_t xs[Q * kXS];       // x [t][p], raw bf16
-    alignas(16) uint16_t bn[Q * kNRS];      // B [t][n], raw bf16
+    alignas(16) uint16_t bn[bn_elems(Q)];   // B [t][n], raw bf16, bn_row layout
     alignas(16) uint16_t hs[2 * kP * kNRS]; // H^T [p][n]: bf16 high part, then bf16 residual
 };
+
+// A row tile's inputs from global memory, fetched one phase ahead of the
+// tile so that their latency is hidden: C of its 16 rows in the layout that
+// is both the B operand of the Gram tiles and the A operand of the
+// carried-state product, and, for the forward pass, the tile's rows of y as
+// the reverse pass left them (read by the same lane that wrote them).
+struct TileIn {
+    u32x4 cr[kN / 32];
+    float prev[4][4];
+};
+
+template <int D>
+__device__ __forceinline__ void tile_fetch(TileIn &t, const SegArgs &a, int b, int h, int grp,
+                                           int c0, int len, int it, bool add) {
+    if (it < 0) return;   // the wave has no such tile
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+    const int i = 16 * it + l16, i0 = 16 * it + 4 * g4;
+    const uint16_t *cp = (const uint16_t *)a.dir[D].C + (tok(a, b, c0) * a.G + grp) * kN +
+                         (uint32_t)(min(i, len - 1) * a.G * kN) + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < kN / 32; ++ks) t.cr[ks] = ld8(cp + 32 * ks);
+    if (add) {
+        const float *ybase = a.y + (tok(a, b, c0) * a.H + h) * kP + l16;
+        const uint32_t ystride = (uint32_t)(a.H * kP);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t yo = (uint32_t)min(i0 + r, len - 1) * ystride;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) t.prev[pt][r] = ybase[yo + 16 * pt];
+        }
+    }
+}
 
 // Loads of one chunk [c0, c0+len) of direction D, issued ahead of use (the
 // next chunk's are issued before the current chunk's state update, so their
@@ -386,9 +437,10 @@ template <int Q>
 struct ChunkLoads {
     static constexpr int TPL = Q / 64;   // tokens per lane of the scanning waves
     RowStage<Q, kP, kXS, Cfg<Q>::NT> sx;
-    RowStage<Q, kN, kNRS, Cfg<Q>::NT> sb;
+    RowStage<Q, kN, kBS, Cfg<Q>::NT, true> sb;
     uint16_t dtv[TPL];   // raw bf16 bits: no use (and no wait) until the scan
     int sqv[TPL];
+    TileIn tin;          // the wave's first row tile
 
     // position in the chunk of the lane's i-th token; walking order for wave
     // 0, from the outgoing edge for wave 1
@@ -598,7 +650,7 @@ __device__ __forceinline__ f32x4 gram_tile(const uint16_t *bn, int j0, const u32
     f32x4 g = zero4();
 #pragma unroll
     for (int ks = 0; ks < kN / 32; ++ks)
-        g = mfma16x16x32(*(const u32x4 *)(bn + (j0 + l16) * kNRS + 32 * ks + 8 * g4), cr[ks], g);
+        g = mfma16x16x32(*(const u32x4 *)(bn + j0 * kBS + bn_lane(l16) + 32 * ks + 8 * g4), cr[ks], g);
     return g;
 }
 
@@ -624,8 +676,8 @@ __device__ __forceinline__ void gram_pair(const uint16_t *bn, int j0a, int j0b,
     u32x4 oa[kN / 32], ob[kN / 32];
 #pragma unroll
     for (int ks = 0; ks < kN / 32; ++ks) {
-        oa[ks] = *(const u32x4 *)(bn + (j0a + l16) * kNRS + 32 * ks + 8 * g4);
-        ob[ks] = *(const u32x4 *)(bn + (j0b + l16) * kNRS + 32 * ks + 8 * g4);
+        oa[ks] = *(const u32x4 *)(bn + j0a * kBS + bn_lane(l16) + 32 * ks + 8 * g4);
+        ob[ks] = *(const u32x4 *)(bn + j0b * kBS + bn_lane(l16) + 32 * ks + 8 * g4);
     }
     ga = zero4();
     gb = zero4();
@@ -716,35 +768,15 @@ __device__ __forceinline__ void diag_block(f32x4 (&acc)[4], const OutSmem<Q> &sm
 // staged as zeros and their dt is 0, so every such entry is a finite value
 // times 0, and a row past the end only reaches its own (unstored) output.
 template <int Q, bool PACKED, int D>
-__device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, int grp, int c0,
-                         int len, int it, bool has_state, float Dh, bool add) {
+__device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, int c0, int len,
+                         int it, bool has_state, float Dh, bool add, const TileIn &tin) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
-    const DirPtrs &dp = a.dir[D];
     const uint16_t *bn = sm.bn;
     const int I = it >> 2, wq = it & 3;   // 64-row block, tile inside it
     const int i = 16 * it + l16;          // this lane's row (G^T column)
     const int i0 = 16 * it + 4 * g4;      // first of this lane's output rows
     const bool full = 16 * it + 16 <= len;
-    u32x4 cr[kN / 32];
-    {
-        const uint16_t *cp = (const uint16_t *)dp.C + (tok(a, b, c0) * a.G + grp) * kN +
-                             (uint32_t)(min(i, len - 1) * a.G * kN) + 8 * g4;
-#pragma unroll
-        for (int ks = 0; ks < kN / 32; ++ks) cr[ks] = ld8(cp + 32 * ks);
-    }
-    float *ybase = a.y + (tok(a, b, c0) * a.H + h) * kP + l16;
-    const uint32_t ystride = (uint32_t)(a.H * kP);
-    uint32_t yoff[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) yoff[r] = (uint32_t)min(i0 + r, len - 1) * ystride;
-    float prev[4][4];
-    if (add) {
-        // the reverse pass wrote these rows; fetched now, used at the end
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) prev[pt][r] = ybase[yoff[r] + 16 * pt];
-    }
+    const u32x4 (&cr)[kN / 32] = tin.cr;
     const float rli = sm.rl2[i];
     const int sqi = PACKED ? sm.sq[i] : 0;
     f32x4 acc[4];
@@ -848,8 +880,13 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[pt][r] += prev[pt][r];
+            for (int r = 0; r < 4; ++r) acc[pt][r] += tin.prev[pt][r];
     }
+    float *ybase = a.y + (tok(a, b, c0) * a.H + h) * kP + l16;
+    const uint32_t ystride = (uint32_t)(a.H * kP);
+    uint32_t yoff[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yoff[r] = (uint32_t)min(i0 + r, len - 1) * ystride;
     if (full) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
@@ -868,7 +905,7 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
 // and the two waves of a SIMD (w, w+4) get equal shares.
 template <int Q>
 __device__ __forceinline__ int tile_of(int w, int k) {
-    if (Q == 256) return k == 0 ? w : 15 - w;
+    if (Q == 256) return k == 0 ? 15 - w : w;
     if (Q == 128) return k == 0 ? (w < 4 ? w : 11 - w) : -1;
     return k == 0 && w < 4 ? w : -1;
 }
@@ -899,7 +936,7 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[Cfg<Q>::N
         for (int ks = 0; ks < kSub / 32; ++ks)
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
-                aop[ks][q] = tr_operand(sm.bn, kNRS, kSub * sb + 32 * ks, 16 * (nbase + q));
+                aop[ks][q] = tr_operand_bn(sm.bn, kSub * sb + 32 * ks, 16 * (nbase + q));
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks)
             wx_operand(sm.xs, kSub * sb + 32 * ks, 16 * pq, sm.w, bhi[ks], blo[ks]);
@@ -949,6 +986,7 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
         int c0, len;
         chunk_at(0, c0, len);
         ld.issue(a, D, b, h, grp, c0, len);
+        if (Q != 256) tile_fetch<D>(ld.tin, a, b, h, grp, c0, len, tile_of<Q>(w, 0), add);
     }
     f32x4 Hacc[NQ];
 #pragma unroll
@@ -959,11 +997,20 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
         int c0, len;
         chunk_at(s, c0, len);
         chunk_prep<Q>(a, sm, ld, D, b, h, c0, len);
+        if (Q == 256) {
+            // two tiles per wave: each fetches its own inputs (holding them
+            // through the state update would cost spills)
 #pragma unroll 1
-        for (int k = 0; k < 2; ++k) {
-            const int it = tile_of<Q>(w, k);
+            for (int k = 0; k < 2; ++k) {
+                const int it = tile_of<Q>(w, k);
+                TileIn t;
+                tile_fetch<D>(t, a, b, h, grp, c0, len, it, add);
+                if (16 * it < len) row_tile<Q, PACKED, D>(a, sm, b, h, c0, len, it, has_state, Dh, add, t);
+            }
+        } else {
+            const int it = tile_of<Q>(w, 0);
             if (it >= 0 && 16 * it < len)
-                row_tile<Q, PACKED, D>(a, sm, b, h, grp, c0, len, it, has_state, Dh, add);
+                row_tile<Q, PACKED, D>(a, sm, b, h, c0, len, it, has_state, Dh, add, ld.tin);
         }
         const bool last = s == nch - 1;
         {
@@ -973,6 +1020,7 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
             int c0n, lenn;
             chunk_at(last ? s : s + 1, c0n, lenn);
             ld.begin(a, D, b, h, grp, c0n, lenn);
+            if (Q != 256) tile_fetch<D>(ld.tin, a, b, h, grp, c0n, lenn, tile_of<Q>(w, 0), add);
         }
         chunk_state_update<Q>(sm, Hacc, len, !last || want_final, ld);
         // every wave is done with this chunk's tiles and the published state
