@@ -433,7 +433,7 @@ __device__ __forceinline__ void tile_fetch(TileIn &t, const SegArgs &a, int b, i
 // latency overlaps it): x and B for every thread, and for waves 0 and 1 the
 // dt (and sequence index) of the chunk's tokens, Q/64 per lane, in walking
 // order (wave 0) or from the outgoing edge (wave 1).
-template <int Q>
+template <int Q, bool PACKED>
 struct ChunkLoads {
     static constexpr int TPL = Q / 64;   // tokens per lane of the scanning waves
     RowStage<Q, kP, kXS, Cfg<Q>::NT> sx;
@@ -462,13 +462,11 @@ struct ChunkLoads {
             const uint16_t *DT = (const uint16_t *)dp.dt;
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                const int pos = pos_of(d, wv, lane, i);
-                dtv[i] = 0;
-                sqv[i] = 0;
-                if (pos < len) {
-                    dtv[i] = DT[tok(a, b, c0 + pos) * a.H + h];
-                    if (a.seq) sqv[i] = a.seq[tok(a, b, c0 + pos)];
-                }
+                // clamped, unconditional: positions past the end are masked
+                // where the values are used
+                const int pos = min(pos_of(d, wv, lane, i), len - 1);
+                dtv[i] = DT[tok(a, b, c0 + pos) * a.H + h];
+                sqv[i] = PACKED ? a.seq[tok(a, b, c0 + pos)] : 0;
             }
         }
         x0 = (const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP;
@@ -513,10 +511,11 @@ __device__ __forceinline__ void store_run(V *dst, bool asc, int lane, const V (&
 // masks, staged x and B; one barrier. Wave 0 scans a over the chunk in the
 // walking direction, wave 1 toward the outgoing edge, each with Q/64 tokens
 // per lane; the tile-edge values come from lane shuffles.
-template <int Q>
-__device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, int d, int b,
-                           int h, int c0, int len) {
-    constexpr int TPL = ChunkLoads<Q>::TPL;
+template <int Q, bool PACKED>
+__device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q, PACKED> &ld, int d,
+                           int b, int h, int c0, int len) {
+    using LD = ChunkLoads<Q, PACKED>;
+    constexpr int TPL = LD::TPL;
     const int lane = lane_id(), wv = wave_id();
     const float Ah = a.dir[d].A[h];
     ld.sx.store(len, sm.xs);
@@ -524,7 +523,7 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, 
     if (wv < 2) {
         int sq_nb = 0, sq_edge = 0;
         bool has_nb = true;
-        if (a.seq) {
+        if (PACKED) {
             const int nb = d == 0 ? c0 - 1 : c0 + len;
             has_nb = d == 0 ? c0 > 0 : c0 + len < a.L;
             sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
@@ -538,7 +537,7 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, 
         double run = 0.0;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            dtf[i] = bf2f(ld.dtv[i]);
+            dtf[i] = LD::pos_of(d, wv, lane, i) < len ? bf2f(ld.dtv[i]) : 0.f;
             at[i] = dtf[i] * Ah;
             run += (double)at[i];
             cs[i] = run;
@@ -562,12 +561,12 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, 
             float c2v[TPL], rlv[TPL], v16v[TPL], v64v[TPL];
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                const int pos = ChunkLoads<Q>::pos_of(d, 0, lane, i);
+                const int pos = LD::pos_of(d, 0, lane, i);
                 c2v[i] = (float)(cs[i] * kLog2e);
                 rlv[i] = (float)((cs[i] - start) * kLog2e);
                 v16v[i] = exp2_((float)((e16 - cs[i]) * kLog2e)) * dtf[i];
                 v64v[i] = exp2_((float)((e64 - cs[i]) * kLog2e)) * dtf[i];
-                reach |= pos < len && (!a.seq || ld.sqv[i] == sq_nb) && cs[i] >= kDead;
+                reach |= pos < len && (!PACKED || ld.sqv[i] == sq_nb) && cs[i] >= kDead;
             }
             const bool asc = d == 0;   // wave 0 walks ascending positions forward
             store_run<Q, TPL>(sm.cs2, asc, lane, c2v);
@@ -594,9 +593,9 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, 
             }
             if (lane == 63) {
                 bool carry = true;
-                if (a.seq) carry = has_nb && sq_nb == sq_edge;
+                if (PACKED) carry = has_nb && sq_nb == sq_edge;
                 sm.gamma = carry ? expf((float)last) : 0.f;
-                sm.sq_nb = a.seq ? sq_nb : 0;
+                sm.sq_nb = PACKED ? sq_nb : 0;
             }
         } else {
             // exclusive sums toward the outgoing edge -> weight of each token
@@ -605,9 +604,9 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q> &ld, 
             float wv_[TPL];
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                const int pos = ChunkLoads<Q>::pos_of(d, 1, lane, i);
+                const int pos = LD::pos_of(d, 1, lane, i);
                 float wt = 0.f;
-                if (pos < len && (!a.seq || ld.sqv[i] == sq_edge))
+                if (pos < len && (!PACKED || ld.sqv[i] == sq_edge))
                     wt = expf((float)(cs[i] - (double)at[i])) * dtf[i];
                 wv_[i] = wt;
                 nz |= wt != 0.f;
@@ -913,9 +912,9 @@ __device__ __forceinline__ int tile_of(int w, int k) {
 // H <- gamma H + sum over the chunk's tokens of w_t B_t x_t^T (the wave's
 // block of the state). B^T and x come straight from the staged natural tiles
 // through transposing reads: no barrier.
-template <int Q>
+template <int Q, bool PACKED>
 __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[Cfg<Q>::NQ], int len,
-                                   bool math, ChunkLoads<Q> &nxt) {
+                                   bool math, ChunkLoads<Q, PACKED> &nxt) {
     constexpr int NQ = Cfg<Q>::NQ;
     const int w = wave_id();
     const int pq = w & 3, nbase = NQ * (w >> 2);
@@ -981,7 +980,7 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
     };
     // the first chunk's loads go out before the incoming state is read, so
     // the two round trips overlap
-    ChunkLoads<Q> ld;
+    ChunkLoads<Q, PACKED> ld;
     {
         int c0, len;
         chunk_at(0, c0, len);
@@ -996,7 +995,7 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
     for (int s = 0; s < nch; ++s) {
         int c0, len;
         chunk_at(s, c0, len);
-        chunk_prep<Q>(a, sm, ld, D, b, h, c0, len);
+        chunk_prep<Q, PACKED>(a, sm, ld, D, b, h, c0, len);
         if (Q == 256) {
             // two tiles per wave: each fetches its own inputs (holding them
             // through the state update would cost spills)
@@ -1022,7 +1021,7 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
             ld.begin(a, D, b, h, grp, c0n, lenn);
             if (Q != 256) tile_fetch<D>(ld.tin, a, b, h, grp, c0n, lenn, tile_of<Q>(w, 0), add);
         }
-        chunk_state_update<Q>(sm, Hacc, len, !last || want_final, ld);
+        chunk_state_update<Q, PACKED>(sm, Hacc, len, !last || want_final, ld);
         // every wave is done with this chunk's tiles and the published state
         lds_barrier();
         if (!last) {
