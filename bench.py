@@ -235,14 +235,14 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
 
-    # per-step distribution, warm and with the caches flushed before each step
-    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
-    out["step_ms_warm"] = step_stats(step, 50, torch)
-    out["step_ms_cold_cache"] = step_stats(step, 50, torch, flush=flush)
-    del flush
-    torch.cuda.empty_cache()
-
     if not args.no_extra:
+        # per-step distribution, warm and with the caches flushed before each
+        # step (after the timed loop, so a profile of --no-extra sees only it)
+        flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        out["step_ms_warm"] = step_stats(step, 50, torch)
+        out["step_ms_cold_cache"] = step_stats(step, 50, torch, flush=flush)
+        del flush
+        torch.cuda.empty_cache()
         out["extra"] = extras(args, bm, synth, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(f, b, y, w, torch, np)
