@@ -183,7 +183,7 @@ __device__ __forceinline__ float wave_scan(float v) {
 // rows in memory), raw, into dst (row stride RS). All global loads are issued
 // before the first LDS write so that they overlap; rows at or past `tlimit`
 // are loaded clamped and stored as zeros.
-template <int ROWS, int COLS, int RS, int NT, bool BROWS = false>
+template <int ROWS, int COLS, int RS, int NT, bool BROWS = false, int WB = 0>
 struct RowStage {
     static constexpr int CG = COLS / 8;
     static constexpr int ITEMS = ROWS * CG;
@@ -195,7 +195,7 @@ struct RowStage {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             if (k < k0 || k >= k1) continue;
-            const int item = threadIdx.x + k * NT;
+            const int item = (int)threadIdx.x - 64 * WB + k * NT;
             if (ITEMS % NT == 0 || item < ITEMS) {
                 const int row = item / CG, cg = item % CG;
                 v[k] = ld8(m0 + (uint32_t)min(row, tlimit - 1) * rstride + 8 * cg);
@@ -208,7 +208,7 @@ struct RowStage {
     __device__ __forceinline__ void store(int tlimit, uint16_t *dst) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int item = threadIdx.x + k * NT;
+            const int item = (int)threadIdx.x - 64 * WB + k * NT;
             if (ITEMS % NT == 0 || item < ITEMS) {
                 const int row = item / CG, cg = item % CG;
                 const u32x4 z = {0u, 0u, 0u, 0u};
@@ -377,6 +377,11 @@ struct Cfg {
     static constexpr int NQ = 32 / NW;   // 16x16 state tiles per wave
 };
 
+// The wave's index within its group of Cfg<Q>::NW waves: the workgroup, or
+// (WB = 4) the upper half of the two-direction workgroup of k_dual_out.
+template <int WB>
+__device__ __forceinline__ int wave_in() { return wave_id() - WB; }
+
 template <int Q>
 struct OutSmem {
     float cs2[Q];          // inclusive scan of a in the walking direction, times log2(e)
@@ -433,11 +438,11 @@ __device__ __forceinline__ void tile_fetch(TileIn &t, const SegArgs &a, int b, i
 // latency overlaps it): x and B for every thread, and for waves 0 and 1 the
 // dt (and sequence index) of the chunk's tokens, Q/64 per lane, in walking
 // order (wave 0) or from the outgoing edge (wave 1).
-template <int Q, bool PACKED>
+template <int Q, bool PACKED, int WB = 0>
 struct ChunkLoads {
     static constexpr int TPL = Q / 64;   // tokens per lane of the scanning waves
-    RowStage<Q, kP, kXS, Cfg<Q>::NT> sx;
-    RowStage<Q, kN, kBS, Cfg<Q>::NT, true> sb;
+    RowStage<Q, kP, kXS, Cfg<Q>::NT, false, WB> sx;
+    RowStage<Q, kN, kBS, Cfg<Q>::NT, true, WB> sb;
     uint16_t dtv[TPL];   // raw bf16 bits: no use (and no wait) until the scan
     int sqv[TPL];
     TileIn tin;          // the wave's first row tile
@@ -457,7 +462,7 @@ struct ChunkLoads {
     __device__ __forceinline__ void begin(const SegArgs &a, int d, int b, int h, int grp, int c0,
                                           int len) {
         const DirPtrs &dp = a.dir[d];
-        const int wv = wave_id(), lane = lane_id();
+        const int wv = wave_in<WB>(), lane = lane_id();
         if (wv < 2) {
             const uint16_t *DT = (const uint16_t *)dp.dt;
 #pragma unroll
@@ -511,12 +516,12 @@ __device__ __forceinline__ void store_run(V *dst, bool asc, int lane, const V (&
 // masks, staged x and B; one barrier. Wave 0 scans a over the chunk in the
 // walking direction, wave 1 toward the outgoing edge, each with Q/64 tokens
 // per lane; the tile-edge values come from lane shuffles.
-template <int Q, bool PACKED>
-__device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q, PACKED> &ld, int d,
-                           int b, int h, int c0, int len) {
-    using LD = ChunkLoads<Q, PACKED>;
+template <int Q, bool PACKED, int WB = 0>
+__device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q, PACKED, WB> &ld,
+                           int d, int b, int h, int c0, int len) {
+    using LD = ChunkLoads<Q, PACKED, WB>;
     constexpr int TPL = LD::TPL;
-    const int lane = lane_id(), wv = wave_id();
+    const int lane = lane_id(), wv = wave_in<WB>();
     const float Ah = a.dir[d].A[h];
     ld.sx.store(len, sm.xs);
     ld.sb.store(len, sm.bn);
@@ -625,10 +630,10 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q, PACKE
 
 // The wave's state block (p-tile w%4, n-half w/4; fp32 accumulators) into
 // H^T hi / lo.
-template <int Q>
+template <int Q, int WB = 0>
 __device__ void publish_state(OutSmem<Q> &sm, const f32x4 (&Hacc)[Cfg<Q>::NQ]) {
     constexpr int NQ = Cfg<Q>::NQ;
-    const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
+    const int lane = lane_id(), w = wave_in<WB>(), g4 = lane >> 4, l16 = lane & 15;
     const int pq = w & 3, nbase = NQ * (w >> 2);
     uint16_t *hh = sm.hs;
     uint16_t *hl = hh + kP * kNRS;
@@ -766,9 +771,12 @@ __device__ __forceinline__ void diag_block(f32x4 (&acc)[4], const OutSmem<Q> &sm
 // Rows and columns past the chunk's end need no mask: their x and B were
 // staged as zeros and their dt is 0, so every such entry is a finite value
 // times 0, and a row past the end only reaches its own (unstored) output.
-template <int Q, bool PACKED, int D>
+// STORE: adds the reverse pass's rows (add) and writes y; otherwise hands
+// this direction's sums for the tile back in `out`.
+template <int Q, bool PACKED, int D, bool STORE = true>
 __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, int c0, int len,
-                         int it, bool has_state, float Dh, bool add, const TileIn &tin) {
+                         int it, bool has_state, float Dh, bool add, const TileIn &tin,
+                         f32x4 *out = nullptr) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
     const uint16_t *bn = sm.bn;
     const int I = it >> 2, wq = it & 3;   // 64-row block, tile inside it
@@ -875,6 +883,11 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
         acc[pt][2] = fmaf(Dh, b_lo(xv[1]), acc[pt][2]);
         acc[pt][3] = fmaf(Dh, b_hi(xv[1]), acc[pt][3]);
     }
+    if constexpr (!STORE) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) out[pt] = acc[pt];
+        return;
+    }
     if (add) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
@@ -912,11 +925,11 @@ __device__ __forceinline__ int tile_of(int w, int k) {
 // H <- gamma H + sum over the chunk's tokens of w_t B_t x_t^T (the wave's
 // block of the state). B^T and x come straight from the staged natural tiles
 // through transposing reads: no barrier.
-template <int Q, bool PACKED>
+template <int Q, bool PACKED, bool PF = true, int WB = 0>
 __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[Cfg<Q>::NQ], int len,
-                                   bool math, ChunkLoads<Q, PACKED> &nxt) {
+                                   bool math, ChunkLoads<Q, PACKED, WB> &nxt) {
     constexpr int NQ = Cfg<Q>::NQ;
-    const int w = wave_id();
+    const int w = wave_in<WB>();
     const int pq = w & 3, nbase = NQ * (w >> 2);
     if (math) {
         const float gmm = sm.gamma;
@@ -927,7 +940,7 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[Cfg<Q>::N
     for (int sb = 0; sb < Q / kSub; ++sb) {
         // a slice of the next chunk's loads per sub-block, so the memory
         // pipeline works beside the matrix cores
-        nxt.part(sb, Q / kSub);
+        if (PF) nxt.part(sb, Q / kSub);
         if (!math || kSub * sb >= len || !sm.wsub[sb]) continue;   // every weight is exactly 0
         // both 32-token halves' operands first, then their products
         u32x4 aop[kSub / 32][NQ], bhi[kSub / 32], blo[kSub / 32];
@@ -1063,6 +1076,99 @@ k_seg_out(const SegArgs a) {
     }
 }
 
+// ------------------------------------------------------------ k_dual_out
+// Rows of at most one 64-token chunk (the block-decode step), both
+// directions at once: waves 0-3 run the reverse direction and waves 4-7 the
+// forward one, each half with its own staged tiles, so that the two passes
+// (and their memory latencies) overlap instead of running back to back. The
+// reverse half leaves its tile sums in LDS; the forward half adds them and
+// writes y. Both halves pass the same two workgroup barriers.
+constexpr int kEX = kP + 4;   // row stride (floats) of the exchanged tile sums
+
+struct DualSmem {
+    OutSmem<64> half[2];   // [0] reverse, [1] forward
+    alignas(16) float ex[64 * kEX];
+};
+
+// Output rows of row tile `it` (this lane: rows 16 it + 4 g4 + r, column
+// 16 pt + l16): acc[pt][r].
+__device__ __forceinline__ void store_tile(const SegArgs &a, int b, int h, int len, int it,
+                                           const f32x4 (&acc)[4]) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+    const int i0 = 16 * it + 4 * g4;
+    float *ybase = a.y + (tok(a, b, 0) * a.H + h) * kP + l16;
+    const uint32_t ystride = (uint32_t)(a.H * kP);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (i0 + r >= len) continue;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) ybase[(uint32_t)(i0 + r) * ystride + 16 * pt] = acc[pt][r];
+    }
+}
+
+// D: the half's direction; WB: its first wave (0 for D = 1, 4 for D = 0)
+template <int D, int WB>
+__device__ void dual_half(const SegArgs &a, OutSmem<64> &sm, float *ex, int b, int h, int grp) {
+    constexpr int Q = 64, NQ = Cfg<Q>::NQ;
+    const int lane = lane_id(), w = wave_in<WB>(), g4 = lane >> 4, l16 = lane & 15;
+    const int len = a.L;
+    const DirPtrs &dp = a.dir[D];
+    const float Dh = dp.D ? dp.D[h] : 0.f;
+    const size_t PN = (size_t)kP * kN;
+    const int hoff = (16 * w + l16) * kN + 4 * g4;   // + 16 q: this lane's state entries
+    ChunkLoads<Q, false, WB> ld;
+    ld.issue(a, D, b, h, grp, 0, len);
+    TileIn tin;
+    tile_fetch<D>(tin, a, b, h, grp, 0, len, w, false);
+    f32x4 Hacc[NQ];
+    const float *src = D == 0 && a.init_state ? a.init_state + ((size_t)b * a.H + h) * PN : nullptr;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
+    if (src) publish_state<Q, WB>(sm, Hacc);
+    chunk_prep<Q, false, WB>(a, sm, ld, D, b, h, 0, len);   // barrier 1
+    f32x4 acc[4];
+    const bool mine = 16 * w < len;
+    if (mine)
+        row_tile<Q, false, D, false>(a, sm, b, h, 0, len, w, src != nullptr, Dh, false, tin, acc);
+    if (D == 1 && mine) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ex[(16 * w + 4 * g4 + r) * kEX + 16 * pt + l16] = acc[pt][r];
+    }
+    lds_barrier();   // barrier 2: the reverse sums are in LDS
+    if (D == 0) {
+        if (mine) {
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[pt][r] += ex[(16 * w + 4 * g4 + r) * kEX + 16 * pt + l16];
+            store_tile(a, b, h, len, w, acc);
+        }
+        if (a.final_state) {
+            chunk_state_update<Q, false, false, WB>(sm, Hacc, len, true, ld);
+            float *fs = a.final_state + ((size_t)b * a.H + h) * PN;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) *(f32x4 *)(fs + hoff + 16 * q) = Hacc[q];
+        }
+    }
+}
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+k_dual_out(const SegArgs a) {
+    // XCD-aware order as in k_seg_out
+    const int id = blockIdx.x;
+    const int total = a.batch * a.H;
+    const int per = (total + 7) / 8;
+    const int lin = (id & 7) * per + (id >> 3);
+    if (lin >= total) return;
+    const int b = lin / a.H, h = lin % a.H;
+    const int grp = h / (a.H / a.G);
+    __shared__ __attribute__((aligned(16))) DualSmem sm;
+    if (wave_id() < 4) dual_half<1, 0>(a, sm.half[0], sm.ex, b, h, grp);
+    else dual_half<0, 4>(a, sm.half[1], sm.ex, b, h, grp);
+}
+
 int pick_ts(int batch, int L, int H, int Q) {
     int ts = 2048;
     while (ts > Q && (long)batch * ((L + ts - 1) / ts) * H < 512) ts /= 2;
@@ -1079,6 +1185,11 @@ hipError_t launch_q(const SegArgs &a, hipStream_t s) {
                   s, a);
     }
     const int per_xcd = (a.batch * a.nseg * a.H + 7) / 8;
+    if (Q == 64 && a.ndir == 2 && !a.seq && a.L <= 64) {
+        // one chunk per row: both directions at once
+        BM_LAUNCH("ssd_dual_out", k_dual_out, dim3(per_xcd * 8), dim3(512), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.seq)
         BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
     else

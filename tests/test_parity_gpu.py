@@ -356,3 +356,29 @@ def test_segmented_sequential(case, zero_D):
     err, ok = within(fs, fs_ref, dtype)
     print(f"  final state error {err:.3e}", flush=True)
     assert ok, f"{name}: final state error {err:.3e}"
+
+
+@pytest.mark.parametrize("L", [64, 37, 1])
+@pytest.mark.parametrize("zero_D", [False, True], ids=["D", "D0"])
+def test_single_chunk_rows(L, zero_D):
+    """Rows of at most one 64-token chunk (both directions at once in one
+    workgroup), with incoming and outgoing states."""
+    batch, H, P, N = 3, 4, 64, 128
+    print(f"single chunk L={L} zero_D={zero_D}", flush=True)
+    f, b = synth.make_inputs(batch, L, H, P, N, 1, "bf16", 140 + L, device=DEV)
+    if zero_D:
+        f, b = _zero_D(f), _zero_D(b)
+    g = torch.Generator(device=DEV).manual_seed(141 + L)
+    init = torch.randn(batch, H, P, N, generator=g, device=DEV) * 0.5
+    got, fs = _run(f, b, 64, init=init, want_final=True)
+    ref, fs_ref = oracle.bissd(f, b, init_state=init, want_final_state=True)
+    err, ok = within(got, ref, "bf16")
+    print(f"  y error {err:.3e}", flush=True)
+    assert ok, f"y error {err:.3e}"
+    err, ok = within(fs, fs_ref, "bf16")
+    print(f"  final state error {err:.3e}", flush=True)
+    assert ok, f"final state error {err:.3e}"
+    # without incoming state and without the outgoing one
+    got2, _ = _run(f, b, 64)
+    err, ok = within(got2, oracle.bissd(f, b), "bf16")
+    assert ok, f"y (no state) error {err:.3e}"
