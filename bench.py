@@ -87,6 +87,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--prefix", type=int, default=262144,
                     help="prefix length of the block-step state")
+    ap.add_argument("--block-step-only", action="store_true",
+                    help="only the block-decode step lines (one JSON object)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -129,6 +131,37 @@ def time_steps(bm, fn, steps, warmup, torch, live=True):
     ker = {k: (c, t) for k, (c, t) in prof.kernels.items()}
     dom = max(ker, key=lambda k: ker[k][1])
     return e0.elapsed_time(e1) / steps, wall, ker, dom
+
+
+def graph_step_ms(fn, torch, per_graph=20, replays=50):
+    """GPU time per call with the host out of the way: `per_graph` calls
+    captured once into a HIP graph (the calls launch kernels only: no
+    allocation, no memset, no synchronization) and the graph replayed
+    `replays` times between two events. Returns ms per call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (replays * per_graph)
+    del g
+    return ms
 
 
 def step_stats(fn, steps, torch, flush=None):
@@ -184,6 +217,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.block_step_only:
+        print(json.dumps({"block_step": block_step_bench(args, bm, synth, torch, dev, args.steps)}),
+              flush=True)
+        return
     w = synth.WORKLOADS["layer_1p3b_train"]
     f, b = synth.make_workload(w, device=dev)
     torch.cuda.synchronize()
@@ -357,9 +394,13 @@ def block_step_bench(args, bm, synth, torch, dev, steps):
         out[key] = {"ms_per_step": round(ms, 5), "bytes_per_step": per_seq * nseq,
                     "hbm_roofline_frac_step": round(per_seq * nseq / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "roofline": roofline_for(ker, dom, per_seq * nseq)}
+        # the same step with the host out of the way (graph replay): the
+        # launch-bound batch-1 step is mostly host time when called one by one
+        out[key]["ms_per_step_graph"] = round(graph_step_ms(fn, torch), 5)
         fc = lambda: bm.block_step(st, f, b, commit=True, chunk=64, y=y)  # noqa: E731
         msc, _, _, _ = time_steps(bm, fc, 20, 5, torch, live=False)
         out[key]["ms_per_commit_step"] = round(msc, 5)
+        out[key]["ms_per_commit_step_graph"] = round(graph_step_ms(fc, torch), 5)
         st.free()
         del f, b, y
         torch.cuda.empty_cache()

@@ -382,3 +382,52 @@ def test_single_chunk_rows(L, zero_D):
     got2, _ = _run(f, b, 64)
     err, ok = within(got2, oracle.bissd(f, b), "bf16")
     assert ok, f"y (no state) error {err:.3e}"
+
+
+def test_graph_replay_matches_eager():
+    """The calls launch kernels only, so they can be captured into a HIP
+    graph; every replay (with other work in between) reproduces the eager
+    result bit for bit."""
+    c = synth.BLOCK_STEP
+    H, P, N, G = 8, c["headdim"], c["d_state"], c["ngroups"]
+    st = bm.State(2, H, P, N)
+    pf, _ = synth.make_inputs(2, 200, H, P, N, G, "bf16", 151, device=DEV, bidirectional=False)
+    bm.ssd_fwd(pf, None, chunk=64, final_state=st.tensor())
+    f, b = synth.make_inputs(2, 64, H, P, N, G, "bf16", 152, device=DEV)
+    y_blk = torch.empty(2, 64, H, P, device=DEV)
+    lf, lb = synth.make_inputs(1, 4096, H, P, N, G, "bf16", 153, device=DEV)
+    shape = bm.make_shape(lf["x"], lf["B"], 256)
+    ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=DEV)
+    assert bm.workspace_size(shape, 0) > 0   # several segments: three kernels
+    y_long = torch.empty(1, 4096, H, P, device=DEV)
+
+    def step():
+        bm.block_step(st, f, b, commit=False, chunk=64, y=y_blk)
+        bm.ssd_fwd(lf, lb, chunk=256, y=y_long, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_blk, ref_long = y_blk.clone(), y_long.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other_f, other_b = synth.make_inputs(1, 300, H, P, N, G, "bf16", 154, device=DEV)
+    for rep in range(3):
+        y_blk.fill_(float("nan"))
+        y_long.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"replay {rep}", flush=True)
+        assert torch.equal(y_blk, ref_blk), f"block step differs on replay {rep}"
+        assert torch.equal(y_long, ref_long), f"forward call differs on replay {rep}"
+        # eager work between replays
+        bm.ssd_fwd(other_f, other_b, chunk=128)
+        torch.cuda.synchronize()
+    del g
+    st.free()
