@@ -69,6 +69,12 @@ constexpr int bn_elems(int rows) { return rows * kBS; }
 constexpr int kXS = kP + 16;   // LDS row stride (16-bit elements) of x [t][p] tiles
 constexpr float kDead = -110.f;  // expf(x) is exactly 0.0f for every x < kDead
 constexpr float kLog2e = 1.4426950408889634f;
+// Where every decay factor of a block of products is at most 2^kOneRound,
+// its decayed operand is rounded once to bf16 instead of split into hi + lo:
+// the rounding error, at most 2^-9 of an entry, is then at most 2^-17 of the
+// undecayed product, the bound the hi/lo pair gives where the factor is 1.
+constexpr float kOneRound = -8.f;   // log2 of the factor
+
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -79,6 +85,11 @@ __device__ __forceinline__ void split2(float v0, float v1, uint32_t &hi, uint32_
     const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
     const bf16x2_t l = {(__bf16)(v0 - h0), (__bf16)(v1 - h1)};
     lo = __builtin_bit_cast(uint32_t, l);
+}
+// bf16(v0), bf16(v1) packed (one rounding, no residual)
+__device__ __forceinline__ uint32_t pack2(float v0, float v1) {
+    const bf16x2_t h = {(__bf16)v0, (__bf16)v1};
+    return __builtin_bit_cast(uint32_t, h);
 }
 __device__ __forceinline__ float b_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float b_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -222,19 +233,28 @@ struct RowStage {
 // B operand of the state update for the 32 tokens t32..t32+31 and the 16
 // columns p0..p0+15: (w_t x_t[p]) split into bf16 hi / lo. xs: x [t][p]
 // (row stride kXS); wv: the weights, natural token order.
+// With !lo (every weight factor at most 2^kOneRound) only bhi, rounded once.
 __device__ __forceinline__ void wx_operand(const uint16_t *xs, int t32, int p0, const float *wv,
-                                           u32x4 &bhi, u32x4 &blo) {
+                                           u32x4 &bhi, u32x4 &blo, bool lo = true) {
     const int g4 = (threadIdx.x & 63) >> 4;
     const u32x4 xv = tr_operand(xs, kXS, t32, p0);
     const f32x4 w0 = *(const f32x4 *)(wv + t32 + 4 * g4);        // k slots 0..3
     const f32x4 w1 = *(const f32x4 *)(wv + t32 + 16 + 4 * g4);   // k slots 4..7
-    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-    split2(b_lo(xv[0]) * w0[0], b_hi(xv[0]) * w0[1], h0, l0);
-    split2(b_lo(xv[1]) * w0[2], b_hi(xv[1]) * w0[3], h1, l1);
-    split2(b_lo(xv[2]) * w1[0], b_hi(xv[2]) * w1[1], h2, l2);
-    split2(b_lo(xv[3]) * w1[2], b_hi(xv[3]) * w1[3], h3, l3);
-    bhi = u32x4{h0, h1, h2, h3};
-    blo = u32x4{l0, l1, l2, l3};
+    const float v[8] = {b_lo(xv[0]) * w0[0], b_hi(xv[0]) * w0[1], b_lo(xv[1]) * w0[2],
+                        b_hi(xv[1]) * w0[3], b_lo(xv[2]) * w1[0], b_hi(xv[2]) * w1[1],
+                        b_lo(xv[3]) * w1[2], b_hi(xv[3]) * w1[3]};
+    if (lo) {
+        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+        split2(v[0], v[1], h0, l0);
+        split2(v[2], v[3], h1, l1);
+        split2(v[4], v[5], h2, l2);
+        split2(v[6], v[7], h3, l3);
+        bhi = u32x4{h0, h1, h2, h3};
+        blo = u32x4{l0, l1, l2, l3};
+    } else {
+        bhi = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+        blo = u32x4{0u, 0u, 0u, 0u};
+    }
 }
 
 // ----------------------------------------------------------- k_seg_state
@@ -375,6 +395,9 @@ struct Cfg {
     static constexpr int NW = Q == 64 ? 4 : 8;
     static constexpr int NT = 64 * NW;
     static constexpr int NQ = 32 / NW;   // 16x16 state tiles per wave
+    // single rounding where every decay factor is at most 2^kOneRound (off
+    // for 128-token chunks, where the extra branches measured slower)
+    static constexpr bool ONE_ROUND = Q != 128;
 };
 
 // The wave's index within its group of Cfg<Q>::NW waves: the workgroup, or
@@ -393,6 +416,7 @@ struct OutSmem {
     int sq[Q];             // sequence index (packed) of each token
     int utile[Q / 16];     // the carried state reaches some row of the 16-row tile
     int wsub[Q / kSub];    // some weight of the 64-token sub-block is nonzero
+    int wbig[Q / kSub];    // some weight factor of the sub-block exceeds 2^kOneRound
     float gamma;           // decay of the whole chunk (0: the state does not pass)
     float bt2[Q / 64][Q / 64];  // [I][J] (walking order, J < I): sum of a over the blocks strictly between, times log2(e)
     int sq_nb;             // sequence index of the token the carried state comes from
@@ -605,23 +629,29 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q, PACKE
         } else {
             // exclusive sums toward the outgoing edge -> weight of each token
             // in the state leaving the chunk
-            bool nz = false;
+            bool nz = false, big = false;
             float wv_[TPL];
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
                 const int pos = LD::pos_of(d, 1, lane, i);
                 float wt = 0.f;
-                if (pos < len && (!PACKED || ld.sqv[i] == sq_edge))
-                    wt = expf((float)(cs[i] - (double)at[i])) * dtf[i];
+                if (pos < len && (!PACKED || ld.sqv[i] == sq_edge)) {
+                    const double lf = cs[i] - (double)at[i];   // log of the weight factor
+                    wt = expf((float)lf) * dtf[i];
+                    if (Cfg<Q>::ONE_ROUND) big |= lf * (double)kLog2e > (double)kOneRound;
+                }
                 wv_[i] = wt;
                 nz |= wt != 0.f;
             }
             store_run<Q, TPL>(sm.w, d != 0, lane, wv_);   // wave 1 walks from the edge
             const unsigned long long m = __ballot(nz);
+            const unsigned long long mb = Cfg<Q>::ONE_ROUND ? __ballot(big) : 0ull;
             if (lane < Q / 64) {
                 constexpr int LPS = 64 / TPL;   // lanes per 64-token sub-block
-                const bool any = LPS == 64 ? m != 0ull : ((m >> (lane * LPS)) & ((1ull << (LPS & 63)) - 1)) != 0;
-                sm.wsub[d == 0 ? Q / 64 - 1 - lane : lane] = any;
+                constexpr unsigned long long lm = LPS == 64 ? ~0ull : (1ull << (LPS & 63)) - 1;
+                const int sb = d == 0 ? Q / 64 - 1 - lane : lane;
+                sm.wsub[sb] = ((m >> ((lane * LPS) & 63)) & lm) != 0;
+                if (Cfg<Q>::ONE_ROUND) sm.wbig[sb] = ((mb >> ((lane * LPS) & 63)) & lm) != 0;
             }
         }
     }
@@ -662,14 +692,16 @@ __device__ __forceinline__ f32x4 gram_tile(const uint16_t *bn, int j0, const u32
 // in the k order of a Gram accumulator pair, which is the order in which the
 // transposing reads deliver x.
 __device__ __forceinline__ void mx_step(f32x4 (&acc)[4], const uint16_t *xs, int j32, u32x4 mhi,
-                                        u32x4 mlo) {
+                                        u32x4 mlo, bool lo = true) {
     u32x4 xo[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) xo[pt] = tr_operand(xs, kXS, j32, 16 * pt);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16x16x32(mhi, xo[pt], acc[pt]);
+    if (lo) {
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16x16x32(mlo, xo[pt], acc[pt]);
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16x16x32(mlo, xo[pt], acc[pt]);
+    }
 }
 
 // Two G^T tiles (rows j0a.., j0b..) at once: all operand loads first, then
@@ -803,9 +835,10 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
         const float between = sm.bt2[Iw][Jw];
         if (between < kDead * kLog2e) continue;   // every entry is exactly 0
         const float u64 = exp2_(rli + between);
+        const bool lo = !Cfg<Q>::ONE_ROUND || between > kOneRound;   // else one rounding suffices
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            uint32_t ph[4], pl[4];
+            uint32_t ph[4], pl[4] = {0u, 0u, 0u, 0u};
             f32x4 gp[2];
             gram_pair(bn, 64 * J + 32 * kk, 64 * J + 32 * kk + 16, cr, gp[0], gp[1]);
 #pragma unroll
@@ -818,11 +851,16 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
 #pragma unroll
                 for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u64 * vv[r]);
                 seq_mask<Q, PACKED>(mv, sm, jb, sqi);
-                split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
-                split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
+                if (lo) {
+                    split2(mv[0], mv[1], ph[2 * half], pl[2 * half]);
+                    split2(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
+                } else {
+                    ph[2 * half] = pack2(mv[0], mv[1]);
+                    ph[2 * half + 1] = pack2(mv[2], mv[3]);
+                }
             }
             mx_step(acc, sm.xs, 64 * J + 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
-                       u32x4{pl[0], pl[1], pl[2], pl[3]});
+                    u32x4{pl[0], pl[1], pl[2], pl[3]}, lo);
         }
     }
     switch (wq) {
@@ -837,22 +875,36 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
     if (has_state && sm.utile[it]) {
         const uint16_t *hh = sm.hs;
         const uint16_t *hl = hh + kP * kNRS;
+        // the tile's largest factor is that of its first row in walking order
+        const bool lo = !Cfg<Q>::ONE_ROUND || sm.cs2[D == 0 ? 16 * it : 16 * it + 15] > kOneRound;
         f32x4 tt[4];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) tt[pt] = zero4();
+        if (lo) {
 #pragma unroll
-        for (int ks = 0; ks < kN / 32; ++ks) {
-            u32x4 oh[4], ol[4];
+            for (int ks = 0; ks < kN / 32; ++ks) {
+                u32x4 oh[4], ol[4];
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int o = (16 * pt + l16) * kNRS + 32 * ks + 8 * g4;
-                oh[pt] = *(const u32x4 *)(hh + o);
-                ol[pt] = *(const u32x4 *)(hl + o);
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int o = (16 * pt + l16) * kNRS + 32 * ks + 8 * g4;
+                    oh[pt] = *(const u32x4 *)(hh + o);
+                    ol[pt] = *(const u32x4 *)(hl + o);
+                }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32(cr[ks], oh[pt], tt[pt]);
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32(cr[ks], ol[pt], tt[pt]);
             }
+        } else {
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32(cr[ks], oh[pt], tt[pt]);
+            for (int ks = 0; ks < kN / 32; ++ks) {
+                u32x4 oh[4];
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32(cr[ks], ol[pt], tt[pt]);
+                for (int pt = 0; pt < 4; ++pt)
+                    oh[pt] = *(const u32x4 *)(hh + (16 * pt + l16) * kNRS + 32 * ks + 8 * g4);
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32(cr[ks], oh[pt], tt[pt]);
+            }
         }
         const f32x4 c4 = *(const f32x4 *)(sm.cs2 + i0);
         float uu[4];
@@ -949,15 +1001,18 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[Cfg<Q>::N
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
                 aop[ks][q] = tr_operand_bn(sm.bn, kSub * sb + 32 * ks, 16 * (nbase + q));
+        const bool lo = !Cfg<Q>::ONE_ROUND || sm.wbig[sb];   // else one rounding suffices
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks)
-            wx_operand(sm.xs, kSub * sb + 32 * ks, 16 * pq, sm.w, bhi[ks], blo[ks]);
+            wx_operand(sm.xs, kSub * sb + 32 * ks, 16 * pq, sm.w, bhi[ks], blo[ks], lo);
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks) {
 #pragma unroll
             for (int q = 0; q < NQ; ++q) Hacc[q] = mfma16x16x32(aop[ks][q], bhi[ks], Hacc[q]);
+            if (lo) {
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) Hacc[q] = mfma16x16x32(aop[ks][q], blo[ks], Hacc[q]);
+                for (int q = 0; q < NQ; ++q) Hacc[q] = mfma16x16x32(aop[ks][q], blo[ks], Hacc[q]);
+            }
         }
     }
 }
