@@ -431,3 +431,58 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
     del g
     st.free()
+
+
+def _random_cases(n, seed):
+    """Seeded random problems over both kernel families: chunk size, length
+    (ragged tails, a single token, several segments), batch, heads and
+    groups, packed batches (with empty sequences), incoming and outgoing
+    states, one or both directions, D or D = 0."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        chunked = k % 3 != 2
+        dtype = "bf16" if chunked else ["f32", "bf16"][k % 2]
+        P, N = (64, 128) if chunked else ([16, 32, 64][k % 3], [16, 32, 64, 128][k % 4])
+        G = int(rng.choice([1, 2]))
+        H = G * int(rng.integers(1, 4))
+        chunk = int(rng.choice([64, 128, 256]))
+        packed = k % 4 == 1
+        batch = 1 if packed else int(rng.integers(1, 4))
+        L = int(rng.choice([1, 17, 64, 65, 200, 511, 700, 1500, 2100]))
+        cases.append(dict(k=k, dtype=dtype, P=P, N=N, G=G, H=H, chunk=chunk, packed=packed,
+                          batch=batch, L=L, bidir=k % 5 != 3, zero_D=k % 2 == 1,
+                          states=not packed and k % 3 == 0, seed=1000 + k))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(24, 77), ids=lambda c: f"r{c['k']}")
+def test_random_shapes(case):
+    c = case
+    print(f"random case {c}", flush=True)
+    f, b = synth.make_inputs(c["batch"], c["L"], c["H"], c["P"], c["N"], c["G"], c["dtype"],
+                             c["seed"], device=DEV)
+    if c["zero_D"]:
+        f, b = _zero_D(f), _zero_D(b)
+    if not c["bidir"]:
+        b = None
+    cu = None
+    if c["packed"]:
+        rng = np.random.default_rng(c["seed"])
+        cuts = np.sort(rng.integers(0, c["L"] + 1, size=3))
+        cu = [0] + [int(x) for x in cuts] + [c["L"]]   # may hold empty sequences
+    init = None
+    if c["states"]:
+        g = torch.Generator(device=DEV).manual_seed(c["seed"])
+        init = torch.randn(c["batch"], c["H"], c["P"], c["N"], generator=g, device=DEV) * 0.5
+    got, fs = _run(f, b, c["chunk"], cu=cu, init=init, want_final=c["states"])
+    ref = oracle.bissd(f, b, cu_seqlens=cu, init_state=init, want_final_state=c["states"])
+    if c["states"]:
+        ref, fs_ref = ref
+    err, ok = within(got, ref, c["dtype"])
+    print(f"  y error {err:.3e}", flush=True)
+    assert ok, f"y error {err:.3e}"
+    if c["states"]:
+        err, ok = within(fs, fs_ref, c["dtype"])
+        print(f"  final state error {err:.3e}", flush=True)
+        assert ok, f"final state error {err:.3e}"
