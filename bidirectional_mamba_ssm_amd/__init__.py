@@ -29,17 +29,45 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def _dir(d, dtype):
-    for k in ("x", "dt", "B", "C"):
-        t = d[k]
-        if t.dtype != dtype:
-            raise TypeError(f"{k} has dtype {t.dtype}, expected {dtype}")
-        if not t.is_contiguous():
-            raise ValueError(f"{k} must be contiguous")
-    for k in ("A", "D"):
-        t = d.get(k)
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
-            raise TypeError(f"{k} must be a contiguous float32 tensor")
+def _check(t, name, shape, dtype, device):
+    """The library sees plain pointers: every tensor's device, dtype, shape and
+    layout is checked here, before anything is launched."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _cuda_device(x):
+    if x.device.type != "cuda":
+        raise ValueError(f"tensors must be on a CUDA device, not {x.device}")
+    return x.device
+
+
+def _dims(d):
+    x, B = d["x"], d["B"]
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [batch, L, H, P] and B [batch, L, G, N]")
+    batch, L, H, P = x.shape
+    return batch, L, H, P, B.shape[2], B.shape[3]
+
+
+def _dir(d, dtype, dims=None, device=None, name="fwd"):
+    batch, L, H, P, G, N = dims if dims is not None else _dims(d)
+    device = device if device is not None else d["x"].device
+    _check(d["x"], f"{name}.x", (batch, L, H, P), dtype, device)
+    _check(d["dt"], f"{name}.dt", (batch, L, H), dtype, device)
+    _check(d["B"], f"{name}.B", (batch, L, G, N), dtype, device)
+    _check(d["C"], f"{name}.C", (batch, L, G, N), dtype, device)
+    _check(d["A"], f"{name}.A", (H,), torch.float32, device)
+    if d.get("D") is not None:
+        _check(d["D"], f"{name}.D", (H,), torch.float32, device)
     return _abi.Dir(d["x"].data_ptr(), d["dt"].data_ptr(), d["A"].data_ptr(),
                     d["B"].data_ptr(), d["C"].data_ptr(),
                     d["D"].data_ptr() if d.get("D") is not None else None)
@@ -70,20 +98,31 @@ def ssd_fwd(fwd, bwd=None, chunk=256, cu_seqlens=None, init_state=None,
     nseq+1 offsets. Returns y (float32 [b,L,H,P]).
     """
     x = fwd["x"]
+    dims = _dims(fwd)
+    batch, L, H, P, G, N = dims
     shape = make_shape(x, fwd["B"], chunk)
     dtype = x.dtype
-    fd = _dir(fwd, dtype)
-    bd = _dir(bwd, dtype) if bwd is not None else None
+    dev = _cuda_device(x)
+    fd = _dir(fwd, dtype, dims, dev, "fwd")
+    bd = _dir(bwd, dtype, dims, dev, "bwd") if bwd is not None else None
     cu_arr, nseq = None, 0
     if cu_seqlens is not None:
         vals = [int(v) for v in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
         nseq = len(vals) - 1
         cu_arr = (ctypes.c_int32 * len(vals))(*vals)
+    units = nseq if cu_seqlens is not None else batch
+    for t, name in ((init_state, "init_state"), (final_state, "final_state")):
+        if t is not None:
+            _check(t, name, (units, H, P, N), torch.float32, dev)
     if y is None:
-        y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        y = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    _check(y, "y", (batch, L, H, P), torch.float32, dev)
     need = workspace_size(shape, nseq)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {dev}")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _abi.check(lib().bimamba_ssd_fwd(
         ctypes.byref(shape), ctypes.byref(fd), ctypes.byref(bd) if bd is not None else None,
@@ -142,11 +181,14 @@ class State:
 def block_step(state, fwd, bwd, commit=False, chunk=64, y=None, stream=None):
     """One cached block-diffusion step (bimamba_block_step)."""
     x = fwd["x"]
+    dims = _dims(fwd)
     shape = make_shape(x, fwd["B"], chunk)
-    fd = _dir(fwd, x.dtype)
-    bd = _dir(bwd, x.dtype)
+    dev = _cuda_device(x)
+    fd = _dir(fwd, x.dtype, dims, dev, "fwd")
+    bd = _dir(bwd, x.dtype, dims, dev, "bwd")
     if y is None:
         y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _check(y, "y", tuple(x.shape), torch.float32, x.device)
     _abi.check(lib().bimamba_block_step(state.handle, ctypes.byref(shape), ctypes.byref(fd),
                                         ctypes.byref(bd), int(bool(commit)), _ptr(y),
                                         _stream(stream)))
@@ -157,6 +199,8 @@ def seq_index(cu_seqlens, device="cuda", stream=None):
     """Per-token packed-sequence index built on the GPU (int32 [total])."""
     vals = [int(v) for v in cu_seqlens]
     total = vals[-1]
+    if torch.device(device).type != "cuda":
+        raise ValueError(f"device must be a CUDA device, not {device}")
     out = torch.empty(max(total, 1), dtype=torch.int32, device=device)
     arr = (ctypes.c_int32 * len(vals))(*vals)
     _abi.check(lib().bimamba_seq_index(arr, len(vals) - 1, total, _ptr(out), _stream(stream)))
