@@ -250,6 +250,8 @@ int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
     if (bwd && (rc = check_dir(bwd, "reverse", empty))) return rc;
     if (!y && !empty) return fail(BIMAMBA_EINVAL, "y is NULL");
     if (!aligned16(y)) return fail(BIMAMBA_EINVAL, "y must be 16-byte aligned");
+    if (!aligned16(init_state) || !aligned16(final_state))
+        return fail(BIMAMBA_EINVAL, "init_state and final_state must be 16-byte aligned");
     if (cu_seqlens) {
         if (s->batch != 1) return fail(BIMAMBA_EINVAL, "cu_seqlens requires batch == 1");
         if ((rc = check_offsets(cu_seqlens, nseq, s->seqlen))) return rc;

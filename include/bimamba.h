@@ -25,7 +25,7 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    null stream). Nothing synchronizes. A failed launch returns BIMAMBA_EHIP.
  *  - Results are deterministic: the same inputs give the same bits.
- *  - x, B, C and y must be 16-byte aligned.
+ *  - x, B, C, y and the state arrays must be 16-byte aligned.
  */
 #ifndef BIMAMBA_H
 #define BIMAMBA_H

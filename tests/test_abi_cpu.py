@@ -96,6 +96,8 @@ def test_null_arguments(lib):
 def test_misaligned(lib):
     assert call_fwd(lib, shape(), fake_dir(x=FAKE + 2)) == _abi.EINVAL
     assert call_fwd(lib, shape(), fake_dir(), y=FAKE + 4) == _abi.EINVAL
+    assert call_fwd(lib, shape(), fake_dir(), init=FAKE + 4) == _abi.EINVAL
+    assert call_fwd(lib, shape(), fake_dir(), final=FAKE + 8) == _abi.EINVAL
 
 
 def test_bad_offsets(lib):
