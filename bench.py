@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 METRIC = "BiMamba-2 SSD tokens/s + % HBM/MFMA roofline; block-cached step ms"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ssd_seg_out_layer_1p3b_train_hbm_traffic.md")
+MIX_SUMMARY = os.path.join(ROOT, "profiles", "ssd_seg_out_layer_1p3b_train_instruction_mix.md")
 KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_mamba_ssm_amd", "csrc", "ssd_chunked.hip")
 
 
@@ -54,12 +55,12 @@ def flops_per_token(H, P, N, G, Q):
     return 2 * per_dir
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, if it was taken on the kernel source as it stands."""
+def summary_field(path, key):
+    """An integer field of a committed counter summary, if the summary was
+    taken on the kernel source as it stands (else None)."""
     import hashlib
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(path).read()
         src_hash = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
@@ -71,9 +72,14 @@ def measured_traffic():
     if fields.get("kernel_source_sha256") != src_hash:
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields[key])
     except (KeyError, ValueError):
         return None
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE)."""
+    return summary_field(TRAFFIC_SUMMARY, "traffic_bytes_per_launch")
 
 
 def parse():
@@ -194,12 +200,22 @@ def roofline_for(ker, dom, bytes_per_launch, traffic=None):
             "traffic": traffic, "kernel": dom, "avg_us": round(avg_s * 1e6, 2)}
 
 
-def mfma_for(ker, dom, flops_per_launch):
+def mfma_for(ker, dom, flops_per_launch, executed=None):
+    """Algorithmic flops per launch over the kernel's time against the dense
+    bf16 peak; with `executed` (matrix-core flops per launch counted by
+    rocprofv3, SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 x 2) also the executed
+    rate."""
     launches, total_ms = ker[dom]
-    tflops = flops_per_launch / (total_ms / launches / 1e3) / 1e12
-    return {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "kernel": dom,
-            "flops_per_launch": flops_per_launch}
+    sec = total_ms / launches / 1e3
+    tflops = flops_per_launch / sec / 1e12
+    out = {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "kernel": dom,
+           "flops_per_launch": flops_per_launch}
+    if executed:
+        ex = executed / sec / 1e12
+        out.update({"executed_flops_per_launch": executed, "executed_achieved": round(ex, 1),
+                    "executed_frac": round(ex / MFMA_BF16_PEAK_TFLOPS, 4)})
+    return out
 
 
 def main():
@@ -265,7 +281,8 @@ def main():
                    "ngroups": w.ngroups, "chunk": w.chunk, "bidirectional": True,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
-        "mfma": mfma_for(ker, dom, fpt * tokens),
+        "mfma": mfma_for(ker, dom, fpt * tokens,
+                         summary_field(MIX_SUMMARY, "executed_mfma_flops_per_launch")),
         "algorithmic_bytes_per_token": bpt,
         "algorithmic_flops_per_token": fpt,
         "kernels_ms_per_step": {k: round(t / args.steps, 4) for k, (c, t) in ker.items()},
