@@ -52,8 +52,7 @@ def load():
         return _LIB
     if not os.path.exists(LIB_PATH):
         raise LibraryMissing(
-            f"{LIB_PATH} is not built; run __graft_entry__.build() or "
-            "python bidirectional_mamba_ssm_amd/build.py")
+            f"{LIB_PATH} is not built; run python bidirectional_mamba_ssm_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
     sp, dp = ctypes.POINTER(Shape), ctypes.POINTER(Dir)
