@@ -413,7 +413,9 @@ def block_step_bench(args, bm, synth, torch, dev, steps):
                     "roofline": roofline_for(ker, dom, per_seq * nseq)}
         # the same step with the host out of the way (graph replay): the
         # launch-bound batch-1 step is mostly host time when called one by one
-        out[key]["ms_per_step_graph"] = round(graph_step_ms(fn, torch), 5)
+        msg = graph_step_ms(fn, torch)
+        out[key]["ms_per_step_graph"] = round(msg, 5)
+        out[key]["hbm_roofline_frac_graph"] = round(per_seq * nseq / (msg / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
         fc = lambda: bm.block_step(st, f, b, commit=True, chunk=64, y=y)  # noqa: E731
         msc, _, _, _ = time_steps(bm, fc, 20, 5, torch, live=False)
         out[key]["ms_per_commit_step"] = round(msc, 5)
