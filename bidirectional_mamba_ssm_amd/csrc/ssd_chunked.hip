@@ -31,13 +31,20 @@
 //                operand of the next product), the masked decay, M.x, the
 //                carried-state term and D x, with no barrier. The state update
 //                runs with each wave owning a 16 x 64 block of H as MFMA
-//                accumulators.
+//                accumulators. (4 waves and two workgroups per CU for
+//                64-token chunks.)
+//   k_dual_out   rows of at most one 64-token chunk (the block-decode step):
+//                both directions at once, waves 0-3 the reverse one and
+//                waves 4-7 the forward one, the reverse sums handed over
+//                through LDS.
 //
 // Everything runs on v_mfma_f32_16x16x32_bf16. x, B, C are bf16 already and
 // enter exactly. An operand that has to be rounded (the masked decayed Gram
 // matrix M, the carried state H, the dt-weighted inputs w x) is split into
 // hi = bf16(v) and lo = bf16(v - hi) and multiplied twice: ~16 significant
-// bits, fp32's exponent range, no scaling.
+// bits, fp32's exponent range, no scaling. Where every decay factor of such a
+// block is at most 2^-8, one rounding gives the same error bound relative to
+// the undecayed product (kOneRound).
 //
 // Packed sequences: a per-token sequence index masks every term that would
 // cross a sequence boundary, and a chunk or segment holding a boundary (in
