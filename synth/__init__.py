@@ -119,6 +119,34 @@ def make_inputs(batch, L, H, P, N, G, dtype, seed, device="cpu",
     return fwd, bwd
 
 
+# Short convolution in front of the scan (d_conv = 4 over the x | B | C
+# channels): the layer workload's channels, 64 x 64 + 2 x 128 = 4352.
+CONV_LAYER = dict(batch=8, seqlen=1024, nheads=64, headdim=64, ngroups=1,
+                  d_state=128, width=4, dtype="bf16", seed=6)
+
+
+def draw_conv_direction(g, batch, L, ch, width, dtype, device):
+    """One direction's convolution inputs, drawn in this order: the pre-
+    convolution activations xbc ~ N(0, 1) (rounded to the workload dtype),
+    then weight and bias ~ U(-1/sqrt(W), 1/sqrt(W)) (the default initial
+    range of a depthwise Conv1d of width W), fp32."""
+    bound = 1.0 / math.sqrt(width)
+    xbc = torch.randn(batch, L, ch, generator=g, device=device).to(_dtype(dtype))
+    weight = (torch.rand(ch, width, generator=g, device=device) * 2 - 1) * bound
+    bias = (torch.rand(ch, generator=g, device=device) * 2 - 1) * bound
+    return dict(xbc=xbc.contiguous(), weight=weight.float().contiguous(),
+                bias=bias.float().contiguous())
+
+
+def make_conv_inputs(batch, L, ch, width, dtype, seed, device="cpu",
+                     bidirectional=True):
+    """Returns (fwd, bwd) convolution inputs (bwd None if not wanted)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    fwd = draw_conv_direction(g, batch, L, ch, width, dtype, device)
+    bwd = draw_conv_direction(g, batch, L, ch, width, dtype, device) if bidirectional else None
+    return fwd, bwd
+
+
 def make_workload(w: Workload, device="cpu"):
     return make_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.d_state,
                        w.ngroups, w.dtype, w.seed, device)

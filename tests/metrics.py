@@ -38,3 +38,38 @@ def within(got, ref, dtype):
         return e, e <= F32_TOL
     e = rms_err(got, ref)
     return e, e <= BF16_TOL
+
+
+def bf16_rne(v):
+    """Exact round-to-nearest-even of float64 values to bfloat16 (8
+    significant bits), returned as float64. Normal range only."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
+def conv_close(got, ref, scale, dtype, rel=2.0 ** -18):
+    """Output of the short convolution against the fp64 oracle.
+
+    The kernel evaluates each output in fp32 from exact inputs: a handful of
+    fused multiply-adds and one SiLU, so its value before the final rounding
+    lies within delta = rel * (scale + |ref|) of the exact one, where
+    ``scale`` is the same filter applied to |input|, |weight| and |bias|
+    (bounding every partial sum). fp32 outputs must lie within delta; bf16
+    outputs (rounded to nearest even, a monotone map) must lie between the
+    roundings of ref - delta and ref + delta. Returns (worst excess, ok):
+    the largest distance outside the interval in units of delta (0 when
+    every element is inside it); ok is exact interval membership.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    delta = rel * (np.asarray(scale, dtype=np.float64) + np.abs(ref))
+    if got.size == 0:
+        return 0.0, True
+    if dtype == "f32":
+        lo, hi = ref - delta, ref + delta
+    else:
+        lo, hi = bf16_rne(ref - delta), bf16_rne(ref + delta)
+    outside = np.maximum(np.maximum(lo - got, got - hi), 0.0)
+    ok = bool(np.all((got >= lo) & (got <= hi)))
+    return float(np.max(outside / np.maximum(delta, 1e-300))), ok

@@ -79,3 +79,56 @@ def test_pins_catch_mutant(name, tmp_path):
             if not (err <= tol):
                 caught.append(pin)
     assert caught, f"no pin catches mutant {name}"
+
+
+CONV_SRC = open(os.path.join(os.path.dirname(oracle.__file__), "conv.py")).read()
+
+CONV_MUTANTS = {
+    # forward taps applied in the wrong order (filter not reversed in time)
+    "conv_tap_order": ("            src = padded[k:k + T]",
+                       "            src = padded[W - 1 - k:W - 1 - k + T]"),
+    # reverse direction uses the forward (causal) window
+    "conv_reverse_window": ("            src = padded[W - 1 - k:W - 1 - k + T]",
+                            "            src = padded[k:k + T]"),
+    # bias dropped
+    "conv_drop_bias": ("    out = np.zeros((T, ch)) if bias is None else np.tile(bias, (T, 1))",
+                       "    out = np.zeros((T, ch))"),
+    # SiLU with the wrong sign inside the exponential
+    "conv_silu_sign": ("return v / (1.0 + np.exp(-v))", "return v / (1.0 + np.exp(v))"),
+    # taps shifted one token into the past
+    "conv_shift": ("        head = np.zeros((W - 1, ch)) if ctx is None else ctx",
+                   "        head = np.zeros((W, ch)) if ctx is None else np.concatenate([np.zeros((1, ch)), ctx])"),
+    # carried context ignored
+    "conv_ignore_ctx": ("        head = np.zeros((W - 1, ch)) if ctx is None else ctx",
+                        "        head = np.zeros((W - 1, ch))"),
+    # final context written newest first
+    "conv_final_order": ("        final[r] = seq[seq.shape[0] - (W - 1):]",
+                         "        final[r] = seq[seq.shape[0] - (W - 1):][::-1]"),
+    # packed sequences see their neighbours
+    "conv_packed_leak": ("                out[0, a:e] = _filter_row(u[0, a:e], w, b, reverse, None)",
+                         "                out[0, a:e] = _filter_row(u[0], w, b, reverse, None)[a:e]"),
+    # x, B and C split in the wrong order
+    "conv_split_order": ("            out[..., hp:hp + gn].reshape(batch, L, ngroups, d_state),\n            out[..., hp + gn:]",
+                         "            out[..., hp + gn:].reshape(batch, L, ngroups, d_state),\n            out[..., hp:hp + gn]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conv_pins_catch_mutant(name):
+    import types
+    from conv_pins import CONV_PINS
+    a, b = CONV_MUTANTS[name]
+    assert CONV_SRC.count(a) == 1, f"mutation site for {name} not found once"
+    mod = types.ModuleType("conv_mutant")
+    exec(compile(CONV_SRC.replace(a, b), "conv_mutant.py", "exec"), mod.__dict__)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin, (fn, tol) in CONV_PINS.items():
+            try:
+                err = fn(mod)
+            except Exception:
+                caught.append(pin)
+                continue
+            if not (err <= tol):
+                caught.append(pin)
+    assert caught, f"no pin catches mutant {name}"

@@ -1,6 +1,8 @@
 """The oracle against what the pages and the mathematics fix (CPU only)."""
 import pytest
 
+from conv_pins import CONV_PINS
+from oracle import conv
 from pins import ALL_PINS
 
 
@@ -8,4 +10,11 @@ from pins import ALL_PINS
 def test_oracle_pin(name):
     fn, tol = ALL_PINS[name]
     err = fn(None)
+    assert err <= tol, f"pin {name}: error {err} > {tol}"
+
+
+@pytest.mark.parametrize("name", sorted(CONV_PINS))
+def test_conv_oracle_pin(name):
+    fn, tol = CONV_PINS[name]
+    err = fn(conv)
     assert err <= tol, f"pin {name}: error {err} > {tol}"
