@@ -95,6 +95,8 @@ def parse():
                     help="prefix length of the block-step state")
     ap.add_argument("--block-step-only", action="store_true",
                     help="only the block-decode step lines (one JSON object)")
+    ap.add_argument("--conv-only", action="store_true",
+                    help="only the short-convolution line (one JSON object)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -218,6 +220,16 @@ def mfma_for(ker, dom, flops_per_launch, executed=None):
     return out
 
 
+def calibrate_copy(torch, dev):
+    """A plain copy of known size (256 MiB read, 256 MiB written), so that a
+    counter run can scale its byte counters."""
+    src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -233,6 +245,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.conv_only:
+        if args.calibrate_copy:
+            calibrate_copy(torch, dev)
+        print(json.dumps({"conv1d_layer_1p3b_train": conv_bench(args, bm, synth, torch, dev, args.steps)}),
+              flush=True)
+        return
     if args.block_step_only:
         print(json.dumps({"block_step": block_step_bench(args, bm, synth, torch, dev, args.steps)}),
               flush=True)
@@ -249,12 +267,7 @@ def main():
         bm.ssd_fwd(f, b, chunk=w.chunk, y=y, workspace=ws)
 
     if args.calibrate_copy:
-        # a plain copy of known size: 256 MiB read, 256 MiB written
-        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibrate_copy(torch, dev)
 
     ms, wall, ker, dom = time_steps(bm, step, args.steps, args.warmup, torch)
     tokens = w.batch * w.seqlen
@@ -380,6 +393,7 @@ def extras(args, bm, synth, torch, dev):
     torch.cuda.empty_cache()
 
     res["block_step"] = block_step_bench(args, bm, synth, torch, dev, steps)
+    res["conv1d_layer_1p3b_train"] = conv_bench(args, bm, synth, torch, dev, max(steps, 20))
     return res
 
 
@@ -424,6 +438,36 @@ def block_step_bench(args, bm, synth, torch, dev, steps):
         del f, b, y
         torch.cuda.empty_cache()
     return out
+
+
+def conv_bench(args, bm, synth, torch, dev, steps):
+    """The short convolution in front of the scan at the layer's shape (8 x
+    1024 tokens, 64 x 64 + 2 x 128 = 4352 channels, width 4, bf16, SiLU, both
+    directions in one launch). Algorithmic bytes: every input element read
+    once, every output element written once, plus the taps and biases."""
+    c = synth.CONV_LAYER
+    H, P, G, N, W = c["nheads"], c["headdim"], c["ngroups"], c["d_state"], c["width"]
+    ch = bm.conv_channels(H, P, G, N)
+    batch, L = c["batch"], c["seqlen"]
+    f, b = synth.make_conv_inputs(batch, L, ch, W, c["dtype"], c["seed"], device=dev)
+
+    def outs():
+        return dict(x=torch.empty(batch, L, H, P, dtype=torch.bfloat16, device=dev),
+                    B=torch.empty(batch, L, G, N, dtype=torch.bfloat16, device=dev),
+                    C=torch.empty(batch, L, G, N, dtype=torch.bfloat16, device=dev))
+    out = (outs(), outs())
+    fn = lambda: bm.conv1d(f, b, H, P, G, N, out=out)  # noqa: E731
+    ms, _, ker, dom = time_steps(bm, fn, steps, max(3, args.warmup // 10), torch)
+    nbytes = 2 * (2 * batch * L * ch * 2 + ch * (W + 1) * 4)
+    tok = batch * L
+    res = {"workload": f"conv1d {batch}x{L} tokens, {ch} channels, width {W}, bf16, SiLU, both directions",
+           "tokens_per_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+           "bytes_per_launch": nbytes,
+           "roofline": roofline_for(ker, dom, nbytes)}
+    res["ms_per_step_graph"] = round(graph_step_ms(fn, torch), 5)
+    del f, b, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(f, b, y, w, torch, np):

@@ -195,6 +195,84 @@ def block_step(state, fwd, bwd, commit=False, chunk=64, y=None, stream=None):
     return y
 
 
+ACTIVATIONS = {None: 0, "none": 0, "silu": 1}
+
+
+def conv_channels(nheads, headdim, ngroups, d_state):
+    return nheads * headdim + 2 * ngroups * d_state
+
+
+def _conv_dir(d, dims, dtype, device, out, name):
+    batch, L, ch, W = dims
+    _check(d["xbc"], f"{name}.xbc", (batch, L, ch), dtype, device)
+    _check(d["weight"], f"{name}.weight", (ch, W), torch.float32, device)
+    if d.get("bias") is not None:
+        _check(d["bias"], f"{name}.bias", (ch,), torch.float32, device)
+    return _abi.ConvDir(d["xbc"].data_ptr(), d["weight"].data_ptr(),
+                        d["bias"].data_ptr() if d.get("bias") is not None else None,
+                        out["x"].data_ptr(), out["B"].data_ptr(), out["C"].data_ptr())
+
+
+def _conv_out(out, batch, L, nheads, headdim, ngroups, d_state, dtype, device, name):
+    if out is None:
+        out = dict(x=torch.empty(batch, L, nheads, headdim, dtype=dtype, device=device),
+                   B=torch.empty(batch, L, ngroups, d_state, dtype=dtype, device=device),
+                   C=torch.empty(batch, L, ngroups, d_state, dtype=dtype, device=device))
+    _check(out["x"], f"{name}_out.x", (batch, L, nheads, headdim), dtype, device)
+    _check(out["B"], f"{name}_out.B", (batch, L, ngroups, d_state), dtype, device)
+    _check(out["C"], f"{name}_out.C", (batch, L, ngroups, d_state), dtype, device)
+    return out
+
+
+def conv1d(fwd, bwd, nheads, headdim, ngroups, d_state, activation="silu",
+           cu_seqlens=None, init_ctx=None, final_ctx=None, out=None, stream=None):
+    """Short depthwise convolution of the scan inputs (bimamba_conv1d).
+
+    fwd/bwd: dicts of device tensors xbc [b,L,ch] (x | B | C channels, bf16 or
+    fp32), weight [ch,W] f32, bias [ch] f32 or None; bwd may be None.
+    init_ctx/final_ctx: [b, W-1, ch] in xbc's dtype (may be the same tensor).
+    out: optional (fwd_out, bwd_out) dicts of x, B, C to write.
+    Returns (fwd_out, bwd_out), each a dict x [b,L,H,P], B, C [b,L,G,N].
+    """
+    xbc = fwd["xbc"]
+    dev = _cuda_device(xbc)
+    if xbc.dim() != 3 or fwd["weight"].dim() != 2:
+        raise ValueError("xbc must be [batch, L, channels] and weight [channels, width]")
+    batch, L, ch = xbc.shape
+    W = fwd["weight"].shape[1]
+    if ch != conv_channels(nheads, headdim, ngroups, d_state):
+        raise ValueError(f"xbc has {ch} channels, expected nheads*headdim + 2*ngroups*d_state")
+    if xbc.dtype not in DTYPES:
+        raise TypeError(f"unsupported dtype {xbc.dtype}")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation {activation!r} is not one of {sorted(map(str, ACTIVATIONS))}")
+    dims = (batch, L, ch, W)
+    outs = list(out) if out is not None else [None, None]
+    fo = _conv_out(outs[0], batch, L, nheads, headdim, ngroups, d_state, xbc.dtype, dev, "fwd")
+    fd = _conv_dir(fwd, dims, xbc.dtype, dev, fo, "fwd")
+    bo = bd = None
+    if bwd is not None:
+        bo = _conv_out(outs[1], batch, L, nheads, headdim, ngroups, d_state, xbc.dtype, dev, "bwd")
+        bd = _conv_dir(bwd, dims, xbc.dtype, dev, bo, "bwd")
+    cu_arr, nseq = None, 0
+    if cu_seqlens is not None:
+        vals = [int(v) for v in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+        nseq = len(vals) - 1
+        cu_arr = (ctypes.c_int32 * len(vals))(*vals)
+    for t, name in ((init_ctx, "init_ctx"), (final_ctx, "final_ctx")):
+        if t is not None:
+            _check(t, name, (batch, W - 1, ch), xbc.dtype, dev)
+    shape = _abi.ConvShape(batch, L, nheads, headdim, d_state, ngroups, W,
+                           DTYPES[xbc.dtype], ACTIVATIONS[activation], 0)
+    n = ctypes.c_size_t(0)
+    _abi.check(lib().bimamba_conv1d_workspace_size(ctypes.byref(shape), nseq, ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev) if n.value else None
+    _abi.check(lib().bimamba_conv1d(
+        ctypes.byref(shape), ctypes.byref(fd), ctypes.byref(bd) if bd is not None else None,
+        cu_arr, nseq, _ptr(init_ctx), _ptr(final_ctx), _ptr(ws), n.value, _stream(stream)))
+    return fo, bo
+
+
 def seq_index(cu_seqlens, device="cuda", stream=None):
     """Per-token packed-sequence index built on the GPU (int32 [total])."""
     vals = [int(v) for v in cu_seqlens]

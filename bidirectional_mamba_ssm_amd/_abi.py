@@ -20,7 +20,7 @@ EXPORTS = (
     "bimamba_state_reset", "bimamba_state_data", "bimamba_state_free",
     "bimamba_block_step", "bimamba_seq_index", "bimamba_status_str",
     "bimamba_last_error", "bimamba_version", "bimamba_profile_begin",
-    "bimamba_profile_end",
+    "bimamba_profile_end", "bimamba_conv1d_workspace_size", "bimamba_conv1d",
 )
 
 
@@ -36,6 +36,20 @@ class Dir(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p),
                 ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
                 ("C", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+
+
+class ConvShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int), ("seqlen", ctypes.c_int),
+                ("nheads", ctypes.c_int), ("headdim", ctypes.c_int),
+                ("d_state", ctypes.c_int), ("ngroups", ctypes.c_int),
+                ("width", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("activation", ctypes.c_int), ("flags", ctypes.c_int)]
+
+
+class ConvDir(ctypes.Structure):
+    _fields_ = [("xbc", ctypes.c_void_p), ("weight", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("C", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -74,6 +88,11 @@ def load():
     lib.bimamba_profile_end.argtypes = [ctypes.c_char_p, ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    csp, cdp = ctypes.POINTER(ConvShape), ctypes.POINTER(ConvDir)
+    lib.bimamba_conv1d_workspace_size.argtypes = [csp, ctypes.c_int,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+    lib.bimamba_conv1d.argtypes = [csp, cdp, cdp, i32p, ctypes.c_int, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
     for name in EXPORTS:
         getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
     _LIB = lib

@@ -145,6 +145,49 @@ void release_records() {
     g_prof.clear();
 }
 
+int check_conv_shape(const bimamba_conv_shape *s) {
+    if (!s) return fail(BIMAMBA_EINVAL, "shape is NULL");
+    if (s->dtype != BIMAMBA_F32 && s->dtype != BIMAMBA_BF16)
+        return fail(BIMAMBA_EINVAL, "dtype %d is not BIMAMBA_F32 or BIMAMBA_BF16", s->dtype);
+    if (s->batch < 1) return fail(BIMAMBA_EINVAL, "batch %d < 1", s->batch);
+    if (s->seqlen < 0) return fail(BIMAMBA_EINVAL, "seqlen %d < 0", s->seqlen);
+    if (s->nheads < 1 || s->headdim < 1 || s->d_state < 1 || s->ngroups < 1)
+        return fail(BIMAMBA_EINVAL, "nheads/headdim/d_state/ngroups must be >= 1");
+    if (s->width < 2 || s->width > 4)
+        return fail(BIMAMBA_EUNSUPPORTED, "width %d not in [2, 4]", s->width);
+    if (s->activation != 0 && s->activation != 1)
+        return fail(BIMAMBA_EINVAL, "activation %d is neither 0 (none) nor 1 (SiLU)", s->activation);
+    if (s->flags != 0)
+        return fail(BIMAMBA_EINVAL, "flags 0x%x: no flag is defined", s->flags);
+    const long long ch = (long long)s->nheads * s->headdim + 2LL * s->ngroups * s->d_state;
+    if (ch > (1LL << 24))
+        return fail(BIMAMBA_EUNSUPPORTED, "%lld channels exceed 2^24", ch);
+    const long long tok = (long long)s->batch * s->seqlen;
+    if (tok > (1LL << 31) - 1)
+        return fail(BIMAMBA_EUNSUPPORTED, "batch*seqlen %lld exceeds 2^31-1", tok);
+    if ((long long)s->batch * 2 > 65535)
+        return fail(BIMAMBA_EUNSUPPORTED, "batch %d exceeds 32767", s->batch);
+    return BIMAMBA_OK;
+}
+
+int check_conv_dir(const bimamba_conv_dir *d, const char *name, bool empty) {
+    if (!d) return fail(BIMAMBA_EINVAL, "%s direction is NULL", name);
+    if (!d->weight) return fail(BIMAMBA_EINVAL, "%s: weight is required", name);
+    if ((uintptr_t)d->weight & 3u || (uintptr_t)d->bias & 3u)
+        return fail(BIMAMBA_EINVAL, "%s: weight and bias must be 4-byte aligned", name);
+    if (empty) return BIMAMBA_OK;
+    if (!d->xbc || !d->x || !d->B || !d->C)
+        return fail(BIMAMBA_EINVAL, "%s: xbc, x, B and C are required", name);
+    if (!aligned16(d->xbc) || !aligned16(d->x) || !aligned16(d->B) || !aligned16(d->C))
+        return fail(BIMAMBA_EINVAL, "%s: xbc, x, B and C must be 16-byte aligned", name);
+    return BIMAMBA_OK;
+}
+
+// packed rows: the per-token sequence index
+size_t conv_workspace(int nseq, int seqlen) {
+    return nseq > 0 ? align256(sizeof(int32_t) * (seqlen > 0 ? seqlen : 1)) : 0;
+}
+
 }  // namespace
 
 namespace bm {
@@ -399,6 +442,93 @@ int bimamba_seq_index(const int32_t *cu_seqlens, int nseq, int total, int32_t *s
     if (rc) return rc;
     hipError_t e = launch_seq_index(cu_seqlens, nseq, total, seq_idx, (hipStream_t)stream);
     return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "sequence index launch");
+}
+
+
+int bimamba_conv1d_workspace_size(const bimamba_conv_shape *s, int nseq, size_t *bytes) {
+    int rc = check_conv_shape(s);
+    if (rc) return rc;
+    if (!bytes) return fail(BIMAMBA_EINVAL, "bytes is NULL");
+    if (nseq < 0) return fail(BIMAMBA_EINVAL, "nseq %d < 0", nseq);
+    *bytes = conv_workspace(nseq, s->seqlen);
+    return BIMAMBA_OK;
+}
+
+int bimamba_conv1d(const bimamba_conv_shape *s, const bimamba_conv_dir *fwd,
+                   const bimamba_conv_dir *bwd, const int32_t *cu_seqlens, int nseq,
+                   const void *init_ctx, void *final_ctx,
+                   void *workspace, size_t workspace_bytes, bimamba_stream stream) {
+    int rc = check_conv_shape(s);
+    if (rc) return rc;
+    const bool empty = s->seqlen == 0;
+    if ((rc = check_conv_dir(fwd, "forward", empty))) return rc;
+    if (bwd && (rc = check_conv_dir(bwd, "reverse", empty))) return rc;
+    if (!aligned16(init_ctx) || !aligned16(final_ctx))
+        return fail(BIMAMBA_EINVAL, "init_ctx and final_ctx must be 16-byte aligned");
+    const int esz = s->dtype == BIMAMBA_BF16 ? 2 : 4;
+    const long long ch = (long long)s->nheads * s->headdim + 2LL * s->ngroups * s->d_state;
+    const size_t ctx_bytes = (size_t)s->batch * (s->width - 1) * ch * esz;
+    if (init_ctx && final_ctx && init_ctx != final_ctx) {
+        const char *a = (const char *)init_ctx, *b = (const char *)final_ctx;
+        if (a < b + ctx_bytes && b < a + ctx_bytes)
+            return fail(BIMAMBA_EINVAL, "init_ctx and final_ctx overlap without being equal");
+    }
+    if (cu_seqlens) {
+        if (s->batch != 1) return fail(BIMAMBA_EINVAL, "cu_seqlens requires batch == 1");
+        if ((rc = check_offsets(cu_seqlens, nseq, s->seqlen))) return rc;
+        if (init_ctx || final_ctx)
+            return fail(BIMAMBA_EUNSUPPORTED, "init_ctx/final_ctx are not available with cu_seqlens");
+    } else if (nseq != 0) {
+        return fail(BIMAMBA_EINVAL, "nseq %d given without cu_seqlens", nseq);
+    }
+    const size_t need = conv_workspace(cu_seqlens ? nseq : 0, s->seqlen);
+    if (need) {
+        if (!workspace) return fail(BIMAMBA_EWORKSPACE, "workspace of %zu bytes required", need);
+        if (workspace_bytes < need)
+            return fail(BIMAMBA_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+        if ((uintptr_t)workspace & 255u)
+            return fail(BIMAMBA_EINVAL, "workspace must be 256-byte aligned");
+    }
+    if (empty) {
+        // no token: the final context is the initial one (or zeros)
+        if (!final_ctx || final_ctx == init_ctx) return BIMAMBA_OK;
+        hipError_t e = launch_ctx_copy(init_ctx, final_ctx, ctx_bytes / 2, (hipStream_t)stream);
+        return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "copying the context of an empty row");
+    }
+    ConvArgs a;
+    memset(&a, 0, sizeof a);
+    const bimamba_conv_dir *dirs[2] = {fwd, bwd};
+    ConvDirPtrs *ptrs[2] = {&a.fwd, &a.bwd};
+    for (int i = 0; i < (bwd ? 2 : 1); ++i) {
+        ptrs[i]->xbc = dirs[i]->xbc;
+        ptrs[i]->weight = dirs[i]->weight;
+        ptrs[i]->bias = dirs[i]->bias;
+        ptrs[i]->x = dirs[i]->x;
+        ptrs[i]->B = dirs[i]->B;
+        ptrs[i]->C = dirs[i]->C;
+    }
+    a.batch = s->batch;
+    a.L = s->seqlen;
+    a.hp = s->nheads * s->headdim;
+    a.gn = s->ngroups * s->d_state;
+    a.ch = (int)ch;
+    a.W = s->width;
+    a.ndir = bwd ? 2 : 1;
+    a.act = s->activation;
+    a.init = init_ctx;
+    a.final = final_ctx;
+    a.inplace = init_ctx && init_ctx == final_ctx;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (cu_seqlens) {
+        int32_t *seq = (int32_t *)workspace;
+        if ((e = launch_seq_index(cu_seqlens, nseq, s->seqlen, seq, st)) != hipSuccess)
+            return hip_fail(e, "building sequence index");
+        a.seq = seq;
+    }
+    if ((e = launch_conv(a, s->dtype == BIMAMBA_BF16, st)) != hipSuccess)
+        return hip_fail(e, "launching conv1d");
+    return BIMAMBA_OK;
 }
 
 }  // extern "C"

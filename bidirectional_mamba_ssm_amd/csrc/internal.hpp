@@ -57,4 +57,26 @@ bool seq_supported(int P, int N);
 size_t seq_workspace(int batch, int L, int H, int P, int N, bool packed);
 hipError_t launch_scan_seq(const Problem &p, void *ws, hipStream_t s);
 
+// conv1d.hip: short depthwise convolution of the x | B | C channels
+struct ConvDirPtrs {
+    const void *xbc;           // [batch][L][ch]
+    const float *weight;       // [ch][W]
+    const float *bias;         // [ch] or nullptr
+    void *x, *B, *C;           // outputs [batch][L][hp], [batch][L][gn] x2
+};
+struct ConvArgs {
+    ConvDirPtrs fwd;           // forward stream (causal filter)
+    ConvDirPtrs bwd;           // reverse stream (anti-causal filter)
+    int batch, L, hp, gn, ch, W, ndir, act;
+    int nvec;                  // channel vectors per row (set by launch_conv)
+    const int32_t *seq;        // packed: per-token sequence index [L], or nullptr
+    const void *init;          // [batch][W-1][ch] forward context, or nullptr
+    void *final;               // [batch][W-1][ch] or nullptr
+    int inplace;               // final == init: one workgroup walks each row
+};
+bool conv_vectorized(bool bf16, int hp, int gn);
+hipError_t launch_conv(ConvArgs a, bool bf16, hipStream_t s);
+// dst[i] = src ? src[i] : 0 for n 16-bit words (context of an empty row)
+hipError_t launch_ctx_copy(const void *src, void *dst, size_t n, hipStream_t s);
+
 }  // namespace bm

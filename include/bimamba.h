@@ -154,6 +154,76 @@ int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
 int bimamba_seq_index(const int32_t *cu_seqlens, int nseq, int total,
                       int32_t *seq_idx, bimamba_stream stream);
 
+/* ---- Short convolution in front of the scan -------------------------------
+ *
+ * Each direction of the bidirectional block is a whole Mamba block with its
+ * own parameters, run on the flipped sequence for the reverse direction
+ * (DiffuMamba blog, "network architecture"); its configuration gives a
+ * convolution of width d_conv = 4 (same section). The pages do not spell the
+ * convolution out; it is taken as Mamba-2's: the channels that feed the scan,
+ * x (nheads*headdim) then B then C (ngroups*d_state each), each filtered by
+ * its own width-W causal filter with a bias, then SiLU v/(1+exp(-v)):
+ *
+ *   forward  u_t = bias + sum_{k<W} weight[k] * in_{t-(W-1)+k}
+ *   reverse  u_t = bias + sum_{k<W} weight[k] * in_{t+(W-1)-k}
+ *            (the same filter on the flipped sequence)
+ *
+ * Inputs outside a token's own row or packed sequence are zero, except that
+ * the forward filter of a row may start from init_ctx. For cached block
+ * diffusion ("Fixed state, long reach", Sec. 1) the forward context of the
+ * finalized prefix is carried next to the SSM state, and the reverse filter
+ * sees zeros after the active block. The output is rounded to the input
+ * dtype (round to nearest even for bf16) and split into the x, B and C arrays
+ * that bimamba_ssd_fwd / bimamba_block_step read. */
+typedef struct {
+    int batch;      /* rows; 1 when sequences are packed                    */
+    int seqlen;     /* tokens per row (packed: total tokens)                */
+    int nheads;     /* x channels: nheads * headdim                         */
+    int headdim;
+    int d_state;    /* B and C channels: ngroups * d_state each             */
+    int ngroups;
+    int width;      /* W, filter length, 2..4                               */
+    int dtype;      /* bimamba_dtype of the input and of the outputs         */
+    int activation; /* 0: none, 1: SiLU                                     */
+    int flags;      /* reserved, must be 0                                  */
+} bimamba_conv_shape;
+/* One direction. The reverse direction is given in forward time order. */
+typedef struct {
+    const void  *xbc;     /* [batch][seqlen][channels] dtype, read-only;
+                             channels = nheads*headdim + 2*ngroups*d_state,
+                             ordered x | B | C                                */
+    const float *weight;  /* [channels][width] float; tap width-1 multiplies
+                             the token itself                                  */
+    const float *bias;    /* [channels] float, or NULL for no bias            */
+    void *x;              /* out [batch][seqlen][nheads][headdim]   dtype     */
+    void *B;              /* out [batch][seqlen][ngroups][d_state]  dtype     */
+    void *C;              /* out [batch][seqlen][ngroups][d_state]  dtype     */
+} bimamba_conv_dir;
+/* Bytes of device workspace bimamba_conv1d needs (nonzero only when packed). */
+int bimamba_conv1d_workspace_size(const bimamba_conv_shape *s, int nseq, size_t *bytes);
+/* The convolution of both directions in one launch.
+ *
+ *  fwd, bwd     directions; bwd NULL filters the forward direction only.
+ *               Outputs must not overlap any input.
+ *  cu_seqlens   HOST int32[nseq+1] packed-sequence offsets (batch 1) or NULL,
+ *               as for bimamba_ssd_fwd; no filter crosses a sequence start.
+ *  init_ctx     dtype [batch][width-1][channels]: the forward inputs that
+ *               precede token 0 of each row, oldest first; NULL = zeros. Not
+ *               with cu_seqlens.
+ *  final_ctx    dtype [batch][width-1][channels] receiving each row's last
+ *               width-1 forward inputs (reaching into init_ctx when the row is
+ *               shorter), or NULL. Not with cu_seqlens. May equal init_ctx
+ *               (updated in place: then one workgroup walks each row in
+ *               order, which is meant for blocks, not long rows); any other
+ *               overlap is rejected.
+ *  workspace    bimamba_conv1d_workspace_size() bytes, 256-byte aligned.
+ *
+ * xbc, x, B, C and the contexts must be 16-byte aligned; weight and bias
+ * 4-byte aligned. */
+int bimamba_conv1d(const bimamba_conv_shape *s, const bimamba_conv_dir *fwd,
+                   const bimamba_conv_dir *bwd, const int32_t *cu_seqlens, int nseq,
+                   const void *init_ctx, void *final_ctx,
+                   void *workspace, size_t workspace_bytes, bimamba_stream stream);
 /* Per-kernel timing for benchmarks and profilers, per calling thread.
  * Between bimamba_profile_begin() and bimamba_profile_end(), every kernel the
  * library launches from this thread is bracketed by two hipEvents recorded on

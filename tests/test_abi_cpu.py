@@ -22,7 +22,7 @@ def lib():
 
 def header_symbols():
     text = open(os.path.join(ROOT, "include", "bimamba.h")).read()
-    return sorted(set(re.findall(r"\b(bimamba_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(bimamba_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -140,3 +140,75 @@ def test_seq_index_validation(lib):
     arr = (ctypes.c_int32 * 3)(0, 5, 4)
     assert lib.bimamba_seq_index(arr, 2, 4, FAKE, None) == _abi.EINVAL
     assert lib.bimamba_seq_index(None, 2, 4, FAKE, None) == _abi.EINVAL
+
+
+def conv_shape(**kw):
+    d = dict(batch=1, seqlen=64, nheads=4, headdim=16, d_state=16, ngroups=1,
+             width=4, dtype=_abi.BF16, activation=1, flags=0)
+    d.update(kw)
+    return _abi.ConvShape(**d)
+
+
+def fake_conv_dir(**kw):
+    d = dict(xbc=FAKE, weight=FAKE, bias=FAKE, x=FAKE, B=FAKE, C=FAKE)
+    d.update(kw)
+    return _abi.ConvDir(**d)
+
+
+def call_conv(lib, s, f, b=None, cu=None, nseq=0, init=None, final=None, ws=None, wsb=0):
+    arr = (ctypes.c_int32 * len(cu))(*cu) if cu is not None else None
+    return lib.bimamba_conv1d(ctypes.byref(s) if s is not None else None,
+                              ctypes.byref(f) if f is not None else None,
+                              ctypes.byref(b) if b is not None else None,
+                              arr, nseq, init, final, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), _abi.EINVAL),
+    (dict(batch=0), _abi.EINVAL),
+    (dict(seqlen=-2), _abi.EINVAL),
+    (dict(headdim=0), _abi.EINVAL),
+    (dict(width=1), _abi.EUNSUPPORTED),
+    (dict(width=5), _abi.EUNSUPPORTED),
+    (dict(activation=2), _abi.EINVAL),
+    (dict(flags=1), _abi.EINVAL),
+    (dict(batch=40000), _abi.EUNSUPPORTED),
+    (dict(batch=1 << 16, seqlen=1 << 16), _abi.EUNSUPPORTED),
+])
+def test_conv_shape_rejected(lib, kw, code):
+    assert call_conv(lib, conv_shape(**kw), fake_conv_dir()) == code
+    n = ctypes.c_size_t(7)
+    assert lib.bimamba_conv1d_workspace_size(ctypes.byref(conv_shape(**kw)), 0, ctypes.byref(n)) == code
+
+
+def test_conv_arguments_rejected(lib):
+    s = conv_shape()
+    assert call_conv(lib, None, fake_conv_dir()) == _abi.EINVAL
+    assert call_conv(lib, s, None) == _abi.EINVAL
+    for field in ("xbc", "weight", "x", "B", "C"):
+        assert call_conv(lib, s, fake_conv_dir(**{field: None})) == _abi.EINVAL, field
+        assert call_conv(lib, s, fake_conv_dir(), fake_conv_dir(**{field: None})) == _abi.EINVAL, field
+    for field in ("xbc", "x", "B", "C"):
+        assert call_conv(lib, s, fake_conv_dir(**{field: FAKE + 8})) == _abi.EINVAL, field
+    assert call_conv(lib, s, fake_conv_dir(weight=FAKE + 2)) == _abi.EINVAL
+    assert call_conv(lib, s, fake_conv_dir(bias=FAKE + 1)) == _abi.EINVAL
+    assert call_conv(lib, s, fake_conv_dir(), init=FAKE + 4) == _abi.EINVAL
+    # contexts that overlap without being the same array
+    assert call_conv(lib, s, fake_conv_dir(), init=FAKE, final=FAKE + 16) == _abi.EINVAL
+    # packed sequences: bad offsets, batch > 1, contexts, workspace
+    assert call_conv(lib, s, fake_conv_dir(), cu=[0, 70], nseq=1) == _abi.EINVAL
+    assert call_conv(lib, s, fake_conv_dir(), cu=[0, 40, 30, 64], nseq=3) == _abi.EINVAL
+    assert call_conv(lib, conv_shape(batch=2), fake_conv_dir(), cu=[0, 64], nseq=1) == _abi.EINVAL
+    assert call_conv(lib, s, fake_conv_dir(), cu=[0, 64], nseq=1, init=FAKE) == _abi.EUNSUPPORTED
+    assert call_conv(lib, s, fake_conv_dir(), nseq=2) == _abi.EINVAL
+    assert call_conv(lib, s, fake_conv_dir(), cu=[0, 32, 64], nseq=2) == _abi.EWORKSPACE
+    n = ctypes.c_size_t(0)
+    assert lib.bimamba_conv1d_workspace_size(ctypes.byref(s), 2, ctypes.byref(n)) == _abi.OK
+    assert n.value >= 12 and n.value % 256 == 0
+    assert call_conv(lib, s, fake_conv_dir(), cu=[0, 32, 64], nseq=2, ws=FAKE,
+                     wsb=n.value - 1) == _abi.EWORKSPACE
+    assert call_conv(lib, s, fake_conv_dir(), cu=[0, 32, 64], nseq=2, ws=FAKE + 16,
+                     wsb=n.value) == _abi.EINVAL
+    assert lib.bimamba_conv1d_workspace_size(ctypes.byref(s), 0, ctypes.byref(n)) == _abi.OK
+    assert n.value == 0
+    assert lib.bimamba_conv1d_workspace_size(ctypes.byref(s), -1, ctypes.byref(n)) == _abi.EINVAL
