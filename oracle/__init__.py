@@ -9,6 +9,8 @@ Two independent formulations live here:
 * ``bissd`` / ``block_step`` -- the sequential fp64 recurrence in
   ``ssd_oracle.c`` (one token at a time, see that file's header for the
   equations and the passages they follow);
+* ``bissd_bwd`` -- its gradients (the training backward), by the adjoint
+  recurrence in the same file;
 * ``oracle.brute`` -- the quadratic "masked C.B^T" form of the same operator
   in numpy, used to pin the recurrence on tiny inputs.
 
@@ -36,6 +38,10 @@ def bind(path):
     lib.oracle_bissd_f64.argtypes = (
         [ctypes.c_int] * 6 + [dp] * 12 + [ip, ctypes.c_int, dp, dp, dp])
     lib.oracle_bissd_f64.restype = ctypes.c_int
+    pp = ctypes.c_void_p * 6
+    lib.oracle_bissd_bwd_f64.argtypes = (
+        [ctypes.c_int] * 6 + [dp] * 12 + [ip, ctypes.c_int, dp, pp, pp])
+    lib.oracle_bissd_bwd_f64.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     return lib
@@ -125,3 +131,50 @@ def block_step(state, fwd, bwd, commit=False, lib=None):
     y, fs = bissd(fwd, bwd, init_state=state, want_final_state=True, lib=lib)
     new_state = fs if commit else _f64(state).copy()
     return y, new_state
+
+
+GRAD_KEYS = ("x", "dt", "A", "B", "C", "D")
+
+
+def bissd_bwd(fwd, bwd, dy, cu_seqlens=None, lib=None):
+    """Gradients of ``bissd(fwd, bwd)`` with respect to every input, given
+    the output gradient dy [b, L, H, P]. Returns (gfwd, gbwd): dicts with
+    keys x, dt, A, B, C, D (float64, shaped like the inputs; D's gradient
+    is returned even when D is None). gbwd is None when bwd is None."""
+    f = {k: _f64(v) for k, v in fwd.items()}
+    b = {k: _f64(v) for k, v in bwd.items()} if bwd is not None else None
+    g = _f64(dy)
+    batch, L, H, P = f["x"].shape
+    G, N = f["B"].shape[2], f["B"].shape[3]
+    cu, nseq = None, batch
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        nseq = len(cu) - 1
+
+    def grads():
+        return {"x": np.empty((batch, L, H, P)), "dt": np.empty((batch, L, H)),
+                "A": np.empty(H), "B": np.empty((batch, L, G, N)),
+                "C": np.empty((batch, L, G, N)), "D": np.empty(H)}
+
+    gf = grads()
+    gb = grads() if b is not None else None
+
+    def ptrs(gd):
+        arr = (ctypes.c_void_p * 6)()
+        if gd is not None:
+            for i, k in enumerate(GRAD_KEYS):
+                arr[i] = gd[k].ctypes.data
+        return arr
+
+    none = None
+    rc = (lib or _lib()).oracle_bissd_bwd_f64(
+        batch, L, H, P, N, G,
+        _ptr(f["x"]), _ptr(f["dt"]), _ptr(f["A"]), _ptr(f["B"]), _ptr(f["C"]),
+        _ptr(f.get("D")),
+        _ptr(b["x"]) if b else none, _ptr(b["dt"]) if b else none,
+        _ptr(b["A"]) if b else none, _ptr(b["B"]) if b else none,
+        _ptr(b["C"]) if b else none, _ptr(b.get("D")) if b else none,
+        _ptr(cu, ctypes.c_int32), nseq, _ptr(g), ptrs(gf), ptrs(gb))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return gf, gb

@@ -132,3 +132,55 @@ def test_conv_pins_catch_mutant(name):
             if not (err <= tol):
                 caught.append(pin)
     assert caught, f"no pin catches mutant {name}"
+
+
+BWD_MUTANTS = {
+    # the gradient of h_t propagated before the token's own output term
+    "bwd_order": ("                gp[n] += Ct[n] * dyt[p];\n",
+                  "                gp[n] = decay * gp[n] + Ct[n] * dyt[p];\n"),
+    # decay term of ddt dropped
+    "bwd_ddt_decay": ("ddt[(size_t)t * H + h] = r + A[h] * decay * q;",
+                      "ddt[(size_t)t * H + h] = r;"),
+    # <g_t, h_t> used where <g_t, h_{t-1}> belongs
+    "bwd_q_current": ("                    q += gp[n] * prev[(size_t)p * N + n];",
+                      "                    q += gp[n] * cur[(size_t)p * N + n];"),
+    # dt missing from dB
+    "bwd_dB_dt": ("dBt[n] += dtt * gp[n] * xt[p];", "dBt[n] += gp[n] * xt[p];"),
+    # skip term missing from dx
+    "bwd_dx_D": ("dx[((size_t)t * H + h) * P + p] = Dh * dyt[p] + dtt * gb;",
+                 "dx[((size_t)t * H + h) * P + p] = dtt * gb;"),
+    # dt missing from dA
+    "bwd_dA_dt": ("*dA += dtt * decay * q;", "*dA += decay * q;"),
+    # dC from h_{t-1}
+    "bwd_dC_prev": ("dCt[n] += cur[(size_t)p * N + n] * dyt[p];",
+                    "dCt[n] += (prev ? prev[(size_t)p * N + n] : 0.0) * dyt[p];"),
+    # the reverse stream's gradient walked in the forward order
+    "bwd_no_reverse": ("        const int t = reverse ? (t1 - 1 - step) : (t0 + step);\n        const double dtt = dt[(size_t)t * H + h];\n        const double decay = exp(dtt * A[h]);\n        const double *Bt = B + ((size_t)t * G + g) * N;\n        const double *xt = x + ((size_t)t * H + h) * P;\n        const double *prev",
+                       "        const int t = t0 + step;\n        const double dtt = dt[(size_t)t * H + h];\n        const double decay = exp(dtt * A[h]);\n        const double *Bt = B + ((size_t)t * G + g) * N;\n        const double *xt = x + ((size_t)t * H + h) * P;\n        const double *prev"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_pins_catch_mutant(name, tmp_path):
+    from bwd_pins import BWD_PINS
+    a, b = BWD_MUTANTS[name]
+    assert SRC.count(a) == 1, f"mutation site for {name} not found once"
+    src = tmp_path / "mutant.c"
+    src.write_text(SRC.replace(a, b))
+    lib_path = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                    str(src), "-o", lib_path, "-lm"], check=True)
+    lib = oracle.bind(lib_path)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin, (fn, tol) in BWD_PINS.items():
+            if pin == "bwd_finite_differences":
+                continue  # slow; the others must catch every mutant on their own
+            try:
+                err = fn(lib)
+            except Exception:
+                caught.append(pin)
+                continue
+            if not (err <= tol):
+                caught.append(pin)
+    assert caught, f"no pin catches mutant {name}"

@@ -1,6 +1,7 @@
 """The oracle against what the pages and the mathematics fix (CPU only)."""
 import pytest
 
+from bwd_pins import BWD_PINS
 from conv_pins import CONV_PINS
 from oracle import conv
 from pins import ALL_PINS
@@ -17,4 +18,11 @@ def test_oracle_pin(name):
 def test_conv_oracle_pin(name):
     fn, tol = CONV_PINS[name]
     err = fn(conv)
+    assert err <= tol, f"pin {name}: error {err} > {tol}"
+
+
+@pytest.mark.parametrize("name", sorted(BWD_PINS))
+def test_bwd_oracle_pin(name):
+    fn, tol = BWD_PINS[name]
+    err = fn(None)
     assert err <= tol, f"pin {name}: error {err} > {tol}"
