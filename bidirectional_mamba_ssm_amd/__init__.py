@@ -131,6 +131,57 @@ def ssd_fwd(fwd, bwd=None, chunk=256, cu_seqlens=None, init_state=None,
     return y
 
 
+def bwd_workspace_size(shape, has_bwd=True):
+    n = ctypes.c_size_t(0)
+    _abi.check(lib().bimamba_ssd_bwd_workspace_size(ctypes.byref(shape), int(bool(has_bwd)),
+                                                     ctypes.byref(n)))
+    return n.value
+
+
+def _grads(g, dims, dev, name):
+    batch, L, H, P, G, N = dims
+    shapes = {"x": (batch, L, H, P), "dt": (batch, L, H), "A": (H,),
+              "B": (batch, L, G, N), "C": (batch, L, G, N), "D": (H,)}
+    if g is None:
+        g = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
+    for k, v in shapes.items():
+        if k == "D" and g.get("D") is None:
+            continue
+        _check(g[k], f"{name}_grad.{k}", v, torch.float32, dev)
+    return g, _abi.Grad(g["x"].data_ptr(), g["dt"].data_ptr(), g["A"].data_ptr(),
+                        g["B"].data_ptr(), g["C"].data_ptr(),
+                        g["D"].data_ptr() if g.get("D") is not None else None)
+
+
+def ssd_bwd(fwd, bwd, dy, grads=None, workspace=None, stream=None):
+    """Training backward of ssd_fwd (bimamba_ssd_bwd): gradients of every
+    input of both streams given dy (float32 [b,L,H,P]). Returns (gfwd, gbwd),
+    dicts of float32 tensors keyed x, dt, A, B, C, D (gbwd None without bwd).
+    grads: optional (gfwd, gbwd) dicts to write into."""
+    x = fwd["x"]
+    dims = _dims(fwd)
+    batch, L, H, P, G, N = dims
+    shape = make_shape(x, fwd["B"], 64)
+    dev = _cuda_device(x)
+    fd = _dir(fwd, x.dtype, dims, dev, "fwd")
+    bd = _dir(bwd, x.dtype, dims, dev, "bwd") if bwd is not None else None
+    _check(dy, "dy", (batch, L, H, P), torch.float32, dev)
+    gl = list(grads) if grads is not None else [None, None]
+    gf, gfs = _grads(gl[0], dims, dev, "fwd")
+    gb, gbs = _grads(gl[1], dims, dev, "bwd") if bwd is not None else (None, None)
+    need = bwd_workspace_size(shape, bwd is not None)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _abi.check(lib().bimamba_ssd_bwd(
+        ctypes.byref(shape), ctypes.byref(fd), ctypes.byref(bd) if bd is not None else None,
+        _ptr(dy), ctypes.byref(gfs), ctypes.byref(gbs) if gbs is not None else None,
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return gf, gb
+
+
 class State:
     """Library-owned forward-state cache: float [nslots, H, P, N] on the GPU."""
 

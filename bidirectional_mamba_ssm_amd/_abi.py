@@ -21,6 +21,7 @@ EXPORTS = (
     "bimamba_block_step", "bimamba_seq_index", "bimamba_status_str",
     "bimamba_last_error", "bimamba_version", "bimamba_profile_begin",
     "bimamba_profile_end", "bimamba_conv1d_workspace_size", "bimamba_conv1d",
+    "bimamba_ssd_bwd_workspace_size", "bimamba_ssd_bwd",
 )
 
 
@@ -36,6 +37,12 @@ class Dir(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p),
                 ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
                 ("C", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+
+
+class Grad(ctypes.Structure):
+    _fields_ = [("dx", ctypes.c_void_p), ("ddt", ctypes.c_void_p),
+                ("dA", ctypes.c_void_p), ("dB", ctypes.c_void_p),
+                ("dC", ctypes.c_void_p), ("dD", ctypes.c_void_p)]
 
 
 class ConvShape(ctypes.Structure):
@@ -88,6 +95,9 @@ def load():
     lib.bimamba_profile_end.argtypes = [ctypes.c_char_p, ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    gp = ctypes.POINTER(Grad)
+    lib.bimamba_ssd_bwd_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.bimamba_ssd_bwd.argtypes = [sp, dp, dp, vp, gp, gp, vp, ctypes.c_size_t, vp]
     csp, cdp = ctypes.POINTER(ConvShape), ctypes.POINTER(ConvDir)
     lib.bimamba_conv1d_workspace_size.argtypes = [csp, ctypes.c_int,
                                                   ctypes.POINTER(ctypes.c_size_t)]

@@ -184,6 +184,19 @@ int check_conv_dir(const bimamba_conv_dir *d, const char *name, bool empty) {
 }
 
 // packed rows: the per-token sequence index
+int check_grad(const bimamba_grad *g, const char *name, bool empty) {
+    if (!g) return fail(BIMAMBA_EINVAL, "%s gradients are NULL", name);
+    if (!g->dA) return fail(BIMAMBA_EINVAL, "%s: dA is required", name);
+    if (!aligned16(g->dA) || !aligned16(g->dD))
+        return fail(BIMAMBA_EINVAL, "%s: dA and dD must be 16-byte aligned", name);
+    if (empty) return BIMAMBA_OK;
+    if (!g->dx || !g->ddt || !g->dB || !g->dC)
+        return fail(BIMAMBA_EINVAL, "%s: dx, ddt, dB and dC are required", name);
+    if (!aligned16(g->dx) || !aligned16(g->ddt) || !aligned16(g->dB) || !aligned16(g->dC))
+        return fail(BIMAMBA_EINVAL, "%s: gradient arrays must be 16-byte aligned", name);
+    return BIMAMBA_OK;
+}
+
 size_t conv_workspace(int nseq, int seqlen) {
     return nseq > 0 ? align256(sizeof(int32_t) * (seqlen > 0 ? seqlen : 1)) : 0;
 }
@@ -444,6 +457,71 @@ int bimamba_seq_index(const int32_t *cu_seqlens, int nseq, int total, int32_t *s
     return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "sequence index launch");
 }
 
+
+int bimamba_ssd_bwd_workspace_size(const bimamba_shape *s, int has_bwd, size_t *bytes) {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    if (!bytes) return fail(BIMAMBA_EINVAL, "bytes is NULL");
+    if (!bwd_supported(s->headdim, s->d_state))
+        return fail(BIMAMBA_EUNSUPPORTED, "backward: headdim %d / d_state %d not in {16, 64} x {16, 128}",
+                    s->headdim, s->d_state);
+    *bytes = bwd_workspace(s->batch, s->seqlen, s->nheads, s->headdim, s->d_state, has_bwd ? 2 : 1);
+    return BIMAMBA_OK;
+}
+
+int bimamba_ssd_bwd(const bimamba_shape *s, const bimamba_dir *fwd, const bimamba_dir *bwd,
+                    const float *dy, const bimamba_grad *gfwd, const bimamba_grad *gbwd,
+                    void *workspace, size_t workspace_bytes, bimamba_stream stream) {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    if (!bwd_supported(s->headdim, s->d_state))
+        return fail(BIMAMBA_EUNSUPPORTED, "backward: headdim %d / d_state %d not in {16, 64} x {16, 128}",
+                    s->headdim, s->d_state);
+    const bool empty = s->seqlen == 0;
+    if ((rc = check_dir(fwd, "forward", empty))) return rc;
+    if (bwd && (rc = check_dir(bwd, "reverse", empty))) return rc;
+    if (!dy && !empty) return fail(BIMAMBA_EINVAL, "dy is NULL");
+    if (!aligned16(dy)) return fail(BIMAMBA_EINVAL, "dy must be 16-byte aligned");
+    if ((rc = check_grad(gfwd, "forward", empty))) return rc;
+    if (bwd && (rc = check_grad(gbwd, "reverse", empty))) return rc;
+    const size_t need = bwd_workspace(s->batch, s->seqlen, s->nheads, s->headdim, s->d_state, bwd ? 2 : 1);
+    if (need) {
+        if (!workspace) return fail(BIMAMBA_EWORKSPACE, "workspace of %zu bytes required", need);
+        if (workspace_bytes < need)
+            return fail(BIMAMBA_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+        if ((uintptr_t)workspace & 255u)
+            return fail(BIMAMBA_EINVAL, "workspace must be 256-byte aligned");
+    }
+    BwdProblem p;
+    memset(&p, 0, sizeof p);
+    p.batch = s->batch;
+    p.L = s->seqlen;
+    p.H = s->nheads;
+    p.P = s->headdim;
+    p.N = s->d_state;
+    p.G = s->ngroups;
+    p.bf16 = s->dtype == BIMAMBA_BF16;
+    p.has_bwd = bwd != nullptr;
+    const bimamba_dir *dirs[2] = {fwd, bwd};
+    const bimamba_grad *grads[2] = {gfwd, gbwd};
+    for (int i = 0; i < (bwd ? 2 : 1); ++i) {
+        p.dir[i].x = dirs[i]->x;
+        p.dir[i].dt = dirs[i]->dt;
+        p.dir[i].A = dirs[i]->A;
+        p.dir[i].B = dirs[i]->B;
+        p.dir[i].C = dirs[i]->C;
+        p.dir[i].D = dirs[i]->D;
+        p.grad[i].dx = grads[i]->dx;
+        p.grad[i].ddt = grads[i]->ddt;
+        p.grad[i].dA = grads[i]->dA;
+        p.grad[i].dB = grads[i]->dB;
+        p.grad[i].dC = grads[i]->dC;
+        p.grad[i].dD = grads[i]->dD;
+    }
+    p.dy = dy;
+    hipError_t e = launch_bwd(p, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "launching the backward");
+}
 
 int bimamba_conv1d_workspace_size(const bimamba_conv_shape *s, int nseq, size_t *bytes) {
     int rc = check_conv_shape(s);

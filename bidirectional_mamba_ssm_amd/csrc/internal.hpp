@@ -57,6 +57,21 @@ bool seq_supported(int P, int N);
 size_t seq_workspace(int batch, int L, int H, int P, int N, bool packed);
 hipError_t launch_scan_seq(const Problem &p, void *ws, hipStream_t s);
 
+// ssd_bwd.hip: training backward of the bidirectional SSD
+struct GradPtrs {
+    float *dx, *ddt, *dA, *dB, *dC, *dD;   // dD may be nullptr
+};
+struct BwdProblem {
+    int batch, L, H, P, N, G;
+    bool bf16, has_bwd;
+    DirPtrs dir[2];
+    GradPtrs grad[2];
+    const float *dy;
+};
+bool bwd_supported(int P, int N);
+size_t bwd_workspace(int batch, int L, int H, int P, int N, int ndir);
+hipError_t launch_bwd(const BwdProblem &p, void *ws, hipStream_t s);
+
 // conv1d.hip: short depthwise convolution of the x | B | C channels
 struct ConvDirPtrs {
     const void *xbc;           // [batch][L][ch]

@@ -154,6 +154,39 @@ int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
 int bimamba_seq_index(const int32_t *cu_seqlens, int nseq, int total,
                       int32_t *seq_idx, bimamba_stream stream);
 
+/* ---- Training backward ------------------------------------------------------
+ *
+ * Gradients of bimamba_ssd_fwd's y (whole sequences, zero initial state, no
+ * packing) with respect to every input of both streams, given dy. The
+ * output being the sum of the two streams (gist.science/ja DiffuMamba
+ * summary, Sec. 2), both receive the same dy; each stream has its own
+ * parameters (DiffuMamba blog, "network architecture"), so each gets its
+ * own gradients. The models train at 1024 tokens ("Fixed state, long
+ * reach", Sec. 1, contributions) with a masked-diffusion objective
+ * (DiffuMamba blog, "DiffuMamba architecture", design principles).
+ * Computed in fp32 from the exact inputs (bf16 or fp32), by the chain rule
+ * through the block form of the recurrence in blocks of 64 positions (the
+ * shape's chunk is not used here); deterministic. */
+typedef struct {
+    float *dx;    /* [batch][seqlen][nheads][headdim]                          */
+    float *ddt;   /* [batch][seqlen][nheads]                                   */
+    float *dA;    /* [nheads]                                                  */
+    float *dB;    /* [batch][seqlen][ngroups][d_state] (summed over the heads
+                     of each group)                                            */
+    float *dC;    /* [batch][seqlen][ngroups][d_state]                         */
+    float *dD;    /* [nheads], or NULL if not wanted                           */
+} bimamba_grad;
+/* Bytes of device workspace bimamba_ssd_bwd needs (has_bwd: both streams). */
+int bimamba_ssd_bwd_workspace_size(const bimamba_shape *s, int has_bwd, size_t *bytes);
+/* dy: float [batch][seqlen][nheads][headdim]. gfwd (required) and gbwd
+ * (required when bwd is given) receive the gradients; every array is fully
+ * overwritten and must not overlap an input. Supported: headdim in {16, 64},
+ * d_state in {16, 128}. Pointers 16-byte aligned, workspace 256-byte
+ * aligned. */
+int bimamba_ssd_bwd(const bimamba_shape *s, const bimamba_dir *fwd,
+                    const bimamba_dir *bwd, const float *dy,
+                    const bimamba_grad *gfwd, const bimamba_grad *gbwd,
+                    void *workspace, size_t workspace_bytes, bimamba_stream stream);
 /* ---- Short convolution in front of the scan -------------------------------
  *
  * Each direction of the bidirectional block is a whole Mamba block with its

@@ -1,0 +1,121 @@
+"""GPU parity of the training backward (bimamba_ssd_bwd, through the C ABI)
+against the oracle's adjoint recurrence (fp64), element by element, every
+gradient of both streams."""
+import numpy as np
+import pytest
+import torch
+
+import bidirectional_mamba_ssm_amd as bm
+import oracle
+import synth
+from metrics import rel_err_f32, rms_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+KEYS = ("x", "dt", "A", "B", "C", "D")
+# fp32 arithmetic from exact inputs. A gradient element is a sum of many
+# products of both signs (over the block, the state and, for dB and dC, the
+# heads of a group), so its rounding error scales with the size of those
+# products -- about the RMS of the whole array -- not with its own value:
+# the bar is max|g - g_ref| <= 1e-4 * RMS(g_ref) per array (measured: a few
+# 1e-6). The elementwise relative error with the 1 %-of-RMS floor is
+# printed beside it.
+TOL = 1e-4
+
+
+def _dy(batch, L, H, P, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return torch.randn(batch, L, H, P, generator=g, device=DEV)
+
+
+def _compare(gpu, ref, tag):
+    worst, elem = {}, {}
+    for k in KEYS:
+        if gpu.get(k) is None:
+            continue
+        got = gpu[k].double().cpu().numpy()
+        elem[k] = rel_err_f32(got, ref[k])
+        worst[k] = rms_err(got, ref[k]) if np.any(ref[k]) else float(np.max(np.abs(got), initial=0.0))
+    print(f"  {tag}: max|err|/RMS " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()) +
+          " | elementwise " + ", ".join(f"{k} {v:.1e}" for k, v in elem.items()), flush=True)
+    bad = {k: v for k, v in worst.items() if not v <= TOL}
+    assert not bad, f"{tag}: {bad}"
+
+
+CASES = [
+    # name, batch, L, H, P, N, G, dtype, seed
+    ("f32_tiny_ragged", 1, 130, 4, 16, 16, 1, "f32", 70),
+    ("f32_groups_one_block", 2, 64, 4, 16, 128, 2, "f32", 71),
+    ("f32_p64_n16", 1, 200, 2, 64, 16, 1, "f32", 72),
+    ("bf16_layer_slice", 2, 300, 4, 64, 128, 1, "bf16", 73),
+    ("bf16_short", 3, 5, 2, 64, 128, 1, "bf16", 74),
+    ("bf16_L1", 2, 1, 2, 16, 16, 1, "bf16", 75),
+    ("bf16_groups", 1, 257, 8, 64, 128, 4, "bf16", 76),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("bidir", [True, False], ids=["bi", "fwd"])
+def test_bwd_parity(case, bidir):
+    name, batch, L, H, P, N, G, dtype, seed = case
+    print(f"case {name} bidir={bidir}", flush=True)
+    f, b = synth.make_inputs(batch, L, H, P, N, G, dtype, seed, device=DEV)
+    if not bidir:
+        b = None
+    dy = _dy(batch, L, H, P, seed + 1000)
+    gf, gb = bm.ssd_bwd(f, b, dy)
+    torch.cuda.synchronize()
+    rf, rb = oracle.bissd_bwd(f, b, dy)
+    _compare(gf, rf, "forward stream")
+    if bidir:
+        _compare(gb, rb, "reverse stream")
+    else:
+        assert gb is None
+
+
+def test_bwd_without_D():
+    f, b = synth.make_inputs(1, 100, 2, 16, 16, 1, "f32", 77, device=DEV)
+    f["D"] = None
+    b["D"] = None
+    dy = _dy(1, 100, 2, 16, 78)
+    gf, gb = bm.ssd_bwd(f, b, dy)
+    torch.cuda.synchronize()
+    rf, rb = oracle.bissd_bwd(f, b, dy)
+    _compare(gf, rf, "forward stream")
+    _compare(gb, rb, "reverse stream")
+
+
+def test_bwd_empty():
+    f, b = synth.make_inputs(2, 0, 2, 16, 16, 1, "bf16", 79, device=DEV)
+    dy = torch.empty(2, 0, 2, 16, device=DEV)
+    gf, gb = bm.ssd_bwd(f, b, dy)
+    torch.cuda.synchronize()
+    for g in (gf, gb):
+        assert torch.count_nonzero(g["A"]) == 0 and torch.count_nonzero(g["D"]) == 0
+
+
+def test_bwd_deterministic():
+    f, b = synth.make_inputs(2, 200, 4, 64, 128, 1, "bf16", 80, device=DEV)
+    dy = _dy(2, 200, 4, 64, 81)
+    g1 = bm.ssd_bwd(f, b, dy)
+    g2 = bm.ssd_bwd(f, b, dy)
+    torch.cuda.synchronize()
+    for a, c in zip(g1, g2):
+        for k in KEYS:
+            assert torch.equal(a[k], c[k]), k
+
+
+def test_bwd_layer_full_size():
+    """The training layer (8 x 1024 tokens, 64 heads x 64, d_state 128, bf16,
+    both streams) in the launch the benchmark times, every gradient element
+    against the oracle."""
+    w = synth.WORKLOADS["layer_1p3b_train"]
+    f, b = synth.make_workload(w, device=DEV)
+    dy = _dy(w.batch, w.seqlen, w.nheads, w.headdim, 82)
+    print("layer backward", flush=True)
+    gf, gb = bm.ssd_bwd(f, b, dy)
+    torch.cuda.synchronize()
+    rf, rb = oracle.bissd_bwd(f, b, dy)
+    _compare(gf, rf, "forward stream")
+    _compare(gb, rb, "reverse stream")
