@@ -95,6 +95,8 @@ def parse():
                     help="prefix length of the block-step state")
     ap.add_argument("--block-step-only", action="store_true",
                     help="only the block-decode step lines (one JSON object)")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="only the training-backward line (one JSON object)")
     ap.add_argument("--conv-only", action="store_true",
                     help="only the short-convolution line (one JSON object)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -245,6 +247,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.bwd_only:
+        print(json.dumps({"bwd_layer_1p3b_train": bwd_bench(args, bm, synth, torch, dev, args.steps)}),
+              flush=True)
+        return
     if args.conv_only:
         if args.calibrate_copy:
             calibrate_copy(torch, dev)
@@ -394,6 +400,7 @@ def extras(args, bm, synth, torch, dev):
 
     res["block_step"] = block_step_bench(args, bm, synth, torch, dev, steps)
     res["conv1d_layer_1p3b_train"] = conv_bench(args, bm, synth, torch, dev, max(steps, 20))
+    res["bwd_layer_1p3b_train"] = bwd_bench(args, bm, synth, torch, dev, max(3, steps // 4))
     return res
 
 
@@ -438,6 +445,38 @@ def block_step_bench(args, bm, synth, torch, dev, steps):
         del f, b, y
         torch.cuda.empty_cache()
     return out
+
+
+def bwd_bytes_per_token(H, P, N, G, e):
+    """Algorithmic bytes of the training backward per token, both streams:
+    read x, dt, B, C of each stream and dy once; write dx, ddt, dB, dC of
+    each stream once (fp32)."""
+    return 2 * (H * P * e + H * e + 2 * G * N * e) + H * P * 4 + 2 * (H * P + H + 2 * G * N) * 4
+
+
+def bwd_bench(args, bm, synth, torch, dev, steps):
+    """The training backward at the training layer's shape (8 x 1024 tokens,
+    64 heads x 64, d_state 128, bf16, both streams)."""
+    w = synth.WORKLOADS["layer_1p3b_train"]
+    f, b = synth.make_workload(w, device=dev)
+    g = torch.Generator(device=dev).manual_seed(82)
+    dy = torch.randn(w.batch, w.seqlen, w.nheads, w.headdim, generator=g, device=dev)
+    shape = bm.make_shape(f["x"], f["B"], 64)
+    ws = torch.empty(bm.bwd_workspace_size(shape, True), dtype=torch.uint8, device=dev)
+    grads = bm.ssd_bwd(f, b, dy, workspace=ws)
+    fn = lambda: bm.ssd_bwd(f, b, dy, grads=grads, workspace=ws)  # noqa: E731
+    ms, _, ker, dom = time_steps(bm, fn, steps, max(3, args.warmup // 10), torch)
+    tok = w.batch * w.seqlen
+    bpt = bwd_bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
+    res = {"workload": f"training backward, {w.name} (8 x 1024 tokens, 64 x 64 heads, d_state 128, bf16 in, fp32 gradients, both streams)",
+           "tokens_per_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+           "algorithmic_bytes_per_token": bpt,
+           "hbm_roofline_frac_step": round(bpt * tok / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "kernels_ms_per_step": {k: round(t / steps, 4) for k, (c, t) in ker.items()},
+           "dominant_kernel": dom}
+    del f, b, dy, ws, grads
+    torch.cuda.empty_cache()
+    return res
 
 
 def conv_bench(args, bm, synth, torch, dev, steps):

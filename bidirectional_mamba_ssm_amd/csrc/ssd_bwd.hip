@@ -39,6 +39,7 @@
 //                blocks, in a fixed order (deterministic results).
 #include "common.hpp"
 #include "internal.hpp"
+#include "mfma.hpp"
 
 namespace bm {
 namespace {
@@ -63,28 +64,70 @@ struct BwdArgs {
 
 __device__ __forceinline__ int tok_of(int k, int L, bool rev) { return rev ? L - 1 - k : k; }
 
-// fp64 running sums of a = dt*A over the block's scan positions (one thread)
+// dt of the block's positions into dtv (zero past len) and the running sums
+// of a = dt*A into sv (fp64): one lane per position in wave 0 (a block is
+// one wave wide), a shuffle scan. Ends with a workgroup barrier.
 template <typename T>
 __device__ void block_scan(const BwdArgs &a, const DirPtrs &d, size_t rowt, int h, int k0,
                            int len, bool rev, double *sv, float *dtv) {
-    double s = 0.0;
-    const double A = (double)d.A[h];
-    const T *DT = (const T *)d.dt;
-    for (int r = 0; r < len; ++r) {
-        const int t = tok_of(k0 + r, a.L, rev);
-        const float dtr = Elem<T>::load(DT, (rowt + t) * a.H + h);
-        s += (double)dtr * A;
-        sv[r] = s;
-        dtv[r] = dtr;
+    static_assert(kQ == 64, "one wave per block");
+    const int tid = threadIdx.x;
+    if (tid < kQ) {
+        const float dtr = tid < len
+            ? Elem<T>::load((const T *)d.dt, (rowt + tok_of(k0 + tid, a.L, rev)) * a.H + h)
+            : 0.f;
+        dtv[tid] = dtr;
+        double v = (double)dtr * (double)d.A[h];
+        for (int off = 1; off < kQ; off <<= 1) {
+            const double u = __shfl_up(v, off);
+            if (tid >= off) v += u;
+        }
+        sv[tid] = v;
     }
+    __syncthreads();
+}
+
+// Sum over the 8 lanes of an aligned group (the same value in all of them).
+__device__ __forceinline__ float sum8(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// Inclusive running sum over the 64 lanes of a wave (lane order), fp64.
+__device__ __forceinline__ double wave_scan(double v, int lane) {
+    for (int off = 1; off < 64; off <<= 1) {
+        const double u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+    }
+    return v;
+}
+
+// One 16x16 output tile of a product on the fp32 matrix cores
+// (v_mfma_f32_16x16x4f32; lane l, g = l / 16, m = l % 16: A supplies
+// A[m][k + g], B supplies B[k + g][m], the result holds rows 4g .. 4g+3 of
+// column m). a(m, k) and b(k, m) read the operands (from LDS).
+template <class FA, class FB>
+__device__ __forceinline__ f32x4 mm(FA a, FB b, int k0, int k1, f32x4 acc) {
+    const int l = threadIdx.x & 63, g = l >> 4, m = l & 15;
+    for (int k = k0; k < k1; k += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m, k + g), b(k + g, m), acc, 0, 0, 0);
+    return acc;
 }
 
 template <typename T, int P, int N>
 __global__ __launch_bounds__(kStateThreads) void k_bwd_state(BwdArgs a) {
-    constexpr int NT = kStateThreads, NPT = N * P / NT;
-    static_assert(N * P % NT == 0, "state elements per thread");
-    __shared__ float Wm[kQ][N];
-    __shared__ float Vm[kQ][P];
+    constexpr int NT = kStateThreads, NW = NT / 64;
+    constexpr int TN = N / 16, TP = P / 16, TILES = TN * TP, TPW = (TILES + NW - 1) / NW;
+    constexpr int SW = N + 4, SV = P + 4;     // padded LDS rows
+    __shared__ __attribute__((aligned(16))) float Wm[kQ][SW];
+    __shared__ __attribute__((aligned(16))) float Vm[kQ][SV];
     __shared__ double sv[kQ];
     __shared__ float dtv[kQ];
     const int c = blockIdx.x, h = blockIdx.y;
@@ -95,79 +138,52 @@ __global__ __launch_bounds__(kStateThreads) void k_bwd_state(BwdArgs a) {
     const int k0 = c * kQ;
     const int len = min(kQ, a.L - k0);
     const size_t rowt = (size_t)b * a.L;
-    const int tid = threadIdx.x;
-    if (tid == 0) block_scan<T>(a, d, rowt, h, k0, len, rev, sv, dtv);
-    __syncthreads();
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    block_scan<T>(a, d, rowt, h, k0, len, rev, sv, dtv);
     const double send = sv[len - 1];
     const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
     const size_t so = (unit * a.nc + c) * (size_t)(N * P);
 
-    // S = sum_j (e^{s_end - s_j} dt_j B_j) x_j^T
-    for (int e = tid; e < kQ * N; e += NT) {
-        const int r = e / N, n = e % N;
-        float v = 0.f;
-        if (r < len) {
-            const int t = tok_of(k0 + r, a.L, rev);
-            v = Elem<T>::load((const T *)d.B, ((rowt + t) * a.G + g) * N + n) *
-                (expf((float)(send - sv[r])) * dtv[r]);
+    for (int pass = 0; pass < 2; ++pass) {
+        // pass 0: S = sum_j (e^{s_end - s_j} dt_j B_j) x_j^T
+        // pass 1: R = sum_i (e^{s_i} C_i) dy_i^T
+        for (int e = tid; e < kQ * N; e += NT) {
+            const int r = e / N, n = e % N;
+            float v = 0.f;
+            if (r < len) {
+                const int t = tok_of(k0 + r, a.L, rev);
+                const size_t o = ((rowt + t) * a.G + g) * N + n;
+                v = pass == 0 ? Elem<T>::load((const T *)d.B, o) * (expf((float)(send - sv[r])) * dtv[r])
+                              : Elem<T>::load((const T *)d.C, o) * expf((float)sv[r]);
+            }
+            Wm[r][n] = v;
         }
-        Wm[r][n] = v;
-    }
-    for (int e = tid; e < kQ * P; e += NT) {
-        const int r = e / P, p = e % P;
-        float v = 0.f;
-        if (r < len) {
-            const int t = tok_of(k0 + r, a.L, rev);
-            v = Elem<T>::load((const T *)d.x, ((rowt + t) * a.H + h) * P + p);
+        for (int e = tid; e < kQ * P; e += NT) {
+            const int r = e / P, p = e % P;
+            float v = 0.f;
+            if (r < len) {
+                const size_t o = ((rowt + tok_of(k0 + r, a.L, rev)) * a.H + h) * P + p;
+                v = pass == 0 ? Elem<T>::load((const T *)d.x, o) : a.dy[o];
+            }
+            Vm[r][p] = v;
         }
-        Vm[r][p] = v;
-    }
-    __syncthreads();
-    float acc[NPT];
+        __syncthreads();
+        float *out = pass == 0 ? a.S : a.R;
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) acc[k] = 0.f;
-    for (int r = 0; r < len; ++r) {
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wave + u * NW;
+            if (t < TILES) {
+                const int nt = t / TP, pt = t % TP;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mm([&](int mm_, int k) { return Wm[k][nt * 16 + mm_]; },
+                         [&](int k, int mm_) { return Vm[k][pt * 16 + mm_]; }, 0, kQ, acc);
+                const int gq = lane >> 4, col = pt * 16 + (lane & 15);
 #pragma unroll
-        for (int k = 0; k < NPT; ++k) {
-            const int e = tid + k * NT;
-            acc[k] = fmaf(Wm[r][e / P], Vm[r][e % P], acc[k]);
+                for (int r = 0; r < 4; ++r) out[so + (size_t)(nt * 16 + 4 * gq + r) * P + col] = acc[r];
+            }
         }
+        __syncthreads();
     }
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) a.S[so + tid + k * NT] = acc[k];
-    __syncthreads();
-
-    // R = sum_i (e^{s_i} C_i) dy_i^T
-    for (int e = tid; e < kQ * N; e += NT) {
-        const int r = e / N, n = e % N;
-        float v = 0.f;
-        if (r < len) {
-            const int t = tok_of(k0 + r, a.L, rev);
-            v = Elem<T>::load((const T *)d.C, ((rowt + t) * a.G + g) * N + n) * expf((float)sv[r]);
-        }
-        Wm[r][n] = v;
-    }
-    for (int e = tid; e < kQ * P; e += NT) {
-        const int r = e / P, p = e % P;
-        float v = 0.f;
-        if (r < len) {
-            const int t = tok_of(k0 + r, a.L, rev);
-            v = a.dy[((rowt + t) * a.H + h) * P + p];
-        }
-        Vm[r][p] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) acc[k] = 0.f;
-    for (int r = 0; r < len; ++r) {
-#pragma unroll
-        for (int k = 0; k < NPT; ++k) {
-            const int e = tid + k * NT;
-            acc[k] = fmaf(Wm[r][e / P], Vm[r][e % P], acc[k]);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) a.R[so + tid + k * NT] = acc[k];
     if (tid == 0) a.lg[unit * a.nc + c] = send;
 }
 
@@ -196,33 +212,35 @@ __global__ __launch_bounds__(256) void k_bwd_pass(BwdArgs a, int np) {
 
 template <int P, int N>
 struct GradSmem {
-    float Bs[kQ][N + 1];
-    float Cs[kQ][N + 1];
-    float Xs[kQ][P + 1];
-    float Ys[kQ][P + 1];
+    static constexpr int SN = N + 4, SP = P + 4, SQ = kQ + 4;   // padded rows
+    float Bs[kQ][SN];
+    float Cs[kQ][SN];
+    float Xs[kQ][SP];
+    float Ys[kQ][SP];
     union {
         struct {
-            float Ms[kQ][kQ + 1];   // M = L o G
-            float Gs[kQ][kQ + 1];   // L o dM
-            float Zs[kQ][kQ + 1];   // dM o M
+            float Ms[kQ][SQ];   // M = L o G
+            float Gs[kQ][SQ];   // L o dM
+            float Zs[kQ][SQ];   // dM o M
         } q;
         struct {
-            float Hs[N][P + 1];     // entering state, then leaving-state gradient
-            float Tq[kQ][P + 1];    // per-position products summed over p
+            float Hs[N][SP];    // entering state, then leaving-state gradient
+            float Tq[kQ][SP];   // per-position products summed over p
         } st;
-        float Dx[kQ][P + 1];        // dxd, at the end
+        float Dx[kQ][SP];       // dxd, at the end
     } u;
     double sv[kQ];
-    double dav[kQ];
     float dtv[kQ], es[kQ], wv[kQ], dsi[kQ], dso[kQ], dss[kQ];
     float red[kGradThreads];
 };
 
 template <typename T, int P, int N>
 __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
-    constexpr int NT = kGradThreads;
-    constexpr int QP = kQ * P / NT, QN = kQ * N / NT, QQ = kQ * kQ / NT, NP = N * P;
-    static_assert(kQ * P % NT == 0 && kQ * N % NT == 0, "work per thread");
+    constexpr int NT = kGradThreads, NW = NT / 64, NP = N * P;
+    constexpr int TQ = kQ / 16, TN = N / 16, TP = P / 16;
+    constexpr int XT = TQ * TP, XPW = (XT + NW - 1) / NW;     // (position, p) tiles
+    constexpr int CT = TQ * TN, CPW = (CT + NW - 1) / NW;     // (position, n) tiles
+    constexpr int LT = TQ * (TQ + 1) / 2;                     // lower (i, j) tiles
     __shared__ __attribute__((aligned(16))) GradSmem<P, N> sm;
     const int c = blockIdx.x, h = blockIdx.y;
     const int dir = (int)(blockIdx.z % (unsigned)a.ndir), b = (int)(blockIdx.z / (unsigned)a.ndir);
@@ -233,12 +251,13 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     const int k0 = c * kQ;
     const int len = min(kQ, a.L - k0);
     const size_t rowt = (size_t)b * a.L;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int gq = lane >> 4, lm = lane & 15;     // result rows 4gq .. 4gq+3, column lm
     const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
     const size_t so = (unit * a.nc + c) * (size_t)NP;
 
     // ---- inputs of the block
-    if (tid == 0) block_scan<T>(a, d, rowt, h, k0, len, rev, sm.sv, sm.dtv);
+    block_scan<T>(a, d, rowt, h, k0, len, rev, sm.sv, sm.dtv);
     for (int e = tid; e < kQ * N; e += NT) {
         const int r = e / N, n = e % N;
         float vb = 0.f, vc = 0.f;
@@ -267,66 +286,83 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
         const int r = tid;
         sm.es[r] = r < len ? expf((float)sm.sv[r]) : 0.f;
         sm.wv[r] = r < len ? expf((float)(send - sm.sv[r])) : 0.f;
-        if (r >= len) sm.dtv[r] = 0.f;
     }
     __syncthreads();
 
-    // ---- the block's quadratic form: M, L o dM, dM o M
-    for (int e = tid; e < kQ * kQ; e += NT) {
-        const int i = e / kQ, j = e % kQ;
-        float M = 0.f, dG = 0.f, Z = 0.f;
-        if (j <= i && i < len) {
-            float G = 0.f, dm = 0.f;
-            #pragma unroll 4
-            for (int n = 0; n < N; ++n) G = fmaf(sm.Cs[i][n], sm.Bs[j][n], G);
-            #pragma unroll 4
-            for (int p = 0; p < P; ++p) dm = fmaf(sm.Ys[i][p], sm.Xs[j][p], dm);
-            dm *= sm.dtv[j];
-            const float Lij = expf((float)(sm.sv[i] - sm.sv[j]));
-            M = Lij * G;
-            dG = Lij * dm;
-            Z = dm * M;
+    // ---- the block's quadratic form: M = L o G, L o dM and dM o M, lower
+    // tiles on the matrix cores, upper tiles zero
+    for (int t = wave; t < TQ * TQ; t += NW) {
+        const int it = t / TQ, jt = t % TQ;
+        f32x4 G = {0.f, 0.f, 0.f, 0.f}, D = {0.f, 0.f, 0.f, 0.f};
+        if (jt <= it) {
+            G = mm([&](int m, int k) { return sm.Cs[it * 16 + m][k]; },
+                   [&](int k, int m) { return sm.Bs[jt * 16 + m][k]; }, 0, N, G);
+            D = mm([&](int m, int k) { return sm.Ys[it * 16 + m][k]; },
+                   [&](int k, int m) { return sm.Xs[jt * 16 + m][k]; }, 0, P, D);
         }
-        sm.u.q.Ms[i][j] = M;
-        sm.u.q.Gs[i][j] = dG;
-        sm.u.q.Zs[i][j] = Z;
+        const int j = jt * 16 + lm;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = it * 16 + 4 * gq + r;
+            float M = 0.f, dG = 0.f, Z = 0.f;
+            if (j <= i && i < len) {
+                const float dm = D[r] * sm.dtv[j];
+                const float Lij = expf((float)(sm.sv[i] - sm.sv[j]));
+                M = Lij * G[r];
+                dG = Lij * dm;
+                Z = dm * M;
+            }
+            sm.u.q.Ms[i][j] = M;
+            sm.u.q.Gs[i][j] = dG;
+            sm.u.q.Zs[i][j] = Z;
+        }
     }
+    (void)LT;
     __syncthreads();
-    (void)QQ;
 
     // ---- quadratic-form gradients
-    // the block's share of da_k = sum_{i >= k} ds_i: summed over i >= k of
-    // (row i of Z minus column i of Z), the pairs with both ends >= k cancel,
-    // leaving the rectangle i >= k > j; summing that directly avoids the
-    // cancellation
-    if (tid < kQ) {
-        const int k = tid;
-        float acc = 0.f;
-        for (int i = k; i < len; ++i)
-            for (int j = 0; j < k; ++j) acc += sm.u.q.Zs[i][j];
-        sm.dsi[k] = acc;
-    }
-    float dxd[QP], dcv[QN], dbv[QN];
-#pragma unroll
-    for (int k = 0; k < QP; ++k) {
-        const int e = tid + k * NT, j = e / P, p = e % P;
-        float acc = 0.f;
-        #pragma unroll 4
-        for (int i = j; i < len; ++i) acc = fmaf(sm.u.q.Ms[i][j], sm.Ys[i][p], acc);
-        dxd[k] = acc;
-    }
-#pragma unroll
-    for (int k = 0; k < QN; ++k) {
-        const int e = tid + k * NT, r = e / N, n = e % N;
-        float ac = 0.f, ab = 0.f;
-        if (r < len) {
-            #pragma unroll 4
-            for (int j = 0; j <= r; ++j) ac = fmaf(sm.u.q.Gs[r][j], sm.Bs[j][n], ac);
-            #pragma unroll 4
-            for (int i = r; i < len; ++i) ab = fmaf(sm.u.q.Gs[i][r], sm.Cs[i][n], ab);
+    // the block's share of da_k = sum_{i >= k} ds_i. Summed over i >= k,
+    // (row i of Z minus column i of Z) leaves the rectangle R(k) =
+    // sum_{i >= k > j} Z_ij (the pairs with both ends >= k cancel); it is
+    // built without that cancellation as R(k+1) = R(k) + sum_{i > k} Z_ik -
+    // sum_{j < k} Z_kj. Here: those two sums per k, 8 lanes per k.
+    {
+        const int k = tid >> 3, part = tid & 7;
+        float cs = 0.f, rp = 0.f;
+        for (int i = part; i < kQ; i += 8) {
+            if (i > k) cs += sm.u.q.Zs[i][k];
+            if (i < k) rp += sm.u.q.Zs[k][i];
         }
-        dcv[k] = ac;
-        dbv[k] = ab;
+        cs = sum8(cs);
+        rp = sum8(rp);
+        if (part == 0) sm.dsi[k] = cs - rp;
+    }
+    f32x4 dxd[XPW], dcv[CPW], dbv[CPW];
+#pragma unroll
+    for (int u = 0; u < XPW; ++u) {
+        const int t = wave + u * NW;
+        dxd[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t < XT) {
+            const int jt = t / TP, pt = t % TP;
+            // dxd_j = sum_{i >= j} M_ij dy_i
+            dxd[u] = mm([&](int m, int k) { return sm.u.q.Ms[k][jt * 16 + m]; },
+                        [&](int k, int m) { return sm.Ys[k][pt * 16 + m]; }, jt * 16, kQ, dxd[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+        const int t = wave + u * NW;
+        dcv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dbv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t < CT) {
+            const int rt = t / TN, nt = t % TN;
+            // dC_i = sum_{j <= i} (L o dM)_ij B_j
+            dcv[u] = mm([&](int m, int k) { return sm.u.q.Gs[rt * 16 + m][k]; },
+                        [&](int k, int m) { return sm.Bs[k][nt * 16 + m]; }, 0, rt * 16 + 16, dcv[u]);
+            // dB_j = sum_{i >= j} (L o dM)_ij C_i
+            dbv[u] = mm([&](int m, int k) { return sm.u.q.Gs[k][rt * 16 + m]; },
+                        [&](int k, int m) { return sm.Cs[k][nt * 16 + m]; }, rt * 16, kQ, dbv[u]);
+        }
     }
     __syncthreads();
 
@@ -334,22 +370,33 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     for (int e = tid; e < NP; e += NT) sm.u.st.Hs[e / P][e % P] = a.S[so + e];
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < QN; ++k) {
-        const int e = tid + k * NT, r = e / N, n = e % N;
-        if (r < len) {
-            float acc = 0.f;
-            #pragma unroll 4
-            for (int p = 0; p < P; ++p) acc = fmaf(sm.u.st.Hs[n][p], sm.Ys[r][p], acc);
-            dcv[k] = fmaf(sm.es[r], acc, dcv[k]);
+    for (int u = 0; u < CPW; ++u) {
+        const int t = wave + u * NW;
+        if (t < CT) {
+            const int rt = t / TN, nt = t % TN;
+            // dC_i += e^{s_i} Hp dy_i
+            f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+            tmp = mm([&](int m, int k) { return sm.Ys[rt * 16 + m][k]; },
+                     [&](int k, int m) { return sm.u.st.Hs[nt * 16 + m][k]; }, 0, P, tmp);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dcv[u][r] = fmaf(sm.es[rt * 16 + 4 * gq + r], tmp[r], dcv[u][r]);
         }
     }
 #pragma unroll
-    for (int k = 0; k < QP; ++k) {
-        const int e = tid + k * NT, r = e / P, p = e % P;
-        float ch = 0.f;
-        #pragma unroll 4
-        for (int n = 0; n < N; ++n) ch = fmaf(sm.Cs[r][n], sm.u.st.Hs[n][p], ch);
-        sm.u.st.Tq[r][p] = ch * sm.Ys[r][p];
+    for (int u = 0; u < XPW; ++u) {
+        const int t = wave + u * NW;
+        if (t < XT) {
+            const int it = t / TP, pt = t % TP;
+            // (C_i^T Hp)[p] dy_i[p], summed over p below
+            f32x4 ch = {0.f, 0.f, 0.f, 0.f};
+            ch = mm([&](int m, int k) { return sm.Cs[it * 16 + m][k]; },
+                    [&](int k, int m) { return sm.u.st.Hs[k][pt * 16 + m]; }, 0, N, ch);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = it * 16 + 4 * gq + r, p = pt * 16 + lm;
+                sm.u.st.Tq[i][p] = ch[r] * sm.Ys[i][p];
+            }
+        }
     }
     // <Hp, dHe> over the whole state (block tree, fixed order)
     float hd = 0.f;
@@ -361,10 +408,12 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
         __syncthreads();
     }
     const float hp_dhe = sm.red[0];
-    if (tid < kQ) {
+    {
+        const int r = tid >> 3, part = tid & 7;
         float acc = 0.f;
-        for (int p = 0; p < P; ++p) acc += sm.u.st.Tq[tid][p];
-        sm.dso[tid] = tid < len ? sm.es[tid] * acc : 0.f;
+        for (int p = part; p < P; p += 8) acc += sm.u.st.Tq[r][p];
+        acc = sum8(acc);
+        if (part == 0) sm.dso[r] = r < len ? sm.es[r] * acc : 0.f;
     }
     __syncthreads();
 
@@ -372,97 +421,122 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     for (int e = tid; e < NP; e += NT) sm.u.st.Hs[e / P][e % P] = a.R[so + e];
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < QP; ++k) {
-        const int e = tid + k * NT, j = e / P, p = e % P;
-        float bdh = 0.f;
-        #pragma unroll 4
-        for (int n = 0; n < N; ++n) bdh = fmaf(sm.Bs[j][n], sm.u.st.Hs[n][p], bdh);
-        dxd[k] = fmaf(sm.wv[j], bdh, dxd[k]);
-        sm.u.st.Tq[j][p] = sm.Xs[j][p] * bdh;
+    for (int u = 0; u < XPW; ++u) {
+        const int t = wave + u * NW;
+        if (t < XT) {
+            const int jt = t / TP, pt = t % TP;
+            // (B_j^T dHe)[p]: dxd_j += e^{s_end - s_j} B_j^T dHe
+            f32x4 bdh = {0.f, 0.f, 0.f, 0.f};
+            bdh = mm([&](int m, int k) { return sm.Bs[jt * 16 + m][k]; },
+                     [&](int k, int m) { return sm.u.st.Hs[k][pt * 16 + m]; }, 0, N, bdh);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = jt * 16 + 4 * gq + r, p = pt * 16 + lm;
+                dxd[u][r] = fmaf(sm.wv[j], bdh[r], dxd[u][r]);
+                sm.u.st.Tq[j][p] = sm.Xs[j][p] * bdh[r];
+            }
+        }
     }
 #pragma unroll
-    for (int k = 0; k < QN; ++k) {
-        const int e = tid + k * NT, r = e / N, n = e % N;
-        if (r < len) {
-            float acc = 0.f;
-            #pragma unroll 4
-            for (int p = 0; p < P; ++p) acc = fmaf(sm.u.st.Hs[n][p], sm.Xs[r][p], acc);
-            dbv[k] = fmaf(sm.wv[r] * sm.dtv[r], acc, dbv[k]);
+    for (int u = 0; u < CPW; ++u) {
+        const int t = wave + u * NW;
+        if (t < CT) {
+            const int rt = t / TN, nt = t % TN;
+            // dB_j += e^{s_end - s_j} dt_j dHe x_j
+            f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+            tmp = mm([&](int m, int k) { return sm.Xs[rt * 16 + m][k]; },
+                     [&](int k, int m) { return sm.u.st.Hs[nt * 16 + m][k]; }, 0, P, tmp);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = rt * 16 + 4 * gq + r;
+                dbv[u][r] = fmaf(sm.wv[j] * sm.dtv[j], tmp[r], dbv[u][r]);
+            }
         }
     }
     __syncthreads();
-    if (tid < kQ) {
+    {
+        const int r = tid >> 3, part = tid & 7;
         float acc = 0.f;
-        for (int p = 0; p < P; ++p) acc += sm.u.st.Tq[tid][p];
-        sm.dss[tid] = -sm.wv[tid] * sm.dtv[tid] * acc;
+        for (int p = part; p < P; p += 8) acc += sm.u.st.Tq[r][p];
+        acc = sum8(acc);
+        if (part == 0) sm.dss[r] = -sm.wv[r] * sm.dtv[r] * acc;
     }
 
     // ---- per-head dB, dC into the workspace; dxd into LDS
     const size_t pb = unit * (size_t)a.L * N;
 #pragma unroll
-    for (int k = 0; k < QN; ++k) {
-        const int e = tid + k * NT, r = e / N, n = e % N;
-        if (r < len) {
-            const size_t o = pb + (size_t)tok_of(k0 + r, a.L, rev) * N + n;
-            a.dBp[o] = dbv[k];
-            a.dCp[o] = dcv[k];
+    for (int u = 0; u < CPW; ++u) {
+        const int t = wave + u * NW;
+        if (t < CT) {
+            const int rt = t / TN, nt = t % TN;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rt * 16 + 4 * gq + r;
+                if (row < len) {
+                    const size_t o = pb + (size_t)tok_of(k0 + row, a.L, rev) * N + nt * 16 + lm;
+                    a.dBp[o] = dbv[u][r];
+                    a.dCp[o] = dcv[u][r];
+                }
+            }
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < QP; ++k) {
-        const int e = tid + k * NT;
-        sm.u.Dx[e / P][e % P] = dxd[k];
+    for (int u = 0; u < XPW; ++u) {
+        const int t = wave + u * NW;
+        if (t < XT) {
+            const int jt = t / TP, pt = t % TP;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.u.Dx[jt * 16 + 4 * gq + r][pt * 16 + lm] = dxd[u][r];
+        }
+    }
+    __syncthreads();
+
+    // ---- per-position sums x . dxd and x . dy, 8 lanes per position
+    {
+        const int r = tid >> 3, part = tid & 7;
+        float xd = 0.f, xy = 0.f;
+        for (int p = part; p < P; p += 8) {
+            xd = fmaf(sm.Xs[r][p], sm.u.Dx[r][p], xd);
+            xy = fmaf(sm.Xs[r][p], sm.Ys[r][p], xy);
+        }
+        xd = sum8(xd);
+        xy = sum8(xy);
+        if (part == 0) {
+            sm.red[r] = xd;
+            sm.red[kQ + r] = xy;
+        }
     }
     __syncthreads();
 
     // ---- da_k = sum_{i >= k} ds_i, each part summed without cancellation:
-    // the quadratic form's rectangle (above), the carried-state terms over
-    // i >= k, and the leaving-state terms, whose sum over i >= k is
-    // e^{s_end} <Hp, dHe> minus their sum over j < k
-    if (tid == 0) {
-        double tail = 0.0;
-        for (int r = len - 1; r >= 0; --r) {
-            tail += sm.dso[r];
-            sm.dav[r] = tail;
-        }
-        double head = 0.0;
-        const double end_term = (double)sm.es[len - 1] * hp_dhe;
-        for (int r = 0; r < len; ++r) {
-            sm.dav[r] += (double)sm.dsi[r] + end_term + head;
-            head -= sm.dss[r];
-        }
-    }
-    __syncthreads();
+    // the quadratic form's rectangle R(k) (an exclusive running sum of the
+    // per-k terms above), the carried-state terms over i >= k, and the
+    // leaving-state terms, whose sum over i >= k is e^{s_end} <Hp, dHe>
+    // minus their sum over j < k. One lane per position, fp64 scans.
     const float A = d.A[h];
     const float Dh = d.D ? d.D[h] : 0.f;
-    if (tid < len) {
+    if (tid < kQ) {
         const int r = tid;
-        float xdx = 0.f;
-        for (int p = 0; p < P; ++p) xdx = fmaf(sm.Xs[r][p], sm.u.Dx[r][p], xdx);
-        gr.ddt[(rowt + tok_of(k0 + r, a.L, rev)) * a.H + h] = xdx + A * (float)sm.dav[r];
+        const double q = sm.dsi[r];
+        const double rect = wave_scan(q, r) - q;
+        const double so_rev = wave_scan((double)sm.dso[kQ - 1 - r], r);   // suffix sums, reversed
+        const double so_suf = __shfl(so_rev, kQ - 1 - r);
+        const double ss = sm.dss[r];
+        const double ss_pre = wave_scan(ss, r) - ss;
+        const double da = r < len ? rect + so_suf + (double)sm.es[len - 1] * hp_dhe - ss_pre : 0.0;
+        if (r < len) gr.ddt[(rowt + tok_of(k0 + r, a.L, rev)) * a.H + h] = sm.red[r] + A * (float)da;
+        const float sa = wave_sum(r < len ? sm.dtv[r] * (float)da : 0.f);
+        const float sd = wave_sum(sm.red[kQ + r]);
+        if (r == 0) {
+            a.dDp[unit * a.nc + c] = sd;
+            a.dAp[unit * a.nc + c] = sa;
+        }
     }
     for (int e = tid; e < len * P; e += NT) {
         const int r = e / P, p = e % P;
         gr.dx[((rowt + tok_of(k0 + r, a.L, rev)) * a.H + h) * P + p] =
             fmaf(Dh, sm.Ys[r][p], sm.dtv[r] * sm.u.Dx[r][p]);
-    }
-    if (tid < kQ) {
-        const int r = tid;
-        float xy = 0.f;
-        for (int p = 0; p < P; ++p) xy = fmaf(sm.Xs[r][p], sm.Ys[r][p], xy);
-        sm.red[r] = xy;
-        sm.red[kQ + r] = r < len ? sm.dtv[r] * (float)sm.dav[r] : 0.f;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float sd = 0.f, sa = 0.f;
-        for (int r = 0; r < kQ; ++r) {
-            sd += sm.red[r];
-            sa += sm.red[kQ + r];
-        }
-        a.dDp[unit * a.nc + c] = sd;
-        a.dAp[unit * a.nc + c] = sa;
     }
 }
 
