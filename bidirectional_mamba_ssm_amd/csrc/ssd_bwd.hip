@@ -109,6 +109,94 @@ __device__ __forceinline__ double wave_scan(double v, int lane) {
     return v;
 }
 
+// Four consecutive elements as floats (8-byte bf16 or 16-byte fp32 loads).
+__device__ __forceinline__ void ld4(const float *p, float *o) {
+    const float4 v = *(const float4 *)p;
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void ld4(const uint16_t *p, float *o) {
+    const uint2 v = *(const uint2 *)p;
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+// A block's rows of a per-token array (row r is token tok_of(k0 + r); W
+// columns from element off of each token's stride), held in registers:
+// thread t owns 4-vectors t, t + NT, ... All loads are issued before any
+// is used.
+template <int W, int NT>
+struct Rows {
+    static constexpr int NV = kQ * W / 4, VPT = (NV + NT - 1) / NT;
+    float v[VPT][4];
+};
+
+template <typename T, int W, int NT>
+__device__ __forceinline__ void fetch_rows(Rows<W, NT> &rw, const void *src, size_t rowt,
+                                           size_t stride, size_t off, int k0, int len, int L,
+                                           bool rev) {
+#pragma unroll
+    for (int k = 0; k < Rows<W, NT>::VPT; ++k) {
+        const int e4 = threadIdx.x + k * NT;
+        const int r = e4 * 4 / W, c = e4 * 4 % W;
+        if (e4 < Rows<W, NT>::NV && r < len) {
+            ld4((const T *)src + (rowt + tok_of(k0 + r, L, rev)) * stride + off + c, rw.v[k]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rw.v[k][i] = 0.f;
+        }
+    }
+}
+
+// Stores held rows into an LDS array [kQ][S], each row scaled by scale(r).
+template <int W, int NT, int S, class F>
+__device__ __forceinline__ void store_rows(const Rows<W, NT> &rw, float (*dst)[S], F scale) {
+#pragma unroll
+    for (int k = 0; k < Rows<W, NT>::VPT; ++k) {
+        const int e4 = threadIdx.x + k * NT;
+        if (e4 < Rows<W, NT>::NV) {
+            const int r = e4 * 4 / W, c = e4 * 4 % W;
+            const float sc = scale(r);
+            *(float4 *)&dst[r][c] = make_float4(rw.v[k][0] * sc, rw.v[k][1] * sc,
+                                                rw.v[k][2] * sc, rw.v[k][3] * sc);
+        }
+    }
+}
+
+// An N x P state (flat, 16-byte aligned) in registers, and into LDS [N][S].
+template <int NP, int NT>
+struct Flat {
+    static constexpr int VPT = (NP / 4 + NT - 1) / NT;
+    float v[VPT][4];
+};
+
+template <int NP, int NT>
+__device__ __forceinline__ void fetch_flat(Flat<NP, NT> &f, const float *src) {
+#pragma unroll
+    for (int k = 0; k < Flat<NP, NT>::VPT; ++k) {
+        const int e4 = threadIdx.x + k * NT;
+        if (e4 < NP / 4) {
+            ld4(src + 4 * e4, f.v[k]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f.v[k][i] = 0.f;
+        }
+    }
+}
+
+template <int NP, int NT, int P, int S>
+__device__ __forceinline__ void store_flat(const Flat<NP, NT> &f, float (*dst)[S]) {
+#pragma unroll
+    for (int k = 0; k < Flat<NP, NT>::VPT; ++k) {
+        const int e4 = threadIdx.x + k * NT;
+        if (e4 < NP / 4) {
+            const int e = 4 * e4;
+            *(float4 *)&dst[e / P][e % P] = make_float4(f.v[k][0], f.v[k][1], f.v[k][2], f.v[k][3]);
+        }
+    }
+}
+
 // One 16x16 output tile of a product on the fp32 matrix cores
 // (v_mfma_f32_16x16x4f32; lane l, g = l / 16, m = l % 16: A supplies
 // A[m][k + g], B supplies B[k + g][m], the result holds rows 4g .. 4g+3 of
@@ -128,6 +216,7 @@ __global__ __launch_bounds__(kStateThreads) void k_bwd_state(BwdArgs a) {
     constexpr int SW = N + 4, SV = P + 4;     // padded LDS rows
     __shared__ __attribute__((aligned(16))) float Wm[kQ][SW];
     __shared__ __attribute__((aligned(16))) float Vm[kQ][SV];
+    static_assert(SW % 4 == 0 && SV % 4 == 0, "16-byte LDS rows");
     __shared__ double sv[kQ];
     __shared__ float dtv[kQ];
     const int c = blockIdx.x, h = blockIdx.y;
@@ -144,28 +233,23 @@ __global__ __launch_bounds__(kStateThreads) void k_bwd_state(BwdArgs a) {
     const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
     const size_t so = (unit * a.nc + c) * (size_t)(N * P);
 
+    const size_t sgn = (size_t)a.G * N, hp = (size_t)a.H * P;
+    Rows<N, NT> rb;
+    Rows<P, NT> rx;
+    fetch_rows<T>(rb, d.B, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+    fetch_rows<T>(rx, d.x, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
     for (int pass = 0; pass < 2; ++pass) {
         // pass 0: S = sum_j (e^{s_end - s_j} dt_j B_j) x_j^T
         // pass 1: R = sum_i (e^{s_i} C_i) dy_i^T
-        for (int e = tid; e < kQ * N; e += NT) {
-            const int r = e / N, n = e % N;
-            float v = 0.f;
-            if (r < len) {
-                const int t = tok_of(k0 + r, a.L, rev);
-                const size_t o = ((rowt + t) * a.G + g) * N + n;
-                v = pass == 0 ? Elem<T>::load((const T *)d.B, o) * (expf((float)(send - sv[r])) * dtv[r])
-                              : Elem<T>::load((const T *)d.C, o) * expf((float)sv[r]);
-            }
-            Wm[r][n] = v;
-        }
-        for (int e = tid; e < kQ * P; e += NT) {
-            const int r = e / P, p = e % P;
-            float v = 0.f;
-            if (r < len) {
-                const size_t o = ((rowt + tok_of(k0 + r, a.L, rev)) * a.H + h) * P + p;
-                v = pass == 0 ? Elem<T>::load((const T *)d.x, o) : a.dy[o];
-            }
-            Vm[r][p] = v;
+        if (pass == 0) {
+            store_rows(rb, Wm, [&](int r) { return r < len ? expf((float)(send - sv[r])) * dtv[r] : 0.f; });
+            store_rows(rx, Vm, [&](int) { return 1.f; });
+            // the second pass's rows, in flight during the first pass's products
+            fetch_rows<T>(rb, d.C, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+            fetch_rows<float>(rx, a.dy, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
+        } else {
+            store_rows(rb, Wm, [&](int r) { return r < len ? expf((float)sv[r]) : 0.f; });
+            store_rows(rx, Vm, [&](int) { return 1.f; });
         }
         __syncthreads();
         float *out = pass == 0 ? a.S : a.R;
@@ -212,7 +296,7 @@ __global__ __launch_bounds__(256) void k_bwd_pass(BwdArgs a, int np) {
 
 template <int P, int N>
 struct GradSmem {
-    static constexpr int SN = N + 4, SP = P + 4, SQ = kQ + 4;   // padded rows
+    static constexpr int SN = N + 4, SP = P + 4, SQ = kQ + 4;   // padded rows, 16-byte aligned
     float Bs[kQ][SN];
     float Cs[kQ][SN];
     float Xs[kQ][SP];
@@ -256,30 +340,25 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
     const size_t so = (unit * a.nc + c) * (size_t)NP;
 
-    // ---- inputs of the block
-    block_scan<T>(a, d, rowt, h, k0, len, rev, sm.sv, sm.dtv);
-    for (int e = tid; e < kQ * N; e += NT) {
-        const int r = e / N, n = e % N;
-        float vb = 0.f, vc = 0.f;
-        if (r < len) {
-            const size_t o = ((rowt + tok_of(k0 + r, a.L, rev)) * a.G + g) * N + n;
-            vb = Elem<T>::load((const T *)d.B, o);
-            vc = Elem<T>::load((const T *)d.C, o);
-        }
-        sm.Bs[r][n] = vb;
-        sm.Cs[r][n] = vc;
+    // ---- inputs of the block; the entering state and the leaving-state
+    // gradient are fetched now too and held until their phases
+    const size_t sgn = (size_t)a.G * N, hp = (size_t)a.H * P;
+    {
+        Rows<N, NT> rb, rc;
+        Rows<P, NT> rx, ry;
+        fetch_rows<T>(rb, d.B, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+        fetch_rows<T>(rc, d.C, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+        fetch_rows<T>(rx, d.x, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
+        fetch_rows<float>(ry, a.dy, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
+        block_scan<T>(a, d, rowt, h, k0, len, rev, sm.sv, sm.dtv);
+        store_rows(rb, sm.Bs, [](int) { return 1.f; });
+        store_rows(rc, sm.Cs, [](int) { return 1.f; });
+        store_rows(rx, sm.Xs, [](int) { return 1.f; });
+        store_rows(ry, sm.Ys, [](int) { return 1.f; });
     }
-    for (int e = tid; e < kQ * P; e += NT) {
-        const int r = e / P, p = e % P;
-        float vx = 0.f, vy = 0.f;
-        if (r < len) {
-            const size_t o = ((rowt + tok_of(k0 + r, a.L, rev)) * a.H + h) * P + p;
-            vx = Elem<T>::load((const T *)d.x, o);
-            vy = a.dy[o];
-        }
-        sm.Xs[r][p] = vx;
-        sm.Ys[r][p] = vy;
-    }
+    Flat<NP, NT> fhp, fdh;
+    fetch_flat(fhp, a.S + so);
+    fetch_flat(fdh, a.R + so);
     __syncthreads();
     const double send = sm.sv[len - 1];
     if (tid < kQ) {
@@ -367,7 +446,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     __syncthreads();
 
     // ---- terms of the entering state Hp
-    for (int e = tid; e < NP; e += NT) sm.u.st.Hs[e / P][e % P] = a.S[so + e];
+    store_flat<NP, NT, P>(fhp, sm.u.st.Hs);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
@@ -400,7 +479,10 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     }
     // <Hp, dHe> over the whole state (block tree, fixed order)
     float hd = 0.f;
-    for (int e = tid; e < NP; e += NT) hd = fmaf(sm.u.st.Hs[e / P][e % P], a.R[so + e], hd);
+#pragma unroll
+    for (int k = 0; k < Flat<NP, NT>::VPT; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hd = fmaf(fhp.v[k][i], fdh.v[k][i], hd);
     sm.red[tid] = hd;
     __syncthreads();
     for (int w = NT / 2; w > 0; w >>= 1) {
@@ -418,7 +500,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     __syncthreads();
 
     // ---- terms of the leaving-state gradient dHe
-    for (int e = tid; e < NP; e += NT) sm.u.st.Hs[e / P][e % P] = a.R[so + e];
+    store_flat<NP, NT, P>(fdh, sm.u.st.Hs);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < XPW; ++u) {
