@@ -46,7 +46,7 @@ namespace {
 
 constexpr int kQ = 64;          // scan positions per block
 constexpr int kStateThreads = 256;
-constexpr int kGradThreads = 512;
+constexpr int kGradThreads = 1024;   // 16 waves: one workgroup fills a CU (LDS)
 
 struct BwdArgs {
     DirPtrs fwd, bwd;
@@ -87,11 +87,11 @@ __device__ void block_scan(const BwdArgs &a, const DirPtrs &d, size_t rowt, int 
     __syncthreads();
 }
 
-// Sum over the 8 lanes of an aligned group (the same value in all of them).
-__device__ __forceinline__ float sum8(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
+// Sum over the G lanes of an aligned group (the same value in all of them).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off);
     return v;
 }
 
@@ -321,6 +321,7 @@ struct GradSmem {
 template <typename T, int P, int N>
 __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     constexpr int NT = kGradThreads, NW = NT / 64, NP = N * P;
+    constexpr int LPR = NT / kQ;                              // lanes per position
     constexpr int TQ = kQ / 16, TN = N / 16, TP = P / 16;
     constexpr int XT = TQ * TP, XPW = (XT + NW - 1) / NW;     // (position, p) tiles
     constexpr int CT = TQ * TN, CPW = (CT + NW - 1) / NW;     // (position, n) tiles
@@ -406,14 +407,14 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     // built without that cancellation as R(k+1) = R(k) + sum_{i > k} Z_ik -
     // sum_{j < k} Z_kj. Here: those two sums per k, 8 lanes per k.
     {
-        const int k = tid >> 3, part = tid & 7;
+        const int k = tid / LPR, part = tid % LPR;
         float cs = 0.f, rp = 0.f;
-        for (int i = part; i < kQ; i += 8) {
+        for (int i = part; i < kQ; i += LPR) {
             if (i > k) cs += sm.u.q.Zs[i][k];
             if (i < k) rp += sm.u.q.Zs[k][i];
         }
-        cs = sum8(cs);
-        rp = sum8(rp);
+        cs = group_sum<LPR>(cs);
+        rp = group_sum<LPR>(rp);
         if (part == 0) sm.dsi[k] = cs - rp;
     }
     f32x4 dxd[XPW], dcv[CPW], dbv[CPW];
@@ -483,18 +484,17 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     for (int k = 0; k < Flat<NP, NT>::VPT; ++k)
 #pragma unroll
         for (int i = 0; i < 4; ++i) hd = fmaf(fhp.v[k][i], fdh.v[k][i], hd);
-    sm.red[tid] = hd;
+    hd = wave_sum(hd);
+    if (lane == 0) sm.red[wave] = hd;
     __syncthreads();
-    for (int w = NT / 2; w > 0; w >>= 1) {
-        if (tid < w) sm.red[tid] += sm.red[tid + w];
-        __syncthreads();
-    }
-    const float hp_dhe = sm.red[0];
+    float hp_dhe = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) hp_dhe += sm.red[w];
     {
-        const int r = tid >> 3, part = tid & 7;
+        const int r = tid / LPR, part = tid % LPR;
         float acc = 0.f;
-        for (int p = part; p < P; p += 8) acc += sm.u.st.Tq[r][p];
-        acc = sum8(acc);
+        for (int p = part; p < P; p += LPR) acc += sm.u.st.Tq[r][p];
+        acc = group_sum<LPR>(acc);
         if (part == 0) sm.dso[r] = r < len ? sm.es[r] * acc : 0.f;
     }
     __syncthreads();
@@ -537,15 +537,16 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     }
     __syncthreads();
     {
-        const int r = tid >> 3, part = tid & 7;
+        const int r = tid / LPR, part = tid % LPR;
         float acc = 0.f;
-        for (int p = part; p < P; p += 8) acc += sm.u.st.Tq[r][p];
-        acc = sum8(acc);
+        for (int p = part; p < P; p += LPR) acc += sm.u.st.Tq[r][p];
+        acc = group_sum<LPR>(acc);
         if (part == 0) sm.dss[r] = -sm.wv[r] * sm.dtv[r] * acc;
     }
 
-    // ---- per-head dB, dC into the workspace; dxd into LDS
-    const size_t pb = unit * (size_t)a.L * N;
+    // ---- per-head dB, dC into the workspace (staged in LDS over B and C,
+    // which are no longer read, then written a row at a time); dxd into LDS
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
         const int t = wave + u * NW;
@@ -553,16 +554,11 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
             const int rt = t / TN, nt = t % TN;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = rt * 16 + 4 * gq + r;
-                if (row < len) {
-                    const size_t o = pb + (size_t)tok_of(k0 + row, a.L, rev) * N + nt * 16 + lm;
-                    a.dBp[o] = dbv[u][r];
-                    a.dCp[o] = dcv[u][r];
-                }
+                sm.Bs[rt * 16 + 4 * gq + r][nt * 16 + lm] = dbv[u][r];
+                sm.Cs[rt * 16 + 4 * gq + r][nt * 16 + lm] = dcv[u][r];
             }
         }
     }
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < XPW; ++u) {
         const int t = wave + u * NW;
@@ -573,17 +569,26 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
         }
     }
     __syncthreads();
+    {
+        const size_t pb = unit * (size_t)a.L * N;
+        for (int e4 = tid; e4 < len * (N / 4); e4 += NT) {
+            const int row = e4 / (N / 4), cc = (e4 % (N / 4)) * 4;
+            const size_t o = pb + (size_t)tok_of(k0 + row, a.L, rev) * N + cc;
+            *(float4 *)(a.dBp + o) = *(const float4 *)&sm.Bs[row][cc];
+            *(float4 *)(a.dCp + o) = *(const float4 *)&sm.Cs[row][cc];
+        }
+    }
 
     // ---- per-position sums x . dxd and x . dy, 8 lanes per position
     {
-        const int r = tid >> 3, part = tid & 7;
+        const int r = tid / LPR, part = tid % LPR;
         float xd = 0.f, xy = 0.f;
-        for (int p = part; p < P; p += 8) {
+        for (int p = part; p < P; p += LPR) {
             xd = fmaf(sm.Xs[r][p], sm.u.Dx[r][p], xd);
             xy = fmaf(sm.Xs[r][p], sm.Ys[r][p], xy);
         }
-        xd = sum8(xd);
-        xy = sum8(xy);
+        xd = group_sum<LPR>(xd);
+        xy = group_sum<LPR>(xy);
         if (part == 0) {
             sm.red[r] = xd;
             sm.red[kQ + r] = xy;
