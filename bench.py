@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3   # dense fp32 matrix (and vector) peak
 METRIC = "BiMamba-2 SSD tokens/s + % HBM/MFMA roofline; block-cached step ms"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ssd_seg_out_layer_1p3b_train_hbm_traffic.md")
 MIX_SUMMARY = os.path.join(ROOT, "profiles", "ssd_seg_out_layer_1p3b_train_instruction_mix.md")
@@ -454,6 +455,18 @@ def bwd_bytes_per_token(H, P, N, G, e):
     return 2 * (H * P * e + H * e + 2 * G * N * e) + H * P * 4 + 2 * (H * P + H + 2 * G * N) * 4
 
 
+def bwd_flops_per_token(H, P, N, G, Q=64):
+    """Algorithmic flops of the training backward per token, both streams,
+    counting the block products on the parts they use (triangles for the
+    within-block ones): per block of Q positions and head, C.B^T and dy.x^T
+    and the within-block dxd, dC, dB over the lower triangle, the four
+    entering/leaving-state products and the block state and gradient feed
+    over the full block."""
+    tri = Q * (Q + 1) // 2
+    mac = tri * N + tri * P + tri * P + 2 * tri * N + 6 * Q * N * P
+    return 2 * 2 * H * mac // Q
+
+
 def bwd_bench(args, bm, synth, torch, dev, steps):
     """The training backward at the training layer's shape (8 x 1024 tokens,
     64 heads x 64, d_state 128, bf16, both streams)."""
@@ -468,10 +481,15 @@ def bwd_bench(args, bm, synth, torch, dev, steps):
     ms, _, ker, dom = time_steps(bm, fn, steps, max(3, args.warmup // 10), torch)
     tok = w.batch * w.seqlen
     bpt = bwd_bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
+    fpt = bwd_flops_per_token(w.nheads, w.headdim, w.d_state, w.ngroups)
+    tfl = fpt * tok / (ms / 1e3) / 1e12
     res = {"workload": f"training backward, {w.name} (8 x 1024 tokens, 64 x 64 heads, d_state 128, bf16 in, fp32 gradients, both streams)",
            "tokens_per_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
            "algorithmic_bytes_per_token": bpt,
            "hbm_roofline_frac_step": round(bpt * tok / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "algorithmic_flops_per_token": fpt,
+           "mfma_fp32": {"achieved": round(tfl, 1), "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tfl / MFMA_FP32_PEAK_TFLOPS, 4)},
            "kernels_ms_per_step": {k: round(t / steps, 4) for k, (c, t) in ker.items()},
            "dominant_kernel": dom}
     del f, b, dy, ws, grads
