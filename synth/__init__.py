@@ -147,6 +147,17 @@ def make_conv_inputs(batch, L, ch, width, dtype, seed, device="cpu",
     return fwd, bwd
 
 
+def make_epilogue_inputs(rows, C, dtype, seed, device="cpu"):
+    """Inputs of the gated-norm epilogue, drawn in this order: the scan's
+    output y ~ N(0, 1) (fp32), the gate branch z ~ N(0, 1) (rounded to the
+    workload dtype), the per-channel weight ~ U(0.5, 1.5) (fp32)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    y = torch.randn(rows, C, generator=g, device=device)
+    z = torch.randn(rows, C, generator=g, device=device).to(_dtype(dtype))
+    w = torch.rand(C, generator=g, device=device) + 0.5
+    return y.contiguous(), z.contiguous(), w.float().contiguous()
+
+
 def make_workload(w: Workload, device="cpu"):
     return make_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.d_state,
                        w.ngroups, w.dtype, w.seed, device)

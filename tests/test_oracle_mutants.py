@@ -184,3 +184,44 @@ def test_bwd_pins_catch_mutant(name, tmp_path):
             if not (err <= tol):
                 caught.append(pin)
     assert caught, f"no pin catches mutant {name}"
+
+
+EPI_SRC = open(os.path.join(os.path.dirname(oracle.__file__), "epilogue.py")).read()
+
+EPI_MUTANTS = {
+    # eps added outside the square root
+    "epi_eps_outside": ("part / np.sqrt(ms + eps)", "part / (np.sqrt(ms) + eps)"),
+    # the gate dropped
+    "epi_no_gate": ("    v = y * silu(z)\n", "    v = y\n"),
+    # the gate's sigmoid without the factor z
+    "epi_sigmoid_gate": ("return u / (1.0 + np.exp(-u))", "return 1.0 / (1.0 + np.exp(-u))"),
+    # mean over the whole row instead of the group
+    "epi_whole_row": ("ms = np.mean(part * part, axis=-1, keepdims=True)",
+                      "ms = np.mean(v * v, axis=-1, keepdims=True)"),
+    # per-channel weight dropped
+    "epi_no_weight": (" * w[g0:g0 + group_size]", ""),
+    # sum of squares instead of their mean
+    "epi_sum_not_mean": ("ms = np.mean(part * part, axis=-1, keepdims=True)",
+                         "ms = np.sum(part * part, axis=-1, keepdims=True)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EPI_MUTANTS))
+def test_epilogue_pins_catch_mutant(name):
+    import types
+    from epilogue_pins import EPILOGUE_PINS
+    a, b = EPI_MUTANTS[name]
+    assert EPI_SRC.count(a) == 1, f"mutation site for {name} not found once"
+    mod = types.ModuleType("epilogue_mutant")
+    exec(compile(EPI_SRC.replace(a, b), "epilogue_mutant.py", "exec"), mod.__dict__)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin, (fn, tol) in EPILOGUE_PINS.items():
+            try:
+                err = fn(mod)
+            except Exception:
+                caught.append(pin)
+                continue
+            if not (err <= tol):
+                caught.append(pin)
+    assert caught, f"no pin catches mutant {name}"

@@ -3,6 +3,8 @@ import pytest
 
 from bwd_pins import BWD_PINS
 from conv_pins import CONV_PINS
+from epilogue_pins import EPILOGUE_PINS
+from oracle import epilogue
 from oracle import conv
 from pins import ALL_PINS
 
@@ -25,4 +27,11 @@ def test_conv_oracle_pin(name):
 def test_bwd_oracle_pin(name):
     fn, tol = BWD_PINS[name]
     err = fn(None)
+    assert err <= tol, f"pin {name}: error {err} > {tol}"
+
+
+@pytest.mark.parametrize("name", sorted(EPILOGUE_PINS))
+def test_epilogue_oracle_pin(name):
+    fn, tol = EPILOGUE_PINS[name]
+    err = fn(epilogue)
     assert err <= tol, f"pin {name}: error {err} > {tol}"
