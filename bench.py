@@ -98,6 +98,8 @@ def parse():
                     help="only the block-decode step lines (one JSON object)")
     ap.add_argument("--bwd-only", action="store_true",
                     help="only the training-backward line (one JSON object)")
+    ap.add_argument("--epilogue-only", action="store_true",
+                    help="only the gated-norm epilogue line (one JSON object)")
     ap.add_argument("--conv-only", action="store_true",
                     help="only the short-convolution line (one JSON object)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -248,6 +250,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.epilogue_only:
+        if args.calibrate_copy:
+            calibrate_copy(torch, dev)
+        print(json.dumps({"gated_norm_layer_1p3b_train": epilogue_bench(args, bm, synth, torch, dev, args.steps)}),
+              flush=True)
+        return
     if args.bwd_only:
         print(json.dumps({"bwd_layer_1p3b_train": bwd_bench(args, bm, synth, torch, dev, args.steps)}),
               flush=True)
@@ -402,6 +410,7 @@ def extras(args, bm, synth, torch, dev):
     res["block_step"] = block_step_bench(args, bm, synth, torch, dev, steps)
     res["conv1d_layer_1p3b_train"] = conv_bench(args, bm, synth, torch, dev, max(steps, 20))
     res["bwd_layer_1p3b_train"] = bwd_bench(args, bm, synth, torch, dev, max(3, steps // 4))
+    res["gated_norm_layer_1p3b_train"] = epilogue_bench(args, bm, synth, torch, dev, max(steps, 20))
     return res
 
 
@@ -492,7 +501,45 @@ def bwd_bench(args, bm, synth, torch, dev, steps):
                          "frac": round(tfl / MFMA_FP32_PEAK_TFLOPS, 4)},
            "kernels_ms_per_step": {k: round(t / steps, 4) for k, (c, t) in ker.items()},
            "dominant_kernel": dom}
+    if not args.no_cpu_baseline:
+        # the oracle's adjoint (C, fp64) on one row of the same inputs; its
+        # work is spread over rows, so one row runs on one core
+        import oracle
+        fr = {k: (v[:1] if v.dim() > 1 else v) for k, v in f.items()}
+        br = {k: (v[:1] if v.dim() > 1 else v) for k, v in b.items()}
+        t0 = time.perf_counter()
+        oracle.bissd_bwd(fr, br, dy[:1])
+        sec = time.perf_counter() - t0
+        res["cpu_oracle"] = {"tokens_per_s": round(w.seqlen / sec, 1), "kind": "oracle", "cores": 1,
+                             "sample": f"1 of {w.batch} rows ({w.seqlen} tokens), both streams, fp64 adjoint, {sec:.1f} s"}
     del f, b, dy, ws, grads
+    torch.cuda.empty_cache()
+    return res
+
+
+def epilogue_bench(args, bm, synth, torch, dev, steps):
+    """The gated-norm epilogue at the layer's shape: 8 x 1024 tokens, 4096
+    channels, one group, fp32 y, bf16 gate and output. Algorithmic bytes:
+    y, z read once, the output written once, plus the weight."""
+    rows, C = 8 * 1024, 4096
+    y, z, w = synth.make_epilogue_inputs(rows, C, "bf16", 108, device=dev)
+    out = torch.empty(rows, C, dtype=torch.bfloat16, device=dev)
+    fn = lambda: bm.gated_norm(y, z, w, out=out)  # noqa: E731
+    ms, _, ker, dom = time_steps(bm, fn, steps, max(3, args.warmup // 10), torch)
+    nbytes = rows * C * (4 + 2 + 2) + C * 4
+    res = {"workload": f"gated RMS norm, {rows} tokens x {C} channels, one group, bf16 gate and output",
+           "tokens_per_s": round(rows / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+           "bytes_per_launch": nbytes, "roofline": roofline_for(ker, dom, nbytes),
+           "ms_per_step_graph": round(graph_step_ms(fn, torch), 5)}
+    if not args.no_cpu_baseline:
+        from oracle import epilogue as oepi
+        n = 1024
+        t0 = time.perf_counter()
+        oepi.gated_rmsnorm(y[:n], z[:n], w, C)
+        sec = time.perf_counter() - t0
+        res["cpu_oracle"] = {"tokens_per_s": round(n / sec, 1), "kind": "oracle",
+                             "sample": f"{n} of {rows} tokens, numpy fp64, {sec:.2f} s"}
+    del y, z, w, out
     torch.cuda.empty_cache()
     return res
 
@@ -522,6 +569,17 @@ def conv_bench(args, bm, synth, torch, dev, steps):
            "bytes_per_launch": nbytes,
            "roofline": roofline_for(ker, dom, nbytes)}
     res["ms_per_step_graph"] = round(graph_step_ms(fn, torch), 5)
+    if not args.no_cpu_baseline:
+        # the oracle (numpy, fp64) on one row of the same inputs, both directions
+        from oracle import conv as oconv
+        fr = {k: (v[:1] if k == "xbc" else v) for k, v in f.items()}
+        br = {k: (v[:1] if k == "xbc" else v) for k, v in b.items()}
+        t0 = time.perf_counter()
+        oconv.conv1d(fr["xbc"], fr["weight"], fr["bias"])
+        oconv.conv1d(br["xbc"], br["weight"], br["bias"], reverse=True)
+        sec = time.perf_counter() - t0
+        res["cpu_oracle"] = {"tokens_per_s": round(L / sec, 1), "kind": "oracle",
+                             "sample": f"1 of {batch} rows ({L} tokens), both directions, numpy fp64, {sec:.2f} s"}
     del f, b, out
     torch.cuda.empty_cache()
     return res

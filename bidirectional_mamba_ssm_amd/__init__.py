@@ -324,6 +324,27 @@ def conv1d(fwd, bwd, nheads, headdim, ngroups, d_state, activation="silu",
     return fo, bo
 
 
+def gated_norm(y, z, weight, group_size=None, eps=1e-5, out=None, stream=None):
+    """Gated RMS norm on the scan output (bimamba_gated_norm): y float32
+    [..., C], z [..., C] (bf16 or fp32, also the output dtype), weight
+    float32 [C]. group_size defaults to C (one group)."""
+    dev = _cuda_device(y)
+    C = y.shape[-1]
+    rows = y.numel() // C if C else 0
+    if z.dtype not in DTYPES:
+        raise TypeError(f"unsupported dtype {z.dtype}")
+    _check(y, "y", tuple(y.shape), torch.float32, dev)
+    _check(z, "z", tuple(y.shape), z.dtype, dev)
+    _check(weight, "weight", (C,), torch.float32, dev)
+    if out is None:
+        out = torch.empty(y.shape, dtype=z.dtype, device=dev)
+    _check(out, "out", tuple(y.shape), z.dtype, dev)
+    _abi.check(lib().bimamba_gated_norm(rows, C, C if group_size is None else int(group_size),
+                                        DTYPES[z.dtype], _ptr(y), _ptr(z), _ptr(weight),
+                                        float(eps), _ptr(out), _stream(stream)))
+    return out
+
+
 def seq_index(cu_seqlens, device="cuda", stream=None):
     """Per-token packed-sequence index built on the GPU (int32 [total])."""
     vals = [int(v) for v in cu_seqlens]

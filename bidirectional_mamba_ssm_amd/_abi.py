@@ -21,7 +21,7 @@ EXPORTS = (
     "bimamba_block_step", "bimamba_seq_index", "bimamba_status_str",
     "bimamba_last_error", "bimamba_version", "bimamba_profile_begin",
     "bimamba_profile_end", "bimamba_conv1d_workspace_size", "bimamba_conv1d",
-    "bimamba_ssd_bwd_workspace_size", "bimamba_ssd_bwd",
+    "bimamba_ssd_bwd_workspace_size", "bimamba_ssd_bwd", "bimamba_gated_norm",
 )
 
 
@@ -98,6 +98,8 @@ def load():
     gp = ctypes.POINTER(Grad)
     lib.bimamba_ssd_bwd_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.bimamba_ssd_bwd.argtypes = [sp, dp, dp, vp, gp, gp, vp, ctypes.c_size_t, vp]
+    lib.bimamba_gated_norm.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       vp, vp, vp, ctypes.c_float, vp, vp]
     csp, cdp = ctypes.POINTER(ConvShape), ctypes.POINTER(ConvDir)
     lib.bimamba_conv1d_workspace_size.argtypes = [csp, ctypes.c_int,
                                                   ctypes.POINTER(ctypes.c_size_t)]

@@ -609,4 +609,33 @@ int bimamba_conv1d(const bimamba_conv_shape *s, const bimamba_conv_dir *fwd,
     return BIMAMBA_OK;
 }
 
+int bimamba_gated_norm(long long rows, int channels, int group_size, int dtype,
+                       const float *y, const void *z, const float *weight, float eps,
+                       void *out, bimamba_stream stream) {
+    if (dtype != BIMAMBA_F32 && dtype != BIMAMBA_BF16)
+        return fail(BIMAMBA_EINVAL, "dtype %d is not BIMAMBA_F32 or BIMAMBA_BF16", dtype);
+    if (rows < 0) return fail(BIMAMBA_EINVAL, "rows %lld < 0", rows);
+    if (rows > (1LL << 31) - 1) return fail(BIMAMBA_EUNSUPPORTED, "rows %lld exceed 2^31-1", rows);
+    if (channels <= 0 || channels % 256 || channels > 8192)
+        return fail(BIMAMBA_EUNSUPPORTED, "channels %d: need a multiple of 256 up to 8192", channels);
+    if (group_size <= 0 || group_size % 256 || channels % group_size)
+        return fail(BIMAMBA_EINVAL, "group_size %d: need a multiple of 256 dividing %d", group_size, channels);
+    if (!(eps >= 0.f) || eps > 3.0e38f) return fail(BIMAMBA_EINVAL, "eps must be finite and >= 0");
+    if (rows == 0) return BIMAMBA_OK;
+    if (!y || !z || !weight || !out) return fail(BIMAMBA_EINVAL, "y, z, weight and out are required");
+    if (!aligned16(y) || !aligned16(z) || !aligned16(weight) || !aligned16(out))
+        return fail(BIMAMBA_EINVAL, "y, z, weight and out must be 16-byte aligned");
+    EpiArgs a;
+    a.rows = rows;
+    a.C = channels;
+    a.gs = group_size;
+    a.eps = eps;
+    a.y = y;
+    a.z = z;
+    a.w = weight;
+    a.out = out;
+    hipError_t e = launch_gated_norm(a, dtype == BIMAMBA_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "launching the gated norm");
+}
+
 }  // extern "C"

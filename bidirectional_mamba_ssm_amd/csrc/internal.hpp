@@ -72,6 +72,18 @@ bool bwd_supported(int P, int N);
 size_t bwd_workspace(int batch, int L, int H, int P, int N, int ndir);
 hipError_t launch_bwd(const BwdProblem &p, void *ws, hipStream_t s);
 
+// epilogue.hip: gated RMS norm of the scan's output
+struct EpiArgs {
+    long long rows;
+    int C, gs;                 // channels (multiple of 256, <= 8192), group size
+    float eps;
+    const float *y;            // [rows][C]
+    const void *z;             // [rows][C] bf16 or fp32
+    const float *w;            // [C]
+    void *out;                 // [rows][C], z's dtype
+};
+hipError_t launch_gated_norm(const EpiArgs &a, bool bf16, hipStream_t s);
+
 // conv1d.hip: short depthwise convolution of the x | B | C channels
 struct ConvDirPtrs {
     const void *xbc;           // [batch][L][ch]

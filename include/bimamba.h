@@ -187,6 +187,31 @@ int bimamba_ssd_bwd(const bimamba_shape *s, const bimamba_dir *fwd,
                     const bimamba_dir *bwd, const float *dy,
                     const bimamba_grad *gfwd, const bimamba_grad *gbwd,
                     void *workspace, size_t workspace_bytes, bimamba_stream stream);
+/* ---- Gated-norm epilogue ----------------------------------------------------
+ *
+ * The output stage after the scan: each direction is a whole Mamba block
+ * (DiffuMamba blog, "network architecture") and the mixer is Mamba-2
+ * (DiffuMamba summaries, methodology); the pages do not spell the stage out,
+ * and Mamba-2's default is taken: the scan output y is gated by SiLU of the
+ * gate branch z, then RMS-normalized over groups of consecutive channels and
+ * scaled per channel:
+ *
+ *   v = y * silu(z),  out = v / sqrt(mean over the group of v^2 + eps) * weight
+ *
+ *  rows        tokens (batch * seqlen), >= 0
+ *  channels    per token (nheads * headdim): a multiple of 256, at most 8192
+ *  group_size  a multiple of 256 dividing channels (channels: one group)
+ *  dtype       of z and of out (bimamba_dtype)
+ *  y           float [rows][channels] (bimamba_ssd_fwd's output)
+ *  z           dtype [rows][channels]
+ *  weight      float [channels]
+ *  eps         >= 0
+ *  out         dtype [rows][channels]; may not overlap the inputs
+ * Pointers 16-byte aligned. Computed in fp32; bf16 output rounded to nearest
+ * even. */
+int bimamba_gated_norm(long long rows, int channels, int group_size, int dtype,
+                       const float *y, const void *z, const float *weight, float eps,
+                       void *out, bimamba_stream stream);
 /* ---- Short convolution in front of the scan -------------------------------
  *
  * Each direction of the bidirectional block is a whole Mamba block with its

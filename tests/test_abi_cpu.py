@@ -212,3 +212,28 @@ def test_conv_arguments_rejected(lib):
     assert lib.bimamba_conv1d_workspace_size(ctypes.byref(s), 0, ctypes.byref(n)) == _abi.OK
     assert n.value == 0
     assert lib.bimamba_conv1d_workspace_size(ctypes.byref(s), -1, ctypes.byref(n)) == _abi.EINVAL
+
+
+def test_gated_norm_validation(lib):
+    f = lib.bimamba_gated_norm
+    ok = dict(rows=4, channels=512, group_size=256, dtype=_abi.BF16, y=FAKE, z=FAKE,
+              weight=FAKE, eps=1e-5, out=FAKE)
+
+    def call(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return f(d["rows"], d["channels"], d["group_size"], d["dtype"], d["y"], d["z"],
+                 d["weight"], d["eps"], d["out"], None)
+    assert call(dtype=3) == _abi.EINVAL
+    assert call(rows=-1) == _abi.EINVAL
+    assert call(rows=1 << 31) == _abi.EUNSUPPORTED
+    assert call(channels=100) == _abi.EUNSUPPORTED
+    assert call(channels=8192 + 256) == _abi.EUNSUPPORTED
+    assert call(group_size=128) == _abi.EINVAL
+    assert call(group_size=768) == _abi.EINVAL
+    assert call(eps=-1.0) == _abi.EINVAL
+    assert call(eps=float("nan")) == _abi.EINVAL
+    for k in ("y", "z", "weight", "out"):
+        assert call(**{k: None}) == _abi.EINVAL, k
+        assert call(**{k: FAKE + 4}) == _abi.EINVAL, k
+    assert call(rows=0, y=None, z=None, weight=None, out=None) == _abi.OK
