@@ -63,3 +63,33 @@ EPILOGUE_PINS = {
     "epi_scale_invariant": (pin_scale_invariant, 1e-13),
     "epi_groups_independent": (pin_groups_independent, 0.0),
 }
+
+
+# ---- the step-size preprocessing (oracle/dt.py)
+
+def pin_dt_torch(mod, seed=94):
+    """== torch.nn.functional.softplus(raw + bias) in fp64 (its linear region
+    starts at 20, where the two differ by less than e^-20)."""
+    rng = np.random.default_rng(seed)
+    raw = rng.standard_normal((5, 7)) * 6
+    bias = rng.uniform(-3, 1, 7)
+    got = mod.preprocess_dt(raw, bias)
+    ref = F.softplus(torch.from_numpy(raw + bias)).numpy()
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-300)))
+
+
+def pin_dt_identities(mod):
+    """softplus(0) = ln 2; softplus(v) - softplus(-v) = v; softplus(-40) =
+    e^-40 to 1e-17 relative."""
+    v = np.linspace(-30, 30, 121)
+    worst = abs(float(mod.softplus(np.array([0.0]))[0]) - np.log(2.0))
+    worst = max(worst, float(np.max(np.abs(mod.softplus(v) - mod.softplus(-v) - v))))
+    small = float(mod.softplus(np.array([-40.0]))[0])
+    worst = max(worst, abs(small - np.exp(-40.0)) / np.exp(-40.0))
+    return worst
+
+
+DT_PINS = {
+    "dt_torch": (pin_dt_torch, 1e-9),
+    "dt_identities": (pin_dt_identities, 1e-14),
+}

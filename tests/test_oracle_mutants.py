@@ -225,3 +225,37 @@ def test_epilogue_pins_catch_mutant(name):
             if not (err <= tol):
                 caught.append(pin)
     assert caught, f"no pin catches mutant {name}"
+
+
+DT_SRC = open(os.path.join(os.path.dirname(oracle.__file__), "dt.py")).read()
+
+DT_MUTANTS = {
+    # the naive form: overflows, loses very negative inputs
+    "dt_naive": ("return np.maximum(v, 0.0) + np.log1p(np.exp(-np.abs(v)))",
+                 "return np.log(1.0 + np.exp(v))"),
+    # bias subtracted
+    "dt_bias_sign": ("raw = raw + _f64(bias)", "raw = raw - _f64(bias)"),
+    # exp instead of softplus
+    "dt_exp": ("return np.maximum(v, 0.0) + np.log1p(np.exp(-np.abs(v)))", "return np.exp(v)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DT_MUTANTS))
+def test_dt_pins_catch_mutant(name):
+    import types
+    from epilogue_pins import DT_PINS
+    a, b = DT_MUTANTS[name]
+    assert DT_SRC.count(a) == 1, f"mutation site for {name} not found once"
+    mod = types.ModuleType("dt_mutant")
+    exec(compile(DT_SRC.replace(a, b), "dt_mutant.py", "exec"), mod.__dict__)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin, (fn, tol) in DT_PINS.items():
+            try:
+                err = fn(mod)
+            except Exception:
+                caught.append(pin)
+                continue
+            if not (err <= tol):
+                caught.append(pin)
+    assert caught, f"no pin catches mutant {name}"

@@ -3,7 +3,7 @@ import pytest
 
 from bwd_pins import BWD_PINS
 from conv_pins import CONV_PINS
-from epilogue_pins import EPILOGUE_PINS
+from epilogue_pins import DT_PINS, EPILOGUE_PINS
 from oracle import epilogue
 from oracle import conv
 from pins import ALL_PINS
@@ -34,4 +34,12 @@ def test_bwd_oracle_pin(name):
 def test_epilogue_oracle_pin(name):
     fn, tol = EPILOGUE_PINS[name]
     err = fn(epilogue)
+    assert err <= tol, f"pin {name}: error {err} > {tol}"
+
+
+@pytest.mark.parametrize("name", sorted(DT_PINS))
+def test_dt_oracle_pin(name):
+    from oracle import dt as odt
+    fn, tol = DT_PINS[name]
+    err = fn(odt)
     assert err <= tol, f"pin {name}: error {err} > {tol}"
