@@ -68,19 +68,22 @@ def _dir(d, dtype, dims=None, device=None, name="fwd"):
     _check(d["A"], f"{name}.A", (H,), torch.float32, device)
     if d.get("D") is not None:
         _check(d["D"], f"{name}.D", (H,), torch.float32, device)
+    if d.get("dt_bias") is not None:
+        _check(d["dt_bias"], f"{name}.dt_bias", (H,), torch.float32, device)
     return _abi.Dir(d["x"].data_ptr(), d["dt"].data_ptr(), d["A"].data_ptr(),
                     d["B"].data_ptr(), d["C"].data_ptr(),
-                    d["D"].data_ptr() if d.get("D") is not None else None)
+                    d["D"].data_ptr() if d.get("D") is not None else None,
+                    d["dt_bias"].data_ptr() if d.get("dt_bias") is not None else None)
 
 
-def make_shape(x, B, chunk, seqlen=None):
+def make_shape(x, B, chunk, seqlen=None, dt_softplus=False):
     """Shape of a problem whose x is [batch, L, H, P] and B [batch, L, G, N]."""
     batch, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     if x.dtype not in DTYPES:
         raise TypeError(f"unsupported dtype {x.dtype}")
     return _abi.Shape(batch, L if seqlen is None else seqlen, H, P, N, G, chunk,
-                      DTYPES[x.dtype], 0)
+                      DTYPES[x.dtype], _abi.DT_SOFTPLUS if dt_softplus else 0)
 
 
 def workspace_size(shape, nseq=0):
@@ -90,17 +93,18 @@ def workspace_size(shape, nseq=0):
 
 
 def ssd_fwd(fwd, bwd=None, chunk=256, cu_seqlens=None, init_state=None,
-            final_state=None, y=None, workspace=None, stream=None):
+            final_state=None, y=None, workspace=None, stream=None, dt_softplus=False):
     """Bidirectional SSD (see include/bimamba.h, bimamba_ssd_fwd).
 
     fwd/bwd: dicts of device tensors x [b,L,H,P], dt [b,L,H], A [H] f32,
-    B/C [b,L,G,N], D [H] f32 or None. cu_seqlens: host list/tensor of
-    nseq+1 offsets. Returns y (float32 [b,L,H,P]).
+    B/C [b,L,G,N], D [H] f32 or None, and (with dt_softplus, where dt is the
+    pre-activation) dt_bias [H] f32 or None. cu_seqlens: host list/tensor
+    of nseq+1 offsets. Returns y (float32 [b,L,H,P]).
     """
     x = fwd["x"]
     dims = _dims(fwd)
     batch, L, H, P, G, N = dims
-    shape = make_shape(x, fwd["B"], chunk)
+    shape = make_shape(x, fwd["B"], chunk, dt_softplus=dt_softplus)
     dtype = x.dtype
     dev = _cuda_device(x)
     fd = _dir(fwd, dtype, dims, dev, "fwd")
@@ -229,11 +233,11 @@ class State:
         return self._h
 
 
-def block_step(state, fwd, bwd, commit=False, chunk=64, y=None, stream=None):
+def block_step(state, fwd, bwd, commit=False, chunk=64, y=None, stream=None, dt_softplus=False):
     """One cached block-diffusion step (bimamba_block_step)."""
     x = fwd["x"]
     dims = _dims(fwd)
-    shape = make_shape(x, fwd["B"], chunk)
+    shape = make_shape(x, fwd["B"], chunk, dt_softplus=dt_softplus)
     dev = _cuda_device(x)
     fd = _dir(fwd, x.dtype, dims, dev, "fwd")
     bd = _dir(bwd, x.dtype, dims, dev, "bwd")

@@ -36,7 +36,11 @@ class Shape(ctypes.Structure):
 class Dir(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p),
                 ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
-                ("C", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+                ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p)]
+
+
+DT_SOFTPLUS = 1
 
 
 class Grad(ctypes.Structure):

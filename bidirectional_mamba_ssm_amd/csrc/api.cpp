@@ -42,8 +42,8 @@ int check_shape(const bimamba_shape *s, bool block_step) {
     if (s->seqlen < 0) return fail(BIMAMBA_EINVAL, "seqlen %d < 0", s->seqlen);
     if (s->nheads < 1 || s->headdim < 1 || s->d_state < 1 || s->ngroups < 1)
         return fail(BIMAMBA_EINVAL, "nheads/headdim/d_state/ngroups must be >= 1");
-    if (s->flags != 0)
-        return fail(BIMAMBA_EINVAL, "flags 0x%x: no flag is defined", s->flags);
+    if (s->flags & ~BIMAMBA_DT_SOFTPLUS)
+        return fail(BIMAMBA_EINVAL, "flags 0x%x: only BIMAMBA_DT_SOFTPLUS is defined", s->flags);
     if (s->nheads % s->ngroups)
         return fail(BIMAMBA_EINVAL, "ngroups %d does not divide nheads %d", s->ngroups, s->nheads);
     if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256)
@@ -119,6 +119,12 @@ DirPtrs to_ptrs(const bimamba_dir *d) {
     DirPtrs p;
     p.x = d->x; p.dt = d->dt; p.B = d->B; p.C = d->C; p.A = d->A; p.D = d->D;
     return p;
+}
+
+void set_dt(Problem &p, int flags, const bimamba_dir *fwd, const bimamba_dir *bwd) {
+    p.dt_softplus = (flags & BIMAMBA_DT_SOFTPLUS) != 0;
+    p.dt_bias[0] = p.dt_softplus ? fwd->dt_bias : nullptr;
+    p.dt_bias[1] = p.dt_softplus && bwd ? bwd->dt_bias : nullptr;
 }
 
 struct ProfRecord {
@@ -333,6 +339,7 @@ int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
     p.has_bwd = bwd != nullptr;
     p.dir[0] = to_ptrs(fwd);
     p.dir[1] = bwd ? to_ptrs(bwd) : to_ptrs(fwd);
+    set_dt(p, s->flags, fwd, bwd);
     p.cu_dev = nullptr;
     p.seq_idx = nullptr;
     p.nseq = cu_seqlens ? nseq : 0;
@@ -434,6 +441,7 @@ int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
     p.has_bwd = true;
     p.dir[0] = to_ptrs(fwd);
     p.dir[1] = to_ptrs(bwd);
+    set_dt(p, s->flags, fwd, bwd);
     p.cu_dev = nullptr; p.seq_idx = nullptr; p.nseq = 0;
     p.init_state = st->data;
     p.final_state = commit ? st->data : nullptr;
@@ -465,6 +473,8 @@ int bimamba_ssd_bwd_workspace_size(const bimamba_shape *s, int has_bwd, size_t *
     if (!bwd_supported(s->headdim, s->d_state))
         return fail(BIMAMBA_EUNSUPPORTED, "backward: headdim %d / d_state %d not in {16, 64} x {16, 128}",
                     s->headdim, s->d_state);
+    if (s->flags)
+        return fail(BIMAMBA_EUNSUPPORTED, "backward: dt is taken as the forward used it (no BIMAMBA_DT_SOFTPLUS)");
     *bytes = bwd_workspace(s->batch, s->seqlen, s->nheads, s->headdim, s->d_state, has_bwd ? 2 : 1);
     return BIMAMBA_OK;
 }
@@ -477,6 +487,8 @@ int bimamba_ssd_bwd(const bimamba_shape *s, const bimamba_dir *fwd, const bimamb
     if (!bwd_supported(s->headdim, s->d_state))
         return fail(BIMAMBA_EUNSUPPORTED, "backward: headdim %d / d_state %d not in {16, 64} x {16, 128}",
                     s->headdim, s->d_state);
+    if (s->flags)
+        return fail(BIMAMBA_EUNSUPPORTED, "backward: dt is taken as the forward used it (no BIMAMBA_DT_SOFTPLUS)");
     const bool empty = s->seqlen == 0;
     if ((rc = check_dir(fwd, "forward", empty))) return rc;
     if (bwd && (rc = check_dir(bwd, "reverse", empty))) return rc;

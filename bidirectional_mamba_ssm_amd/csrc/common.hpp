@@ -20,6 +20,13 @@ __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
     return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }
 
+// dt as the scan uses it when a direction carries its pre-activation:
+// softplus(v) = max(v, 0) + log1p(e^{-|v|}) (no overflow, no loss for
+// very negative v)
+__device__ __forceinline__ float softplus_dt(float v) {
+    return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v)));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     __device__ __forceinline__ static float load(const float *p, size_t i) { return p[i]; }

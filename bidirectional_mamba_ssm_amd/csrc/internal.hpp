@@ -23,6 +23,8 @@ struct Problem {
     const float *init_state;   // [units][H][P][N] or nullptr
     float *final_state;        // [units][H][P][N] or nullptr
     float *y;
+    bool dt_softplus;          // dt holds the pre-activation: softplus(dt + bias)
+    const float *dt_bias[2];   // with dt_softplus: [H] per direction, or nullptr (zero)
 };
 
 // Profiling hooks (api.cpp): no-ops unless bimamba_profile_begin() is active

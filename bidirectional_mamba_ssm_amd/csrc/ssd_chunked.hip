@@ -145,6 +145,7 @@ struct SegArgs {
     const float *init_state;  // [batch][H][P][N] or nullptr
     float *final_state;       // [batch][H][P][N] or nullptr
     float *y;                 // [batch][L][H][P]
+    const float *dt_bias[2];  // with the softplus step size: [H] per direction or nullptr
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -272,6 +273,8 @@ struct StateSmem {
     float run[2];   // running sum of a from the outgoing edge, by step parity
 };
 
+// SP: dt holds the step size's pre-activation (softplus(dt + bias) is used)
+template <bool SP>
 __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
     const int seg = blockIdx.x, d = blockIdx.y;
     const int b = blockIdx.z / a.H, h = blockIdx.z % a.H;
@@ -283,6 +286,7 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
     const uint16_t *DT = (const uint16_t *)dp.dt;
     const uint16_t *Bm = (const uint16_t *)dp.B;
     const float Ah = dp.A[h];
+    const float dtb = SP && a.dt_bias[d] ? a.dt_bias[d][h] : 0.f;
     __shared__ __attribute__((aligned(16))) StateSmem sm;
 
     const int edge = d == 0 ? t1 - 1 : t0;
@@ -317,6 +321,7 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
             float at = 0.f, dtt = 0.f;
             if (in) {
                 dtt = bf2f(DT[tok(a, b, s0 + pos) * a.H + h]);
+                if (SP) dtt = softplus_dt(dtt + dtb);
                 at = dtt * Ah;
             }
             const float incl = wave_scan(at);
@@ -547,13 +552,14 @@ __device__ __forceinline__ void store_run(V *dst, bool asc, int lane, const V (&
 // masks, staged x and B; one barrier. Wave 0 scans a over the chunk in the
 // walking direction, wave 1 toward the outgoing edge, each with Q/64 tokens
 // per lane; the tile-edge values come from lane shuffles.
-template <int Q, bool PACKED, int WB = 0>
+template <int Q, bool PACKED, int WB = 0, bool SP = false>
 __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q, PACKED, WB> &ld,
                            int d, int b, int h, int c0, int len) {
     using LD = ChunkLoads<Q, PACKED, WB>;
     constexpr int TPL = LD::TPL;
     const int lane = lane_id(), wv = wave_in<WB>();
     const float Ah = a.dir[d].A[h];
+    const float dtb = SP && a.dt_bias[d] ? a.dt_bias[d][h] : 0.f;
     ld.sx.store(len, sm.xs);
     ld.sb.store(len, sm.bn);
     if (wv < 2) {
@@ -574,6 +580,7 @@ __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q, PACKE
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
             dtf[i] = LD::pos_of(d, wv, lane, i) < len ? bf2f(ld.dtv[i]) : 0.f;
+            if (SP) dtf[i] = LD::pos_of(d, wv, lane, i) < len ? softplus_dt(dtf[i] + dtb) : 0.f;
             at[i] = dtf[i] * Ah;
             run += (double)at[i];
             cs[i] = run;
@@ -1025,7 +1032,7 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[Cfg<Q>::N
 }
 
 // One direction's walk over the segment's chunks.
-template <int Q, bool PACKED, int D>
+template <int Q, bool PACKED, int D, bool SP>
 __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h, int grp, bool add) {
     constexpr int NQ = Cfg<Q>::NQ;
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
@@ -1070,7 +1077,7 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
     for (int s = 0; s < nch; ++s) {
         int c0, len;
         chunk_at(s, c0, len);
-        chunk_prep<Q, PACKED>(a, sm, ld, D, b, h, c0, len);
+        chunk_prep<Q, PACKED, 0, SP>(a, sm, ld, D, b, h, c0, len);
         if (Q == 256) {
             // two tiles per wave: each fetches its own inputs (holding them
             // through the state update would cost spills)
@@ -1111,7 +1118,7 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
     }
 }
 
-template <int Q, bool PACKED>
+template <int Q, bool PACKED, bool SP>
 __global__ void __launch_bounds__(Cfg<Q>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 k_seg_out(const SegArgs a) {
     // XCD-aware order: consecutive workgroup ids go round-robin over the 8
@@ -1131,10 +1138,10 @@ k_seg_out(const SegArgs a) {
     __shared__ __attribute__((aligned(16))) OutSmem<Q> sm;
     if (a.ndir == 2) {
         // reverse first, then the forward pass adds its part
-        seg_pass<Q, PACKED, 1>(a, sm, b, seg, h, grp, false);
-        seg_pass<Q, PACKED, 0>(a, sm, b, seg, h, grp, true);
+        seg_pass<Q, PACKED, 1, SP>(a, sm, b, seg, h, grp, false);
+        seg_pass<Q, PACKED, 0, SP>(a, sm, b, seg, h, grp, true);
     } else {
-        seg_pass<Q, PACKED, 0>(a, sm, b, seg, h, grp, false);
+        seg_pass<Q, PACKED, 0, SP>(a, sm, b, seg, h, grp, false);
     }
 }
 
@@ -1169,7 +1176,7 @@ __device__ __forceinline__ void store_tile(const SegArgs &a, int b, int h, int l
 }
 
 // D: the half's direction; WB: its first wave (0 for D = 1, 4 for D = 0)
-template <int D, int WB>
+template <int D, int WB, bool SP>
 __device__ void dual_half(const SegArgs &a, OutSmem<64> &sm, float *ex, int b, int h, int grp) {
     constexpr int Q = 64, NQ = Cfg<Q>::NQ;
     const int lane = lane_id(), w = wave_in<WB>(), g4 = lane >> 4, l16 = lane & 15;
@@ -1187,7 +1194,7 @@ __device__ void dual_half(const SegArgs &a, OutSmem<64> &sm, float *ex, int b, i
 #pragma unroll
     for (int q = 0; q < NQ; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
     if (src) publish_state<Q, WB>(sm, Hacc);
-    chunk_prep<Q, false, WB>(a, sm, ld, D, b, h, 0, len);   // barrier 1
+    chunk_prep<Q, false, WB, SP>(a, sm, ld, D, b, h, 0, len);   // barrier 1
     f32x4 acc[4];
     const bool mine = 16 * w < len;
     if (mine)
@@ -1216,6 +1223,7 @@ __device__ void dual_half(const SegArgs &a, OutSmem<64> &sm, float *ex, int b, i
     }
 }
 
+template <bool SP>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 k_dual_out(const SegArgs a) {
     // XCD-aware order as in k_seg_out
@@ -1227,8 +1235,8 @@ k_dual_out(const SegArgs a) {
     const int b = lin / a.H, h = lin % a.H;
     const int grp = h / (a.H / a.G);
     __shared__ __attribute__((aligned(16))) DualSmem sm;
-    if (wave_id() < 4) dual_half<1, 0>(a, sm.half[0], sm.ex, b, h, grp);
-    else dual_half<0, 4>(a, sm.half[1], sm.ex, b, h, grp);
+    if (wave_id() < 4) dual_half<1, 0, SP>(a, sm.half[0], sm.ex, b, h, grp);
+    else dual_half<0, 4, SP>(a, sm.half[1], sm.ex, b, h, grp);
 }
 
 int pick_ts(int batch, int L, int H, int Q) {
@@ -1237,11 +1245,11 @@ int pick_ts(int batch, int L, int H, int Q) {
     return ts < Q ? Q : ts;
 }
 
-template <int Q>
+template <int Q, bool SP>
 hipError_t launch_q(const SegArgs &a, hipStream_t s) {
     const int nd = a.ndir;
     if (a.nseg > 1) {
-        BM_LAUNCH("ssd_seg_state", k_seg_state, dim3(a.nseg, nd, a.batch * a.H), dim3(kThreads), 0,
+        BM_LAUNCH("ssd_seg_state", k_seg_state<SP>, dim3(a.nseg, nd, a.batch * a.H), dim3(kThreads), 0,
                   s, a);
         BM_LAUNCH("ssd_seg_scan", k_seg_scan, dim3(kP * kN / 256, a.H, a.batch * nd), dim3(256), 0,
                   s, a);
@@ -1249,13 +1257,13 @@ hipError_t launch_q(const SegArgs &a, hipStream_t s) {
     const int per_xcd = (a.batch * a.nseg * a.H + 7) / 8;
     if (Q == 64 && a.ndir == 2 && !a.seq && a.L <= 64) {
         // one chunk per row: both directions at once
-        BM_LAUNCH("ssd_dual_out", k_dual_out, dim3(per_xcd * 8), dim3(512), 0, s, a);
+        BM_LAUNCH("ssd_dual_out", k_dual_out<SP>, dim3(per_xcd * 8), dim3(512), 0, s, a);
         return hipGetLastError();
     }
     if (a.seq)
-        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true, SP>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
     else
-        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, false>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, false, SP>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1301,10 +1309,13 @@ hipError_t launch_chunked(const Problem &p, void *ws, hipStream_t s) {
     a.init_state = p.init_state;
     a.final_state = p.final_state;
     a.y = p.y;
+    a.dt_bias[0] = p.dt_bias[0];
+    a.dt_bias[1] = p.dt_bias[1];
+    const bool sp = p.dt_softplus;
     switch (p.Q) {
-        case 64: return launch_q<64>(a, s);
-        case 128: return launch_q<128>(a, s);
-        case 256: return launch_q<256>(a, s);
+        case 64: return sp ? launch_q<64, true>(a, s) : launch_q<64, false>(a, s);
+        case 128: return sp ? launch_q<128, true>(a, s) : launch_q<128, false>(a, s);
+        case 256: return sp ? launch_q<256, true>(a, s) : launch_q<256, false>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -38,6 +38,8 @@ struct SeqArgs {
     float *S;                 // [batch][2][nseg][H][P][N] segment states from zero
     float *Hin;               // [batch][2][nseg][H][P][N] segment incoming states
     float *tot;               // [batch][2][nseg][H] total of a over the segment
+    int dt_softplus;          // dt holds the pre-activation: softplus(dt + bias)
+    const float *dt_bias[2];  // [H] per direction, or nullptr (zero)
 };
 
 template <int N>
@@ -87,7 +89,9 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, i
         }
         for (int i = threadIdx.x; i < nsteps; i += blockDim.x) {
             const int t = d == 0 ? t0 + base + i : t1 - 1 - base - i;
-            sm.dt[i] = Elem<T>::load(DT, (row_tok + t) * H + h);
+            float dtv = Elem<T>::load(DT, (row_tok + t) * H + h);
+            if (a.dt_softplus) dtv = softplus_dt(dtv + (a.dt_bias[d] ? a.dt_bias[d][h] : 0.f));
+            sm.dt[i] = dtv;
         }
         __syncthreads();
         if (p < P) {
@@ -292,6 +296,9 @@ hipError_t launch_scan_seq(const Problem &p, void *ws, hipStream_t s) {
     a.init_state = p.init_state;
     a.final_state = p.final_state;
     a.y = p.y;
+    a.dt_softplus = p.dt_softplus;
+    a.dt_bias[0] = p.dt_bias[0];
+    a.dt_bias[1] = p.dt_bias[1];
     a.seg_len = p.L > 0 ? p.L : 1;
     a.nseg = 1;
     a.S = a.Hin = a.tot = nullptr;

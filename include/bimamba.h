@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define BIMAMBA_VERSION 1
+#define BIMAMBA_VERSION 2
 
 typedef enum {
     BIMAMBA_F32 = 0,   /* x, dt, B, C are float                        */
@@ -66,8 +66,14 @@ typedef struct {
     int ngroups;    /* G, divides H; head h reads B/C group h/(H/G)          */
     int chunk;      /* Q: 64, 128 or 256                                    */
     int dtype;      /* bimamba_dtype of x, dt, B, C                          */
-    int flags;      /* reserved, must be 0                                  */
+    int flags;      /* 0, or BIMAMBA_DT_SOFTPLUS                              */
 } bimamba_shape;
+/* Shape flag: each direction's dt holds the pre-activation of the step size
+ * and the scan uses softplus(dt + dt_bias[h]) (computed in fp32 as each dt
+ * is read; no stored copy). Mamba-2's step-size parameterization, the mixer
+ * the DiffuMamba pages name; the pages do not give it, so this is its
+ * plainest form (no clamping). bimamba_ssd_fwd and bimamba_block_step only. */
+#define BIMAMBA_DT_SOFTPLUS 1
 
 /* One direction's inputs, all read-only device pointers. The reverse
  * direction is given in the SAME (forward) time order; the library walks it
@@ -75,11 +81,15 @@ typedef struct {
 typedef struct {
     const void  *x;   /* [batch][seqlen][nheads][headdim]   dtype               */
     const void  *dt;  /* [batch][seqlen][nheads]            dtype, > 0, used as
-                         given (already softplus'd)                            */
+                         given (already softplus'd), or the pre-activation
+                         with BIMAMBA_DT_SOFTPLUS                              */
     const float *A;   /* [nheads] float, the per-head decay rate (<= 0)         */
     const void  *B;   /* [batch][seqlen][ngroups][d_state]  dtype               */
     const void  *C;   /* [batch][seqlen][ngroups][d_state]  dtype               */
     const float *D;   /* [nheads] float skip weights; NULL means D = 0          */
+    const float *dt_bias; /* [nheads] float, added to dt before softplus when
+                         the shape has BIMAMBA_DT_SOFTPLUS; NULL means 0;
+                         ignored otherwise                                     */
 } bimamba_dir;
 
 /* Opaque per-sequence forward-state cache (the block cache of cached block

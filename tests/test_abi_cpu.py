@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bimamba_version() == 1
+    assert lib.bimamba_version() == 2
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.bimamba_status_str(code)
     assert lib.bimamba_status_str(99) == b"unknown status"
@@ -212,6 +212,18 @@ def test_conv_arguments_rejected(lib):
     assert lib.bimamba_conv1d_workspace_size(ctypes.byref(s), 0, ctypes.byref(n)) == _abi.OK
     assert n.value == 0
     assert lib.bimamba_conv1d_workspace_size(ctypes.byref(s), -1, ctypes.byref(n)) == _abi.EINVAL
+
+
+def test_dt_softplus_flag(lib):
+    # defined for the forward and the block step only
+    assert call_fwd(lib, shape(flags=2), fake_dir()) == _abi.EINVAL
+    s = shape(flags=1)
+    n = ctypes.c_size_t(0)
+    assert lib.bimamba_ssd_bwd_workspace_size(ctypes.byref(s), 1, ctypes.byref(n)) == _abi.EUNSUPPORTED
+    g = _abi.Grad(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    f = fake_dir()
+    assert lib.bimamba_ssd_bwd(ctypes.byref(s), ctypes.byref(f), None, FAKE, ctypes.byref(g), None,
+                               FAKE, 1 << 30, None) == _abi.EUNSUPPORTED
 
 
 def test_gated_norm_validation(lib):

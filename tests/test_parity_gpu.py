@@ -486,3 +486,80 @@ def test_random_shapes(case):
         err, ok = within(fs, fs_ref, c["dtype"])
         print(f"  final state error {err:.3e}", flush=True)
         assert ok, f"final state error {err:.3e}"
+
+
+def _preact(f, seed):
+    """Replace dt by a pre-activation and a per-head bias whose softplus
+    follows the recipe's distribution (softplus(z - 2), z ~ N(0, 1))."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    batch, L, H = f["dt"].shape
+    d = dict(f)
+    d["dt"] = torch.randn(batch, L, H, generator=g, device=DEV).to(f["dt"].dtype).contiguous()
+    d["dt_bias"] = (torch.rand(H, generator=g, device=DEV) * 2 - 3).contiguous()
+    return d
+
+
+def _postact(d):
+    """The oracle's view: dt = softplus(raw + bias) in fp64."""
+    from oracle import dt as odt
+    e = dict(d)
+    e["dt"] = odt.preprocess_dt(d["dt"], d["dt_bias"])
+    del e["dt_bias"]
+    return e
+
+
+SOFTPLUS_CASES = [
+    # name, batch, L, H, P, N, G, dtype, chunk, seed
+    ("bf16_q256", 2, 300, 4, 64, 128, 1, "bf16", 256, 120),
+    ("bf16_q64", 1, 200, 4, 64, 128, 2, "bf16", 64, 121),
+    ("bf16_q128_segments", 1, 2100, 2, 64, 128, 1, "bf16", 128, 122),
+    ("f32_seq", 2, 150, 4, 16, 16, 1, "f32", 64, 123),
+    ("bf16_seq_small", 1, 257, 4, 16, 16, 1, "bf16", 64, 124),
+]
+
+
+@pytest.mark.parametrize("case", SOFTPLUS_CASES, ids=[c[0] for c in SOFTPLUS_CASES])
+@pytest.mark.parametrize("zero_D", [False, True], ids=["D", "D0"])
+def test_dt_softplus(case, zero_D):
+    """dt given as a pre-activation: the scan reads softplus(dt + dt_bias)."""
+    name, batch, L, H, P, N, G, dtype, chunk, seed = case
+    print(f"case {name} zero_D={zero_D}", flush=True)
+    f, b = synth.make_inputs(batch, L, H, P, N, G, dtype, seed, device=DEV)
+    f, b = _preact(f, seed + 1), _preact(b, seed + 2)
+    if zero_D:
+        f, b = _zero_D(f), _zero_D(b)
+    y = bm.ssd_fwd(f, b, chunk=chunk, dt_softplus=True)
+    torch.cuda.synchronize()
+    ref = oracle.bissd(_postact(f), _postact(b))
+    err, ok = within(y.double().cpu().numpy(), ref, dtype)
+    print(f"  error {err:.3e}", flush=True)
+    assert ok, f"{name}: error {err:.3e}"
+
+
+def test_dt_softplus_packed_and_block_step():
+    lens = [100, 0, 37, 300]
+    cu = synth.cu_seqlens_of(lens)
+    f, b = synth.make_inputs(1, cu[-1], 4, 64, 128, 1, "bf16", 125, device=DEV)
+    f, b = _preact(f, 126), _preact(b, 127)
+    y = bm.ssd_fwd(f, b, chunk=256, cu_seqlens=cu, dt_softplus=True)
+    torch.cuda.synchronize()
+    ref = oracle.bissd(_postact(f), _postact(b), cu_seqlens=cu)
+    err, ok = within(y.double().cpu().numpy(), ref, "bf16")
+    assert ok, f"packed: error {err:.3e}"
+    # block step from a carried state (single-chunk fast path)
+    st = bm.State(2, 4, 64, 128)
+    try:
+        g = torch.Generator(device=DEV).manual_seed(128)
+        st.tensor().copy_(torch.randn(2, 4, 64, 128, generator=g, device=DEV) * 0.5)
+        state0 = st.tensor().clone()
+        f, b = synth.make_inputs(2, 64, 4, 64, 128, 1, "bf16", 129, device=DEV)
+        f, b = _preact(f, 130), _preact(b, 131)
+        y = bm.block_step(st, f, b, commit=True, chunk=64, dt_softplus=True)
+        torch.cuda.synchronize()
+        ref, ref_state = oracle.block_step(state0, _postact(f), _postact(b), commit=True)
+        err, ok = within(y.double().cpu().numpy(), ref, "bf16")
+        assert ok, f"block step: error {err:.3e}"
+        err, ok = within(st.tensor().double().cpu().numpy(), ref_state, "bf16")
+        assert ok, f"block step state: error {err:.3e}"
+    finally:
+        st.free()
