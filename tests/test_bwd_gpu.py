@@ -15,13 +15,20 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 KEYS = ("x", "dt", "A", "B", "C", "D")
 # fp32 arithmetic from exact inputs. A gradient element is a sum of many
-# products of both signs (over the block, the state and, for dB and dC, the
-# heads of a group), so its rounding error scales with the size of those
-# products -- about the RMS of the whole array -- not with its own value:
-# the bar is max|g - g_ref| <= 1e-4 * RMS(g_ref) per array (measured: a few
-# 1e-6). The elementwise relative error with the 1 %-of-RMS floor is
-# printed beside it.
+# products of both signs (over the block, the carried state, and for dB and
+# dC the heads of a group), so its rounding error follows the size of those
+# products, not its own value, which cancellation can make arbitrarily
+# small (one token with three heads: dB is C times a sum over heads that
+# nearly cancels). The bar is therefore relative to S, the same gradient
+# with every contribution taken positive -- the oracle's adjoint on |x|,
+# |dy|, |B|, |C|, |D|, step sizes and decays being positive already -- for
+# dx, dB, dC, dA and dD: |g - g_ref| <= 1e-5 * S elementwise (fp32 sums
+# of up to a few thousand terms, tree- and matrix-core-accumulated, stay
+# well inside). ddt mixes a term of each sign by construction (A < 0), so
+# S does not bound it; it is held to max|g - g_ref| <= 1e-4 * RMS(g_ref).
+# The elementwise relative error with the 1 %-of-RMS floor is printed.
 TOL = 1e-4
+TOL_SUM = 1e-5
 
 
 def _dy(batch, L, H, P, seed):
@@ -29,17 +36,36 @@ def _dy(batch, L, H, P, seed):
     return torch.randn(batch, L, H, P, generator=g, device=DEV)
 
 
-def _compare(gpu, ref, tag):
+def _abs_scale(f, b, dy):
+    """Gradients with every contribution positive (bounds for all but ddt)."""
+    def ab(d):
+        if d is None:
+            return None
+        e = dict(d)
+        for k in ("x", "B", "C", "D"):
+            if e.get(k) is not None:
+                e[k] = e[k].abs()
+        return e
+    return oracle.bissd_bwd(ab(f), ab(b), dy.abs())
+
+
+def _compare(gpu, ref, tag, scale=None):
     worst, elem = {}, {}
     for k in KEYS:
         if gpu.get(k) is None:
             continue
         got = gpu[k].double().cpu().numpy()
         elem[k] = rel_err_f32(got, ref[k])
-        worst[k] = rms_err(got, ref[k]) if np.any(ref[k]) else float(np.max(np.abs(got), initial=0.0))
-    print(f"  {tag}: max|err|/RMS " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()) +
+        if k != "dt" and scale is not None:
+            # |err| / S against TOL_SUM
+            worst[k] = (float(np.max(np.abs(got - ref[k]) / np.maximum(scale[k], 1e-300),
+                                     initial=0.0)), TOL_SUM)
+            continue
+        err = rms_err(got, ref[k]) if np.any(ref[k]) else float(np.max(np.abs(got), initial=0.0))
+        worst[k] = (err, TOL)
+    print(f"  {tag}: max|err|/S (dt: /RMS) " + ", ".join(f"{k} {v[0]:.2e}" for k, v in worst.items()) +
           " | elementwise " + ", ".join(f"{k} {v:.1e}" for k, v in elem.items()), flush=True)
-    bad = {k: v for k, v in worst.items() if not v <= TOL}
+    bad = {k: v[0] for k, v in worst.items() if not v[0] <= v[1]}
     assert not bad, f"{tag}: {bad}"
 
 
@@ -67,9 +93,10 @@ def test_bwd_parity(case, bidir):
     gf, gb = bm.ssd_bwd(f, b, dy)
     torch.cuda.synchronize()
     rf, rb = oracle.bissd_bwd(f, b, dy)
-    _compare(gf, rf, "forward stream")
+    sf, sb = _abs_scale(f, b, dy)
+    _compare(gf, rf, "forward stream", sf)
     if bidir:
-        _compare(gb, rb, "reverse stream")
+        _compare(gb, rb, "reverse stream", sb)
     else:
         assert gb is None
 
@@ -82,8 +109,9 @@ def test_bwd_without_D():
     gf, gb = bm.ssd_bwd(f, b, dy)
     torch.cuda.synchronize()
     rf, rb = oracle.bissd_bwd(f, b, dy)
-    _compare(gf, rf, "forward stream")
-    _compare(gb, rb, "reverse stream")
+    sf, sb = _abs_scale(f, b, dy)
+    _compare(gf, rf, "forward stream", sf)
+    _compare(gb, rb, "reverse stream", sb)
 
 
 def test_bwd_empty():
@@ -117,5 +145,43 @@ def test_bwd_layer_full_size():
     gf, gb = bm.ssd_bwd(f, b, dy)
     torch.cuda.synchronize()
     rf, rb = oracle.bissd_bwd(f, b, dy)
-    _compare(gf, rf, "forward stream")
-    _compare(gb, rb, "reverse stream")
+    sf, sb = _abs_scale(f, b, dy)
+    _compare(gf, rf, "forward stream", sf)
+    _compare(gb, rb, "reverse stream", sb)
+
+
+def _random_bwd_cases(n, seed):
+    """Seeded random backward problems: both supported head shapes, lengths
+    with ragged last blocks, grouped heads, one or both streams, D or not."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        P, N = [(64, 128), (16, 16), (64, 16), (16, 128)][k % 4]
+        G = int(rng.choice([1, 2]))
+        H = G * int(rng.integers(1, 4))
+        cases.append(dict(k=k, dtype=["bf16", "f32"][k % 2], P=P, N=N, G=G, H=H,
+                          batch=int(rng.integers(1, 3)),
+                          L=int(rng.choice([1, 3, 63, 64, 65, 129, 200, 333])),
+                          bidir=k % 3 != 2, with_D=k % 4 != 3, seed=2000 + k))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_bwd_cases(16, 91), ids=lambda c: f"r{c['k']}")
+def test_bwd_random_shapes(case):
+    c = case
+    print(f"random case {c}", flush=True)
+    f, b = synth.make_inputs(c["batch"], c["L"], c["H"], c["P"], c["N"], c["G"], c["dtype"],
+                             c["seed"], device=DEV)
+    if not c["with_D"]:
+        f["D"] = None
+        b["D"] = None
+    if not c["bidir"]:
+        b = None
+    dy = _dy(c["batch"], c["L"], c["H"], c["P"], c["seed"] + 1)
+    gf, gb = bm.ssd_bwd(f, b, dy)
+    torch.cuda.synchronize()
+    rf, rb = oracle.bissd_bwd(f, b, dy)
+    sf, sb = _abs_scale(f, b, dy)
+    _compare(gf, rf, "forward stream", sf)
+    if b is not None:
+        _compare(gb, rb, "reverse stream", sb)

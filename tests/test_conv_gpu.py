@@ -204,3 +204,36 @@ def test_block_step_with_conv():
     assert ok, f"block step after conv: error {err:.3e}"
     err, ok = within(_np(st.tensor()), st_new, "bf16")
     assert ok, f"committed state: error {err:.3e}"
+
+
+def _random_conv_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        H = int(rng.integers(1, 9))
+        P = int(rng.choice([3, 4, 8, 16, 64]))
+        G = int(rng.choice([1, 2]))
+        N = int(rng.choice([4, 5, 16, 128]))
+        cases.append(dict(k=k, H=H, P=P, G=G, N=N, W=int(rng.integers(2, 5)),
+                          dtype=["bf16", "f32"][k % 2], act=["silu", "none"][k % 3 == 2],
+                          batch=int(rng.integers(1, 4)),
+                          L=int(rng.choice([1, 2, 15, 16, 17, 64, 65, 100, 257])),
+                          bidir=k % 4 != 1, seed=3000 + k))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_conv_cases(20, 93), ids=lambda c: f"r{c['k']}")
+def test_conv_random_shapes(case):
+    c = case
+    print(f"random case {c}", flush=True)
+    ch = bm.conv_channels(c["H"], c["P"], c["G"], c["N"])
+    f, b = synth.make_conv_inputs(c["batch"], c["L"], ch, c["W"], c["dtype"], c["seed"],
+                                  device=DEV, bidirectional=c["bidir"])
+    fo, bo = bm.conv1d(f, b, c["H"], c["P"], c["G"], c["N"], activation=c["act"])
+    torch.cuda.synchronize()
+    dims = (c["H"], c["P"], c["G"], c["N"])
+    worst, ok = _check_dir(fo, f, False, dims, c["dtype"], c["act"])
+    assert ok, f"forward: {worst:.3f} delta outside"
+    if c["bidir"]:
+        worst, ok = _check_dir(bo, b, True, dims, c["dtype"], c["act"])
+        assert ok, f"reverse: {worst:.3f} delta outside"
