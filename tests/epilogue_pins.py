@@ -93,3 +93,40 @@ DT_PINS = {
     "dt_torch": (pin_dt_torch, 1e-9),
     "dt_identities": (pin_dt_identities, 1e-14),
 }
+
+
+# ---- the concatenating merge (oracle/merge.py)
+
+def _merge_draw(seed, rows=5, cin=3, cout=4):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((rows, cin)), rng.standard_normal((rows, cin)),
+            rng.standard_normal((cout, 2 * cin)), rng.standard_normal(cout))
+
+
+def pin_merge_loops(mod, seed=95):
+    """Explicit sums: out[t][o] = sum_c W[o][c] y_fwd[t][c] + W[o][cin + c] y_bwd[t][c] + b[o]."""
+    yf, yb, w, b = _merge_draw(seed)
+    got = mod.merge_linear(yf, yb, w, b)
+    worst = 0.0
+    for t in range(yf.shape[0]):
+        for o in range(w.shape[0]):
+            ref = b[o]
+            for c in range(yf.shape[1]):
+                ref += w[o][c] * yf[t][c] + w[o][yf.shape[1] + c] * yb[t][c]
+            worst = max(worst, abs(got[t][o] - ref))
+    return worst
+
+
+def pin_merge_torch(mod, seed=96):
+    """== torch.nn.functional.linear(cat(y_fwd, y_bwd), W, b) in fp64."""
+    yf, yb, w, b = _merge_draw(seed, rows=7, cin=6, cout=5)
+    got = mod.merge_linear(yf, yb, w, b)
+    ref = F.linear(torch.cat([torch.from_numpy(yf), torch.from_numpy(yb)], -1),
+                   torch.from_numpy(w), torch.from_numpy(b)).numpy()
+    return float(np.max(np.abs(got - ref)))
+
+
+MERGE_PINS = {
+    "merge_loops": (pin_merge_loops, 1e-13),
+    "merge_torch": (pin_merge_torch, 1e-13),
+}

@@ -259,3 +259,37 @@ def test_dt_pins_catch_mutant(name):
             if not (err <= tol):
                 caught.append(pin)
     assert caught, f"no pin catches mutant {name}"
+
+
+MERGE_SRC = open(os.path.join(os.path.dirname(oracle.__file__), "merge.py")).read()
+
+MERGE_MUTANTS = {
+    # the streams concatenated in the other order
+    "merge_order": ("cat = np.concatenate([yf, yb], axis=-1)", "cat = np.concatenate([yb, yf], axis=-1)"),
+    # bias dropped
+    "merge_no_bias": ("        out = out + b\n", "        out = out\n"),
+    # the streams summed instead of concatenated (first half of W only)
+    "merge_sum": ("    cat = np.concatenate([yf, yb], axis=-1)\n    out = cat @ w.T\n",
+                  "    out = (yf + yb) @ w[:, :yf.shape[-1]].T\n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MERGE_MUTANTS))
+def test_merge_pins_catch_mutant(name):
+    import types
+    from epilogue_pins import MERGE_PINS
+    a, b = MERGE_MUTANTS[name]
+    assert MERGE_SRC.count(a) == 1, f"mutation site for {name} not found once"
+    mod = types.ModuleType("merge_mutant")
+    exec(compile(MERGE_SRC.replace(a, b), "merge_mutant.py", "exec"), mod.__dict__)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin, (fn, tol) in MERGE_PINS.items():
+            try:
+                err = fn(mod)
+            except Exception:
+                caught.append(pin)
+                continue
+            if not (err <= tol):
+                caught.append(pin)
+    assert caught, f"no pin catches mutant {name}"

@@ -3,7 +3,7 @@ import pytest
 
 from bwd_pins import BWD_PINS
 from conv_pins import CONV_PINS
-from epilogue_pins import DT_PINS, EPILOGUE_PINS
+from epilogue_pins import DT_PINS, EPILOGUE_PINS, MERGE_PINS
 from oracle import epilogue
 from oracle import conv
 from pins import ALL_PINS
@@ -42,4 +42,12 @@ def test_dt_oracle_pin(name):
     from oracle import dt as odt
     fn, tol = DT_PINS[name]
     err = fn(odt)
+    assert err <= tol, f"pin {name}: error {err} > {tol}"
+
+
+@pytest.mark.parametrize("name", sorted(MERGE_PINS))
+def test_merge_oracle_pin(name):
+    from oracle import merge as omerge
+    fn, tol = MERGE_PINS[name]
+    err = fn(omerge)
     assert err <= tol, f"pin {name}: error {err} > {tol}"
