@@ -100,6 +100,8 @@ def parse():
                     help="only the training-backward line (one JSON object)")
     ap.add_argument("--epilogue-only", action="store_true",
                     help="only the gated-norm epilogue line (one JSON object)")
+    ap.add_argument("--merge-only", action="store_true",
+                    help="only the concatenating-merge lines (one JSON object)")
     ap.add_argument("--conv-only", action="store_true",
                     help="only the short-convolution line (one JSON object)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -254,6 +256,12 @@ def main():
         if args.calibrate_copy:
             calibrate_copy(torch, dev)
         print(json.dumps({"gated_norm_layer_1p3b_train": epilogue_bench(args, bm, synth, torch, dev, args.steps)}),
+              flush=True)
+        return
+    if args.merge_only:
+        if args.calibrate_copy:
+            calibrate_copy(torch, dev)
+        print(json.dumps({"merge_layer_1p3b_train": merge_bench(args, bm, synth, torch, dev, args.steps)}),
               flush=True)
         return
     if args.bwd_only:
@@ -411,6 +419,7 @@ def extras(args, bm, synth, torch, dev):
     res["conv1d_layer_1p3b_train"] = conv_bench(args, bm, synth, torch, dev, max(steps, 20))
     res["bwd_layer_1p3b_train"] = bwd_bench(args, bm, synth, torch, dev, max(3, steps // 4))
     res["gated_norm_layer_1p3b_train"] = epilogue_bench(args, bm, synth, torch, dev, max(steps, 20))
+    res["merge_layer_1p3b_train"] = merge_bench(args, bm, synth, torch, dev, max(steps, 20))
     return res
 
 
@@ -540,6 +549,65 @@ def epilogue_bench(args, bm, synth, torch, dev, steps):
         res["cpu_oracle"] = {"tokens_per_s": round(n / sec, 1), "kind": "oracle",
                              "sample": f"{n} of {rows} tokens, numpy fp64, {sec:.2f} s"}
     del y, z, w, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def merge_bench(args, bm, synth, torch, dev, steps):
+    """The concatenating merge at the layer's shape. (1) The scan with the
+    two streams written apart (8 x 1024 tokens, 64 heads x 64, d_state 128,
+    bf16), against the summing scan. (2) The Linear merge over the block
+    outputs: 8 x 1024 tokens, 2 x 2048 channels in, 2048 out (d_model 2048),
+    bf16 weight, fp32 streams and output; bound by the matrix cores
+    (2 x 4096 x 2048 flops per token)."""
+    w = synth.WORKLOADS["layer_1p3b_train"]
+    f, b = synth.make_workload(w, device=dev)
+    tok = w.batch * w.seqlen
+    yf = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+    yb = torch.empty_like(yf)
+    shape = bm.make_shape(f["x"], f["B"], w.chunk)
+    ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=dev)
+    fn = lambda: bm.ssd_fwd_streams(f, b, chunk=w.chunk, y_fwd=yf, y_bwd=yb, workspace=ws)  # noqa: E731
+    ms_s, _, ker_s, dom_s = time_steps(bm, fn, steps, max(3, args.warmup // 10), torch)
+    fn = lambda: bm.ssd_fwd(f, b, chunk=w.chunk, y=yf, workspace=ws)  # noqa: E731
+    ms_f, _, _, _ = time_steps(bm, fn, steps, max(3, args.warmup // 10), torch)
+    # one more fp32 output of y: the streams written apart
+    bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2) + w.nheads * w.headdim * 4
+    res = {"streams": {"workload": "scan with the streams kept apart, 8 x 1024 tokens, 64 heads x 64, "
+                                   "d_state 128, bf16",
+                       "tokens_per_s": round(tok / (ms_s / 1e3), 1), "ms_per_step": round(ms_s, 4),
+                       "ms_per_step_summed_scan": round(ms_f, 4),
+                       "roofline": roofline_for(ker_s, dom_s, bpt * tok)}}
+    del f, b, yf, yb, ws
+    torch.cuda.empty_cache()
+
+    rows, cin, cout = tok, 2048, 2048
+    g = torch.Generator(device=dev).manual_seed(109)
+    yf = torch.randn(rows, cin, generator=g, device=dev)
+    yb = torch.randn(rows, cin, generator=g, device=dev)
+    wt = (torch.randn(cout, 2 * cin, generator=g, device=dev) / (2 * cin) ** 0.5).to(torch.bfloat16)
+    bias = torch.randn(cout, generator=g, device=dev)
+    out = torch.empty(rows, cout, dtype=torch.float32, device=dev)
+    fn = lambda: bm.merge_linear(yf, yb, wt, bias, out=out)  # noqa: E731
+    ms, _, ker, dom = time_steps(bm, fn, steps, max(3, args.warmup // 10), torch)
+    flops = 2 * rows * 2 * cin * cout
+    nbytes = rows * (2 * cin + cout) * 4 + cout * 2 * cin * 2 + cout * 4
+    m = mfma_for(ker, dom, flops)
+    m["bound"] = "mfma"
+    res["linear"] = {"workload": f"Linear merge, {rows} tokens, 2 x {cin} -> {cout}, bf16 weight, "
+                                "fp32 streams and output",
+                     "tokens_per_s": round(rows / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+                     "roofline": m, "hbm": roofline_for(ker, dom, nbytes)}
+    if not args.no_cpu_baseline:
+        from oracle import merge as omerge
+        n = 512
+        a, c, wc, bc = yf[:n].cpu(), yb[:n].cpu(), wt.float().cpu(), bias.cpu()
+        t0 = time.perf_counter()
+        omerge.merge_linear(a, c, wc, bc)
+        sec = time.perf_counter() - t0
+        res["linear"]["cpu_oracle"] = {"tokens_per_s": round(n / sec, 1), "kind": "oracle",
+                                       "sample": f"{n} of {rows} tokens, numpy fp64, {sec:.2f} s"}
+    del yf, yb, wt, bias, out
     torch.cuda.empty_cache()
     return res
 

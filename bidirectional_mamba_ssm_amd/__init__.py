@@ -186,6 +186,65 @@ def ssd_bwd(fwd, bwd, dy, grads=None, workspace=None, stream=None):
     return gf, gb
 
 
+def ssd_fwd_streams(fwd, bwd, chunk=256, cu_seqlens=None, init_state=None,
+                    final_state=None, y_fwd=None, y_bwd=None, workspace=None, stream=None):
+    """bimamba_ssd_fwd_streams: the two streams' outputs kept apart.
+    Returns (y_fwd, y_bwd), float32 [b,L,H,P] each."""
+    x = fwd["x"]
+    dims = _dims(fwd)
+    batch, L, H, P, G, N = dims
+    shape = make_shape(x, fwd["B"], chunk)
+    dev = _cuda_device(x)
+    fd = _dir(fwd, x.dtype, dims, dev, "fwd")
+    bd = _dir(bwd, x.dtype, dims, dev, "bwd")
+    cu_arr, nseq = None, 0
+    if cu_seqlens is not None:
+        vals = [int(v) for v in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+        nseq = len(vals) - 1
+        cu_arr = (ctypes.c_int32 * len(vals))(*vals)
+    units = nseq if cu_seqlens is not None else batch
+    for t, name in ((init_state, "init_state"), (final_state, "final_state")):
+        if t is not None:
+            _check(t, name, (units, H, P, N), torch.float32, dev)
+    outs = []
+    for t, name in ((y_fwd, "y_fwd"), (y_bwd, "y_bwd")):
+        if t is None:
+            t = torch.empty(x.shape, dtype=torch.float32, device=dev)
+        _check(t, name, (batch, L, H, P), torch.float32, dev)
+        outs.append(t)
+    need = workspace_size(shape, nseq)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _abi.check(lib().bimamba_ssd_fwd_streams(
+        ctypes.byref(shape), ctypes.byref(fd), ctypes.byref(bd), cu_arr, nseq,
+        _ptr(init_state), _ptr(final_state), _ptr(outs[0]), _ptr(outs[1]),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return outs[0], outs[1]
+
+
+def merge_linear(y_fwd, y_bwd, weight, bias=None, out=None, stream=None):
+    """bimamba_merge_linear: W [y_fwd ; y_bwd] + bias per token. y_fwd,
+    y_bwd float32 [..., cin]; weight bf16 [cout, 2 cin]; bias float32 [cout]
+    or None. Returns float32 [..., cout]."""
+    dev = _cuda_device(y_fwd)
+    cin = y_fwd.shape[-1]
+    rows = y_fwd.numel() // cin if cin else 0
+    cout = weight.shape[0]
+    _check(y_fwd, "y_fwd", tuple(y_fwd.shape), torch.float32, dev)
+    _check(y_bwd, "y_bwd", tuple(y_fwd.shape), torch.float32, dev)
+    _check(weight, "weight", (cout, 2 * cin), torch.bfloat16, dev)
+    if bias is not None:
+        _check(bias, "bias", (cout,), torch.float32, dev)
+    oshape = tuple(y_fwd.shape[:-1]) + (cout,)
+    if out is None:
+        out = torch.empty(oshape, dtype=torch.float32, device=dev)
+    _check(out, "out", oshape, torch.float32, dev)
+    _abi.check(lib().bimamba_merge_linear(rows, cin, cout, _ptr(y_fwd), _ptr(y_bwd), _ptr(weight),
+                                          _ptr(bias), _ptr(out), _stream(stream)))
+    return out
+
+
 class State:
     """Library-owned forward-state cache: float [nslots, H, P, N] on the GPU."""
 

@@ -300,11 +300,16 @@ int bimamba_ssd_workspace_size(const bimamba_shape *s, int nseq, size_t *bytes) 
     return BIMAMBA_OK;
 }
 
-int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
-                    const bimamba_dir *bwd, const int32_t *cu_seqlens, int nseq,
-                    const float *init_state, float *final_state, float *y,
-                    void *workspace, size_t workspace_bytes,
-                    bimamba_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward scan. y2 == nullptr: y = sum of the streams; else y receives
+// the reverse stream and y2 the forward stream.
+int ssd_fwd_impl(const bimamba_shape *s, const bimamba_dir *fwd,
+                 const bimamba_dir *bwd, const int32_t *cu_seqlens, int nseq,
+                 const float *init_state, float *final_state, float *y, float *y2,
+                 void *workspace, size_t workspace_bytes, bimamba_stream stream) {
     int rc = check_shape(s, false);
     if (rc) return rc;
     const bool empty = s->seqlen == 0;
@@ -346,6 +351,7 @@ int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
     p.init_state = init_state;
     p.final_state = final_state;
     p.y = y;
+    p.y2 = y2;
 
     hipError_t e;
     if (cu_seqlens) {
@@ -366,6 +372,35 @@ int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
         return hip_fail(e, "scan launch");
     }
     return BIMAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
+                    const bimamba_dir *bwd, const int32_t *cu_seqlens, int nseq,
+                    const float *init_state, float *final_state, float *y,
+                    void *workspace, size_t workspace_bytes,
+                    bimamba_stream stream) {
+    return ssd_fwd_impl(s, fwd, bwd, cu_seqlens, nseq, init_state, final_state, y, nullptr,
+                        workspace, workspace_bytes, stream);
+}
+
+int bimamba_ssd_fwd_streams(const bimamba_shape *s, const bimamba_dir *fwd,
+                            const bimamba_dir *bwd, const int32_t *cu_seqlens, int nseq,
+                            const float *init_state, float *final_state, float *y_fwd,
+                            float *y_bwd, void *workspace, size_t workspace_bytes,
+                            bimamba_stream stream) {
+    if (!bwd) return fail(BIMAMBA_EINVAL, "both streams are required");
+    if (!s) return fail(BIMAMBA_EINVAL, "shape is NULL");
+    if (s->flags) return fail(BIMAMBA_EUNSUPPORTED, "streams kept apart: no shape flag is supported");
+    const bool empty = s->seqlen == 0;
+    if (!empty && (!y_fwd || !y_bwd)) return fail(BIMAMBA_EINVAL, "y_fwd and y_bwd are required");
+    if (!aligned16(y_fwd)) return fail(BIMAMBA_EINVAL, "y_fwd must be 16-byte aligned");
+    if (y_fwd == y_bwd && !empty) return fail(BIMAMBA_EINVAL, "y_fwd and y_bwd must differ");
+    return ssd_fwd_impl(s, fwd, bwd, cu_seqlens, nseq, init_state, final_state, y_bwd, y_fwd,
+                        workspace, workspace_bytes, stream);
 }
 
 int bimamba_state_alloc(bimamba_state **out, int nslots, int nheads, int headdim,
@@ -446,6 +481,7 @@ int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
     p.init_state = st->data;
     p.final_state = commit ? st->data : nullptr;
     p.y = y;
+    p.y2 = nullptr;
     // the block is one segment of its row: the chunked kernels need no
     // workspace then (each workgroup reads its slice of the cache before it
     // writes it back, so the in-place update is safe)
@@ -648,6 +684,34 @@ int bimamba_gated_norm(long long rows, int channels, int group_size, int dtype,
     a.out = out;
     hipError_t e = launch_gated_norm(a, dtype == BIMAMBA_BF16, (hipStream_t)stream);
     return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "launching the gated norm");
+}
+
+int bimamba_merge_linear(long long rows, int cin, int cout, const float *y_fwd,
+                         const float *y_bwd, const void *weight, const float *bias,
+                         float *out, bimamba_stream stream) {
+    if (rows < 0) return fail(BIMAMBA_EINVAL, "rows %lld < 0", rows);
+    if (rows > (1LL << 31) - 1) return fail(BIMAMBA_EUNSUPPORTED, "rows %lld exceed 2^31-1", rows);
+    if (cin <= 0 || cin % 32) return fail(BIMAMBA_EUNSUPPORTED, "cin %d: need a positive multiple of 32", cin);
+    if (cout <= 0 || cout % 16) return fail(BIMAMBA_EUNSUPPORTED, "cout %d: need a positive multiple of 16", cout);
+    if (cin > (1 << 24) || cout > (1 << 24)) return fail(BIMAMBA_EUNSUPPORTED, "cin/cout too large");
+    if (rows == 0) return BIMAMBA_OK;
+    if (!y_fwd || !y_bwd || !weight || !out)
+        return fail(BIMAMBA_EINVAL, "y_fwd, y_bwd, weight and out are required");
+    if (!aligned16(y_fwd) || !aligned16(y_bwd) || !aligned16(weight) || !aligned16(out))
+        return fail(BIMAMBA_EINVAL, "y_fwd, y_bwd, weight and out must be 16-byte aligned");
+    if ((uintptr_t)bias & 3u) return fail(BIMAMBA_EINVAL, "bias must be 4-byte aligned");
+    MergeArgs a;
+    memset(&a, 0, sizeof a);
+    a.rows = rows;
+    a.cin = cin;
+    a.cout = cout;
+    a.yf = y_fwd;
+    a.yb = y_bwd;
+    a.w = weight;
+    a.bias = bias;
+    a.out = out;
+    hipError_t e = launch_merge(a, (hipStream_t)stream);
+    return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "launching the merge");
 }
 
 }  // extern "C"

@@ -25,6 +25,8 @@ struct Problem {
     float *y;
     bool dt_softplus;          // dt holds the pre-activation: softplus(dt + bias)
     const float *dt_bias[2];   // with dt_softplus: [H] per direction, or nullptr (zero)
+    float *y2;                 // streams kept apart: y gets the reverse stream, y2 the
+                               // forward stream; nullptr: y gets their sum
 };
 
 // Profiling hooks (api.cpp): no-ops unless bimamba_profile_begin() is active
@@ -73,6 +75,18 @@ struct BwdProblem {
 bool bwd_supported(int P, int N);
 size_t bwd_workspace(int batch, int L, int H, int P, int N, int ndir);
 hipError_t launch_bwd(const BwdProblem &p, void *ws, hipStream_t s);
+
+// merge.hip: concatenating merge of the two streams (Linear on [y_fwd ; y_bwd])
+struct MergeArgs {
+    long long rows;
+    int cin, cout;
+    int mblk, nblk;            // token panels, output blocks (set by launch_merge)
+    const float *yf, *yb;      // [rows][cin]
+    const void *w;             // bf16 [cout][2 cin]
+    const float *bias;         // [cout] or nullptr
+    float *out;                // [rows][cout]
+};
+hipError_t launch_merge(MergeArgs a, hipStream_t s);
 
 // epilogue.hip: gated RMS norm of the scan's output
 struct EpiArgs {

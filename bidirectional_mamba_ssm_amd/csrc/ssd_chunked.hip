@@ -146,6 +146,7 @@ struct SegArgs {
     float *final_state;       // [batch][H][P][N] or nullptr
     float *y;                 // [batch][L][H][P]
     const float *dt_bias[2];  // with the softplus step size: [H] per direction or nullptr
+    float *y2;                // streams kept apart: the forward stream's output
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -819,7 +820,8 @@ __device__ __forceinline__ void diag_block(f32x4 (&acc)[4], const OutSmem<Q> &sm
 // times 0, and a row past the end only reaches its own (unstored) output.
 // STORE: adds the reverse pass's rows (add) and writes y; otherwise hands
 // this direction's sums for the tile back in `out`.
-template <int Q, bool PACKED, int D, bool STORE = true>
+// Y2: the forward stream's output goes to y2 (streams kept apart)
+template <int Q, bool PACKED, int D, bool STORE = true, bool Y2 = false>
 __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, int c0, int len,
                          int it, bool has_state, float Dh, bool add, const TileIn &tin,
                          f32x4 *out = nullptr) {
@@ -960,7 +962,7 @@ __device__ void row_tile(const SegArgs &a, const OutSmem<Q> &sm, int b, int h, i
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[pt][r] += tin.prev[pt][r];
     }
-    float *ybase = a.y + (tok(a, b, c0) * a.H + h) * kP + l16;
+    float *ybase = (Y2 ? a.y2 : a.y) + (tok(a, b, c0) * a.H + h) * kP + l16;
     const uint32_t ystride = (uint32_t)(a.H * kP);
     uint32_t yoff[4];
 #pragma unroll
@@ -1032,7 +1034,7 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[Cfg<Q>::N
 }
 
 // One direction's walk over the segment's chunks.
-template <int Q, bool PACKED, int D, bool SP>
+template <int Q, bool PACKED, int D, bool SP, bool Y2 = false>
 __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h, int grp, bool add) {
     constexpr int NQ = Cfg<Q>::NQ;
     const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
@@ -1086,12 +1088,12 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
                 const int it = tile_of<Q>(w, k);
                 TileIn t;
                 tile_fetch<D>(t, a, b, h, grp, c0, len, it, add);
-                if (16 * it < len) row_tile<Q, PACKED, D>(a, sm, b, h, c0, len, it, has_state, Dh, add, t);
+                if (16 * it < len) row_tile<Q, PACKED, D, true, Y2>(a, sm, b, h, c0, len, it, has_state, Dh, add, t);
             }
         } else {
             const int it = tile_of<Q>(w, 0);
             if (it >= 0 && 16 * it < len)
-                row_tile<Q, PACKED, D>(a, sm, b, h, c0, len, it, has_state, Dh, add, ld.tin);
+                row_tile<Q, PACKED, D, true, Y2>(a, sm, b, h, c0, len, it, has_state, Dh, add, ld.tin);
         }
         const bool last = s == nch - 1;
         {
@@ -1118,7 +1120,7 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
     }
 }
 
-template <int Q, bool PACKED, bool SP>
+template <int Q, bool PACKED, bool SP, bool SPLIT = false>
 __global__ void __launch_bounds__(Cfg<Q>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 k_seg_out(const SegArgs a) {
     // XCD-aware order: consecutive workgroup ids go round-robin over the 8
@@ -1139,7 +1141,10 @@ k_seg_out(const SegArgs a) {
     if (a.ndir == 2) {
         // reverse first, then the forward pass adds its part
         seg_pass<Q, PACKED, 1, SP>(a, sm, b, seg, h, grp, false);
-        seg_pass<Q, PACKED, 0, SP>(a, sm, b, seg, h, grp, true);
+        if (SPLIT)
+            seg_pass<Q, PACKED, 0, SP, true>(a, sm, b, seg, h, grp, false);
+        else
+            seg_pass<Q, PACKED, 0, SP>(a, sm, b, seg, h, grp, true);
     } else {
         seg_pass<Q, PACKED, 0, SP>(a, sm, b, seg, h, grp, false);
     }
@@ -1245,7 +1250,7 @@ int pick_ts(int batch, int L, int H, int Q) {
     return ts < Q ? Q : ts;
 }
 
-template <int Q, bool SP>
+template <int Q, bool SP, bool SPLIT = false>
 hipError_t launch_q(const SegArgs &a, hipStream_t s) {
     const int nd = a.ndir;
     if (a.nseg > 1) {
@@ -1255,15 +1260,15 @@ hipError_t launch_q(const SegArgs &a, hipStream_t s) {
                   s, a);
     }
     const int per_xcd = (a.batch * a.nseg * a.H + 7) / 8;
-    if (Q == 64 && a.ndir == 2 && !a.seq && a.L <= 64) {
+    if (Q == 64 && a.ndir == 2 && !a.seq && a.L <= 64 && !SPLIT) {
         // one chunk per row: both directions at once
         BM_LAUNCH("ssd_dual_out", k_dual_out<SP>, dim3(per_xcd * 8), dim3(512), 0, s, a);
         return hipGetLastError();
     }
     if (a.seq)
-        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true, SP>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, true, SP, SPLIT>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
     else
-        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, false, SP>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
+        BM_LAUNCH("ssd_seg_out", (k_seg_out<Q, false, SP, SPLIT>), dim3(per_xcd * 8), dim3(Cfg<Q>::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1311,7 +1316,18 @@ hipError_t launch_chunked(const Problem &p, void *ws, hipStream_t s) {
     a.y = p.y;
     a.dt_bias[0] = p.dt_bias[0];
     a.dt_bias[1] = p.dt_bias[1];
+    a.y2 = p.y2;
     const bool sp = p.dt_softplus;
+    // streams kept apart (no softplus step size in that mode)
+    if (p.y2) {
+        if (sp || a.ndir != 2) return hipErrorInvalidValue;
+        switch (p.Q) {
+            case 64: return launch_q<64, false, true>(a, s);
+            case 128: return launch_q<128, false, true>(a, s);
+            case 256: return launch_q<256, false, true>(a, s);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (p.Q) {
         case 64: return sp ? launch_q<64, true>(a, s) : launch_q<64, false>(a, s);
         case 128: return sp ? launch_q<128, true>(a, s) : launch_q<128, false>(a, s);

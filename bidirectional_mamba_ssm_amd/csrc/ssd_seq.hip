@@ -40,6 +40,7 @@ struct SeqArgs {
     float *tot;               // [batch][2][nseg][H] total of a over the segment
     int dt_softplus;          // dt holds the pre-activation: softplus(dt + bias)
     const float *dt_bias[2];  // [H] per direction, or nullptr (zero)
+    float *y2;                // streams kept apart: the forward stream's output
 };
 
 template <int N>
@@ -59,6 +60,8 @@ struct SeqSmem {
 template <typename T, int N, int MODE>
 __device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, int h, int g,
                       int t0, int t1, float (&st)[N]) {
+    // the output this direction writes (or adds into)
+    float *Y = (a.y2 && d == 0) ? a.y2 : a.y;
     const int p = threadIdx.x;
     const int H = a.H, P = a.P, G = a.G;
     const DirPtrs &dp = a.dir[d];
@@ -85,7 +88,7 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, i
             const int t = d == 0 ? t0 + base + s : t1 - 1 - base - s;
             const size_t o = ((row_tok + t) * H + h) * P + pp;
             sm.x[s][pp] = Elem<T>::load(X, o);
-            if (MODE == 2) sm.y[s][pp] = a.y[o];
+            if (MODE == 2) sm.y[s][pp] = Y[o];
         }
         for (int i = threadIdx.x; i < nsteps; i += blockDim.x) {
             const int t = d == 0 ? t0 + base + i : t1 - 1 - base - i;
@@ -117,7 +120,7 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, i
             for (int i = threadIdx.x; i < nsteps * P; i += blockDim.x) {
                 const int s = i / P, pp = i - s * P;
                 const int t = d == 0 ? t0 + base + s : t1 - 1 - base - s;
-                a.y[((row_tok + t) * H + h) * P + pp] = sm.y[s][pp];
+                Y[((row_tok + t) * H + h) * P + pp] = sm.y[s][pp];
             }
         }
     }
@@ -153,7 +156,8 @@ __global__ void __launch_bounds__(kMaxP) k_scan_seq(const SeqArgs a) {
     if (a.ndir == 2) {
 #pragma unroll
         for (int n = 0; n < N; ++n) st[n] = 0.f;
-        walk<T, N, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
+        if (a.y2) walk<T, N, 1>(a, sm, 1, row_tok, h, g, t0, t1, st);
+        else walk<T, N, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
     }
 }
 
@@ -221,7 +225,7 @@ __global__ void __launch_bounds__(kMaxP) k_seq_seg_out(const SeqArgs a) {
 #pragma unroll
             for (int n = 0; n < N; ++n) st[n] = 0.f;
         }
-        if (d == 0) walk<T, N, 1>(a, sm, 0, row_tok, h, g, t0, t1, st);
+        if (d == 0 || a.y2) walk<T, N, 1>(a, sm, d, row_tok, h, g, t0, t1, st);
         else walk<T, N, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
     }
 }
@@ -297,6 +301,7 @@ hipError_t launch_scan_seq(const Problem &p, void *ws, hipStream_t s) {
     a.final_state = p.final_state;
     a.y = p.y;
     a.dt_softplus = p.dt_softplus;
+    a.y2 = p.y2;
     a.dt_bias[0] = p.dt_bias[0];
     a.dt_bias[1] = p.dt_bias[1];
     a.seg_len = p.L > 0 ? p.L : 1;

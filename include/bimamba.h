@@ -131,6 +131,36 @@ int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
                     void *workspace, size_t workspace_bytes,
                     bimamba_stream stream);
 
+/* The same scan with the two streams kept apart, for the concatenating merge
+ * (DiffuMamba blog, "network architecture": the block concatenates the
+ * forward and the flipped-back reverse output and applies a Linear layer;
+ * see bimamba_merge_linear). y_fwd receives the forward stream, y_bwd the
+ * reverse stream, each float [batch][seqlen][nheads][headdim], fully
+ * overwritten; bwd is required; no shape flag. Other arguments as
+ * bimamba_ssd_fwd. */
+int bimamba_ssd_fwd_streams(const bimamba_shape *s, const bimamba_dir *fwd,
+                            const bimamba_dir *bwd, const int32_t *cu_seqlens, int nseq,
+                            const float *init_state, float *final_state, float *y_fwd,
+                            float *y_bwd, void *workspace, size_t workspace_bytes,
+                            bimamba_stream stream);
+/* The concatenating merge (DiffuMamba blog, "network architecture": a Linear
+ * layer from the concatenated streams back to one width):
+ *
+ *   out[t] = W [y_fwd[t] ; y_bwd[t]] + bias,  W: cout x (2 cin)
+ *
+ *  rows      tokens (>= 0)
+ *  cin       channels of each stream, a multiple of 32
+ *  cout      output channels, a multiple of 16
+ *  y_fwd     float [rows][cin], y_bwd float [rows][cin]
+ *  weight    bf16 [cout][2 cin] (row o: cin weights of the forward stream,
+ *            then cin of the reverse stream: a Linear layer's layout)
+ *  bias      float [cout], or NULL
+ *  out       float [rows][cout]; must not overlap the inputs
+ * On the bf16 matrix cores: the streams are rounded to bf16 (nearest even)
+ * as they are read; products accumulate in fp32. Pointers 16-byte aligned. */
+int bimamba_merge_linear(long long rows, int cin, int cout, const float *y_fwd,
+                         const float *y_bwd, const void *weight, const float *bias,
+                         float *out, bimamba_stream stream);
 /* State cache objects. alloc allocates and zeroes (synchronously) nslots
  * forward states; reset zeroes the listed slots (HOST int32 slot indices,
  * NULL = all) asynchronously on `stream`; data returns the device pointer

@@ -249,3 +249,44 @@ def test_gated_norm_validation(lib):
         assert call(**{k: None}) == _abi.EINVAL, k
         assert call(**{k: FAKE + 4}) == _abi.EINVAL, k
     assert call(rows=0, y=None, z=None, weight=None, out=None) == _abi.OK
+
+
+def test_streams_validation(lib):
+    s, f, b = shape(), fake_dir(), fake_dir()
+
+    def call(s=s, f=f, b=b, yf=FAKE, yb=FAKE + 4096):
+        return lib.bimamba_ssd_fwd_streams(ctypes.byref(s) if s is not None else None,
+                                           ctypes.byref(f) if f is not None else None,
+                                           ctypes.byref(b) if b is not None else None,
+                                           None, 0, None, None, yf, yb, None, 0, None)
+    assert call(b=None) == _abi.EINVAL
+    assert call(s=None) == _abi.EINVAL
+    assert call(s=shape(flags=_abi.DT_SOFTPLUS)) == _abi.EUNSUPPORTED
+    assert call(yf=None) == _abi.EINVAL
+    assert call(yb=None) == _abi.EINVAL
+    assert call(yb=FAKE) == _abi.EINVAL
+    assert call(yf=FAKE + 4) == _abi.EINVAL
+    assert call(yb=FAKE + 4100) == _abi.EINVAL
+    assert call(s=shape(dtype=7)) == _abi.EINVAL
+
+
+def test_merge_validation(lib):
+    f = lib.bimamba_merge_linear
+    ok = dict(rows=4, cin=64, cout=32, yf=FAKE, yb=FAKE, w=FAKE, bias=None, out=FAKE)
+
+    def call(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return f(d["rows"], d["cin"], d["cout"], d["yf"], d["yb"], d["w"], d["bias"],
+                 d["out"], None)
+    assert call(rows=-1) == _abi.EINVAL
+    assert call(rows=1 << 31) == _abi.EUNSUPPORTED
+    assert call(cin=48) == _abi.EUNSUPPORTED
+    assert call(cin=0) == _abi.EUNSUPPORTED
+    assert call(cout=24) == _abi.EUNSUPPORTED
+    assert call(cout=-16) == _abi.EUNSUPPORTED
+    for k in ("yf", "yb", "w", "out"):
+        assert call(**{k: None}) == _abi.EINVAL, k
+        assert call(**{k: FAKE + 4}) == _abi.EINVAL, k
+    assert call(bias=FAKE + 2) == _abi.EINVAL
+    assert call(rows=0, yf=None, yb=None, w=None, out=None) == _abi.OK
