@@ -3,11 +3,10 @@
 // flipped-back reverse output and applies a Linear layer back to one width):
 //   out[t] = W [y_fwd[t] ; y_bwd[t]] + bias,   W: cout x (2 cin), bf16
 //
-// A bf16 matrix-core GEMM (v_mfma_f32_16x16x32_bf16). Workgroup tile 128
-// tokens x 128 outputs, four waves of 64 x 64 (4 x 4 MFMA tiles each), K in
-// steps of 32. The streams are fp32: each step's 128 x 32 slice is read as
-// 16-byte vectors, rounded to bf16 by the hardware conversion and staged in
-// LDS next to the weight slice (rows of 32 + 8 halves); the next step's
+// A bf16 matrix-core GEMM (v_mfma_f32_16x16x32_bf16), K in steps of 32 or
+// 64.
+// The streams are fp32: each step's slice is read as 16-byte vectors, rounded to bf16 by the hardware conversion and staged in
+// LDS next to the weight slice (rows of K step + 8 halves); the next step's
 // slices are loaded into registers while the current one is multiplied
 // (double-buffered LDS, one barrier per step). A K step never straddles the
 // two streams (cin is a multiple of 32). Workgroups of one token panel are
@@ -19,9 +18,7 @@
 namespace bm {
 namespace {
 
-constexpr int kMT = 128, kNT = 128, kKT = 32;
 constexpr int kMergeThreads = 256;
-constexpr int kRS = kKT + 8;   // LDS row stride in halves (80 bytes)
 
 typedef __bf16 mbf16x2 __attribute__((ext_vector_type(2)));
 typedef float mf32x2 __attribute__((ext_vector_type(2)));
@@ -31,9 +28,21 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, mbf16x2));
 }
 
+// Workgroup tile (32 TI) x (32 TJ): four waves in 2 x 2, each (16 TI) x
+// (16 TJ) as TI x TJ MFMA tiles. TI = TJ = 8 (256 x 256, 256 accumulator
+// registers per lane, one workgroup per CU) for large problems: per K element
+// it fetches 256 x 4 + 256 x 2 bytes for 2 x 256 x 256 flops, which the
+// per-CU load path sustains at the matrix-core rate; TI = TJ = 4 (128 x
+// 128) fills the chip on small ones.
+template <int TI, int TJ, int KT>
 __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kMT * kRS];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kNT * kRS];
+    constexpr int MT = 32 * TI, NT = 32 * TJ;
+    constexpr int kRS = KT + 8;           // LDS row stride in halves
+    constexpr int A4 = KT / 4, B8 = KT / 8;  // 16-byte vectors per slice row
+    constexpr int AV = MT * A4 / kMergeThreads;  // stream vectors per thread
+    constexpr int BV = NT * B8 / kMergeThreads;  // weight vectors per thread
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][MT * kRS];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][NT * kRS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
     // XCD-aware order: consecutive workgroup ids go to different XCDs, so
@@ -45,27 +54,27 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
     const int panel = (k / per_panel) * 8 + xcd;  // token panel of this workgroup
     const int nb = k % per_panel;
     if (panel >= a.mblk) return;
-    const int m0 = panel * kMT, n0 = nb * kNT;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int m0 = panel * MT, n0 = nb * NT;
+    const int wm = (wave >> 1) * (16 * TI), wn = (wave & 1) * (16 * TJ);
     const int K = 2 * a.cin;
     const uint16_t *W = (const uint16_t *)a.w;
 
-    float4 ra[4];
-    uint4 rb[2];
+    float4 ra[AV];
+    uint4 rb[BV];
     auto fetch = [&](int k0) {
         const bool first = k0 < a.cin;
         const float *src = first ? a.yf : a.yb;
         const int kk = first ? k0 : k0 - a.cin;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + kMergeThreads * i, r = e >> 3, c4 = e & 7;
+        for (int i = 0; i < AV; ++i) {
+            const int e = tid + kMergeThreads * i, r = e / A4, c4 = e % A4;
             const long long m = (long long)m0 + r;
             ra[i] = m < a.rows ? *(const float4 *)(src + m * a.cin + kk + 4 * c4)
                                : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int e = tid + kMergeThreads * i, r = e >> 2, c8 = e & 3;
+        for (int i = 0; i < BV; ++i) {
+            const int e = tid + kMergeThreads * i, r = e / B8, c8 = e % B8;
             const int n = n0 + r;
             rb[i] = n < a.cout ? *(const uint4 *)(W + (size_t)n * K + k0 + 8 * c8)
                                : make_uint4(0u, 0u, 0u, 0u);
@@ -73,50 +82,54 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
     };
     auto stash = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + kMergeThreads * i, r = e >> 3, c4 = e & 7;
+        for (int i = 0; i < AV; ++i) {
+            const int e = tid + kMergeThreads * i, r = e / A4, c4 = e % A4;
             *(uint2 *)&As[buf][r * kRS + 4 * c4] =
                 make_uint2(cvt2(ra[i].x, ra[i].y), cvt2(ra[i].z, ra[i].w));
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int e = tid + kMergeThreads * i, r = e >> 2, c8 = e & 3;
+        for (int i = 0; i < BV; ++i) {
+            const int e = tid + kMergeThreads * i, r = e / B8, c8 = e % B8;
             *(uint4 *)&Bs[buf][r * kRS + 8 * c8] = rb[i];
         }
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+        for (int j = 0; j < TJ; ++j) acc[i][j] = zero4();
     fetch(0);
     stash(0);
     __syncthreads();
-    const int nk = K / kKT;
+    const int nk = K / KT;
     for (int ks = 0; ks < nk; ++ks) {
         const int cur = ks & 1;
-        if (ks + 1 < nk) fetch((ks + 1) * kKT);
-        u32x4 av[4], bv[4];
+        if (ks + 1 < nk) fetch((ks + 1) * KT);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = *(const u32x4 *)&As[cur][(wm + 16 * i + l16) * kRS + 8 * g];
+        for (int kq = 0; kq < KT; kq += 32) {
+            u32x4 bv[TJ];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = *(const u32x4 *)&Bs[cur][(wn + 16 * j + l16) * kRS + 8 * g];
+            for (int j = 0; j < TJ; ++j)
+                bv[j] = *(const u32x4 *)&Bs[cur][(wn + 16 * j + l16) * kRS + kq + 8 * g];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < TI; ++i) {
+                const u32x4 av = *(const u32x4 *)&As[cur][(wm + 16 * i + l16) * kRS + kq + 8 * g];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(av[i], bv[j], acc[i][j]);
+                for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16x16x32(av, bv[j], acc[i][j]);
+            }
+        }
         if (ks + 1 < nk) stash(cur ^ 1);
         __syncthreads();
     }
     // out rows m0 + wm + 16 i + 4 g + r, column n0 + wn + 16 j + l16
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TJ; ++j) {
         const int n = n0 + wn + 16 * j + l16;
         if (n >= a.cout) continue;
         const float bn = a.bias ? a.bias[n] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const long long m = (long long)m0 + wm + 16 * i + 4 * g + r;
@@ -125,18 +138,28 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_merge(MergeArgs a, hipStream_t s) {
-    if (a.rows == 0) return hipSuccess;
-    a.mblk = (int)((a.rows + kMT - 1) / kMT);
-    a.nblk = (a.cout + kNT - 1) / kNT;
+template <int TI, int TJ, int KT>
+hipError_t launch_tile(MergeArgs a, hipStream_t s) {
+    a.mblk = (int)((a.rows + 32 * TI - 1) / (32 * TI));
+    a.nblk = (a.cout + 32 * TJ - 1) / (32 * TJ);
     // whole groups of eight panels, one per XCD
     const long long groups = (a.mblk + 7) / 8;
     const long long blocks = groups * 8 * a.nblk;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    BM_LAUNCH("merge_linear", k_merge, dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, a);
+    BM_LAUNCH("merge_linear", (k_merge<TI, TJ, KT>), dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(MergeArgs a, hipStream_t s) {
+    if (a.rows == 0) return hipSuccess;
+    // the large tile once it alone gives every CU a workgroup
+    const long long big = ((a.rows + 255) / 256) * ((a.cout + 255) / 256);
+    if (big >= 256) return launch_tile<8, 8, 32>(a, s);
+    // the small tile: K steps of 64 where they do not straddle the two
+    // streams (half the barriers; measured faster there, not on the large tile)
+    return a.cin % 64 == 0 ? launch_tile<4, 4, 64>(a, s) : launch_tile<4, 4, 32>(a, s);
 }
 
 }  // namespace bm

@@ -223,3 +223,15 @@ def test_streams_then_merge_end_to_end():
     err, ok = within(_np(out), ref, "bf16")
     print(f"  streams + merge error {err:.3e}", flush=True)
     assert ok, f"streams + merge: {err:.3e}"
+
+
+def test_merge_large_tile_ragged():
+    """The large-tile launch (256 x 256 workgroup tiles) with a ragged last
+    token panel, a ragged last output block and an odd number of 32-channel
+    K steps per stream; sampled rows against the oracle."""
+    rows, cin, cout = 8192 + 77, 1056, 2048 + 16
+    yf, yb, w, b = _merge_inputs(rows, cin, cout, 171)
+    out = bm.merge_linear(yf, yb, w, b)
+    torch.cuda.synchronize()
+    idx = torch.tensor([0, 255, 256, 4097, rows - 78, rows - 77, rows - 2, rows - 1], device=DEV)
+    _check_merge(yf[idx], yb[idx], w, b, out[idx], "large ragged sample")
