@@ -18,7 +18,6 @@
 namespace bm {
 namespace {
 
-constexpr int kMergeThreads = 256;
 
 typedef __bf16 mbf16x2 __attribute__((ext_vector_type(2)));
 typedef float mf32x2 __attribute__((ext_vector_type(2)));
@@ -28,15 +27,17 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, mbf16x2));
 }
 
-// Workgroup tile (32 TI) x (32 TJ): four waves in 2 x 2, each (16 TI) x
-// (16 TJ) as TI x TJ MFMA tiles. TI = TJ = 8 (256 x 256, 256 accumulator
-// registers per lane, one workgroup per CU) for large problems: per K element
-// it fetches 256 x 4 + 256 x 2 bytes for 2 x 256 x 256 flops, which the
-// per-CU load path sustains at the matrix-core rate; TI = TJ = 4 (128 x
-// 128) fills the chip on small ones.
-template <int TI, int TJ, int KT>
-__global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
-    constexpr int MT = 32 * TI, NT = 32 * TJ;
+// Workgroup tile (16 TI WM) x (16 TJ WN): WM x WN waves, each (16 TI) x
+// (16 TJ) as TI x TJ MFMA tiles. Large problems take 256 x 256 tiles with
+// eight waves of 128 x 64 (two waves per SIMD: one wave alone issues its
+// independent products at little more than half the matrix-core rate); per K
+// element such a tile fetches 256 x 4 + 256 x 2 bytes for 2 x 256 x 256
+// flops. Small ones take 128 x 128 tiles with four waves of 64 x 64, which
+// fill the chip.
+template <int TI, int TJ, int KT, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void k_merge(MergeArgs a) {
+    constexpr int kMergeThreads = 64 * WM * WN;
+    constexpr int MT = 16 * TI * WM, NT = 16 * TJ * WN;
     constexpr int kRS = KT + 8;           // LDS row stride in halves
     constexpr int A4 = KT / 4, B8 = KT / 8;  // 16-byte vectors per slice row
     constexpr int AV = MT * A4 / kMergeThreads;  // stream vectors per thread
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
     const int nb = k % per_panel;
     if (panel >= a.mblk) return;
     const int m0 = panel * MT, n0 = nb * NT;
-    const int wm = (wave >> 1) * (16 * TI), wn = (wave & 1) * (16 * TJ);
+    const int wm = (wave / WN) * (16 * TI), wn = (wave % WN) * (16 * TJ);
     const int K = 2 * a.cin;
     const uint16_t *W = (const uint16_t *)a.w;
 
@@ -108,16 +109,19 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
         if (ks + 1 < nk) fetch((ks + 1) * KT);
 #pragma unroll
         for (int kq = 0; kq < KT; kq += 32) {
-            u32x4 bv[TJ];
+            // every fragment of the step read at once, so that the reads'
+            // latency is paid once and not before each row of products
+            u32x4 av[TI], bv[TJ];
 #pragma unroll
             for (int j = 0; j < TJ; ++j)
                 bv[j] = *(const u32x4 *)&Bs[cur][(wn + 16 * j + l16) * kRS + kq + 8 * g];
 #pragma unroll
-            for (int i = 0; i < TI; ++i) {
-                const u32x4 av = *(const u32x4 *)&As[cur][(wm + 16 * i + l16) * kRS + kq + 8 * g];
+            for (int i = 0; i < TI; ++i)
+                av[i] = *(const u32x4 *)&As[cur][(wm + 16 * i + l16) * kRS + kq + 8 * g];
 #pragma unroll
-                for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16x16x32(av, bv[j], acc[i][j]);
-            }
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16x16x32(av[i], bv[j], acc[i][j]);
         }
         if (ks + 1 < nk) stash(cur ^ 1);
         __syncthreads();
@@ -138,15 +142,16 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
     }
 }
 
-template <int TI, int TJ, int KT>
+template <int TI, int TJ, int KT, int WM, int WN>
 hipError_t launch_tile(MergeArgs a, hipStream_t s) {
-    a.mblk = (int)((a.rows + 32 * TI - 1) / (32 * TI));
-    a.nblk = (a.cout + 32 * TJ - 1) / (32 * TJ);
+    constexpr int MT = 16 * TI * WM, NT = 16 * TJ * WN;
+    a.mblk = (int)((a.rows + MT - 1) / MT);
+    a.nblk = (a.cout + NT - 1) / NT;
     // whole groups of eight panels, one per XCD
     const long long groups = (a.mblk + 7) / 8;
     const long long blocks = groups * 8 * a.nblk;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    BM_LAUNCH("merge_linear", (k_merge<TI, TJ, KT>), dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, a);
+    BM_LAUNCH("merge_linear", (k_merge<TI, TJ, KT, WM, WN>), dim3((unsigned)blocks), dim3(64 * WM * WN), 0, s, a);
     return hipGetLastError();
 }
 
@@ -156,10 +161,11 @@ hipError_t launch_merge(MergeArgs a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
     // the large tile once it alone gives every CU a workgroup
     const long long big = ((a.rows + 255) / 256) * ((a.cout + 255) / 256);
-    if (big >= 256) return launch_tile<8, 8, 32>(a, s);
-    // the small tile: K steps of 64 where they do not straddle the two
-    // streams (half the barriers; measured faster there, not on the large tile)
-    return a.cin % 64 == 0 ? launch_tile<4, 4, 64>(a, s) : launch_tile<4, 4, 32>(a, s);
+    if (big >= 256)
+        return a.cin % 64 == 0 ? launch_tile<8, 4, 64, 2, 4>(a, s) : launch_tile<8, 4, 32, 2, 4>(a, s);
+    // K steps of 64 where they do not straddle the two streams (half the
+    // barriers)
+    return a.cin % 64 == 0 ? launch_tile<4, 4, 64, 2, 2>(a, s) : launch_tile<4, 4, 32, 2, 2>(a, s);
 }
 
 }  // namespace bm
