@@ -699,7 +699,7 @@ int bimamba_merge_linear(long long rows, int cin, int cout, const float *y_fwd,
         return fail(BIMAMBA_EINVAL, "y_fwd, y_bwd, weight and out are required");
     if (!aligned16(y_fwd) || !aligned16(y_bwd) || !aligned16(weight) || !aligned16(out))
         return fail(BIMAMBA_EINVAL, "y_fwd, y_bwd, weight and out must be 16-byte aligned");
-    if ((uintptr_t)bias & 3u) return fail(BIMAMBA_EINVAL, "bias must be 4-byte aligned");
+    if (!aligned16(bias)) return fail(BIMAMBA_EINVAL, "bias must be 16-byte aligned");
     MergeArgs a;
     memset(&a, 0, sizeof a);
     a.rows = rows;

@@ -126,19 +126,36 @@ __global__ __launch_bounds__(64 * WM * WN) void k_merge(MergeArgs a) {
         if (ks + 1 < nk) stash(cur ^ 1);
         __syncthreads();
     }
-    // out rows m0 + wm + 16 i + 4 g + r, column n0 + wn + 16 j + l16
+    // The products leave row 4 g + r, column 16 j + l16 of each 16 x 16 tile
+    // in a lane; each wave turns its 16 x 64 strips into whole rows through
+    // LDS (the operand buffers are free after the last barrier) and writes
+    // 16-byte pieces, four rows of 256 bytes per instruction.
+    static_assert(TJ == 4, "the row write-out assumes 64-column wave strips");
+    constexpr int kSS = 64 + 4;   // staging row stride in floats
+    static_assert(sizeof(As) >= (size_t)(kMergeThreads / 64) * 16 * kSS * sizeof(float),
+                  "staging does not fit");
+    float *stg = reinterpret_cast<float *>(&As[0][0]) + wave * 16 * kSS;
+    const int rr = lane >> 4, cc = 4 * (lane & 15);
+    const int n = n0 + wn + cc;
+    float4 bn = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.bias && n < a.cout) bn = *(const float4 *)(a.bias + n);
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-        const int n = n0 + wn + 16 * j + l16;
-        if (n >= a.cout) continue;
-        const float bn = a.bias ? a.bias[n] : 0.f;
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const long long m = (long long)m0 + wm + 16 * i + 4 * g + r;
-                if (m < a.rows) a.out[m * a.cout + n] = acc[i][j][r] + bn;
-            }
+            for (int r = 0; r < 4; ++r) stg[(4 * g + r) * kSS + 16 * j + l16] = acc[i][j][r];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = rr + 4 * q;
+            const long long m = (long long)m0 + wm + 16 * i + row;
+            const float4 v = *(const float4 *)&stg[row * kSS + cc];
+            if (m < a.rows && n < a.cout)
+                *(float4 *)(a.out + m * a.cout + n) =
+                    make_float4(v.x + bn.x, v.y + bn.y, v.z + bn.z, v.w + bn.w);
+        }
+        __syncthreads();
     }
 }
 

@@ -289,4 +289,5 @@ def test_merge_validation(lib):
         assert call(**{k: None}) == _abi.EINVAL, k
         assert call(**{k: FAKE + 4}) == _abi.EINVAL, k
     assert call(bias=FAKE + 2) == _abi.EINVAL
+    assert call(bias=FAKE + 4) == _abi.EINVAL
     assert call(rows=0, yf=None, yb=None, w=None, out=None) == _abi.OK
