@@ -265,6 +265,8 @@ def main():
               flush=True)
         return
     if args.bwd_only:
+        if args.calibrate_copy:
+            calibrate_copy(torch, dev)
         print(json.dumps({"bwd_layer_1p3b_train": bwd_bench(args, bm, synth, torch, dev, args.steps)}),
               flush=True)
         return
