@@ -60,18 +60,30 @@ struct BwdArgs {
     float *dCp;    // [batch][ndir][H][L][N]
     float *dAp;    // [batch][ndir][H][nc]
     float *dDp;    // [batch][ndir][H][nc]
+    int head_loop; // the gradient kernel walks each group's heads (no dBp, dCp)
 };
 
 __device__ __forceinline__ int tok_of(int k, int L, bool rev) { return rev ? L - 1 - k : k; }
 
+// threadIdx.x; with LT behind an empty asm statement, a fresh value wherever
+// it is read, so that the compiler recomputes lane addresses inside the loop
+// over heads instead of hoisting them all out of it and running out of
+// registers (elsewhere the plain value lets it share them).
+template <bool LT>
+__device__ __forceinline__ int lane_tid() {
+    int t = threadIdx.x;
+    if (LT) asm volatile("" : "+v"(t));
+    return t;
+}
+
 // dt of the block's positions into dtv (zero past len) and the running sums
 // of a = dt*A into sv (fp64): one lane per position in wave 0 (a block is
 // one wave wide), a shuffle scan. Ends with a workgroup barrier.
-template <typename T>
+template <typename T, bool LT = false>
 __device__ void block_scan(const BwdArgs &a, const DirPtrs &d, size_t rowt, int h, int k0,
                            int len, bool rev, double *sv, float *dtv) {
     static_assert(kQ == 64, "one wave per block");
-    const int tid = threadIdx.x;
+    const int tid = lane_tid<LT>();
     if (tid < kQ) {
         const float dtr = tid < len
             ? Elem<T>::load((const T *)d.dt, (rowt + tok_of(k0 + tid, a.L, rev)) * a.H + h)
@@ -132,13 +144,13 @@ struct Rows {
     float v[VPT][4];
 };
 
-template <typename T, int W, int NT>
+template <typename T, bool LT = false, int W, int NT>
 __device__ __forceinline__ void fetch_rows(Rows<W, NT> &rw, const void *src, size_t rowt,
                                            size_t stride, size_t off, int k0, int len, int L,
                                            bool rev) {
 #pragma unroll
     for (int k = 0; k < Rows<W, NT>::VPT; ++k) {
-        const int e4 = threadIdx.x + k * NT;
+        const int e4 = lane_tid<LT>() + k * NT;
         const int r = e4 * 4 / W, c = e4 * 4 % W;
         if (e4 < Rows<W, NT>::NV && r < len) {
             ld4((const T *)src + (rowt + tok_of(k0 + r, L, rev)) * stride + off + c, rw.v[k]);
@@ -150,11 +162,11 @@ __device__ __forceinline__ void fetch_rows(Rows<W, NT> &rw, const void *src, siz
 }
 
 // Stores held rows into an LDS array [kQ][S], each row scaled by scale(r).
-template <int W, int NT, int S, class F>
+template <bool LT = false, int W, int NT, int S, class F>
 __device__ __forceinline__ void store_rows(const Rows<W, NT> &rw, float (*dst)[S], F scale) {
 #pragma unroll
     for (int k = 0; k < Rows<W, NT>::VPT; ++k) {
-        const int e4 = threadIdx.x + k * NT;
+        const int e4 = lane_tid<LT>() + k * NT;
         if (e4 < Rows<W, NT>::NV) {
             const int r = e4 * 4 / W, c = e4 * 4 % W;
             const float sc = scale(r);
@@ -171,11 +183,11 @@ struct Flat {
     float v[VPT][4];
 };
 
-template <int NP, int NT>
+template <bool LT = false, int NP, int NT>
 __device__ __forceinline__ void fetch_flat(Flat<NP, NT> &f, const float *src) {
 #pragma unroll
     for (int k = 0; k < Flat<NP, NT>::VPT; ++k) {
-        const int e4 = threadIdx.x + k * NT;
+        const int e4 = lane_tid<LT>() + k * NT;
         if (e4 < NP / 4) {
             ld4(src + 4 * e4, f.v[k]);
         } else {
@@ -185,11 +197,11 @@ __device__ __forceinline__ void fetch_flat(Flat<NP, NT> &f, const float *src) {
     }
 }
 
-template <int NP, int NT, int P, int S>
+template <int NP, int NT, int P, bool LT = false, int S>
 __device__ __forceinline__ void store_flat(const Flat<NP, NT> &f, float (*dst)[S]) {
 #pragma unroll
     for (int k = 0; k < Flat<NP, NT>::VPT; ++k) {
-        const int e4 = threadIdx.x + k * NT;
+        const int e4 = lane_tid<LT>() + k * NT;
         if (e4 < NP / 4) {
             const int e = 4 * e4;
             *(float4 *)&dst[e / P][e % P] = make_float4(f.v[k][0], f.v[k][1], f.v[k][2], f.v[k][3]);
@@ -201,9 +213,9 @@ __device__ __forceinline__ void store_flat(const Flat<NP, NT> &f, float (*dst)[S
 // (v_mfma_f32_16x16x4f32; lane l, g = l / 16, m = l % 16: A supplies
 // A[m][k + g], B supplies B[k + g][m], the result holds rows 4g .. 4g+3 of
 // column m). a(m, k) and b(k, m) read the operands (from LDS).
-template <class FA, class FB>
+template <bool LT = false, class FA, class FB>
 __device__ __forceinline__ f32x4 mm(FA a, FB b, int k0, int k1, f32x4 acc) {
-    const int l = threadIdx.x & 63, g = l >> 4, m = l & 15;
+    const int l = lane_tid<LT>() & 63, g = l >> 4, m = l & 15;
     for (int k = k0; k < k1; k += 4)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m, k + g), b(k + g, m), acc, 0, 0, 0);
     return acc;
@@ -318,17 +330,20 @@ struct GradSmem {
     float red[kGradThreads];
 };
 
-template <typename T, int P, int N>
-__global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
+// The gradients of one (row, stream, head, block). HSUM: the head's dB and
+// dC fragments are added to accb / accc (registers of the caller, which
+// walks the heads of the group in order: the same fp32 sums as the
+// separate head-sum kernel); else they go to the workspace.
+template <typename T, int P, int N, bool HSUM>
+__device__ __forceinline__ void grad_block(const BwdArgs &a, GradSmem<P, N> &sm, const int c,
+                                           const int h, const int dir, const int b, const bool first,
+                                           f32x4 *accb, f32x4 *accc) {
     constexpr int NT = kGradThreads, NW = NT / 64, NP = N * P;
     constexpr int LPR = NT / kQ;                              // lanes per position
     constexpr int TQ = kQ / 16, TN = N / 16, TP = P / 16;
     constexpr int XT = TQ * TP, XPW = (XT + NW - 1) / NW;     // (position, p) tiles
     constexpr int CT = TQ * TN, CPW = (CT + NW - 1) / NW;     // (position, n) tiles
     constexpr int LT = TQ * (TQ + 1) / 2;                     // lower (i, j) tiles
-    __shared__ __attribute__((aligned(16))) GradSmem<P, N> sm;
-    const int c = blockIdx.x, h = blockIdx.y;
-    const int dir = (int)(blockIdx.z % (unsigned)a.ndir), b = (int)(blockIdx.z / (unsigned)a.ndir);
     const bool rev = dir == 1;
     const DirPtrs d = rev ? a.bwd : a.fwd;
     const GradPtrs gr = rev ? a.gbwd : a.gfwd;
@@ -336,7 +351,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     const int k0 = c * kQ;
     const int len = min(kQ, a.L - k0);
     const size_t rowt = (size_t)b * a.L;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = lane_tid<HSUM>(), wave = tid >> 6, lane = tid & 63;
     const int gq = lane >> 4, lm = lane & 15;     // result rows 4gq .. 4gq+3, column lm
     const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
     const size_t so = (unit * a.nc + c) * (size_t)NP;
@@ -347,19 +362,19 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     {
         Rows<N, NT> rb, rc;
         Rows<P, NT> rx, ry;
-        fetch_rows<T>(rb, d.B, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
-        fetch_rows<T>(rc, d.C, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
-        fetch_rows<T>(rx, d.x, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
-        fetch_rows<float>(ry, a.dy, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
-        block_scan<T>(a, d, rowt, h, k0, len, rev, sm.sv, sm.dtv);
-        store_rows(rb, sm.Bs, [](int) { return 1.f; });
-        store_rows(rc, sm.Cs, [](int) { return 1.f; });
-        store_rows(rx, sm.Xs, [](int) { return 1.f; });
-        store_rows(ry, sm.Ys, [](int) { return 1.f; });
+        fetch_rows<T, HSUM>(rb, d.B, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+        fetch_rows<T, HSUM>(rc, d.C, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+        fetch_rows<T, HSUM>(rx, d.x, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
+        fetch_rows<float, HSUM>(ry, a.dy, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
+        block_scan<T, HSUM>(a, d, rowt, h, k0, len, rev, sm.sv, sm.dtv);
+        store_rows<HSUM>(rb, sm.Bs, [](int) { return 1.f; });
+        store_rows<HSUM>(rc, sm.Cs, [](int) { return 1.f; });
+        store_rows<HSUM>(rx, sm.Xs, [](int) { return 1.f; });
+        store_rows<HSUM>(ry, sm.Ys, [](int) { return 1.f; });
     }
     Flat<NP, NT> fhp, fdh;
-    fetch_flat(fhp, a.S + so);
-    fetch_flat(fdh, a.R + so);
+    fetch_flat<HSUM>(fhp, a.S + so);
+    fetch_flat<HSUM>(fdh, a.R + so);
     __syncthreads();
     const double send = sm.sv[len - 1];
     if (tid < kQ) {
@@ -375,9 +390,9 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
         const int it = t / TQ, jt = t % TQ;
         f32x4 G = {0.f, 0.f, 0.f, 0.f}, D = {0.f, 0.f, 0.f, 0.f};
         if (jt <= it) {
-            G = mm([&](int m, int k) { return sm.Cs[it * 16 + m][k]; },
+            G = mm<HSUM>([&](int m, int k) { return sm.Cs[it * 16 + m][k]; },
                    [&](int k, int m) { return sm.Bs[jt * 16 + m][k]; }, 0, N, G);
-            D = mm([&](int m, int k) { return sm.Ys[it * 16 + m][k]; },
+            D = mm<HSUM>([&](int m, int k) { return sm.Ys[it * 16 + m][k]; },
                    [&](int k, int m) { return sm.Xs[jt * 16 + m][k]; }, 0, P, D);
         }
         const int j = jt * 16 + lm;
@@ -425,7 +440,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
         if (t < XT) {
             const int jt = t / TP, pt = t % TP;
             // dxd_j = sum_{i >= j} M_ij dy_i
-            dxd[u] = mm([&](int m, int k) { return sm.u.q.Ms[k][jt * 16 + m]; },
+            dxd[u] = mm<HSUM>([&](int m, int k) { return sm.u.q.Ms[k][jt * 16 + m]; },
                         [&](int k, int m) { return sm.Ys[k][pt * 16 + m]; }, jt * 16, kQ, dxd[u]);
         }
     }
@@ -437,17 +452,17 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
         if (t < CT) {
             const int rt = t / TN, nt = t % TN;
             // dC_i = sum_{j <= i} (L o dM)_ij B_j
-            dcv[u] = mm([&](int m, int k) { return sm.u.q.Gs[rt * 16 + m][k]; },
+            dcv[u] = mm<HSUM>([&](int m, int k) { return sm.u.q.Gs[rt * 16 + m][k]; },
                         [&](int k, int m) { return sm.Bs[k][nt * 16 + m]; }, 0, rt * 16 + 16, dcv[u]);
             // dB_j = sum_{i >= j} (L o dM)_ij C_i
-            dbv[u] = mm([&](int m, int k) { return sm.u.q.Gs[k][rt * 16 + m]; },
+            dbv[u] = mm<HSUM>([&](int m, int k) { return sm.u.q.Gs[k][rt * 16 + m]; },
                         [&](int k, int m) { return sm.Cs[k][nt * 16 + m]; }, rt * 16, kQ, dbv[u]);
         }
     }
     __syncthreads();
 
     // ---- terms of the entering state Hp
-    store_flat<NP, NT, P>(fhp, sm.u.st.Hs);
+    store_flat<NP, NT, P, HSUM>(fhp, sm.u.st.Hs);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
             const int rt = t / TN, nt = t % TN;
             // dC_i += e^{s_i} Hp dy_i
             f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-            tmp = mm([&](int m, int k) { return sm.Ys[rt * 16 + m][k]; },
+            tmp = mm<HSUM>([&](int m, int k) { return sm.Ys[rt * 16 + m][k]; },
                      [&](int k, int m) { return sm.u.st.Hs[nt * 16 + m][k]; }, 0, P, tmp);
 #pragma unroll
             for (int r = 0; r < 4; ++r) dcv[u][r] = fmaf(sm.es[rt * 16 + 4 * gq + r], tmp[r], dcv[u][r]);
@@ -469,7 +484,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
             const int it = t / TP, pt = t % TP;
             // (C_i^T Hp)[p] dy_i[p], summed over p below
             f32x4 ch = {0.f, 0.f, 0.f, 0.f};
-            ch = mm([&](int m, int k) { return sm.Cs[it * 16 + m][k]; },
+            ch = mm<HSUM>([&](int m, int k) { return sm.Cs[it * 16 + m][k]; },
                     [&](int k, int m) { return sm.u.st.Hs[k][pt * 16 + m]; }, 0, N, ch);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -500,7 +515,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     __syncthreads();
 
     // ---- terms of the leaving-state gradient dHe
-    store_flat<NP, NT, P>(fdh, sm.u.st.Hs);
+    store_flat<NP, NT, P, HSUM>(fdh, sm.u.st.Hs);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < XPW; ++u) {
@@ -509,7 +524,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
             const int jt = t / TP, pt = t % TP;
             // (B_j^T dHe)[p]: dxd_j += e^{s_end - s_j} B_j^T dHe
             f32x4 bdh = {0.f, 0.f, 0.f, 0.f};
-            bdh = mm([&](int m, int k) { return sm.Bs[jt * 16 + m][k]; },
+            bdh = mm<HSUM>([&](int m, int k) { return sm.Bs[jt * 16 + m][k]; },
                      [&](int k, int m) { return sm.u.st.Hs[k][pt * 16 + m]; }, 0, N, bdh);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -526,7 +541,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
             const int rt = t / TN, nt = t % TN;
             // dB_j += e^{s_end - s_j} dt_j dHe x_j
             f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-            tmp = mm([&](int m, int k) { return sm.Xs[rt * 16 + m][k]; },
+            tmp = mm<HSUM>([&](int m, int k) { return sm.Xs[rt * 16 + m][k]; },
                      [&](int k, int m) { return sm.u.st.Hs[nt * 16 + m][k]; }, 0, P, tmp);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -545,12 +560,20 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     }
 
     // ---- per-head dB, dC into the workspace (staged in LDS over B and C,
-    // which are no longer read, then written a row at a time); dxd into LDS
+    // which are no longer read, then written a row at a time), or summed
+    // over the heads in registers; dxd into LDS
+    if (HSUM) {
+#pragma unroll
+        for (int u = 0; u < CPW; ++u) {
+            accb[u] = first ? dbv[u] : accb[u] + dbv[u];
+            accc[u] = first ? dcv[u] : accc[u] + dcv[u];
+        }
+    }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
         const int t = wave + u * NW;
-        if (t < CT) {
+        if (!HSUM && t < CT) {
             const int rt = t / TN, nt = t % TN;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -569,7 +592,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
         }
     }
     __syncthreads();
-    {
+    if (!HSUM) {
         const size_t pb = unit * (size_t)a.L * N;
         for (int e4 = tid; e4 < len * (N / 4); e4 += NT) {
             const int row = e4 / (N / 4), cc = (e4 % (N / 4)) * 4;
@@ -627,6 +650,57 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
     }
 }
 
+// One workgroup per (block, head, row and stream); dB, dC per head.
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kGradThreads) void k_bwd_grad(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) GradSmem<P, N> sm;
+    const int dir = (int)(blockIdx.z % (unsigned)a.ndir), b = (int)(blockIdx.z / (unsigned)a.ndir);
+    grad_block<T, P, N, false>(a, sm, blockIdx.x, blockIdx.y, dir, b, false, nullptr, nullptr);
+}
+
+// One workgroup per (block, group, row and stream), walking the group's
+// heads in order; dB, dC summed over them in place.
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kGradThreads) void k_bwd_grad_heads(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) GradSmem<P, N> sm;
+    const int dir = (int)(blockIdx.z % (unsigned)a.ndir), b = (int)(blockIdx.z / (unsigned)a.ndir);
+    constexpr int NT = kGradThreads, NW = NT / 64, TQ = kQ / 16, TN = N / 16;
+    constexpr int CT = TQ * TN, CPW = (CT + NW - 1) / NW;
+    const int hg = a.H / a.G, g = blockIdx.y, h0 = g * hg, c = blockIdx.x;
+    f32x4 accb[CPW], accc[CPW];
+    for (int k = 0; k < hg; ++k) {
+        if (k) __syncthreads();   // the previous head's last phase reads the LDS rows
+        grad_block<T, P, N, true>(a, sm, c, h0 + k, dir, b, k == 0, accb, accc);
+    }
+    // the group's dB, dC of the block: staged over B and C in LDS, then
+    // written a row at a time
+    const bool rev = dir == 1;
+    const GradPtrs gr = rev ? a.gbwd : a.gfwd;
+    const int k0 = c * kQ, len = min(kQ, a.L - k0);
+    const size_t rowt = (size_t)b * a.L;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4, lm = lane & 15;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+        const int t = wave + u * NW;
+        if (t < CT) {
+            const int rt = t / TN, nt = t % TN;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sm.Bs[rt * 16 + 4 * gq + r][nt * 16 + lm] = accb[u][r];
+                sm.Cs[rt * 16 + 4 * gq + r][nt * 16 + lm] = accc[u][r];
+            }
+        }
+    }
+    __syncthreads();
+    for (int e4 = tid; e4 < len * (N / 4); e4 += NT) {
+        const int row = e4 / (N / 4), cc = (e4 % (N / 4)) * 4;
+        const size_t o = ((rowt + tok_of(k0 + row, a.L, rev)) * a.G + g) * N + cc;
+        *(float4 *)(gr.dB + o) = *(const float4 *)&sm.Bs[row][cc];
+        *(float4 *)(gr.dC + o) = *(const float4 *)&sm.Cs[row][cc];
+    }
+}
+
 // dB, dC of one stream: sums over the heads of each group, in head order.
 __global__ __launch_bounds__(256) void k_bwd_sum_bc(BwdArgs a, int N, size_t total) {
     const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -674,10 +748,15 @@ hipError_t launch_pn(BwdArgs &a, hipStream_t s) {
         BM_LAUNCH("bwd_state", (k_bwd_state<T, P, N>), grid, dim3(kStateThreads), 0, s, a);
         const dim3 pgrid((N * P + 255) / 256, a.H, a.batch * a.ndir);
         BM_LAUNCH("bwd_pass", k_bwd_pass, pgrid, dim3(256), 0, s, a, N * P);
-        BM_LAUNCH("bwd_grad", (k_bwd_grad<T, P, N>), grid, dim3(kGradThreads), 0, s, a);
-        const size_t total = (size_t)a.batch * a.L * a.G * N;
-        const dim3 sgrid((unsigned)((total + 255) / 256), a.ndir);
-        BM_LAUNCH("bwd_sum_bc", k_bwd_sum_bc, sgrid, dim3(256), 0, s, a, N, total);
+        if (a.head_loop) {
+            const dim3 ggrid(a.nc, a.G, a.batch * a.ndir);
+            BM_LAUNCH("bwd_grad", (k_bwd_grad_heads<T, P, N>), ggrid, dim3(kGradThreads), 0, s, a);
+        } else {
+            BM_LAUNCH("bwd_grad", (k_bwd_grad<T, P, N>), grid, dim3(kGradThreads), 0, s, a);
+            const size_t total = (size_t)a.batch * a.L * a.G * N;
+            const dim3 sgrid((unsigned)((total + 255) / 256), a.ndir);
+            BM_LAUNCH("bwd_sum_bc", k_bwd_sum_bc, sgrid, dim3(256), 0, s, a, N, total);
+        }
     }
     BM_LAUNCH("bwd_sum_ad", k_bwd_sum_ad, dim3((a.H + 63) / 64, a.ndir), dim3(64), 0, s, a);
     return hipGetLastError();
@@ -698,16 +777,26 @@ struct BwdLayout {
 
 size_t al(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Whether the gradient kernel walks the heads of each group: once the
+// (block, row, stream) workgroups alone cover the CUs (one gradient
+// workgroup fits per CU), walking the heads costs no parallelism and removes
+// the per-head dB, dC arrays and their sum.
+bool head_loop(int batch, int L, int ndir) {
+    const long long nc = (L + kQ - 1) / kQ;
+    return nc * batch * ndir >= 256;
+}
+
 BwdLayout layout(int batch, int L, int H, int P, int N, int ndir) {
     const size_t nc = (size_t)(L + kQ - 1) / kQ;
     const size_t units = (size_t)batch * ndir * H;
+    const size_t per_head = head_loop(batch, L, ndir) ? 0 : units * (size_t)L * N * sizeof(float);
     BwdLayout w;
     size_t off = 0;
     w.S = off; off += al(units * nc * N * P * sizeof(float));
     w.R = off; off += al(units * nc * N * P * sizeof(float));
     w.lg = off; off += al(units * nc * sizeof(double));
-    w.dBp = off; off += al(units * (size_t)L * N * sizeof(float));
-    w.dCp = off; off += al(units * (size_t)L * N * sizeof(float));
+    w.dBp = off; off += al(per_head);
+    w.dCp = off; off += al(per_head);
     w.dAp = off; off += al(units * nc * sizeof(float));
     w.dDp = off; off += al(units * nc * sizeof(float));
     w.total = off;
@@ -735,6 +824,7 @@ hipError_t launch_bwd(const BwdProblem &p, void *ws, hipStream_t s) {
     a.G = p.G;
     a.ndir = p.has_bwd ? 2 : 1;
     a.nc = (p.L + kQ - 1) / kQ;
+    a.head_loop = head_loop(p.batch, p.L, a.ndir);
     const BwdLayout w = layout(p.batch, p.L, p.H, p.P, p.N, a.ndir);
     char *base = (char *)ws;
     a.S = (float *)(base + w.S);

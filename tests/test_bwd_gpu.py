@@ -185,3 +185,49 @@ def test_bwd_random_shapes(case):
     _compare(gf, rf, "forward stream", sf)
     if b is not None:
         _compare(gb, rb, "reverse stream", sb)
+
+
+# Shapes with at least 256 (block, row, stream) workgroups take the gradient
+# kernel that walks the heads of each group and sums dB, dC over them in
+# place; smaller ones keep one workgroup per head and a separate head sum.
+HEAD_LOOP_CASES = [
+    # name, batch, L, H, P, N, G, dtype, bidir, seed
+    ("bf16_groups_ragged_bi", 8, 1000, 4, 64, 128, 2, "bf16", True, 83),
+    ("f32_ragged_fwd_only", 16, 1001, 3, 16, 16, 1, "f32", False, 84),
+]
+
+
+@pytest.mark.parametrize("case", HEAD_LOOP_CASES, ids=[c[0] for c in HEAD_LOOP_CASES])
+def test_bwd_head_loop(case):
+    name, batch, L, H, P, N, G, dtype, bidir, seed = case
+    print(f"head-loop case {name}", flush=True)
+    f, b = synth.make_inputs(batch, L, H, P, N, G, dtype, seed, device=DEV)
+    if not bidir:
+        b = None
+    dy = _dy(batch, L, H, P, seed + 1000)
+    gf, gb = bm.ssd_bwd(f, b, dy)
+    torch.cuda.synchronize()
+    rf, rb = oracle.bissd_bwd(f, b, dy)
+    sf, sb = _abs_scale(f, b, dy)
+    _compare(gf, rf, "forward stream", sf)
+    if bidir:
+        _compare(gb, rb, "reverse stream", sb)
+
+
+def test_bwd_head_loop_matches_per_head_form():
+    """A batch that takes the head-walking gradient kernel against each row
+    alone (too few workgroups: one per head and a separate head sum): the
+    per-token gradients are the same numbers (both forms add the heads in
+    order from zero)."""
+    batch, L, H, P, N, G = 8, 1000, 4, 64, 128, 2
+    f, b = synth.make_inputs(batch, L, H, P, N, G, "bf16", 85, device=DEV)
+    dy = _dy(batch, L, H, P, 86)
+    gf, gb = bm.ssd_bwd(f, b, dy)
+    for r in (0, 5):
+        fr = {k: (v[r:r + 1].contiguous() if v.dim() > 1 else v) for k, v in f.items()}
+        br = {k: (v[r:r + 1].contiguous() if v.dim() > 1 else v) for k, v in b.items()}
+        sf, sb = bm.ssd_bwd(fr, br, dy[r:r + 1].contiguous())
+        torch.cuda.synchronize()
+        for whole, one in ((gf, sf), (gb, sb)):
+            for k in ("x", "dt", "B", "C"):
+                assert torch.equal(whole[k][r:r + 1], one[k]), (r, k)
