@@ -458,6 +458,10 @@ def block_step_bench(args, bm, synth, torch, dev, steps):
         msg = graph_step_ms(fn, torch)
         out[key]["ms_per_step_graph"] = round(msg, 5)
         out[key]["hbm_roofline_frac_graph"] = round(per_seq * nseq / (msg / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+        # the same step through a plan bound once (no per-call argument checks)
+        plan = bm.BlockStepPlan(st, f, b, commit=False, chunk=64, y=y)
+        msp, _, _, _ = time_steps(bm, plan.run, max(steps, 10), max(3, args.warmup), torch, live=False)
+        out[key]["ms_per_step_plan"] = round(msp, 5)
         fc = lambda: bm.block_step(st, f, b, commit=True, chunk=64, y=y)  # noqa: E731
         msc, _, _, _ = time_steps(bm, fc, 20, 5, torch, live=False)
         out[key]["ms_per_commit_step"] = round(msc, 5)

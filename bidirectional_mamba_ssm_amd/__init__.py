@@ -309,6 +309,38 @@ def block_step(state, fwd, bwd, commit=False, chunk=64, y=None, stream=None, dt_
     return y
 
 
+class BlockStepPlan:
+    """A block step with its arguments checked and bound once, for decode
+    loops: run() calls bimamba_block_step on the same tensors (and the
+    stream current at construction) without checking them again, so a step
+    costs the C call and the launch. Write each step's inputs into the
+    bound tensors in place; keep them alive and unchanged in shape while the
+    plan is used. Same arguments as block_step."""
+
+    def __init__(self, state, fwd, bwd, commit=False, chunk=64, y=None, stream=None,
+                 dt_softplus=False):
+        x = fwd["x"]
+        dims = _dims(fwd)
+        self._shape = make_shape(x, fwd["B"], chunk, dt_softplus=dt_softplus)
+        dev = _cuda_device(x)
+        self._fd = _dir(fwd, x.dtype, dims, dev, "fwd")
+        self._bd = _dir(bwd, x.dtype, dims, dev, "bwd")
+        if y is None:
+            y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        _check(y, "y", tuple(x.shape), torch.float32, x.device)
+        self.y = y
+        self._keep = (state, fwd, bwd)
+        self._fn = lib().bimamba_block_step
+        self._args = (state.handle, ctypes.byref(self._shape), ctypes.byref(self._fd),
+                      ctypes.byref(self._bd), int(bool(commit)), _ptr(y), _stream(stream))
+
+    def run(self):
+        rc = self._fn(*self._args)
+        if rc:
+            _abi.check(rc)
+        return self.y
+
+
 ACTIVATIONS = {None: 0, "none": 0, "silu": 1}
 
 

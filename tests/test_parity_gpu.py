@@ -563,3 +563,25 @@ def test_dt_softplus_packed_and_block_step():
         assert ok, f"block step state: error {err:.3e}"
     finally:
         st.free()
+
+
+def test_block_step_plan_matches_call():
+    """A plan bound once gives the same bits as block_step, step after step
+    (with commit, so each step reads the state the previous one wrote)."""
+    c = synth.BLOCK_STEP
+    H, P, N, G, Lb = c["nheads"], c["headdim"], c["d_state"], c["ngroups"], c["block"]
+    sa, sb_ = bm.State(2, H, P, N), bm.State(2, H, P, N)
+    f, b = synth.make_inputs(2, Lb, H, P, N, G, "bf16", 123, device=DEV)
+    plan = bm.BlockStepPlan(sb_, f, b, commit=True, chunk=64)
+    for step in range(3):
+        fs, bs = synth.make_inputs(2, Lb, H, P, N, G, "bf16", 124 + step, device=DEV)
+        for k in ("x", "dt", "B", "C"):
+            f[k].copy_(fs[k])
+            b[k].copy_(bs[k])
+        y_call = bm.block_step(sa, f, b, commit=True, chunk=64)
+        y_plan = plan.run()
+        torch.cuda.synchronize()
+        assert torch.equal(y_call, y_plan), step
+        assert torch.equal(sa.tensor(), sb_.tensor()), step
+    sa.free()
+    sb_.free()
