@@ -329,13 +329,16 @@ class BlockStepPlan:
             y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
         _check(y, "y", tuple(x.shape), torch.float32, x.device)
         self.y = y
-        self._keep = (state, fwd, bwd)
+        self._state = state
+        self._keep = (fwd, bwd)
         self._fn = lib().bimamba_block_step
-        self._args = (state.handle, ctypes.byref(self._shape), ctypes.byref(self._fd),
-                      ctypes.byref(self._bd), int(bool(commit)), _ptr(y), _stream(stream))
+        self._args = (ctypes.byref(self._shape), ctypes.byref(self._fd), ctypes.byref(self._bd),
+                      int(bool(commit)), _ptr(y), _stream(stream))
 
     def run(self):
-        rc = self._fn(*self._args)
+        # the cache's handle is read per call: a freed cache is rejected by
+        # the library instead of being used through a stale pointer
+        rc = self._fn(self._state.handle, *self._args)
         if rc:
             _abi.check(rc)
         return self.y

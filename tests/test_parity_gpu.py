@@ -585,3 +585,5 @@ def test_block_step_plan_matches_call():
         assert torch.equal(sa.tensor(), sb_.tensor()), step
     sa.free()
     sb_.free()
+    with pytest.raises(bm.BimambaError):   # a freed cache is rejected, not used
+        plan.run()
