@@ -1260,8 +1260,11 @@ hipError_t launch_q(const SegArgs &a, hipStream_t s) {
                   s, a);
     }
     const int per_xcd = (a.batch * a.nseg * a.H + 7) / 8;
-    if (Q == 64 && a.ndir == 2 && !a.seq && a.L <= 64 && !SPLIT) {
-        // one chunk per row: both directions at once
+    // one chunk per row: both directions at once, except for committing
+    // steps over many (row, head) pairs, where the segment kernel (both
+    // directions in turn, two workgroups per CU) measured 3-7 % faster
+    const bool many_commit = a.final_state && (long)a.batch * a.H >= 320;
+    if (Q == 64 && a.ndir == 2 && !a.seq && a.L <= 64 && !SPLIT && !many_commit) {
         BM_LAUNCH("ssd_dual_out", k_dual_out<SP>, dim3(per_xcd * 8), dim3(512), 0, s, a);
         return hipGetLastError();
     }
