@@ -194,6 +194,8 @@ HEAD_LOOP_CASES = [
     # name, batch, L, H, P, N, G, dtype, bidir, seed
     ("bf16_groups_ragged_bi", 8, 1000, 4, 64, 128, 2, "bf16", True, 83),
     ("f32_ragged_fwd_only", 16, 1001, 3, 16, 16, 1, "f32", False, 84),
+    ("bf16_small_state_fwd_only", 16, 1024, 2, 64, 16, 1, "bf16", False, 87),
+    ("f32_p16_n128_bi", 8, 999, 2, 16, 128, 2, "f32", True, 88),
 ]
 
 
