@@ -290,19 +290,36 @@ __global__ __launch_bounds__(256) void k_bwd_pass(BwdArgs a, int np) {
     const int h = blockIdx.y;
     const int dir = (int)(blockIdx.z % (unsigned)a.ndir), b = (int)(blockIdx.z / (unsigned)a.ndir);
     const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
+    // eight blocks' values are loaded before any is overwritten, so that
+    // their loads are in flight together (the in-place stores would
+    // otherwise hold each load back until the previous store)
+    constexpr int kB = 8;
+    const size_t base = unit * a.nc * (size_t)np + e;
     float carry = 0.f;
-    for (int c = 0; c < a.nc; ++c) {
-        const size_t i = (unit * a.nc + c) * (size_t)np + e;
-        const float s = a.S[i];
-        a.S[i] = carry;
-        carry = fmaf(expf((float)a.lg[unit * a.nc + c]), carry, s);
+    for (int c0 = 0; c0 < a.nc; c0 += kB) {
+        float v[kB];
+#pragma unroll
+        for (int k = 0; k < kB; ++k)
+            v[k] = c0 + k < a.nc ? a.S[base + (size_t)(c0 + k) * np] : 0.f;
+#pragma unroll
+        for (int k = 0; k < kB; ++k) {
+            if (c0 + k >= a.nc) break;
+            a.S[base + (size_t)(c0 + k) * np] = carry;
+            carry = fmaf(expf((float)a.lg[unit * a.nc + c0 + k]), carry, v[k]);
+        }
     }
     carry = 0.f;
-    for (int c = a.nc - 1; c >= 0; --c) {
-        const size_t i = (unit * a.nc + c) * (size_t)np + e;
-        const float r = a.R[i];
-        a.R[i] = carry;
-        carry = fmaf(expf((float)a.lg[unit * a.nc + c]), carry, r);
+    for (int c0 = a.nc - 1; c0 >= 0; c0 -= kB) {
+        float v[kB];
+#pragma unroll
+        for (int k = 0; k < kB; ++k)
+            v[k] = c0 - k >= 0 ? a.R[base + (size_t)(c0 - k) * np] : 0.f;
+#pragma unroll
+        for (int k = 0; k < kB; ++k) {
+            if (c0 - k < 0) break;
+            a.R[base + (size_t)(c0 - k) * np] = carry;
+            carry = fmaf(expf((float)a.lg[unit * a.nc + c0 - k]), carry, v[k]);
+        }
     }
 }
 
