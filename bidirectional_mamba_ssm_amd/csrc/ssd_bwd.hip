@@ -376,16 +376,23 @@ __device__ __forceinline__ void grad_block(const BwdArgs &a, GradSmem<P, N> &sm,
     // ---- inputs of the block; the entering state and the leaving-state
     // gradient are fetched now too and held until their phases
     const size_t sgn = (size_t)a.G * N, hp = (size_t)a.H * P;
+    // (walking the heads of a group, B and C of the block stay in LDS from
+    // the first head on: nothing else writes those rows then)
+    const bool bc = !HSUM || first;
     {
         Rows<N, NT> rb, rc;
         Rows<P, NT> rx, ry;
-        fetch_rows<T, HSUM>(rb, d.B, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
-        fetch_rows<T, HSUM>(rc, d.C, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+        if (bc) {
+            fetch_rows<T, HSUM>(rb, d.B, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+            fetch_rows<T, HSUM>(rc, d.C, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+        }
         fetch_rows<T, HSUM>(rx, d.x, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
         fetch_rows<float, HSUM>(ry, a.dy, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
         block_scan<T, HSUM>(a, d, rowt, h, k0, len, rev, sm.sv, sm.dtv);
-        store_rows<HSUM>(rb, sm.Bs, [](int) { return 1.f; });
-        store_rows<HSUM>(rc, sm.Cs, [](int) { return 1.f; });
+        if (bc) {
+            store_rows<HSUM>(rb, sm.Bs, [](int) { return 1.f; });
+            store_rows<HSUM>(rc, sm.Cs, [](int) { return 1.f; });
+        }
         store_rows<HSUM>(rx, sm.Xs, [](int) { return 1.f; });
         store_rows<HSUM>(ry, sm.Ys, [](int) { return 1.f; });
     }
