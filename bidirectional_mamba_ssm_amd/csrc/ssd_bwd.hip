@@ -240,16 +240,17 @@ __global__ __launch_bounds__(kStateThreads) void k_bwd_state(BwdArgs a) {
     const int len = min(kQ, a.L - k0);
     const size_t rowt = (size_t)b * a.L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    block_scan<T>(a, d, rowt, h, k0, len, rev, sv, dtv);
-    const double send = sv[len - 1];
     const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
     const size_t so = (unit * a.nc + c) * (size_t)(N * P);
 
+    // the first pass's rows are in flight during the scan of dt
     const size_t sgn = (size_t)a.G * N, hp = (size_t)a.H * P;
     Rows<N, NT> rb;
     Rows<P, NT> rx;
     fetch_rows<T>(rb, d.B, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
     fetch_rows<T>(rx, d.x, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
+    block_scan<T>(a, d, rowt, h, k0, len, rev, sv, dtv);
+    const double send = sv[len - 1];
     for (int pass = 0; pass < 2; ++pass) {
         // pass 0: S = sum_j (e^{s_end - s_j} dt_j B_j) x_j^T
         // pass 1: R = sum_i (e^{s_i} C_i) dy_i^T
