@@ -382,7 +382,14 @@ __global__ void __launch_bounds__(256) k_seg_scan(const SegArgs a) {
     // segment about to be left when `have` is set
     float hv = 0.f;
     bool have = true;
-    if (d == 0 && a.init_state) hv = a.init_state[((size_t)b * a.H + h) * PN + e];
+    if (d == 0 && a.init_state) {
+        hv = a.init_state[((size_t)b * a.H + h) * PN + e];
+        // the first segment's copy of the caller's incoming state (its slot of
+        // Hs is otherwise unused): the output kernel reads this copy, so no
+        // workgroup of it reads init_state while the last segment's workgroup
+        // writes final_state (which may be the same array)
+        a.Hs[slot(0) * PN + e] = hv;
+    }
     for (int s = 0; s + 1 < ns; ++s) {
         const int k = d == 0 ? s : ns - 1 - s;           // segment being left
         const int kn = d == 0 ? k + 1 : k - 1;           // segment being entered
@@ -1049,7 +1056,12 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
     // incoming state of this segment in the walking direction
     const float *src = nullptr;
     if (D == 0) {
-        if (seg == 0) src = a.init_state ? a.init_state + ((size_t)b * a.H + h) * PN : nullptr;
+        // several segments: the first one reads the copy k_seg_scan made of
+        // the incoming state (final_state may alias init_state, and the last
+        // segment's workgroup writes it during this launch)
+        if (seg == 0) src = a.init_state ? (a.nseg > 1 ? a.Hs + slot(0, 0) * PN
+                                                        : a.init_state + ((size_t)b * a.H + h) * PN)
+                                         : nullptr;
         else src = a.gam[slot(0, seg - 1)] == 0.f ? a.S + slot(0, seg - 1) * PN : a.Hs + slot(0, seg) * PN;
     } else {
         if (seg == a.nseg - 1) src = nullptr;

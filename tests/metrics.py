@@ -20,6 +20,9 @@ def rel_err_f32(got, ref):
     if ref.size == 0:
         return 0.0
     rms = float(np.sqrt(np.mean(ref ** 2)))
+    if rms == 0.0:
+        # an all-zero reference: the largest deviation itself (0 when exact)
+        return float(np.max(np.abs(got)))
     return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 0.01 * rms)))
 
 
@@ -29,6 +32,8 @@ def rms_err(got, ref):
     if ref.size == 0:
         return 0.0
     rms = float(np.sqrt(np.mean(ref ** 2)))
+    if rms == 0.0:
+        return float(np.max(np.abs(got)))
     return float(np.max(np.abs(got - ref)) / rms)
 
 

@@ -25,3 +25,12 @@ def test_conv_close_interval():
     # fp32: inside / outside the absolute bound
     assert conv_close(ref + 1e-7, ref, np.ones(3), "f32", rel=2 ** -18)[1]
     assert not conv_close(ref + 1e-5, ref, np.ones(3), "f32", rel=2 ** -18)[1]
+
+
+def test_errors_of_an_all_zero_reference_are_finite():
+    from metrics import rel_err_f32, rms_err
+    z = np.zeros(8)
+    assert rel_err_f32(z, z) == 0.0 and rms_err(z, z) == 0.0
+    got = np.array([0.0, 1e-9, -2e-9, 0.0])
+    assert rel_err_f32(got, np.zeros(4)) == 2e-9
+    assert rms_err(got, np.zeros(4)) == 2e-9

@@ -587,3 +587,29 @@ def test_block_step_plan_matches_call():
     sb_.free()
     with pytest.raises(bm.BimambaError):   # a freed cache is rejected, not used
         plan.run()
+
+
+@pytest.mark.parametrize("bidir", [False, True], ids=["fwd", "bi"])
+def test_inplace_state_many_segments(bidir):
+    """final_state given as the very array of init_state (updated in place)
+    on a row cut into 8 segments, the way a long prefix is built in 8192-token
+    pieces chained through the cache: no workgroup may read the incoming
+    state after another one wrote the outgoing state."""
+    c = synth.BLOCK_STEP
+    H, P, N, G = c["nheads"], c["headdim"], c["d_state"], c["ngroups"]
+    L = 8192
+    f, b = synth.make_inputs(1, L, H, P, N, G, "bf16", 161, device=DEV, bidirectional=bidir)
+    shape = bm.make_shape(f["x"], f["B"], 256)
+    assert bm.workspace_size(shape, 0) > 0   # several segments per row
+    g = torch.Generator(device=DEV).manual_seed(162)
+    state = (torch.randn(1, H, P, N, generator=g, device=DEV) * 0.5).contiguous()
+    init = state.clone()
+    y = bm.ssd_fwd(f, b, chunk=256, init_state=state, final_state=state)
+    torch.cuda.synchronize()
+    ref, fs_ref = oracle.bissd(f, b, init_state=init, want_final_state=True)
+    err, ok = within(y.double().cpu().numpy(), ref, "bf16")
+    print(f"in place, 8 segments, bidir={bidir}: y {err:.3e}", flush=True)
+    assert ok, f"y error {err:.3e}"
+    err, ok = within(state.double().cpu().numpy(), fs_ref, "bf16")
+    print(f"  final state {err:.3e}", flush=True)
+    assert ok, f"final state error {err:.3e}"
