@@ -104,6 +104,9 @@ def parse():
                     help="only the concatenating-merge lines (one JSON object)")
     ap.add_argument("--conv-only", action="store_true",
                     help="only the short-convolution line (one JSON object)")
+    ap.add_argument("--workload", default="layer_1p3b_train",
+                    help="workload of the main line (a name in synth.WORKLOADS)")
+    ap.add_argument("--chunk", type=int, default=None, help="chunk of the main line (default: the workload's)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -280,7 +283,10 @@ def main():
         print(json.dumps({"block_step": block_step_bench(args, bm, synth, torch, dev, args.steps)}),
               flush=True)
         return
-    w = synth.WORKLOADS["layer_1p3b_train"]
+    w = synth.WORKLOADS[args.workload]
+    if args.chunk:
+        import dataclasses
+        w = dataclasses.replace(w, chunk=args.chunk)
     f, b = synth.make_workload(w, device=dev)
     torch.cuda.synchronize()
     y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=dev)

@@ -477,6 +477,15 @@ __device__ __forceinline__ void tile_fetch(TileIn &t, const SegArgs &a, int b, i
     }
 }
 
+// Position in a chunk of Q tokens of the i-th of the Q/64 tokens that lane
+// `lane` of a scanning wave holds: walking order for wave 0, from the
+// outgoing edge for wave 1.
+template <int Q>
+__device__ __forceinline__ int scan_pos(int d, int wv, int lane, int i) {
+    const int k = lane * (Q / 64) + i;
+    return (wv == 0) == (d == 0) ? k : Q - 1 - k;
+}
+
 // Loads of one chunk [c0, c0+len) of direction D, issued ahead of use (the
 // next chunk's are issued before the current chunk's state update, so their
 // latency overlaps it): x and B for every thread, and for waves 0 and 1 the
@@ -491,11 +500,8 @@ struct ChunkLoads {
     int sqv[TPL];
     TileIn tin;          // the wave's first row tile
 
-    // position in the chunk of the lane's i-th token; walking order for wave
-    // 0, from the outgoing edge for wave 1
     __device__ static __forceinline__ int pos_of(int d, int wv, int lane, int i) {
-        const int k = lane * TPL + i;
-        return (wv == 0) == (d == 0) ? k : Q - 1 - k;
+        return scan_pos<Q>(d, wv, lane, i);
     }
 
     const uint16_t *x0, *b0;
@@ -556,127 +562,138 @@ __device__ __forceinline__ void store_run(V *dst, bool asc, int lane, const V (&
     }
 }
 
-// One chunk [c0, c0+len) of direction d: scans, decay factors, weights, skip
-// masks, staged x and B; one barrier. Wave 0 scans a over the chunk in the
-// walking direction, wave 1 toward the outgoing edge, each with Q/64 tokens
-// per lane; the tile-edge values come from lane shuffles.
+// The scans of one chunk [c0, c0+len) of direction d for head h, by the two
+// scanning waves (wv 0 and 1) of the group of waves that serves the head:
+// wave 0 scans a over the chunk in the walking direction (the decay factors,
+// the 16-tiles the carried state reaches, the chunk's decay), wave 1 toward
+// the outgoing edge (the state-update weights); Q/64 tokens per lane, the
+// tile-edge values from lane shuffles. dtv / sqv: the raw step sizes (and
+// sequence indices) of the lane's tokens (scan_pos order). SM is any shared
+// layout with the per-token arrays and flags used below.
+template <int Q, bool PACKED, bool SP, typename SM>
+__device__ __forceinline__ void chunk_scans(const SegArgs &a, SM &sm, int wv,
+                                            const uint16_t (&dtv)[Q / 64], const int (&sqv)[Q / 64],
+                                            int d, int b, int h, int c0, int len) {
+    constexpr int TPL = Q / 64;
+    const int lane = lane_id();
+    const float Ah = a.dir[d].A[h];
+    const float dtb = SP && a.dt_bias[d] ? a.dt_bias[d][h] : 0.f;
+    int sq_nb = 0, sq_edge = 0;
+    bool has_nb = true;
+    if (PACKED) {
+        const int nb = d == 0 ? c0 - 1 : c0 + len;
+        has_nb = d == 0 ? c0 > 0 : c0 + len < a.L;
+        sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
+        sq_edge = a.seq[tok(a, b, d == 0 ? c0 + len - 1 : c0)];
+    }
+    // inclusive scan over the lane's tokens, then across lanes, in fp64:
+    // every exponent below is a difference of these sums, formed in fp64
+    // and rounded once, so none is the difference of two large fp32 values
+    float at[TPL], dtf[TPL];
+    double cs[TPL];
+    double run = 0.0;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+        dtf[i] = scan_pos<Q>(d, wv, lane, i) < len ? bf2f(dtv[i]) : 0.f;
+        if (SP) dtf[i] = scan_pos<Q>(d, wv, lane, i) < len ? softplus_dt(dtf[i] + dtb) : 0.f;
+        at[i] = dtf[i] * Ah;
+        run += (double)at[i];
+        cs[i] = run;
+    }
+    const double incl = wave_scan_d(run);
+    const double excl = incl - run;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) cs[i] += excl;
+    if (wv == 0) {
+        // in walking order a token's 16-tile (64-block) ends at the last
+        // token of lane (lane | (16/TPL - 1)) (resp. lane | (64/TPL - 1));
+        // its 64-block starts after the last token of lane
+        // (lane & ~(64/TPL - 1)) - 1
+        const double last = cs[TPL - 1];
+        const double e16 = __shfl(last, lane | (16 / TPL - 1), 64);
+        const double e64 = __shfl(last, lane | (64 / TPL - 1), 64);
+        const int sl = (lane & ~(64 / TPL - 1)) - 1;
+        const double b64 = __shfl(last, sl < 0 ? 0 : sl, 64);
+        const double start = sl < 0 ? 0.0 : b64;
+        bool reach = false;
+        float c2v[TPL], rlv[TPL], v16v[TPL], v64v[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int pos = scan_pos<Q>(d, 0, lane, i);
+            c2v[i] = (float)(cs[i] * kLog2e);
+            rlv[i] = (float)((cs[i] - start) * kLog2e);
+            v16v[i] = exp2_((float)((e16 - cs[i]) * kLog2e)) * dtf[i];
+            v64v[i] = exp2_((float)((e64 - cs[i]) * kLog2e)) * dtf[i];
+            reach |= pos < len && (!PACKED || sqv[i] == sq_nb) && cs[i] >= kDead;
+        }
+        const bool asc = d == 0;   // wave 0 walks ascending positions forward
+        store_run<Q, TPL>(sm.cs2, asc, lane, c2v);
+        store_run<Q, TPL>(sm.rl2, asc, lane, rlv);
+        store_run<Q, TPL>(sm.dt, asc, lane, dtf);
+        store_run<Q, TPL>(sm.sq, asc, lane, sqv);
+        store_run<Q, TPL>(sm.v16, asc, lane, v16v);
+        store_run<Q, TPL>(sm.v64, asc, lane, v64v);
+        // block table: the last token of walking block K is lane
+        // 64/TPL*(K+1) - 1; bt2[I][J] = cs(end of I-1) - cs(end of J)
+        {
+            const bool tl = lane < (Q / 64) * (Q / 64);
+            const int I = tl ? lane / (Q / 64) : 0, J = tl ? lane % (Q / 64) : 0;
+            const double eI = __shfl(last, (64 / TPL) * (I > 0 ? I : 1) - 1, 64);
+            const double eJ = __shfl(last, (64 / TPL) * (J + 1) - 1, 64);
+            if (tl) sm.bt2[I][J] = J < I ? (float)((eI - eJ) * kLog2e) : 0.f;
+        }
+        // 16-tiles (walking order m) the carried state reaches
+        const unsigned long long m = __ballot(reach);
+        if (lane < Q / 16) {
+            constexpr int LPT = 16 / TPL;   // lanes per 16-tile
+            const bool any = ((m >> (lane * LPT)) & ((1ull << LPT) - 1)) != 0;
+            sm.utile[d == 0 ? lane : Q / 16 - 1 - lane] = any;
+        }
+        if (lane == 63) {
+            bool carry = true;
+            if (PACKED) carry = has_nb && sq_nb == sq_edge;
+            sm.gamma = carry ? expf((float)last) : 0.f;
+            sm.sq_nb = PACKED ? sq_nb : 0;
+        }
+    } else {
+        // exclusive sums toward the outgoing edge -> weight of each token
+        // in the state leaving the chunk
+        bool nz = false, big = false;
+        float wv_[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int pos = scan_pos<Q>(d, 1, lane, i);
+            float wt = 0.f;
+            if (pos < len && (!PACKED || sqv[i] == sq_edge)) {
+                const double lf = cs[i] - (double)at[i];   // log of the weight factor
+                wt = expf((float)lf) * dtf[i];
+                if (Cfg<Q>::ONE_ROUND) big |= lf * (double)kLog2e > (double)kOneRound;
+            }
+            wv_[i] = wt;
+            nz |= wt != 0.f;
+        }
+        store_run<Q, TPL>(sm.w, d != 0, lane, wv_);   // wave 1 walks from the edge
+        const unsigned long long m = __ballot(nz);
+        const unsigned long long mb = Cfg<Q>::ONE_ROUND ? __ballot(big) : 0ull;
+        if (lane < Q / 64) {
+            constexpr int LPS = 64 / TPL;   // lanes per 64-token sub-block
+            constexpr unsigned long long lm = LPS == 64 ? ~0ull : (1ull << (LPS & 63)) - 1;
+            const int sb = d == 0 ? Q / 64 - 1 - lane : lane;
+            sm.wsub[sb] = ((m >> ((lane * LPS) & 63)) & lm) != 0;
+            if (Cfg<Q>::ONE_ROUND) sm.wbig[sb] = ((mb >> ((lane * LPS) & 63)) & lm) != 0;
+        }
+    }
+}
+
+// One chunk [c0, c0+len) of direction d: staged x and B, the scans
+// (chunk_scans); one barrier.
 template <int Q, bool PACKED, int WB = 0, bool SP = false>
 __device__ void chunk_prep(const SegArgs &a, OutSmem<Q> &sm, ChunkLoads<Q, PACKED, WB> &ld,
                            int d, int b, int h, int c0, int len) {
-    using LD = ChunkLoads<Q, PACKED, WB>;
-    constexpr int TPL = LD::TPL;
-    const int lane = lane_id(), wv = wave_in<WB>();
-    const float Ah = a.dir[d].A[h];
-    const float dtb = SP && a.dt_bias[d] ? a.dt_bias[d][h] : 0.f;
+    const int wv = wave_in<WB>();
     ld.sx.store(len, sm.xs);
     ld.sb.store(len, sm.bn);
-    if (wv < 2) {
-        int sq_nb = 0, sq_edge = 0;
-        bool has_nb = true;
-        if (PACKED) {
-            const int nb = d == 0 ? c0 - 1 : c0 + len;
-            has_nb = d == 0 ? c0 > 0 : c0 + len < a.L;
-            sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
-            sq_edge = a.seq[tok(a, b, d == 0 ? c0 + len - 1 : c0)];
-        }
-        // inclusive scan over the lane's tokens, then across lanes, in fp64:
-        // every exponent below is a difference of these sums, formed in fp64
-        // and rounded once, so none is the difference of two large fp32 values
-        float at[TPL], dtf[TPL];
-        double cs[TPL];
-        double run = 0.0;
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            dtf[i] = LD::pos_of(d, wv, lane, i) < len ? bf2f(ld.dtv[i]) : 0.f;
-            if (SP) dtf[i] = LD::pos_of(d, wv, lane, i) < len ? softplus_dt(dtf[i] + dtb) : 0.f;
-            at[i] = dtf[i] * Ah;
-            run += (double)at[i];
-            cs[i] = run;
-        }
-        const double incl = wave_scan_d(run);
-        const double excl = incl - run;
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) cs[i] += excl;
-        if (wv == 0) {
-            // in walking order a token's 16-tile (64-block) ends at the last
-            // token of lane (lane | (16/TPL - 1)) (resp. lane | (64/TPL - 1));
-            // its 64-block starts after the last token of lane
-            // (lane & ~(64/TPL - 1)) - 1
-            const double last = cs[TPL - 1];
-            const double e16 = __shfl(last, lane | (16 / TPL - 1), 64);
-            const double e64 = __shfl(last, lane | (64 / TPL - 1), 64);
-            const int sl = (lane & ~(64 / TPL - 1)) - 1;
-            const double b64 = __shfl(last, sl < 0 ? 0 : sl, 64);
-            const double start = sl < 0 ? 0.0 : b64;
-            bool reach = false;
-            float c2v[TPL], rlv[TPL], v16v[TPL], v64v[TPL];
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                const int pos = LD::pos_of(d, 0, lane, i);
-                c2v[i] = (float)(cs[i] * kLog2e);
-                rlv[i] = (float)((cs[i] - start) * kLog2e);
-                v16v[i] = exp2_((float)((e16 - cs[i]) * kLog2e)) * dtf[i];
-                v64v[i] = exp2_((float)((e64 - cs[i]) * kLog2e)) * dtf[i];
-                reach |= pos < len && (!PACKED || ld.sqv[i] == sq_nb) && cs[i] >= kDead;
-            }
-            const bool asc = d == 0;   // wave 0 walks ascending positions forward
-            store_run<Q, TPL>(sm.cs2, asc, lane, c2v);
-            store_run<Q, TPL>(sm.rl2, asc, lane, rlv);
-            store_run<Q, TPL>(sm.dt, asc, lane, dtf);
-            store_run<Q, TPL>(sm.sq, asc, lane, ld.sqv);
-            store_run<Q, TPL>(sm.v16, asc, lane, v16v);
-            store_run<Q, TPL>(sm.v64, asc, lane, v64v);
-            // block table: the last token of walking block K is lane
-            // 64/TPL*(K+1) - 1; bt2[I][J] = cs(end of I-1) - cs(end of J)
-            {
-                const bool tl = lane < (Q / 64) * (Q / 64);
-                const int I = tl ? lane / (Q / 64) : 0, J = tl ? lane % (Q / 64) : 0;
-                const double eI = __shfl(last, (64 / TPL) * (I > 0 ? I : 1) - 1, 64);
-                const double eJ = __shfl(last, (64 / TPL) * (J + 1) - 1, 64);
-                if (tl) sm.bt2[I][J] = J < I ? (float)((eI - eJ) * kLog2e) : 0.f;
-            }
-            // 16-tiles (walking order m) the carried state reaches
-            const unsigned long long m = __ballot(reach);
-            if (lane < Q / 16) {
-                constexpr int LPT = 16 / TPL;   // lanes per 16-tile
-                const bool any = ((m >> (lane * LPT)) & ((1ull << LPT) - 1)) != 0;
-                sm.utile[d == 0 ? lane : Q / 16 - 1 - lane] = any;
-            }
-            if (lane == 63) {
-                bool carry = true;
-                if (PACKED) carry = has_nb && sq_nb == sq_edge;
-                sm.gamma = carry ? expf((float)last) : 0.f;
-                sm.sq_nb = PACKED ? sq_nb : 0;
-            }
-        } else {
-            // exclusive sums toward the outgoing edge -> weight of each token
-            // in the state leaving the chunk
-            bool nz = false, big = false;
-            float wv_[TPL];
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                const int pos = LD::pos_of(d, 1, lane, i);
-                float wt = 0.f;
-                if (pos < len && (!PACKED || ld.sqv[i] == sq_edge)) {
-                    const double lf = cs[i] - (double)at[i];   // log of the weight factor
-                    wt = expf((float)lf) * dtf[i];
-                    if (Cfg<Q>::ONE_ROUND) big |= lf * (double)kLog2e > (double)kOneRound;
-                }
-                wv_[i] = wt;
-                nz |= wt != 0.f;
-            }
-            store_run<Q, TPL>(sm.w, d != 0, lane, wv_);   // wave 1 walks from the edge
-            const unsigned long long m = __ballot(nz);
-            const unsigned long long mb = Cfg<Q>::ONE_ROUND ? __ballot(big) : 0ull;
-            if (lane < Q / 64) {
-                constexpr int LPS = 64 / TPL;   // lanes per 64-token sub-block
-                constexpr unsigned long long lm = LPS == 64 ? ~0ull : (1ull << (LPS & 63)) - 1;
-                const int sb = d == 0 ? Q / 64 - 1 - lane : lane;
-                sm.wsub[sb] = ((m >> ((lane * LPS) & 63)) & lm) != 0;
-                if (Cfg<Q>::ONE_ROUND) sm.wbig[sb] = ((mb >> ((lane * LPS) & 63)) & lm) != 0;
-            }
-        }
-    }
+    if (wv < 2) chunk_scans<Q, PACKED, SP>(a, sm, wv, ld.dtv, ld.sqv, d, b, h, c0, len);
     lds_barrier();
 }
 
@@ -700,34 +717,44 @@ __device__ void publish_state(OutSmem<Q> &sm, const f32x4 (&Hacc)[Cfg<Q>::NQ]) {
     }
 }
 
+// One 16x16x32 matrix-core product: bf16 operands, or fp16 ones with F16.
+template <bool F16>
+__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (F16) return mfma16x16x32_f16(a, b, c);
+    else return mfma16x16x32(a, b, c);
+}
+
 // G^T tile rows j0..j0+15 x this lane group's 16 rows i: gg[r] = G[i][j0 + 4g4 + r]
+template <bool F16 = false>
 __device__ __forceinline__ f32x4 gram_tile(const uint16_t *bn, int j0, const u32x4 (&cr)[kN / 32]) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
     f32x4 g = zero4();
 #pragma unroll
     for (int ks = 0; ks < kN / 32; ++ks)
-        g = mfma16x16x32(*(const u32x4 *)(bn + j0 * kBS + bn_lane(l16) + 32 * ks + 8 * g4), cr[ks], g);
+        g = mma<F16>(*(const u32x4 *)(bn + j0 * kBS + bn_lane(l16) + 32 * ks + 8 * g4), cr[ks], g);
     return g;
 }
 
 // acc[pt] += M x over the 32 columns j32..j32+31; M given as a hi / lo pair
 // in the k order of a Gram accumulator pair, which is the order in which the
 // transposing reads deliver x.
+template <bool F16 = false>
 __device__ __forceinline__ void mx_step(f32x4 (&acc)[4], const uint16_t *xs, int j32, u32x4 mhi,
                                         u32x4 mlo, bool lo = true) {
     u32x4 xo[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) xo[pt] = tr_operand(xs, kXS, j32, 16 * pt);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16x16x32(mhi, xo[pt], acc[pt]);
+    for (int pt = 0; pt < 4; ++pt) acc[pt] = mma<F16>(mhi, xo[pt], acc[pt]);
     if (lo) {
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16x16x32(mlo, xo[pt], acc[pt]);
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = mma<F16>(mlo, xo[pt], acc[pt]);
     }
 }
 
 // Two G^T tiles (rows j0a.., j0b..) at once: all operand loads first, then
 // the two MFMA chains interleaved.
+template <bool F16 = false>
 __device__ __forceinline__ void gram_pair(const uint16_t *bn, int j0a, int j0b,
                                           const u32x4 (&cr)[kN / 32], f32x4 &ga, f32x4 &gb) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
@@ -741,14 +768,14 @@ __device__ __forceinline__ void gram_pair(const uint16_t *bn, int j0a, int j0b,
     gb = zero4();
 #pragma unroll
     for (int ks = 0; ks < kN / 32; ++ks) {
-        ga = mfma16x16x32(oa[ks], cr[ks], ga);
-        gb = mfma16x16x32(ob[ks], cr[ks], gb);
+        ga = mma<F16>(oa[ks], cr[ks], ga);
+        gb = mma<F16>(ob[ks], cr[ks], gb);
     }
 }
 
 // Zero the entries of columns jb..jb+3 that belong to another sequence.
-template <int Q, bool PACKED>
-__device__ __forceinline__ void seq_mask(float (&mv)[4], const OutSmem<Q> &sm, int jb, int sqi) {
+template <int Q, bool PACKED, typename SM>
+__device__ __forceinline__ void seq_mask(float (&mv)[4], const SM &sm, int jb, int sqi) {
     if (PACKED) {
         const int4 s4 = *(const int4 *)(sm.sq + jb);
         mv[0] = s4.x == sqi ? mv[0] : 0.f;
@@ -1040,11 +1067,12 @@ __device__ void chunk_state_update(const OutSmem<Q> &sm, f32x4 (&Hacc)[Cfg<Q>::N
     }
 }
 
-// One direction's walk over the segment's chunks.
-template <int Q, bool PACKED, int D, bool SP, bool Y2 = false>
+// One direction's walk over the segment's chunks (by the Cfg<Q>::NW waves
+// starting at wave WB).
+template <int Q, bool PACKED, int D, bool SP, bool Y2 = false, int WB = 0>
 __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h, int grp, bool add) {
     constexpr int NQ = Cfg<Q>::NQ;
-    const int lane = lane_id(), w = wave_id(), g4 = lane >> 4, l16 = lane & 15;
+    const int lane = lane_id(), w = wave_in<WB>(), g4 = lane >> 4, l16 = lane & 15;
     const int pq = w & 3, nbase = NQ * (w >> 2);
     const int t0 = seg * a.Ts, t1 = min(t0 + a.Ts, a.L);
     const int cfirst = t0 / Q, clast = (t1 - 1) / Q;
@@ -1076,7 +1104,7 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
     };
     // the first chunk's loads go out before the incoming state is read, so
     // the two round trips overlap
-    ChunkLoads<Q, PACKED> ld;
+    ChunkLoads<Q, PACKED, WB> ld;
     {
         int c0, len;
         chunk_at(0, c0, len);
@@ -1087,11 +1115,11 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
 #pragma unroll
     for (int q = 0; q < NQ; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
     bool has_state = src != nullptr;
-    if (has_state) publish_state<Q>(sm, Hacc);
+    if (has_state) publish_state<Q, WB>(sm, Hacc);
     for (int s = 0; s < nch; ++s) {
         int c0, len;
         chunk_at(s, c0, len);
-        chunk_prep<Q, PACKED, 0, SP>(a, sm, ld, D, b, h, c0, len);
+        chunk_prep<Q, PACKED, WB, SP>(a, sm, ld, D, b, h, c0, len);
         if (Q == 256) {
             // two tiles per wave: each fetches its own inputs (holding them
             // through the state update would cost spills)
@@ -1117,11 +1145,11 @@ __device__ void seg_pass(const SegArgs &a, OutSmem<Q> &sm, int b, int seg, int h
             ld.begin(a, D, b, h, grp, c0n, lenn);
             if (Q != 256) tile_fetch<D>(ld.tin, a, b, h, grp, c0n, lenn, tile_of<Q>(w, 0), add);
         }
-        chunk_state_update<Q, PACKED>(sm, Hacc, len, !last || want_final, ld);
+        chunk_state_update<Q, PACKED, true, WB>(sm, Hacc, len, !last || want_final, ld);
         // every wave is done with this chunk's tiles and the published state
         lds_barrier();
         if (!last) {
-            publish_state<Q>(sm, Hacc);
+            publish_state<Q, WB>(sm, Hacc);
             has_state = true;
         }
     }
@@ -1256,10 +1284,685 @@ k_dual_out(const SegArgs a) {
     else dual_half<0, 4, SP>(a, sm.half[1], sm.ex, b, h, grp);
 }
 
+// ------------------------------------------------------------ k_pair_out
+// The output kernel in fp16 matrix-core form: 64-token chunks, two heads of
+// one group per workgroup of 8 waves (waves 0-3 serve the first head, 4-7
+// the second), the reverse pass writing y and the forward pass adding its
+// part, as in k_seg_out.
+//
+// Every product runs on v_mfma_f32_16x16x32_f16 with fp32 accumulation. x, B
+// and C arrive as bf16 and are converted to fp16 as they are staged in LDS
+// (exact for magnitudes in fp16's normal range); B and C are staged once for
+// both heads. The operands computed on the way are rounded once to fp16 (11
+// significant bits against bf16's 8): the decay-masked Gram matrix M, the
+// carried state H and the weighted inputs w x -- except the 32 columns of M
+// that hold the diagonal 16-tile, which the rows' own terms dominate: they
+// are split into fp16 hi + lo. The skip term D x rides on the diagonal of M.
+//
+// Range: fp16 overflows at 65504. Each fp16 operand reaches an output or the
+// state, so an operand that overflowed leaves a non-finite value in y or in
+// the final state: the last pass sums its outputs per lane, and if a sum is
+// not finite anywhere in the workgroup, the workgroup recomputes its segment
+// for both heads with the split-bf16 path (seg_pass with 64-token chunks,
+// fp32's range), which overwrites every output. final_state is written only
+// after that check. Magnitudes below fp16's normal range (2^-14) keep an
+// absolute error of at most 2^-25 per rounded value.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_h(float a, float b) {
+    const f16x2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+// v = hi + lo, both fp16, per pair of values
+__device__ __forceinline__ void split_h(float v0, float v1, uint32_t &hi, uint32_t &lo) {
+    const f16x2_t h = {(_Float16)v0, (_Float16)v1};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const f16x2_t l = {(_Float16)(v0 - (float)h[0]), (_Float16)(v1 - (float)h[1])};
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+// a pair of bf16 (raw bits) as a pair of fp16
+__device__ __forceinline__ uint32_t bf2h(uint32_t u) {
+    return pk_h(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+__device__ __forceinline__ u32x4 bf2h4(u32x4 v) {
+    return u32x4{bf2h(v[0]), bf2h(v[1]), bf2h(v[2]), bf2h(v[3])};
+}
+__device__ __forceinline__ uint32_t mul_h(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) * __builtin_bit_cast(f16x2_t, b));
+}
+
+// One chunk's scan results for one head.
+struct PairScan {
+    float cs2[64];         // inclusive scan of a in the walking direction, times log2(e)
+    float w[64];           // state-update weights
+    float v16[64];         // e^{cs(edge of the token's 16-tile) - cs} dt
+    float dt[64];
+    int sq[64];            // sequence index (packed)
+    int utile[4];          // the carried state reaches some row of the 16-row tile
+    int wsub;              // some weight of the chunk is nonzero
+    float gamma;           // decay of the whole chunk (0: the state does not pass)
+    int sq_nb;             // sequence index of the token the carried state comes from
+};
+
+// fp64 value of lane `src` (uniform)
+__device__ __forceinline__ double lane_d(double v, int src) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = __builtin_amdgcn_readlane((unsigned)(u & 0xffffffffull), src);
+    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), src);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// The scans of one 64-token chunk [c0, c0+len) of direction d for head h by
+// one wave; lane k holds the k-th token in walking order (position k forward,
+// 63 - k reverse; positions past the end carry dt = 0). Sums in fp64 as in
+// chunk_scans: every exponent is a difference of them rounded once. A
+// token's state-update weight is e^(the sum of a after it) dt, that sum being
+// the chunk's total minus the token's walking sum.
+template <bool PACKED, bool SP>
+__device__ __forceinline__ void pair_scans(const SegArgs &a, PairScan &sm, uint16_t dtv, int sqv,
+                                           int d, int b, int h, int c0, int len) {
+    const int lane = lane_id();
+    const int pos = d == 0 ? lane : 63 - lane;
+    const float Ah = a.dir[d].A[h];
+    const float dtb = SP && a.dt_bias[d] ? a.dt_bias[d][h] : 0.f;
+    int sq_nb = 0, sq_edge = 0;
+    bool has_nb = true;
+    if (PACKED) {
+        const int nb = d == 0 ? c0 - 1 : c0 + len;
+        has_nb = d == 0 ? c0 > 0 : c0 + len < a.L;
+        sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
+        sq_edge = a.seq[tok(a, b, d == 0 ? c0 + len - 1 : c0)];
+    }
+    const bool in = pos < len;
+    float dtf = in ? bf2f(dtv) : 0.f;
+    if (SP) dtf = in ? softplus_dt(dtf + dtb) : 0.f;
+    const float at = dtf * Ah;
+    const double cs = wave_scan_d((double)at);
+    const double total = lane_d(cs, 63);
+    // the walking sum at the end of the lane's 16-tile (lane | 15)
+    const double t0 = lane_d(cs, 15), t1 = lane_d(cs, 31), t2 = lane_d(cs, 47);
+    const int row = lane >> 4;
+    const double e16 = row == 0 ? t0 : row == 1 ? t1 : row == 2 ? t2 : total;
+    sm.cs2[pos] = (float)(cs * kLog2e);
+    sm.dt[pos] = dtf;
+    if (PACKED) sm.sq[pos] = sqv;
+    sm.v16[pos] = exp2_((float)((e16 - cs) * kLog2e)) * dtf;
+    const bool reach = in && (!PACKED || sqv == sq_nb) && cs >= kDead;
+    const unsigned long long m = __ballot(reach);
+    if (lane < 4) sm.utile[d == 0 ? lane : 3 - lane] = ((m >> (16 * lane)) & 0xffffull) != 0;
+    float wt = 0.f;
+    if (in && (!PACKED || sqv == sq_edge)) wt = expf((float)(total - cs)) * dtf;
+    sm.w[pos] = wt;
+    const bool nz = __ballot(wt != 0.f) != 0ull;
+    if (lane == 0) {
+        bool carry = true;
+        if (PACKED) carry = has_nb && sq_nb == sq_edge;
+        sm.gamma = carry ? expf((float)total) : 0.f;
+        sm.sq_nb = PACKED ? sq_nb : 0;
+        sm.wsub = nz;
+    }
+}
+// One head's share of the pair kernel's shared memory. The scans of chunk
+// s + 1 run while chunk s is in use, so they alternate between two buffers.
+struct PairHalf {
+    PairScan sc[2];
+    alignas(16) uint16_t xs[64 * kXS];   // x [t][p], fp16
+    alignas(16) uint16_t hs[kP * kNRS];  // H^T [p][n], fp16
+};
+constexpr int kTS = kP + 4;   // row stride (floats) of a wave's output tile in LDS
+struct PairSmem {
+    PairHalf half[2];
+    alignas(16) uint16_t bn[bn_elems(64)];   // B [t][n], fp16, bn_row layout
+    alignas(16) uint16_t cn[bn_elems(64)];   // C [t][n], fp16, bn_row layout
+    alignas(16) float tile[8][16 * kTS];     // per wave: its 16 output rows, row-major
+    int bad[8];                              // per wave: a non-finite output or state
+};
+union PairShared {
+    PairSmem fast;
+    OutSmem<64> slow[2];   // the split-bf16 recomputation, one per head
+};
+
+// Loads of one 64-token chunk, issued ahead of use: x of the half's head (two
+// 16-byte pieces per thread of the half), B and C (two pieces each per thread
+// of the workgroup), and for the half's scanning wave the step size (and
+// sequence index) of the lane's token.
+template <bool PACKED>
+struct PairLoads {
+    u32x4 xv[2], bv[2], cv[2];
+    uint16_t dtv[1];
+    int sqv[1];
+    uint32_t ox[2], ob[2];   // element offsets of this thread's pieces in a whole chunk
+
+    __device__ __forceinline__ void init(const SegArgs &a) {
+        const int th = threadIdx.x & 255, tid = threadIdx.x;
+        const uint32_t xstride = (uint32_t)(a.H * kP), bstride = (uint32_t)(a.G * kN);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = th + 256 * k;
+            ox[k] = (uint32_t)(item >> 3) * xstride + 8 * (item & 7);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = tid + 512 * k;
+            ob[k] = (uint32_t)(item >> 4) * bstride + 8 * (item & 15);
+        }
+    }
+    __device__ __forceinline__ void issue(const SegArgs &a, int d, int b, int h, int grp, int c0,
+                                          int len, bool scanner) {
+        const DirPtrs &dp = a.dir[d];
+        const int lane = lane_id(), th = threadIdx.x & 255, tid = threadIdx.x;
+        if (scanner) {
+            const int pos = min(d == 0 ? lane : 63 - lane, len - 1);
+            dtv[0] = ((const uint16_t *)dp.dt)[tok(a, b, c0 + pos) * a.H + h];
+            sqv[0] = PACKED ? a.seq[tok(a, b, c0 + pos)] : 0;
+        }
+        const uint16_t *X = (const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP;
+        const size_t bo = (tok(a, b, c0) * a.G + grp) * kN;
+        const uint16_t *Bm = (const uint16_t *)dp.B + bo, *Cm = (const uint16_t *)dp.C + bo;
+        if (len == 64) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) xv[k] = ld8(X + ox[k]);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                bv[k] = ld8(Bm + ob[k]);
+                cv[k] = ld8(Cm + ob[k]);
+            }
+            return;
+        }
+        // a partial chunk: rows past its end are read clamped (and staged as 0)
+        const uint32_t xstride = (uint32_t)(a.H * kP), bstride = (uint32_t)(a.G * kN);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = th + 256 * k, row = item >> 3, cg = item & 7;
+            xv[k] = ld8(X + (uint32_t)min(row, len - 1) * xstride + 8 * cg);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = tid + 512 * k, row = item >> 4, cg = item & 15;
+            const uint32_t o = (uint32_t)min(row, len - 1) * bstride + 8 * cg;
+            bv[k] = ld8(Bm + o);
+            cv[k] = ld8(Cm + o);
+        }
+    }
+    // converted to fp16 into LDS; rows at or past len as zeros
+    __device__ __forceinline__ void store(PairSmem &sm, PairHalf &hf, int len) const {
+        const int th = threadIdx.x & 255, tid = threadIdx.x;
+        if (len == 64) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int item = th + 256 * k, row = item >> 3, cg = item & 7;
+                *(u32x4 *)(hf.xs + row * kXS + 8 * cg) = bf2h4(xv[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int item = tid + 512 * k, row = item >> 4, cg = item & 15;
+                *(u32x4 *)(sm.bn + bn_row(row) + 8 * cg) = bf2h4(bv[k]);
+                *(u32x4 *)(sm.cn + bn_row(row) + 8 * cg) = bf2h4(cv[k]);
+            }
+            return;
+        }
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = th + 256 * k, row = item >> 3, cg = item & 7;
+            *(u32x4 *)(hf.xs + row * kXS + 8 * cg) = row < len ? bf2h4(xv[k]) : z;
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = tid + 512 * k, row = item >> 4, cg = item & 15;
+            *(u32x4 *)(sm.bn + bn_row(row) + 8 * cg) = row < len ? bf2h4(bv[k]) : z;
+            *(u32x4 *)(sm.cn + bn_row(row) + 8 * cg) = row < len ? bf2h4(cv[k]) : z;
+        }
+    }
+};
+
+// The diagonal 64-block of row tile WQ (all of a 64-token chunk): 16-tiles on
+// the far side of the diagonal are 0; the others factor the decay through
+// their edge nearest the diagonal; the diagonal tile takes one exponential per
+// entry and D on its diagonal. The 32-column pair holding the diagonal tile
+// is split into fp16 hi + lo, the other pair rounded once.
+template <bool PACKED, int D, int WQ>
+__device__ __forceinline__ void pair_diag(f32x4 (&acc)[4], const PairSmem &sm, const PairHalf &hf,
+                                          const PairScan &sc, const u32x4 (&cr)[kN / 32],
+                                          float rli, int sqi, const float (&tmask)[4],
+                                          const float (&dadd)[4]) {
+    const int g4 = lane_id() >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        if (D == 0 ? 2 * kk > WQ : 2 * kk + 1 < WQ) continue;   // both tiles dead
+        const bool live0 = D == 0 ? 2 * kk <= WQ : 2 * kk >= WQ;
+        const bool live1 = D == 0 ? 2 * kk + 1 <= WQ : 2 * kk + 1 >= WQ;
+        const bool band = kk == WQ / 2;
+        f32x4 gp[2];
+        if (live0 && live1) {
+            gram_pair<true>(sm.bn, 32 * kk, 32 * kk + 16, cr, gp[0], gp[1]);
+        } else {
+            gp[0] = live0 ? gram_tile<true>(sm.bn, 32 * kk, cr) : zero4();
+            gp[1] = live1 ? gram_tile<true>(sm.bn, 32 * kk + 16, cr) : zero4();
+        }
+        uint32_t ph[4], pl[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int jt = 2 * kk + half;
+            const int j0 = 16 * jt;
+            float mv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (D == 0 ? jt <= WQ : jt >= WQ) {
+                const f32x4 gg = gp[half];
+                const int jb = j0 + 4 * g4;
+                if (jt != WQ) {
+                    const float u16 = exp2_(rli - sc.cs2[D == 0 ? j0 + 15 : j0]);
+                    const f32x4 vv = *(const f32x4 *)(sc.v16 + jb);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u16 * vv[r]);
+                } else {
+                    // the far side of the diagonal through an exponent of -inf
+                    // (exactly 0), D on the diagonal itself
+                    const f32x4 c4 = *(const f32x4 *)(sc.cs2 + jb);
+                    const f32x4 d4 = *(const f32x4 *)(sc.dt + jb);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        mv[r] = fmaf(gg[r], exp2_((rli + tmask[r]) - c4[r]) * d4[r], dadd[r]);
+                }
+                seq_mask<64, PACKED>(mv, sc, jb, sqi);
+            }
+            if (band) {
+                split_h(mv[0], mv[1], ph[2 * half], pl[2 * half]);
+                split_h(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
+            } else {
+                ph[2 * half] = pk_h(mv[0], mv[1]);
+                ph[2 * half + 1] = pk_h(mv[2], mv[3]);
+            }
+        }
+        mx_step<true>(acc, hf.xs, 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
+                      u32x4{pl[0], pl[1], pl[2], pl[3]}, band);
+    }
+}
+
+// Output rows are moved as 16-byte pieces: after the row tile, lane l holds
+// row 16 rt + 4 k + l / 16, columns 4 (l % 16) .. + 3, in out[k]; oy[k] is
+// that piece's offset from the chunk's first row of the head.
+__device__ __forceinline__ void pair_yoff(uint32_t (&oy)[4], const SegArgs &a, int rt) {
+    const int lane = lane_id();
+    const uint32_t ystride = (uint32_t)(a.H * kP);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        oy[k] = (uint32_t)(16 * rt + 4 * k + (lane >> 4)) * ystride + 4 * (lane & 15);
+}
+
+// The reverse pass's rows of y in that layout (read back by the lane that
+// wrote them).
+__device__ __forceinline__ void pair_prev(f32x4 (&prev)[4], const SegArgs &a, const uint32_t (&oy)[4],
+                                          int b, int h, int c0, int len, int rt) {
+    const float *yb = a.y + (tok(a, b, c0) * a.H + h) * kP;
+    if (16 * rt + 16 <= len) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) prev[k] = *(const f32x4 *)(yb + oy[k]);
+        return;
+    }
+    const int lane = lane_id();
+    const uint32_t ystride = (uint32_t)(a.H * kP);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int row = min(16 * rt + 4 * k + (lane >> 4), len - 1);
+        prev[k] = *(const f32x4 *)(yb + (uint32_t)row * ystride + 4 * (lane & 15));
+    }
+}
+
+// acc (matrix-core layout: rows 4 g4 + r, columns 16 pt + l16 of the tile)
+// into the row layout of pair_prev, through the wave's own LDS tile.
+__device__ __forceinline__ void pair_to_rows(f32x4 (&out)[4], const f32x4 (&acc)[4], float *tb) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tb[(4 * g4 + r) * kTS + 16 * pt + l16] = acc[pt][r];
+    // the wave reads what its other lanes wrote: order the LDS accesses
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = *(const f32x4 *)(tb + (4 * k + g4) * kTS + 4 * l16);
+}
+
+// Row tile rt (16 rows) of the chunk for the half's head: intra-chunk form
+// (with D x) and carried state into acc (this lane's outputs: rows
+// 16 rt + 4 g4 + r, columns 16 pt + l16).
+template <bool PACKED, int D>
+__device__ __forceinline__ void pair_row_tile(f32x4 (&acc)[4], const PairSmem &sm,
+                                              const PairHalf &hf, const PairScan &sc, int rt,
+                                              bool has_state, const float (&tmask)[4],
+                                              const float (&dadd)[4]) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+    const int i = 16 * rt + l16, i0 = 16 * rt + 4 * g4;
+    u32x4 cr[kN / 32];
+#pragma unroll
+    for (int ks = 0; ks < kN / 32; ++ks)
+        cr[ks] = *(const u32x4 *)(sm.cn + 16 * rt * kBS + bn_lane(l16) + 32 * ks + 8 * g4);
+    const float rli = sc.cs2[i];
+    const int sqi = PACKED ? sc.sq[i] : 0;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
+    switch (rt) {
+        case 0: pair_diag<PACKED, D, 0>(acc, sm, hf, sc, cr, rli, sqi, tmask, dadd); break;
+        case 1: pair_diag<PACKED, D, 1>(acc, sm, hf, sc, cr, rli, sqi, tmask, dadd); break;
+        case 2: pair_diag<PACKED, D, 2>(acc, sm, hf, sc, cr, rli, sqi, tmask, dadd); break;
+        default: pair_diag<PACKED, D, 3>(acc, sm, hf, sc, cr, rli, sqi, tmask, dadd); break;
+    }
+    // carried state: e^{cs_i} C_i . H (tiles it does not reach: skipped, exact)
+    if (has_state && sc.utile[rt]) {
+        f32x4 tt[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) tt[pt] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < kN / 32; ++ks) {
+            u32x4 oh[4];
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                oh[pt] = *(const u32x4 *)(hf.hs + (16 * pt + l16) * kNRS + 32 * ks + 8 * g4);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32_f16(cr[ks], oh[pt], tt[pt]);
+        }
+        const f32x4 c4 = *(const f32x4 *)(sc.cs2 + i0);
+        float uu[4];
+        if (PACKED) {
+            const int4 s4 = *(const int4 *)(sc.sq + i0);
+            const int nb = sc.sq_nb;
+            uu[0] = s4.x == nb ? exp2_(c4[0]) : 0.f;
+            uu[1] = s4.y == nb ? exp2_(c4[1]) : 0.f;
+            uu[2] = s4.z == nb ? exp2_(c4[2]) : 0.f;
+            uu[3] = s4.w == nb ? exp2_(c4[3]) : 0.f;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) uu[r] = exp2_(c4[r]);
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(uu[r], tt[pt][r], acc[pt][r]);
+    }
+}
+
+// The row tile's outputs (row layout) into y; rows past the chunk's end are
+// not written. With `check`, their sum joins chk (a non-finite output makes
+// it non-finite).
+__device__ __forceinline__ void pair_store(const SegArgs &a, const f32x4 (&out)[4],
+                                           const uint32_t (&oy)[4], int b, int h, int c0, int len,
+                                           int rt, float &chk, bool check) {
+    float *yb = a.y + (tok(a, b, c0) * a.H + h) * kP;
+    if (16 * rt + 16 <= len) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *(f32x4 *)(yb + oy[k]) = out[k];
+    } else {
+        const int lane = lane_id();
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (16 * rt + 4 * k + (lane >> 4) < len) *(f32x4 *)(yb + oy[k]) = out[k];
+    }
+    if (check) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            s0 += out[k][0] + out[k][1];
+            s1 += out[k][2] + out[k][3];
+        }
+        chk += s0 + s1;
+    }
+}
+
+// H <- gamma H + sum over the chunk's tokens of w_t B_t x_t^T for the wave's
+// block of the state: n = 32 v .. 32 v + 31, every p; Hacc[4 nt + pt][r] =
+// H[n = 32 v + 16 nt + 4 g4 + r][p = 16 pt + l16]. B^T and x come from the
+// staged tiles through transposing reads, w x as packed fp16 products.
+__device__ __forceinline__ void pair_state_update(const PairSmem &sm, const PairHalf &hf,
+                                                  const PairScan &sc, f32x4 (&Hacc)[8], int v) {
+    const float gmm = sc.gamma;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) Hacc[q] *= gmm;
+    if (!sc.wsub) return;   // every weight is exactly 0
+    const int g4 = lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        u32x4 aop[2], bx[4];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) aop[nt] = tr_operand_bn(sm.bn, 32 * ks, 32 * v + 16 * nt);
+        const f32x4 w0 = *(const f32x4 *)(sc.w + 32 * ks + 4 * g4);        // k slots 0..3
+        const f32x4 w1 = *(const f32x4 *)(sc.w + 32 * ks + 16 + 4 * g4);   // k slots 4..7
+        const u32x4 wp = {pk_h(w0[0], w0[1]), pk_h(w0[2], w0[3]), pk_h(w1[0], w1[1]), pk_h(w1[2], w1[3])};
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            const u32x4 xv = tr_operand(hf.xs, kXS, 32 * ks, 16 * pt);
+            bx[pt] = u32x4{mul_h(xv[0], wp[0]), mul_h(xv[1], wp[1]), mul_h(xv[2], wp[2]), mul_h(xv[3], wp[3])};
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                Hacc[4 * nt + pt] = mfma16x16x32_f16(aop[nt], bx[pt], Hacc[4 * nt + pt]);
+    }
+}
+
+// Offset in a [p][n] state of this lane's entries of Hacc[4 nt + pt]
+// (4 consecutive n).
+__device__ __forceinline__ int pair_hoff(int v, int q) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+    return (16 * (q & 3) + l16) * kN + 32 * v + 16 * (q >> 2) + 4 * g4;
+}
+
+// The wave's block of the state (fp32 accumulators) into H^T, fp16.
+__device__ __forceinline__ void pair_publish(PairHalf &hf, const f32x4 (&Hacc)[8], int v) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int o = (16 * (q & 3) + l16) * kNRS + 32 * v + 16 * (q >> 2) + 4 * g4;
+        *(u32x2 *)(hf.hs + o) = u32x2{pk_h(Hacc[q][0], Hacc[q][1]), pk_h(Hacc[q][2], Hacc[q][3])};
+    }
+}
+
+// One direction's walk over the segment's chunks for the half's head (wave v
+// of the half owns row tile rt and the state block of n = 32 v .. 32 v + 31).
+// Returns the outgoing state in Hacc.
+template <bool PACKED, int D, bool SP>
+__device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b, int seg, int h,
+                                          int grp, bool add, int half, int v, f32x4 (&Hacc)[8],
+                                          float &chk, bool check) {
+    constexpr int Q = 64;
+    // row tiles mirrored in the second half: the two waves of a SIMD (v and
+    // v + 4) then carry 16-row tiles of complementary causal length
+    const int rt = half == 0 ? v : 3 - v;
+    PairHalf &hf = sm.half[half];
+    const int t0 = seg * a.Ts, t1 = min(t0 + a.Ts, a.L);
+    const int cfirst = t0 / Q, clast = (t1 - 1) / Q;
+    const size_t PN = (size_t)kP * kN;
+    auto slot = [&](int d, int k) { return (((size_t)b * 2 + d) * a.nseg + k) * a.H + h; };
+    const DirPtrs &dp = a.dir[D];
+    const float Dh = dp.D ? dp.D[h] : 0.f;
+    // incoming state of this segment in the walking direction (as seg_pass)
+    const float *src = nullptr;
+    if (D == 0) {
+        if (seg == 0) src = a.init_state ? (a.nseg > 1 ? a.Hs + slot(0, 0) * PN
+                                                        : a.init_state + ((size_t)b * a.H + h) * PN)
+                                         : nullptr;
+        else src = a.gam[slot(0, seg - 1)] == 0.f ? a.S + slot(0, seg - 1) * PN : a.Hs + slot(0, seg) * PN;
+    } else {
+        if (seg == a.nseg - 1) src = nullptr;
+        else src = a.gam[slot(1, seg + 1)] == 0.f ? a.S + slot(1, seg + 1) * PN : a.Hs + slot(1, seg) * PN;
+    }
+    const int nch = clast - cfirst + 1;
+    const bool want_final = D == 0 && seg == a.nseg - 1 && a.final_state;
+    auto chunk_at = [&](int s, int &c0, int &len) {
+        const int c = D == 0 ? cfirst + s : clast - s;
+        c0 = c * Q;
+        len = min(Q, a.L - c0);
+    };
+    PairLoads<PACKED> ld;
+    ld.init(a);
+    f32x4 prev[4];
+    uint32_t oy[4];
+    pair_yoff(oy, a, rt);
+    float *tb = sm.tile[wave_id()];
+    // the scans run on the wave with the shortest row tile
+    const bool scanner = rt == 0;
+    // diagonal tile of row tile rt: lane (g4, l16) holds columns 4 g4 + r of
+    // row l16; those on the far side get an exponent of -inf, the diagonal
+    // entry D
+    float tmask[4], dadd[4];
+    {
+        const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 4 * g4 + r;
+            tmask[r] = (D == 0 ? j <= l16 : j >= l16) ? 0.f : -__builtin_huge_valf();
+            dadd[r] = j == l16 ? Dh : 0.f;
+        }
+    }
+    {
+        int c0, len;
+        chunk_at(0, c0, len);
+        ld.issue(a, D, b, h, grp, c0, len, scanner);
+        if (add) pair_prev(prev, a, oy, b, h, c0, len, rt);
+        if (scanner) pair_scans<PACKED, SP>(a, hf.sc[0], ld.dtv[0], ld.sqv[0], D, b, h, c0, len);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) Hacc[q] = src ? *(const f32x4 *)(src + pair_hoff(v, q)) : zero4();
+    bool has_state = src != nullptr;
+    if (has_state) pair_publish(hf, Hacc, v);
+    for (int s = 0; s < nch; ++s) {
+        int c0, len;
+        chunk_at(s, c0, len);
+        const PairScan &sc = hf.sc[s & 1];
+        ld.store(sm, hf, len);
+        lds_barrier();   // chunk s staged, its scans and the published state visible
+        f32x4 out[4];
+        const bool mine = 16 * rt < len;
+        if (mine) {
+            f32x4 acc[4];
+            pair_row_tile<PACKED, D>(acc, sm, hf, sc, rt, has_state, tmask, dadd);
+            pair_to_rows(out, acc, tb);
+            if (add) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) out[k] += prev[k];
+            }
+        }
+        const bool last = s == nch - 1;
+        int c0n, lenn;
+        chunk_at(last ? s : s + 1, c0n, lenn);
+        // the next chunk's loads (the last chunk re-reads its own) go out
+        // before this tile's stores, which would hold them up in the memory
+        // pipeline, and stay in flight across the state update
+        ld.issue(a, D, b, h, grp, c0n, lenn, scanner);
+        if (add) pair_prev(prev, a, oy, b, h, c0n, lenn, rt);
+        if (mine) pair_store(a, out, oy, b, h, c0, len, rt, chk, check);
+        if (!last || want_final) pair_state_update(sm, hf, sc, Hacc, v);
+        // the next chunk's scans, into the other buffer
+        if (!last && scanner) pair_scans<PACKED, SP>(a, hf.sc[(s + 1) & 1], ld.dtv[0], ld.sqv[0], D, b, h, c0n, lenn);
+        // every wave is done with this chunk's tiles and the published state
+        lds_barrier();
+        if (!last) {
+            pair_publish(hf, Hacc, v);
+            has_state = true;
+        }
+    }
+}
+
+// The split-bf16 recomputation of one head's segment by the four waves from
+// WB. Kept out of line (it runs only after an fp16 overflow, and inlined its
+// registers would crowd the fast path's), with the arguments copied: a
+// reference to the kernel's arguments would move them to private memory for
+// the fast path too.
+template <bool PACKED, bool SP, int WB>
+__device__ __attribute__((noinline)) void pair_exact(const SegArgs a, OutSmem<64> &sm, int b, int seg, int h, int grp) {
+    if (a.ndir == 2) {
+        seg_pass<64, PACKED, 1, SP, false, WB>(a, sm, b, seg, h, grp, false);
+        seg_pass<64, PACKED, 0, SP, false, WB>(a, sm, b, seg, h, grp, true);
+    } else {
+        seg_pass<64, PACKED, 0, SP, false, WB>(a, sm, b, seg, h, grp, false);
+    }
+}
+
+// Both passes of the fp16 form; returns the forward direction's outgoing
+// state in Hacc and the check sum of the last pass in chk.
+template <bool PACKED, bool SP>
+__device__ __forceinline__ void pair_fast(const SegArgs &a, PairSmem &sm, int b, int seg, int h,
+                                                    int grp, int half, int v, f32x4 (&Hacc)[8],
+                                                    float &chk) {
+    if (a.ndir == 2) {
+        pair_pass<PACKED, 1, SP>(a, sm, b, seg, h, grp, false, half, v, Hacc, chk, false);
+        pair_pass<PACKED, 0, SP>(a, sm, b, seg, h, grp, true, half, v, Hacc, chk, true);
+    } else {
+        pair_pass<PACKED, 0, SP>(a, sm, b, seg, h, grp, false, half, v, Hacc, chk, true);
+    }
+}
+
+template <bool PACKED, bool SP>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+k_pair_out(const SegArgs a) {
+    // XCD-aware order as in k_seg_out, over (row-segment, head pair)
+    const int id = blockIdx.x;
+    const int HP = a.H / 2;
+    const int total = a.batch * a.nseg * HP;
+    const int per = (total + 7) / 8;
+    const int lin = (id & 7) * per + (id >> 3);
+    if (lin >= total) return;
+    const int rs = lin / HP, hp = lin % HP;
+    const int b = rs / a.nseg, seg = rs % a.nseg;
+    const int half = wave_id() >> 2, v = wave_id() & 3;
+    const int h = 2 * hp + half;
+    const int grp = (2 * hp) / (a.H / a.G);
+    __shared__ __attribute__((aligned(16))) PairShared sh;
+    f32x4 Hacc[8];
+    float chk = 0.f;
+    pair_fast<PACKED, SP>(a, sh.fast, b, seg, h, grp, half, v, Hacc, chk);
+    const bool want_final = seg == a.nseg - 1 && a.final_state;
+    if (want_final) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) chk += (Hacc[q][0] + Hacc[q][1]) + (Hacc[q][2] + Hacc[q][3]);
+    }
+    const unsigned long long bad = __ballot(!__builtin_isfinite(chk));
+    if (lane_id() == 0) sh.fast.bad[wave_id()] = bad != 0ull;
+    lds_barrier();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) any |= sh.fast.bad[w];
+    if (!any) {
+        if (want_final) {
+            float *fs = a.final_state + ((size_t)b * a.H + h) * (kP * kN);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) *(f32x4 *)(fs + pair_hoff(v, q)) = Hacc[q];
+        }
+        return;
+    }
+    // an fp16 operand overflowed: recompute the segment of both heads exactly
+    lds_barrier();   // every wave has read the flags before the memory is reused
+    if (half == 0) pair_exact<PACKED, SP, 0>(a, sh.slow[0], b, seg, h, grp);
+    else pair_exact<PACKED, SP, 4>(a, sh.slow[1], b, seg, h, grp);
+}
+
+// Segment length: at most 1024 tokens (the reverse pass's outputs, read back
+// by the forward pass, then stay in the caches), shortened until the output
+// kernel has at least 256 workgroups of two heads (one per CU).
 int pick_ts(int batch, int L, int H, int Q) {
-    int ts = 2048;
-    while (ts > Q && (long)batch * ((L + ts - 1) / ts) * H < 512) ts /= 2;
+    int ts = 1024;
+    while (ts > Q && (long)batch * ((L + ts - 1) / ts) * ((H + 1) / 2) < 256) ts /= 2;
     return ts < Q ? Q : ts;
+}
+
+// The pair kernel serves two heads of one group per workgroup.
+bool pair_ok(const SegArgs &a) { return a.H % 2 == 0 && (a.H / a.G) % 2 == 0; }
+
+template <bool SP>
+hipError_t launch_pair(const SegArgs &a, hipStream_t s) {
+    if (a.nseg > 1) {
+        BM_LAUNCH("ssd_seg_state", k_seg_state<SP>, dim3(a.nseg, a.ndir, a.batch * a.H), dim3(kThreads), 0,
+                  s, a);
+        BM_LAUNCH("ssd_seg_scan", k_seg_scan, dim3(kP * kN / 256, a.H, a.batch * a.ndir), dim3(256), 0,
+                  s, a);
+    }
+    const int per_xcd = (a.batch * a.nseg * (a.H / 2) + 7) / 8;
+    if (a.seq)
+        BM_LAUNCH("ssd_pair_out", (k_pair_out<true, SP>), dim3(per_xcd * 8), dim3(512), 0, s, a);
+    else
+        BM_LAUNCH("ssd_pair_out", (k_pair_out<false, SP>), dim3(per_xcd * 8), dim3(512), 0, s, a);
+    return hipGetLastError();
 }
 
 template <int Q, bool SP, bool SPLIT = false>
@@ -1343,6 +2046,10 @@ hipError_t launch_chunked(const Problem &p, void *ws, hipStream_t s) {
         }
         return hipErrorInvalidValue;
     }
+    // the fp16 pair kernel, except for rows of one 64-token chunk with both
+    // directions (the block step), which k_dual_out serves in one pass
+    const bool dual = p.Q == 64 && a.ndir == 2 && !a.seq && a.L <= 64;
+    if (pair_ok(a) && !dual) return sp ? launch_pair<true>(a, s) : launch_pair<false>(a, s);
     switch (p.Q) {
         case 64: return sp ? launch_q<64, true>(a, s) : launch_q<64, false>(a, s);
         case 128: return sp ? launch_q<128, true>(a, s) : launch_q<128, false>(a, s);

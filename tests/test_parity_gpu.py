@@ -223,7 +223,8 @@ def test_full_size_sampled(name):
     y = bm.ssd_fwd(f, b, chunk=w.chunk)
     torch.cuda.synchronize()
     rows = [0, w.batch - 1] if w.batch > 1 else [0]
-    heads = [0, 37] if w.seqlen <= 32768 else [5]
+    # heads spread over the workgroup order (head pairs of both halves)
+    heads = [0, 37] if w.seqlen <= 32768 else [5, 22, 39, 60]
     for r in rows:
         for zero_D in (False, True):
             fr = {k: (v[r:r + 1] if v.dim() > 1 else v) for k, v in f.items()}
@@ -613,3 +614,151 @@ def test_inplace_state_many_segments(bidir):
     err, ok = within(state.double().cpu().numpy(), fs_ref, "bf16")
     print(f"  final state {err:.3e}", flush=True)
     assert ok, f"final state error {err:.3e}"
+
+
+def _scaled(d, **mult):
+    """The same inputs with some arrays multiplied by exact powers of two
+    (the bf16 values stay exact)."""
+    out = dict(d)
+    for k, m in mult.items():
+        out[k] = (d[k].float() * m).to(d[k].dtype).contiguous()
+    return out
+
+
+RANGE_CASES = [
+    # name, per-direction multipliers (powers of two), A scale, D value
+    ("x_beyond_fp16", dict(x=2.0 ** 17), 1.0, None),
+    ("gram_beyond_fp16", dict(B=2.0 ** 9, C=2.0 ** 9), 1.0, None),
+    ("skip_beyond_fp16", dict(), 1.0, 1.0e5),
+    ("state_beyond_fp16", dict(x=2.0 ** 12, B=2.0 ** 4), 0.0, 0.0),
+    ("small_inputs", dict(x=2.0 ** -4, B=2.0 ** -3, C=2.0 ** -3), 1.0, None),
+]
+
+
+@pytest.mark.parametrize("case", RANGE_CASES, ids=[c[0] for c in RANGE_CASES])
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_fp16_range_guard(case, chunk):
+    """The fp16 products overflow at 65504: outputs, states and skip terms
+    beyond that range (reachable with bf16 inputs) are recomputed exactly by
+    the workgroup that meets them; small magnitudes stay within the bar."""
+    name, mult, a_scale, dval = case
+    print(f"range case {name} chunk={chunk}", flush=True)
+    H, P, N = 4, 64, 128
+    f, b = synth.make_inputs(2, 700, H, P, N, 1, "bf16", 171, device=DEV)
+    # scale only the first row's later half, so that other workgroups of the
+    # same launch stay on the fast path
+    def prep(d):
+        e = dict(d)
+        for k, m in mult.items():
+            v = d[k].float().clone()
+            v[0, 350:] *= m
+            e[k] = v.to(d[k].dtype).contiguous()
+        e["A"] = (d["A"] * a_scale).contiguous()
+        if dval is not None:
+            e["D"] = torch.full_like(d["D"], dval)
+        return e
+    f, b = prep(f), prep(b)
+    g = torch.Generator(device=DEV).manual_seed(172)
+    init = torch.randn(2, H, P, N, generator=g, device=DEV) * 0.5
+    got, fs = _run(f, b, chunk, init=init, want_final=True)
+    ref, fs_ref = oracle.bissd(f, b, init_state=init, want_final_state=True)
+    for r in range(2):
+        err, ok = within(got[r], ref[r], "bf16")
+        print(f"  row {r} y error {err:.3e}", flush=True)
+        assert ok, f"{name} row {r}: y error {err:.3e}"
+        err, ok = within(fs[r], fs_ref[r], "bf16")
+        print(f"  row {r} final state error {err:.3e}", flush=True)
+        assert ok, f"{name} row {r}: final state error {err:.3e}"
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(fs))
+
+
+def _cut(d, lo, hi, heads):
+    """Tokens [lo, hi) of heads `heads` of a one-row input, on the host."""
+    out = {}
+    for k, v in d.items():
+        if k in ("x", "dt"):
+            out[k] = v[:, lo:hi][:, :, heads].contiguous().cpu()
+        elif k in ("B", "C"):
+            out[k] = v[:, lo:hi].contiguous().cpu()
+        else:
+            out[k] = v[heads].contiguous().cpu()
+    return out
+
+
+def test_packed_full_size():
+    """The packed batch at full size (32 sequences, lengths U[512, 8192],
+    148 170 tokens, 64 heads x 64, d_state 128, chunk 256) in the benchmark's
+    launch configuration, against the oracle on every token of four heads
+    spread over the workgroup order: every sequence and both edges of each,
+    with D and with D = 0."""
+    w = synth.packed_workload()
+    cu = synth.cu_seqlens_of(w.seqlens)
+    assert len(cu) == 33 and cu[-1] == w.seqlen
+    f, b = synth.make_inputs(1, w.seqlen, w.nheads, w.headdim, w.d_state, w.ngroups,
+                             w.dtype, w.seed, device=DEV)
+    heads = [3, 20, 41, 62]
+    for zero_D in (False, True):
+        ff, bb = (_zero_D(f), _zero_D(b)) if zero_D else (f, b)
+        y = bm.ssd_fwd(ff, bb, chunk=w.chunk, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        got = y[:, :, heads].double().cpu().numpy()
+        del y
+        ref = oracle.bissd(_cut(ff, 0, w.seqlen, heads), _cut(bb, 0, w.seqlen, heads), cu_seqlens=cu)
+        err, ok = within(got, ref, "bf16")
+        print(f"packed full size zero_D={zero_D}: {err:.3e}", flush=True)
+        assert ok, f"packed full size zero_D={zero_D}: {err:.3e}"
+        # every sequence separately, with its two edge tokens
+        for i in range(32):
+            sl = slice(cu[i], cu[i + 1])
+            e_i, ok_i = within(got[:, sl], ref[:, sl], "bf16")
+            assert e_i <= 1e-2 * 2, f"sequence {i}: {e_i:.3e}"
+
+
+@pytest.mark.parametrize("nseq", [1, 16])
+def test_block_step_long_prefix(nseq):
+    """The decode step at the cached-decode shape (80 heads x 64, d_state 128,
+    block 64) from the state of a 262 144-token prefix built as the benchmark
+    builds it: 8192-token pieces, each resuming the cache in place. The oracle
+    follows the same pieces in fp64 on three heads; the step and its commit
+    are checked against it."""
+    c = synth.BLOCK_STEP
+    H, P, N, G, Lb = c["nheads"], c["headdim"], c["d_state"], c["ngroups"], c["block"]
+    heads = [0, 41, 79]
+    prefix, seg = c["prefix"], 8192
+    st = bm.State(nseq, H, P, N)
+    ref_state = np.zeros((nseq, len(heads), P, N))
+    done, k = 0, 0
+    while done < prefix:
+        n = min(seg, prefix - done)
+        pf, _ = synth.make_inputs(nseq, n, H, P, N, G, "bf16", c["seed"] * 1000 + k,
+                                  device=DEV, bidirectional=False)
+        bm.ssd_fwd(pf, None, chunk=256, init_state=st.tensor(), final_state=st.tensor())
+        host = {kk: (v[:, :, heads].contiguous().cpu() if kk in ("x", "dt") else
+                     (v.cpu() if kk in ("B", "C") else v[heads].cpu())) for kk, v in pf.items()}
+        _, ref_state = oracle.bissd(host, None, init_state=ref_state, want_final_state=True)
+        done += n
+        k += 1
+        del pf
+    torch.cuda.synchronize()
+    err, ok = within(st.tensor()[:, heads].double().cpu().numpy(), ref_state, "bf16")
+    print(f"prefix state b{nseq}: {err:.3e}", flush=True)
+    assert ok, f"prefix state error {err:.3e}"
+    f, b = synth.make_inputs(nseq, Lb, H, P, N, G, "bf16", c["seed"], device=DEV)
+    state0 = st.tensor()[:, heads].double().cpu().numpy()
+    y = bm.block_step(st, f, b, commit=False, chunk=64)
+    torch.cuda.synchronize()
+    fr, br = _heads(f, heads), _heads(b, heads)
+    ref, _ = oracle.block_step(ref_state, fr, br, commit=False)
+    err, ok = within(y[:, :, heads].double().cpu().numpy(), ref, "bf16")
+    print(f"block step from the long prefix b{nseq}: {err:.3e}", flush=True)
+    assert ok, f"y error {err:.3e}"
+    assert np.array_equal(st.tensor()[:, heads].double().cpu().numpy(), state0)
+    y = bm.block_step(st, f, b, commit=True, chunk=64)
+    torch.cuda.synchronize()
+    ref, new_state = oracle.block_step(ref_state, fr, br, commit=True)
+    err, ok = within(y[:, :, heads].double().cpu().numpy(), ref, "bf16")
+    assert ok, f"committing step y error {err:.3e}"
+    err, ok = within(st.tensor()[:, heads].double().cpu().numpy(), new_state, "bf16")
+    print(f"  committed state {err:.3e}", flush=True)
+    assert ok, f"committed state error {err:.3e}"
+    st.free()
