@@ -186,6 +186,34 @@ def ssd_bwd(fwd, bwd, dy, grads=None, workspace=None, stream=None):
     return gf, gb
 
 
+def ssd_fwd_noalloc(fwd, bwd, y, chunk=256, cu_seqlens=None, init_state=None,
+                    final_state=None, stream=None, dt_softplus=False):
+    """bimamba_ssd_fwd_noalloc: ssd_fwd with the library's static device
+    buffer as its workspace (the call allocates nothing; y is the caller's
+    float32 [b,L,H,P]). Returns y."""
+    x = fwd["x"]
+    dims = _dims(fwd)
+    batch, L, H, P, G, N = dims
+    shape = make_shape(x, fwd["B"], chunk, dt_softplus=dt_softplus)
+    dev = _cuda_device(x)
+    fd = _dir(fwd, x.dtype, dims, dev, "fwd")
+    bd = _dir(bwd, x.dtype, dims, dev, "bwd") if bwd is not None else None
+    cu_arr, nseq = None, 0
+    if cu_seqlens is not None:
+        vals = [int(v) for v in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+        nseq = len(vals) - 1
+        cu_arr = (ctypes.c_int32 * len(vals))(*vals)
+    units = nseq if cu_seqlens is not None else batch
+    for t, name in ((init_state, "init_state"), (final_state, "final_state")):
+        if t is not None:
+            _check(t, name, (units, H, P, N), torch.float32, dev)
+    _check(y, "y", (batch, L, H, P), torch.float32, dev)
+    _abi.check(lib().bimamba_ssd_fwd_noalloc(
+        ctypes.byref(shape), ctypes.byref(fd), ctypes.byref(bd) if bd is not None else None,
+        cu_arr, nseq, _ptr(init_state), _ptr(final_state), _ptr(y), _stream(stream)))
+    return y
+
+
 def ssd_fwd_streams(fwd, bwd, chunk=256, cu_seqlens=None, init_state=None,
                     final_state=None, y_fwd=None, y_bwd=None, workspace=None, stream=None):
     """bimamba_ssd_fwd_streams: the two streams' outputs kept apart.

@@ -22,8 +22,9 @@ EXPORTS = (
     "bimamba_last_error", "bimamba_version", "bimamba_profile_begin",
     "bimamba_profile_end", "bimamba_conv1d_workspace_size", "bimamba_conv1d",
     "bimamba_ssd_bwd_workspace_size", "bimamba_ssd_bwd", "bimamba_gated_norm",
-    "bimamba_ssd_fwd_streams", "bimamba_merge_linear",
+    "bimamba_ssd_fwd_streams", "bimamba_merge_linear", "bimamba_ssd_fwd_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Shape(ctypes.Structure):
@@ -105,6 +106,7 @@ def load():
     lib.bimamba_ssd_bwd.argtypes = [sp, dp, dp, vp, gp, gp, vp, ctypes.c_size_t, vp]
     lib.bimamba_ssd_fwd_streams.argtypes = [sp, dp, dp, i32p, ctypes.c_int, vp, vp, vp, vp,
                                             vp, ctypes.c_size_t, vp]
+    lib.bimamba_ssd_fwd_noalloc.argtypes = [sp, dp, dp, i32p, ctypes.c_int, vp, vp, vp, vp]
     lib.bimamba_merge_linear.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
                                          vp, vp, vp, vp, vp, vp]
     lib.bimamba_gated_norm.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,

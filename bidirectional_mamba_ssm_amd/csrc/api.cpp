@@ -94,10 +94,13 @@ bool use_chunked(const bimamba_shape *s) {
 }
 
 struct Layout {
-    size_t cu_off = 0, seq_off = 0, scan_off = 0, total = 0;
+    size_t cu_off = 0, seq_off = 0, scan_off = 0, scan_bytes = 0, total = 0;
 };
 
-Layout workspace_layout(const bimamba_shape *s, int nseq) {
+// limit: the largest workspace available (SIZE_MAX: as much as the fastest
+// form needs). Under a limit the chunked scan lengthens its segments and the
+// token-sequential scan runs whole rows; the packed-sequence tables must fit.
+Layout workspace_layout(const bimamba_shape *s, int nseq, size_t limit = SIZE_MAX) {
     Layout w;
     size_t off = 0;
     if (nseq > 0) {
@@ -107,10 +110,14 @@ Layout workspace_layout(const bimamba_shape *s, int nseq) {
         off += align256((size_t)s->seqlen * 4);
     }
     w.scan_off = off;
-    if (use_chunked(s))
-        off += chunked_workspace(s->batch, s->seqlen, s->nheads, s->ngroups, s->chunk);
-    else
-        off += seq_workspace(s->batch, s->seqlen, s->nheads, s->headdim, s->d_state, nseq > 0);
+    const size_t rest = limit > off ? limit - off : 0;
+    if (use_chunked(s)) {
+        w.scan_bytes = chunked_workspace(s->batch, s->seqlen, s->nheads, s->ngroups, s->chunk, rest);
+    } else {
+        w.scan_bytes = seq_workspace(s->batch, s->seqlen, s->nheads, s->headdim, s->d_state, nseq > 0);
+        if (w.scan_bytes > rest) w.scan_bytes = 0;   // whole rows need none
+    }
+    off += w.scan_bytes;
     w.total = off;
     return w;
 }
@@ -302,14 +309,17 @@ int bimamba_ssd_workspace_size(const bimamba_shape *s, int nseq, size_t *bytes) 
 
 }  // extern "C"
 
-namespace {
+namespace bm {
 
 // The forward scan. y2 == nullptr: y = sum of the streams; else y receives
-// the reverse stream and y2 the forward stream.
+// the reverse stream and y2 the forward stream. limit: as workspace_layout.
+int api_fail(int code, const char *msg) { return fail(code, "%s", msg); }
+
 int ssd_fwd_impl(const bimamba_shape *s, const bimamba_dir *fwd,
                  const bimamba_dir *bwd, const int32_t *cu_seqlens, int nseq,
                  const float *init_state, float *final_state, float *y, float *y2,
-                 void *workspace, size_t workspace_bytes, bimamba_stream stream) {
+                 void *workspace, size_t workspace_bytes, bimamba_stream stream,
+                 size_t limit, bool validate_only) {
     int rc = check_shape(s, false);
     if (rc) return rc;
     const bool empty = s->seqlen == 0;
@@ -327,7 +337,11 @@ int ssd_fwd_impl(const bimamba_shape *s, const bimamba_dir *fwd,
     } else if (nseq != 0) {
         return fail(BIMAMBA_EINVAL, "nseq %d given without cu_seqlens", nseq);
     }
-    const Layout w = workspace_layout(s, cu_seqlens ? nseq : 0);
+    const Layout w = workspace_layout(s, cu_seqlens ? nseq : 0, limit);
+    if (w.total > limit)
+        return fail(BIMAMBA_EWORKSPACE, "the packed-sequence tables need %zu bytes, more than %zu",
+                    w.total, limit);
+    if (validate_only) return BIMAMBA_OK;
     if (w.total > 0) {
         if (!workspace) return fail(BIMAMBA_EWORKSPACE, "workspace of %zu bytes required", w.total);
         if (workspace_bytes < w.total)
@@ -365,16 +379,17 @@ int ssd_fwd_impl(const bimamba_shape *s, const bimamba_dir *fwd,
         p.cu_dev = cu_dev;
         p.seq_idx = seq;
     }
+    void *scan_ws = w.scan_bytes ? (char *)workspace + w.scan_off : nullptr;
     if (use_chunked(s)) {
-        if ((e = launch_chunked(p, (char *)workspace + w.scan_off, st)) != hipSuccess)
+        if ((e = launch_chunked(p, scan_ws, limit - w.scan_off, st)) != hipSuccess)
             return hip_fail(e, "chunked scan launch");
-    } else if ((e = launch_scan_seq(p, (char *)workspace + w.scan_off, st)) != hipSuccess) {
+    } else if ((e = launch_scan_seq(p, scan_ws, st)) != hipSuccess) {
         return hip_fail(e, "scan launch");
     }
     return BIMAMBA_OK;
 }
 
-}  // namespace
+}  // namespace bm
 
 extern "C" {
 
@@ -384,7 +399,7 @@ int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
                     void *workspace, size_t workspace_bytes,
                     bimamba_stream stream) {
     return ssd_fwd_impl(s, fwd, bwd, cu_seqlens, nseq, init_state, final_state, y, nullptr,
-                        workspace, workspace_bytes, stream);
+                        workspace, workspace_bytes, stream, SIZE_MAX, false);
 }
 
 int bimamba_ssd_fwd_streams(const bimamba_shape *s, const bimamba_dir *fwd,
@@ -400,7 +415,7 @@ int bimamba_ssd_fwd_streams(const bimamba_shape *s, const bimamba_dir *fwd,
     if (!aligned16(y_fwd)) return fail(BIMAMBA_EINVAL, "y_fwd must be 16-byte aligned");
     if (y_fwd == y_bwd && !empty) return fail(BIMAMBA_EINVAL, "y_fwd and y_bwd must differ");
     return ssd_fwd_impl(s, fwd, bwd, cu_seqlens, nseq, init_state, final_state, y_bwd, y_fwd,
-                        workspace, workspace_bytes, stream);
+                        workspace, workspace_bytes, stream, SIZE_MAX, false);
 }
 
 int bimamba_state_alloc(bimamba_state **out, int nslots, int nheads, int headdim,
@@ -486,7 +501,7 @@ int bimamba_block_step(bimamba_state *st, const bimamba_shape *s,
     // workspace then (each workgroup reads its slice of the cache before it
     // writes it back, so the in-place update is safe)
     hipError_t e = chunked_supported(p) && chunked_workspace(p.batch, p.L, p.H, p.G, p.Q) == 0
-                       ? launch_chunked(p, nullptr, (hipStream_t)stream)
+                       ? launch_chunked(p, nullptr, 0, (hipStream_t)stream)
                        : launch_scan_seq(p, nullptr, (hipStream_t)stream);
     return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "block step launch");
 }

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/bimamba.h"
+
 namespace bm {
 
 struct DirPtrs {
@@ -49,10 +51,24 @@ hipError_t launch_seq_index(const int32_t *cu_host, int nseq, int total,
 hipError_t launch_zero_slots(float *data, size_t slot_elems, const int32_t *slots,
                              int n, int nslots, hipStream_t s);
 
+// api.cpp: the forward scan behind bimamba_ssd_fwd (validation, workspace
+// layout within `limit` bytes, launches); returns a bimamba_status. With
+// validate_only it checks the arguments (no HIP call) and returns.
+int ssd_fwd_impl(const bimamba_shape *s, const bimamba_dir *fwd, const bimamba_dir *bwd,
+                 const int32_t *cu_seqlens, int nseq, const float *init_state,
+                 float *final_state, float *y, float *y2, void *workspace,
+                 size_t workspace_bytes, bimamba_stream stream, size_t limit,
+                 bool validate_only);
+// api.cpp: records a failure for bimamba_last_error and returns `code`
+int api_fail(int code, const char *msg);
+
 // ssd_chunked.hip: matrix-core chunked scan (bf16, headdim 64, d_state 128)
 bool chunked_supported(const Problem &p);
-size_t chunked_workspace(int batch, int L, int H, int G, int Q);
-hipError_t launch_chunked(const Problem &p, void *ws, hipStream_t s);
+// limit: the largest workspace the caller can give; segments are lengthened
+// until their states fit (a whole row per segment needs none). The size
+// query and the launch must be given the same limit.
+size_t chunked_workspace(int batch, int L, int H, int G, int Q, size_t limit = SIZE_MAX);
+hipError_t launch_chunked(const Problem &p, void *ws, size_t limit, hipStream_t s);
 
 // ssd_seq.hip: token-sequential scan, any (P <= 128, N in {16,32,64,128}).
 // Long unpacked rows with few (row, head) pairs run in segments when the

@@ -1937,13 +1937,28 @@ k_pair_out(const SegArgs a) {
     else pair_exact<PACKED, SP, 4>(a, sh.slow[1], b, seg, h, grp);
 }
 
+size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace of segment length ts: the segment states S, Hs and the carry
+// factors when a row has more than one segment.
+size_t seg_workspace(int batch, int L, int H, long ts) {
+    const size_t nseg = (size_t)((L + ts - 1) / ts);
+    if (nseg <= 1) return 0;   // one segment per row: no segment states
+    const size_t st = (size_t)batch * 2 * nseg * H * (size_t)(kP * kN) * 4;
+    return al256(st) * 2 + al256((size_t)batch * 2 * nseg * H * 4);
+}
+
 // Segment length: at most 1024 tokens (the reverse pass's outputs, read back
 // by the forward pass, then stay in the caches), shortened until the output
-// kernel has at least 256 workgroups of two heads (one per CU).
-int pick_ts(int batch, int L, int H, int Q) {
-    int ts = 1024;
+// kernel has at least 256 workgroups of two heads (one per CU); then, with a
+// workspace limit, doubled until the segment states fit in it (a whole row is
+// one segment and needs none).
+int pick_ts(int batch, int L, int H, int Q, size_t limit) {
+    long ts = 1024;
     while (ts > Q && (long)batch * ((L + ts - 1) / ts) * ((H + 1) / 2) < 256) ts /= 2;
-    return ts < Q ? Q : ts;
+    if (ts < Q) ts = Q;
+    while (ts < L && seg_workspace(batch, L, H, ts) > limit) ts *= 2;
+    return (int)(ts < L ? ts : (L > Q ? L : Q));
 }
 
 // The pair kernel serves two heads of one group per workgroup.
@@ -1990,8 +2005,6 @@ hipError_t launch_q(const SegArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
-
 }  // namespace
 
 bool chunked_supported(const Problem &p) {
@@ -1999,23 +2012,19 @@ bool chunked_supported(const Problem &p) {
            (p.Q == 64 || p.Q == 128 || p.Q == 256);
 }
 
-size_t chunked_workspace(int batch, int L, int H, int G, int Q) {
-    const int ts = pick_ts(batch, L, H, Q);
-    const size_t nseg = (size_t)(L + ts - 1) / ts;
+size_t chunked_workspace(int batch, int L, int H, int G, int Q, size_t limit) {
     (void)G;
-    if (nseg == 1) return 0;   // one segment per row: no segment states
-    const size_t st = batch * 2 * nseg * H * (size_t)(kP * kN) * 4;
-    return al256(st) * 2 + al256(batch * 2 * nseg * H * 4);
+    return seg_workspace(batch, L, H, pick_ts(batch, L, H, Q, limit));
 }
 
-hipError_t launch_chunked(const Problem &p, void *ws, hipStream_t s) {
+hipError_t launch_chunked(const Problem &p, void *ws, size_t limit, hipStream_t s) {
     SegArgs a;
     a.dir[0] = p.dir[0];
     a.dir[1] = p.dir[1];
     a.ndir = p.has_bwd ? 2 : 1;
     a.batch = p.batch; a.L = p.L; a.H = p.H; a.G = p.G;
     a.nC = (p.L + p.Q - 1) / p.Q;
-    a.Ts = pick_ts(p.batch, p.L, p.H, p.Q);
+    a.Ts = pick_ts(p.batch, p.L, p.H, p.Q, limit);
     a.nseg = (p.L + a.Ts - 1) / a.Ts;
     a.seq = p.seq_idx;
     const size_t nseg = a.nseg;

@@ -131,6 +131,25 @@ int bimamba_ssd_fwd(const bimamba_shape *s, const bimamba_dir *fwd,
                     void *workspace, size_t workspace_bytes,
                     bimamba_stream stream);
 
+/* bimamba_ssd_fwd with no device allocation, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Arguments and results as bimamba_ssd_fwd, without the
+ * workspace: the library's own static device buffer of
+ * BIMAMBA_NOALLOC_SCRATCH_BYTES serves instead, held by every device the
+ * library runs on until the process ends (its address is looked up once per
+ * device). Within that buffer the scan lengthens its segments until their
+ * states fit (a row that is one segment needs none), so every shape
+ * bimamba_ssd_fwd accepts runs, except packed batches whose sequence tables
+ * ((nseq + 1) * 4 + seqlen * 4 bytes, each rounded up to 256) exceed the
+ * buffer: those return BIMAMBA_EWORKSPACE before any HIP call. Calls that
+ * overlap on one device share the buffer and race: order them on one stream
+ * (or synchronize). Nothing in the buffer needs clearing. */
+#define BIMAMBA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int bimamba_ssd_fwd_noalloc(const bimamba_shape *s, const bimamba_dir *fwd,
+                            const bimamba_dir *bwd, const int32_t *cu_seqlens, int nseq,
+                            const float *init_state, float *final_state, float *y,
+                            bimamba_stream stream);
+
 /* The same scan with the two streams kept apart, for the concatenating merge
  * (DiffuMamba blog, "network architecture": the block concatenates the
  * forward and the flipped-back reverse output and applies a Linear layer;
