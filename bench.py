@@ -2,24 +2,29 @@
 """Benchmark of the bidirectional Mamba-2 SSD mixer on one MI355X.
 
 A step is one bidirectional bimamba_ssd_fwd call (every kernel of the scan:
-planning, chunk states, state passing, outputs) over one batch of synthetic
-input already resident in HBM. The headline workload is one mixer layer of a
-DiffuMamba-1.3B-shaped model at its training length: batch 8 x 1024 tokens,
-64 heads x headdim 64 (d_inner 4096), d_state 128, chunk 256, bf16 inputs,
-fp32 accumulation and output.
+segment states, state passing, outputs) over one batch of synthetic input
+already resident in HBM. The headline workload is the long-sequence prefill
+at 131 072 tokens (batch 1, 64 heads x headdim 64 = d_inner 4096 of a
+1.3B-shaped model, d_state 128, chunk 256, bf16 inputs, fp32 accumulation and
+output), the largest single-GPU configuration and the one the >= 60 % HBM
+roofline target is set on.
 
 Prints ONE JSON line. Besides the contract fields it carries:
+  settle        the untimed fixed-duration phase that brings the clocks to
+                their steady state before the warm-up and the timed steps
   roofline      HBM roofline of the dominant kernel (algorithmic bytes per
                 launch / its average HIP-event duration over the timed steps);
                 `traffic` is the measured HBM bytes per launch from the
-                committed counter summary when it was taken on the kernel
-                source as it stands, else null
-  mfma          the same launches against the dense bf16 matrix-core peak,
-                counting the algorithmic flops of the chunked SSD form
+                committed counter summary of that kernel and workload when it
+                was taken on the kernel source as it stands, else null
+  mfma          the same launches against the dense fp16/bf16 matrix-core
+                peak, counting the algorithmic flops of the chunked form
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded
-                sample of the same inputs, with its parity against the GPU
-  extra         the long-sequence (32k, 128k), packed-varlen and cached
-                block-step workloads, each with its own roofline fraction
+                sample of the same inputs (a subset of the heads, every
+                token), with its parity against the GPU
+  extra         the training-length layer, the 32k prefill, the latency fit
+                time(L) = a + bL + cL^2, slowly decaying heads, the packed
+                batch, the cached block step and the follow-on kernels
 """
 import argparse
 import json
@@ -35,9 +40,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_FP32_PEAK_TFLOPS = 157.3   # dense fp32 matrix (and vector) peak
 METRIC = "BiMamba-2 SSD tokens/s + % HBM/MFMA roofline; block-cached step ms"
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ssd_seg_out_layer_1p3b_train_hbm_traffic.md")
-MIX_SUMMARY = os.path.join(ROOT, "profiles", "ssd_seg_out_layer_1p3b_train_instruction_mix.md")
 KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_mamba_ssm_amd", "csrc", "ssd_chunked.hip")
+TILE = 64   # block length of the matrix-core kernel's decomposition (every chunk size)
+
+
+def summary_path(kernel, workload, kind):
+    """Committed rocprofv3 summary of one kernel on one workload."""
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_{kind}.md")
 
 
 def bytes_per_token(H, P, N, G, elem):
@@ -78,9 +87,10 @@ def summary_field(path, key):
         return None
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE)."""
-    return summary_field(TRAFFIC_SUMMARY, "traffic_bytes_per_launch")
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of a kernel (FETCH_SIZE + WRITE_SIZE), from its
+    committed counter summary, or None."""
+    return summary_field(summary_path(kernel, workload, "hbm_traffic"), "traffic_bytes_per_launch")
 
 
 def parse():
@@ -88,8 +98,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     # the GPU takes some tens of milliseconds of work to reach its steady
     # clock; the default warm-up covers that
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed seconds of steps before the warm-up (steady clocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--prefix", type=int, default=262144,
@@ -104,12 +116,25 @@ def parse():
                     help="only the concatenating-merge lines (one JSON object)")
     ap.add_argument("--conv-only", action="store_true",
                     help="only the short-convolution line (one JSON object)")
-    ap.add_argument("--workload", default="layer_1p3b_train",
+    ap.add_argument("--workload", default="long_128k",
                     help="workload of the main line (a name in synth.WORKLOADS)")
     ap.add_argument("--chunk", type=int, default=None, help="chunk of the main line (default: the workload's)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
+
+
+def settle(fn, seconds, torch):
+    """Runs fn untimed for at least `seconds` (the GPU reaches its steady
+    clock after some tens of milliseconds of work). Returns the calls made."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
 
 
 def time_steps(bm, fn, steps, warmup, torch, live=True):
@@ -300,12 +325,15 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(torch, dev)
 
+    t0 = time.perf_counter()
+    n_settle = settle(step, args.settle_s, torch)
+    settle_s = time.perf_counter() - t0
     ms, wall, ker, dom = time_steps(bm, step, args.steps, args.warmup, torch)
     tokens = w.batch * w.seqlen
     bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
-    fpt = flops_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, w.chunk)
+    fpt = flops_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, TILE)
     # the dominant kernel reads every input of the step once and writes y
-    roof = roofline_for(ker, dom, bpt * tokens, measured_traffic() if dom == "ssd_seg_out" else None)
+    roof = roofline_for(ker, dom, bpt * tokens, measured_traffic(dom, w.name))
 
     out = {
         "metric": METRIC,
@@ -324,11 +352,14 @@ def main():
                    "nheads": w.nheads, "headdim": w.headdim, "d_state": w.d_state,
                    "ngroups": w.ngroups, "chunk": w.chunk, "bidirectional": True,
                    "parallelism": "none (1 GPU)"},
+        "settle": {"seconds": round(settle_s, 3), "steps": n_settle},
         "roofline": roof,
         "mfma": mfma_for(ker, dom, fpt * tokens,
-                         summary_field(MIX_SUMMARY, "executed_mfma_flops_per_launch")),
+                         summary_field(summary_path(dom, w.name, "instruction_mix"),
+                                       "executed_mfma_flops_per_launch")),
         "algorithmic_bytes_per_token": bpt,
         "algorithmic_flops_per_token": fpt,
+        "hbm_roofline_frac_step": round(bpt * tokens / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_ms_per_step": {k: round(t / args.steps, 4) for k, (c, t) in ker.items()},
         "wall_s_timed": round(wall, 3),
     }
@@ -337,55 +368,84 @@ def main():
         # per-step distribution, warm and with the caches flushed before each
         # step (after the timed loop, so a profile of --no-extra sees only it)
         flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
-        out["step_ms_warm"] = step_stats(step, 50, torch)
-        out["step_ms_cold_cache"] = step_stats(step, 50, torch, flush=flush)
+        out["step_ms_warm"] = step_stats(step, 30, torch)
+        out["step_ms_cold_cache"] = step_stats(step, 30, torch, flush=flush)
         del flush
         torch.cuda.empty_cache()
-        out["extra"] = extras(args, bm, synth, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(f, b, y, w, torch, np)
+    del f, b, y, ws
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        out["extra"] = extras(args, bm, synth, torch, dev)
     print(json.dumps(out), flush=True)
 
 
-def extras(args, bm, synth, torch, dev):
-    res = {}
-    steps = max(3, args.steps // 4)
-    for name in ("long_32k", "long_128k"):
-        w = synth.WORKLOADS[name]
-        f, b = synth.make_workload(w, device=dev)
-        y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=dev)
-        shape = bm.make_shape(f["x"], f["B"], w.chunk)
-        ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=dev)
-        fn = lambda: bm.ssd_fwd(f, b, chunk=w.chunk, y=y, workspace=ws)  # noqa: E731
-        ms, _, ker, dom = time_steps(bm, fn, steps, max(2, args.warmup // 10), torch)
-        tok = w.batch * w.seqlen
-        bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
-        fpt = flops_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, w.chunk)
-        res[name] = {"tokens_per_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-                     "hbm_roofline_frac_step": round(bpt * tok / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "kernels_ms_per_step": {k: round(t / steps, 4) for k, (c, t) in ker.items()},
-                     "roofline": roofline_for(ker, dom, bpt * tok),
-                     "mfma": mfma_for(ker, dom, fpt * tok)}
-        del f, b, y, ws
-        torch.cuda.empty_cache()
+def scan_line(bm, torch, f, b, w, chunk, steps, warmup, cu=None, traffic=True):
+    """Times one bidirectional scan workload; its own roofline line."""
+    y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=f["x"].device)
+    shape = bm.make_shape(f["x"], f["B"], chunk)
+    nseq = len(cu) - 1 if cu is not None else 0
+    ws = torch.empty(max(bm.workspace_size(shape, nseq), 256), dtype=torch.uint8, device=f["x"].device)
+    fn = lambda: bm.ssd_fwd(f, b, chunk=chunk, cu_seqlens=cu, y=y, workspace=ws)  # noqa: E731
+    settle(fn, 0.2, torch)
+    ms, _, ker, dom = time_steps(bm, fn, steps, warmup, torch)
+    tok = w.batch * w.seqlen
+    bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
+    fpt = flops_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, TILE)
+    res = {"tokens_per_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+           "hbm_roofline_frac_step": round(bpt * tok / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "kernels_ms_per_step": {k: round(t / steps, 4) for k, (c, t) in ker.items()},
+           "roofline": roofline_for(ker, dom, bpt * tok, measured_traffic(dom, w.name) if traffic else None),
+           "mfma": mfma_for(ker, dom, fpt * tok)}
+    del y, ws
+    return res
 
-    # the headline layer and the 32k prefill with 64-token chunks: the same
-    # operator through a smaller block decomposition (4-wave workgroups, two
-    # per CU), for comparison with the configured chunk of 256
+
+def extras(args, bm, synth, torch, dev):
+    import numpy as np
+    res = {}
+    steps = max(3, args.steps // 2)
+    # one mixer layer at the training length (8 x 1024 tokens), and the 32k prefill
     for name in ("layer_1p3b_train", "long_32k"):
         w = synth.WORKLOADS[name]
         f, b = synth.make_workload(w, device=dev)
-        y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=dev)
-        shape = bm.make_shape(f["x"], f["B"], 64)
-        ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=dev)
-        fn = lambda: bm.ssd_fwd(f, b, chunk=64, y=y, workspace=ws)  # noqa: E731
-        ms, _, ker, dom = time_steps(bm, fn, steps, max(2, args.warmup // 10), torch)
-        tok = w.batch * w.seqlen
-        bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
-        res[name + "_chunk64"] = {"tokens_per_s": round(tok / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-                                  "hbm_roofline_frac_step": round(bpt * tok / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
-        del f, b, y, ws
+        res[name] = scan_line(bm, torch, f, b, w, w.chunk, max(steps, 50), 10)
+        del f, b
         torch.cuda.empty_cache()
+
+    # latency against length at batch 1 (the long-prefill shape): the fit
+    # time(L) = a + b L + c L^2 splits it into a constant, a linear and a
+    # quadratic part; a scan's quadratic part should be ~0
+    base = synth.WORKLOADS["long_128k"]
+    lens = [1024, 4096, 16384, 32768, 65536, 131072]
+    times = []
+    import dataclasses
+    for L in lens:
+        w = dataclasses.replace(base, seqlen=L)
+        f, b = synth.make_workload(w, device=dev)
+        r = scan_line(bm, torch, f, b, w, w.chunk, max(10, min(200, 4 * 131072 // L)), 5, traffic=False)
+        times.append(r["ms_per_step"])
+        del f, b
+        torch.cuda.empty_cache()
+    Lv = np.array(lens, dtype=np.float64)
+    coef, *_ = np.linalg.lstsq(np.stack([np.ones_like(Lv), Lv, Lv ** 2], 1), np.array(times), rcond=None)
+    a, bl, c = (float(v) for v in coef)
+    res["latency_fit"] = {"lengths": lens, "ms_per_step": times,
+                          "fit_ms": {"a": round(a, 5), "b_per_token": bl, "c_per_token2": c},
+                          "quadratic_share_at_131072": round(c * 131072 ** 2 / times[-1], 5),
+                          "linear_share_at_131072": round(bl * 131072 / times[-1], 5)}
+
+    # slowly decaying heads (A scaled by 1e-2): the carried state reaches far,
+    # so no exact-zero decay lets any work be skipped
+    w = base
+    f, b = synth.make_workload(w, device=dev)
+    f = dict(f, A=(f["A"] * 1e-2).contiguous())
+    b = dict(b, A=(b["A"] * 1e-2).contiguous())
+    res["long_128k_slow_decay"] = dict(scan_line(bm, torch, f, b, w, w.chunk, steps, 5, traffic=False),
+                                       A_scale=1e-2)
+    del f, b
+    torch.cuda.empty_cache()
 
     # the secondary reading of the long-prefill shape: the tiny head shape
     # (4 heads x headdim 16, d_state 16) at 131 072 tokens, chunk 256, bf16
@@ -410,20 +470,12 @@ def extras(args, bm, synth, torch, dev):
     f, b = synth.make_inputs(1, w.seqlen, w.nheads, w.headdim, w.d_state, w.ngroups,
                              w.dtype, w.seed, device=dev)
     cu = synth.cu_seqlens_of(w.seqlens)
-    y = torch.empty(1, w.seqlen, w.nheads, w.headdim, dtype=torch.float32, device=dev)
-    shape = bm.make_shape(f["x"], f["B"], w.chunk)
-    ws = torch.empty(max(bm.workspace_size(shape, len(cu) - 1), 256), dtype=torch.uint8, device=dev)
-    fn = lambda: bm.ssd_fwd(f, b, chunk=w.chunk, cu_seqlens=cu, y=y, workspace=ws)  # noqa: E731
-    ms, _, ker, dom = time_steps(bm, fn, steps, max(2, args.warmup // 10), torch)
-    bpt = bytes_per_token(w.nheads, w.headdim, w.d_state, w.ngroups, 2)
-    res["packed_varlen"] = {"tokens_per_s": round(w.seqlen / (ms / 1e3), 1),
-                            "ms_per_step": round(ms, 4), "tokens": w.seqlen, "nseq": len(cu) - 1,
-                            "hbm_roofline_frac_step": round(bpt * w.seqlen / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "kernels_ms_per_step": {k: round(t / steps, 4) for k, (c, t) in ker.items()}}
-    del f, b, y, ws
+    res["packed_varlen"] = dict(scan_line(bm, torch, f, b, w, w.chunk, steps, 5, cu=cu),
+                                tokens=w.seqlen, nseq=len(cu) - 1)
+    del f, b
     torch.cuda.empty_cache()
 
-    res["block_step"] = block_step_bench(args, bm, synth, torch, dev, steps)
+    res["block_step"] = block_step_bench(args, bm, synth, torch, dev, max(steps, 100))
     res["conv1d_layer_1p3b_train"] = conv_bench(args, bm, synth, torch, dev, max(steps, 20))
     res["bwd_layer_1p3b_train"] = bwd_bench(args, bm, synth, torch, dev, max(3, steps // 4))
     res["gated_norm_layer_1p3b_train"] = epilogue_bench(args, bm, synth, torch, dev, max(steps, 20))
@@ -666,34 +718,50 @@ def conv_bench(args, bm, synth, torch, dev, steps):
 
 
 def cpu_baseline(f, b, y, w, torch, np):
-    """The fp64 oracle on this host's cores, on whole rows of the same inputs
-    (as many rows as fit in about 10-20 s), plus parity of those rows."""
+    """The fp64 oracle on this host's cores on a bounded sample of the same
+    inputs, about 10-20 s of CPU work: whole rows where the batch has several,
+    else a subset of the heads over every token of the row (heads are
+    independent units of the oracle's work, each a full pass over the
+    sequence in both directions). The rate is scaled to tokens/s of the whole
+    workload (all heads), with the parity of the sample against the GPU."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     oracle.set_num_threads(cores)
 
-    def rows(lo, hi):
-        fr = {k: (v[lo:hi] if v.dim() > 1 else v) for k, v in f.items()}
-        br = {k: (v[lo:hi] if v.dim() > 1 else v) for k, v in b.items()}
-        return fr, br
+    def sample(lo, hi, heads):
+        def cut(d):
+            out = {}
+            for k, v in d.items():
+                if k in ("x", "dt"):
+                    out[k] = v[lo:hi][:, :, heads].contiguous().cpu()
+                elif k in ("B", "C"):
+                    out[k] = v[lo:hi].contiguous().cpu()
+                else:
+                    out[k] = v[heads].contiguous().cpu()
+            return out
+        return cut(f), cut(b)
 
-    # whole rows of the same inputs; the full batch is repeated until about
-    # 10 s of CPU time have been spent (rows are independent units of work)
-    fr, br = rows(0, 1)
+    H = w.nheads
+    if w.batch > 1:
+        rows, heads = (0, 1), list(range(H))
+    else:
+        rows, heads = (0, 1), list(range(0, H, max(1, H // cores)))[:cores]
+    fr, br = sample(rows[0], rows[1], heads)
     t0 = time.perf_counter()
-    ref0 = oracle.bissd(fr, br)
+    ref = oracle.bissd(fr, br)
     t1 = time.perf_counter() - t0
-    n_rows = int(min(w.batch, max(1, math.ceil(10.0 / max(t1, 1e-3)))))
-    fr, br = rows(0, n_rows)
-    reps, total_t, ref = 0, 0.0, None
-    while reps == 0 or total_t < 10.0:
-        t0 = time.perf_counter()
-        ref = oracle.bissd(fr, br)
-        total_t += time.perf_counter() - t0
-        reps += 1
-        if reps >= 1000:
-            break
-    got = y[:n_rows].double().cpu().numpy()
+    # grow the sample to about 10 s of CPU time
+    if w.batch > 1:
+        n_rows = int(min(w.batch, max(1, math.ceil(10.0 / max(t1, 1e-3)))))
+        rows = (0, n_rows)
+    else:
+        n_heads = int(min(H, max(len(heads), math.ceil(len(heads) * 10.0 / max(t1, 1e-3)))))
+        heads = list(range(0, H, max(1, H // n_heads)))[:n_heads]
+    fr, br = sample(rows[0], rows[1], heads)
+    t0 = time.perf_counter()
+    ref = oracle.bissd(fr, br)
+    sec = time.perf_counter() - t0
+    got = y[rows[0]:rows[1]][:, :, heads].double().cpu().numpy()
     rms = float(np.sqrt(np.mean(ref ** 2)))
     err = float(np.max(np.abs(got - ref)) / rms)
     cpu_model = "unknown"
@@ -704,10 +772,14 @@ def cpu_baseline(f, b, y, w, torch, np):
                 break
     except OSError:
         pass
-    return {"value": round(reps * n_rows * w.seqlen / total_t, 2), "unit": "tokens/s",
+    nrow = rows[1] - rows[0]
+    # tokens/s of the whole workload: sample work / whole work = rows * heads / (batch * H)
+    value = nrow * w.seqlen * (len(heads) / H) / sec
+    return {"value": round(value, 2), "unit": "tokens/s",
             "cores": int(oracle.num_threads()), "kind": "oracle",
-            "sample": f"{n_rows} of {w.batch} rows x {w.seqlen} tokens of the same inputs, "
-                      f"run {reps}x, fp64 sequential recurrence, {total_t:.1f} s",
+            "sample": f"{nrow} of {w.batch} rows x {w.seqlen} tokens, {len(heads)} of {H} heads, "
+                      f"both directions, of the same inputs; fp64 sequential recurrence, {sec:.1f} s; "
+                      f"rate scaled to all {H} heads",
             "cpu_model": cpu_model,
             "parity_max_abs_err_over_rms": err, "parity_ok": err <= 1e-2}
 

@@ -1447,15 +1447,17 @@ struct PairLoads {
             ob[k] = (uint32_t)(item >> 4) * bstride + 8 * (item & 15);
         }
     }
+    // the step size (and sequence index) of the scanning wave's token
+    __device__ __forceinline__ void issue_dt(const SegArgs &a, int d, int b, int h, int c0,
+                                             int len) {
+        const int pos = min(d == 0 ? lane_id() : 63 - lane_id(), len - 1);
+        dtv[0] = ((const uint16_t *)a.dir[d].dt)[tok(a, b, c0 + pos) * a.H + h];
+        sqv[0] = PACKED ? a.seq[tok(a, b, c0 + pos)] : 0;
+    }
     __device__ __forceinline__ void issue(const SegArgs &a, int d, int b, int h, int grp, int c0,
-                                          int len, bool scanner) {
+                                          int len) {
         const DirPtrs &dp = a.dir[d];
-        const int lane = lane_id(), th = threadIdx.x & 255, tid = threadIdx.x;
-        if (scanner) {
-            const int pos = min(d == 0 ? lane : 63 - lane, len - 1);
-            dtv[0] = ((const uint16_t *)dp.dt)[tok(a, b, c0 + pos) * a.H + h];
-            sqv[0] = PACKED ? a.seq[tok(a, b, c0 + pos)] : 0;
-        }
+        const int th = threadIdx.x & 255, tid = threadIdx.x;
         const uint16_t *X = (const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP;
         const size_t bo = (tok(a, b, c0) * a.G + grp) * kN;
         const uint16_t *Bm = (const uint16_t *)dp.B + bo, *Cm = (const uint16_t *)dp.C + bo;
@@ -1818,7 +1820,8 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     {
         int c0, len;
         chunk_at(0, c0, len);
-        ld.issue(a, D, b, h, grp, c0, len, scanner);
+        if (scanner) ld.issue_dt(a, D, b, h, c0, len);
+        ld.issue(a, D, b, h, grp, c0, len);
         if (add) pair_prev(prev, a, oy, b, h, c0, len, rt);
         if (scanner) pair_scans<PACKED, SP>(a, hf.sc[0], ld.dtv[0], ld.sqv[0], D, b, h, c0, len);
     }
@@ -1831,6 +1834,12 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         chunk_at(s, c0, len);
         const PairScan &sc = hf.sc[s & 1];
         ld.store(sm, hf, len);
+        const bool last = s == nch - 1;
+        int c0n, lenn;
+        chunk_at(last ? s : s + 1, c0n, lenn);
+        // the next chunk's step sizes go out first: its scans need them after
+        // this chunk's tiles and state update
+        if (scanner && !last) ld.issue_dt(a, D, b, h, c0n, lenn);
         lds_barrier();   // chunk s staged, its scans and the published state visible
         f32x4 out[4];
         const bool mine = 16 * rt < len;
@@ -1843,13 +1852,10 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
                 for (int k = 0; k < 4; ++k) out[k] += prev[k];
             }
         }
-        const bool last = s == nch - 1;
-        int c0n, lenn;
-        chunk_at(last ? s : s + 1, c0n, lenn);
         // the next chunk's loads (the last chunk re-reads its own) go out
         // before this tile's stores, which would hold them up in the memory
         // pipeline, and stay in flight across the state update
-        ld.issue(a, D, b, h, grp, c0n, lenn, scanner);
+        ld.issue(a, D, b, h, grp, c0n, lenn);
         if (add) pair_prev(prev, a, oy, b, h, c0n, lenn, rt);
         if (mine) pair_store(a, out, oy, b, h, c0, len, rt, chk, check);
         if (!last || want_final) pair_state_update(sm, hf, sc, Hacc, v);

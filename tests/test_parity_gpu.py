@@ -762,3 +762,35 @@ def test_block_step_long_prefix(nseq):
     print(f"  committed state {err:.3e}", flush=True)
     assert ok, f"committed state error {err:.3e}"
     st.free()
+
+
+def test_block_cache_save_and_reload():
+    """Checkpoint and resume through the cache ("Fixed state, long reach",
+    Sec. 1: the carried state is the whole of the prefix the decoder needs):
+    a cache saved to the host, freed and loaded into a new cache object gives
+    the same bits, step after step, as the cache that stayed on the GPU."""
+    c = synth.BLOCK_STEP
+    H, P, N, G, Lb = c["nheads"], c["headdim"], c["d_state"], c["ngroups"], c["block"]
+    nseq = 3
+    keep = bm.State(nseq, H, P, N)
+    pf, _ = synth.make_inputs(nseq, 700, H, P, N, G, "bf16", 191, device=DEV, bidirectional=False)
+    bm.ssd_fwd(pf, None, chunk=256, final_state=keep.tensor())
+    f, b = synth.make_inputs(nseq, Lb, H, P, N, G, "bf16", 192, device=DEV)
+    bm.block_step(keep, f, b, commit=True, chunk=64)
+    torch.cuda.synchronize()
+    saved = keep.tensor().cpu().numpy().copy()            # checkpoint
+    tmp = bm.State(nseq, H, P, N)
+    tmp.tensor().copy_(torch.from_numpy(saved).to(DEV))
+    tmp.free()                                            # the process "ends"
+    resumed = bm.State(nseq, H, P, N)                     # resume
+    resumed.tensor().copy_(torch.from_numpy(saved).to(DEV))
+    assert torch.equal(resumed.tensor(), keep.tensor())
+    for step in range(3):
+        fs, bs = synth.make_inputs(nseq, Lb, H, P, N, G, "bf16", 193 + step, device=DEV)
+        y1 = bm.block_step(keep, fs, bs, commit=True, chunk=64)
+        y2 = bm.block_step(resumed, fs, bs, commit=True, chunk=64)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), step
+        assert torch.equal(keep.tensor(), resumed.tensor()), step
+    keep.free()
+    resumed.free()
