@@ -1344,27 +1344,41 @@ struct PairScan {
     int sq_nb;             // sequence index of the token the carried state comes from
 };
 
-// fp64 value of lane `src` (uniform)
-__device__ __forceinline__ double lane_d(double v, int src) {
-    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-    const unsigned lo = __builtin_amdgcn_readlane((unsigned)(u & 0xffffffffull), src);
-    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), src);
-    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+// fp32 value moved across lanes by a DPP control; lanes without a source (or
+// outside ROWMASK) read 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xf, true));
+}
+// Inclusive fp32 scan over the wave's 64 lanes (as wave_scan_d).
+__device__ __forceinline__ float wave_scan_f(float v) {
+    v += dpp_f<0x111, 0xf>(v);   // row_shr:1
+    v += dpp_f<0x112, 0xf>(v);   // row_shr:2
+    v += dpp_f<0x114, 0xf>(v);   // row_shr:4
+    v += dpp_f<0x118, 0xf>(v);   // row_shr:8
+    v += dpp_f<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_f<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+__device__ __forceinline__ float lane_f(float v, int src) {
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), src));
 }
 
 // The scans of one 64-token chunk [c0, c0+len) of direction d for head h by
 // one wave; lane k holds the k-th token in walking order (position k forward,
-// 63 - k reverse; positions past the end carry dt = 0). Sums in fp64 as in
-// chunk_scans: every exponent is a difference of them rounded once. A
-// token's state-update weight is e^(the sum of a after it) dt, that sum being
-// the chunk's total minus the token's walking sum.
+// 63 - k reverse; positions past the end carry dt = 0). The sums of
+// a = dt A are taken in log2 units in fp32: within 64 tokens every exponent
+// used is a difference of two such sums whose error is a few ulps of at most
+// 64 |a|, and where |a| is large enough for that to matter the only factors
+// that survive have an exponent of exactly 0 (a token's own). A token's
+// state-update weight is 2^(the sum of a after it) dt, that sum being the
+// chunk's total minus the token's walking sum.
+// A2: A_h log2(e); dtb: the step-size bias (with SP), both read once per pass.
 template <bool PACKED, bool SP>
 __device__ __forceinline__ void pair_scans(const SegArgs &a, PairScan &sm, uint16_t dtv, int sqv,
-                                           int d, int b, int h, int c0, int len) {
+                                           float A2, float dtb, int d, int b, int c0, int len) {
     const int lane = lane_id();
     const int pos = d == 0 ? lane : 63 - lane;
-    const float Ah = a.dir[d].A[h];
-    const float dtb = SP && a.dt_bias[d] ? a.dt_bias[d][h] : 0.f;
     int sq_nb = 0, sq_edge = 0;
     bool has_nb = true;
     if (PACKED) {
@@ -1376,28 +1390,27 @@ __device__ __forceinline__ void pair_scans(const SegArgs &a, PairScan &sm, uint1
     const bool in = pos < len;
     float dtf = in ? bf2f(dtv) : 0.f;
     if (SP) dtf = in ? softplus_dt(dtf + dtb) : 0.f;
-    const float at = dtf * Ah;
-    const double cs = wave_scan_d((double)at);
-    const double total = lane_d(cs, 63);
+    const float cs = wave_scan_f(dtf * A2);
+    const float total = lane_f(cs, 63);
     // the walking sum at the end of the lane's 16-tile (lane | 15)
-    const double t0 = lane_d(cs, 15), t1 = lane_d(cs, 31), t2 = lane_d(cs, 47);
+    const float t0 = lane_f(cs, 15), t1 = lane_f(cs, 31), t2 = lane_f(cs, 47);
     const int row = lane >> 4;
-    const double e16 = row == 0 ? t0 : row == 1 ? t1 : row == 2 ? t2 : total;
-    sm.cs2[pos] = (float)(cs * kLog2e);
+    const float e16 = row == 0 ? t0 : row == 1 ? t1 : row == 2 ? t2 : total;
+    sm.cs2[pos] = cs;
     sm.dt[pos] = dtf;
     if (PACKED) sm.sq[pos] = sqv;
-    sm.v16[pos] = exp2_((float)((e16 - cs) * kLog2e)) * dtf;
-    const bool reach = in && (!PACKED || sqv == sq_nb) && cs >= kDead;
+    sm.v16[pos] = exp2_(e16 - cs) * dtf;
+    const bool reach = in && (!PACKED || sqv == sq_nb) && cs >= kDead * kLog2e;
     const unsigned long long m = __ballot(reach);
     if (lane < 4) sm.utile[d == 0 ? lane : 3 - lane] = ((m >> (16 * lane)) & 0xffffull) != 0;
     float wt = 0.f;
-    if (in && (!PACKED || sqv == sq_edge)) wt = expf((float)(total - cs)) * dtf;
+    if (in && (!PACKED || sqv == sq_edge)) wt = exp2_(total - cs) * dtf;
     sm.w[pos] = wt;
     const bool nz = __ballot(wt != 0.f) != 0ull;
     if (lane == 0) {
         bool carry = true;
         if (PACKED) carry = has_nb && sq_nb == sq_edge;
-        sm.gamma = carry ? expf((float)total) : 0.f;
+        sm.gamma = carry ? exp2_(total) : 0.f;
         sm.sq_nb = PACKED ? sq_nb : 0;
         sm.wsub = nz;
     }
@@ -1718,9 +1731,20 @@ __device__ __forceinline__ void pair_store(const SegArgs &a, const f32x4 (&out)[
 __device__ __forceinline__ void pair_state_update(const PairSmem &sm, const PairHalf &hf,
                                                   const PairScan &sc, f32x4 (&Hacc)[8], int v) {
     const float gmm = sc.gamma;
+    // a chunk whose decay is exactly 0 starts the new state from nothing:
+    // the first products take a zero accumulator instead of a scaled one
+    const bool fresh = gmm == 0.f;
+    if (!fresh) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) Hacc[q] *= gmm;
-    if (!sc.wsub) return;   // every weight is exactly 0
+        for (int q = 0; q < 8; ++q) Hacc[q] *= gmm;
+    }
+    if (!sc.wsub) {   // every weight is exactly 0
+        if (fresh) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) Hacc[q] = zero4();
+        }
+        return;
+    }
     const int g4 = lane_id() >> 4;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -1735,11 +1759,19 @@ __device__ __forceinline__ void pair_state_update(const PairSmem &sm, const Pair
             const u32x4 xv = tr_operand(hf.xs, kXS, 32 * ks, 16 * pt);
             bx[pt] = u32x4{mul_h(xv[0], wp[0]), mul_h(xv[1], wp[1]), mul_h(xv[2], wp[2]), mul_h(xv[3], wp[3])};
         }
+        if (ks == 0 && fresh) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-                Hacc[4 * nt + pt] = mfma16x16x32_f16(aop[nt], bx[pt], Hacc[4 * nt + pt]);
+                for (int pt = 0; pt < 4; ++pt)
+                    Hacc[4 * nt + pt] = mfma16x16x32_f16(aop[nt], bx[pt], zero4());
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+                    Hacc[4 * nt + pt] = mfma16x16x32_f16(aop[nt], bx[pt], Hacc[4 * nt + pt]);
+        }
     }
 }
 
@@ -1801,9 +1833,11 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     f32x4 prev[4];
     uint32_t oy[4];
     pair_yoff(oy, a, rt);
-    float *tb = sm.tile[wave_id()];
+    float *tb = sm.tile[4 * half + v];
     // the scans run on the wave with the shortest row tile
     const bool scanner = rt == 0;
+    const float A2 = dp.A[h] * kLog2e;
+    const float dtb = SP && a.dt_bias[D] ? a.dt_bias[D][h] : 0.f;
     // diagonal tile of row tile rt: lane (g4, l16) holds columns 4 g4 + r of
     // row l16; those on the far side get an exponent of -inf, the diagonal
     // entry D
@@ -1823,7 +1857,7 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         if (scanner) ld.issue_dt(a, D, b, h, c0, len);
         ld.issue(a, D, b, h, grp, c0, len);
         if (add) pair_prev(prev, a, oy, b, h, c0, len, rt);
-        if (scanner) pair_scans<PACKED, SP>(a, hf.sc[0], ld.dtv[0], ld.sqv[0], D, b, h, c0, len);
+        if (scanner) pair_scans<PACKED, SP>(a, hf.sc[0], ld.dtv[0], ld.sqv[0], A2, dtb, D, b, c0, len);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) Hacc[q] = src ? *(const f32x4 *)(src + pair_hoff(v, q)) : zero4();
@@ -1860,7 +1894,7 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         if (mine) pair_store(a, out, oy, b, h, c0, len, rt, chk, check);
         if (!last || want_final) pair_state_update(sm, hf, sc, Hacc, v);
         // the next chunk's scans, into the other buffer
-        if (!last && scanner) pair_scans<PACKED, SP>(a, hf.sc[(s + 1) & 1], ld.dtv[0], ld.sqv[0], D, b, h, c0n, lenn);
+        if (!last && scanner) pair_scans<PACKED, SP>(a, hf.sc[(s + 1) & 1], ld.dtv[0], ld.sqv[0], A2, dtb, D, b, c0n, lenn);
         // every wave is done with this chunk's tiles and the published state
         lds_barrier();
         if (!last) {
@@ -1911,7 +1945,10 @@ k_pair_out(const SegArgs a) {
     if (lin >= total) return;
     const int rs = lin / HP, hp = lin % HP;
     const int b = rs / a.nseg, seg = rs % a.nseg;
-    const int half = wave_id() >> 2, v = wave_id() & 3;
+    // the wave index as a scalar: head, row tile and roles are then uniform
+    // to the compiler (scalar loads of the per-head parameters, scalar branches)
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+    const int half = wave >> 2, v = wave & 3;
     const int h = 2 * hp + half;
     const int grp = (2 * hp) / (a.H / a.G);
     __shared__ __attribute__((aligned(16))) PairShared sh;
@@ -1924,7 +1961,7 @@ k_pair_out(const SegArgs a) {
         for (int q = 0; q < 8; ++q) chk += (Hacc[q][0] + Hacc[q][1]) + (Hacc[q][2] + Hacc[q][3]);
     }
     const unsigned long long bad = __ballot(!__builtin_isfinite(chk));
-    if (lane_id() == 0) sh.fast.bad[wave_id()] = bad != 0ull;
+    if (lane_id() == 0) sh.fast.bad[wave] = bad != 0ull;
     lds_barrier();
     int any = 0;
 #pragma unroll
