@@ -737,18 +737,21 @@ __device__ __forceinline__ f32x4 gram_tile(const uint16_t *bn, int j0, const u32
 
 // acc[pt] += M x over the 32 columns j32..j32+31; M given as a hi / lo pair
 // in the k order of a Gram accumulator pair, which is the order in which the
-// transposing reads deliver x.
-template <bool F16 = false>
+// transposing reads deliver x. An operand's registers read the same as A
+// (row = lane % 16) or as B (column = lane % 16), so with TR the product is
+// taken as x^T M^T: acc then holds (M x)^T, lane (g4, l16) the entries
+// [row l16][columns 16 pt + 4 g4 + r].
+template <bool F16 = false, bool TR = false>
 __device__ __forceinline__ void mx_step(f32x4 (&acc)[4], const uint16_t *xs, int j32, u32x4 mhi,
                                         u32x4 mlo, bool lo = true) {
     u32x4 xo[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) xo[pt] = tr_operand(xs, kXS, j32, 16 * pt);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) acc[pt] = mma<F16>(mhi, xo[pt], acc[pt]);
+    for (int pt = 0; pt < 4; ++pt) acc[pt] = TR ? mma<F16>(xo[pt], mhi, acc[pt]) : mma<F16>(mhi, xo[pt], acc[pt]);
     if (lo) {
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] = mma<F16>(mlo, xo[pt], acc[pt]);
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = TR ? mma<F16>(xo[pt], mlo, acc[pt]) : mma<F16>(mlo, xo[pt], acc[pt]);
     }
 }
 
@@ -1422,12 +1425,10 @@ struct PairHalf {
     alignas(16) uint16_t xs[64 * kXS];   // x [t][p], fp16
     alignas(16) uint16_t hs[kP * kNRS];  // H^T [p][n], fp16
 };
-constexpr int kTS = kP + 4;   // row stride (floats) of a wave's output tile in LDS
 struct PairSmem {
     PairHalf half[2];
     alignas(16) uint16_t bn[bn_elems(64)];   // B [t][n], fp16, bn_row layout
     alignas(16) uint16_t cn[bn_elems(64)];   // C [t][n], fp16, bn_row layout
-    alignas(16) float tile[8][16 * kTS];     // per wave: its 16 output rows, row-major
     int bad[8];                              // per wave: a non-finite output or state
 };
 union PairShared {
@@ -1460,20 +1461,19 @@ struct PairLoads {
             ob[k] = (uint32_t)(item >> 4) * bstride + 8 * (item & 15);
         }
     }
-    // the step size (and sequence index) of the scanning wave's token
-    __device__ __forceinline__ void issue_dt(const SegArgs &a, int d, int b, int h, int c0,
-                                             int len) {
+    // the step size (and sequence index) of the scanning wave's token; dt and
+    // sq point at the chunk's first token (dt of the head)
+    __device__ __forceinline__ void issue_dt(const uint16_t *dt, const int32_t *sq, uint32_t dstride,
+                                             int d, int len) {
         const int pos = min(d == 0 ? lane_id() : 63 - lane_id(), len - 1);
-        dtv[0] = ((const uint16_t *)a.dir[d].dt)[tok(a, b, c0 + pos) * a.H + h];
-        sqv[0] = PACKED ? a.seq[tok(a, b, c0 + pos)] : 0;
+        dtv[0] = dt[(uint32_t)pos * dstride];
+        sqv[0] = PACKED ? sq[pos] : 0;
     }
-    __device__ __forceinline__ void issue(const SegArgs &a, int d, int b, int h, int grp, int c0,
-                                          int len) {
-        const DirPtrs &dp = a.dir[d];
+    // X: the chunk's first row of x for the half's head; Bm, Cm: of B and C
+    // for the group
+    __device__ __forceinline__ void issue(const SegArgs &a, const uint16_t *X, const uint16_t *Bm,
+                                          const uint16_t *Cm, int len) {
         const int th = threadIdx.x & 255, tid = threadIdx.x;
-        const uint16_t *X = (const uint16_t *)dp.x + (tok(a, b, c0) * a.H + h) * kP;
-        const size_t bo = (tok(a, b, c0) * a.G + grp) * kN;
-        const uint16_t *Bm = (const uint16_t *)dp.B + bo, *Cm = (const uint16_t *)dp.C + bo;
         if (len == 64) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) xv[k] = ld8(X + ox[k]);
@@ -1516,17 +1516,18 @@ struct PairLoads {
             }
             return;
         }
-        const u32x4 z = {0u, 0u, 0u, 0u};
+        // masked rather than branched: every lane passes the same waits
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int item = th + 256 * k, row = item >> 3, cg = item & 7;
-            *(u32x4 *)(hf.xs + row * kXS + 8 * cg) = row < len ? bf2h4(xv[k]) : z;
+            *(u32x4 *)(hf.xs + row * kXS + 8 * cg) = bf2h4(xv[k]) & (row < len ? ~0u : 0u);
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int item = tid + 512 * k, row = item >> 4, cg = item & 15;
-            *(u32x4 *)(sm.bn + bn_row(row) + 8 * cg) = row < len ? bf2h4(bv[k]) : z;
-            *(u32x4 *)(sm.cn + bn_row(row) + 8 * cg) = row < len ? bf2h4(cv[k]) : z;
+            const uint32_t m = row < len ? ~0u : 0u;
+            *(u32x4 *)(sm.bn + bn_row(row) + 8 * cg) = bf2h4(bv[k]) & m;
+            *(u32x4 *)(sm.cn + bn_row(row) + 8 * cg) = bf2h4(cv[k]) & m;
         }
     }
 };
@@ -1588,67 +1589,34 @@ __device__ __forceinline__ void pair_diag(f32x4 (&acc)[4], const PairSmem &sm, c
                 ph[2 * half + 1] = pk_h(mv[2], mv[3]);
             }
         }
-        mx_step<true>(acc, hf.xs, 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
+        mx_step<true, true>(acc, hf.xs, 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
                       u32x4{pl[0], pl[1], pl[2], pl[3]}, band);
     }
 }
 
-// Output rows are moved as 16-byte pieces: after the row tile, lane l holds
-// row 16 rt + 4 k + l / 16, columns 4 (l % 16) .. + 3, in out[k]; oy[k] is
-// that piece's offset from the chunk's first row of the head.
-__device__ __forceinline__ void pair_yoff(uint32_t (&oy)[4], const SegArgs &a, int rt) {
-    const int lane = lane_id();
-    const uint32_t ystride = (uint32_t)(a.H * kP);
+// A row tile's outputs are held transposed (see mx_step): lane (g4, l16) has
+// row 16 rt + l16, columns 16 pt + 4 g4 .. + 3 in acc[pt], four consecutive
+// floats of y. yb points at the chunk's first row of y for the head. The
+// reverse pass's rows are read back in that layout by the lane that wrote
+// them; rows past the chunk's end read its last row.
+__device__ __forceinline__ void pair_prev(f32x4 (&prev)[4], const float *yb, uint32_t ystride,
+                                          int len, int rt) {
+    const int lane = lane_id(), row = min(16 * rt + (lane & 15), len - 1);
+    const float *yr = yb + (uint32_t)row * ystride + 4 * (lane >> 4);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        oy[k] = (uint32_t)(16 * rt + 4 * k + (lane >> 4)) * ystride + 4 * (lane & 15);
-}
-
-// The reverse pass's rows of y in that layout (read back by the lane that
-// wrote them).
-__device__ __forceinline__ void pair_prev(f32x4 (&prev)[4], const SegArgs &a, const uint32_t (&oy)[4],
-                                          int b, int h, int c0, int len, int rt) {
-    const float *yb = a.y + (tok(a, b, c0) * a.H + h) * kP;
-    if (16 * rt + 16 <= len) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) prev[k] = *(const f32x4 *)(yb + oy[k]);
-        return;
-    }
-    const int lane = lane_id();
-    const uint32_t ystride = (uint32_t)(a.H * kP);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int row = min(16 * rt + 4 * k + (lane >> 4), len - 1);
-        prev[k] = *(const f32x4 *)(yb + (uint32_t)row * ystride + 4 * (lane & 15));
-    }
-}
-
-// acc (matrix-core layout: rows 4 g4 + r, columns 16 pt + l16 of the tile)
-// into the row layout of pair_prev, through the wave's own LDS tile.
-__device__ __forceinline__ void pair_to_rows(f32x4 (&out)[4], const f32x4 (&acc)[4], float *tb) {
-    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tb[(4 * g4 + r) * kTS + 16 * pt + l16] = acc[pt][r];
-    // the wave reads what its other lanes wrote: order the LDS accesses
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = *(const f32x4 *)(tb + (4 * k + g4) * kTS + 4 * l16);
+    for (int pt = 0; pt < 4; ++pt) prev[pt] = *(const f32x4 *)(yr + 16 * pt);
 }
 
 // Row tile rt (16 rows) of the chunk for the half's head: intra-chunk form
-// (with D x) and carried state into acc (this lane's outputs: rows
-// 16 rt + 4 g4 + r, columns 16 pt + l16).
+// (with D x) and carried state into acc (this lane's outputs: row
+// 16 rt + l16, columns 16 pt + 4 g4 + r).
 template <bool PACKED, int D>
 __device__ __forceinline__ void pair_row_tile(f32x4 (&acc)[4], const PairSmem &sm,
                                               const PairHalf &hf, const PairScan &sc, int rt,
                                               bool has_state, const float (&tmask)[4],
                                               const float (&dadd)[4]) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
-    const int i = 16 * rt + l16, i0 = 16 * rt + 4 * g4;
+    const int i = 16 * rt + l16;
     u32x4 cr[kN / 32];
 #pragma unroll
     for (int ks = 0; ks < kN / 32; ++ks)
@@ -1675,50 +1643,32 @@ __device__ __forceinline__ void pair_row_tile(f32x4 (&acc)[4], const PairSmem &s
             for (int pt = 0; pt < 4; ++pt)
                 oh[pt] = *(const u32x4 *)(hf.hs + (16 * pt + l16) * kNRS + 32 * ks + 8 * g4);
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32_f16(cr[ks], oh[pt], tt[pt]);
+            for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32_f16(oh[pt], cr[ks], tt[pt]);
         }
-        const f32x4 c4 = *(const f32x4 *)(sc.cs2 + i0);
-        float uu[4];
-        if (PACKED) {
-            const int4 s4 = *(const int4 *)(sc.sq + i0);
-            const int nb = sc.sq_nb;
-            uu[0] = s4.x == nb ? exp2_(c4[0]) : 0.f;
-            uu[1] = s4.y == nb ? exp2_(c4[1]) : 0.f;
-            uu[2] = s4.z == nb ? exp2_(c4[2]) : 0.f;
-            uu[3] = s4.w == nb ? exp2_(c4[3]) : 0.f;
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) uu[r] = exp2_(c4[r]);
-        }
+        const float u = (!PACKED || sqi == sc.sq_nb) ? exp2_(rli) : 0.f;
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(uu[r], tt[pt][r], acc[pt][r]);
+            for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(u, tt[pt][r], acc[pt][r]);
     }
 }
 
-// The row tile's outputs (row layout) into y; rows past the chunk's end are
-// not written. With `check`, their sum joins chk (a non-finite output makes
-// it non-finite).
-__device__ __forceinline__ void pair_store(const SegArgs &a, const f32x4 (&out)[4],
-                                           const uint32_t (&oy)[4], int b, int h, int c0, int len,
-                                           int rt, float &chk, bool check) {
-    float *yb = a.y + (tok(a, b, c0) * a.H + h) * kP;
-    if (16 * rt + 16 <= len) {
+// The row tile's outputs into y; rows past the chunk's end are not written.
+// With `check`, their sum joins chk (a non-finite output makes it non-finite).
+__device__ __forceinline__ void pair_store(float *yb, uint32_t ystride, const f32x4 (&out)[4],
+                                           int len, int rt, float &chk, bool check) {
+    const int lane = lane_id(), row = 16 * rt + (lane & 15);
+    float *yr = yb + (uint32_t)row * ystride + 4 * (lane >> 4);
+    if (row < len) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) *(f32x4 *)(yb + oy[k]) = out[k];
-    } else {
-        const int lane = lane_id();
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (16 * rt + 4 * k + (lane >> 4) < len) *(f32x4 *)(yb + oy[k]) = out[k];
+        for (int pt = 0; pt < 4; ++pt) *(f32x4 *)(yr + 16 * pt) = out[pt];
     }
     if (check) {
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            s0 += out[k][0] + out[k][1];
-            s1 += out[k][2] + out[k][3];
+        for (int pt = 0; pt < 4; ++pt) {
+            s0 += out[pt][0] + out[pt][1];
+            s1 += out[pt][2] + out[pt][3];
         }
         chk += s0 + s1;
     }
@@ -1831,9 +1781,22 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     PairLoads<PACKED> ld;
     ld.init(a);
     f32x4 prev[4];
-    uint32_t oy[4];
-    pair_yoff(oy, a, rt);
-    float *tb = sm.tile[4 * half + v];
+    // the row's first token of x, dt, y for the head, of B, C for the group
+    const size_t row0 = tok(a, b, 0);
+    const uint32_t xstride = (uint32_t)(a.H * kP), bstride = (uint32_t)(a.G * kN);
+    const uint16_t *xrow = (const uint16_t *)dp.x + (row0 * a.H + h) * kP;
+    const uint16_t *brow = (const uint16_t *)dp.B + (row0 * a.G + grp) * kN;
+    const uint16_t *crow = (const uint16_t *)dp.C + (row0 * a.G + grp) * kN;
+    const uint16_t *dtrow = (const uint16_t *)dp.dt + row0 * a.H + h;
+    const int32_t *sqrow = PACKED ? a.seq + row0 : nullptr;
+    float *yrow = a.y + (row0 * a.H + h) * kP;
+    auto issue = [&](int c0, int len) {
+        ld.issue(a, xrow + (size_t)c0 * xstride, brow + (size_t)c0 * bstride,
+                 crow + (size_t)c0 * bstride, len);
+    };
+    auto issue_dt = [&](int c0, int len) {
+        ld.issue_dt(dtrow + (size_t)c0 * a.H, PACKED ? sqrow + c0 : nullptr, (uint32_t)a.H, D, len);
+    };
     // the scans run on the wave with the shortest row tile
     const bool scanner = rt == 0;
     const float A2 = dp.A[h] * kLog2e;
@@ -1854,10 +1817,9 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     {
         int c0, len;
         chunk_at(0, c0, len);
-        if (scanner) ld.issue_dt(a, D, b, h, c0, len);
-        ld.issue(a, D, b, h, grp, c0, len);
-        if (add) pair_prev(prev, a, oy, b, h, c0, len, rt);
-        if (scanner) pair_scans<PACKED, SP>(a, hf.sc[0], ld.dtv[0], ld.sqv[0], A2, dtb, D, b, c0, len);
+        issue(c0, len);
+        issue_dt(c0, len);
+        if (add) pair_prev(prev, yrow + (size_t)c0 * xstride, xstride, len, rt);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) Hacc[q] = src ? *(const f32x4 *)(src + pair_hoff(v, q)) : zero4();
@@ -1868,33 +1830,29 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         chunk_at(s, c0, len);
         const PairScan &sc = hf.sc[s & 1];
         ld.store(sm, hf, len);
+        // the chunk's scans, from step sizes that arrived with its x, B, C
+        if (scanner) pair_scans<PACKED, SP>(a, hf.sc[s & 1], ld.dtv[0], ld.sqv[0], A2, dtb, D, b, c0, len);
         const bool last = s == nch - 1;
         int c0n, lenn;
         chunk_at(last ? s : s + 1, c0n, lenn);
-        // the next chunk's step sizes go out first: its scans need them after
-        // this chunk's tiles and state update
-        if (scanner && !last) ld.issue_dt(a, D, b, h, c0n, lenn);
         lds_barrier();   // chunk s staged, its scans and the published state visible
         f32x4 out[4];
         const bool mine = 16 * rt < len;
         if (mine) {
-            f32x4 acc[4];
-            pair_row_tile<PACKED, D>(acc, sm, hf, sc, rt, has_state, tmask, dadd);
-            pair_to_rows(out, acc, tb);
+            pair_row_tile<PACKED, D>(out, sm, hf, sc, rt, has_state, tmask, dadd);
             if (add) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) out[k] += prev[k];
+                for (int pt = 0; pt < 4; ++pt) out[pt] += prev[pt];
             }
         }
         // the next chunk's loads (the last chunk re-reads its own) go out
         // before this tile's stores, which would hold them up in the memory
         // pipeline, and stay in flight across the state update
-        ld.issue(a, D, b, h, grp, c0n, lenn);
-        if (add) pair_prev(prev, a, oy, b, h, c0n, lenn, rt);
-        if (mine) pair_store(a, out, oy, b, h, c0, len, rt, chk, check);
+        issue(c0n, lenn);
+        issue_dt(c0n, lenn);   // read by every wave, used by the scanner: no branch
+        if (add) pair_prev(prev, yrow + (size_t)c0n * xstride, xstride, lenn, rt);
+        if (mine) pair_store(yrow + (size_t)c0 * xstride, xstride, out, len, rt, chk, check);
         if (!last || want_final) pair_state_update(sm, hf, sc, Hacc, v);
-        // the next chunk's scans, into the other buffer
-        if (!last && scanner) pair_scans<PACKED, SP>(a, hf.sc[(s + 1) & 1], ld.dtv[0], ld.sqv[0], A2, dtb, D, b, c0n, lenn);
         // every wave is done with this chunk's tiles and the published state
         lds_barrier();
         if (!last) {
