@@ -1462,10 +1462,12 @@ struct PairLoads {
         }
     }
     // the step size (and sequence index) of the scanning wave's token; dt and
-    // sq point at the chunk's first token (dt of the head)
+    // sq point at the chunk's first token (dt of the head). Every wave loads
+    // (no branch for the compiler to move); a wave that does not scan (own
+    // false) reads the first token in every lane, one cache line.
     __device__ __forceinline__ void issue_dt(const uint16_t *dt, const int32_t *sq, uint32_t dstride,
-                                             int d, int len) {
-        const int pos = min(d == 0 ? lane_id() : 63 - lane_id(), len - 1);
+                                             int d, int len, bool own) {
+        const int pos = own ? min(d == 0 ? lane_id() : 63 - lane_id(), len - 1) : 0;
         dtv[0] = dt[(uint32_t)pos * dstride];
         sqv[0] = PACKED ? sq[pos] : 0;
     }
@@ -1540,8 +1542,7 @@ struct PairLoads {
 template <bool PACKED, int D, int WQ>
 __device__ __forceinline__ void pair_diag(f32x4 (&acc)[4], const PairSmem &sm, const PairHalf &hf,
                                           const PairScan &sc, const u32x4 (&cr)[kN / 32],
-                                          float rli, int sqi, const float (&tmask)[4],
-                                          const float (&dadd)[4]) {
+                                          float rli, int sqi, float td, float Dh) {
     const int g4 = lane_id() >> 4;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -1571,13 +1572,18 @@ __device__ __forceinline__ void pair_diag(f32x4 (&acc)[4], const PairSmem &sm, c
 #pragma unroll
                     for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u16 * vv[r]);
                 } else {
-                    // the far side of the diagonal through an exponent of -inf
-                    // (exactly 0), D on the diagonal itself
+                    // td = l16 - 4 g4 (row minus column of entry r = 0): the
+                    // far side of the diagonal gets an exponent below -2^98
+                    // (exactly 0 after exp2), the diagonal itself adds D
                     const f32x4 c4 = *(const f32x4 *)(sc.cs2 + jb);
                     const f32x4 d4 = *(const f32x4 *)(sc.dt + jb);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        mv[r] = fmaf(gg[r], exp2_((rli + tmask[r]) - c4[r]) * d4[r], dadd[r]);
+                    for (int r = 0; r < 4; ++r) {
+                        const float off = D == 0 ? td - (float)r : (float)r - td;
+                        const float far = fminf(off + 0.5f, 0.f) * 1e30f;
+                        const float dg = fmaxf(1.f - fabsf(off), 0.f) * Dh;
+                        mv[r] = fmaf(gg[r], exp2_((rli + far) - c4[r]) * d4[r], dg);
+                    }
                 }
                 seq_mask<64, PACKED>(mv, sc, jb, sqi);
             }
@@ -1608,13 +1614,13 @@ __device__ __forceinline__ void pair_prev(f32x4 (&prev)[4], const float *yb, uin
 }
 
 // Row tile rt (16 rows) of the chunk for the half's head: intra-chunk form
-// (with D x) and carried state into acc (this lane's outputs: row
-// 16 rt + l16, columns 16 pt + 4 g4 + r).
+// (with D x) and carried state added to acc (this lane's outputs: row
+// 16 rt + l16, columns 16 pt + 4 g4 + r), which comes in holding the other
+// direction's part or zeros.
 template <bool PACKED, int D>
 __device__ __forceinline__ void pair_row_tile(f32x4 (&acc)[4], const PairSmem &sm,
                                               const PairHalf &hf, const PairScan &sc, int rt,
-                                              bool has_state, const float (&tmask)[4],
-                                              const float (&dadd)[4]) {
+                                              bool has_state, float Dh) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
     const int i = 16 * rt + l16;
     u32x4 cr[kN / 32];
@@ -1623,13 +1629,12 @@ __device__ __forceinline__ void pair_row_tile(f32x4 (&acc)[4], const PairSmem &s
         cr[ks] = *(const u32x4 *)(sm.cn + 16 * rt * kBS + bn_lane(l16) + 32 * ks + 8 * g4);
     const float rli = sc.cs2[i];
     const int sqi = PACKED ? sc.sq[i] : 0;
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
+    const float td = (float)(l16 - 4 * g4);
     switch (rt) {
-        case 0: pair_diag<PACKED, D, 0>(acc, sm, hf, sc, cr, rli, sqi, tmask, dadd); break;
-        case 1: pair_diag<PACKED, D, 1>(acc, sm, hf, sc, cr, rli, sqi, tmask, dadd); break;
-        case 2: pair_diag<PACKED, D, 2>(acc, sm, hf, sc, cr, rli, sqi, tmask, dadd); break;
-        default: pair_diag<PACKED, D, 3>(acc, sm, hf, sc, cr, rli, sqi, tmask, dadd); break;
+        case 0: pair_diag<PACKED, D, 0>(acc, sm, hf, sc, cr, rli, sqi, td, Dh); break;
+        case 1: pair_diag<PACKED, D, 1>(acc, sm, hf, sc, cr, rli, sqi, td, Dh); break;
+        case 2: pair_diag<PACKED, D, 2>(acc, sm, hf, sc, cr, rli, sqi, td, Dh); break;
+        default: pair_diag<PACKED, D, 3>(acc, sm, hf, sc, cr, rli, sqi, td, Dh); break;
     }
     // carried state: e^{cs_i} C_i . H (tiles it does not reach: skipped, exact)
     if (has_state && sc.utile[rt]) {
@@ -1745,9 +1750,9 @@ __device__ __forceinline__ void pair_publish(PairHalf &hf, const f32x4 (&Hacc)[8
 // One direction's walk over the segment's chunks for the half's head (wave v
 // of the half owns row tile rt and the state block of n = 32 v .. 32 v + 31).
 // Returns the outgoing state in Hacc.
-template <bool PACKED, int D, bool SP>
+template <bool PACKED, int D, bool SP, bool ADD>
 __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b, int seg, int h,
-                                          int grp, bool add, int half, int v, f32x4 (&Hacc)[8],
+                                          int grp, int half, int v, f32x4 (&Hacc)[8],
                                           float &chk, bool check) {
     constexpr int Q = 64;
     // row tiles mirrored in the second half: the two waves of a SIMD (v and
@@ -1794,32 +1799,19 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         ld.issue(a, xrow + (size_t)c0 * xstride, brow + (size_t)c0 * bstride,
                  crow + (size_t)c0 * bstride, len);
     };
-    auto issue_dt = [&](int c0, int len) {
-        ld.issue_dt(dtrow + (size_t)c0 * a.H, PACKED ? sqrow + c0 : nullptr, (uint32_t)a.H, D, len);
-    };
     // the scans run on the wave with the shortest row tile
     const bool scanner = rt == 0;
+    auto issue_dt = [&](int c0, int len) {
+        ld.issue_dt(dtrow + (size_t)c0 * a.H, PACKED ? sqrow + c0 : nullptr, (uint32_t)a.H, D, len, scanner);
+    };
     const float A2 = dp.A[h] * kLog2e;
     const float dtb = SP && a.dt_bias[D] ? a.dt_bias[D][h] : 0.f;
-    // diagonal tile of row tile rt: lane (g4, l16) holds columns 4 g4 + r of
-    // row l16; those on the far side get an exponent of -inf, the diagonal
-    // entry D
-    float tmask[4], dadd[4];
-    {
-        const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = 4 * g4 + r;
-            tmask[r] = (D == 0 ? j <= l16 : j >= l16) ? 0.f : -__builtin_huge_valf();
-            dadd[r] = j == l16 ? Dh : 0.f;
-        }
-    }
     {
         int c0, len;
         chunk_at(0, c0, len);
         issue(c0, len);
         issue_dt(c0, len);
-        if (add) pair_prev(prev, yrow + (size_t)c0 * xstride, xstride, len, rt);
+        if (ADD) pair_prev(prev, yrow + (size_t)c0 * xstride, xstride, len, rt);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) Hacc[q] = src ? *(const f32x4 *)(src + pair_hoff(v, q)) : zero4();
@@ -1836,21 +1828,17 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         int c0n, lenn;
         chunk_at(last ? s : s + 1, c0n, lenn);
         lds_barrier();   // chunk s staged, its scans and the published state visible
+        issue(c0n, lenn);
+        issue_dt(c0n, lenn);
         f32x4 out[4];
-        const bool mine = 16 * rt < len;
-        if (mine) {
-            pair_row_tile<PACKED, D>(out, sm, hf, sc, rt, has_state, tmask, dadd);
-            if (add) {
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) out[pt] += prev[pt];
-            }
-        }
+        for (int pt = 0; pt < 4; ++pt) out[pt] = ADD ? prev[pt] : zero4();
+        const bool mine = 16 * rt < len;
+        if (mine) pair_row_tile<PACKED, D>(out, sm, hf, sc, rt, has_state, Dh);
         // the next chunk's loads (the last chunk re-reads its own) go out
         // before this tile's stores, which would hold them up in the memory
         // pipeline, and stay in flight across the state update
-        issue(c0n, lenn);
-        issue_dt(c0n, lenn);   // read by every wave, used by the scanner: no branch
-        if (add) pair_prev(prev, yrow + (size_t)c0n * xstride, xstride, lenn, rt);
+        if (ADD) pair_prev(prev, yrow + (size_t)c0n * xstride, xstride, lenn, rt);
         if (mine) pair_store(yrow + (size_t)c0 * xstride, xstride, out, len, rt, chk, check);
         if (!last || want_final) pair_state_update(sm, hf, sc, Hacc, v);
         // every wave is done with this chunk's tiles and the published state
@@ -1877,21 +1865,23 @@ __device__ __attribute__((noinline)) void pair_exact(const SegArgs a, OutSmem<64
     }
 }
 
-// Both passes of the fp16 form; returns the forward direction's outgoing
-// state in Hacc and the check sum of the last pass in chk.
-template <bool PACKED, bool SP>
+// Both passes of the fp16 form (NDIR directions); returns the forward
+// direction's outgoing state in Hacc and the check sum of the last pass in chk.
+template <bool PACKED, bool SP, int NDIR>
 __device__ __forceinline__ void pair_fast(const SegArgs &a, PairSmem &sm, int b, int seg, int h,
-                                                    int grp, int half, int v, f32x4 (&Hacc)[8],
-                                                    float &chk) {
-    if (a.ndir == 2) {
-        pair_pass<PACKED, 1, SP>(a, sm, b, seg, h, grp, false, half, v, Hacc, chk, false);
-        pair_pass<PACKED, 0, SP>(a, sm, b, seg, h, grp, true, half, v, Hacc, chk, true);
+                                          int grp, int half, int v, f32x4 (&Hacc)[8], float &chk) {
+    if (NDIR == 2) {
+        pair_pass<PACKED, 1, SP, false>(a, sm, b, seg, h, grp, half, v, Hacc, chk, false);
+        pair_pass<PACKED, 0, SP, true>(a, sm, b, seg, h, grp, half, v, Hacc, chk, true);
     } else {
-        pair_pass<PACKED, 0, SP>(a, sm, b, seg, h, grp, false, half, v, Hacc, chk, true);
+        pair_pass<PACKED, 0, SP, false>(a, sm, b, seg, h, grp, half, v, Hacc, chk, true);
     }
 }
 
-template <bool PACKED, bool SP>
+// NDIR (the number of directions, a.ndir) is a template argument: with it a
+// run-time branch, both passes share live ranges across it and the
+// register allocator spills the state.
+template <bool PACKED, bool SP, int NDIR>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 k_pair_out(const SegArgs a) {
     // XCD-aware order as in k_seg_out, over (row-segment, head pair)
@@ -1908,11 +1898,13 @@ k_pair_out(const SegArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
     const int half = wave >> 2, v = wave & 3;
     const int h = 2 * hp + half;
+    // the wave with the longer row tile of each SIMD's pair issues first
+    if ((half == 0 ? v : 3 - v) >= 2) __builtin_amdgcn_s_setprio(1);
     const int grp = (2 * hp) / (a.H / a.G);
     __shared__ __attribute__((aligned(16))) PairShared sh;
     f32x4 Hacc[8];
     float chk = 0.f;
-    pair_fast<PACKED, SP>(a, sh.fast, b, seg, h, grp, half, v, Hacc, chk);
+    pair_fast<PACKED, SP, NDIR>(a, sh.fast, b, seg, h, grp, half, v, Hacc, chk);
     const bool want_final = seg == a.nseg - 1 && a.final_state;
     if (want_final) {
 #pragma unroll
@@ -1974,10 +1966,14 @@ hipError_t launch_pair(const SegArgs &a, hipStream_t s) {
                   s, a);
     }
     const int per_xcd = (a.batch * a.nseg * (a.H / 2) + 7) / 8;
-    if (a.seq)
-        BM_LAUNCH("ssd_pair_out", (k_pair_out<true, SP>), dim3(per_xcd * 8), dim3(512), 0, s, a);
-    else
-        BM_LAUNCH("ssd_pair_out", (k_pair_out<false, SP>), dim3(per_xcd * 8), dim3(512), 0, s, a);
+    const dim3 grid(per_xcd * 8), block(512);
+    if (a.seq) {
+        if (a.ndir == 2) BM_LAUNCH("ssd_pair_out", (k_pair_out<true, SP, 2>), grid, block, 0, s, a);
+        else BM_LAUNCH("ssd_pair_out", (k_pair_out<true, SP, 1>), grid, block, 0, s, a);
+    } else {
+        if (a.ndir == 2) BM_LAUNCH("ssd_pair_out", (k_pair_out<false, SP, 2>), grid, block, 0, s, a);
+        else BM_LAUNCH("ssd_pair_out", (k_pair_out<false, SP, 1>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 
