@@ -1418,18 +1418,25 @@ __device__ __forceinline__ void pair_scans(const SegArgs &a, PairScan &sm, uint1
         sm.wsub = nz;
     }
 }
-// One head's share of the pair kernel's shared memory. The scans of chunk
-// s + 1 run while chunk s is in use, so they alternate between two buffers.
-struct PairHalf {
-    PairScan sc[2];
-    alignas(16) uint16_t xs[64 * kXS];   // x [t][p], fp16
-    alignas(16) uint16_t hs[kP * kNRS];  // H^T [p][n], fp16
+// One chunk's staged inputs (fp16): B and C of the group, x of each head.
+// Two of them alternate, so the next chunk is staged while this one is in use.
+struct PairStage {
+    alignas(16) uint16_t bn[bn_elems(64)];   // B [t][n], bn_row layout
+    alignas(16) uint16_t cn[bn_elems(64)];   // C [t][n], bn_row layout
+    alignas(16) uint16_t xs[2][64 * kXS];    // x [t][p] of each head
+};
+// The decay-masked Gram matrix M of each head as matrix-core operands: per
+// 16-row tile, the fp16 images that its lanes hand to the product, for the
+// 32-column pairs 0 and 1 (hi) and the residual (lo) of the pair holding the
+// diagonal tile.
+struct PairM {
+    u32x4 op[4][3][64];   // [row tile][pair 0 hi, pair 1 hi, band lo][lane]
 };
 struct PairSmem {
-    PairHalf half[2];
-    alignas(16) uint16_t bn[bn_elems(64)];   // B [t][n], fp16, bn_row layout
-    alignas(16) uint16_t cn[bn_elems(64)];   // C [t][n], fp16, bn_row layout
-    int bad[8];                              // per wave: a non-finite output or state
+    PairStage st[2];
+    PairScan sc[2][2];    // [head][chunk parity]
+    PairM m[2];           // [head]
+    int bad[8];           // per wave: a non-finite output or state
 };
 union PairShared {
     PairSmem fast;
@@ -1501,49 +1508,37 @@ struct PairLoads {
             cv[k] = ld8(Cm + o);
         }
     }
-    // converted to fp16 into LDS; rows at or past len as zeros
-    __device__ __forceinline__ void store(PairSmem &sm, PairHalf &hf, int len) const {
+    // converted to fp16 into the stage (x into the half's head); rows at or
+    // past len as zeros, masked rather than branched so that every lane
+    // passes the same waits
+    __device__ __forceinline__ void store(PairStage &st, int half, int len) const {
         const int th = threadIdx.x & 255, tid = threadIdx.x;
-        if (len == 64) {
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int item = th + 256 * k, row = item >> 3, cg = item & 7;
-                *(u32x4 *)(hf.xs + row * kXS + 8 * cg) = bf2h4(xv[k]);
-            }
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int item = tid + 512 * k, row = item >> 4, cg = item & 15;
-                *(u32x4 *)(sm.bn + bn_row(row) + 8 * cg) = bf2h4(bv[k]);
-                *(u32x4 *)(sm.cn + bn_row(row) + 8 * cg) = bf2h4(cv[k]);
-            }
-            return;
-        }
-        // masked rather than branched: every lane passes the same waits
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int item = th + 256 * k, row = item >> 3, cg = item & 7;
-            *(u32x4 *)(hf.xs + row * kXS + 8 * cg) = bf2h4(xv[k]) & (row < len ? ~0u : 0u);
+            *(u32x4 *)(st.xs[half] + row * kXS + 8 * cg) = bf2h4(xv[k]) & (row < len ? ~0u : 0u);
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int item = tid + 512 * k, row = item >> 4, cg = item & 15;
             const uint32_t m = row < len ? ~0u : 0u;
-            *(u32x4 *)(sm.bn + bn_row(row) + 8 * cg) = bf2h4(bv[k]) & m;
-            *(u32x4 *)(sm.cn + bn_row(row) + 8 * cg) = bf2h4(cv[k]) & m;
+            *(u32x4 *)(st.bn + bn_row(row) + 8 * cg) = bf2h4(bv[k]) & m;
+            *(u32x4 *)(st.cn + bn_row(row) + 8 * cg) = bf2h4(cv[k]) & m;
         }
     }
 };
 
-// The diagonal 64-block of row tile WQ (all of a 64-token chunk): 16-tiles on
-// the far side of the diagonal are 0; the others factor the decay through
-// their edge nearest the diagonal; the diagonal tile takes one exponential per
-// entry and D on its diagonal. The 32-column pair holding the diagonal tile
-// is split into fp16 hi + lo, the other pair rounded once.
+// Row tile WQ of M (16 rows, the whole 64-token chunk), written to mo as
+// matrix-core operands: 16-tiles on the far side of the diagonal are 0 (not
+// written; their readers skip them); the others factor the decay through
+// their edge nearest the diagonal; the diagonal tile takes one exponential
+// per entry and D on its diagonal. The 32-column pair holding the diagonal
+// tile is split into fp16 hi + lo, the other pair rounded once.
 template <bool PACKED, int D, int WQ>
-__device__ __forceinline__ void pair_diag(f32x4 (&acc)[4], const PairSmem &sm, const PairHalf &hf,
-                                          const PairScan &sc, const u32x4 (&cr)[kN / 32],
-                                          float rli, int sqi, float td, float Dh) {
-    const int g4 = lane_id() >> 4;
+__device__ __forceinline__ void pair_mrows_q(u32x4 (&mo)[3][64], const PairStage &st,
+                                             const PairScan &sc, const u32x4 (&cr)[kN / 32],
+                                             float rli, int sqi, float td, float Dh) {
+    const int lane = lane_id(), g4 = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         if (D == 0 ? 2 * kk > WQ : 2 * kk + 1 < WQ) continue;   // both tiles dead
@@ -1552,10 +1547,10 @@ __device__ __forceinline__ void pair_diag(f32x4 (&acc)[4], const PairSmem &sm, c
         const bool band = kk == WQ / 2;
         f32x4 gp[2];
         if (live0 && live1) {
-            gram_pair<true>(sm.bn, 32 * kk, 32 * kk + 16, cr, gp[0], gp[1]);
+            gram_pair<true>(st.bn, 32 * kk, 32 * kk + 16, cr, gp[0], gp[1]);
         } else {
-            gp[0] = live0 ? gram_tile<true>(sm.bn, 32 * kk, cr) : zero4();
-            gp[1] = live1 ? gram_tile<true>(sm.bn, 32 * kk + 16, cr) : zero4();
+            gp[0] = live0 ? gram_tile<true>(st.bn, 32 * kk, cr) : zero4();
+            gp[1] = live1 ? gram_tile<true>(st.bn, 32 * kk + 16, cr) : zero4();
         }
         uint32_t ph[4], pl[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -1595,161 +1590,221 @@ __device__ __forceinline__ void pair_diag(f32x4 (&acc)[4], const PairSmem &sm, c
                 ph[2 * half + 1] = pk_h(mv[2], mv[3]);
             }
         }
-        mx_step<true, true>(acc, hf.xs, 32 * kk, u32x4{ph[0], ph[1], ph[2], ph[3]},
-                      u32x4{pl[0], pl[1], pl[2], pl[3]}, band);
+        mo[kk][lane] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+        if (band) mo[2][lane] = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
 }
 
-// A row tile's outputs are held transposed (see mx_step): lane (g4, l16) has
-// row 16 rt + l16, columns 16 pt + 4 g4 .. + 3 in acc[pt], four consecutive
-// floats of y. yb points at the chunk's first row of y for the head. The
-// reverse pass's rows are read back in that layout by the lane that wrote
-// them; rows past the chunk's end read its last row.
-__device__ __forceinline__ void pair_prev(f32x4 (&prev)[4], const float *yb, uint32_t ystride,
-                                          int len, int rt) {
-    const int lane = lane_id(), row = min(16 * rt + (lane & 15), len - 1);
-    const float *yr = yb + (uint32_t)row * ystride + 4 * (lane >> 4);
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) prev[pt] = *(const f32x4 *)(yr + 16 * pt);
-}
-
-// Row tile rt (16 rows) of the chunk for the half's head: intra-chunk form
-// (with D x) and carried state added to acc (this lane's outputs: row
-// 16 rt + l16, columns 16 pt + 4 g4 + r), which comes in holding the other
-// direction's part or zeros.
+// The wave's row tile rt of M into LDS.
 template <bool PACKED, int D>
-__device__ __forceinline__ void pair_row_tile(f32x4 (&acc)[4], const PairSmem &sm,
-                                              const PairHalf &hf, const PairScan &sc, int rt,
-                                              bool has_state, float Dh) {
+__device__ __forceinline__ void pair_mrows(PairM &pm, const PairStage &st, const PairScan &sc, int rt,
+                                           float Dh) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
-    const int i = 16 * rt + l16;
     u32x4 cr[kN / 32];
 #pragma unroll
     for (int ks = 0; ks < kN / 32; ++ks)
-        cr[ks] = *(const u32x4 *)(sm.cn + 16 * rt * kBS + bn_lane(l16) + 32 * ks + 8 * g4);
+        cr[ks] = *(const u32x4 *)(st.cn + 16 * rt * kBS + bn_lane(l16) + 32 * ks + 8 * g4);
+    const int i = 16 * rt + l16;
     const float rli = sc.cs2[i];
     const int sqi = PACKED ? sc.sq[i] : 0;
     const float td = (float)(l16 - 4 * g4);
     switch (rt) {
-        case 0: pair_diag<PACKED, D, 0>(acc, sm, hf, sc, cr, rli, sqi, td, Dh); break;
-        case 1: pair_diag<PACKED, D, 1>(acc, sm, hf, sc, cr, rli, sqi, td, Dh); break;
-        case 2: pair_diag<PACKED, D, 2>(acc, sm, hf, sc, cr, rli, sqi, td, Dh); break;
-        default: pair_diag<PACKED, D, 3>(acc, sm, hf, sc, cr, rli, sqi, td, Dh); break;
-    }
-    // carried state: e^{cs_i} C_i . H (tiles it does not reach: skipped, exact)
-    if (has_state && sc.utile[rt]) {
-        f32x4 tt[4];
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) tt[pt] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < kN / 32; ++ks) {
-            u32x4 oh[4];
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-                oh[pt] = *(const u32x4 *)(hf.hs + (16 * pt + l16) * kNRS + 32 * ks + 8 * g4);
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) tt[pt] = mfma16x16x32_f16(oh[pt], cr[ks], tt[pt]);
-        }
-        const float u = (!PACKED || sqi == sc.sq_nb) ? exp2_(rli) : 0.f;
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(u, tt[pt][r], acc[pt][r]);
+        case 0: pair_mrows_q<PACKED, D, 0>(pm.op[0], st, sc, cr, rli, sqi, td, Dh); break;
+        case 1: pair_mrows_q<PACKED, D, 1>(pm.op[1], st, sc, cr, rli, sqi, td, Dh); break;
+        case 2: pair_mrows_q<PACKED, D, 2>(pm.op[2], st, sc, cr, rli, sqi, td, Dh); break;
+        default: pair_mrows_q<PACKED, D, 3>(pm.op[3], st, sc, cr, rli, sqi, td, Dh); break;
     }
 }
 
-// The row tile's outputs into y; rows past the chunk's end are not written.
-// With `check`, their sum joins chk (a non-finite output makes it non-finite).
-__device__ __forceinline__ void pair_store(float *yb, uint32_t ystride, const f32x4 (&out)[4],
-                                           int len, int rt, float &chk, bool check) {
-    const int lane = lane_id(), row = 16 * rt + (lane & 15);
-    float *yr = yb + (uint32_t)row * ystride + 4 * (lane >> 4);
-    if (row < len) {
+// The wave's 16 columns p = 16 v .. 16 v + 15 of the outputs, for all four
+// row tiles, are held transposed: acc[rt] lane (g4, l16) has row 16 rt + l16,
+// columns 16 v + 4 g4 .. + 3, four consecutive floats of y. In memory the
+// four 16-byte pieces of a row are taken by four consecutive lanes (one
+// 64-byte run per lane quad, which the memory pipeline moves at full rate):
+// lane (g4, 4 a + b) moves row 16 rt + 4 a + g4, columns 16 v + 4 b .. + 3,
+// the piece that lane (b, 4 a + g4) holds -- the lane index with its bits
+// 0-1 and 4-5 exchanged, a permutation that is its own inverse.
+__device__ __forceinline__ f32x4 quad_swap(f32x4 x) {
+    const int l = lane_id();
+    const int src = 4 * ((l & 12) | ((l & 3) << 4) | ((l >> 4) & 3));
+    f32x4 y;
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) *(f32x4 *)(yr + 16 * pt) = out[pt];
+    for (int r = 0; r < 4; ++r) y[r] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(x[r])));
+    return y;
+}
+// the row of y that this lane moves for row tile rt
+__device__ __forceinline__ int pair_mem_row(int rt) {
+    const int l = lane_id();
+    return 16 * rt + (l & 12) + (l >> 4);
+}
+// yb points at the chunk's first row of y for the head. The reverse pass's
+// rows are read back (rows past the chunk's end read its last row).
+__device__ __forceinline__ void pair_prev(f32x4 (&prev)[4], const float *yb, uint32_t ystride,
+                                          int len, int v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int row = min(pair_mem_row(rt), len - 1);
+        prev[rt] = *(const f32x4 *)(yb + (uint32_t)row * ystride + 16 * v + 4 * (lane & 3));
+    }
+}
+// prev as loaded into the register layout of acc
+__device__ __forceinline__ void pair_prev_regs(f32x4 (&acc)[4]) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = quad_swap(acc[rt]);
+}
+
+// acc += M x for the wave's columns: M from the operand images in LDS, x^T
+// through transposing reads (the k order of the images). Every operand is
+// read first (rows past the chunk's end included: computed, not stored).
+template <int D>
+__device__ __forceinline__ void pair_mx(f32x4 (&acc)[4], const PairM &pm, const uint16_t *xs, int v) {
+    const int lane = lane_id();
+    u32x4 xo[2], mo[4][3];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) xo[kk] = tr_operand(xs, kXS, 32 * kk, 16 * v);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const bool live = q == 2 || (D == 0 ? 2 * q <= rt : 2 * q + 1 >= rt);
+            mo[rt][q] = live ? pm.op[rt][q][lane] : u32x4{0u, 0u, 0u, 0u};
+        }
+    // products grouped by operand, the row tiles' chains interleaved
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            if (q < 2 && (D == 0 ? 2 * q > rt : 2 * q + 1 < rt)) continue;
+            acc[rt] = mfma16x16x32_f16(xo[q < 2 ? q : rt / 2], mo[rt][q], acc[rt]);
+        }
+}
+
+// The state's part of the outputs for the wave's columns: acc[rt] +=
+// e^{cs_i} C_i . H, H held in registers (Hacc; see pair_state_update) and
+// handed to the matrix cores as fp16: lane group g4 holds n = 32 ks + 8 g4 ..
+// + 7, the order of a plain C row read. Row tiles the state does not reach
+// (u = 0) are computed and dropped.
+template <bool PACKED>
+__device__ __forceinline__ void pair_state_out(f32x4 (&acc)[4], const PairStage &st, const PairScan &sc,
+                                               const f32x4 (&Hacc)[8]) {
+    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
+    u32x4 ho[kN / 32];
+#pragma unroll
+    for (int ks = 0; ks < kN / 32; ++ks) {
+        const f32x4 h0 = Hacc[2 * ks], h1 = Hacc[2 * ks + 1];
+        ho[ks] = u32x4{pk_h(h0[0], h0[1]), pk_h(h0[2], h0[3]), pk_h(h1[0], h1[1]), pk_h(h1[2], h1[3])};
+    }
+    // k steps outer, the four row tiles' chains interleaved (independent
+    // products back to back); a k step's C operands are read a step ahead
+    const uint16_t *cb = st.cn + bn_lane(l16) + 8 * g4;
+    u32x4 co[2][4];
+    f32x4 tt[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        co[0][rt] = *(const u32x4 *)(cb + 16 * rt * kBS);
+        tt[rt] = zero4();
+    }
+#pragma unroll
+    for (int ks = 0; ks < kN / 32; ++ks) {
+        if (ks + 1 < kN / 32) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                co[(ks + 1) & 1][rt] = *(const u32x4 *)(cb + 16 * rt * kBS + 32 * (ks + 1));
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) tt[rt] = mfma16x16x32_f16(ho[ks], co[ks & 1][rt], tt[rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int t = 16 * rt + l16;
+        const float u = (!PACKED || sc.sq[t] == sc.sq_nb) ? exp2_(sc.cs2[t]) : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[rt][r] = fmaf(u, tt[rt][r], acc[rt][r]);
+    }
+}
+
+// The outputs (rows below len) into y; with `check`, their sum joins chk (a
+// non-finite output makes it non-finite).
+__device__ __forceinline__ void pair_store(float *yb, uint32_t ystride, const f32x4 (&out)[4], int len,
+                                           int v, float &chk, bool check) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int row = pair_mem_row(rt);
+        const f32x4 o = quad_swap(out[rt]);
+        if (row < len) *(f32x4 *)(yb + (uint32_t)row * ystride + 16 * v + 4 * (lane & 3)) = o;
     }
     if (check) {
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            s0 += out[pt][0] + out[pt][1];
-            s1 += out[pt][2] + out[pt][3];
+        for (int rt = 0; rt < 4; ++rt) {
+            s0 += out[rt][0] + out[rt][1];
+            s1 += out[rt][2] + out[rt][3];
         }
         chk += s0 + s1;
     }
 }
 
+// B^T as the A operand of the state update, rows n in the state's order: for
+// tile nt = 2 ks + e, row m = 4 g + r is n = 32 ks + 8 g + 4 e + r (so that a
+// lane group of the product holds 8 consecutive n of each 32). As
+// tr_operand_bn with the lanes' column pointers spread accordingly.
+__device__ __forceinline__ u32x4 tr_operand_bt(const uint16_t *bn, int t32, int nt) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, s = lane & 15;
+    const uint16_t *p = bn + t32 * kBS + bn_lane(4 * g4 + (s >> 2)) + 32 * (nt >> 1) + 8 * (s & 3) +
+                        4 * (nt & 1);
+    const u32x2 a = ld_tr(p), b = ld_tr(p + 16 * kBS);
+    return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // H <- gamma H + sum over the chunk's tokens of w_t B_t x_t^T for the wave's
-// block of the state: n = 32 v .. 32 v + 31, every p; Hacc[4 nt + pt][r] =
-// H[n = 32 v + 16 nt + 4 g4 + r][p = 16 pt + l16]. B^T and x come from the
-// staged tiles through transposing reads, w x as packed fp16 products.
-__device__ __forceinline__ void pair_state_update(const PairSmem &sm, const PairHalf &hf,
-                                                  const PairScan &sc, f32x4 (&Hacc)[8], int v) {
-    const float gmm = sc.gamma;
-    // a chunk whose decay is exactly 0 starts the new state from nothing:
-    // the first products take a zero accumulator instead of a scaled one
-    const bool fresh = gmm == 0.f;
-    if (!fresh) {
+// columns p = 16 v .. 16 v + 15, all n: Hacc[nt][r] = H[n][p = 16 v + l16]
+// with n = 32 (nt / 2) + 8 g4 + 4 (nt % 2) + r. B^T and x come from the stage
+// through transposing reads, w x as packed fp16 products.
+__device__ __forceinline__ void pair_state_update(const PairStage &st, int half, const PairScan &sc,
+                                                  f32x4 (&Hacc)[8], int v) {
+    // (uniform values, read as scalars)
+    const float gmm = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sc.gamma)));
+    // a chunk whose decay is exactly 0 starts the new state from nothing
+    // (assigned, not scaled: 0 times a non-finite state is not 0)
+    if (gmm == 0.f) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) Hacc[q] = zero4();
+    } else {
 #pragma unroll
         for (int q = 0; q < 8; ++q) Hacc[q] *= gmm;
     }
-    if (!sc.wsub) {   // every weight is exactly 0
-        if (fresh) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) Hacc[q] = zero4();
-        }
-        return;
-    }
+    if (!__builtin_amdgcn_readfirstlane(sc.wsub)) return;   // every weight is exactly 0
     const int g4 = lane_id() >> 4;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        u32x4 aop[2], bx[4];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) aop[nt] = tr_operand_bn(sm.bn, 32 * ks, 32 * v + 16 * nt);
         const f32x4 w0 = *(const f32x4 *)(sc.w + 32 * ks + 4 * g4);        // k slots 0..3
         const f32x4 w1 = *(const f32x4 *)(sc.w + 32 * ks + 16 + 4 * g4);   // k slots 4..7
         const u32x4 wp = {pk_h(w0[0], w0[1]), pk_h(w0[2], w0[3]), pk_h(w1[0], w1[1]), pk_h(w1[2], w1[3])};
+        const u32x4 xv = tr_operand(st.xs[half], kXS, 32 * ks, 16 * v);
+        const u32x4 bx = {mul_h(xv[0], wp[0]), mul_h(xv[1], wp[1]), mul_h(xv[2], wp[2]), mul_h(xv[3], wp[3])};
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const u32x4 xv = tr_operand(hf.xs, kXS, 32 * ks, 16 * pt);
-            bx[pt] = u32x4{mul_h(xv[0], wp[0]), mul_h(xv[1], wp[1]), mul_h(xv[2], wp[2]), mul_h(xv[3], wp[3])};
-        }
-        if (ks == 0 && fresh) {
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-                    Hacc[4 * nt + pt] = mfma16x16x32_f16(aop[nt], bx[pt], zero4());
-        } else {
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-                    Hacc[4 * nt + pt] = mfma16x16x32_f16(aop[nt], bx[pt], Hacc[4 * nt + pt]);
+        for (int nt = 0; nt < 8; ++nt) {
+            const u32x4 aop = tr_operand_bt(st.bn, 32 * ks, nt);
+            Hacc[nt] = mfma16x16x32_f16(aop, bx, Hacc[nt]);
         }
     }
 }
 
-// Offset in a [p][n] state of this lane's entries of Hacc[4 nt + pt]
-// (4 consecutive n).
-__device__ __forceinline__ int pair_hoff(int v, int q) {
+// Offset in a [p][n] state of this lane's entries of Hacc[nt] (4 consecutive n).
+__device__ __forceinline__ int pair_hoff(int v, int nt) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
-    return (16 * (q & 3) + l16) * kN + 32 * v + 16 * (q >> 2) + 4 * g4;
+    return (16 * v + l16) * kN + 32 * (nt >> 1) + 8 * g4 + 4 * (nt & 1);
 }
 
-// The wave's block of the state (fp32 accumulators) into H^T, fp16.
-__device__ __forceinline__ void pair_publish(PairHalf &hf, const f32x4 (&Hacc)[8], int v) {
-    const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int o = (16 * (q & 3) + l16) * kNRS + 32 * v + 16 * (q >> 2) + 4 * g4;
-        *(u32x2 *)(hf.hs + o) = u32x2{pk_h(Hacc[q][0], Hacc[q][1]), pk_h(Hacc[q][2], Hacc[q][3])};
-    }
-}
-
-// One direction's walk over the segment's chunks for the half's head (wave v
-// of the half owns row tile rt and the state block of n = 32 v .. 32 v + 31).
-// Returns the outgoing state in Hacc.
+// One direction's walk over the segment's chunks for the half's head. Wave v
+// of the half owns the 16 columns p = 16 v .. + 15 (of the outputs and of the
+// state, which stays in its registers) and row tile rt of M, which it shares
+// through LDS. Per chunk, between the two barriers: M's row tile, the state's
+// part of the outputs and the state update (all from the stage and the
+// registers); after the second: M x, the outputs, the next chunk's stage and
+// scans. Returns the outgoing state in Hacc.
 template <bool PACKED, int D, bool SP, bool ADD>
 __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b, int seg, int h,
                                           int grp, int half, int v, f32x4 (&Hacc)[8],
@@ -1758,7 +1813,6 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     // row tiles mirrored in the second half: the two waves of a SIMD (v and
     // v + 4) then carry 16-row tiles of complementary causal length
     const int rt = half == 0 ? v : 3 - v;
-    PairHalf &hf = sm.half[half];
     const int t0 = seg * a.Ts, t1 = min(t0 + a.Ts, a.L);
     const int cfirst = t0 / Q, clast = (t1 - 1) / Q;
     const size_t PN = (size_t)kP * kN;
@@ -1777,7 +1831,6 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         else src = a.gam[slot(1, seg + 1)] == 0.f ? a.S + slot(1, seg + 1) * PN : a.Hs + slot(1, seg) * PN;
     }
     const int nch = clast - cfirst + 1;
-    const bool want_final = D == 0 && seg == a.nseg - 1 && a.final_state;
     auto chunk_at = [&](int s, int &c0, int &len) {
         const int c = D == 0 ? cfirst + s : clast - s;
         c0 = c * Q;
@@ -1785,7 +1838,6 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     };
     PairLoads<PACKED> ld;
     ld.init(a);
-    f32x4 prev[4];
     // the row's first token of x, dt, y for the head, of B, C for the group
     const size_t row0 = tok(a, b, 0);
     const uint32_t xstride = (uint32_t)(a.H * kP), bstride = (uint32_t)(a.G * kN);
@@ -1806,47 +1858,50 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     };
     const float A2 = dp.A[h] * kLog2e;
     const float dtb = SP && a.dt_bias[D] ? a.dt_bias[D][h] : 0.f;
+    f32x4 acc[4];   // the outputs of the wave's columns (pair_prev's layout)
     {
         int c0, len;
         chunk_at(0, c0, len);
         issue(c0, len);
         issue_dt(c0, len);
-        if (ADD) pair_prev(prev, yrow + (size_t)c0 * xstride, xstride, len, rt);
+        if (ADD) pair_prev(acc, yrow + (size_t)c0 * xstride, xstride, len, v);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) Hacc[q] = src ? *(const f32x4 *)(src + pair_hoff(v, q)) : zero4();
-    bool has_state = src != nullptr;
-    if (has_state) pair_publish(hf, Hacc, v);
     for (int s = 0; s < nch; ++s) {
         int c0, len;
         chunk_at(s, c0, len);
-        const PairScan &sc = hf.sc[s & 1];
-        ld.store(sm, hf, len);
-        // the chunk's scans, from step sizes that arrived with its x, B, C
-        if (scanner) pair_scans<PACKED, SP>(a, hf.sc[s & 1], ld.dtv[0], ld.sqv[0], A2, dtb, D, b, c0, len);
+        PairStage &st = sm.st[s & 1];
+        PairScan &sc = sm.sc[half][s & 1];
+        // stage and scans of chunk s: the buffers were last read two chunks
+        // ago, before the previous chunk's first barrier
+        ld.store(st, half, len);
+        if (scanner) pair_scans<PACKED, SP>(a, sc, ld.dtv[0], ld.sqv[0], A2, dtb, D, b, c0, len);
         const bool last = s == nch - 1;
         int c0n, lenn;
         chunk_at(last ? s : s + 1, c0n, lenn);
-        lds_barrier();   // chunk s staged, its scans and the published state visible
+        lds_barrier();   // chunk s staged and scanned
+        // the next chunk's loads (the last chunk re-reads its own) go out at
+        // once, to land during this chunk's work
         issue(c0n, lenn);
         issue_dt(c0n, lenn);
-        f32x4 out[4];
+        if (ADD) {
+            pair_prev_regs(acc);
+        } else {
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) out[pt] = ADD ? prev[pt] : zero4();
-        const bool mine = 16 * rt < len;
-        if (mine) pair_row_tile<PACKED, D>(out, sm, hf, sc, rt, has_state, Dh);
-        // the next chunk's loads (the last chunk re-reads its own) go out
-        // before this tile's stores, which would hold them up in the memory
-        // pipeline, and stay in flight across the state update
-        if (ADD) pair_prev(prev, yrow + (size_t)c0n * xstride, xstride, lenn, rt);
-        if (mine) pair_store(yrow + (size_t)c0 * xstride, xstride, out, len, rt, chk, check);
-        if (!last || want_final) pair_state_update(sm, hf, sc, Hacc, v);
-        // every wave is done with this chunk's tiles and the published state
-        lds_barrier();
-        if (!last) {
-            pair_publish(hf, Hacc, v);
-            has_state = true;
+            for (int k = 0; k < 4; ++k) acc[k] = zero4();
         }
+        // straight-line code, so that the scheduler can interleave the three:
+        // a row tile past the chunk's end is computed (not read), the state's
+        // part is taken with a zero state before the first update, and the
+        // last chunk's update is kept (its result unused unless final)
+        pair_mrows<PACKED, D>(sm.m[half], st, sc, rt, Dh);
+        pair_state_out<PACKED>(acc, st, sc, Hacc);
+        pair_state_update(st, half, sc, Hacc, v);
+        lds_barrier();   // every row tile of M written
+        pair_mx<D>(acc, sm.m[half], st.xs[half], v);
+        pair_store(yrow + (size_t)c0 * xstride, xstride, acc, len, v, chk, check);
+        if (ADD) pair_prev(acc, yrow + (size_t)c0n * xstride, xstride, lenn, v);
     }
 }
 
