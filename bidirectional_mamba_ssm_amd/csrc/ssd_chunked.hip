@@ -1648,10 +1648,15 @@ __device__ __forceinline__ void pair_prev(f32x4 (&prev)[4], const float *yb, uin
         prev[rt] = *(const f32x4 *)(yb + (uint32_t)row * ystride + 16 * v + 4 * (lane & 3));
     }
 }
-// prev as loaded into the register layout of acc
-__device__ __forceinline__ void pair_prev_regs(f32x4 (&acc)[4]) {
+// prev as loaded into the register layout of acc. The reverse pass leaves a
+// whole chunk's rows unpermuted (each lane's pieces in the places that it
+// moves: y between the passes is the kernel's own), so only a partial
+// chunk's rows are permuted.
+__device__ __forceinline__ void pair_prev_regs(f32x4 (&acc)[4], int len) {
+    if (len < 64) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[rt] = quad_swap(acc[rt]);
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = quad_swap(acc[rt]);
+    }
 }
 
 // acc += M x for the wave's columns: M from the operand images in LDS, x^T
@@ -1726,13 +1731,15 @@ __device__ __forceinline__ void pair_state_out(f32x4 (&acc)[4], const PairStage 
 
 // The outputs (rows below len) into y; with `check`, their sum joins chk (a
 // non-finite output makes it non-finite).
+// With perm false (a whole chunk of the reverse pass, read back by the
+// forward pass), the pieces are written unpermuted.
 __device__ __forceinline__ void pair_store(float *yb, uint32_t ystride, const f32x4 (&out)[4], int len,
-                                           int v, float &chk, bool check) {
+                                           int v, float &chk, bool check, bool perm) {
     const int lane = lane_id();
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         const int row = pair_mem_row(rt);
-        const f32x4 o = quad_swap(out[rt]);
+        const f32x4 o = perm ? quad_swap(out[rt]) : out[rt];
         if (row < len) *(f32x4 *)(yb + (uint32_t)row * ystride + 16 * v + 4 * (lane & 3)) = o;
     }
     if (check) {
@@ -1886,7 +1893,7 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         issue(c0n, lenn);
         issue_dt(c0n, lenn);
         if (ADD) {
-            pair_prev_regs(acc);
+            pair_prev_regs(acc, len);
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) acc[k] = zero4();
@@ -1900,7 +1907,8 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         pair_state_update(st, half, sc, Hacc, v);
         lds_barrier();   // every row tile of M written
         pair_mx<D>(acc, sm.m[half], st.xs[half], v);
-        pair_store(yrow + (size_t)c0 * xstride, xstride, acc, len, v, chk, check);
+        // the reverse pass of two writes y for the forward pass to read back
+        pair_store(yrow + (size_t)c0 * xstride, xstride, acc, len, v, chk, check, D == 0 || len < 64);
         if (ADD) pair_prev(acc, yrow + (size_t)c0n * xstride, xstride, lenn, v);
     }
 }
