@@ -1528,91 +1528,103 @@ struct PairLoads {
     }
 };
 
-// Row tile WQ of M (16 rows, the whole 64-token chunk), written to mo as
-// matrix-core operands: 16-tiles on the far side of the diagonal are 0 (not
-// written; their readers skip them); the others factor the decay through
-// their edge nearest the diagonal; the diagonal tile takes one exponential
-// per entry and D on its diagonal. The 32-column pair holding the diagonal
-// tile is split into fp16 hi + lo, the other pair rounded once.
-template <bool PACKED, int D, int WQ>
-__device__ __forceinline__ void pair_mrows_q(u32x4 (&mo)[3][64], const PairStage &st,
-                                             const PairScan &sc, const u32x4 (&cr)[kN / 32],
-                                             float rli, int sqi, float td, float Dh) {
-    const int lane = lane_id(), g4 = lane >> 4;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        if (D == 0 ? 2 * kk > WQ : 2 * kk + 1 < WQ) continue;   // both tiles dead
-        const bool live0 = D == 0 ? 2 * kk <= WQ : 2 * kk >= WQ;
-        const bool live1 = D == 0 ? 2 * kk + 1 <= WQ : 2 * kk + 1 >= WQ;
-        const bool band = kk == WQ / 2;
+// One unit of M: the 32-column pair KK of row tile WQ (16 rows) for both heads
+// of the workgroup, from one Gram computation (B and C are the group's, shared
+// by its heads); written to pm[e].op as matrix-core operands. 16-tiles on the
+// far side of the diagonal are 0 (not written; their readers skip them); the
+// others factor the decay through their edge nearest the diagonal; the
+// diagonal tile takes one exponential per entry and D on its diagonal. The
+// pair holding the diagonal tile is split into fp16 hi + lo, the other pair
+// rounded once.
+template <bool PACKED, int D, int WQ, int KK>
+__device__ __forceinline__ void pair_munit(PairM (&pm)[2], const PairStage &st, const PairScan &s0,
+                                           const PairScan &s1, const u32x4 (&cr)[kN / 32], int i,
+                                           float td, float Dh0, float Dh1) {
+    if constexpr (D == 0 ? 2 * KK > WQ : 2 * KK + 1 < WQ) {
+        return;   // both tiles dead
+    } else {
+        const int lane = lane_id(), g4 = lane >> 4;
+        constexpr bool live0 = D == 0 ? 2 * KK <= WQ : 2 * KK >= WQ;
+        constexpr bool live1 = D == 0 ? 2 * KK + 1 <= WQ : 2 * KK + 1 >= WQ;
+        constexpr bool band = KK == WQ / 2;
         f32x4 gp[2];
         if (live0 && live1) {
-            gram_pair<true>(st.bn, 32 * kk, 32 * kk + 16, cr, gp[0], gp[1]);
+            gram_pair<true>(st.bn, 32 * KK, 32 * KK + 16, cr, gp[0], gp[1]);
         } else {
-            gp[0] = live0 ? gram_tile<true>(st.bn, 32 * kk, cr) : zero4();
-            gp[1] = live1 ? gram_tile<true>(st.bn, 32 * kk + 16, cr) : zero4();
+            gp[0] = live0 ? gram_tile<true>(st.bn, 32 * KK, cr) : zero4();
+            gp[1] = live1 ? gram_tile<true>(st.bn, 32 * KK + 16, cr) : zero4();
         }
-        uint32_t ph[4], pl[4] = {0u, 0u, 0u, 0u};
+        // the sequence index is the token's, the same for both heads
+        const int sqi = PACKED ? s0.sq[i] : 0;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int jt = 2 * kk + half;
-            const int j0 = 16 * jt;
-            float mv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (D == 0 ? jt <= WQ : jt >= WQ) {
-                const f32x4 gg = gp[half];
-                const int jb = j0 + 4 * g4;
-                if (jt != WQ) {
-                    const float u16 = exp2_(rli - sc.cs2[D == 0 ? j0 + 15 : j0]);
-                    const f32x4 vv = *(const f32x4 *)(sc.v16 + jb);
+        for (int e = 0; e < 2; ++e) {
+            const PairScan &sc = e == 0 ? s0 : s1;
+            const float Dh = e == 0 ? Dh0 : Dh1;
+            const float rli = sc.cs2[i];
+            uint32_t ph[4], pl[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u16 * vv[r]);
-                } else {
-                    // td = l16 - 4 g4 (row minus column of entry r = 0): the
-                    // far side of the diagonal gets an exponent below -2^98
-                    // (exactly 0 after exp2), the diagonal itself adds D
-                    const f32x4 c4 = *(const f32x4 *)(sc.cs2 + jb);
-                    const f32x4 d4 = *(const f32x4 *)(sc.dt + jb);
+            for (int half = 0; half < 2; ++half) {
+                const int jt = 2 * KK + half;
+                const int j0 = 16 * jt;
+                float mv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (D == 0 ? jt <= WQ : jt >= WQ) {
+                    const f32x4 gg = gp[half];
+                    const int jb = j0 + 4 * g4;
+                    if (jt != WQ) {
+                        const float u16 = exp2_(rli - sc.cs2[D == 0 ? j0 + 15 : j0]);
+                        const f32x4 vv = *(const f32x4 *)(sc.v16 + jb);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float off = D == 0 ? td - (float)r : (float)r - td;
-                        const float far = fminf(off + 0.5f, 0.f) * 1e30f;
-                        const float dg = fmaxf(1.f - fabsf(off), 0.f) * Dh;
-                        mv[r] = fmaf(gg[r], exp2_((rli + far) - c4[r]) * d4[r], dg);
+                        for (int r = 0; r < 4; ++r) mv[r] = gg[r] * (u16 * vv[r]);
+                    } else {
+                        // td = l16 - 4 g4 (row minus column of entry r = 0): the
+                        // far side of the diagonal gets an exponent below -2^98
+                        // (exactly 0 after exp2), the diagonal itself adds D
+                        const f32x4 c4 = *(const f32x4 *)(sc.cs2 + jb);
+                        const f32x4 d4 = *(const f32x4 *)(sc.dt + jb);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float off = D == 0 ? td - (float)r : (float)r - td;
+                            const float far = fminf(off + 0.5f, 0.f) * 1e30f;
+                            const float dg = fmaxf(1.f - fabsf(off), 0.f) * Dh;
+                            mv[r] = fmaf(gg[r], exp2_((rli + far) - c4[r]) * d4[r], dg);
+                        }
                     }
+                    seq_mask<64, PACKED>(mv, sc, jb, sqi);
                 }
-                seq_mask<64, PACKED>(mv, sc, jb, sqi);
+                if (band) {
+                    split_h(mv[0], mv[1], ph[2 * half], pl[2 * half]);
+                    split_h(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
+                } else {
+                    ph[2 * half] = pk_h(mv[0], mv[1]);
+                    ph[2 * half + 1] = pk_h(mv[2], mv[3]);
+                }
             }
-            if (band) {
-                split_h(mv[0], mv[1], ph[2 * half], pl[2 * half]);
-                split_h(mv[2], mv[3], ph[2 * half + 1], pl[2 * half + 1]);
-            } else {
-                ph[2 * half] = pk_h(mv[0], mv[1]);
-                ph[2 * half + 1] = pk_h(mv[2], mv[3]);
-            }
+            pm[e].op[WQ][KK][lane] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+            if (band) pm[e].op[WQ][2][lane] = u32x4{pl[0], pl[1], pl[2], pl[3]};
         }
-        mo[kk][lane] = u32x4{ph[0], ph[1], ph[2], ph[3]};
-        if (band) mo[2][lane] = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
 }
 
-// The wave's row tile rt of M into LDS.
+// The wave's unit of M (row tile rt, column pair kk) into LDS for both heads.
 template <bool PACKED, int D>
-__device__ __forceinline__ void pair_mrows(PairM &pm, const PairStage &st, const PairScan &sc, int rt,
-                                           float Dh) {
+__device__ __forceinline__ void pair_mrows(PairM (&pm)[2], const PairStage &st, const PairScan &s0,
+                                           const PairScan &s1, int rt, int kk, float Dh0, float Dh1) {
     const int lane = lane_id(), g4 = lane >> 4, l16 = lane & 15;
     u32x4 cr[kN / 32];
 #pragma unroll
     for (int ks = 0; ks < kN / 32; ++ks)
         cr[ks] = *(const u32x4 *)(st.cn + 16 * rt * kBS + bn_lane(l16) + 32 * ks + 8 * g4);
     const int i = 16 * rt + l16;
-    const float rli = sc.cs2[i];
-    const int sqi = PACKED ? sc.sq[i] : 0;
     const float td = (float)(l16 - 4 * g4);
-    switch (rt) {
-        case 0: pair_mrows_q<PACKED, D, 0>(pm.op[0], st, sc, cr, rli, sqi, td, Dh); break;
-        case 1: pair_mrows_q<PACKED, D, 1>(pm.op[1], st, sc, cr, rli, sqi, td, Dh); break;
-        case 2: pair_mrows_q<PACKED, D, 2>(pm.op[2], st, sc, cr, rli, sqi, td, Dh); break;
-        default: pair_mrows_q<PACKED, D, 3>(pm.op[3], st, sc, cr, rli, sqi, td, Dh); break;
+    switch (2 * rt + kk) {
+        case 0: pair_munit<PACKED, D, 0, 0>(pm, st, s0, s1, cr, i, td, Dh0, Dh1); break;
+        case 1: pair_munit<PACKED, D, 0, 1>(pm, st, s0, s1, cr, i, td, Dh0, Dh1); break;
+        case 2: pair_munit<PACKED, D, 1, 0>(pm, st, s0, s1, cr, i, td, Dh0, Dh1); break;
+        case 3: pair_munit<PACKED, D, 1, 1>(pm, st, s0, s1, cr, i, td, Dh0, Dh1); break;
+        case 4: pair_munit<PACKED, D, 2, 0>(pm, st, s0, s1, cr, i, td, Dh0, Dh1); break;
+        case 5: pair_munit<PACKED, D, 2, 1>(pm, st, s0, s1, cr, i, td, Dh0, Dh1); break;
+        case 6: pair_munit<PACKED, D, 3, 0>(pm, st, s0, s1, cr, i, td, Dh0, Dh1); break;
+        default: pair_munit<PACKED, D, 3, 1>(pm, st, s0, s1, cr, i, td, Dh0, Dh1); break;
     }
 }
 
@@ -1825,7 +1837,12 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     const size_t PN = (size_t)kP * kN;
     auto slot = [&](int d, int k) { return (((size_t)b * 2 + d) * a.nseg + k) * a.H + h; };
     const DirPtrs &dp = a.dir[D];
-    const float Dh = dp.D ? dp.D[h] : 0.f;
+    // D of the workgroup's two heads (2 hp, 2 hp + 1)
+    const float Dh0 = dp.D ? dp.D[h & ~1] : 0.f, Dh1 = dp.D ? dp.D[h | 1] : 0.f;
+    // the wave's unit of M: the first half takes the column pair every row
+    // tile has, the second half the other pair of the mirrored row tile
+    // (absent for two of its waves)
+    const int kk = half == 0 ? (D == 0 ? 0 : 1) : (D == 0 ? 1 : 0);
     // incoming state of this segment in the walking direction (as seg_pass)
     const float *src = nullptr;
     if (D == 0) {
@@ -1902,7 +1919,7 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         // a row tile past the chunk's end is computed (not read), the state's
         // part is taken with a zero state before the first update, and the
         // last chunk's update is kept (its result unused unless final)
-        pair_mrows<PACKED, D>(sm.m[half], st, sc, rt, Dh);
+        pair_mrows<PACKED, D>(sm.m, st, sm.sc[0][s & 1], sm.sc[1][s & 1], rt, kk, Dh0, Dh1);
         pair_state_out<PACKED>(acc, st, sc, Hacc);
         pair_state_update(st, half, sc, Hacc, v);
         lds_barrier();   // every row tile of M written
@@ -1961,8 +1978,9 @@ k_pair_out(const SegArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
     const int half = wave >> 2, v = wave & 3;
     const int h = 2 * hp + half;
-    // the wave with the longer row tile of each SIMD's pair issues first
-    if ((half == 0 ? v : 3 - v) >= 2) __builtin_amdgcn_s_setprio(1);
+    // the wave with the shorter row tile of each SIMD's pair issues first
+    // (it carries the scans and runs on the critical path between barriers)
+    if ((half == 0 ? v : 3 - v) < 2) __builtin_amdgcn_s_setprio(1);
     const int grp = (2 * hp) / (a.H / a.G);
     __shared__ __attribute__((aligned(16))) PairShared sh;
     f32x4 Hacc[8];
