@@ -2022,15 +2022,17 @@ size_t seg_workspace(int batch, int L, int H, long ts) {
     return al256(st) * 2 + al256((size_t)batch * 2 * nseg * H * 4);
 }
 
-// Segment length: at most 1024 tokens (the reverse pass's outputs, read back
-// by the forward pass, then stay in the caches), shortened until the output
-// kernel has at least 256 workgroups of two heads (one per CU); then, with a
-// workspace limit, doubled until the segment states fit in it (a whole row is
-// one segment and needs none).
+// Segment length: the longest power-of-two multiple of the chunk for which
+// the output kernel still has at least 256 workgroups of two heads (one per
+// CU): fewer segments mean fewer segment states to write, scan and read, and
+// the segment pass stops reading a segment once its decay has underflowed,
+// so it reads a smaller share of a longer one. With a workspace limit, then
+// doubled until the segment states fit in it (a whole row is one segment and
+// needs none).
 int pick_ts(int batch, int L, int H, int Q, size_t limit) {
-    long ts = 1024;
+    long ts = Q;
+    while (ts < L) ts *= 2;
     while (ts > Q && (long)batch * ((L + ts - 1) / ts) * ((H + 1) / 2) < 256) ts /= 2;
-    if (ts < Q) ts = Q;
     while (ts < L && seg_workspace(batch, L, H, ts) > limit) ts *= 2;
     return (int)(ts < L ? ts : (L > Q ? L : Q));
 }
