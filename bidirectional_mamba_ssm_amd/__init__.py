@@ -274,13 +274,42 @@ def merge_linear(y_fwd, y_bwd, weight, bias=None, out=None, stream=None):
 
 
 class State:
-    """Library-owned forward-state cache: float [nslots, H, P, N] on the GPU."""
+    """Library-owned forward-state cache: float [nslots, H, P, N] on the GPU;
+    with conv=(ngroups, width, dtype) it also carries the short convolution's
+    context, [nslots, width-1, channels] of that dtype (bimamba_state_alloc_conv)."""
 
-    def __init__(self, nslots, nheads, headdim, d_state):
+    def __init__(self, nslots, nheads, headdim, d_state, conv=None):
         self._h = ctypes.c_void_p()
-        _abi.check(lib().bimamba_state_alloc(ctypes.byref(self._h), nslots, nheads,
-                                             headdim, d_state))
+        self.conv = None
+        if conv is None:
+            _abi.check(lib().bimamba_state_alloc(ctypes.byref(self._h), nslots, nheads,
+                                                 headdim, d_state))
+        else:
+            ngroups, width, dtype = conv
+            if dtype not in DTYPES:
+                raise TypeError(f"unsupported dtype {dtype}")
+            _abi.check(lib().bimamba_state_alloc_conv(ctypes.byref(self._h), nslots, nheads, headdim,
+                                                      d_state, ngroups, width, DTYPES[dtype]))
+            ch = conv_channels(nheads, headdim, ngroups, d_state)
+            self.conv = (ngroups, width, dtype, ch)
         self.shape = (nslots, nheads, headdim, d_state)
+
+    def ctx_tensor(self):
+        """A zero-copy torch view of the convolution context (valid while
+        this object lives)."""
+        if self.conv is None:
+            raise ValueError("this state carries no convolution context")
+        ptr = lib().bimamba_state_conv_ctx(self._h)
+        _, width, dtype, ch = self.conv
+        shape = (self.shape[0], width - 1, ch)
+        typestr = "<f4" if dtype == torch.float32 else "<u2"
+
+        class _View:
+            __cuda_array_interface__ = {
+                "shape": shape, "typestr": typestr, "data": (ptr, False),
+                "version": 2, "strides": None}
+        t = torch.as_tensor(_View(), device="cuda")
+        return t.view(torch.bfloat16) if dtype == torch.bfloat16 else t
 
     def data_ptr(self):
         return lib().bimamba_state_data(self._h)
@@ -334,6 +363,54 @@ def block_step(state, fwd, bwd, commit=False, chunk=64, y=None, stream=None, dt_
     _abi.check(lib().bimamba_block_step(state.handle, ctypes.byref(shape), ctypes.byref(fd),
                                         ctypes.byref(bd), int(bool(commit)), _ptr(y),
                                         _stream(stream)))
+    return y
+
+
+def block_step_conv(state, fwd, bwd, conv_fwd, conv_bwd, commit=False, chunk=64, y=None,
+                    activation="silu", conv_out=None, stream=None, dt_softplus=False):
+    """One cached block step from the block's raw convolution inputs
+    (bimamba_block_step_conv) for a State made with conv=...: the short
+    convolution of both directions (the forward one from the state's
+    context), then the block step; with commit the SSM state and the
+    context both move past the block.
+
+    conv_fwd/conv_bwd: dicts xbc [b, L, ch], weight [ch, W] f32, bias [ch] f32
+    or None. fwd/bwd: dicts dt, A, D (and optionally dt_bias) of each
+    direction; x, B, C are the convolution's outputs (allocated here, or
+    given in conv_out as for conv1d). Returns y."""
+    if state.conv is None:
+        raise ValueError("the state carries no convolution context")
+    ngroups, W, cdtype, ch = state.conv
+    xbc = conv_fwd["xbc"]
+    dev = _cuda_device(xbc)
+    if xbc.dim() != 3:
+        raise ValueError("xbc must be [batch, L, channels]")
+    batch, L, chx = xbc.shape
+    _, H, P, N = state.shape
+    if chx != ch or conv_fwd["weight"].shape != (ch, W) or xbc.dtype != cdtype:
+        raise ValueError("the convolution's inputs do not match the state's context")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation {activation!r} is not one of {sorted(map(str, ACTIVATIONS))}")
+    dims = (batch, L, ch, W)
+    outs = list(conv_out) if conv_out is not None else [None, None]
+    fo = _conv_out(outs[0], batch, L, H, P, ngroups, N, xbc.dtype, dev, "fwd")
+    bo = _conv_out(outs[1], batch, L, H, P, ngroups, N, xbc.dtype, dev, "bwd")
+    cfd = _conv_dir(conv_fwd, dims, xbc.dtype, dev, fo, "fwd")
+    cbd = _conv_dir(conv_bwd, dims, xbc.dtype, dev, bo, "bwd")
+    sf = dict(fwd, x=fo["x"], B=fo["B"], C=fo["C"])
+    sb = dict(bwd, x=bo["x"], B=bo["B"], C=bo["C"])
+    sdims = _dims(sf)
+    shape = make_shape(fo["x"], fo["B"], chunk, dt_softplus=dt_softplus)
+    fd = _dir(sf, xbc.dtype, sdims, dev, "fwd")
+    bd = _dir(sb, xbc.dtype, sdims, dev, "bwd")
+    if y is None:
+        y = torch.empty((batch, L, H, P), dtype=torch.float32, device=dev)
+    _check(y, "y", (batch, L, H, P), torch.float32, dev)
+    cshape = _abi.ConvShape(batch, L, H, P, N, ngroups, W, DTYPES[xbc.dtype], ACTIVATIONS[activation], 0)
+    _abi.check(lib().bimamba_block_step_conv(
+        state.handle, ctypes.byref(cshape), ctypes.byref(cfd), ctypes.byref(cbd),
+        ctypes.byref(shape), ctypes.byref(fd), ctypes.byref(bd), int(bool(commit)), _ptr(y),
+        _stream(stream)))
     return y
 
 

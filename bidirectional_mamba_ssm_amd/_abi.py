@@ -23,6 +23,7 @@ EXPORTS = (
     "bimamba_profile_end", "bimamba_conv1d_workspace_size", "bimamba_conv1d",
     "bimamba_ssd_bwd_workspace_size", "bimamba_ssd_bwd", "bimamba_gated_norm",
     "bimamba_ssd_fwd_streams", "bimamba_merge_linear", "bimamba_ssd_fwd_noalloc",
+    "bimamba_state_alloc_conv", "bimamba_state_conv_ctx", "bimamba_block_step_conv",
 )
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -116,6 +117,12 @@ def load():
                                                   ctypes.POINTER(ctypes.c_size_t)]
     lib.bimamba_conv1d.argtypes = [csp, cdp, cdp, i32p, ctypes.c_int, vp, vp, vp,
                                    ctypes.c_size_t, vp]
+    lib.bimamba_state_alloc_conv.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int]
+    lib.bimamba_state_conv_ctx.argtypes = [vp]
+    lib.bimamba_state_conv_ctx.restype = vp
+    lib.bimamba_block_step_conv.argtypes = [vp, csp, cdp, cdp, sp, dp, dp, ctypes.c_int, vp, vp]
     for name in EXPORTS:
         getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
     _LIB = lib

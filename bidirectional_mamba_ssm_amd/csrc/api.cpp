@@ -241,6 +241,10 @@ void prof_after(hipStream_t s) {
 struct bimamba_state {
     float *data;
     int nslots, nheads, headdim, d_state;
+    // the short convolution's context (bimamba_state_alloc_conv), or null
+    void *ctx;
+    int ngroups, width, cdtype;
+    size_t ctx_slot_bytes;   // (width - 1) * channels * element size
 };
 
 extern "C" {
@@ -440,9 +444,51 @@ int bimamba_state_alloc(bimamba_state **out, int nslots, int nheads, int headdim
     bimamba_state *st = new bimamba_state;
     st->data = data;
     st->nslots = nslots; st->nheads = nheads; st->headdim = headdim; st->d_state = d_state;
+    st->ctx = nullptr;
+    st->ngroups = st->width = st->cdtype = 0;
+    st->ctx_slot_bytes = 0;
     *out = st;
     return BIMAMBA_OK;
 }
+
+int bimamba_state_alloc_conv(bimamba_state **out, int nslots, int nheads, int headdim,
+                             int d_state, int ngroups, int width, int dtype) {
+    if (!out) return fail(BIMAMBA_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (ngroups < 1 || nheads % ngroups != 0)
+        return fail(BIMAMBA_EINVAL, "ngroups %d must be >= 1 and divide nheads %d", ngroups, nheads);
+    if (width < 2 || width > 4) return fail(BIMAMBA_EINVAL, "width %d not in 2..4", width);
+    if (dtype != BIMAMBA_BF16 && dtype != BIMAMBA_F32) return fail(BIMAMBA_EINVAL, "unknown dtype %d", dtype);
+    const size_t esz = dtype == BIMAMBA_BF16 ? 2 : 4;
+    const size_t ch = (size_t)nheads * headdim + 2 * (size_t)ngroups * d_state;
+    const size_t slot_bytes = (size_t)(width - 1) * ch * esz;
+    if (slot_bytes % 16)
+        return fail(BIMAMBA_EUNSUPPORTED, "a slot's context (%zu bytes) must be a multiple of 16 bytes", slot_bytes);
+    bimamba_state *st = nullptr;
+    int rc = bimamba_state_alloc(&st, nslots, nheads, headdim, d_state);
+    if (rc) return rc;
+    void *ctx = nullptr;
+    hipError_t e = hipMalloc(&ctx, slot_bytes * nslots);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        bimamba_state_free(st);
+        return fail(BIMAMBA_ENOMEM, "hipMalloc(%zu): %s", slot_bytes * nslots, hipGetErrorString(e));
+    }
+    e = hipMemset(ctx, 0, slot_bytes * nslots);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(ctx);
+        bimamba_state_free(st);
+        return hip_fail(e, "zeroing the convolution context");
+    }
+    st->ctx = ctx;
+    st->ngroups = ngroups; st->width = width; st->cdtype = dtype;
+    st->ctx_slot_bytes = slot_bytes;
+    *out = st;
+    return BIMAMBA_OK;
+}
+
+void *bimamba_state_conv_ctx(bimamba_state *st) { return st ? st->ctx : nullptr; }
 
 int bimamba_state_reset(bimamba_state *st, const int32_t *slots, int n,
                         bimamba_stream stream) {
@@ -457,6 +503,9 @@ int bimamba_state_reset(bimamba_state *st, const int32_t *slots, int n,
     const size_t slot_elems = (size_t)st->nheads * st->headdim * st->d_state;
     hipError_t e = launch_zero_slots(st->data, slot_elems, slots, n, st->nslots,
                                      (hipStream_t)stream);
+    if (e == hipSuccess && st->ctx)   // the context: zeroed as floats (slots of 16-byte multiples)
+        e = launch_zero_slots((float *)st->ctx, st->ctx_slot_bytes / 4, slots, n, st->nslots,
+                              (hipStream_t)stream);
     return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "state reset");
 }
 
@@ -465,6 +514,10 @@ float *bimamba_state_data(bimamba_state *st) { return st ? st->data : nullptr; }
 int bimamba_state_free(bimamba_state *st) {
     if (!st) return BIMAMBA_OK;
     hipError_t e = hipFree(st->data);
+    if (st->ctx) {
+        const hipError_t e2 = hipFree(st->ctx);
+        if (e == hipSuccess) e = e2;
+    }
     delete st;
     return e == hipSuccess ? BIMAMBA_OK : hip_fail(e, "hipFree");
 }
@@ -670,6 +723,45 @@ int bimamba_conv1d(const bimamba_conv_shape *s, const bimamba_conv_dir *fwd,
     if ((e = launch_conv(a, s->dtype == BIMAMBA_BF16, st)) != hipSuccess)
         return hip_fail(e, "launching conv1d");
     return BIMAMBA_OK;
+}
+
+int bimamba_block_step_conv(bimamba_state *st, const bimamba_conv_shape *cs,
+                            const bimamba_conv_dir *cfwd, const bimamba_conv_dir *cbwd,
+                            const bimamba_shape *s, const bimamba_dir *fwd,
+                            const bimamba_dir *bwd, int commit, float *y,
+                            bimamba_stream stream) {
+    if (!st) return fail(BIMAMBA_EINVAL, "state is NULL");
+    if (!st->ctx) return fail(BIMAMBA_EINVAL, "the state carries no convolution context (bimamba_state_alloc_conv)");
+    if (!cs || !s) return fail(BIMAMBA_EINVAL, "shapes are NULL");
+    if (!cfwd || !cbwd || !fwd || !bwd) return fail(BIMAMBA_EINVAL, "both directions are required");
+    if (!y) return fail(BIMAMBA_EINVAL, "y is NULL");
+    if (!aligned16(y)) return fail(BIMAMBA_EINVAL, "y must be 16-byte aligned");
+    if (cs->batch != s->batch || cs->seqlen != s->seqlen || cs->nheads != s->nheads ||
+        cs->headdim != s->headdim || cs->d_state != s->d_state || cs->ngroups != s->ngroups ||
+        cs->dtype != s->dtype)
+        return fail(BIMAMBA_EINVAL, "the convolution's shape does not match the block's");
+    if (cs->width != st->width || cs->dtype != st->cdtype || cs->ngroups != st->ngroups)
+        return fail(BIMAMBA_EINVAL, "the convolution (width %d, dtype %d, ngroups %d) does not match the "
+                    "state's context (%d, %d, %d)", cs->width, cs->dtype, cs->ngroups, st->width,
+                    st->cdtype, st->ngroups);
+    if (cs->batch > st->nslots)
+        return fail(BIMAMBA_EINVAL, "batch %d exceeds the state's %d slots", cs->batch, st->nslots);
+    if (fwd->x != cfwd->x || fwd->B != cfwd->B || fwd->C != cfwd->C || bwd->x != cbwd->x ||
+        bwd->B != cbwd->B || bwd->C != cbwd->C)
+        return fail(BIMAMBA_EINVAL, "the block's x, B, C must be the convolution's outputs");
+    // validate the scan's arguments before anything is launched
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if (s->nheads != st->nheads || s->headdim != st->headdim || s->d_state != st->d_state)
+        return fail(BIMAMBA_EINVAL, "shape (H=%d, P=%d, N=%d) does not match the state (%d, %d, %d)",
+                    s->nheads, s->headdim, s->d_state, st->nheads, st->headdim, st->d_state);
+    if ((rc = check_dir(fwd, "forward", false))) return rc;
+    if ((rc = check_dir(bwd, "reverse", false))) return rc;
+    // the context advances only with a committed block (in place: one
+    // workgroup walks each row's block in order)
+    rc = bimamba_conv1d(cs, cfwd, cbwd, nullptr, 0, st->ctx, commit ? st->ctx : nullptr, nullptr, 0, stream);
+    if (rc) return rc;
+    return bimamba_block_step(st, s, fwd, bwd, commit, y, stream);
 }
 
 int bimamba_gated_norm(long long rows, int channels, int group_size, int dtype,

@@ -191,6 +191,22 @@ int bimamba_state_reset(bimamba_state *st, const int32_t *slots, int n,
 float *bimamba_state_data(bimamba_state *st);
 int bimamba_state_free(bimamba_state *st);
 
+/* A state cache object that also carries the short convolution's context
+ * (the depthwise filter in front of the scan, DiffuMamba blog, "network
+ * architecture", d_conv = 4): besides the nslots forward SSM states, each
+ * slot's last width-1 raw forward inputs (the convolution's input channels,
+ * dtype [nslots][width-1][channels], channels = nheads*headdim +
+ * 2*ngroups*d_state, oldest first), so that the cache of a finalized prefix
+ * is exact for the whole mixer ("Fixed state, long reach", Sec. 1). Both
+ * start at zero; bimamba_state_reset zeroes both for the listed slots;
+ * bimamba_state_free releases both. width 2..4, dtype BIMAMBA_BF16 or
+ * BIMAMBA_F32. */
+int bimamba_state_alloc_conv(bimamba_state **out, int nslots, int nheads, int headdim,
+                             int d_state, int ngroups, int width, int dtype);
+/* Device pointer of the convolution context (layout above) for saving and
+ * loading, or NULL when the object carries none. */
+void *bimamba_state_conv_ctx(bimamba_state *st);
+
 /* One cached block-diffusion denoising step ("Fixed state, long reach",
  * Sec. 1: the forward SSM state of the finalized prefix is the cache, and the
  * reverse scan is restricted to the active block). For every slot b in
@@ -341,6 +357,28 @@ int bimamba_conv1d(const bimamba_conv_shape *s, const bimamba_conv_dir *fwd,
                    const bimamba_conv_dir *bwd, const int32_t *cu_seqlens, int nseq,
                    const void *init_ctx, void *final_ctx,
                    void *workspace, size_t workspace_bytes, bimamba_stream stream);
+
+/* The block step from the block's raw convolution inputs, for a state made
+ * by bimamba_state_alloc_conv: the short convolution of both directions over
+ * the block (bimamba_conv1d; the forward filter starts from the state's
+ * context, the reverse filter sees zeros after the block's end), then
+ * bimamba_block_step on the filtered values, in stream order.
+ *  cs        the convolution's shape: batch, seqlen, nheads, headdim,
+ *            d_state, ngroups, dtype as in s; width and dtype as the
+ *            state's context
+ *  cfwd/cbwd raw inputs (xbc), filters, and the x, B, C the filtered values
+ *            are written to (bimamba_conv_dir)
+ *  s, fwd, bwd, y, commit
+ *            as for bimamba_block_step; fwd/bwd's x, B and C must be
+ *            cfwd/cbwd's outputs (checked)
+ * With commit != 0 the SSM state and the context both move past the block
+ * (the context then holds the block's last width-1 raw forward inputs);
+ * otherwise neither changes. */
+int bimamba_block_step_conv(bimamba_state *st, const bimamba_conv_shape *cs,
+                            const bimamba_conv_dir *cfwd, const bimamba_conv_dir *cbwd,
+                            const bimamba_shape *s, const bimamba_dir *fwd,
+                            const bimamba_dir *bwd, int commit, float *y,
+                            bimamba_stream stream);
 /* Per-kernel timing for benchmarks and profilers, per calling thread.
  * Between bimamba_profile_begin() and bimamba_profile_end(), every kernel the
  * library launches from this thread is bracketed by two hipEvents recorded on

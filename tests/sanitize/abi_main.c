@@ -81,6 +81,10 @@ int main(void) {
     expect(bimamba_conv1d(&cs, &cd, NULL, NULL, 0, dev, (void *)((uintptr_t)dev + 16), NULL, 0, NULL),
            BIMAMBA_EINVAL, "conv contexts overlap");
     expect(bimamba_conv1d_workspace_size(&cs, -2, &n), BIMAMBA_EINVAL, "conv nseq");
+    expect(bimamba_state_alloc_conv(&st, 1, 4, 64, 128, 1, 5, BIMAMBA_BF16), BIMAMBA_EINVAL, "conv state width");
+    expect(bimamba_state_alloc_conv(&st, 1, 1, 3, 2, 1, 4, BIMAMBA_BF16), BIMAMBA_EUNSUPPORTED, "conv state slot bytes");
+    expect(bimamba_state_conv_ctx(NULL) == NULL ? 0 : 1, 0, "conv ctx null");
+    expect(bimamba_block_step_conv(NULL, &cs, &cd, &cd, &s, &d, &d, 1, y, NULL), BIMAMBA_EINVAL, "conv step no state");
     expect(bimamba_gated_norm(8, 300, 300, BIMAMBA_BF16, y, dev, y, 1e-5f, dev, NULL), BIMAMBA_EUNSUPPORTED, "norm channels");
     expect(bimamba_gated_norm(8, 512, 256, 9, y, dev, y, 1e-5f, dev, NULL), BIMAMBA_EINVAL, "norm dtype");
     expect(bimamba_merge_linear(8, 33, 16, y, y, dev, NULL, y, NULL), BIMAMBA_EUNSUPPORTED, "merge cin");

@@ -136,6 +136,26 @@ def test_state_and_block_step_validation(lib):
                                   ctypes.byref(fake_dir()), 0, FAKE, None) == _abi.EINVAL
 
 
+def test_conv_state_validation(lib):
+    """The state with a convolution context and the raw-input block step:
+    malformed arguments are rejected before any allocation or launch."""
+    h = ctypes.c_void_p()
+    assert lib.bimamba_state_alloc_conv(None, 1, 4, 64, 128, 1, 4, _abi.BF16) == _abi.EINVAL
+    assert lib.bimamba_state_alloc_conv(ctypes.byref(h), 1, 4, 64, 128, 1, 5, _abi.BF16) == _abi.EINVAL
+    assert lib.bimamba_state_alloc_conv(ctypes.byref(h), 1, 4, 64, 128, 1, 1, _abi.BF16) == _abi.EINVAL
+    assert lib.bimamba_state_alloc_conv(ctypes.byref(h), 1, 4, 64, 128, 3, 4, _abi.BF16) == _abi.EINVAL
+    assert lib.bimamba_state_alloc_conv(ctypes.byref(h), 1, 4, 64, 128, 1, 4, 7) == _abi.EINVAL
+    # a slot's context that is not a multiple of 16 bytes: 3 x (3 + 2 * 2) bf16 values
+    assert lib.bimamba_state_alloc_conv(ctypes.byref(h), 1, 1, 3, 2, 1, 4, _abi.BF16) == _abi.EUNSUPPORTED
+    assert lib.bimamba_state_conv_ctx(None) is None
+    cs, s = conv_shape(), shape(seqlen=64)
+    rc = lib.bimamba_block_step_conv(None, ctypes.byref(cs), ctypes.byref(fake_conv_dir()),
+                                     ctypes.byref(fake_conv_dir()), ctypes.byref(s),
+                                     ctypes.byref(fake_dir()), ctypes.byref(fake_dir()), 1, FAKE, None)
+    assert rc == _abi.EINVAL
+    assert b"state is NULL" in lib.bimamba_last_error()
+
+
 def test_seq_index_validation(lib):
     arr = (ctypes.c_int32 * 3)(0, 5, 4)
     assert lib.bimamba_seq_index(arr, 2, 4, FAKE, None) == _abi.EINVAL

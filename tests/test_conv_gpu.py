@@ -206,6 +206,85 @@ def test_block_step_with_conv():
     assert ok, f"committed state: error {err:.3e}"
 
 
+def test_block_step_conv_state():
+    """The convolution's context carried in the state object
+    (bimamba_state_alloc_conv, bimamba_block_step_conv): a prefix is filtered
+    (into the state's context) and scanned (into its SSM state), then two
+    committed blocks and one uncommitted block run from raw inputs. Outputs
+    and committed states match the oracle's convolution of the whole
+    sequence (forward) and of each block alone (reverse) fed to its block
+    step; the context equals the last width-1 raw forward inputs, bit for
+    bit; the uncommitted block changes neither the state nor the context."""
+    H, P, G, N, W = 4, 64, 1, 128, 4
+    ch = bm.conv_channels(H, P, G, N)
+    nseq, Lp, Lb = 2, 150, 64
+    L = Lp + 3 * Lb
+    f, b = synth.make_conv_inputs(nseq, L, ch, W, "bf16", 57, device=DEV)
+    ssd_f, ssd_b = synth.make_inputs(nseq, L, H, P, N, G, "bf16", 58, device=DEV)
+
+    def part(d, lo, hi):
+        return dict(xbc=d["xbc"][:, lo:hi].contiguous(), weight=d["weight"], bias=d["bias"])
+
+    def scan_part(d, lo, hi, conv_out=None):
+        out = dict(dt=d["dt"][:, lo:hi].contiguous(), A=d["A"], D=d["D"])
+        if conv_out is not None:
+            out.update(x=conv_out["x"], B=conv_out["B"], C=conv_out["C"])
+        return out
+
+    st = bm.State(nseq, H, P, N, conv=(G, W, torch.bfloat16))
+    ctx = st.ctx_tensor()
+    assert tuple(ctx.shape) == (nseq, W - 1, ch) and not bool(ctx.abs().sum())
+    # prefix: filtered into the state's context, scanned into its SSM state
+    pf, _ = bm.conv1d(part(f, 0, Lp), None, H, P, G, N, init_ctx=ctx, final_ctx=ctx)
+    bm.ssd_fwd(scan_part(ssd_f, 0, Lp, pf), None, chunk=64, init_state=st.tensor(),
+               final_state=st.tensor())
+    torch.cuda.synchronize()
+    _, st_ref = oracle.bissd(scan_part(ssd_f, 0, Lp, pf), None, want_final_state=True)
+
+    whole = oconv.conv1d(f["xbc"], f["weight"], f["bias"])
+    for k, commit in enumerate((True, True, False)):
+        lo, hi = Lp + k * Lb, Lp + (k + 1) * Lb
+        state_before = st.tensor().clone()
+        ctx_before = ctx.clone()
+        outs = ({}, {})
+        for o in outs:
+            o.update(x=torch.empty(nseq, Lb, H, P, dtype=torch.bfloat16, device=DEV),
+                     B=torch.empty(nseq, Lb, G, N, dtype=torch.bfloat16, device=DEV),
+                     C=torch.empty(nseq, Lb, G, N, dtype=torch.bfloat16, device=DEV))
+        y = bm.block_step_conv(st, scan_part(ssd_f, lo, hi), scan_part(ssd_b, lo, hi),
+                               part(f, lo, hi), part(b, lo, hi), commit=commit, chunk=64,
+                               conv_out=outs)
+        torch.cuda.synchronize()
+        # the filtered values: the forward filter continues the whole
+        # sequence, the reverse one sees only the block
+        got_f = np.concatenate([_np(outs[0][n]).reshape(nseq, Lb, -1) for n in ("x", "B", "C")], axis=-1)
+        worst, ok = conv_close(got_f, whole[:, lo:hi], _scale(f, False)[:, lo:hi], "bf16")
+        assert ok, f"block {k}: forward conv {worst:.3f} delta outside"
+        blk_rev = oconv.conv1d(part(b, lo, hi)["xbc"], b["weight"], b["bias"], reverse=True)
+        got_b = np.concatenate([_np(outs[1][n]).reshape(nseq, Lb, -1) for n in ("x", "B", "C")], axis=-1)
+        worst, ok = conv_close(got_b, blk_rev, _scale(part(b, lo, hi), True), "bf16")
+        assert ok, f"block {k}: reverse conv {worst:.3f} delta outside"
+        y_ref, st_next = oracle.block_step(st_ref, scan_part(ssd_f, lo, hi, outs[0]),
+                                           scan_part(ssd_b, lo, hi, outs[1]), commit=commit)
+        err, ok = within(_np(y), y_ref, "bf16")
+        print(f"block {k} (commit={commit}): y {err:.3e}", flush=True)
+        assert ok, f"block {k}: y error {err:.3e}"
+        if commit:
+            err, ok = within(_np(st.tensor()), st_next, "bf16")
+            assert ok, f"block {k}: committed state error {err:.3e}"
+            assert torch.equal(ctx, f["xbc"][:, hi - (W - 1):hi]), f"block {k}: carried context"
+            st_ref = st_next
+        else:
+            assert torch.equal(st.tensor(), state_before), "uncommitted block changed the state"
+            assert torch.equal(ctx, ctx_before), "uncommitted block changed the context"
+    # reset zeroes both
+    st.reset([1])
+    torch.cuda.synchronize()
+    assert not bool(ctx[1].float().abs().sum()) and not bool(st.tensor()[1].abs().sum())
+    assert bool(ctx[0].float().abs().sum())
+    st.free()
+
+
 def _random_conv_cases(n, seed):
     rng = np.random.default_rng(seed)
     cases = []
