@@ -1378,17 +1378,22 @@ __device__ __forceinline__ float lane_f(float v, int src) {
 // chunk's total minus the token's walking sum.
 // A2: A_h log2(e); dtb: the step-size bias (with SP), both read once per pass.
 template <bool PACKED, bool SP>
+// With PACKED, sqv is the sequence index of the lane's token and sqn that of
+// the token the carried state comes from (-1: none), both loaded with the
+// step sizes.
 __device__ __forceinline__ void pair_scans(const SegArgs &a, PairScan &sm, uint16_t dtv, int sqv,
-                                           float A2, float dtb, int d, int b, int c0, int len) {
+                                           int sqn, float A2, float dtb, int d, int b, int c0,
+                                           int len) {
     const int lane = lane_id();
     const int pos = d == 0 ? lane : 63 - lane;
     int sq_nb = 0, sq_edge = 0;
     bool has_nb = true;
     if (PACKED) {
-        const int nb = d == 0 ? c0 - 1 : c0 + len;
-        has_nb = d == 0 ? c0 > 0 : c0 + len < a.L;
-        sq_nb = has_nb ? a.seq[tok(a, b, nb)] : -1;
-        sq_edge = a.seq[tok(a, b, d == 0 ? c0 + len - 1 : c0)];
+        sq_nb = __builtin_amdgcn_readfirstlane(sqn);
+        has_nb = sq_nb >= 0;
+        // the chunk's outgoing edge: position len - 1 forward (lane len - 1),
+        // position 0 backward (lane 63)
+        sq_edge = __builtin_amdgcn_readlane(sqv, d == 0 ? len - 1 : 63);
     }
     const bool in = pos < len;
     float dtf = in ? bf2f(dtv) : 0.f;
@@ -1451,7 +1456,7 @@ template <bool PACKED>
 struct PairLoads {
     u32x4 xv[2], bv[2], cv[2];
     uint16_t dtv[1];
-    int sqv[1];
+    int sqv[1], sqn[1];
     uint32_t ox[2], ob[2];   // element offsets of this thread's pieces in a whole chunk
 
     __device__ __forceinline__ void init(const SegArgs &a) {
@@ -1473,10 +1478,17 @@ struct PairLoads {
     // (no branch for the compiler to move); a wave that does not scan (own
     // false) reads the first token in every lane, one cache line.
     __device__ __forceinline__ void issue_dt(const uint16_t *dt, const int32_t *sq, uint32_t dstride,
-                                             int d, int len, bool own) {
+                                             int d, int len, bool own, bool has_nb) {
         const int pos = own ? min(d == 0 ? lane_id() : 63 - lane_id(), len - 1) : 0;
         dtv[0] = dt[(uint32_t)pos * dstride];
-        sqv[0] = PACKED ? sq[pos] : 0;
+        if (PACKED) {
+            sqv[0] = sq[pos];
+            // the token the carried state comes from: before the chunk
+            // forward, after it backward
+            sqn[0] = has_nb ? sq[d == 0 ? -1 : len] : -1;
+        } else {
+            sqv[0] = sqn[0] = 0;
+        }
     }
     // X: the chunk's first row of x for the half's head; Bm, Cm: of B and C
     // for the group
@@ -1878,7 +1890,8 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     // the scans run on the wave with the shortest row tile
     const bool scanner = rt == 0;
     auto issue_dt = [&](int c0, int len) {
-        ld.issue_dt(dtrow + (size_t)c0 * a.H, PACKED ? sqrow + c0 : nullptr, (uint32_t)a.H, D, len, scanner);
+        ld.issue_dt(dtrow + (size_t)c0 * a.H, PACKED ? sqrow + c0 : nullptr, (uint32_t)a.H, D, len, scanner,
+                    D == 0 ? c0 > 0 : c0 + len < a.L);
     };
     const float A2 = dp.A[h] * kLog2e;
     const float dtb = SP && a.dt_bias[D] ? a.dt_bias[D][h] : 0.f;
@@ -1900,7 +1913,7 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         // stage and scans of chunk s: the buffers were last read two chunks
         // ago, before the previous chunk's first barrier
         ld.store(st, half, len);
-        if (scanner) pair_scans<PACKED, SP>(a, sc, ld.dtv[0], ld.sqv[0], A2, dtb, D, b, c0, len);
+        if (scanner) pair_scans<PACKED, SP>(a, sc, ld.dtv[0], ld.sqv[0], ld.sqn[0], A2, dtb, D, b, c0, len);
         const bool last = s == nch - 1;
         int c0n, lenn;
         chunk_at(last ? s : s + 1, c0n, lenn);
@@ -2022,17 +2035,26 @@ size_t seg_workspace(int batch, int L, int H, long ts) {
     return al256(st) * 2 + al256((size_t)batch * 2 * nseg * H * 4);
 }
 
-// Segment length: the longest power-of-two multiple of the chunk for which
-// the output kernel still has at least 256 workgroups of two heads (one per
-// CU): fewer segments mean fewer segment states to write, scan and read, and
-// the segment pass stops reading a segment once its decay has underflowed,
-// so it reads a smaller share of a longer one. With a workspace limit, then
-// doubled until the segment states fit in it (a whole row is one segment and
-// needs none).
+// Segment length: a power-of-two multiple of the chunk chosen for the output
+// kernel's time, estimated as (rounds of 256 workgroups, one per CU) x (the
+// segment's tokens + 256 tokens' worth of per-workgroup overhead), ties to
+// the longer segment: long segments mean fewer segment states to write, scan
+// and read, and the segment pass stops reading a segment once its decay has
+// underflowed, but a partial last round of workgroups costs as much as a
+// full one. With a workspace limit, then doubled until the segment states fit
+// in it (a whole row is one segment and needs none).
 int pick_ts(int batch, int L, int H, int Q, size_t limit) {
-    long ts = Q;
-    while (ts < L) ts *= 2;
-    while (ts > Q && (long)batch * ((L + ts - 1) / ts) * ((H + 1) / 2) < 256) ts /= 2;
+    const long pairs = (long)batch * ((H + 1) / 2);
+    long ts = Q, best_cost = -1;
+    for (long t = Q;; t *= 2) {
+        const long rounds = (pairs * ((L + t - 1) / t) + 255) / 256;
+        const long cost = rounds * (t + 256);
+        if (best_cost < 0 || cost <= best_cost) {
+            ts = t;
+            best_cost = cost;
+        }
+        if (t >= L) break;
+    }
     while (ts < L && seg_workspace(batch, L, H, ts) > limit) ts *= 2;
     return (int)(ts < L ? ts : (L > Q ? L : Q));
 }

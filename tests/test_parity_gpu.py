@@ -593,9 +593,9 @@ def test_block_step_plan_matches_call():
 @pytest.mark.parametrize("bidir", [False, True], ids=["fwd", "bi"])
 def test_inplace_state_many_segments(bidir):
     """final_state given as the very array of init_state (updated in place)
-    on a row cut into 8 segments, the way a long prefix is built in 8192-token
-    pieces chained through the cache: no workgroup may read the incoming
-    state after another one wrote the outgoing state."""
+    on a row cut into several segments, the way a long prefix is built in
+    8192-token pieces chained through the cache: no workgroup may read the
+    incoming state after another one wrote the outgoing state."""
     c = synth.BLOCK_STEP
     H, P, N, G = c["nheads"], c["headdim"], c["d_state"], c["ngroups"]
     L = 8192
@@ -609,7 +609,7 @@ def test_inplace_state_many_segments(bidir):
     torch.cuda.synchronize()
     ref, fs_ref = oracle.bissd(f, b, init_state=init, want_final_state=True)
     err, ok = within(y.double().cpu().numpy(), ref, "bf16")
-    print(f"in place, 8 segments, bidir={bidir}: y {err:.3e}", flush=True)
+    print(f"in place, several segments, bidir={bidir}: y {err:.3e}", flush=True)
     assert ok, f"y error {err:.3e}"
     err, ok = within(state.double().cpu().numpy(), fs_ref, "bf16")
     print(f"  final state {err:.3e}", flush=True)
