@@ -37,6 +37,8 @@
 //                per head, dA and dD per block, into the workspace.
 //   k_bwd_sum_bc / k_bwd_sum_ad: sums over the heads of a group and over the
 //                blocks, in a fixed order (deterministic results).
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "mfma.hpp"
@@ -53,17 +55,29 @@ struct BwdArgs {
     GradPtrs gfwd, gbwd;
     const float *dy;
     int batch, L, H, G, ndir, nc;
-    float *S;      // [batch][ndir][H][nc][N][P]: block states, then entering states
-    float *R;      // [batch][ndir][H][nc][N][P]: output-gradient feeds, then dHe
+    float *S;      // [batch][ndir][H][nc][N x P]: block states, then entering states
+    float *R;      // [batch][ndir][H][nc][N x P]: output-gradient feeds, then dHe
     double *lg;    // [batch][ndir][H][nc]: s_end of each block
     float *dBp;    // [batch][ndir][H][L][N]
     float *dCp;    // [batch][ndir][H][L][N]
     float *dAp;    // [batch][ndir][H][nc]
     float *dDp;    // [batch][ndir][H][nc]
     int head_loop; // the gradient kernel walks each group's heads (no dBp, dCp)
+    int chain;     // Hp and dHe by k_bwd_chain (else k_bwd_state + k_bwd_pass)
 };
 
 __device__ __forceinline__ int tok_of(int k, int L, bool rev) { return rev ? L - 1 - k : k; }
+
+// An N x P state in the workspace, in the matrix cores' result layout: 16 x
+// 16 tiles (n-tile major), each as the 64 lanes' 4-vectors of a 16x16
+// product's result (lane l: column l % 16, rows 4 (l / 16) .. +3), so that a
+// wave writes a tile as one contiguous kilobyte. Element (n, p) is at
+//   ((n / 16) (P / 16) + p / 16) 256 + 4 (16 ((n % 16) / 4) + p % 16) + n % 4;
+// tile_pos gives the start of lane's 4-vector in tile (nt, pt).
+template <int P>
+__device__ __forceinline__ int tile_pos(int nt, int pt, int lane) {
+    return (nt * (P / 16) + pt) * 256 + lane * 4;
+}
 
 // threadIdx.x; with LT behind an empty asm statement, a fresh value wherever
 // it is read, so that the compiler recomputes lane addresses inside the loop
@@ -197,14 +211,19 @@ __device__ __forceinline__ void fetch_flat(Flat<NP, NT> &f, const float *src) {
     }
 }
 
+// A state held as loaded (the tile layout of tile_pos) into LDS [N][S]:
+// 4-vector e4 is lane e4 % 64 of tile e4 / 64, rows 4 (lane / 16) .. +3 of
+// column lane % 16.
 template <int NP, int NT, int P, bool LT = false, int S>
 __device__ __forceinline__ void store_flat(const Flat<NP, NT> &f, float (*dst)[S]) {
 #pragma unroll
     for (int k = 0; k < Flat<NP, NT>::VPT; ++k) {
         const int e4 = lane_tid<LT>() + k * NT;
         if (e4 < NP / 4) {
-            const int e = 4 * e4;
-            *(float4 *)&dst[e / P][e % P] = make_float4(f.v[k][0], f.v[k][1], f.v[k][2], f.v[k][3]);
+            const int tile = e4 >> 6, ln = e4 & 63;
+            const int n0 = (tile / (P / 16)) * 16 + 4 * (ln >> 4), p = (tile % (P / 16)) * 16 + (ln & 15);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[n0 + i][p] = f.v[k][i];
         }
     }
 }
@@ -274,9 +293,7 @@ __global__ __launch_bounds__(kStateThreads) void k_bwd_state(BwdArgs a) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = mm([&](int mm_, int k) { return Wm[k][nt * 16 + mm_]; },
                          [&](int k, int mm_) { return Vm[k][pt * 16 + mm_]; }, 0, kQ, acc);
-                const int gq = lane >> 4, col = pt * 16 + (lane & 15);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) out[so + (size_t)(nt * 16 + 4 * gq + r) * P + col] = acc[r];
+                *(f32x4 *)&out[so + tile_pos<P>(nt, pt, lane)] = acc;
             }
         }
         __syncthreads();
@@ -322,6 +339,247 @@ __global__ __launch_bounds__(256) void k_bwd_pass(BwdArgs a, int np) {
             carry = fmaf(expf((float)a.lg[unit * a.nc + c0 - k]), carry, v[k]);
         }
     }
+}
+
+// ---- the chained form of the two kernels above, for many (row, stream,
+// head) units: one workgroup per unit walks its blocks forward, then
+// backward, the state in the matrix-core accumulators, and writes each
+// block's entering state Hp_c (over S) and leaving-state gradient dHe_c (over
+// R) before folding the block in:
+//   Hp_{c+1}   = e^{s_end} Hp_c   + sum_j (e^{s_end - s_j} dt_j x_j) B_j^T-side
+//   dHe_{c-1}  = e^{s_end} dHe_c  + sum_i (e^{s_i} dy_i) C_i^T-side
+// (the block's own S and R of k_bwd_state never leave the CU). Products on
+// the bf16 matrix cores (v_mfma_f32_16x16x32_bf16): an fp32 operand enters as
+// the exact sum of three bf16 parts, bf16 inputs B and C as they are, so the
+// products are those of fp32 operands, accumulated in fp32.
+
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef short v4i16_v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_v lds_v4i16_v;
+
+__device__ __forceinline__ uint32_t bf_pair(float v0, float v1) {
+    const bf16x2_v h = {(__bf16)v0, (__bf16)v1};
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ float bf_low(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_high(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// v = p[0] + p[1] + p[2] exactly (each part bf16, rounded to nearest; the
+// residues v - p[0] and v - p[0] - p[1] are exact in fp32), for a pair.
+__device__ __forceinline__ void split3(float v0, float v1, uint32_t (&p)[3]) {
+    p[0] = bf_pair(v0, v1);
+    const float r0 = v0 - bf_low(p[0]), r1 = v1 - bf_high(p[0]);
+    p[1] = bf_pair(r0, r1);
+    p[2] = bf_pair(r0 - bf_low(p[1]), r1 - bf_high(p[1]));
+}
+
+// Matrix-core operand (A or B of v_mfma_f32_16x16x32_bf16) for the 16
+// columns c0 .. c0+15 of a row-major [t][c] bf16 tile in LDS (row stride rs
+// elements), k over its 32 rows t32 .. t32+31, by two transposing LDS reads
+// (ds_read_b64_tr_b16: within 16 lanes, lane s points at row t + s/4,
+// column c0 + 4 (s%4), and lane i receives column c0 + i of those 4 rows).
+// Lane group g holds k slots 0..3 = rows t32 + 4g + (0..3) and 4..7 = rows
+// t32 + 16 + 4g + (0..3); both operands of a product read this way agree.
+__device__ __forceinline__ u32x4 tr_op(const uint16_t *base, int rs, int t32, int c0) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, s = lane & 15;
+    const uint16_t *p = base + (t32 + 4 * g4 + (s >> 2)) * rs + c0 + 4 * (s & 3);
+    const v4i16_v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_v *)p);
+    const v4i16_v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_v *)(p + 16 * rs));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+constexpr int kChainThreads = 256;
+
+// A block's rows of a per-token array as loaded (bf16 bits or fp32), for
+// loads that stay in flight across a loop iteration: every load is issued
+// (rows past the block's end re-read its last row, and are zeroed where
+// used) and nothing reads the registers until then, so no wait falls between
+// the loads and the work they overlap.
+template <typename T, int W, int NT>
+struct RawRows {
+    static constexpr int NV = kQ * W / 4, VPT = NV / NT;
+    static_assert(NV % NT == 0, "whole 4-vectors per thread");
+    using V = typename std::conditional<sizeof(T) == 2, u32x2, f32x4>::type;
+    V v[VPT];
+    __device__ __forceinline__ void fetch(const void *src, size_t rowt, size_t stride, size_t off,
+                                          int k0, int len, int L, bool rev) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int e4 = (int)threadIdx.x + k * NT;
+            const int r = min(e4 * 4 / W, len - 1), c = e4 * 4 % W;
+            v[k] = *(const V *)((const T *)src + (rowt + tok_of(k0 + r, L, rev)) * stride + off + c);
+        }
+    }
+    // the four values of vector k as floats
+    __device__ __forceinline__ void get(int k, float *o) const {
+        if constexpr (sizeof(T) == 2) {
+            o[0] = __uint_as_float(v[k][0] << 16);
+            o[1] = __uint_as_float(v[k][0] & 0xffff0000u);
+            o[2] = __uint_as_float(v[k][1] << 16);
+            o[3] = __uint_as_float(v[k][1] & 0xffff0000u);
+        } else {
+            o[0] = v[k][0]; o[1] = v[k][1]; o[2] = v[k][2]; o[3] = v[k][3];
+        }
+    }
+};
+
+template <int P, int N, bool EXACT>
+struct ChainSmem {
+    static constexpr int NA = EXACT ? 1 : 3;
+    static constexpr int RA = N + 8, RB = P + 8;   // bf16 row strides (8-byte aligned reads)
+    uint16_t a[NA][kQ][RA];   // B (forward sweep) or C (backward sweep) rows, [t][n]
+    uint16_t b[3][kQ][RB];    // weighted x or dy rows, [t][p], three parts
+    float w[kQ];
+    float gamma;
+};
+
+// One sweep: SW 0 walks blocks forward (B, x; Hp over S), SW 1 backward (C,
+// dy; dHe over R).
+template <typename T, int P, int N, int SW>
+__device__ __forceinline__ void chain_sweep(const BwdArgs &a, ChainSmem<P, N, sizeof(T) == 2> &sm,
+                                            int h, int dir, int b) {
+    constexpr bool EXACT = sizeof(T) == 2;
+    using Sm = ChainSmem<P, N, EXACT>;
+    constexpr int NT = kChainThreads, NW = NT / 64;
+    constexpr int TN = N / 16, TP = P / 16, TILES = TN * TP, TPW = (TILES + NW - 1) / NW;
+    static_assert(NW % TP == 0, "a wave's tiles share their columns p");
+    using XT = typename std::conditional<SW == 0, T, float>::type;
+    const bool rev = dir == 1;
+    const DirPtrs d = rev ? a.bwd : a.fwd;
+    const int g = h / (a.H / a.G);
+    const size_t rowt = (size_t)b * a.L;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
+    const size_t sgn = (size_t)a.G * N, hp = (size_t)a.H * P;
+    const void *asrc = SW == 0 ? d.B : d.C;
+    const void *bsrc = SW == 0 ? d.x : (const void *)a.dy;
+    float *out = SW == 0 ? a.S : a.R;
+    const float A = d.A[h];
+    const int pt = wave % TP;
+
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) acc[u] = zero4();
+
+    RawRows<T, N, NT> ra;
+    RawRows<XT, P, NT> rb;
+    T dtn = 0;   // (as loaded; lanes of wave 0, one position each)
+    auto fetch = [&](int c) {
+        const int k0 = c * kQ, len = min(kQ, a.L - k0);
+        ra.fetch(asrc, rowt, sgn, (size_t)g * N, k0, len, a.L, rev);
+        rb.fetch(bsrc, rowt, hp, (size_t)h * P, k0, len, a.L, rev);
+        if (tid < kQ) dtn = ((const T *)d.dt)[(rowt + tok_of(k0 + min(tid, len - 1), a.L, rev)) * a.H + h];
+    };
+    fetch(SW == 0 ? 0 : a.nc - 1);
+    for (int step = 0; step < a.nc; ++step) {
+        const int c = SW == 0 ? step : a.nc - 1 - step;
+        const int k0 = c * kQ, len = min(kQ, a.L - k0);
+        // running sums of dt A over the block (fp64, one lane per position),
+        // the weights and the block's decay
+        if (tid < kQ) {
+            const float dtf = tid < len ? Elem<T>::load(&dtn, 0) : 0.f;
+            const double s = wave_scan((double)dtf * (double)A, tid);
+            const double send = __shfl(s, len - 1);
+            sm.w[tid] = tid >= len ? 0.f : SW == 0 ? expf((float)(send - s)) * dtf : expf((float)s);
+            if (tid == 0) sm.gamma = expf((float)send);
+        }
+        __syncthreads();   // (also: the previous block's products are done with the tiles)
+        // the block's rows into LDS: B or C as bf16 (exact for bf16 inputs,
+        // else three parts), x or dy times the weight of its row in three
+        // parts; rows past the block's end as zeros
+#pragma unroll
+        for (int k = 0; k < RawRows<T, N, NT>::VPT; ++k) {
+            const int e4 = tid + k * NT;
+            const int r = e4 * 4 / N, cc = e4 * 4 % N;
+            float v[4];
+            ra.get(k, v);
+            if (EXACT) {
+                *(u32x2 *)&sm.a[0][r][cc] = u32x2{bf_pair(r < len ? v[0] : 0.f, r < len ? v[1] : 0.f),
+                                                  bf_pair(r < len ? v[2] : 0.f, r < len ? v[3] : 0.f)};
+            } else {
+                uint32_t p01[3], p23[3];
+                split3(r < len ? v[0] : 0.f, r < len ? v[1] : 0.f, p01);
+                split3(r < len ? v[2] : 0.f, r < len ? v[3] : 0.f, p23);
+#pragma unroll
+                for (int q = 0; q < Sm::NA; ++q) *(u32x2 *)&sm.a[q][r][cc] = u32x2{p01[q], p23[q]};
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < RawRows<XT, P, NT>::VPT; ++k) {
+            const int e4 = tid + k * NT;
+            const int r = e4 * 4 / P, cc = e4 * 4 % P;
+            const float wr = sm.w[r];
+            float v[4];
+            rb.get(k, v);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = r < len ? v[i] * wr : 0.f;
+            uint32_t p01[3], p23[3];
+            split3(v[0], v[1], p01);
+            split3(v[2], v[3], p23);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) *(u32x2 *)&sm.b[q][r][cc] = u32x2{p01[q], p23[q]};
+        }
+        const float gmm = sm.gamma;
+        // the next block's rows are in flight during this block's products
+        // (the last block loads its own again: no branch around the loads)
+        fetch(SW == 0 ? min(c + 1, a.nc - 1) : max(c - 1, 0));
+        __syncthreads();
+        // the state before the block, then the update
+        const size_t so = (unit * a.nc + c) * (size_t)(N * P);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wave + u * NW;
+            if (t < TILES) {
+                const int nt = t / TP;
+                *(f32x4 *)&out[so + tile_pos<P>(nt, pt, lane)] = acc[u];
+                // a block whose decay is exactly 0 starts from nothing
+                // (assigned: 0 times a non-finite state is not 0)
+                acc[u] = gmm == 0.f ? zero4() : acc[u] * gmm;
+            }
+        }
+        (void)len;
+#pragma unroll
+        for (int ks = 0; ks < kQ / 32; ++ks) {
+            u32x4 bo[3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) bo[q] = tr_op(&sm.b[q][0][0], Sm::RB, 32 * ks, pt * 16);
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int t = wave + u * NW;
+                if (t < TILES) {
+                    const int nt = t / TP;
+                    // result rows n (the A operand's columns), columns p
+                    const u32x4 a0 = tr_op(&sm.a[0][0][0], Sm::RA, 32 * ks, nt * 16);
+                    if (EXACT) {
+                        acc[u] = mfma16x16x32(a0, bo[2], acc[u]);
+                        acc[u] = mfma16x16x32(a0, bo[1], acc[u]);
+                        acc[u] = mfma16x16x32(a0, bo[0], acc[u]);
+                    } else {
+                        const u32x4 a1 = tr_op(&sm.a[Sm::NA > 1 ? 1 : 0][0][0], Sm::RA, 32 * ks, nt * 16);
+                        const u32x4 a2 = tr_op(&sm.a[Sm::NA > 2 ? 2 : 0][0][0], Sm::RA, 32 * ks, nt * 16);
+                        // the six products down to 2^-16 x 2^-16 of the leading one
+                        acc[u] = mfma16x16x32(a1, bo[1], acc[u]);
+                        acc[u] = mfma16x16x32(a2, bo[0], acc[u]);
+                        acc[u] = mfma16x16x32(a0, bo[2], acc[u]);
+                        acc[u] = mfma16x16x32(a1, bo[0], acc[u]);
+                        acc[u] = mfma16x16x32(a0, bo[1], acc[u]);
+                        acc[u] = mfma16x16x32(a0, bo[0], acc[u]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kChainThreads) void k_bwd_chain(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) ChainSmem<P, N, sizeof(T) == 2> sm;
+    const int h = blockIdx.x;
+    const int dir = (int)(blockIdx.y % (unsigned)a.ndir), b = (int)(blockIdx.y / (unsigned)a.ndir);
+    chain_sweep<T, P, N, 0>(a, sm, h, dir, b);
+    __syncthreads();
+    chain_sweep<T, P, N, 1>(a, sm, h, dir, b);
 }
 
 template <int P, int N>
@@ -770,9 +1028,14 @@ template <typename T, int P, int N>
 hipError_t launch_pn(BwdArgs &a, hipStream_t s) {
     if (a.L > 0) {
         const dim3 grid(a.nc, a.H, a.batch * a.ndir);
-        BM_LAUNCH("bwd_state", (k_bwd_state<T, P, N>), grid, dim3(kStateThreads), 0, s, a);
-        const dim3 pgrid((N * P + 255) / 256, a.H, a.batch * a.ndir);
-        BM_LAUNCH("bwd_pass", k_bwd_pass, pgrid, dim3(256), 0, s, a, N * P);
+        if (a.chain) {
+            BM_LAUNCH("bwd_chain", (k_bwd_chain<T, P, N>), dim3(a.H, a.batch * a.ndir),
+                      dim3(kChainThreads), 0, s, a);
+        } else {
+            BM_LAUNCH("bwd_state", (k_bwd_state<T, P, N>), grid, dim3(kStateThreads), 0, s, a);
+            const dim3 pgrid((N * P + 255) / 256, a.H, a.batch * a.ndir);
+            BM_LAUNCH("bwd_pass", k_bwd_pass, pgrid, dim3(256), 0, s, a, N * P);
+        }
         if (a.head_loop) {
             const dim3 ggrid(a.nc, a.G, a.batch * a.ndir);
             BM_LAUNCH("bwd_grad", (k_bwd_grad_heads<T, P, N>), ggrid, dim3(kGradThreads), 0, s, a);
@@ -809,6 +1072,16 @@ size_t al(size_t n) { return (n + 255) & ~(size_t)255; }
 bool head_loop(int batch, int L, int ndir) {
     const long long nc = (L + kQ - 1) / kQ;
     return nc * batch * ndir >= 256;
+}
+
+// Whether the entering states and leaving-state gradients come from the
+// chained kernel: it walks a unit's blocks one after another, so it needs
+// units to fill the CUs (two or more chains per CU) or few blocks per chain;
+// otherwise the block-parallel state kernel and the element-parallel pass
+// over its output take less time despite their traffic.
+bool use_chain(int batch, int L, int H, int ndir) {
+    const long long nc = (L + kQ - 1) / kQ, units = (long long)batch * ndir * H;
+    return units >= 512 || nc <= 16;
 }
 
 BwdLayout layout(int batch, int L, int H, int P, int N, int ndir) {
@@ -850,6 +1123,7 @@ hipError_t launch_bwd(const BwdProblem &p, void *ws, hipStream_t s) {
     a.ndir = p.has_bwd ? 2 : 1;
     a.nc = (p.L + kQ - 1) / kQ;
     a.head_loop = head_loop(p.batch, p.L, a.ndir);
+    a.chain = use_chain(p.batch, p.L, p.H, a.ndir);
     const BwdLayout w = layout(p.batch, p.L, p.H, p.P, p.N, a.ndir);
     char *base = (char *)ws;
     a.S = (float *)(base + w.S);

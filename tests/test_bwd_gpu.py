@@ -78,6 +78,13 @@ CASES = [
     ("bf16_short", 3, 5, 2, 64, 128, 1, "bf16", 74),
     ("bf16_L1", 2, 1, 2, 16, 16, 1, "bf16", 75),
     ("bf16_groups", 1, 257, 8, 64, 128, 4, "bf16", 76),
+    # more than 16 blocks and fewer than 512 (row, stream, head) units: the
+    # block-parallel state kernel and the pass over its output
+    ("bf16_state_pass", 1, 1100, 2, 64, 128, 1, "bf16", 89),
+    ("f32_state_pass", 2, 1090, 2, 16, 16, 1, "f32", 90),
+    # 512 units and 21 blocks: the chained kernel over a longer walk
+    ("f32_long_chain", 2, 1300, 128, 16, 16, 1, "f32", 92),
+    ("bf16_long_chain_groups", 1, 1350, 256, 16, 128, 2, "bf16", 93),
 ]
 
 
