@@ -984,6 +984,510 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad_heads(BwdArgs a) {
     }
 }
 
+// ---- the gradient block on the bf16 matrix cores (bf16 inputs, headdim
+// 64, d_state 128): the same terms as grad_block, every product a sum of
+// bf16 products with fp32 accumulation. B, C and x enter as given (exact);
+// the fp32 operands (dy, M = L o G, L o dM, Hp, dHe) as the exact sum of
+// three bf16 parts. Operands are read so that both of a product agree on the
+// order of k inside an instruction: lane group g holds k32 + 4g + (0..3) and
+// k32 + 16 + 4g + (0..3), read along a row (dir_op) or down the rows of a
+// row-major tile (tr_op).
+
+// The bf16 tiles of this kernel are row-major [row][col] arrays padded by
+// 16 elements a row (so that consecutive rows start 4 bank pairs apart, of
+// 16 pairs of 4-byte banks), with bits 2..3 of the column index XORed with
+// (row / 4) % 4: the 16 lanes that one LDS cycle serves then fall on 16
+// different bank pairs both when they read one 4-column group of 16
+// consecutive rows (dir_op, and the row-wise writes) and when they read 4
+// groups of 4 consecutive rows (tr_ops). The XOR touches only the bits that
+// vary between a wave's lanes, so an operand's address is a per-lane base
+// plus an offset fixed where it is read.
+__device__ __forceinline__ int swz_x(int r) { return ((r >> 2) & 3) << 2; }
+template <int RS>
+__device__ __forceinline__ int swz(int r, int col) { return r * RS + (col ^ swz_x(r)); }
+
+// Matrix-core operand from rows m0 + (lane % 16) of a swizzled tile (row
+// stride RS; m0 a multiple of 16), k along the row from k32.
+template <int RS>
+__device__ __forceinline__ u32x4 dir_op(const uint16_t *base, int m0, int k32) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, m = lane & 15;
+    const uint16_t *p = base + (m0 + m) * RS + k32 + ((4 * g4) ^ swz_x(m));
+    const u32x2 x0 = *(const u32x2 *)p, x1 = *(const u32x2 *)(p + 16);
+    return u32x4{x0[0], x0[1], x1[0], x1[1]};
+}
+
+// Matrix-core operand for the 16 columns c0 .. c0+15 (c0 a multiple of 16)
+// of a swizzled tile, k down its rows t32 .. t32+31 (t32 a multiple of 32),
+// by two transposing LDS reads (ds_read_b64_tr_b16: lane s of a 16-lane
+// group points at row t + s/4, columns c0 + 4 (s%4) .. +3, and lane i
+// receives column c0 + i of those 4 rows; here (row / 4) % 4 is the lane
+// group g, so the XOR is (s%4) ^ g).
+template <int RS>
+__device__ __forceinline__ u32x4 tr_ops(const uint16_t *base, int t32, int c0) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, s = lane & 15;
+    const uint16_t *p = base + (t32 + 4 * g4 + (s >> 2)) * RS + c0 + 4 * ((s & 3) ^ g4);
+    const v4i16_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_v *)p);
+    const v4i16_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_v *)(p + 16 * RS));
+    const u32x2 ua = __builtin_bit_cast(u32x2, x0), ub = __builtin_bit_cast(u32x2, x1);
+    return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// acc += A B with both operands in three parts, the six products down to
+// the second parts' product (the rest is below 2^-24 of the leading one)
+__device__ __forceinline__ f32x4 mfma_split6(const u32x4 (&x)[3], const u32x4 (&y)[3], f32x4 acc) {
+    acc = mfma16x16x32(x[1], y[1], acc);
+    acc = mfma16x16x32(x[2], y[0], acc);
+    acc = mfma16x16x32(x[0], y[2], acc);
+    acc = mfma16x16x32(x[1], y[0], acc);
+    acc = mfma16x16x32(x[0], y[1], acc);
+    return mfma16x16x32(x[0], y[0], acc);
+}
+
+// the value an element of a three-part array holds (the parts' exact sum)
+__device__ __forceinline__ float part_sum(const uint16_t *p0, size_t stride) {
+    return (bf2f(p0[2 * stride]) + bf2f(p0[stride])) + bf2f(p0[0]);
+}
+
+// four values (rows of one column) as three parts, into [col][row0 .. row0+3]
+// of three [.][rs] arrays spaced by stride elements
+__device__ __forceinline__ void put_split4(uint16_t *dst, size_t stride, const float *v) {
+    uint32_t p01[3], p23[3];
+    split3(v[0], v[1], p01);
+    split3(v[2], v[3], p23);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) *(u32x2 *)(dst + q * stride) = u32x2{p01[q], p23[q]};
+}
+
+// sum over the 16 lanes of a lane group (the same value in all of them)
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+constexpr int kMxThreads = 1024;   // 16 waves: one per 16 x 16 tile of the block's square
+
+struct GradMxSmem {
+    static constexpr int P = 64, N = 128;
+    static constexpr int RN = N + 16, RP = P + 16, RQ = kQ + 16;   // bf16 row strides
+    uint16_t bx[kQ * RN];      // B rows [t][n]
+    uint16_t cx[kQ * RN];      // C rows [t][n]
+    uint16_t xx[kQ * RP];      // x rows [t][p]
+    uint16_t y3[3][kQ * RP];   // dy rows [t][p], three parts
+    union {
+        struct {
+            uint16_t mt[3][kQ * RQ];   // M^T [j][i], three parts
+            uint16_t gt[3][kQ * RQ];   // (L o dM)^T [j][i], three parts
+        } q;
+        uint16_t ht[3][P * RN];        // Hp^T, then dHe^T: [p][n], three parts
+    } u;
+    float colz[4][kQ];   // sums of the strictly lower Z over each tile row of i, per column
+    float rowz[4][kQ];   // ... over each tile column of j, per row
+    float dsop[4][kQ];   // per position, sums over each 16 p of (C^T Hp) o dy
+    float dssp[4][kQ];   // ... of x o (B^T dHe)
+    float xdp[4][kQ];    // ... of x o dxd
+    float xyr[kQ];       // per position, x . dy
+    double sv[kQ];
+    float dtv[kQ], es[kQ], wv[kQ];
+    float red[16];
+};
+
+template <bool HSUM>
+__device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const int c, const int h,
+                                        const int dir, const int b, const bool first,
+                                        f32x4 (&accb)[2], f32x4 (&accc)[2]) {
+    using Sm = GradMxSmem;
+    constexpr int P = Sm::P, N = Sm::N, RN = Sm::RN, RP = Sm::RP, RQ = Sm::RQ;
+    constexpr size_t YS = (size_t)kQ * RP, QS = (size_t)kQ * RQ, HS = (size_t)P * RN;   // part strides
+    const bool rev = dir == 1;
+    const DirPtrs d = rev ? a.bwd : a.fwd;
+    const GradPtrs gr = rev ? a.gbwd : a.gfwd;
+    const int g = h / (a.H / a.G);
+    const int k0 = c * kQ;
+    const int len = min(kQ, a.L - k0);
+    const size_t rowt = (size_t)b * a.L;
+    const int tid = lane_tid<HSUM>(), wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
+    const size_t so = (unit * a.nc + c) * (size_t)(N * P);
+    const size_t sgn = (size_t)a.G * N, hp = (size_t)a.H * P;
+
+    // ---- loads, all issued before any is used (rows past the block's end
+    // re-read its last row and are zeroed when staged): B and C rows (two
+    // 4-vectors per thread), x and dy rows (one), dt (wave 0), and Hp, dHe
+    // (two 4-vectors each, held until their phases)
+    const bool bc = !HSUM || first;
+    u32x2 rbv[2], rcv[2], rxv;
+    f32x4 ryv, fhp[2], fdh[2];
+    uint16_t dtr = 0;
+    if (bc) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e4 = tid + k * kMxThreads, r = min(e4 >> 5, len - 1), cc = (e4 & 31) * 4;
+            const size_t o = (rowt + tok_of(k0 + r, a.L, rev)) * sgn + (size_t)g * N + cc;
+            rbv[k] = *(const u32x2 *)((const uint16_t *)d.B + o);
+            rcv[k] = *(const u32x2 *)((const uint16_t *)d.C + o);
+        }
+    }
+    {
+        const int r = min(tid >> 4, len - 1), cc = (tid & 15) * 4;
+        const size_t o = (rowt + tok_of(k0 + r, a.L, rev)) * hp + (size_t)h * P + cc;
+        rxv = *(const u32x2 *)((const uint16_t *)d.x + o);
+        ryv = *(const f32x4 *)(a.dy + o);
+    }
+    if (tid < kQ) dtr = ((const uint16_t *)d.dt)[(rowt + tok_of(k0 + min(tid, len - 1), a.L, rev)) * a.H + h];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        fhp[k] = *(const f32x4 *)(a.S + so + 4 * (tid + k * kMxThreads));
+        fdh[k] = *(const f32x4 *)(a.R + so + 4 * (tid + k * kMxThreads));
+    }
+
+    // ---- the block's running sums of dt A (fp64), weights; the rows into LDS
+    if (tid < kQ) {
+        const float dtf = tid < len ? bf2f(dtr) : 0.f;
+        const double s = wave_scan((double)dtf * (double)d.A[h], tid);
+        const double send = __shfl(s, len - 1);
+        sm.sv[tid] = s;
+        sm.dtv[tid] = dtf;
+        sm.es[tid] = tid < len ? expf((float)s) : 0.f;
+        sm.wv[tid] = tid < len ? expf((float)(send - s)) : 0.f;
+    }
+    if (bc) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e4 = tid + k * kMxThreads, r = e4 >> 5, cc = (e4 & 31) * 4;
+            const bool ok = r < len;
+            *(u32x2 *)&sm.bx[swz<RN>(r, cc)] = u32x2{ok ? rbv[k][0] : 0u, ok ? rbv[k][1] : 0u};
+            *(u32x2 *)&sm.cx[swz<RN>(r, cc)] = u32x2{ok ? rcv[k][0] : 0u, ok ? rcv[k][1] : 0u};
+        }
+    }
+    {
+        const int r = tid >> 4, cc = (tid & 15) * 4;
+        const bool ok = r < len;
+        const u32x2 xv = u32x2{ok ? rxv[0] : 0u, ok ? rxv[1] : 0u};
+        *(u32x2 *)&sm.xx[swz<RP>(r, cc)] = xv;
+        float yv[4] = {ok ? ryv[0] : 0.f, ok ? ryv[1] : 0.f, ok ? ryv[2] : 0.f, ok ? ryv[3] : 0.f};
+        put_split4(&sm.y3[0][swz<RP>(r, cc)], YS, yv);
+        // x . dy of the position (the thread's four p, then the row's 16 lanes)
+        float xy = bf_low(xv[0]) * yv[0];
+        xy = fmaf(bf_high(xv[0]), yv[1], xy);
+        xy = fmaf(bf_low(xv[1]), yv[2], xy);
+        xy = fmaf(bf_high(xv[1]), yv[3], xy);
+        xy = sum16(xy);
+        if ((tid & 15) == 0) sm.xyr[r] = xy;
+    }
+    __syncthreads();
+
+    // ---- the block's quadratic form, one 16 x 16 tile (it, jt) per wave:
+    // G = C B^T, dM = dy x^T dt_j; M = L o G, L o dM into LDS (transposed,
+    // three parts; zeros above the diagonal), and the strictly lower Z = dM o
+    // M summed over the tile's rows and columns
+    const int it = wave >> 2, jt = wave & 3;
+    {
+        float M[4] = {0.f, 0.f, 0.f, 0.f}, dG[4] = {0.f, 0.f, 0.f, 0.f}, zs[4] = {0.f, 0.f, 0.f, 0.f};
+        const int j = jt * 16 + l16;
+        if (jt <= it) {
+            f32x4 G = zero4(), D = zero4();
+#pragma unroll
+            for (int kc = 0; kc < N / 32; ++kc)
+                G = mfma16x16x32(dir_op<RN>(sm.cx, it * 16, 32 * kc), dir_op<RN>(sm.bx, jt * 16, 32 * kc), G);
+#pragma unroll
+            for (int kc = 0; kc < P / 32; ++kc) {
+                const u32x4 xo = dir_op<RP>(sm.xx, jt * 16, 32 * kc);
+#pragma unroll
+                for (int q = 2; q >= 0; --q) D = mfma16x16x32(dir_op<RP>(sm.y3[q], it * 16, 32 * kc), xo, D);
+            }
+            const float dtj = sm.dtv[j];
+            const double svj = sm.sv[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = it * 16 + 4 * g4 + r;
+                if (j <= i && i < len) {
+                    const float dm = D[r] * dtj;
+                    const float Lij = expf((float)(sm.sv[i] - svj));
+                    M[r] = Lij * G[r];
+                    dG[r] = Lij * dm;
+                    zs[r] = j < i ? dm * M[r] : 0.f;
+                }
+            }
+        }
+        put_split4(&sm.u.q.mt[0][swz<RQ>(j, it * 16 + 4 * g4)], QS, M);
+        put_split4(&sm.u.q.gt[0][swz<RQ>(j, it * 16 + 4 * g4)], QS, dG);
+        float cz = (zs[0] + zs[1]) + (zs[2] + zs[3]);
+        cz += __shfl_xor(cz, 16);
+        cz += __shfl_xor(cz, 32);
+        if (g4 == 0) sm.colz[it][j] = cz;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float rz = sum16(zs[r]);
+            if (l16 == 0) sm.rowz[jt][it * 16 + 4 * g4 + r] = rz;
+        }
+    }
+    __syncthreads();
+
+    // ---- the quadratic form's gradients: dxd (tile (jt, pt) = (it, jt) of
+    // the wave), dC and dB (two tiles each: t = wave, wave + 16 of 4 x 8)
+    f32x4 dxd = zero4(), dcv[2], dbv[2];
+    {
+        const int jr = it, pt = jt;   // dxd_j = sum_{i >= j} M_ij dy_i
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            if (kc == 0 && jr > 1) continue;
+            u32x4 x3[3], y3[3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                x3[q] = dir_op<RQ>(sm.u.q.mt[q], jr * 16, 32 * kc);
+                y3[q] = tr_ops<RP>(sm.y3[q], 32 * kc, pt * 16);
+            }
+            dxd = mfma_split6(x3, y3, dxd);
+        }
+    }
+    // (the wave's two tiles t = wave, wave + 16 of the 4 x 8 (row, n) tiles
+    // share their columns n: rows rt0 = wave / 8 and rt0 + 2)
+    const int rt0 = wave >> 3, ntw = wave & 7;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        dcv[u] = zero4();
+        dbv[u] = zero4();
+    }
+    // dC_i = sum_{j <= i} (L o dM)_ij B_j (j chunk 1 only for rows 32 ..)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const u32x4 bo = tr_ops<RN>(sm.bx, 32 * kc, ntw * 16);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (kc == 1 && u == 0) continue;
+#pragma unroll
+            for (int q = 2; q >= 0; --q)
+                dcv[u] = mfma16x16x32(tr_ops<RQ>(sm.u.q.gt[q], 32 * kc, (rt0 + 2 * u) * 16), bo, dcv[u]);
+        }
+    }
+    // dB_j = sum_{i >= j} (L o dM)_ij C_i (i chunk 0 only for rows .. 31)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const u32x4 co = tr_ops<RN>(sm.cx, 32 * kc, ntw * 16);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (kc == 0 && u == 1) continue;
+#pragma unroll
+            for (int q = 2; q >= 0; --q)
+                dbv[u] = mfma16x16x32(dir_op<RQ>(sm.u.q.gt[q], (rt0 + 2 * u) * 16, 32 * kc), co, dbv[u]);
+        }
+    }
+    __syncthreads();
+
+    // ---- terms of the entering state Hp (staged transposed, three parts)
+    float hd = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int e4 = tid + k * kMxThreads, tile = e4 >> 6, ln = e4 & 63;
+        const int n0 = (tile >> 2) * 16 + 4 * (ln >> 4), p = (tile & 3) * 16 + (ln & 15);
+        const float v[4] = {fhp[k][0], fhp[k][1], fhp[k][2], fhp[k][3]};
+        put_split4(&sm.u.ht[0][swz<RN>(p, n0)], HS, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hd = fmaf(fhp[k][i], fdh[k][i], hd);
+    }
+    hd = wave_sum(hd);
+    if (lane == 0) sm.red[wave] = hd;
+    __syncthreads();
+    {
+        // dC_i += e^{s_i} Hp dy_i (Hp's operand shared by the two tiles)
+        f32x4 tmp[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int kc = 0; kc < P / 32; ++kc) {
+            u32x4 h3[3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) h3[q] = tr_ops<RN>(sm.u.ht[q], 32 * kc, ntw * 16);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                u32x4 x3[3];
+#pragma unroll
+                for (int q = 0; q < 3; ++q) x3[q] = dir_op<RP>(sm.y3[q], (rt0 + 2 * u) * 16, 32 * kc);
+                tmp[u] = mfma_split6(x3, h3, tmp[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dcv[u][r] = fmaf(sm.es[(rt0 + 2 * u) * 16 + 4 * g4 + r], tmp[u][r], dcv[u][r]);
+    }
+    {
+        // (C_i^T Hp)[p] dy_i[p], summed over p: tile (i, p) = (it, jt)
+        f32x4 ch = zero4();
+#pragma unroll
+        for (int kc = 0; kc < N / 32; ++kc) {
+            const u32x4 co = dir_op<RN>(sm.cx, it * 16, 32 * kc);
+#pragma unroll
+            for (int q = 2; q >= 0; --q) ch = mfma16x16x32(co, dir_op<RN>(sm.u.ht[q], jt * 16, 32 * kc), ch);
+        }
+        const int p = jt * 16 + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = it * 16 + 4 * g4 + r;
+            const float v = sum16(ch[r] * part_sum(&sm.y3[0][swz<RP>(i, p)], YS));
+            if (l16 == 0) sm.dsop[jt][i] = v;
+        }
+    }
+    __syncthreads();
+
+    // ---- terms of the leaving-state gradient dHe (over Hp in LDS)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int e4 = tid + k * kMxThreads, tile = e4 >> 6, ln = e4 & 63;
+        const int n0 = (tile >> 2) * 16 + 4 * (ln >> 4), p = (tile & 3) * 16 + (ln & 15);
+        const float v[4] = {fdh[k][0], fdh[k][1], fdh[k][2], fdh[k][3]};
+        put_split4(&sm.u.ht[0][swz<RN>(p, n0)], HS, v);
+    }
+    __syncthreads();
+    {
+        // (B_j^T dHe)[p]: dxd_j += e^{s_end - s_j} B_j^T dHe; x_j . (B_j^T dHe)
+        f32x4 bdh = zero4();
+#pragma unroll
+        for (int kc = 0; kc < N / 32; ++kc) {
+            const u32x4 bo = dir_op<RN>(sm.bx, it * 16, 32 * kc);
+#pragma unroll
+            for (int q = 2; q >= 0; --q) bdh = mfma16x16x32(bo, dir_op<RN>(sm.u.ht[q], jt * 16, 32 * kc), bdh);
+        }
+        const int p = jt * 16 + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = it * 16 + 4 * g4 + r;
+            dxd[r] = fmaf(sm.wv[j], bdh[r], dxd[r]);
+            const float v = sum16(bf2f(sm.xx[swz<RP>(j, p)]) * bdh[r]);
+            if (l16 == 0) sm.dssp[jt][j] = v;
+        }
+    }
+    {
+        // dB_j += e^{s_end - s_j} dt_j dHe x_j (dHe's operand shared)
+        f32x4 tmp[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int kc = 0; kc < P / 32; ++kc) {
+            u32x4 h3[3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) h3[q] = tr_ops<RN>(sm.u.ht[q], 32 * kc, ntw * 16);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const u32x4 xo = dir_op<RP>(sm.xx, (rt0 + 2 * u) * 16, 32 * kc);
+#pragma unroll
+                for (int q = 2; q >= 0; --q) tmp[u] = mfma16x16x32(xo, h3[q], tmp[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = (rt0 + 2 * u) * 16 + 4 * g4 + r;
+                dbv[u][r] = fmaf(sm.wv[j] * sm.dtv[j], tmp[u][r], dbv[u][r]);
+            }
+    }
+
+    // ---- dB, dC: summed over the heads in registers, or per head into the
+    // workspace; x . dxd per position; dx
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (HSUM) {
+            accb[u] = first ? dbv[u] : accb[u] + dbv[u];
+            accc[u] = first ? dcv[u] : accc[u] + dcv[u];
+        } else {
+            const int rt = rt0 + 2 * u, nt = ntw;
+            const size_t pb = unit * (size_t)a.L * N;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rt * 16 + 4 * g4 + r;
+                if (row < len) {
+                    const size_t o = pb + (size_t)tok_of(k0 + row, a.L, rev) * N + nt * 16 + l16;
+                    a.dBp[o] = dbv[u][r];
+                    a.dCp[o] = dcv[u][r];
+                }
+            }
+        }
+    }
+    const float A = d.A[h];
+    const float Dh = d.D ? d.D[h] : 0.f;
+    {
+        const int p = jt * 16 + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = it * 16 + 4 * g4 + r;
+            const float v = sum16(bf2f(sm.xx[swz<RP>(j, p)]) * dxd[r]);
+            if (l16 == 0) sm.xdp[jt][j] = v;
+            if (j < len)
+                gr.dx[((rowt + tok_of(k0 + j, a.L, rev)) * a.H + h) * P + p] =
+                    fmaf(Dh, part_sum(&sm.y3[0][swz<RP>(j, p)], YS), sm.dtv[j] * dxd[r]);
+        }
+    }
+    __syncthreads();
+
+    // ---- da_k = sum_{i >= k} ds_i as in grad_block; ddt, and the block's
+    // shares of dA and dD. One lane per position, fp64 scans.
+    if (tid < kQ) {
+        const int r = tid;
+        const float dsi = ((sm.colz[0][r] + sm.colz[1][r]) + (sm.colz[2][r] + sm.colz[3][r])) -
+                          ((sm.rowz[0][r] + sm.rowz[1][r]) + (sm.rowz[2][r] + sm.rowz[3][r]));
+        const float dso = r < len ? sm.es[r] * ((sm.dsop[0][r] + sm.dsop[1][r]) + (sm.dsop[2][r] + sm.dsop[3][r]))
+                                  : 0.f;
+        const float dss = -sm.wv[r] * sm.dtv[r] * ((sm.dssp[0][r] + sm.dssp[1][r]) + (sm.dssp[2][r] + sm.dssp[3][r]));
+        const float xd = (sm.xdp[0][r] + sm.xdp[1][r]) + (sm.xdp[2][r] + sm.xdp[3][r]);
+        float hp_dhe = 0.f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) hp_dhe += sm.red[w];
+        const double q = dsi;
+        const double rect = wave_scan(q, r) - q;
+        const double so_rev = wave_scan((double)__shfl(dso, kQ - 1 - r), r);   // suffix sums, reversed
+        const double so_suf = __shfl(so_rev, kQ - 1 - r);
+        const double ss = dss;
+        const double ss_pre = wave_scan(ss, r) - ss;
+        const double da = r < len ? rect + so_suf + (double)sm.es[len - 1] * hp_dhe - ss_pre : 0.0;
+        if (r < len) gr.ddt[(rowt + tok_of(k0 + r, a.L, rev)) * a.H + h] = xd + A * (float)da;
+        const float sa = wave_sum(r < len ? sm.dtv[r] * (float)da : 0.f);
+        const float sd = wave_sum(sm.xyr[r]);
+        if (r == 0) {
+            a.dDp[unit * a.nc + c] = sd;
+            a.dAp[unit * a.nc + c] = sa;
+        }
+    }
+}
+
+// One workgroup per (block, head, row and stream); dB, dC per head.
+__global__ __launch_bounds__(kMxThreads) void k_bwd_grad_mx(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) GradMxSmem sm;
+    const int dir = (int)(blockIdx.z % (unsigned)a.ndir), b = (int)(blockIdx.z / (unsigned)a.ndir);
+    f32x4 accb[2], accc[2];
+    grad_mx<false>(a, sm, blockIdx.x, blockIdx.y, dir, b, false, accb, accc);
+}
+
+// One workgroup per (block, group, row and stream), walking the group's
+// heads in order; dB, dC summed over them in registers.
+__global__ __launch_bounds__(kMxThreads) void k_bwd_grad_heads_mx(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) GradMxSmem sm;
+    constexpr int N = GradMxSmem::N;
+    const int dir = (int)(blockIdx.z % (unsigned)a.ndir), b = (int)(blockIdx.z / (unsigned)a.ndir);
+    const int hg = a.H / a.G, g = blockIdx.y, h0 = g * hg, c = blockIdx.x;
+    f32x4 accb[2], accc[2];
+    for (int k = 0; k < hg; ++k) {
+        if (k) __syncthreads();   // the previous head's last phase reads the LDS rows
+        grad_mx<true>(a, sm, c, h0 + k, dir, b, k == 0, accb, accc);
+    }
+    const bool rev = dir == 1;
+    const GradPtrs gr = rev ? a.gbwd : a.gfwd;
+    const int k0 = c * kQ, len = min(kQ, a.L - k0);
+    const size_t rowt = (size_t)b * a.L;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int t = wave + 16 * u, rt = t >> 3, nt = t & 7;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = rt * 16 + 4 * g4 + r;
+            if (row < len) {
+                const size_t o = ((rowt + tok_of(k0 + row, a.L, rev)) * a.G + g) * N + nt * 16 + l16;
+                gr.dB[o] = accb[u][r];
+                gr.dC[o] = accc[u][r];
+            }
+        }
+    }
+}
+
 // dB, dC of one stream: sums over the heads of each group, in head order.
 __global__ __launch_bounds__(256) void k_bwd_sum_bc(BwdArgs a, int N, size_t total) {
     const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1036,11 +1540,20 @@ hipError_t launch_pn(BwdArgs &a, hipStream_t s) {
             const dim3 pgrid((N * P + 255) / 256, a.H, a.batch * a.ndir);
             BM_LAUNCH("bwd_pass", k_bwd_pass, pgrid, dim3(256), 0, s, a, N * P);
         }
+        // bf16 inputs at headdim 64, d_state 128: the gradient block on the
+        // bf16 matrix cores
+        constexpr bool MX = sizeof(T) == 2 && P == GradMxSmem::P && N == GradMxSmem::N;
         if (a.head_loop) {
             const dim3 ggrid(a.nc, a.G, a.batch * a.ndir);
-            BM_LAUNCH("bwd_grad", (k_bwd_grad_heads<T, P, N>), ggrid, dim3(kGradThreads), 0, s, a);
+            if (MX)
+                BM_LAUNCH("bwd_grad", k_bwd_grad_heads_mx, ggrid, dim3(kMxThreads), 0, s, a);
+            else
+                BM_LAUNCH("bwd_grad", (k_bwd_grad_heads<T, P, N>), ggrid, dim3(kGradThreads), 0, s, a);
         } else {
-            BM_LAUNCH("bwd_grad", (k_bwd_grad<T, P, N>), grid, dim3(kGradThreads), 0, s, a);
+            if (MX)
+                BM_LAUNCH("bwd_grad", k_bwd_grad_mx, grid, dim3(kMxThreads), 0, s, a);
+            else
+                BM_LAUNCH("bwd_grad", (k_bwd_grad<T, P, N>), grid, dim3(kGradThreads), 0, s, a);
             const size_t total = (size_t)a.batch * a.L * a.G * N;
             const dim3 sgrid((unsigned)((total + 255) / 256), a.ndir);
             BM_LAUNCH("bwd_sum_bc", k_bwd_sum_bc, sgrid, dim3(256), 0, s, a, N, total);
