@@ -1058,11 +1058,54 @@ __device__ __forceinline__ void put_split4(uint16_t *dst, size_t stride, const f
     for (int q = 0; q < 3; ++q) *(u32x2 *)(dst + q * stride) = u32x2{p01[q], p23[q]};
 }
 
-// sum over the 16 lanes of a lane group (the same value in all of them)
+// Cross-lane sums by DPP (data-parallel primitives: a VALU operand read from
+// another lane of the same 16-lane row, row_shr:n = 0x110 + n, or the last
+// lane of a row broadcast to the next rows, row_bcast:15 = 0x142 and
+// row_bcast:31 = 0x143), instead of LDS permutes. Lanes whose source falls
+// outside the row, or whose row is masked off, add 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, true));
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long u = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)u, CTRL, ROWS, 0xf, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, ROWS, 0xf, true);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Sum over each 16-lane row of the wave, in the row's last lane (lane % 16
+// == 15; the other lanes hold partial sums).
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+    v += dpp_f<0x111>(v);
+    v += dpp_f<0x112>(v);
+    v += dpp_f<0x114>(v);
+    v += dpp_f<0x118>(v);
     return v;
+}
+
+// Inclusive running sum over the 64 lanes (lane order), fp64: within rows,
+// then each row adds the totals of the rows before it.
+__device__ __forceinline__ double wave_scan_dpp(double v) {
+    v += dpp_d<0x111>(v);
+    v += dpp_d<0x112>(v);
+    v += dpp_d<0x114>(v);
+    v += dpp_d<0x118>(v);
+    v += dpp_d<0x142, 0xa>(v);
+    v += dpp_d<0x143, 0xc>(v);
+    return v;
+}
+
+// Sum over the wave (in every lane).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f<0x111>(v);
+    v += dpp_f<0x112>(v);
+    v += dpp_f<0x114>(v);
+    v += dpp_f<0x118>(v);
+    v += dpp_f<0x142, 0xa>(v);
+    v += dpp_f<0x143, 0xc>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 constexpr int kMxThreads = 1024;   // 16 waves: one per 16 x 16 tile of the block's square
@@ -1144,8 +1187,11 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
     // ---- the block's running sums of dt A (fp64), weights; the rows into LDS
     if (tid < kQ) {
         const float dtf = tid < len ? bf2f(dtr) : 0.f;
-        const double s = wave_scan((double)dtf * (double)d.A[h], tid);
-        const double send = __shfl(s, len - 1);
+        const double s = wave_scan_dpp((double)dtf * (double)d.A[h]);
+        const long long su = __double_as_longlong(s);
+        const double send = __longlong_as_double(
+            ((long long)__builtin_amdgcn_readlane((int)(su >> 32), len - 1) << 32) |
+            (unsigned)__builtin_amdgcn_readlane((int)su, len - 1));
         sm.sv[tid] = s;
         sm.dtv[tid] = dtf;
         sm.es[tid] = tid < len ? expf((float)s) : 0.f;
@@ -1173,7 +1219,7 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
         xy = fmaf(bf_low(xv[1]), yv[2], xy);
         xy = fmaf(bf_high(xv[1]), yv[3], xy);
         xy = sum16(xy);
-        if ((tid & 15) == 0) sm.xyr[r] = xy;
+        if ((tid & 15) == 15) sm.xyr[r] = xy;
     }
     __syncthreads();
 
@@ -1219,7 +1265,7 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float rz = sum16(zs[r]);
-            if (l16 == 0) sm.rowz[jt][it * 16 + 4 * g4 + r] = rz;
+            if (l16 == 15) sm.rowz[jt][it * 16 + 4 * g4 + r] = rz;
         }
     }
     __syncthreads();
@@ -1286,7 +1332,7 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
 #pragma unroll
         for (int i = 0; i < 4; ++i) hd = fmaf(fhp[k][i], fdh[k][i], hd);
     }
-    hd = wave_sum(hd);
+    hd = wave_sum_dpp(hd);
     if (lane == 0) sm.red[wave] = hd;
     __syncthreads();
     {
@@ -1325,7 +1371,7 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
         for (int r = 0; r < 4; ++r) {
             const int i = it * 16 + 4 * g4 + r;
             const float v = sum16(ch[r] * part_sum(&sm.y3[0][swz<RP>(i, p)], YS));
-            if (l16 == 0) sm.dsop[jt][i] = v;
+            if (l16 == 15) sm.dsop[jt][i] = v;
         }
     }
     __syncthreads();
@@ -1354,7 +1400,7 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
             const int j = it * 16 + 4 * g4 + r;
             dxd[r] = fmaf(sm.wv[j], bdh[r], dxd[r]);
             const float v = sum16(bf2f(sm.xx[swz<RP>(j, p)]) * bdh[r]);
-            if (l16 == 0) sm.dssp[jt][j] = v;
+            if (l16 == 15) sm.dssp[jt][j] = v;
         }
     }
     {
@@ -1410,7 +1456,7 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
         for (int r = 0; r < 4; ++r) {
             const int j = it * 16 + 4 * g4 + r;
             const float v = sum16(bf2f(sm.xx[swz<RP>(j, p)]) * dxd[r]);
-            if (l16 == 0) sm.xdp[jt][j] = v;
+            if (l16 == 15) sm.xdp[jt][j] = v;
             if (j < len)
                 gr.dx[((rowt + tok_of(k0 + j, a.L, rev)) * a.H + h) * P + p] =
                     fmaf(Dh, part_sum(&sm.y3[0][swz<RP>(j, p)], YS), sm.dtv[j] * dxd[r]);
@@ -1432,15 +1478,15 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
 #pragma unroll
         for (int w = 0; w < 16; ++w) hp_dhe += sm.red[w];
         const double q = dsi;
-        const double rect = wave_scan(q, r) - q;
-        const double so_rev = wave_scan((double)__shfl(dso, kQ - 1 - r), r);   // suffix sums, reversed
+        const double rect = wave_scan_dpp(q) - q;
+        const double so_rev = wave_scan_dpp((double)__shfl(dso, kQ - 1 - r));   // suffix sums, reversed
         const double so_suf = __shfl(so_rev, kQ - 1 - r);
         const double ss = dss;
-        const double ss_pre = wave_scan(ss, r) - ss;
+        const double ss_pre = wave_scan_dpp(ss) - ss;
         const double da = r < len ? rect + so_suf + (double)sm.es[len - 1] * hp_dhe - ss_pre : 0.0;
         if (r < len) gr.ddt[(rowt + tok_of(k0 + r, a.L, rev)) * a.H + h] = xd + A * (float)da;
-        const float sa = wave_sum(r < len ? sm.dtv[r] * (float)da : 0.f);
-        const float sd = wave_sum(sm.xyr[r]);
+        const float sa = wave_sum_dpp(r < len ? sm.dtv[r] * (float)da : 0.f);
+        const float sd = wave_sum_dpp(sm.xyr[r]);
         if (r == 0) {
             a.dDp[unit * a.nc + c] = sd;
             a.dAp[unit * a.nc + c] = sa;
