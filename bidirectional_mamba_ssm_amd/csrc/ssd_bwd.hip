@@ -449,7 +449,7 @@ __device__ __forceinline__ void chain_sweep(const BwdArgs &a, ChainSmem<P, N, si
     const DirPtrs d = rev ? a.bwd : a.fwd;
     const int g = h / (a.H / a.G);
     const size_t rowt = (size_t)b * a.L;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const size_t unit = ((size_t)b * a.ndir + dir) * a.H + h;
     const size_t sgn = (size_t)a.G * N, hp = (size_t)a.H * P;
     const void *asrc = SW == 0 ? d.B : d.C;
