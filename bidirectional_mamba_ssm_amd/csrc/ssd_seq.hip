@@ -1,8 +1,9 @@
 // Token-sequential bidirectional SSD scan.
 //
-// One workgroup per (sequence or segment, head), one lane per headdim column
-// p; lane p keeps column p of the d_state x headdim state in registers and
-// applies the Mamba-2 recurrence one token at a time:
+// One workgroup per (sequence or segment, head), LPP lanes per headdim column
+// p (LPP = 4 for headdim <= 16, 2 for <= 32, else 1, so that a wave's lanes
+// are used); the LPP lanes of column p keep its d_state entries in registers,
+// N / LPP each, and apply the Mamba-2 recurrence one token at a time:
 //   h <- exp(dt_t*A_h) h + dt_t B_t x_t[p],   y_t[p] = C_t . h + D_h x_t[p]
 // forward over the sequence, then backward over it with the reverse stream's
 // parameters: the flip of the DiffuMamba blog's bidirectional block ("network
@@ -50,20 +51,41 @@ struct SeqSmem {
     float x[kSeqTile][kMaxP];
     float y[kSeqTile][kMaxP];
     float dt[kSeqTile];
+    float at[kSeqTile];    // dt * A
+    float dec[kSeqTile];   // exp(dt * A)
 };
+
+// Lanes per headdim column for a headdim of P.
+inline int seq_lpp(int P) { return P <= 16 ? 4 : P <= 32 ? 2 : 1; }
+
+// Sum over the LPP consecutive lanes of a column, in its last lane (DPP row
+// shifts within a 16-lane row; LPP divides 16, so a column's lanes share a
+// row; the other lanes hold partial sums).
+template <int LPP>
+__device__ __forceinline__ float col_sum(float v) {
+    if (LPP >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    if (LPP >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    return v;
+}
 
 // Walks tokens [t0, t1) of one direction (upwards for d == 0, downwards for
 // d == 1) from the state in st and returns the sum of dt*A over them.
 // MODE 0: state only; MODE 1: writes y; MODE 2: adds into y. y goes through
 // LDS a tile at a time (the old values of a MODE 2 tile are read with the
 // inputs), so no token waits on a global load.
-template <typename T, int N, int MODE>
+template <typename T, int N, int LPP, int MODE>
 __device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, int h, int g,
-                      int t0, int t1, float (&st)[N]) {
+                      int t0, int t1, float (&st)[N / LPP]) {
+    constexpr int NL = N / LPP;            // state entries per lane
+    constexpr int NA = NL >= 16 ? 4 : NL >= 8 ? 2 : 1;   // independent partial sums of y
     // the output this direction writes (or adds into)
     float *Y = (a.y2 && d == 0) ? a.y2 : a.y;
-    const int p = threadIdx.x;
     const int H = a.H, P = a.P, G = a.G;
+    // column p, entries q NL .. q NL + NL - 1 (lanes past the last column
+    // compute on column P - 1 and write nothing)
+    const int p = (int)threadIdx.x / LPP, q = (int)threadIdx.x % LPP;
+    const int pc = min(p, P - 1);
+    const bool own = p < P && q == LPP - 1;
     const DirPtrs &dp = a.dir[d];
     const T *X = (const T *)dp.x;
     const T *DT = (const T *)dp.dt;
@@ -90,29 +112,40 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, i
             sm.x[s][pp] = Elem<T>::load(X, o);
             if (MODE == 2) sm.y[s][pp] = Y[o];
         }
+        // the step sizes and decays of the tile, in parallel (off the
+        // token-to-token chain)
         for (int i = threadIdx.x; i < nsteps; i += blockDim.x) {
             const int t = d == 0 ? t0 + base + i : t1 - 1 - base - i;
             float dtv = Elem<T>::load(DT, (row_tok + t) * H + h);
             if (a.dt_softplus) dtv = softplus_dt(dtv + (a.dt_bias[d] ? a.dt_bias[d][h] : 0.f));
             sm.dt[i] = dtv;
+            const float at = dtv * Ah;
+            sm.at[i] = at;
+            sm.dec[i] = expf(at);
         }
         __syncthreads();
-        if (p < P) {
-            for (int s = 0; s < nsteps; ++s) {
-                const float dtt = sm.dt[s];
-                const float at = dtt * Ah;
-                asum += at;
-                const float decay = expf(at);
-                const float xv = sm.x[s][p];
-                const float dx = dtt * xv;
-                float acc = 0.f;
+        for (int s = 0; s < nsteps; ++s) {
+            const float decay = sm.dec[s];
+            asum += sm.at[s];
+            const float xv = sm.x[s][pc];
+            const float dx = sm.dt[s] * xv;
+            float acc[NA];
 #pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    st[n] = fmaf(decay, st[n], dx * sm.B[s][n]);
-                    if (MODE != 0) acc = fmaf(sm.C[s][n], st[n], acc);
+            for (int k = 0; k < NA; ++k) acc[k] = 0.f;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                st[i] = fmaf(decay, st[i], dx * sm.B[s][q * NL + i]);
+                if (MODE != 0) acc[i % NA] = fmaf(sm.C[s][q * NL + i], st[i], acc[i % NA]);
+            }
+            if (MODE != 0) {
+                float yv = acc[0];
+#pragma unroll
+                for (int k = 1; k < NA; ++k) yv += acc[k];
+                yv = col_sum<LPP>(yv);
+                if (own) {
+                    if (MODE == 1) sm.y[s][p] = fmaf(Dh, xv, yv);
+                    if (MODE == 2) sm.y[s][p] += fmaf(Dh, xv, yv);
                 }
-                if (MODE == 1) sm.y[s][p] = fmaf(Dh, xv, acc);
-                if (MODE == 2) sm.y[s][p] += fmaf(Dh, xv, acc);
             }
         }
         if (MODE != 0) {
@@ -127,37 +160,46 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, i
     return asum;
 }
 
+// The lane's state entries: column p, entries q NL .. q NL + NL - 1 of the
+// [P][N] state at base (lanes past the last column hold zeros, write nothing).
+template <int N, int LPP>
+__device__ __forceinline__ void state_load(float (&st)[N / LPP], const float *base, int P) {
+    constexpr int NL = N / LPP;
+    const int p = (int)threadIdx.x / LPP, q = (int)threadIdx.x % LPP;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) st[i] = (base && p < P) ? base[(size_t)p * N + q * NL + i] : 0.f;
+}
+template <int N, int LPP>
+__device__ __forceinline__ void state_store(const float (&st)[N / LPP], float *base, int P) {
+    constexpr int NL = N / LPP;
+    const int p = (int)threadIdx.x / LPP, q = (int)threadIdx.x % LPP;
+    if (p < P) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) base[(size_t)p * N + q * NL + i] = st[i];
+    }
+}
+
 // Whole rows or packed sequences: one workgroup per (unit, head).
-template <typename T, int N>
+template <typename T, int N, int LPP>
 __global__ void __launch_bounds__(kMaxP) k_scan_seq(const SeqArgs a) {
     __shared__ SeqSmem<N> sm;
     const int unit = blockIdx.x;
     const int h = blockIdx.y;
-    const int p = threadIdx.x;
     const int g = h / (a.H / a.G);
     int row, t0, t1;
     if (a.cu) { row = 0; t0 = a.cu[unit]; t1 = a.cu[unit + 1]; }
     else      { row = unit; t0 = 0; t1 = a.L; }
     const size_t row_tok = (size_t)row * a.L;
-    const size_t state_off = (((size_t)unit * a.H + h) * a.P + p) * N;
-    float st[N];
-    if (a.init_state && p < a.P) {
-#pragma unroll
-        for (int n = 0; n < N; ++n) st[n] = a.init_state[state_off + n];
-    } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n) st[n] = 0.f;
-    }
-    walk<T, N, 1>(a, sm, 0, row_tok, h, g, t0, t1, st);
-    if (a.final_state && p < a.P) {
-#pragma unroll
-        for (int n = 0; n < N; ++n) a.final_state[state_off + n] = st[n];
-    }
+    const size_t state_off = ((size_t)unit * a.H + h) * a.P * N;
+    float st[N / LPP];
+    state_load<N, LPP>(st, a.init_state ? a.init_state + state_off : nullptr, a.P);
+    walk<T, N, LPP, 1>(a, sm, 0, row_tok, h, g, t0, t1, st);
+    if (a.final_state) state_store<N, LPP>(st, a.final_state + state_off, a.P);
     if (a.ndir == 2) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) st[n] = 0.f;
-        if (a.y2) walk<T, N, 1>(a, sm, 1, row_tok, h, g, t0, t1, st);
-        else walk<T, N, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
+        for (int i = 0; i < N / LPP; ++i) st[i] = 0.f;
+        if (a.y2) walk<T, N, LPP, 1>(a, sm, 1, row_tok, h, g, t0, t1, st);
+        else walk<T, N, LPP, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
     }
 }
 
@@ -166,28 +208,26 @@ __device__ __forceinline__ size_t seg_slot(const SeqArgs &a, int row, int d, int
 }
 
 // Pass 1: every segment from a zero state; its outgoing state and sum of a.
-template <typename T, int N>
+template <typename T, int N, int LPP>
 __global__ void __launch_bounds__(kMaxP) k_seq_seg_state(const SeqArgs a) {
     __shared__ SeqSmem<N> sm;
     const int seg = blockIdx.x, h = blockIdx.y;
     const int row = blockIdx.z / a.ndir, d = blockIdx.z % a.ndir;
-    const int p = threadIdx.x;
     const int g = h / (a.H / a.G);
     const int t0 = seg * a.seg_len, t1 = min(t0 + a.seg_len, a.L);
-    float st[N];
+    float st[N / LPP];
 #pragma unroll
-    for (int n = 0; n < N; ++n) st[n] = 0.f;
-    const float asum = walk<T, N, 0>(a, sm, d, (size_t)row * a.L, h, g, t0, t1, st);
+    for (int i = 0; i < N / LPP; ++i) st[i] = 0.f;
+    const float asum = walk<T, N, LPP, 0>(a, sm, d, (size_t)row * a.L, h, g, t0, t1, st);
     const size_t slot = seg_slot(a, row, d, seg, h);
-    if (p < a.P) {
-#pragma unroll
-        for (int n = 0; n < N; ++n) a.S[(slot * a.P + p) * N + n] = st[n];
-    }
-    if (p == 0) a.tot[slot] = asum;
+    state_store<N, LPP>(st, a.S + slot * a.P * N, a.P);
+    if (threadIdx.x == 0) a.tot[slot] = asum;
 }
 
 // Pass 2: incoming state of every segment, one thread per state element,
-// sequential over the segments in the walking direction.
+// sequential over the segments in the walking direction. Eight segments'
+// values are loaded (at clamped indices, without branches) before any is
+// used, so that their loads are in flight together.
 template <int N>
 __global__ void __launch_bounds__(256) k_seq_seg_scan(const SeqArgs a) {
     const int e = blockIdx.x * 256 + threadIdx.x;   // p * N + n
@@ -195,38 +235,44 @@ __global__ void __launch_bounds__(256) k_seq_seg_scan(const SeqArgs a) {
     const int row = blockIdx.z / a.ndir, d = blockIdx.z % a.ndir;
     const int PN = a.P * N;
     if (e >= PN) return;
+    constexpr int kB = 8;
     float hv = 0.f;
     if (d == 0 && a.init_state) hv = a.init_state[((size_t)row * a.H + h) * PN + e];
-    for (int s = 0; s < a.nseg; ++s) {
-        const int k = d == 0 ? s : a.nseg - 1 - s;
-        const size_t slot = seg_slot(a, row, d, k, h);
-        a.Hin[slot * PN + e] = hv;
-        hv = fmaf(expf(a.tot[slot]), hv, a.S[slot * PN + e]);
+    for (int s0 = 0; s0 < a.nseg; s0 += kB) {
+        float sv[kB], tv[kB];
+#pragma unroll
+        for (int k = 0; k < kB; ++k) {
+            const int s = min(s0 + k, a.nseg - 1);
+            const size_t slot = seg_slot(a, row, d, d == 0 ? s : a.nseg - 1 - s, h);
+            sv[k] = a.S[slot * PN + e];
+            tv[k] = a.tot[slot];
+        }
+#pragma unroll
+        for (int k = 0; k < kB; ++k) {
+            if (s0 + k >= a.nseg) break;
+            const int s = s0 + k;
+            const size_t slot = seg_slot(a, row, d, d == 0 ? s : a.nseg - 1 - s, h);
+            a.Hin[slot * PN + e] = hv;
+            hv = fmaf(expf(tv[k]), hv, sv[k]);
+        }
     }
     if (d == 0 && a.final_state) a.final_state[((size_t)row * a.H + h) * PN + e] = hv;
 }
 
 // Pass 3: every segment from its incoming state, both directions, y.
-template <typename T, int N>
+template <typename T, int N, int LPP>
 __global__ void __launch_bounds__(kMaxP) k_seq_seg_out(const SeqArgs a) {
     __shared__ SeqSmem<N> sm;
     const int seg = blockIdx.x, h = blockIdx.y, row = blockIdx.z;
-    const int p = threadIdx.x;
     const int g = h / (a.H / a.G);
     const int t0 = seg * a.seg_len, t1 = min(t0 + a.seg_len, a.L);
     const size_t row_tok = (size_t)row * a.L;
     for (int d = 0; d < a.ndir; ++d) {
         const size_t slot = seg_slot(a, row, d, seg, h);
-        float st[N];
-        if (p < a.P) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) st[n] = a.Hin[(slot * a.P + p) * N + n];
-        } else {
-#pragma unroll
-            for (int n = 0; n < N; ++n) st[n] = 0.f;
-        }
-        if (d == 0 || a.y2) walk<T, N, 1>(a, sm, d, row_tok, h, g, t0, t1, st);
-        else walk<T, N, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
+        float st[N / LPP];
+        state_load<N, LPP>(st, a.Hin + slot * a.P * N, a.P);
+        if (d == 0 || a.y2) walk<T, N, LPP, 1>(a, sm, d, row_tok, h, g, t0, t1, st);
+        else walk<T, N, LPP, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
     }
 }
 
@@ -263,20 +309,29 @@ size_t seq_workspace(int batch, int L, int H, int P, int N, bool packed) {
     return 2 * al256(st) + al256((size_t)batch * 2 * nseg * H * 4);
 }
 
-template <typename T, int N>
-static hipError_t launch_typed(const SeqArgs &a, int units, hipStream_t s) {
-    const int threads = ((a.P + 63) / 64) * 64;
+template <typename T, int N, int LPP>
+static hipError_t launch_lpp(const SeqArgs &a, int units, hipStream_t s) {
+    const int threads = ((a.P * LPP + 63) / 64) * 64;
     if (a.nseg <= 1) {
-        BM_LAUNCH("scan_seq", (k_scan_seq<T, N>), dim3(units, a.H), dim3(threads), 0, s, a);
+        BM_LAUNCH("scan_seq", (k_scan_seq<T, N, LPP>), dim3(units, a.H), dim3(threads), 0, s, a);
     } else {
-        BM_LAUNCH("seq_seg_state", (k_seq_seg_state<T, N>), dim3(a.nseg, a.H, a.batch * a.ndir),
+        BM_LAUNCH("seq_seg_state", (k_seq_seg_state<T, N, LPP>), dim3(a.nseg, a.H, a.batch * a.ndir),
                   dim3(threads), 0, s, a);
         BM_LAUNCH("seq_seg_scan", (k_seq_seg_scan<N>), dim3((a.P * N + 255) / 256, a.H, a.batch * a.ndir),
                   dim3(256), 0, s, a);
-        BM_LAUNCH("seq_seg_out", (k_seq_seg_out<T, N>), dim3(a.nseg, a.H, a.batch), dim3(threads), 0,
+        BM_LAUNCH("seq_seg_out", (k_seq_seg_out<T, N, LPP>), dim3(a.nseg, a.H, a.batch), dim3(threads), 0,
                   s, a);
     }
     return hipGetLastError();
+}
+
+template <typename T, int N>
+static hipError_t launch_typed(const SeqArgs &a, int units, hipStream_t s) {
+    switch (seq_lpp(a.P)) {
+        case 4: return launch_lpp<T, N, 4>(a, units, s);
+        case 2: return launch_lpp<T, N, 2>(a, units, s);
+    }
+    return launch_lpp<T, N, 1>(a, units, s);
 }
 
 template <typename T>
