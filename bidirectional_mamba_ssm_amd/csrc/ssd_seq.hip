@@ -38,25 +38,32 @@ struct SeqArgs {
     float *y;
     float *S;                 // [batch][2][nseg][H][P][N] segment states from zero
     float *Hin;               // [batch][2][nseg][H][P][N] segment incoming states
-    float *tot;               // [batch][2][nseg][H] total of a over the segment
+    float *tot;               // [batch][2][nseg][H] e^{total of a over the segment}
     int dt_softplus;          // dt holds the pre-activation: softplus(dt + bias)
     const float *dt_bias[2];  // [H] per direction, or nullptr (zero)
     float *y2;                // streams kept apart: the forward stream's output
 };
 
-template <int N>
+// A tile's inputs and outputs for headdim up to PM (small heads leave room
+// for more workgroups per CU).
+template <int N, int PM>
 struct SeqSmem {
     float B[kSeqTile][N];
     float C[kSeqTile][N];
-    float x[kSeqTile][kMaxP];
-    float y[kSeqTile][kMaxP];
+    float x[kSeqTile][PM];
+    float y[kSeqTile][PM];
     float dt[kSeqTile];
     float at[kSeqTile];    // dt * A
     float dec[kSeqTile];   // exp(dt * A)
 };
 
-// Lanes per headdim column for a headdim of P.
-inline int seq_lpp(int P) { return P <= 16 ? 4 : P <= 32 ? 2 : 1; }
+// The headdim bound PM a launch is compiled for (16, 32, 64 or 128: the
+// tiles' width), and its lanes per headdim column.
+inline int seq_pm(int P) { return P <= 16 ? 16 : P <= 32 ? 32 : P <= 64 ? 64 : kMaxP; }
+template <int PM>
+struct SeqLPP {
+    static constexpr int value = PM <= 16 ? 4 : PM <= 32 ? 2 : 1;
+};
 
 // Sum over the LPP consecutive lanes of a column, in its last lane (DPP row
 // shifts within a 16-lane row; LPP divides 16, so a column's lanes share a
@@ -73,9 +80,10 @@ __device__ __forceinline__ float col_sum(float v) {
 // MODE 0: state only; MODE 1: writes y; MODE 2: adds into y. y goes through
 // LDS a tile at a time (the old values of a MODE 2 tile are read with the
 // inputs), so no token waits on a global load.
-template <typename T, int N, int LPP, int MODE>
-__device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, int h, int g,
-                      int t0, int t1, float (&st)[N / LPP]) {
+template <typename T, int N, int PM, int MODE>
+__device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
+                      int t0, int t1, float (&st)[N / SeqLPP<PM>::value]) {
+    constexpr int LPP = SeqLPP<PM>::value;
     constexpr int NL = N / LPP;            // state entries per lane
     constexpr int NA = NL >= 16 ? 4 : NL >= 8 ? 2 : 1;   // independent partial sums of y
     // the output this direction writes (or adds into)
@@ -125,6 +133,14 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, i
         }
         __syncthreads();
         for (int s = 0; s < nsteps; ++s) {
+            // the token's operands first (reads in flight together), then
+            // the arithmetic
+            float bv[NL], cv[NL];
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                bv[i] = sm.B[s][q * NL + i];
+                cv[i] = MODE != 0 ? sm.C[s][q * NL + i] : 0.f;
+            }
             const float decay = sm.dec[s];
             asum += sm.at[s];
             const float xv = sm.x[s][pc];
@@ -134,8 +150,8 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N> &sm, int d, size_t row_tok, i
             for (int k = 0; k < NA; ++k) acc[k] = 0.f;
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                st[i] = fmaf(decay, st[i], dx * sm.B[s][q * NL + i]);
-                if (MODE != 0) acc[i % NA] = fmaf(sm.C[s][q * NL + i], st[i], acc[i % NA]);
+                st[i] = fmaf(decay, st[i], dx * bv[i]);
+                if (MODE != 0) acc[i % NA] = fmaf(cv[i], st[i], acc[i % NA]);
             }
             if (MODE != 0) {
                 float yv = acc[0];
@@ -180,9 +196,10 @@ __device__ __forceinline__ void state_store(const float (&st)[N / LPP], float *b
 }
 
 // Whole rows or packed sequences: one workgroup per (unit, head).
-template <typename T, int N, int LPP>
+template <typename T, int N, int PM>
 __global__ void __launch_bounds__(kMaxP) k_scan_seq(const SeqArgs a) {
-    __shared__ SeqSmem<N> sm;
+    __shared__ SeqSmem<N, PM> sm;
+    constexpr int LPP = SeqLPP<PM>::value;
     const int unit = blockIdx.x;
     const int h = blockIdx.y;
     const int g = h / (a.H / a.G);
@@ -193,13 +210,13 @@ __global__ void __launch_bounds__(kMaxP) k_scan_seq(const SeqArgs a) {
     const size_t state_off = ((size_t)unit * a.H + h) * a.P * N;
     float st[N / LPP];
     state_load<N, LPP>(st, a.init_state ? a.init_state + state_off : nullptr, a.P);
-    walk<T, N, LPP, 1>(a, sm, 0, row_tok, h, g, t0, t1, st);
+    walk<T, N, PM, 1>(a, sm, 0, row_tok, h, g, t0, t1, st);
     if (a.final_state) state_store<N, LPP>(st, a.final_state + state_off, a.P);
     if (a.ndir == 2) {
 #pragma unroll
         for (int i = 0; i < N / LPP; ++i) st[i] = 0.f;
-        if (a.y2) walk<T, N, LPP, 1>(a, sm, 1, row_tok, h, g, t0, t1, st);
-        else walk<T, N, LPP, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
+        if (a.y2) walk<T, N, PM, 1>(a, sm, 1, row_tok, h, g, t0, t1, st);
+        else walk<T, N, PM, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
     }
 }
 
@@ -207,10 +224,12 @@ __device__ __forceinline__ size_t seg_slot(const SeqArgs &a, int row, int d, int
     return (((size_t)row * 2 + d) * a.nseg + seg) * a.H + h;
 }
 
-// Pass 1: every segment from a zero state; its outgoing state and sum of a.
-template <typename T, int N, int LPP>
+// Pass 1: every segment from a zero state; its outgoing state and decay
+// (e to the sum of a).
+template <typename T, int N, int PM>
 __global__ void __launch_bounds__(kMaxP) k_seq_seg_state(const SeqArgs a) {
-    __shared__ SeqSmem<N> sm;
+    __shared__ SeqSmem<N, PM> sm;
+    constexpr int LPP = SeqLPP<PM>::value;
     const int seg = blockIdx.x, h = blockIdx.y;
     const int row = blockIdx.z / a.ndir, d = blockIdx.z % a.ndir;
     const int g = h / (a.H / a.G);
@@ -218,14 +237,14 @@ __global__ void __launch_bounds__(kMaxP) k_seq_seg_state(const SeqArgs a) {
     float st[N / LPP];
 #pragma unroll
     for (int i = 0; i < N / LPP; ++i) st[i] = 0.f;
-    const float asum = walk<T, N, LPP, 0>(a, sm, d, (size_t)row * a.L, h, g, t0, t1, st);
+    const float asum = walk<T, N, PM, 0>(a, sm, d, (size_t)row * a.L, h, g, t0, t1, st);
     const size_t slot = seg_slot(a, row, d, seg, h);
     state_store<N, LPP>(st, a.S + slot * a.P * N, a.P);
-    if (threadIdx.x == 0) a.tot[slot] = asum;
+    if (threadIdx.x == 0) a.tot[slot] = expf(asum);
 }
 
 // Pass 2: incoming state of every segment, one thread per state element,
-// sequential over the segments in the walking direction. Eight segments'
+// sequential over the segments in the walking direction. 32 segments'
 // values are loaded (at clamped indices, without branches) before any is
 // used, so that their loads are in flight together.
 template <int N>
@@ -235,7 +254,7 @@ __global__ void __launch_bounds__(256) k_seq_seg_scan(const SeqArgs a) {
     const int row = blockIdx.z / a.ndir, d = blockIdx.z % a.ndir;
     const int PN = a.P * N;
     if (e >= PN) return;
-    constexpr int kB = 8;
+    constexpr int kB = 32;
     float hv = 0.f;
     if (d == 0 && a.init_state) hv = a.init_state[((size_t)row * a.H + h) * PN + e];
     for (int s0 = 0; s0 < a.nseg; s0 += kB) {
@@ -253,16 +272,17 @@ __global__ void __launch_bounds__(256) k_seq_seg_scan(const SeqArgs a) {
             const int s = s0 + k;
             const size_t slot = seg_slot(a, row, d, d == 0 ? s : a.nseg - 1 - s, h);
             a.Hin[slot * PN + e] = hv;
-            hv = fmaf(expf(tv[k]), hv, sv[k]);
+            hv = fmaf(tv[k], hv, sv[k]);
         }
     }
     if (d == 0 && a.final_state) a.final_state[((size_t)row * a.H + h) * PN + e] = hv;
 }
 
 // Pass 3: every segment from its incoming state, both directions, y.
-template <typename T, int N, int LPP>
+template <typename T, int N, int PM>
 __global__ void __launch_bounds__(kMaxP) k_seq_seg_out(const SeqArgs a) {
-    __shared__ SeqSmem<N> sm;
+    __shared__ SeqSmem<N, PM> sm;
+    constexpr int LPP = SeqLPP<PM>::value;
     const int seg = blockIdx.x, h = blockIdx.y, row = blockIdx.z;
     const int g = h / (a.H / a.G);
     const int t0 = seg * a.seg_len, t1 = min(t0 + a.seg_len, a.L);
@@ -271,8 +291,8 @@ __global__ void __launch_bounds__(kMaxP) k_seq_seg_out(const SeqArgs a) {
         const size_t slot = seg_slot(a, row, d, seg, h);
         float st[N / LPP];
         state_load<N, LPP>(st, a.Hin + slot * a.P * N, a.P);
-        if (d == 0 || a.y2) walk<T, N, LPP, 1>(a, sm, d, row_tok, h, g, t0, t1, st);
-        else walk<T, N, LPP, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
+        if (d == 0 || a.y2) walk<T, N, PM, 1>(a, sm, d, row_tok, h, g, t0, t1, st);
+        else walk<T, N, PM, 2>(a, sm, 1, row_tok, h, g, t0, t1, st);
     }
 }
 
@@ -309,17 +329,18 @@ size_t seq_workspace(int batch, int L, int H, int P, int N, bool packed) {
     return 2 * al256(st) + al256((size_t)batch * 2 * nseg * H * 4);
 }
 
-template <typename T, int N, int LPP>
-static hipError_t launch_lpp(const SeqArgs &a, int units, hipStream_t s) {
+template <typename T, int N, int PM>
+static hipError_t launch_pm(const SeqArgs &a, int units, hipStream_t s) {
+    constexpr int LPP = SeqLPP<PM>::value;
     const int threads = ((a.P * LPP + 63) / 64) * 64;
     if (a.nseg <= 1) {
-        BM_LAUNCH("scan_seq", (k_scan_seq<T, N, LPP>), dim3(units, a.H), dim3(threads), 0, s, a);
+        BM_LAUNCH("scan_seq", (k_scan_seq<T, N, PM>), dim3(units, a.H), dim3(threads), 0, s, a);
     } else {
-        BM_LAUNCH("seq_seg_state", (k_seq_seg_state<T, N, LPP>), dim3(a.nseg, a.H, a.batch * a.ndir),
+        BM_LAUNCH("seq_seg_state", (k_seq_seg_state<T, N, PM>), dim3(a.nseg, a.H, a.batch * a.ndir),
                   dim3(threads), 0, s, a);
         BM_LAUNCH("seq_seg_scan", (k_seq_seg_scan<N>), dim3((a.P * N + 255) / 256, a.H, a.batch * a.ndir),
                   dim3(256), 0, s, a);
-        BM_LAUNCH("seq_seg_out", (k_seq_seg_out<T, N, LPP>), dim3(a.nseg, a.H, a.batch), dim3(threads), 0,
+        BM_LAUNCH("seq_seg_out", (k_seq_seg_out<T, N, PM>), dim3(a.nseg, a.H, a.batch), dim3(threads), 0,
                   s, a);
     }
     return hipGetLastError();
@@ -327,11 +348,12 @@ static hipError_t launch_lpp(const SeqArgs &a, int units, hipStream_t s) {
 
 template <typename T, int N>
 static hipError_t launch_typed(const SeqArgs &a, int units, hipStream_t s) {
-    switch (seq_lpp(a.P)) {
-        case 4: return launch_lpp<T, N, 4>(a, units, s);
-        case 2: return launch_lpp<T, N, 2>(a, units, s);
+    switch (seq_pm(a.P)) {
+        case 16: return launch_pm<T, N, 16>(a, units, s);
+        case 32: return launch_pm<T, N, 32>(a, units, s);
+        case 64: return launch_pm<T, N, 64>(a, units, s);
     }
-    return launch_lpp<T, N, 1>(a, units, s);
+    return launch_pm<T, N, kMaxP>(a, units, s);
 }
 
 template <typename T>
