@@ -1836,7 +1836,7 @@ __device__ __forceinline__ int pair_hoff(int v, int nt) {
 // part of the outputs and the state update (all from the stage and the
 // registers); after the second: M x, the outputs, the next chunk's stage and
 // scans. Returns the outgoing state in Hacc.
-template <bool PACKED, int D, bool SP, bool ADD>
+template <bool PACKED, int D, bool SP, bool ADD, bool Y2 = false>
 __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b, int seg, int h,
                                           int grp, int half, int v, f32x4 (&Hacc)[8],
                                           float &chk, bool check) {
@@ -1882,7 +1882,8 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
     const uint16_t *crow = (const uint16_t *)dp.C + (row0 * a.G + grp) * kN;
     const uint16_t *dtrow = (const uint16_t *)dp.dt + row0 * a.H + h;
     const int32_t *sqrow = PACKED ? a.seq + row0 : nullptr;
-    float *yrow = a.y + (row0 * a.H + h) * kP;
+    // (streams kept apart: the forward pass writes y2)
+    float *yrow = ((Y2 && D == 0) ? a.y2 : a.y) + (row0 * a.H + h) * kP;
     auto issue = [&](int c0, int len) {
         ld.issue(a, xrow + (size_t)c0 * xstride, brow + (size_t)c0 * bstride,
                  crow + (size_t)c0 * bstride, len);
@@ -1938,7 +1939,8 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         lds_barrier();   // every row tile of M written
         pair_mx<D>(acc, sm.m[half], st.xs[half], v);
         // the reverse pass of two writes y for the forward pass to read back
-        pair_store(yrow + (size_t)c0 * xstride, xstride, acc, len, v, chk, check, D == 0 || len < 64);
+        // (in the lanes' own order; a final output in memory order)
+        pair_store(yrow + (size_t)c0 * xstride, xstride, acc, len, v, chk, check, D == 0 || Y2 || len < 64);
         if (ADD) pair_prev(acc, yrow + (size_t)c0n * xstride, xstride, lenn, v);
     }
 }
@@ -1948,24 +1950,25 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
 // registers would crowd the fast path's), with the arguments copied: a
 // reference to the kernel's arguments would move them to private memory for
 // the fast path too.
-template <bool PACKED, bool SP, int WB>
+template <bool PACKED, bool SP, int WB, bool Y2 = false>
 __device__ __attribute__((noinline)) void pair_exact(const SegArgs a, OutSmem<64> &sm, int b, int seg, int h, int grp) {
     if (a.ndir == 2) {
         seg_pass<64, PACKED, 1, SP, false, WB>(a, sm, b, seg, h, grp, false);
-        seg_pass<64, PACKED, 0, SP, false, WB>(a, sm, b, seg, h, grp, true);
+        seg_pass<64, PACKED, 0, SP, Y2, WB>(a, sm, b, seg, h, grp, !Y2);
     } else {
         seg_pass<64, PACKED, 0, SP, false, WB>(a, sm, b, seg, h, grp, false);
     }
 }
 
 // Both passes of the fp16 form (NDIR directions); returns the forward
-// direction's outgoing state in Hacc and the check sum of the last pass in chk.
-template <bool PACKED, bool SP, int NDIR>
+// direction's outgoing state in Hacc and the check sum of the last pass in chk
+// (of both passes with the streams kept apart, Y2: each is an output then).
+template <bool PACKED, bool SP, int NDIR, bool Y2 = false>
 __device__ __forceinline__ void pair_fast(const SegArgs &a, PairSmem &sm, int b, int seg, int h,
                                           int grp, int half, int v, f32x4 (&Hacc)[8], float &chk) {
     if (NDIR == 2) {
-        pair_pass<PACKED, 1, SP, false>(a, sm, b, seg, h, grp, half, v, Hacc, chk, false);
-        pair_pass<PACKED, 0, SP, true>(a, sm, b, seg, h, grp, half, v, Hacc, chk, true);
+        pair_pass<PACKED, 1, SP, false, Y2>(a, sm, b, seg, h, grp, half, v, Hacc, chk, Y2);
+        pair_pass<PACKED, 0, SP, !Y2, Y2>(a, sm, b, seg, h, grp, half, v, Hacc, chk, true);
     } else {
         pair_pass<PACKED, 0, SP, false>(a, sm, b, seg, h, grp, half, v, Hacc, chk, true);
     }
@@ -1974,7 +1977,7 @@ __device__ __forceinline__ void pair_fast(const SegArgs &a, PairSmem &sm, int b,
 // NDIR (the number of directions, a.ndir) is a template argument: with it a
 // run-time branch, both passes share live ranges across it and the
 // register allocator spills the state.
-template <bool PACKED, bool SP, int NDIR>
+template <bool PACKED, bool SP, int NDIR, bool Y2 = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 k_pair_out(const SegArgs a) {
     // XCD-aware order as in k_seg_out, over (row-segment, head pair)
@@ -1998,7 +2001,7 @@ k_pair_out(const SegArgs a) {
     __shared__ __attribute__((aligned(16))) PairShared sh;
     f32x4 Hacc[8];
     float chk = 0.f;
-    pair_fast<PACKED, SP, NDIR>(a, sh.fast, b, seg, h, grp, half, v, Hacc, chk);
+    pair_fast<PACKED, SP, NDIR, Y2>(a, sh.fast, b, seg, h, grp, half, v, Hacc, chk);
     const bool want_final = seg == a.nseg - 1 && a.final_state;
     if (want_final) {
 #pragma unroll
@@ -2020,8 +2023,8 @@ k_pair_out(const SegArgs a) {
     }
     // an fp16 operand overflowed: recompute the segment of both heads exactly
     lds_barrier();   // every wave has read the flags before the memory is reused
-    if (half == 0) pair_exact<PACKED, SP, 0>(a, sh.slow[0], b, seg, h, grp);
-    else pair_exact<PACKED, SP, 4>(a, sh.slow[1], b, seg, h, grp);
+    if (half == 0) pair_exact<PACKED, SP, 0, Y2>(a, sh.slow[0], b, seg, h, grp);
+    else pair_exact<PACKED, SP, 4, Y2>(a, sh.slow[1], b, seg, h, grp);
 }
 
 size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -2062,7 +2065,7 @@ int pick_ts(int batch, int L, int H, int Q, size_t limit) {
 // The pair kernel serves two heads of one group per workgroup.
 bool pair_ok(const SegArgs &a) { return a.H % 2 == 0 && (a.H / a.G) % 2 == 0; }
 
-template <bool SP>
+template <bool SP, bool Y2 = false>
 hipError_t launch_pair(const SegArgs &a, hipStream_t s) {
     if (a.nseg > 1) {
         BM_LAUNCH("ssd_seg_state", k_seg_state<SP>, dim3(a.nseg, a.ndir, a.batch * a.H), dim3(kThreads), 0,
@@ -2072,7 +2075,10 @@ hipError_t launch_pair(const SegArgs &a, hipStream_t s) {
     }
     const int per_xcd = (a.batch * a.nseg * (a.H / 2) + 7) / 8;
     const dim3 grid(per_xcd * 8), block(512);
-    if (a.seq) {
+    if (Y2) {   // (both directions)
+        if (a.seq) BM_LAUNCH("ssd_pair_out", (k_pair_out<true, SP, 2, true>), grid, block, 0, s, a);
+        else BM_LAUNCH("ssd_pair_out", (k_pair_out<false, SP, 2, true>), grid, block, 0, s, a);
+    } else if (a.seq) {
         if (a.ndir == 2) BM_LAUNCH("ssd_pair_out", (k_pair_out<true, SP, 2>), grid, block, 0, s, a);
         else BM_LAUNCH("ssd_pair_out", (k_pair_out<true, SP, 1>), grid, block, 0, s, a);
     } else {
@@ -2147,9 +2153,14 @@ hipError_t launch_chunked(const Problem &p, void *ws, size_t limit, hipStream_t 
     a.dt_bias[1] = p.dt_bias[1];
     a.y2 = p.y2;
     const bool sp = p.dt_softplus;
-    // streams kept apart (no softplus step size in that mode)
+    // the fp16 pair kernel, except for rows of one 64-token chunk with both
+    // directions (the block step), which k_dual_out serves in one pass
+    const bool dual = p.Q == 64 && a.ndir == 2 && !a.seq && a.L <= 64;
+    // streams kept apart (no softplus step size in that mode): the pair
+    // kernel as for the summed output, else the exact kernels
     if (p.y2) {
         if (sp || a.ndir != 2) return hipErrorInvalidValue;
+        if (pair_ok(a) && !dual) return launch_pair<false, true>(a, s);
         switch (p.Q) {
             case 64: return launch_q<64, false, true>(a, s);
             case 128: return launch_q<128, false, true>(a, s);
@@ -2157,9 +2168,6 @@ hipError_t launch_chunked(const Problem &p, void *ws, size_t limit, hipStream_t 
         }
         return hipErrorInvalidValue;
     }
-    // the fp16 pair kernel, except for rows of one 64-token chunk with both
-    // directions (the block step), which k_dual_out serves in one pass
-    const bool dual = p.Q == 64 && a.ndir == 2 && !a.seq && a.L <= 64;
     if (pair_ok(a) && !dual) return sp ? launch_pair<true>(a, s) : launch_pair<false>(a, s);
     switch (p.Q) {
         case 64: return sp ? launch_q<64, true>(a, s) : launch_q<64, false>(a, s);
