@@ -44,6 +44,12 @@ CASES = [
     ("bf16_q128", 1, 384, 2, 64, 128, 1, "bf16", 128, 16),
     ("bf16_q256_ragged", 1, 777, 2, 64, 128, 1, "bf16", 256, 17),
     ("bf16_q256_short", 3, 40, 2, 64, 128, 1, "bf16", 256, 18),
+    # token-sequential lane groupings: headdim above 64 (two waves, one lane
+    # per column), 24 (two lanes per column, the last groups past the last
+    # column), 8 (four lanes per column, half the wave past it)
+    ("f32_p96_n32", 1, 150, 2, 96, 32, 1, "f32", 64, 19),
+    ("f32_p24_n16_groups", 2, 100, 4, 24, 16, 2, "f32", 64, 20),
+    ("bf16_p8_n64", 1, 90, 2, 8, 64, 1, "bf16", 64, 21),
 ]
 
 
@@ -332,6 +338,7 @@ SEGMENTED = [
     ("f32_one_pair_ragged", 1, 4001, 1, 16, 16, 1, "f32", 64, 131),
     ("f32_two_rows_p64", 2, 1800, 1, 64, 64, 1, "f32", 128, 132),
     ("bf16_small_heads", 1, 3000, 2, 16, 16, 1, "bf16", 256, 133),
+    ("f32_p24_n128", 1, 2600, 1, 24, 128, 1, "f32", 64, 134),
 ]
 
 
