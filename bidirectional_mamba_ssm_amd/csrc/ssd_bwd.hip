@@ -1135,10 +1135,12 @@ struct GradMxSmem {
     float red[16];
 };
 
+// G holds the wave's tile of the block's Gram C B^T: the same for every head
+// of a group, so computed with the first head only when walking them (HSUM).
 template <bool HSUM>
 __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const int c, const int h,
                                         const int dir, const int b, const bool first,
-                                        f32x4 (&accb)[2], f32x4 (&accc)[2]) {
+                                        f32x4 (&accb)[2], f32x4 (&accc)[2], f32x4 &G) {
     using Sm = GradMxSmem;
     constexpr int P = Sm::P, N = Sm::N, RN = Sm::RN, RP = Sm::RP, RQ = Sm::RQ;
     constexpr size_t YS = (size_t)kQ * RP, QS = (size_t)kQ * RQ, HS = (size_t)P * RN;   // part strides
@@ -1232,10 +1234,13 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
         float M[4] = {0.f, 0.f, 0.f, 0.f}, dG[4] = {0.f, 0.f, 0.f, 0.f}, zs[4] = {0.f, 0.f, 0.f, 0.f};
         const int j = jt * 16 + l16;
         if (jt <= it) {
-            f32x4 G = zero4(), D = zero4();
+            f32x4 D = zero4();
+            if (!HSUM || first) {
+                G = zero4();
 #pragma unroll
-            for (int kc = 0; kc < N / 32; ++kc)
-                G = mfma16x16x32(dir_op<RN>(sm.cx, it * 16, 32 * kc), dir_op<RN>(sm.bx, jt * 16, 32 * kc), G);
+                for (int kc = 0; kc < N / 32; ++kc)
+                    G = mfma16x16x32(dir_op<RN>(sm.cx, it * 16, 32 * kc), dir_op<RN>(sm.bx, jt * 16, 32 * kc), G);
+            }
 #pragma unroll
             for (int kc = 0; kc < P / 32; ++kc) {
                 const u32x4 xo = dir_op<RP>(sm.xx, jt * 16, 32 * kc);
@@ -1498,8 +1503,8 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
 __global__ __launch_bounds__(kMxThreads) void k_bwd_grad_mx(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) GradMxSmem sm;
     const int dir = (int)(blockIdx.z % (unsigned)a.ndir), b = (int)(blockIdx.z / (unsigned)a.ndir);
-    f32x4 accb[2], accc[2];
-    grad_mx<false>(a, sm, blockIdx.x, blockIdx.y, dir, b, false, accb, accc);
+    f32x4 accb[2], accc[2], G;
+    grad_mx<false>(a, sm, blockIdx.x, blockIdx.y, dir, b, false, accb, accc, G);
 }
 
 // One workgroup per (block, group, row and stream), walking the group's
@@ -1509,10 +1514,10 @@ __global__ __launch_bounds__(kMxThreads) void k_bwd_grad_heads_mx(BwdArgs a) {
     constexpr int N = GradMxSmem::N;
     const int dir = (int)(blockIdx.z % (unsigned)a.ndir), b = (int)(blockIdx.z / (unsigned)a.ndir);
     const int hg = a.H / a.G, g = blockIdx.y, h0 = g * hg, c = blockIdx.x;
-    f32x4 accb[2], accc[2];
+    f32x4 accb[2], accc[2], G = zero4();
     for (int k = 0; k < hg; ++k) {
         if (k) __syncthreads();   // the previous head's last phase reads the LDS rows
-        grad_mx<true>(a, sm, c, h0 + k, dir, b, k == 0, accb, accc);
+        grad_mx<true>(a, sm, c, h0 + k, dir, b, k == 0, accb, accc, G);
     }
     const bool rev = dir == 1;
     const GradPtrs gr = rev ? a.gbwd : a.gfwd;
