@@ -26,15 +26,25 @@
 //   da_k  = sum_{i >= k} ds_i,  ddt_k = x_k . dxd_k + A da_k,  dA = sum dt_k da_k
 //   dx_k  = D dy_k + dt_k dxd_k,  dD = sum x_k . dy_k
 //
-// Kernels (fp32 arithmetic; the running sums s in fp64):
+// Kernels (products of fp32 values, accumulated in fp32; the running sums s
+// in fp64):
+//   k_bwd_chain  per (row, stream, head): walks the blocks forward and then
+//                backward with the state in the matrix-core accumulators and
+//                writes every block's entering state Hp and leaving-state
+//                gradient dHe (taken when such units fill the CUs or rows are
+//                short); otherwise
 //   k_bwd_state  per (row, stream, head, block): the block's own state
 //                S = sum_j e^{s_end - s_j} dt_j B_j x_j^T, its output-gradient
-//                feed R = sum_i e^{s_i} C_i dy_i^T and s_end.
-//   k_bwd_pass   per (row, stream, head, state element): the entering states
-//                Hp (forward over blocks) and leaving-state gradients dHe
-//                (backward over blocks), written over S and R.
-//   k_bwd_grad   per (row, stream, head, block): everything above; dB and dC
-//                per head, dA and dD per block, into the workspace.
+//                feed R = sum_i e^{s_i} C_i dy_i^T and s_end, and
+//   k_bwd_pass   per (row, stream, head, state element): Hp (forward over
+//                blocks) and dHe (backward over blocks), written over S and R.
+//   k_bwd_grad[_heads][_mx]  per (row, stream, block) and head, or walking the
+//                heads of a group: everything above; dB and dC per head into
+//                the workspace, or summed over the group's heads in registers;
+//                dA and dD per block. The _mx form (bf16 inputs, headdim 64,
+//                d_state 128) runs every product on the bf16 matrix cores
+//                with fp32 operands as exact sums of three bf16 parts, the
+//                other on the fp32 matrix cores.
 //   k_bwd_sum_bc / k_bwd_sum_ad: sums over the heads of a group and over the
 //                blocks, in a fixed order (deterministic results).
 #include <type_traits>
@@ -346,8 +356,8 @@ __global__ __launch_bounds__(256) void k_bwd_pass(BwdArgs a, int np) {
 // backward, the state in the matrix-core accumulators, and writes each
 // block's entering state Hp_c (over S) and leaving-state gradient dHe_c (over
 // R) before folding the block in:
-//   Hp_{c+1}   = e^{s_end} Hp_c   + sum_j (e^{s_end - s_j} dt_j x_j) B_j^T-side
-//   dHe_{c-1}  = e^{s_end} dHe_c  + sum_i (e^{s_i} dy_i) C_i^T-side
+//   Hp_{c+1}   = e^{s_end} Hp_c   + sum_j B_j (e^{s_end - s_j} dt_j x_j)^T
+//   dHe_{c-1}  = e^{s_end} dHe_c  + sum_i C_i (e^{s_i} dy_i)^T
 // (the block's own S and R of k_bwd_state never leave the CU). Products on
 // the bf16 matrix cores (v_mfma_f32_16x16x32_bf16): an fp32 operand enters as
 // the exact sum of three bf16 parts, bf16 inputs B and C as they are, so the
@@ -494,7 +504,7 @@ __device__ __forceinline__ void chain_sweep(const BwdArgs &a, ChainSmem<P, N, si
             const int r = e4 * 4 / N, cc = e4 * 4 % N;
             float v[4];
             ra.get(k, v);
-            if (EXACT) {
+            if constexpr (EXACT) {
                 *(u32x2 *)&sm.a[0][r][cc] = u32x2{bf_pair(r < len ? v[0] : 0.f, r < len ? v[1] : 0.f),
                                                   bf_pair(r < len ? v[2] : 0.f, r < len ? v[3] : 0.f)};
             } else {
@@ -538,7 +548,6 @@ __device__ __forceinline__ void chain_sweep(const BwdArgs &a, ChainSmem<P, N, si
                 acc[u] = gmm == 0.f ? zero4() : acc[u] * gmm;
             }
         }
-        (void)len;
 #pragma unroll
         for (int ks = 0; ks < kQ / 32; ++ks) {
             u32x4 bo[3];
@@ -551,13 +560,13 @@ __device__ __forceinline__ void chain_sweep(const BwdArgs &a, ChainSmem<P, N, si
                     const int nt = t / TP;
                     // result rows n (the A operand's columns), columns p
                     const u32x4 a0 = tr_op(&sm.a[0][0][0], Sm::RA, 32 * ks, nt * 16);
-                    if (EXACT) {
+                    if constexpr (EXACT) {
                         acc[u] = mfma16x16x32(a0, bo[2], acc[u]);
                         acc[u] = mfma16x16x32(a0, bo[1], acc[u]);
                         acc[u] = mfma16x16x32(a0, bo[0], acc[u]);
                     } else {
-                        const u32x4 a1 = tr_op(&sm.a[Sm::NA > 1 ? 1 : 0][0][0], Sm::RA, 32 * ks, nt * 16);
-                        const u32x4 a2 = tr_op(&sm.a[Sm::NA > 2 ? 2 : 0][0][0], Sm::RA, 32 * ks, nt * 16);
+                        const u32x4 a1 = tr_op(&sm.a[1][0][0], Sm::RA, 32 * ks, nt * 16);
+                        const u32x4 a2 = tr_op(&sm.a[2][0][0], Sm::RA, 32 * ks, nt * 16);
                         // the six products down to 2^-16 x 2^-16 of the leading one
                         acc[u] = mfma16x16x32(a1, bo[1], acc[u]);
                         acc[u] = mfma16x16x32(a2, bo[0], acc[u]);
@@ -991,7 +1000,7 @@ __global__ __launch_bounds__(kGradThreads) void k_bwd_grad_heads(BwdArgs a) {
 // three bf16 parts. Operands are read so that both of a product agree on the
 // order of k inside an instruction: lane group g holds k32 + 4g + (0..3) and
 // k32 + 16 + 4g + (0..3), read along a row (dir_op) or down the rows of a
-// row-major tile (tr_op).
+// row-major tile (tr_ops).
 
 // The bf16 tiles of this kernel are row-major [row][col] arrays padded by
 // 16 elements a row (so that consecutive rows start 4 bank pairs apart, of
