@@ -272,11 +272,16 @@ struct StateSmem {
     alignas(16) uint16_t bn[bn_elems(kSub)];   // B [t][n], bn_row layout
     alignas(16) uint16_t xs[kSub * kXS];    // x [t][p]
     float run[2];   // running sum of a from the outgoing edge, by step parity
+    int stop[2];    // the previous sub-block reached another sequence
 };
 
-// SP: dt holds the step size's pre-activation (softplus(dt + bias) is used)
+// SP: dt holds the step size's pre-activation (softplus(dt + bias) is used).
+// The sub-blocks are walked one after another; each one's rows (B, x, and on
+// wave 0 its step sizes and sequence indices) are fetched into registers
+// while the one before is multiplied, so a step costs about one of the two
+// rather than their sum.
 template <bool SP>
-__global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) k_seg_state(const SegArgs a) {
     const int seg = blockIdx.x, d = blockIdx.y;
     const int b = blockIdx.z / a.H, h = blockIdx.z % a.H;
     const int grp = h / (a.H / a.G);
@@ -292,51 +297,73 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
 
     const int edge = d == 0 ? t1 - 1 : t0;
     const int edge_seq = a.seq ? a.seq[tok(a, b, edge)] : 0;
-    if (tid == 0) sm.run[0] = 0.f;
+    if (tid == 0) {
+        sm.run[0] = 0.f;
+        sm.stop[0] = 0;
+    }
     // wave w owns state columns p = 16w..16w+15 for all n
     f32x4 Hacc[kN / 16];
 #pragma unroll
     for (int nt = 0; nt < kN / 16; ++nt) Hacc[nt] = zero4();
-    __syncthreads();
 
     const int nsub = (t1 - t0 + kSub - 1) / kSub;
-    int step = 0;
-    for (; step < nsub; ++step) {
-        // sub-block [s0, s1), the step-th counted away from the outgoing edge
-        const int s0 = d == 0 ? max(t0, t1 - kSub * (step + 1)) : t0 + kSub * step;
-        const int s1 = d == 0 ? t1 - kSub * step : min(t1, s0 + kSub);
-        const int n = s1 - s0;
-        // every remaining weight is e^{<= run} * dt == 0.0f exactly, or every
-        // remaining token belongs to another sequence: nothing left to add
-        const float run = sm.run[step & 1];
-        if (run < kDead) break;
-        if (a.seq && a.seq[tok(a, b, d == 0 ? s1 - 1 : s0)] != edge_seq) break;
-        RowStage<kSub, kN, kBS, kThreads, true> sb;
-        RowStage<kSub, kP, kXS, kThreads> sx;
+    // sub-block k = [s0, s0 + n), the k-th counted away from the outgoing edge
+    auto sub0 = [&](int k) { return d == 0 ? max(t0, t1 - kSub * (k + 1)) : t0 + kSub * k; };
+    auto subn = [&](int k) { return d == 0 ? t1 - kSub * k - sub0(k) : min(t1, t0 + kSub * (k + 1)) - sub0(k); };
+    RowStage<kSub, kN, kBS, kThreads, true> sb;
+    RowStage<kSub, kP, kXS, kThreads> sx;
+    uint16_t dtr = 0;     // wave 0: raw step size of the lane's token
+    int sqr = edge_seq;   // wave 0: its sequence index
+    auto fetch = [&](int k) {
+        const int s0 = sub0(k), n = subn(k);
         sb.load(Bm + (tok(a, b, s0) * a.G + grp) * kN, (uint32_t)(a.G * kN), n);
         sx.load(X + (tok(a, b, s0) * a.H + h) * kP, (uint32_t)(a.H * kP), n);
         if (w == 0) {
-            // lane 0 is the token nearest the outgoing edge
+            // lane 0 is the token nearest the outgoing edge; lanes past the
+            // sub-block re-read its last token (not used)
+            const int pos = min(d == 0 ? n - 1 - lane : lane, n - 1);
+            const size_t ti = tok(a, b, s0 + max(pos, 0));
+            dtr = DT[ti * a.H + h];
+            if (a.seq) sqr = a.seq[ti];
+        }
+    };
+    fetch(0);
+    __syncthreads();
+
+    int step = 0;
+    for (; step < nsub; ++step) {
+        const int n = subn(step);
+        // every remaining weight is e^{<= run} * dt == 0.0f exactly, or every
+        // remaining token belongs to another sequence: nothing left to add
+        const float run = sm.run[step & 1];
+        if (run < kDead || sm.stop[step & 1]) break;
+        if (w == 0) {
             const bool in = lane < n;
             const int pos = d == 0 ? n - 1 - lane : lane;
             float at = 0.f, dtt = 0.f;
             if (in) {
-                dtt = bf2f(DT[tok(a, b, s0 + pos) * a.H + h]);
+                dtt = bf2f(dtr);
                 if (SP) dtt = softplus_dt(dtt + dtb);
                 at = dtt * Ah;
             }
             const float incl = wave_scan(at);
             float wt = 0.f;
-            if (in && (!a.seq || a.seq[tok(a, b, s0 + pos)] == edge_seq))
-                wt = expf(run + incl - at) * dtt;
+            if (in && (!a.seq || sqr == edge_seq)) wt = expf(run + incl - at) * dtt;
             if (in) sm.w[pos] = wt;
             else sm.w[lane] = 0.f;
             const float tot = __shfl(incl, 63, 64);
-            if (lane == 0) sm.run[(step + 1) & 1] = run + tot;
+            // the sub-block's token farthest from the edge (lane n - 1): once
+            // it lies in another sequence, so does everything past it
+            const int far_seq = __shfl(sqr, n - 1, 64);
+            if (lane == 0) {
+                sm.run[(step + 1) & 1] = run + tot;
+                sm.stop[(step + 1) & 1] = a.seq && far_seq != edge_seq;
+            }
         }
         sb.store(n, sm.bn);
         sx.store(n, sm.xs);
-        __syncthreads();
+        lds_barrier();
+        if (step + 1 < nsub) fetch(step + 1);
         // H[n][p] += sum_t B^T[n][t] (w_t x_t[p]): A = B^T rows, B = w x
 #pragma unroll
         for (int ks = 0; ks < kSub / 32; ++ks) {
@@ -349,7 +376,7 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
                 Hacc[nt] = mfma16x16x32(aop, blo, Hacc[nt]);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     // Hacc[nt][r] = H[n = 16nt + 4g4 + r][p = 16w + l16]
     const size_t si = (((size_t)b * 2 + d) * a.nseg + seg) * a.H + h;
@@ -361,7 +388,7 @@ __global__ void __launch_bounds__(kThreads) k_seg_state(const SegArgs a) {
         // the incoming state passes through iff the whole segment was walked
         // (its total decay did not underflow), and no sequence boundary lies
         // between the segment's incoming side and its edge
-        bool carry = step == nsub;
+        bool carry = step == nsub && !sm.stop[nsub & 1];
         if (carry && a.seq) {
             if (d == 0 && t0 > 0) carry = a.seq[tok(a, b, t0 - 1)] == edge_seq;
             if (d == 1 && t1 < a.L) carry = a.seq[tok(a, b, t1)] == edge_seq;
