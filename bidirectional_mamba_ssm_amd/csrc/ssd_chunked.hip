@@ -2065,25 +2065,33 @@ size_t seg_workspace(int batch, int L, int H, long ts) {
     return al256(st) * 2 + al256((size_t)batch * 2 * nseg * H * 4);
 }
 
-// Segment length: a power-of-two multiple of the chunk chosen for the output
-// kernel's time, estimated as (rounds of 256 workgroups, one per CU) x (the
-// segment's tokens + 256 tokens' worth of per-workgroup overhead), ties to
-// the longer segment: long segments mean fewer segment states to write, scan
-// and read, and the segment pass stops reading a segment once its decay has
+// Segment length: a multiple of the chunk chosen for the output kernel's
+// time, estimated as (rounds of 256 workgroups, one per CU) x (the segment's
+// tokens + 256 tokens' worth of per-workgroup overhead), ties to the longer
+// segment: long segments mean fewer segment states to write, scan and read,
+// and the segment pass stops reading a segment once its decay has
 // underflowed, but a partial last round of workgroups costs as much as a
-// full one. With a workspace limit, then doubled until the segment states fit
-// in it (a whole row is one segment and needs none).
+// full one. The candidates are, for each segment count n, the shortest
+// multiple of the chunk that cuts a row into n segments (so a row whose
+// length is not a power of two can still fill whole rounds); counts are
+// tried until they would need eight rounds. With a workspace limit, the
+// length is then doubled until the segment states fit in it (a whole row is
+// one segment and needs none).
 int pick_ts(int batch, int L, int H, int Q, size_t limit) {
     const long pairs = (long)batch * ((H + 1) / 2);
+    const long nmax = ((long)L + Q - 1) / Q;
     long ts = Q, best_cost = -1;
-    for (long t = Q;; t *= 2) {
-        const long rounds = (pairs * ((L + t - 1) / t) + 255) / 256;
+    for (long n = 1; n <= nmax && (n == 1 || pairs * n <= 8L * 256); ++n) {
+        long t = ((long)L + n - 1) / n;
+        t = (t + Q - 1) / Q * Q;
+        const long segs = ((long)L + t - 1) / t;
+        if (segs != n) continue;   // the same length as a smaller count
+        const long rounds = (pairs * segs + 255) / 256;
         const long cost = rounds * (t + 256);
-        if (best_cost < 0 || cost <= best_cost) {
+        if (best_cost < 0 || cost < best_cost || (cost == best_cost && t > ts)) {
             ts = t;
             best_cost = cost;
         }
-        if (t >= L) break;
     }
     while (ts < L && seg_workspace(batch, L, H, ts) > limit) ts *= 2;
     return (int)(ts < L ? ts : (L > Q ? L : Q));
