@@ -1260,14 +1260,15 @@ __device__ void dual_half(const SegArgs &a, OutSmem<64> &sm, float *ex, int b, i
     const float Dh = dp.D ? dp.D[h] : 0.f;
     const size_t PN = (size_t)kP * kN;
     const int hoff = (16 * w + l16) * kN + 4 * g4;   // + 16 q: this lane's state entries
-    ChunkLoads<Q, false, WB> ld;
-    ld.issue(a, D, b, h, grp, 0, len);
-    TileIn tin;
-    tile_fetch<D>(tin, a, b, h, grp, 0, len, w, false);
+    // the carried state (the largest piece, needed first) goes out first
     f32x4 Hacc[NQ];
     const float *src = D == 0 && a.init_state ? a.init_state + ((size_t)b * a.H + h) * PN : nullptr;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) Hacc[q] = src ? *(const f32x4 *)(src + hoff + 16 * q) : zero4();
+    ChunkLoads<Q, false, WB> ld;
+    ld.issue(a, D, b, h, grp, 0, len);
+    TileIn tin;
+    tile_fetch<D>(tin, a, b, h, grp, 0, len, w, false);
     if (src) publish_state<Q, WB>(sm, Hacc);
     chunk_prep<Q, false, WB, SP>(a, sm, ld, D, b, h, 0, len);   // barrier 1
     f32x4 acc[4];
@@ -1282,18 +1283,22 @@ __device__ void dual_half(const SegArgs &a, OutSmem<64> &sm, float *ex, int b, i
     }
     lds_barrier();   // barrier 2: the reverse sums are in LDS
     if (D == 0) {
+        // the committed state is updated and stored before the y stores: the
+        // waits that the compiler places before reusing a store's registers
+        // count every store in flight (one counter covers loads and stores),
+        // so work after the y stores would first wait for them to land
+        if (a.final_state) {
+            chunk_state_update<Q, false, false, WB>(sm, Hacc, len, true, ld);
+            float *fs = a.final_state + ((size_t)b * a.H + h) * PN;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) *(f32x4 *)(fs + hoff + 16 * q) = Hacc[q];
+        }
         if (mine) {
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[pt][r] += ex[(16 * w + 4 * g4 + r) * kEX + 16 * pt + l16];
             store_tile(a, b, h, len, w, acc);
-        }
-        if (a.final_state) {
-            chunk_state_update<Q, false, false, WB>(sm, Hacc, len, true, ld);
-            float *fs = a.final_state + ((size_t)b * a.H + h) * PN;
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) *(f32x4 *)(fs + hoff + 16 * q) = Hacc[q];
         }
     }
 }
