@@ -311,3 +311,27 @@ def test_merge_validation(lib):
     assert call(bias=FAKE + 2) == _abi.EINVAL
     assert call(bias=FAKE + 4) == _abi.EINVAL
     assert call(rows=0, yf=None, yb=None, w=None, out=None) == _abi.OK
+
+
+def _al256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("batch,L,H,chunk,nseg", [
+    (1, 131072, 64, 256, 8),    # the long prefill: 16 384-token segments, one round of 256 workgroups
+    (1, 148170, 64, 256, 8),    # the packed batch's length: 18 688-token segments (not a power of two)
+    (1, 32768, 64, 256, 8),
+    (1, 5000, 64, 64, 8),       # 640-token segments
+    (8, 1024, 64, 256, 1),      # the training layer: whole rows, no segment states
+    (1, 1000, 4, 256, 4),       # few heads: 256-token segments
+])
+def test_segment_rule_workspace(lib, batch, L, H, chunk, nseg):
+    """The workspace the chunked scan asks for holds the segment states of
+    the segment count its length rule gives (a multiple of the chunk, the
+    shortest for each count, costed in rounds of 256 workgroups)."""
+    s = shape(batch=batch, seqlen=L, nheads=H, headdim=64, d_state=128, chunk=chunk, dtype=_abi.BF16)
+    n = ctypes.c_size_t(0)
+    assert lib.bimamba_ssd_workspace_size(ctypes.byref(s), 0, ctypes.byref(n)) == _abi.OK
+    want = 0 if nseg == 1 else (2 * _al256(batch * 2 * nseg * H * 64 * 128 * 4) +
+                                _al256(batch * 2 * nseg * H * 4))
+    assert n.value == want
