@@ -314,10 +314,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     RowStage<kSub, kP, kXS, kThreads> sx;
     uint16_t dtr = 0;     // wave 0: raw step size of the lane's token
     int sqr = edge_seq;   // wave 0: its sequence index
+    // a whole sub-block (every one but a segment's last, in walking order)
+    // is read without clamping: this thread's pieces sit at fixed offsets
+    // from the sub-block's first row (RowStage's item order: B item
+    // tid + 256 q is row tid / 16 + 16 q, x item tid + 256 q row tid / 8 + 32 q)
+    const uint32_t bstride = (uint32_t)(a.G * kN), xstride = (uint32_t)(a.H * kP);
+    const uint32_t boff = (uint32_t)(tid >> 4) * bstride + 8 * (tid & 15);
+    const uint32_t xoff = (uint32_t)(tid >> 3) * xstride + 8 * (tid & 7);
     auto fetch = [&](int k) {
         const int s0 = sub0(k), n = subn(k);
-        sb.load(Bm + (tok(a, b, s0) * a.G + grp) * kN, (uint32_t)(a.G * kN), n);
-        sx.load(X + (tok(a, b, s0) * a.H + h) * kP, (uint32_t)(a.H * kP), n);
+        const uint16_t *bb = Bm + (tok(a, b, s0) * a.G + grp) * kN;
+        const uint16_t *xb = X + (tok(a, b, s0) * a.H + h) * kP;
+        if (n == kSub) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sb.v[q] = ld8(bb + boff + (uint32_t)q * 16 * bstride);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) sx.v[q] = ld8(xb + xoff + (uint32_t)q * 32 * xstride);
+        } else {
+            sb.load(bb, bstride, n);
+            sx.load(xb, xstride, n);
+        }
         if (w == 0) {
             // lane 0 is the token nearest the outgoing edge; lanes past the
             // sub-block re-read its last token (not used)
@@ -360,8 +376,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
                 sm.stop[(step + 1) & 1] = a.seq && far_seq != edge_seq;
             }
         }
-        sb.store(n, sm.bn);
-        sx.store(n, sm.xs);
+        if (n == kSub) {   // (no row past the end to zero)
+            sb.store(kSub, sm.bn);
+            sx.store(kSub, sm.xs);
+        } else {
+            sb.store(n, sm.bn);
+            sx.store(n, sm.xs);
+        }
         lds_barrier();
         if (step + 1 < nsub) fetch(step + 1);
         // H[n][p] += sum_t B^T[n][t] (w_t x_t[p]): A = B^T rows, B = w x
