@@ -1398,6 +1398,7 @@ struct PairScan {
     int wsub;              // some weight of the chunk is nonzero
     float gamma;           // decay of the whole chunk (0: the state does not pass)
     int sq_nb;             // sequence index of the token the carried state comes from
+    int uni;               // (packed) the chunk's tokens and that token are of one sequence
 };
 
 // fp32 value moved across lanes by a DPP control; lanes without a source (or
@@ -1468,12 +1469,18 @@ __device__ __forceinline__ void pair_scans(const SegArgs &a, PairScan &sm, uint1
     if (in && (!PACKED || sqv == sq_edge)) wt = exp2_(total - cs) * dtf;
     sm.w[pos] = wt;
     const bool nz = __ballot(wt != 0.f) != 0ull;
+    // every token of the chunk in the sequence of its outgoing edge, and the
+    // carried state (if any) from that sequence too: then every sequence mask
+    // of the chunk's products passes, and the unmasked products give the
+    // same values
+    const bool uni = !PACKED || (__ballot(in && sqv != sq_edge) == 0ull && (!has_nb || sq_nb == sq_edge));
     if (lane == 0) {
         bool carry = true;
         if (PACKED) carry = has_nb && sq_nb == sq_edge;
         sm.gamma = carry ? exp2_(total) : 0.f;
         sm.sq_nb = PACKED ? sq_nb : 0;
         sm.wsub = nz;
+        sm.uni = uni;
     }
 }
 // One chunk's staged inputs (fp16): B and C of the group, x of each head.
@@ -1986,7 +1993,11 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         // a row tile past the chunk's end is computed (not read), the state's
         // part is taken with a zero state before the first update, and the
         // last chunk's update is kept (its result unused unless final)
-        pair_mrows<PACKED, D>(sm.m, st, sm.sc[0][s & 1], sm.sc[1][s & 1], rt, kk, Dh0, Dh1);
+        // (packed rows: a chunk inside one sequence builds M unmasked)
+        if (!PACKED || __builtin_amdgcn_readfirstlane(sm.sc[0][s & 1].uni))
+            pair_mrows<false, D>(sm.m, st, sm.sc[0][s & 1], sm.sc[1][s & 1], rt, kk, Dh0, Dh1);
+        else
+            pair_mrows<PACKED, D>(sm.m, st, sm.sc[0][s & 1], sm.sc[1][s & 1], rt, kk, Dh0, Dh1);
         pair_state_out<PACKED>(acc, st, sc, Hacc);
         pair_state_update(st, half, sc, Hacc, v);
         lds_barrier();   // every row tile of M written
