@@ -1585,6 +1585,20 @@ struct PairLoads {
     // passes the same waits
     __device__ __forceinline__ void store(PairStage &st, int half, int len) const {
         const int th = threadIdx.x & 255, tid = threadIdx.x;
+        if (len == 64) {   // a whole chunk (a uniform branch): no row to zero
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int item = th + 256 * k, row = item >> 3, cg = item & 7;
+                *(u32x4 *)(st.xs[half] + row * kXS + 8 * cg) = bf2h4(xv[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int item = tid + 512 * k, row = item >> 4, cg = item & 15;
+                *(u32x4 *)(st.bn + bn_row(row) + 8 * cg) = bf2h4(bv[k]);
+                *(u32x4 *)(st.cn + bn_row(row) + 8 * cg) = bf2h4(cv[k]);
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int item = th + 256 * k, row = item >> 3, cg = item & 7;
