@@ -18,10 +18,15 @@
 // Kernels:
 //   k_seg_state  (4 waves) each segment's (Ts tokens) outgoing state from a
 //                zero state, walking away from the outgoing edge and stopping
-//                where every remaining weight is exactly 0.0f in fp32
+//                where every remaining weight is exactly 0.0f in fp32; the
+//                next sub-block's rows are fetched during the current one's
+//                products
 //   k_seg_scan   incoming state of each segment where a chain carries over;
 //                where a segment's carry factor is 0 the next segment's
 //                incoming state is just the previous segment's local state
+//   k_pair_out   the output kernel wherever a group's heads pair up (8 waves,
+//                two heads per workgroup, 64-token chunks, fp16 products with
+//                a range guard; described at its definition below)
 //   k_seg_out    (8 waves, two per SIMD) per (row, segment, head): the reverse
 //                direction walks the segment's chunks right to left writing
 //                its part of y, the forward direction walks left to right and
@@ -38,7 +43,8 @@
 //                waves 4-7 the forward one, the reverse sums handed over
 //                through LDS.
 //
-// Everything runs on v_mfma_f32_16x16x32_bf16. x, B, C are bf16 already and
+// k_seg_state, k_seg_out and k_dual_out run on v_mfma_f32_16x16x32_bf16 (and
+// k_pair_out on its fp16 form, see there). x, B, C are bf16 already and
 // enter exactly. An operand that has to be rounded (the masked decayed Gram
 // matrix M, the carried state H, the dt-weighted inputs w x) is split into
 // hi = bf16(v) and lo = bf16(v - hi) and multiplied twice: ~16 significant
