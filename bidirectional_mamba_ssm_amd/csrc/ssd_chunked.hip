@@ -1369,6 +1369,11 @@ k_dual_out(const SegArgs a) {
 // fp32's range), which overwrites every output. final_state is written only
 // after that check. Magnitudes below fp16's normal range (2^-14) keep an
 // absolute error of at most 2^-25 per rounded value.
+//
+// Packed sequences: every product is masked by the tokens' sequence indices,
+// except that a chunk whose tokens, and the token its carried state comes
+// from, are all of one sequence (all but the few chunks holding a boundary)
+// builds M with the unmasked code: every mask would pass there.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pk_h(float a, float b) {
@@ -1586,9 +1591,10 @@ struct PairLoads {
             cv[k] = ld8(Cm + o);
         }
     }
-    // converted to fp16 into the stage (x into the half's head); rows at or
-    // past len as zeros, masked rather than branched so that every lane
-    // passes the same waits
+    // converted to fp16 into the stage (x into the half's head); in a
+    // partial chunk, rows at or past len as zeros, masked rather than
+    // branched per row so that every lane passes the same waits (a whole
+    // chunk, the uniform common case, is stored unmasked)
     __device__ __forceinline__ void store(PairStage &st, int half, int len) const {
         const int th = threadIdx.x & 255, tid = threadIdx.x;
         if (len == 64) {   // a whole chunk (a uniform branch): no row to zero
