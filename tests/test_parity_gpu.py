@@ -100,6 +100,10 @@ def test_init_and_final_state(dtype):
     ("bf16", 64, [37, 0, 100, 1, 70, 64]),
     ("bf16", 256, [300, 1, 0, 512, 129, 255, 256, 2]),
     ("bf16", 128, [1] * 9 + [500]),
+    # boundaries on 64-token chunk edges: whole chunks of one sequence next
+    # to a boundary (and, at chunk 64, many segments whose edges meet them)
+    ("bf16", 64, [64, 128, 640, 64, 1024, 192]),
+    ("bf16", 256, [256, 768, 64, 1344]),
 ])
 def test_packed_sequences(dtype, chunk, lens):
     cu = synth.cu_seqlens_of(lens)
