@@ -402,10 +402,51 @@ def scan_line(bm, torch, f, b, w, chunk, steps, warmup, cu=None, traffic=True):
     return res
 
 
+def ceilings(torch, dev):
+    """Practical ceilings on this machine, next to the vendor peaks (context for
+    the roofline fractions; library kernels, not this path): a plain device
+    copy of 1 GiB (bytes read + written per second) and a dense bf16 matrix
+    product of 8192 x 8192 x 8192 (torch.mm on contiguous operands)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    src = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 20 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    g = torch.Generator(device=dev).manual_seed(7)
+    n = 8192
+    a = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16).contiguous()
+    b = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        c = torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    mm_tflops = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_1gib": {"achieved": round(copy_gbs, 1), "unit": "GB/s",
+                          "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4)},
+            "bf16_mm_8192": {"achieved": round(mm_tflops, 1), "unit": "TFLOP/s",
+                             "frac_of_peak": round(mm_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+
+
 def extras(args, bm, synth, torch, dev):
     import numpy as np
     res = {}
     steps = max(3, args.steps // 2)
+    res["ceilings"] = ceilings(torch, dev)
     # one mixer layer at the training length (8 x 1024 tokens), and the 32k prefill
     for name in ("layer_1p3b_train", "long_32k"):
         w = synth.WORKLOADS[name]
