@@ -1563,6 +1563,29 @@ struct PairLoads {
     }
     // X: the chunk's first row of x for the half's head; Bm, Cm: of B and C
     // for the group
+    // the same loads in two parts: x, and B with C (a partial chunk's rows
+    // read clamped), so that a chunk's loads can go out at two points of the
+    // previous chunk's work
+    __device__ __forceinline__ void issue_x(const SegArgs &a, const uint16_t *X, int len) {
+        const int th = threadIdx.x & 255;
+        const uint32_t xstride = (uint32_t)(a.H * kP);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = th + 256 * k, row = item >> 3, cg = item & 7;
+            xv[k] = len == 64 ? ld8(X + ox[k]) : ld8(X + (uint32_t)min(row, len - 1) * xstride + 8 * cg);
+        }
+    }
+    __device__ __forceinline__ void issue_bc(const SegArgs &a, const uint16_t *Bm, const uint16_t *Cm, int len) {
+        const int tid = threadIdx.x;
+        const uint32_t bstride = (uint32_t)(a.G * kN);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = tid + 512 * k, row = item >> 4, cg = item & 15;
+            const uint32_t o = len == 64 ? ob[k] : (uint32_t)min(row, len - 1) * bstride + 8 * cg;
+            bv[k] = ld8(Bm + o);
+            cv[k] = ld8(Cm + o);
+        }
+    }
     __device__ __forceinline__ void issue(const SegArgs &a, const uint16_t *X, const uint16_t *Bm,
                                           const uint16_t *Cm, int len) {
         const int th = threadIdx.x & 255, tid = threadIdx.x;
@@ -2005,9 +2028,11 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         int c0n, lenn;
         chunk_at(last ? s : s + 1, c0n, lenn);
         lds_barrier();   // chunk s staged and scanned
-        // the next chunk's loads (the last chunk re-reads its own) go out at
-        // once, to land during this chunk's work
-        issue(c0n, lenn);
+        // the next chunk's loads (the last chunk re-reads its own) land during
+        // this chunk's work: x and the step sizes now, B and C after the
+        // carried state's term (all eight waves issuing all of them at once
+        // after the barrier held every wave up in the memory pipeline)
+        ld.issue_x(a, xrow + (size_t)c0n * xstride, lenn);
         issue_dt(c0n, lenn);
         if (ADD) {
             pair_prev_regs(acc, len);
@@ -2025,6 +2050,7 @@ __device__ __forceinline__ void pair_pass(const SegArgs &a, PairSmem &sm, int b,
         else
             pair_mrows<PACKED, D>(sm.m, st, sm.sc[0][s & 1], sm.sc[1][s & 1], rt, kk, Dh0, Dh1);
         pair_state_out<PACKED>(acc, st, sc, Hacc);
+        ld.issue_bc(a, brow + (size_t)c0n * bstride, crow + (size_t)c0n * bstride, lenn);
         pair_state_update(st, half, sc, Hacc, v);
         lds_barrier();   // every row tile of M written
         pair_mx<D>(acc, sm.m[half], st.xs[half], v);
