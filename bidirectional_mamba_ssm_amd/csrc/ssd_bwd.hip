@@ -1189,11 +1189,6 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
         ryv = *(const f32x4 *)(a.dy + o);
     }
     if (tid < kQ) dtr = ((const uint16_t *)d.dt)[(rowt + tok_of(k0 + min(tid, len - 1), a.L, rev)) * a.H + h];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        fhp[k] = *(const f32x4 *)(a.S + so + 4 * (tid + k * kMxThreads));
-        fdh[k] = *(const f32x4 *)(a.R + so + 4 * (tid + k * kMxThreads));
-    }
 
     // ---- the block's running sums of dt A (fp64), weights; the rows into LDS
     if (tid < kQ) {
@@ -1233,6 +1228,14 @@ __device__ __forceinline__ void grad_mx(const BwdArgs &a, GradMxSmem &sm, const 
         if ((tid & 15) == 15) sm.xyr[r] = xy;
     }
     __syncthreads();
+    // Hp and dHe (needed after the quadratic form) go out after the first
+    // barrier, which waits for every load in flight: the staging then waits
+    // only for the rows it stores
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        fhp[k] = *(const f32x4 *)(a.S + so + 4 * (tid + k * kMxThreads));
+        fdh[k] = *(const f32x4 *)(a.R + so + 4 * (tid + k * kMxThreads));
+    }
 
     // ---- the block's quadratic form, one 16 x 16 tile (it, jt) per wave:
     // G = C B^T, dM = dy x^T dt_j; M = L o G, L o dM into LDS (transposed,
