@@ -75,6 +75,10 @@ __device__ __forceinline__ float col_sum(float v) {
     return v;
 }
 
+template <typename T, int N, int PM, int MODE>
+__device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
+                         int t0, int t1, float (&st)[N / SeqLPP<PM>::value]);
+
 // Walks tokens [t0, t1) of one direction (upwards for d == 0, downwards for
 // d == 1) from the state in st and returns the sum of dt*A over them.
 // MODE 0: state only; MODE 1: writes y; MODE 2: adds into y. y goes through
@@ -83,6 +87,8 @@ __device__ __forceinline__ float col_sum(float v) {
 template <typename T, int N, int PM, int MODE>
 __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
                       int t0, int t1, float (&st)[N / SeqLPP<PM>::value]) {
+    // small heads (one wave per workgroup) fetch the next tile during this one
+    if constexpr (PM == 16 && N <= 32) return walk_pf<T, N, PM, MODE>(a, sm, d, row_tok, h, g, t0, t1, st);
     constexpr int LPP = SeqLPP<PM>::value;
     constexpr int NL = N / LPP;            // state entries per lane
     constexpr int NA = NL >= 16 ? 4 : NL >= 8 ? 2 : 1;   // independent partial sums of y
@@ -170,6 +176,136 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_to
                 const int s = i / P, pp = i - s * P;
                 const int t = d == 0 ? t0 + base + s : t1 - 1 - base - s;
                 Y[((row_tok + t) * H + h) * P + pp] = sm.y[s][pp];
+            }
+        }
+    }
+    return asum;
+}
+
+// walk for headdim <= 16 (one wave of 64 lanes, LPP = 4) and d_state <= 32:
+// the same arithmetic, with the next tile's inputs (B, C, x, dt, and the old
+// y when adding) loaded into registers while this tile's tokens are walked,
+// so that a tile does not start with a round trip to memory. Each lane keeps
+// one element of a token row (B, C: entry lane % N of token lane / N; x, y:
+// column lane % 16 of token lane / 16) and reaches the k-th token it handles
+// by a stride from its first one; token indices past the tile's end are
+// clamped onto its last token, so every load is in bounds and unconditional,
+// and the LDS rows (or columns past headdim) they fill are never read.
+template <typename T, int N, int PM, int MODE>
+__device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
+                         int t0, int t1, float (&st)[N / SeqLPP<PM>::value]) {
+    static_assert(PM == 16 && N <= 32, "one-wave tiles");
+    constexpr int LPP = SeqLPP<PM>::value;
+    constexpr int NL = N / LPP;
+    constexpr int NA = NL >= 16 ? 4 : NL >= 8 ? 2 : 1;
+    constexpr int RB = 64 / N, KB = kSeqTile / RB;     // B, C: tokens per pass, passes
+    constexpr int KX = kSeqTile / 4;                   // x, y: 4 tokens of 16 columns per pass
+    float *Y = (a.y2 && d == 0) ? a.y2 : a.y;
+    const int H = a.H, P = a.P, G = a.G;
+    const int lane = (int)threadIdx.x;
+    const int p = lane / LPP, q = lane % LPP;
+    const int pc = min(p, P - 1);
+    const bool own = p < P && q == LPP - 1;
+    const DirPtrs &dp = a.dir[d];
+    const float Ah = dp.A[h];
+    const float Dh = dp.D ? dp.D[h] : 0.f;
+    const float dtb = a.dt_softplus && a.dt_bias[d] ? a.dt_bias[d][h] : 0.f;
+    const int len = t1 - t0;
+    if (len <= 0) return 0.f;
+    // the first token walked and the element strides of one token in the
+    // walking direction
+    const size_t tfirst = row_tok + (d == 0 ? t0 : t1 - 1);
+    const int sgn = d == 0 ? 1 : -1;
+    const int sb = lane / N, nb = lane % N;
+    const int sx = lane / 16, px = min(lane % 16, P - 1);
+    const long stepB = (long)sgn * G * N, stepX = (long)sgn * H * P, stepD = (long)sgn * H;
+    const T *pB = (const T *)dp.B + (tfirst * G + g) * N + nb;
+    const T *pC = (const T *)dp.C + (tfirst * G + g) * N + nb;
+    const T *pX = (const T *)dp.x + (tfirst * H + h) * P + px;
+    const float *pY = Y + (tfirst * H + h) * P + px;
+    const T *pD = (const T *)dp.dt + tfirst * H + h;
+    float rb[KB], rc[KB], rx[KX], ry[KX], rdt;
+    auto fetch = [&](int base) {
+        const int last = min(len - base, kSeqTile) - 1;
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const long o = (long)(base + min(sb + RB * k, last)) * stepB;
+            rb[k] = Elem<T>::load(pB, o);
+            if (MODE != 0) rc[k] = Elem<T>::load(pC, o);
+        }
+#pragma unroll
+        for (int k = 0; k < KX; ++k) {
+            const long o = (long)(base + min(sx + 4 * k, last)) * stepX;
+            rx[k] = Elem<T>::load(pX, o);
+            if (MODE == 2) ry[k] = pY[o];
+        }
+        rdt = Elem<T>::load(pD, (long)(base + min(lane, last)) * stepD);
+    };
+    float asum = 0.f;
+    // (adding: the rows of y the other direction wrote, by other lanes, are
+    // read after a barrier)
+    __syncthreads();
+    fetch(0);
+    for (int base = 0; base < len; base += kSeqTile) {
+        const int nsteps = min(len - base, kSeqTile);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            sm.B[sb + RB * k][nb] = rb[k];
+            if (MODE != 0) sm.C[sb + RB * k][nb] = rc[k];
+        }
+#pragma unroll
+        for (int k = 0; k < KX; ++k) {
+            sm.x[sx + 4 * k][lane % 16] = rx[k];
+            if (MODE == 2) sm.y[sx + 4 * k][lane % 16] = ry[k];
+        }
+        if (lane < kSeqTile) {
+            float dtv = rdt;
+            if (a.dt_softplus) dtv = softplus_dt(dtv + dtb);
+            sm.dt[lane] = dtv;
+            const float at = dtv * Ah;
+            sm.at[lane] = at;
+            sm.dec[lane] = expf(at);
+        }
+        __syncthreads();
+        if (base + kSeqTile < len) fetch(base + kSeqTile);
+        for (int s = 0; s < nsteps; ++s) {
+            float bv[NL], cv[NL];
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                bv[i] = sm.B[s][q * NL + i];
+                cv[i] = MODE != 0 ? sm.C[s][q * NL + i] : 0.f;
+            }
+            const float decay = sm.dec[s];
+            asum += sm.at[s];
+            const float xv = sm.x[s][pc];
+            const float dx = sm.dt[s] * xv;
+            float acc[NA];
+#pragma unroll
+            for (int k = 0; k < NA; ++k) acc[k] = 0.f;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                st[i] = fmaf(decay, st[i], dx * bv[i]);
+                if (MODE != 0) acc[i % NA] = fmaf(cv[i], st[i], acc[i % NA]);
+            }
+            if (MODE != 0) {
+                float yv = acc[0];
+#pragma unroll
+                for (int k = 1; k < NA; ++k) yv += acc[k];
+                yv = col_sum<LPP>(yv);
+                if (own) {
+                    if (MODE == 1) sm.y[s][p] = fmaf(Dh, xv, yv);
+                    if (MODE == 2) sm.y[s][p] += fmaf(Dh, xv, yv);
+                }
+            }
+        }
+        if (MODE != 0) {
+            __syncthreads();
+            float *Yt = Y + (tfirst * H + h) * P + lane % 16;
+#pragma unroll
+            for (int k = 0; k < KX; ++k) {
+                const int s = sx + 4 * k;
+                if (lane % 16 < P && s < nsteps) Yt[(long)(base + s) * stepX] = sm.y[s][lane % 16];
             }
         }
     }

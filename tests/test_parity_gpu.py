@@ -343,6 +343,9 @@ SEGMENTED = [
     ("f32_two_rows_p64", 2, 1800, 1, 64, 64, 1, "f32", 128, 132),
     ("bf16_small_heads", 1, 3000, 2, 16, 16, 1, "bf16", 256, 133),
     ("f32_p24_n128", 1, 2600, 1, 24, 128, 1, "f32", 64, 134),
+    ("f32_p12_n32_ragged", 1, 3001, 2, 12, 32, 1, "f32", 64, 135),
+    # headdim x d_state = 80: the chaining pass's last wave is part empty
+    ("f32_p5_n16_part_wave", 1, 2900, 1, 5, 16, 1, "f32", 64, 136),
 ]
 
 
