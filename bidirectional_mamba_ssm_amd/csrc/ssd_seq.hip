@@ -379,39 +379,63 @@ __global__ void __launch_bounds__(kMaxP) k_seq_seg_state(const SeqArgs a) {
     if (threadIdx.x == 0) a.tot[slot] = expf(asum);
 }
 
-// Pass 2: incoming state of every segment, one thread per state element,
-// sequential over the segments in the walking direction. 32 segments'
-// values are loaded (at clamped indices, without branches) before any is
-// used, so that their loads are in flight together.
+// Pass 2: incoming state of every segment, one lane per state element and a
+// run of consecutive segments (in the walking direction) per wave: each wave
+// folds its run from a zero state into the run's decay product and outgoing
+// state, the runs' incoming states are chained through LDS (the same linear
+// recurrence, a run at a time), and each wave reruns its segments from its
+// run's incoming state, storing every segment's. 32 segments' values are
+// loaded (at clamped indices, without branches) before any is used, so that
+// their loads are in flight together; their decays, the same in every lane,
+// come one per lane and are read out lane by lane.
+constexpr int kScanWaves = 16;
+
 template <int N>
-__global__ void __launch_bounds__(256) k_seq_seg_scan(const SeqArgs a) {
-    const int e = blockIdx.x * 256 + threadIdx.x;   // p * N + n
+__global__ void __launch_bounds__(64 * kScanWaves) k_seq_seg_scan(const SeqArgs a) {
+    constexpr int kB = 32;
+    __shared__ float run_s[kScanWaves][64];
+    __shared__ float run_t[kScanWaves];
+    const int lane = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + lane;   // p * N + n
     const int h = blockIdx.y;
     const int row = blockIdx.z / a.ndir, d = blockIdx.z % a.ndir;
     const int PN = a.P * N;
-    if (e >= PN) return;
-    constexpr int kB = 32;
+    // lanes past the last element work on a clamped one and store nothing
+    const bool live = e < PN;
+    const int ec = live ? e : PN - 1;
+    const int per = (a.nseg + kScanWaves - 1) / kScanWaves;
+    const int s_begin = min(w * per, a.nseg), s_end = min(s_begin + per, a.nseg);
+    auto slot_of = [&](int s) { return seg_slot(a, row, d, d == 0 ? s : a.nseg - 1 - s, h); };
+    // walks the run from hv; stores each segment's incoming state if asked;
+    // returns the product of the run's decays
+    auto walk_run = [&](float &hv, bool store) {
+        float tp = 1.f;
+        for (int s0 = s_begin; s0 < s_end; s0 += kB) {
+            float sv[kB];
+#pragma unroll
+            for (int k = 0; k < kB; ++k) sv[k] = a.S[slot_of(min(s0 + k, s_end - 1)) * PN + ec];
+            const float tl = a.tot[slot_of(min(s0 + (lane & (kB - 1)), s_end - 1))];
+#pragma unroll
+            for (int k = 0; k < kB; ++k) {
+                if (s0 + k >= s_end) break;
+                const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tl), k));
+                if (store && live) a.Hin[slot_of(s0 + k) * PN + e] = hv;
+                hv = fmaf(tv, hv, sv[k]);
+                tp *= tv;
+            }
+        }
+        return tp;
+    };
     float hv = 0.f;
-    if (d == 0 && a.init_state) hv = a.init_state[((size_t)row * a.H + h) * PN + e];
-    for (int s0 = 0; s0 < a.nseg; s0 += kB) {
-        float sv[kB], tv[kB];
-#pragma unroll
-        for (int k = 0; k < kB; ++k) {
-            const int s = min(s0 + k, a.nseg - 1);
-            const size_t slot = seg_slot(a, row, d, d == 0 ? s : a.nseg - 1 - s, h);
-            sv[k] = a.S[slot * PN + e];
-            tv[k] = a.tot[slot];
-        }
-#pragma unroll
-        for (int k = 0; k < kB; ++k) {
-            if (s0 + k >= a.nseg) break;
-            const int s = s0 + k;
-            const size_t slot = seg_slot(a, row, d, d == 0 ? s : a.nseg - 1 - s, h);
-            a.Hin[slot * PN + e] = hv;
-            hv = fmaf(tv[k], hv, sv[k]);
-        }
-    }
-    if (d == 0 && a.final_state) a.final_state[((size_t)row * a.H + h) * PN + e] = hv;
+    const float tp = walk_run(hv, false);
+    run_s[w][lane] = hv;
+    if (lane == 0) run_t[w] = tp;
+    __syncthreads();
+    hv = d == 0 && a.init_state ? a.init_state[((size_t)row * a.H + h) * PN + ec] : 0.f;
+    for (int v = 0; v < w; ++v) hv = fmaf(run_t[v], hv, run_s[v][lane]);
+    walk_run(hv, true);
+    if (live && d == 0 && a.final_state && s_begin < s_end && s_end == a.nseg)
+        a.final_state[((size_t)row * a.H + h) * PN + e] = hv;
 }
 
 // Pass 3: every segment from its incoming state, both directions, y.
@@ -474,8 +498,8 @@ static hipError_t launch_pm(const SeqArgs &a, int units, hipStream_t s) {
     } else {
         BM_LAUNCH("seq_seg_state", (k_seq_seg_state<T, N, PM>), dim3(a.nseg, a.H, a.batch * a.ndir),
                   dim3(threads), 0, s, a);
-        BM_LAUNCH("seq_seg_scan", (k_seq_seg_scan<N>), dim3((a.P * N + 255) / 256, a.H, a.batch * a.ndir),
-                  dim3(256), 0, s, a);
+        BM_LAUNCH("seq_seg_scan", (k_seq_seg_scan<N>), dim3((a.P * N + 63) / 64, a.H, a.batch * a.ndir),
+                  dim3(64 * kScanWaves), 0, s, a);
         BM_LAUNCH("seq_seg_out", (k_seq_seg_out<T, N, PM>), dim3(a.nseg, a.H, a.batch), dim3(threads), 0,
                   s, a);
     }
