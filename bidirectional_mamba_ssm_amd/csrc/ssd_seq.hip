@@ -380,14 +380,15 @@ __global__ void __launch_bounds__(kMaxP) k_seq_seg_state(const SeqArgs a) {
 }
 
 // Pass 2: incoming state of every segment, one lane per state element and a
-// run of consecutive segments (in the walking direction) per wave: each wave
+// run of consecutive segments (in the walking direction) per wave (one wave
+// per 4 segments, at most kScanWaves; the launch's width): each wave
 // folds its run from a zero state into the run's decay product and outgoing
 // state, the runs' incoming states are chained through LDS (the same linear
 // recurrence, a run at a time), and each wave reruns its segments from its
-// run's incoming state, storing every segment's. 32 segments' values are
-// loaded (at clamped indices, without branches) before any is used, so that
-// their loads are in flight together; their decays, the same in every lane,
-// come one per lane and are read out lane by lane.
+// run's incoming state, storing every segment's. Up to 32 segments' values
+// are loaded before any is used, so that their loads are in flight together;
+// their decays, the same in every lane, come one per lane (at clamped
+// indices) and are read out lane by lane.
 constexpr int kScanWaves = 16;
 
 template <int N>
@@ -403,7 +404,8 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_seq_seg_scan(const SeqArgs 
     // lanes past the last element work on a clamped one and store nothing
     const bool live = e < PN;
     const int ec = live ? e : PN - 1;
-    const int per = (a.nseg + kScanWaves - 1) / kScanWaves;
+    const int nw = (int)blockDim.x >> 6;
+    const int per = (a.nseg + nw - 1) / nw;
     const int s_begin = min(w * per, a.nseg), s_end = min(s_begin + per, a.nseg);
     auto slot_of = [&](int s) { return seg_slot(a, row, d, d == 0 ? s : a.nseg - 1 - s, h); };
     // walks the run from hv; stores each segment's incoming state if asked;
@@ -413,7 +415,8 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_seq_seg_scan(const SeqArgs 
         for (int s0 = s_begin; s0 < s_end; s0 += kB) {
             float sv[kB];
 #pragma unroll
-            for (int k = 0; k < kB; ++k) sv[k] = a.S[slot_of(min(s0 + k, s_end - 1)) * PN + ec];
+            for (int k = 0; k < kB; ++k)
+                if (s0 + k < s_end) sv[k] = a.S[slot_of(s0 + k) * PN + ec];
             const float tl = a.tot[slot_of(min(s0 + (lane & (kB - 1)), s_end - 1))];
 #pragma unroll
             for (int k = 0; k < kB; ++k) {
@@ -498,8 +501,9 @@ static hipError_t launch_pm(const SeqArgs &a, int units, hipStream_t s) {
     } else {
         BM_LAUNCH("seq_seg_state", (k_seq_seg_state<T, N, PM>), dim3(a.nseg, a.H, a.batch * a.ndir),
                   dim3(threads), 0, s, a);
+        const int nw = (a.nseg + 3) / 4 < kScanWaves ? (a.nseg + 3) / 4 : kScanWaves;
         BM_LAUNCH("seq_seg_scan", (k_seq_seg_scan<N>), dim3((a.P * N + 63) / 64, a.H, a.batch * a.ndir),
-                  dim3(64 * kScanWaves), 0, s, a);
+                  dim3(64 * nw), 0, s, a);
         BM_LAUNCH("seq_seg_out", (k_seq_seg_out<T, N, PM>), dim3(a.nseg, a.H, a.batch), dim3(threads), 0,
                   s, a);
     }
