@@ -87,8 +87,8 @@ __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row
 template <typename T, int N, int PM, int MODE>
 __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
                       int t0, int t1, float (&st)[N / SeqLPP<PM>::value]) {
-    // small heads (one wave per workgroup) fetch the next tile during this one
-    if constexpr (PM == 16 && N <= 32) return walk_pf<T, N, PM, MODE>(a, sm, d, row_tok, h, g, t0, t1, st);
+    // one-wave workgroups with small states fetch the next tile during this one
+    if constexpr (PM <= 64 && N <= 32 && PM * N <= 1024) return walk_pf<T, N, PM, MODE>(a, sm, d, row_tok, h, g, t0, t1, st);
     constexpr int LPP = SeqLPP<PM>::value;
     constexpr int NL = N / LPP;            // state entries per lane
     constexpr int NA = NL >= 16 ? 4 : NL >= 8 ? 2 : 1;   // independent partial sums of y
@@ -182,24 +182,26 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_to
     return asum;
 }
 
-// walk for headdim <= 16 (one wave of 64 lanes, LPP = 4) and d_state <= 32:
-// the same arithmetic, with the next tile's inputs (B, C, x, dt, and the old
-// y when adding) loaded into registers while this tile's tokens are walked,
-// so that a tile does not start with a round trip to memory. Each lane keeps
-// one element of a token row (B, C: entry lane % N of token lane / N; x, y:
-// column lane % 16 of token lane / 16) and reaches the k-th token it handles
+// walk for headdim bounds up to 64 (one wave of 64 lanes: PM columns of LPP
+// lanes) and d_state <= 32, at most 1024 of both (the prefetch registers):
+// the same arithmetic, with the next tile's inputs
+// (B, C, x, dt, and the old y when adding) loaded into registers while this
+// tile's tokens are walked, so that a tile does not start with a round trip
+// to memory. Each lane keeps one element of a token row (B, C: entry lane % N
+// of token lane / N; x, y: column lane % PM of token lane / PM) and reaches
+// the k-th token it handles
 // by a stride from its first one; token indices past the tile's end are
 // clamped onto its last token, so every load is in bounds and unconditional,
 // and the LDS rows (or columns past headdim) they fill are never read.
 template <typename T, int N, int PM, int MODE>
 __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
                          int t0, int t1, float (&st)[N / SeqLPP<PM>::value]) {
-    static_assert(PM == 16 && N <= 32, "one-wave tiles");
+    static_assert(PM * SeqLPP<PM>::value == 64 && N <= 32 && PM * N <= 1024, "one-wave tiles");
     constexpr int LPP = SeqLPP<PM>::value;
     constexpr int NL = N / LPP;
     constexpr int NA = NL >= 16 ? 4 : NL >= 8 ? 2 : 1;
     constexpr int RB = 64 / N, KB = kSeqTile / RB;     // B, C: tokens per pass, passes
-    constexpr int KX = kSeqTile / 4;                   // x, y: 4 tokens of 16 columns per pass
+    constexpr int RX = 64 / PM, KX = kSeqTile / RX;    // x, y: tokens per pass, passes
     float *Y = (a.y2 && d == 0) ? a.y2 : a.y;
     const int H = a.H, P = a.P, G = a.G;
     const int lane = (int)threadIdx.x;
@@ -217,7 +219,7 @@ __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row
     const size_t tfirst = row_tok + (d == 0 ? t0 : t1 - 1);
     const int sgn = d == 0 ? 1 : -1;
     const int sb = lane / N, nb = lane % N;
-    const int sx = lane / 16, px = min(lane % 16, P - 1);
+    const int sx = lane / PM, cx = lane % PM, px = min(cx, P - 1);
     const long stepB = (long)sgn * G * N, stepX = (long)sgn * H * P, stepD = (long)sgn * H;
     const T *pB = (const T *)dp.B + (tfirst * G + g) * N + nb;
     const T *pC = (const T *)dp.C + (tfirst * G + g) * N + nb;
@@ -235,7 +237,7 @@ __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row
         }
 #pragma unroll
         for (int k = 0; k < KX; ++k) {
-            const long o = (long)(base + min(sx + 4 * k, last)) * stepX;
+            const long o = (long)(base + min(sx + RX * k, last)) * stepX;
             rx[k] = Elem<T>::load(pX, o);
             if (MODE == 2) ry[k] = pY[o];
         }
@@ -256,8 +258,8 @@ __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row
         }
 #pragma unroll
         for (int k = 0; k < KX; ++k) {
-            sm.x[sx + 4 * k][lane % 16] = rx[k];
-            if (MODE == 2) sm.y[sx + 4 * k][lane % 16] = ry[k];
+            sm.x[sx + RX * k][cx] = rx[k];
+            if (MODE == 2) sm.y[sx + RX * k][cx] = ry[k];
         }
         if (lane < kSeqTile) {
             float dtv = rdt;
@@ -301,11 +303,11 @@ __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row
         }
         if (MODE != 0) {
             __syncthreads();
-            float *Yt = Y + (tfirst * H + h) * P + lane % 16;
+            float *Yt = Y + (tfirst * H + h) * P + cx;
 #pragma unroll
             for (int k = 0; k < KX; ++k) {
-                const int s = sx + 4 * k;
-                if (lane % 16 < P && s < nsteps) Yt[(long)(base + s) * stepX] = sm.y[s][lane % 16];
+                const int s = sx + RX * k;
+                if (cx < P && s < nsteps) Yt[(long)(base + s) * stepX] = sm.y[s][cx];
             }
         }
     }
