@@ -108,23 +108,33 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_to
     const float Ah = dp.A[h];
     const float Dh = dp.D ? dp.D[h] : 0.f;
     const int len = t1 - t0;
+    if (len <= 0) return 0.f;
+    // the first token walked and the element strides of one token in the
+    // walking direction (x and y are staged on the PM-column grid, so that
+    // an element's token and column come from shifts)
+    const size_t tfirst = row_tok + (d == 0 ? t0 : t1 - 1);
+    const int sgn = d == 0 ? 1 : -1;
+    const long stepB = (long)sgn * G * N, stepX = (long)sgn * H * P;
+    const T *pB = Bm + (tfirst * G + g) * N;
+    const T *pC = Cm + (tfirst * G + g) * N;
+    const T *pX = X + (tfirst * H + h) * P;
+    float *pY = Y + (tfirst * H + h) * P;
     float asum = 0.f;
     for (int base = 0; base < len; base += kSeqTile) {
         const int nsteps = len - base < kSeqTile ? len - base : kSeqTile;
         __syncthreads();
         for (int i = threadIdx.x; i < nsteps * N; i += blockDim.x) {
-            const int s = i / N, n = i - s * N;
-            const int t = d == 0 ? t0 + base + s : t1 - 1 - base - s;
-            const size_t o = ((row_tok + t) * G + g) * N + n;
-            sm.B[s][n] = Elem<T>::load(Bm, o);
-            if (MODE != 0) sm.C[s][n] = Elem<T>::load(Cm, o);
+            const int s = i / N, n = i % N;
+            const long o = (long)(base + s) * stepB + n;
+            sm.B[s][n] = Elem<T>::load(pB, o);
+            if (MODE != 0) sm.C[s][n] = Elem<T>::load(pC, o);
         }
-        for (int i = threadIdx.x; i < nsteps * P; i += blockDim.x) {
-            const int s = i / P, pp = i - s * P;
-            const int t = d == 0 ? t0 + base + s : t1 - 1 - base - s;
-            const size_t o = ((row_tok + t) * H + h) * P + pp;
-            sm.x[s][pp] = Elem<T>::load(X, o);
-            if (MODE == 2) sm.y[s][pp] = Y[o];
+        for (int i = threadIdx.x; i < nsteps * PM; i += blockDim.x) {
+            const int s = i / PM, pp = i % PM;
+            if (pp >= P) continue;
+            const long o = (long)(base + s) * stepX + pp;
+            sm.x[s][pp] = Elem<T>::load(pX, o);
+            if (MODE == 2) sm.y[s][pp] = pY[o];
         }
         // the step sizes and decays of the tile, in parallel (off the
         // token-to-token chain)
@@ -172,10 +182,9 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_to
         }
         if (MODE != 0) {
             __syncthreads();
-            for (int i = threadIdx.x; i < nsteps * P; i += blockDim.x) {
-                const int s = i / P, pp = i - s * P;
-                const int t = d == 0 ? t0 + base + s : t1 - 1 - base - s;
-                Y[((row_tok + t) * H + h) * P + pp] = sm.y[s][pp];
+            for (int i = threadIdx.x; i < nsteps * PM; i += blockDim.x) {
+                const int s = i / PM, pp = i % PM;
+                if (pp < P) pY[(long)(base + s) * stepX + pp] = sm.y[s][pp];
             }
         }
     }
