@@ -75,6 +75,14 @@ __device__ __forceinline__ float col_sum(float v) {
     return v;
 }
 
+// Whether a walk prefetches the next tile into registers: one-wave
+// workgroups (headdim bound up to 64) whose prefetch registers (B, and C, x,
+// and the old y as the mode needs them) number at most 80 per lane.
+template <int N, int PM, int MODE>
+constexpr bool pf_fits() {
+    return PM <= 64 && (kSeqTile * N / 64) * (MODE != 0 ? 2 : 1) + (kSeqTile * PM / 64) * (MODE == 2 ? 2 : 1) <= 80;
+}
+
 template <typename T, int N, int PM, int MODE>
 __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
                          int t0, int t1, float (&st)[N / SeqLPP<PM>::value]);
@@ -88,7 +96,7 @@ template <typename T, int N, int PM, int MODE>
 __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
                       int t0, int t1, float (&st)[N / SeqLPP<PM>::value]) {
     // one-wave workgroups with small states fetch the next tile during this one
-    if constexpr (PM <= 64 && N <= 32 && PM * N <= 1024) return walk_pf<T, N, PM, MODE>(a, sm, d, row_tok, h, g, t0, t1, st);
+    if constexpr (pf_fits<N, PM, MODE>()) return walk_pf<T, N, PM, MODE>(a, sm, d, row_tok, h, g, t0, t1, st);
     constexpr int LPP = SeqLPP<PM>::value;
     constexpr int NL = N / LPP;            // state entries per lane
     constexpr int NA = NL >= 16 ? 4 : NL >= 8 ? 2 : 1;   // independent partial sums of y
@@ -192,24 +200,23 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_to
 }
 
 // walk for headdim bounds up to 64 (one wave of 64 lanes: PM columns of LPP
-// lanes) and d_state <= 32, at most 1024 of both (the prefetch registers):
-// the same arithmetic, with the next tile's inputs
-// (B, C, x, dt, and the old y when adding) loaded into registers while this
-// tile's tokens are walked, so that a tile does not start with a round trip
-// to memory. Each lane keeps one element of a token row (B, C: entry lane % N
-// of token lane / N; x, y: column lane % PM of token lane / PM) and reaches
-// the k-th token it handles
-// by a stride from its first one; token indices past the tile's end are
+// lanes) when the prefetch registers fit (pf_fits): the same arithmetic, with
+// the next tile's inputs (B, C, x, dt, and the old y when adding) loaded into
+// registers while this tile's tokens are walked, so that a tile does not
+// start with a round trip to memory. Each lane keeps elements of token rows
+// (B, C: element lane + 64 k of the tile's rows; x, y: column lane % PM of
+// token lane / PM) and reaches the k-th token it handles by a stride from
+// its first one; token indices past the tile's end are
 // clamped onto its last token, so every load is in bounds and unconditional,
 // and the LDS rows (or columns past headdim) they fill are never read.
 template <typename T, int N, int PM, int MODE>
 __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
                          int t0, int t1, float (&st)[N / SeqLPP<PM>::value]) {
-    static_assert(PM * SeqLPP<PM>::value == 64 && N <= 32 && PM * N <= 1024, "one-wave tiles");
+    static_assert(PM * SeqLPP<PM>::value == 64 && pf_fits<N, PM, MODE>(), "one-wave tiles");
     constexpr int LPP = SeqLPP<PM>::value;
     constexpr int NL = N / LPP;
     constexpr int NA = NL >= 16 ? 4 : NL >= 8 ? 2 : 1;
-    constexpr int RB = 64 / N, KB = kSeqTile / RB;     // B, C: tokens per pass, passes
+    constexpr int KB = kSeqTile * N / 64;              // B, C: elements per lane
     constexpr int RX = 64 / PM, KX = kSeqTile / RX;    // x, y: tokens per pass, passes
     float *Y = (a.y2 && d == 0) ? a.y2 : a.y;
     const int H = a.H, P = a.P, G = a.G;
@@ -227,11 +234,10 @@ __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row
     // walking direction
     const size_t tfirst = row_tok + (d == 0 ? t0 : t1 - 1);
     const int sgn = d == 0 ? 1 : -1;
-    const int sb = lane / N, nb = lane % N;
     const int sx = lane / PM, cx = lane % PM, px = min(cx, P - 1);
     const long stepB = (long)sgn * G * N, stepX = (long)sgn * H * P, stepD = (long)sgn * H;
-    const T *pB = (const T *)dp.B + (tfirst * G + g) * N + nb;
-    const T *pC = (const T *)dp.C + (tfirst * G + g) * N + nb;
+    const T *pB = (const T *)dp.B + (tfirst * G + g) * N;
+    const T *pC = (const T *)dp.C + (tfirst * G + g) * N;
     const T *pX = (const T *)dp.x + (tfirst * H + h) * P + px;
     const float *pY = Y + (tfirst * H + h) * P + px;
     const T *pD = (const T *)dp.dt + tfirst * H + h;
@@ -240,7 +246,9 @@ __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row
         const int last = min(len - base, kSeqTile) - 1;
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
-            const long o = (long)(base + min(sb + RB * k, last)) * stepB;
+            // element lane + 64 k: token (lane + 64 k) / N, entry (lane + 64 k) % N
+            const int i = lane + 64 * k;
+            const long o = (long)(base + min(i / N, last)) * stepB + i % N;
             rb[k] = Elem<T>::load(pB, o);
             if (MODE != 0) rc[k] = Elem<T>::load(pC, o);
         }
@@ -262,8 +270,9 @@ __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
-            sm.B[sb + RB * k][nb] = rb[k];
-            if (MODE != 0) sm.C[sb + RB * k][nb] = rc[k];
+            const int i = lane + 64 * k;
+            sm.B[i / N][i % N] = rb[k];
+            if (MODE != 0) sm.C[i / N][i % N] = rc[k];
         }
 #pragma unroll
         for (int k = 0; k < KX; ++k) {

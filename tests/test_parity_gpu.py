@@ -354,6 +354,9 @@ SEGMENTED = [
     # 695 segments: each chaining wave walks a run of more than 32
     ("f32_many_segments", 1, 200000, 1, 16, 16, 1, "f32", 64, 137),
     ("bf16_p64_n16_segments", 1, 3000, 2, 64, 16, 1, "bf16", 64, 138),
+    # d_state 64 and 128 at headdim 16: the state pass prefetches B only
+    ("bf16_p16_n128_segments", 1, 3000, 2, 16, 128, 1, "bf16", 64, 139),
+    ("f32_p16_n64_segments", 1, 2700, 1, 16, 64, 1, "f32", 64, 140),
 ]
 
 
