@@ -492,7 +492,7 @@ def extras(args, bm, synth, torch, dev):
     # (4 heads x headdim 16, d_state 16) at 131 072 tokens, chunk 256, bf16
     # (served by the token-sequential kernel in segments: the matrix-core
     # path is built for headdim 64 / d_state 128)
-    f, b = synth.make_inputs(1, 131072, 4, 16, 16, 1, "bf16", 3, device=dev)
+    f, b = synth.make_workload(synth.WORKLOADS["long_128k_small_heads"], device=dev)
     y = torch.empty(1, 131072, 4, 16, dtype=torch.float32, device=dev)
     shape = bm.make_shape(f["x"], f["B"], 256)
     ws = torch.empty(max(bm.workspace_size(shape, 0), 256), dtype=torch.uint8, device=dev)

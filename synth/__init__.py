@@ -65,6 +65,9 @@ WORKLOADS = {
                                  note="d_inner 4096 = 64 heads x 64, d_state 128"),
     "long_32k": Workload("long_32k", 1, 32768, 64, 64, 128, 1, 256, "bf16", 2),
     "long_128k": Workload("long_128k", 1, 131072, 64, 64, 128, 1, 256, "bf16", 3),
+    # the same length with the small head shape (token-sequential path)
+    "long_128k_small_heads": Workload("long_128k_small_heads", 1, 131072, 4, 16, 16, 1, 256,
+                                      "bf16", 3, note="4 heads x 16, d_state 16"),
     # packed variable-length batch with per-sequence resets
     "packed_varlen": Workload("packed_varlen", 1, 0, 64, 64, 128, 1, 256,
                               "bf16", 5, seqlens=None),
