@@ -354,9 +354,11 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "settle": {"seconds": round(settle_s, 3), "steps": n_settle},
         "roofline": roof,
-        "mfma": mfma_for(ker, dom, fpt * tokens,
-                         summary_field(summary_path(dom, w.name, "instruction_mix"),
-                                       "executed_mfma_flops_per_launch")),
+        # (the token-sequential kernels use no matrix cores)
+        "mfma": None if dom.startswith("seq_") else
+        mfma_for(ker, dom, fpt * tokens,
+                 summary_field(summary_path(dom, w.name, "instruction_mix"),
+                               "executed_mfma_flops_per_launch")),
         "algorithmic_bytes_per_token": bpt,
         "algorithmic_flops_per_token": fpt,
         "hbm_roofline_frac_step": round(bpt * tokens / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
