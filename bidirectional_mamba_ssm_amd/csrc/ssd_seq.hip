@@ -134,14 +134,14 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_to
         for (int i = threadIdx.x; i < nsteps * N; i += blockDim.x) {
             const int s = i / N, n = i % N;
             const long o = (long)(base + s) * stepB + n;
-            sm.B[s][n] = Elem<T>::load(pB, o);
-            if (MODE != 0) sm.C[s][n] = Elem<T>::load(pC, o);
+            sm.B[s][n] = Elem<T>::load(pB + o, 0);
+            if (MODE != 0) sm.C[s][n] = Elem<T>::load(pC + o, 0);
         }
         for (int i = threadIdx.x; i < nsteps * PM; i += blockDim.x) {
             const int s = i / PM, pp = i % PM;
             if (pp >= P) continue;
             const long o = (long)(base + s) * stepX + pp;
-            sm.x[s][pp] = Elem<T>::load(pX, o);
+            sm.x[s][pp] = Elem<T>::load(pX + o, 0);
             if (MODE == 2) sm.y[s][pp] = pY[o];
         }
         // the step sizes and decays of the tile, in parallel (off the
@@ -206,9 +206,9 @@ __device__ float walk(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_to
 // start with a round trip to memory. Each lane keeps elements of token rows
 // (B, C: element lane + 64 k of the tile's rows; x, y: column lane % PM of
 // token lane / PM) and reaches the k-th token it handles by a stride from
-// its first one; token indices past the tile's end are
-// clamped onto its last token, so every load is in bounds and unconditional,
-// and the LDS rows (or columns past headdim) they fill are never read.
+// its first one; token indices past the tile's end are clamped onto its last
+// token, so every load is in bounds and unconditional, and the LDS rows (or
+// columns past headdim) they fill are never read.
 template <typename T, int N, int PM, int MODE>
 __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row_tok, int h, int g,
                          int t0, int t1, float (&st)[N / SeqLPP<PM>::value]) {
@@ -249,16 +249,16 @@ __device__ float walk_pf(const SeqArgs &a, SeqSmem<N, PM> &sm, int d, size_t row
             // element lane + 64 k: token (lane + 64 k) / N, entry (lane + 64 k) % N
             const int i = lane + 64 * k;
             const long o = (long)(base + min(i / N, last)) * stepB + i % N;
-            rb[k] = Elem<T>::load(pB, o);
-            if (MODE != 0) rc[k] = Elem<T>::load(pC, o);
+            rb[k] = Elem<T>::load(pB + o, 0);
+            if (MODE != 0) rc[k] = Elem<T>::load(pC + o, 0);
         }
 #pragma unroll
         for (int k = 0; k < KX; ++k) {
             const long o = (long)(base + min(sx + RX * k, last)) * stepX;
-            rx[k] = Elem<T>::load(pX, o);
+            rx[k] = Elem<T>::load(pX + o, 0);
             if (MODE == 2) ry[k] = pY[o];
         }
-        rdt = Elem<T>::load(pD, (long)(base + min(lane, last)) * stepD);
+        rdt = Elem<T>::load(pD + (long)(base + min(lane, last)) * stepD, 0);
     };
     float asum = 0.f;
     // (adding: the rows of y the other direction wrote, by other lanes, are
