@@ -48,10 +48,11 @@ struct SeqArgs {
 // for more workgroups per CU).
 template <int N, int PM>
 struct SeqSmem {
-    float B[kSeqTile][N];
-    float C[kSeqTile][N];
-    float x[kSeqTile][PM];
-    float y[kSeqTile][PM];
+    // (16-byte aligned rows: a lane's run of state entries is one wide read)
+    alignas(16) float B[kSeqTile][N];
+    alignas(16) float C[kSeqTile][N];
+    alignas(16) float x[kSeqTile][PM];
+    alignas(16) float y[kSeqTile][PM];
     float dt[kSeqTile];
     float at[kSeqTile];    // dt * A
     float dec[kSeqTile];   // exp(dt * A)
